@@ -1,0 +1,203 @@
+/*
+ * pkm.h - C ABI of the product-key memory (PKM) lookup for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (per token t, per head h; all heads share one value table):
+ *   q_pre = x W_q^T                       query projection, no bias
+ *   q     = BN(q_pre)                     batch-statistics BatchNorm (optional)
+ *   q1,q2 = first / second half of head h's dq-wide slice of q
+ *   s1[i] = q1 . C[h,i],  s2[j] = q2 . C'[h,j]
+ *   I1 = top-k of s1, I2 = top-k of s2    (score descending, lowest index first on ties)
+ *   candidates (a,b) in I1 x I2: score s1[I1[a]] + s2[I2[b]], row I1[a]*|C'| + I2[b]
+ *   keep the k best candidates (score descending, lowest row first), w = softmax(score / tau)
+ *   y[t]  = sum_h sum_s w[t,h,s] * V[row[t,h,s], :]
+ * The residual add (x + y) belongs to the caller.
+ *
+ * Sources (web pages on product-key memory layers):
+ *  - "Meta AI 可扩展内存层" (zskr.cn article on Meta AI's scalable memory layers):
+ *    section 3.2 (query projection, top-k similarity, softmax, weighted sum),
+ *    section 4.3 (two-half lookup and k1 x k2 candidates), section 4.5 (row offset
+ *    of pair (i, j)), section 5.3 (value matrix [K1*K2, d], only candidate rows
+ *    read), sections 6.1 and 9.2 (only the selected keys and values get gradient),
+ *    section 10.1 (bias-free projection, query halves, row i * num_keys_b + j).
+ *  - gptget.net summary of arXiv 1907.05242 (product-key memory layer):
+ *    method details (C and C' of |C| vectors of dim dq/2; q split into q1, q2;
+ *    top-k per half; k best of the candidate set; weighted sum; multi-head;
+ *    back-propagation into every parameter), key results (BatchNorm on the
+ *    query, h = 4, k = 32), abstract (exact search over the product key set).
+ *
+ * Conventions (every entry point):
+ *  - Pointers named "device" point to device memory the caller owns (for example
+ *    torch tensors); the library never allocates device memory and keeps only
+ *    immutable host state in the handle.  Row-major, contiguous, 16-byte aligned.
+ *  - stream: a hipStream_t passed as void* (NULL = the default stream).  Work is
+ *    enqueued asynchronously and the call returns without synchronising; values
+ *    written on the device (outputs, *n_touched) are valid once the stream has
+ *    reached them.
+ *  - Storage dtype (pkm_config.dtype) applies to x, W_q, C, C', V, y, dY, dx and
+ *    the saved q.  Arithmetic is fp32 (bf16 storage: bf16 MFMA operands, fp32
+ *    accumulation; q is rounded to bf16 after BatchNorm).  All gradients
+ *    except dx are fp32.
+ *  - Errors: every argument is checked before any HIP call; on failure the call
+ *    returns a non-zero pkm_status, touches nothing, and pkm_last_error() gives a
+ *    message.  PKM_ERR_HIP reports a failed launch; a device-side fault shows up
+ *    at the caller's next synchronisation.  No C++ exception crosses the ABI.
+ *  - Threads: a handle is immutable after pkm_create; concurrent calls on one
+ *    handle are safe when they use distinct workspaces and outputs.
+ *  - Inputs must be finite (not checked on the device).
+ */
+#ifndef PKM_H_
+#define PKM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct pkm_handle_s* pkm_handle_t;
+
+typedef enum {
+  PKM_OK = 0,
+  PKM_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size or config value */
+  PKM_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels implement (see limits) */
+  PKM_ERR_WORKSPACE = 3,   /* workspace missing or smaller than pkm_workspace_size() */
+  PKM_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} pkm_status;
+
+typedef enum { PKM_F32 = 0, PKM_BF16 = 1 } pkm_dtype;
+typedef enum { PKM_BN_NONE = 0, PKM_BN_BATCH = 1 } pkm_bn_mode;
+
+/* Layer shape.  Limits checked by pkm_create:
+ *   d_in >= 1, d_in % 8 == 0; heads >= 1; d_query even, 2 <= d_query, (d_query/2) % 8 == 0 ... see below;
+ *   1 <= topk <= 32, topk <= n_keys, topk <= n_keys2; 1 <= n_keys, n_keys2 <= 2048;
+ *   n_keys * n_keys2 < 2^31; d_value >= 1, d_value % 8 == 0; heads * topk <= 1024;
+ *   temperature > 0; bn_eps >= 0.
+ * (d_query/2 must be a multiple of 16 for bf16 and of 4 for fp32 storage.) */
+typedef struct {
+  int32_t d_in;          /* d: width of x */
+  int32_t heads;         /* h */
+  int32_t d_query;       /* dq: per-head query width (two halves of dq/2) */
+  int32_t n_keys;        /* |C|: sub-keys of the first half, per head */
+  int32_t n_keys2;       /* |C'|: sub-keys of the second half, per head */
+  int32_t topk;          /* k: per-half top-k and number of selected slots per head */
+  int32_t d_value;       /* width of a value row and of y */
+  int32_t dtype;         /* pkm_dtype */
+  int32_t bn;            /* pkm_bn_mode */
+  float bn_eps;          /* BatchNorm epsilon (1e-5) */
+  float temperature;     /* tau: w = softmax(score / tau) (1.0) */
+  int32_t accumulate_dv; /* pkm_backward: 1 -> dV[r] += g_r, 0 -> dV[r] = g_r (touched rows only) */
+} pkm_config;
+
+/* State the forward saves for the backward; every buffer is caller-allocated device memory. */
+typedef struct {
+  int32_t* idx;   /* [T, h, k] selected rows, per (t, h) ordered by (score desc, row asc) */
+  float* w;       /* [T, h, k] softmax weights, same order */
+  void* q;        /* [T, h*dq] storage dtype: the query after BatchNorm (and bf16 rounding) */
+  float* q_pre;   /* [T, h*dq] fp32: x W_q^T */
+  float* bn_mean; /* [h*dq] batch mean (BN_BATCH; unused and may be NULL with BN_NONE) */
+  float* bn_rstd; /* [h*dq] 1/sqrt(var + eps) (BN_BATCH; may be NULL with BN_NONE) */
+} pkm_saved;
+
+/* Validate cfg and build a handle (host memory only, no HIP call). */
+pkm_status pkm_create(const pkm_config* cfg, pkm_handle_t* out);
+pkm_status pkm_destroy(pkm_handle_t handle);
+/* The config the handle was created with. */
+pkm_status pkm_get_config(pkm_handle_t handle, pkm_config* out);
+
+/* Device workspace (bytes) that pkm_forward (with_backward = 0) or pkm_backward
+ * (with_backward = 1) needs for T tokens.  The caller allocates it. */
+pkm_status pkm_workspace_size(pkm_handle_t handle, int64_t T, int with_backward, size_t* bytes);
+
+/* Forward m(x) for T >= 1 tokens.  Device pointers:
+ *   x [T, d_in], Wq [h*dq, d_in] (out x in), C [h, |C|, dq/2], Cp [h, |C'|, dq/2],
+ *   V [|C|*|C'|, d_value]: storage dtype.  bn_gamma, bn_beta [h*dq] fp32 (BN_BATCH only).
+ *   y [T, d_value] storage dtype (output).  saved: all its buffers are written.
+ *   ws: workspace of ws_bytes >= pkm_workspace_size(handle, T, 0). */
+pkm_status pkm_forward(pkm_handle_t handle, void* stream, int64_t T, const void* x, const void* Wq,
+                       const float* bn_gamma, const float* bn_beta, const void* C, const void* Cp,
+                       const void* V, void* y, const pkm_saved* saved, void* ws, size_t ws_bytes);
+
+/* Backward of sum(dY * y) given the forward's saved state (same T, same inputs).
+ * Outputs (device):
+ *   dV [|C|*|C'|, d_value] fp32: only touched rows are read/written (accumulate_dv);
+ *   touched [T*h*k] int32: the distinct selected rows, ascending, first *n_touched valid;
+ *   n_touched: one int64 on the device;
+ *   dC [h, |C|, dq/2], dCp [h, |C'|, dq/2], dWq [h*dq, d_in] fp32 (overwritten);
+ *   dgamma, dbeta [h*dq] fp32 (BN_BATCH; may be NULL with BN_NONE);
+ *   dx [T, d_in] storage dtype, may be NULL (not computed).
+ *   ws: workspace of ws_bytes >= pkm_workspace_size(handle, T, 1). */
+pkm_status pkm_backward(pkm_handle_t handle, void* stream, int64_t T, const void* dY, const void* x,
+                        const void* Wq, const float* bn_gamma, const void* C, const void* Cp,
+                        const void* V, const pkm_saved* saved, float* dV, int32_t* touched,
+                        int64_t* n_touched, float* dC, float* dCp, float* dWq, float* dgamma,
+                        float* dbeta, void* dx, void* ws, size_t ws_bytes);
+
+const char* pkm_status_string(pkm_status s);
+/* Message of the last failed call on this thread ("" if none). */
+const char* pkm_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Stage entry points: each launches exactly the kernels the full calls launch
+ * for one step, so every step can be checked on its own inputs.
+ * ------------------------------------------------------------------------- */
+
+/* Steps a1-a2: q_pre = x W_q^T, batch statistics, q = BN(q_pre) rounded to storage.
+ * Writes saved->q_pre, saved->q, saved->bn_mean, saved->bn_rstd (BN_BATCH).
+ * ws >= pkm_workspace_size(handle, T, 0). */
+pkm_status pkm_stage_query(pkm_handle_t handle, void* stream, int64_t T, const void* x, const void* Wq,
+                           const float* bn_gamma, const float* bn_beta, const pkm_saved* saved,
+                           void* ws, size_t ws_bytes);
+
+/* Steps a3-a4: per head and half, scores of q's half against C (C') and the top-k.
+ * q [T, h*dq] storage dtype.  Outputs sub_idx int32 and sub_score fp32, both
+ * [T, h, 2, k]: [..., 0, :] from C, [..., 1, :] from C', each ordered by
+ * (score desc, index asc). */
+pkm_status pkm_stage_score_topk(pkm_handle_t handle, void* stream, int64_t T, const void* q,
+                                const void* C, const void* Cp, int32_t* sub_idx, float* sub_score);
+
+/* Step a5: from sorted per-half lists [T, h, 2, k] (as written by the stage
+ * above), the k best of the k x k candidates and their softmax weights:
+ * idx int32 and w fp32 [T, h, k]; score (may be NULL) fp32 [T, h, k] gets the
+ * selected full-key scores. */
+pkm_status pkm_stage_merge_softmax(pkm_handle_t handle, void* stream, int64_t T,
+                                   const int32_t* sub_idx, const float* sub_score, int32_t* idx,
+                                   float* w, float* score);
+
+/* Step a6: y[t] = sum over (h, s) of w[t,h,s] V[idx[t,h,s]].  idx and w [T, h, k];
+ * every idx must lie in [0, |C|*|C'|) (not checked on the device). */
+pkm_status pkm_stage_gather(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx,
+                            const float* w, const void* V, void* y);
+
+/* Steps a7 (dw) and a8: rows of idx sorted (stable), then per touched row r:
+ * dw[c] = <dY[t(c)], V[r]> for every lookup c with idx[c] == r, and
+ * dV[r] (+)= sum_c w[c] dY[t(c)].  dw [T, h, k] fp32; dV, touched, n_touched as
+ * in pkm_backward.  ws >= pkm_workspace_size(handle, T, 1). */
+pkm_status pkm_stage_value_grad(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx,
+                                const float* w, const void* dY, const void* V, float* dV,
+                                int32_t* touched, int64_t* n_touched, float* dw, void* ws,
+                                size_t ws_bytes);
+
+/* Steps a7 (softmax backward) and a9: ds = w (dw - sum_s w dw) / tau; then
+ * dq[t, h*dq] fp32 (both halves of each head) and dC, dCp (overwritten) through
+ * the selected sub-keys only.  q is the saved query (storage dtype).
+ * ws >= pkm_workspace_size(handle, T, 1). */
+pkm_status pkm_stage_subkey_grad(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx,
+                                 const float* w, const float* dw, const void* q, const void* C,
+                                 const void* Cp, float* dq, float* dC, float* dCp, void* ws,
+                                 size_t ws_bytes);
+
+/* Step a10: BatchNorm backward (batch statistics) and the projection's
+ * gradients: dgamma, dbeta [h*dq], dWq [h*dq, d_in] fp32, dx [T, d_in] storage
+ * dtype (may be NULL).  dq [T, h*dq] fp32; saved->q_pre/bn_mean/bn_rstd as
+ * written by the forward.  ws >= pkm_workspace_size(handle, T, 1). */
+pkm_status pkm_stage_query_grad(pkm_handle_t handle, void* stream, int64_t T, const float* dq,
+                                const void* x, const void* Wq, const float* bn_gamma,
+                                const pkm_saved* saved, float* dWq, float* dgamma, float* dbeta,
+                                void* dx, void* ws, size_t ws_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKM_H_ */

@@ -205,7 +205,11 @@ def lookup(cfg, q: np.ndarray, C: np.ndarray, Cp: np.ndarray, keep_tables: bool 
     sc, rw = candidates(i1[..., :k], v1[..., :k], i2[..., :k], v2[..., :k], cfg.n_keys2)
     rows, scores = select_topk(sc, rw, k)
     w = softmax(scores, cfg.temperature)
-    out = {"rows": rows, "scores": scores, "w": w,
+    # the k+1 best full keys (same exactness argument with k+1 per half), for near-tie checks
+    kk = min(k + 1, k1 * k2)
+    sck, rwk = candidates(i1, v1, i2, v2, cfg.n_keys2)
+    rows_k1, scores_k1 = select_topk(sck, rwk, kk)
+    out = {"rows": rows, "scores": scores, "w": w, "rows_k1": rows_k1, "scores_k1": scores_k1,
            "sub_idx1": i1[..., :k], "sub_val1": v1[..., :k],
            "sub_idx2": i2[..., :k], "sub_val2": v2[..., :k],
            "sub_next1": v1[..., k] if k1 > k else None,

@@ -268,3 +268,25 @@ def random_ints(seed: int, tag: int, shape, lo: int, hi: int, dtype: str = F32) 
     n = int(np.prod(shape))
     a = _fill(seed, 400 + tag, n, "int", lo, hi).reshape(shape)
     return _encode(a, dtype)
+
+
+def random_sublists(seed: int, T: int, heads: int, k: int, nk: int, nk2: int, integer: bool = False):
+    """Per-half candidate lists [T, h, 2, k]: distinct sub-key ids with fp32 scores.
+
+    Each list is arranged by score descending, then id ascending (the order the
+    merge stage expects from the per-half selection).  ``integer`` draws scores
+    from a few small integers so that equal scores are common.
+    """
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(500,))))
+    idx = np.empty((T, heads, 2, k), dtype=np.int32)
+    sc = np.empty((T, heads, 2, k), dtype=np.float32)
+    for p, n in ((0, nk), (1, nk2)):
+        ids = np.argsort(g.random((T * heads, n)), axis=1)[:, :k]
+        if integer:
+            s = g.integers(-2, 3, size=(T * heads, k)).astype(np.float32)
+        else:
+            s = g.standard_normal((T * heads, k)).astype(np.float32)
+        order = np.lexsort((ids, -s), axis=1)
+        idx[:, :, p, :] = np.take_along_axis(ids, order, axis=1).reshape(T, heads, k)
+        sc[:, :, p, :] = np.take_along_axis(s, order, axis=1).reshape(T, heads, k)
+    return idx, sc

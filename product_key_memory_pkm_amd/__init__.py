@@ -1,0 +1,17 @@
+"""Product-key memory (PKM) lookup for AMD Instinct MI355X (gfx950).
+
+The work is done by hand-written HIP kernels in ``libpkm.so`` behind the C ABI
+of ``include/pkm.h``; this package is its thin Python binding (``_lib``) plus a
+convenience layer (``memory``) that allocates the caller-owned buffers with
+torch.  PyTorch provides device memory and streams only.
+"""
+from ._lib import (EXPORTED, PKM_BF16, PKM_BN_BATCH, PKM_BN_NONE, PKM_F32, Handle, PkmError, lib, make_config,
+                   pkm_backward, pkm_config, pkm_create, pkm_forward, pkm_get_config, pkm_saved,
+                   pkm_stage_gather, pkm_stage_merge_softmax, pkm_stage_query, pkm_stage_query_grad,
+                   pkm_stage_score_topk, pkm_stage_subkey_grad, pkm_stage_value_grad, pkm_workspace_size)
+from .memory import ProductKeyMemory
+
+__all__ = ["EXPORTED", "Handle", "PkmError", "ProductKeyMemory", "lib", "make_config", "pkm_backward", "pkm_config",
+           "pkm_create", "pkm_forward", "pkm_get_config", "pkm_saved", "pkm_stage_gather", "pkm_stage_merge_softmax",
+           "pkm_stage_query", "pkm_stage_query_grad", "pkm_stage_score_topk", "pkm_stage_subkey_grad",
+           "pkm_stage_value_grad", "pkm_workspace_size", "PKM_F32", "PKM_BF16", "PKM_BN_NONE", "PKM_BN_BATCH"]

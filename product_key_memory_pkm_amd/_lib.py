@@ -1,0 +1,231 @@
+"""ctypes binding of libpkm.so (the C ABI in include/pkm.h).
+
+Argument marshalling only: every function here checks that torch tensors sit
+on the GPU with the expected dtype and layout, turns them into raw pointers and
+calls the C entry point of the same name on torch's current stream.  All
+arithmetic happens in the library's HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkm.so")
+
+PKM_OK, PKM_ERR_INVALID_ARG, PKM_ERR_UNSUPPORTED, PKM_ERR_WORKSPACE, PKM_ERR_HIP = range(5)
+PKM_F32, PKM_BF16 = 0, 1
+PKM_BN_NONE, PKM_BN_BATCH = 0, 1
+
+_STORAGE = {PKM_F32: torch.float32, PKM_BF16: torch.bfloat16}
+
+
+class PkmError(RuntimeError):
+    def __init__(self, status: int, func: str, msg: str):
+        super().__init__(f"{func}: status {status} ({msg})")
+        self.status = status
+
+
+class pkm_config(ctypes.Structure):
+    _fields_ = [("d_in", ctypes.c_int32), ("heads", ctypes.c_int32), ("d_query", ctypes.c_int32),
+                ("n_keys", ctypes.c_int32), ("n_keys2", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("d_value", ctypes.c_int32), ("dtype", ctypes.c_int32), ("bn", ctypes.c_int32),
+                ("bn_eps", ctypes.c_float), ("temperature", ctypes.c_float), ("accumulate_dv", ctypes.c_int32)]
+
+
+class pkm_saved(ctypes.Structure):
+    _fields_ = [("idx", ctypes.c_void_p), ("w", ctypes.c_void_p), ("q", ctypes.c_void_p),
+                ("q_pre", ctypes.c_void_p), ("bn_mean", ctypes.c_void_p), ("bn_rstd", ctypes.c_void_p)]
+
+
+_lib = None
+
+# name -> argument types (all return pkm_status as int)
+_VP, _I64, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+_SIGS = {
+    "pkm_create": [ctypes.POINTER(pkm_config), ctypes.POINTER(ctypes.c_void_p)],
+    "pkm_destroy": [_VP],
+    "pkm_get_config": [_VP, ctypes.POINTER(pkm_config)],
+    "pkm_workspace_size": [_VP, _I64, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)],
+    "pkm_forward": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_saved), _VP, _SZ],
+    "pkm_backward": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_saved), _VP, _VP, _VP,
+                     _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
+    "pkm_stage_query": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_saved), _VP, _SZ],
+    "pkm_stage_score_topk": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP],
+    "pkm_stage_merge_softmax": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP],
+    "pkm_stage_gather": [_VP, _VP, _I64, _VP, _VP, _VP, _VP],
+    "pkm_stage_value_grad": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
+    "pkm_stage_subkey_grad": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
+    "pkm_stage_query_grad": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_saved), _VP, _VP, _VP, _VP,
+                             _VP, _SZ],
+}
+EXPORTED = sorted(list(_SIGS) + ["pkm_status_string", "pkm_last_error"])
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpkm.so (built in place by ``product_key_memory_pkm_amd.build``); fail loudly if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m product_key_memory_pkm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.pkm_status_string.argtypes = [ctypes.c_int]
+        L.pkm_status_string.restype = ctypes.c_char_p
+        L.pkm_last_error.argtypes = []
+        L.pkm_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int, func: str) -> None:
+    if status != PKM_OK:
+        L = lib()
+        raise PkmError(status, func, L.pkm_last_error().decode() or L.pkm_status_string(status).decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device=None) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _invoke(name: str, h, T: int, *args) -> int:
+    """Call ``name(handle, stream, T, *args)`` on torch's current stream (arguments already marshalled)."""
+    return getattr(lib(), name)(h.ptr, _stream(), T, *args)
+
+
+def _dt(t, want, name):
+    if t is not None and t.dtype != want:
+        raise TypeError(f"{name} must be {want}, got {t.dtype}")
+
+
+class Handle:
+    """An immutable PKM layer handle (host memory only)."""
+
+    def __init__(self, ptr: int, cfg: pkm_config):
+        self.ptr = ctypes.c_void_p(ptr)
+        self.cfg = cfg
+
+    @property
+    def storage(self) -> torch.dtype:
+        return _STORAGE[self.cfg.dtype]
+
+    def __del__(self):
+        if _lib is not None and self.ptr:
+            _lib.pkm_destroy(self.ptr)
+            self.ptr = ctypes.c_void_p(None)
+
+
+def make_config(d_in, heads, d_query, n_keys, n_keys2, topk, d_value, dtype="f32", bn=True, bn_eps=1e-5,
+                temperature=1.0, accumulate_dv=True) -> pkm_config:
+    return pkm_config(d_in, heads, d_query, n_keys, n_keys2, topk, d_value,
+                      PKM_BF16 if dtype in ("bf16", PKM_BF16, torch.bfloat16) else PKM_F32,
+                      PKM_BN_BATCH if bn else PKM_BN_NONE, bn_eps, temperature, 1 if accumulate_dv else 0)
+
+
+def pkm_create(cfg: pkm_config) -> Handle:
+    out = ctypes.c_void_p()
+    _check(lib().pkm_create(ctypes.byref(cfg), ctypes.byref(out)), "pkm_create")
+    return Handle(out.value, cfg)
+
+
+def pkm_get_config(h: Handle) -> pkm_config:
+    c = pkm_config()
+    _check(lib().pkm_get_config(h.ptr, ctypes.byref(c)), "pkm_get_config")
+    return c
+
+
+def pkm_workspace_size(h: Handle, T: int, with_backward: bool) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().pkm_workspace_size(h.ptr, T, int(bool(with_backward)), ctypes.byref(n)), "pkm_workspace_size")
+    return n.value
+
+
+def _saved_struct(saved: dict) -> pkm_saved:
+    return pkm_saved(*[_ptr(saved.get(k)) for k in ("idx", "w", "q", "q_pre", "bn_mean", "bn_rstd")])
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def pkm_forward(h, T, x, Wq, bn_gamma, bn_beta, C, Cp, V, y, saved: dict, ws):
+    st = h.storage
+    for n, t in (("x", x), ("Wq", Wq), ("C", C), ("Cp", Cp), ("V", V), ("y", y)):
+        _dt(t, st, n)
+    sv = _saved_struct(saved)
+    _check(_invoke("pkm_forward", h, T, _ptr(x), _ptr(Wq), _ptr(bn_gamma), _ptr(bn_beta), _ptr(C),
+                             _ptr(Cp), _ptr(V), _ptr(y), ctypes.byref(sv), _ptr(ws), _nbytes(ws)), "pkm_forward")
+
+
+def pkm_backward(h, T, dY, x, Wq, bn_gamma, C, Cp, V, saved: dict, dV, touched, n_touched, dC, dCp, dWq, dgamma,
+                 dbeta, dx, ws):
+    st = h.storage
+    for n, t in (("dY", dY), ("x", x), ("Wq", Wq), ("C", C), ("Cp", Cp), ("V", V), ("dx", dx)):
+        _dt(t, st, n)
+    _dt(dV, torch.float32, "dV")
+    _dt(n_touched, torch.int64, "n_touched")
+    sv = _saved_struct(saved)
+    _check(_invoke("pkm_backward", h, T, _ptr(dY), _ptr(x), _ptr(Wq), _ptr(bn_gamma), _ptr(C), _ptr(Cp),
+                              _ptr(V), ctypes.byref(sv), _ptr(dV), _ptr(touched), _ptr(n_touched), _ptr(dC),
+                              _ptr(dCp), _ptr(dWq), _ptr(dgamma), _ptr(dbeta), _ptr(dx), _ptr(ws), _nbytes(ws)),
+           "pkm_backward")
+
+
+def pkm_stage_query(h, T, x, Wq, bn_gamma, bn_beta, saved: dict, ws):
+    sv = _saved_struct(saved)
+    _check(_invoke("pkm_stage_query", h, T, _ptr(x), _ptr(Wq), _ptr(bn_gamma), _ptr(bn_beta),
+                                 ctypes.byref(sv), _ptr(ws), _nbytes(ws)), "pkm_stage_query")
+
+
+def pkm_stage_score_topk(h, T, q, C, Cp, sub_idx, sub_score):
+    _dt(sub_idx, torch.int32, "sub_idx")
+    _dt(sub_score, torch.float32, "sub_score")
+    _check(_invoke("pkm_stage_score_topk", h, T, _ptr(q), _ptr(C), _ptr(Cp), _ptr(sub_idx),
+                                      _ptr(sub_score)), "pkm_stage_score_topk")
+
+
+def pkm_stage_merge_softmax(h, T, sub_idx, sub_score, idx, w, score=None):
+    _check(_invoke("pkm_stage_merge_softmax", h, T, _ptr(sub_idx), _ptr(sub_score), _ptr(idx), _ptr(w),
+                                         _ptr(score)), "pkm_stage_merge_softmax")
+
+
+def pkm_stage_gather(h, T, idx, w, V, y):
+    _dt(idx, torch.int32, "idx")
+    _dt(w, torch.float32, "w")
+    _check(_invoke("pkm_stage_gather", h, T, _ptr(idx), _ptr(w), _ptr(V), _ptr(y)), "pkm_stage_gather")
+
+
+def pkm_stage_value_grad(h, T, idx, w, dY, V, dV, touched, n_touched, dw, ws):
+    _check(_invoke("pkm_stage_value_grad", h, T, _ptr(idx), _ptr(w), _ptr(dY), _ptr(V), _ptr(dV),
+                                      _ptr(touched), _ptr(n_touched), _ptr(dw), _ptr(ws), _nbytes(ws)),
+           "pkm_stage_value_grad")
+
+
+def pkm_stage_subkey_grad(h, T, idx, w, dw, q, C, Cp, dq, dC, dCp, ws):
+    _check(_invoke("pkm_stage_subkey_grad", h, T, _ptr(idx), _ptr(w), _ptr(dw), _ptr(q), _ptr(C),
+                                       _ptr(Cp), _ptr(dq), _ptr(dC), _ptr(dCp), _ptr(ws), _nbytes(ws)),
+           "pkm_stage_subkey_grad")
+
+
+def pkm_stage_query_grad(h, T, dq, x, Wq, bn_gamma, saved: dict, dWq, dgamma, dbeta, dx, ws):
+    sv = _saved_struct(saved)
+    _check(_invoke("pkm_stage_query_grad", h, T, _ptr(dq), _ptr(x), _ptr(Wq), _ptr(bn_gamma),
+                                      ctypes.byref(sv), _ptr(dWq), _ptr(dgamma), _ptr(dbeta), _ptr(dx), _ptr(ws),
+                                      _nbytes(ws)), "pkm_stage_query_grad")

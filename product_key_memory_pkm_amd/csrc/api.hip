@@ -1,0 +1,608 @@
+// C ABI of the product-key memory lookup: argument checks, workspace layout and
+// the order of kernel launches on the caller's stream.  The steps follow
+// "Meta AI 可扩展内存层" (sections 3.2, 4.3, 4.5, 5.3, 6.1, 9.2, 10.1) and the
+// product-key paper summary (method details, key results); see include/pkm.h.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <new>
+#include <string>
+
+#include "kernels.h"
+#include "pkm.h"
+
+using namespace pkm;
+
+struct pkm_handle_s {
+  pkm_config cfg;
+  int half;   // dq / 2
+  int F;      // heads * dq
+  int elem;   // bytes per storage element
+  int row_bits;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+pkm_status fail(pkm_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+pkm_status hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(PKM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return PKM_OK;
+}
+
+#define PKM_TRY(x)                    \
+  do {                                \
+    pkm_status _st = (x);             \
+    if (_st != PKM_OK) return _st;    \
+  } while (0)
+#define PKM_HIP(call, what) PKM_TRY(hip_check((call), what))
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+pkm_status need(const void* p, const char* name) {
+  if (p == nullptr) return fail(PKM_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(PKM_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return PKM_OK;
+}
+
+size_t al(size_t x) { return (x + 255) & ~size_t(255); }
+
+int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+// Workspace regions.  Forward and backward layouts start at offset 0 and the
+// backward layout never needs the forward's regions, so one buffer of the
+// larger size serves both.
+struct FwdLayout {
+  size_t sub_idx, sub_score, bn_part, total;
+};
+struct BwdLayout {
+  size_t k0, v0, k1, v1, sort_tmp, flags, pos, seg, scan_tmp, nseg, dw, ds, dq, bn_part, dqpre, dqpre_t, x_t, wq_t,
+      split, total;
+  int splits;
+  int64_t tpad;
+};
+
+FwdLayout fwd_layout(const pkm_handle_s* h, int64_t T) {
+  const pkm_config& c = h->cfg;
+  FwdLayout L{};
+  size_t o = 0;
+  const size_t nsub = size_t(T) * c.heads * 2 * c.topk;
+  L.sub_idx = o;  o += al(nsub * 4);
+  L.sub_score = o; o += al(nsub * 4);
+  const size_t nblk = size_t((T + kBnRows - 1) / kBnRows);
+  L.bn_part = o;  o += al(nblk * 2 * h->F * sizeof(double));
+  L.total = o;
+  return L;
+}
+
+int dwq_splits(const pkm_handle_s* h, int64_t tpad) {
+  const int64_t tiles = ((h->F + 127) / 128) * ((h->cfg.d_in + 127) / 128);
+  int64_t s = (2048 + tiles - 1) / tiles;
+  const int64_t maxs = tpad / 256 > 1 ? tpad / 256 : 1;
+  if (s > maxs) s = maxs;
+  if (s > 32) s = 32;
+  if (s < 1) s = 1;
+  return int(s);
+}
+
+BwdLayout bwd_layout(const pkm_handle_s* h, int64_t T) {
+  const pkm_config& c = h->cfg;
+  BwdLayout L{};
+  const size_t N = size_t(T) * c.heads * c.topk;
+  size_t o = 0;
+  L.k0 = o; o += al(N * 4);
+  L.v0 = o; o += al(N * 4);
+  L.k1 = o; o += al(N * 4);
+  L.v1 = o; o += al(N * 4);
+  L.sort_tmp = o; o += al(radix_sort_temp_bytes(int64_t(N)));
+  L.flags = o; o += al(N * 4);
+  L.pos = o; o += al(N * 4);
+  L.seg = o; o += al((N + 1) * 4);
+  L.scan_tmp = o; o += al(256 + scan_temp_bytes(int64_t(N)));
+  L.nseg = o; o += al(4 * sizeof(int64_t));
+  L.dw = o; o += al(N * 4);
+  L.ds = o; o += al(N * 4);
+  L.dq = o; o += al(size_t(T) * h->F * 4);
+  const size_t nblk = size_t((T + kBnRows - 1) / kBnRows);
+  L.bn_part = o; o += al(nblk * 2 * h->F * sizeof(double));
+  L.tpad = round_up(T, 64);
+  L.dqpre = o; o += al(size_t(T) * h->F * h->elem);
+  L.dqpre_t = o; o += al(size_t(h->F) * L.tpad * h->elem);
+  L.x_t = o; o += al(size_t(c.d_in) * L.tpad * h->elem);
+  L.wq_t = o; o += al(size_t(c.d_in) * h->F * h->elem);
+  L.splits = dwq_splits(h, L.tpad);
+  L.split = o; o += al(size_t(L.splits) * h->F * c.d_in * 4);
+  L.total = o;
+  return L;
+}
+
+size_t ws_size(const pkm_handle_s* h, int64_t T, int with_backward) {
+  const size_t f = fwd_layout(h, T).total;
+  if (!with_backward) return f;
+  const size_t b = bwd_layout(h, T).total;
+  return f > b ? f : b;
+}
+
+pkm_status check_handle(pkm_handle_t h) {
+  if (h == nullptr) return fail(PKM_ERR_INVALID_ARG, "handle is NULL");
+  return PKM_OK;
+}
+
+pkm_status check_T(const pkm_handle_s* h, int64_t T) {
+  if (T < 0) return fail(PKM_ERR_INVALID_ARG, "T = %lld is negative", (long long)T);
+  const int64_t N = T * h->cfg.heads * h->cfg.topk;
+  if (N > (int64_t(1) << 26))
+    return fail(PKM_ERR_UNSUPPORTED, "T*heads*topk = %lld exceeds 2^26 lookups per call", (long long)N);
+  return PKM_OK;
+}
+
+pkm_status check_ws(const pkm_handle_s* h, int64_t T, int with_backward, const void* ws, size_t ws_bytes) {
+  const size_t want = ws_size(h, T, with_backward);
+  if (ws == nullptr) return fail(PKM_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", want);
+  if (!aligned16(ws)) return fail(PKM_ERR_WORKSPACE, "workspace is not 16-byte aligned");
+  if (ws_bytes < want) return fail(PKM_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, want);
+  return PKM_OK;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// ---- step groups shared by the full calls and the stage entry points ----
+
+pkm_status run_query(const pkm_handle_s* h, hipStream_t s, int64_t T, const void* x, const void* Wq,
+                     const float* gamma, const float* beta, const pkm_saved* sv, void* ws) {
+  const pkm_config& c = h->cfg;
+  const FwdLayout L = fwd_layout(h, T);
+  PKM_HIP(launch_gemm_nt(s, c.dtype, T, h->F, c.d_in, x, c.d_in, Wq, c.d_in, sv->q_pre, h->F, false, 1, 0),
+          "projection GEMM");
+  if (c.bn == PKM_BN_BATCH) {
+    double* part = at<double>(ws, L.bn_part);
+    const int nblk = int((T + kBnRows - 1) / kBnRows);
+    PKM_HIP(launch_bn_partials(s, sv->q_pre, T, h->F, part), "BatchNorm partial sums");
+    PKM_HIP(launch_bn_finalize(s, part, nblk, T, h->F, c.bn_eps, sv->bn_mean, sv->bn_rstd), "BatchNorm finalize");
+    PKM_HIP(launch_bn_apply(s, c.dtype, sv->q_pre, T, h->F, sv->bn_mean, sv->bn_rstd, gamma, beta, sv->q),
+            "BatchNorm apply");
+  } else {
+    PKM_HIP(launch_bn_apply(s, c.dtype, sv->q_pre, T, h->F, nullptr, nullptr, nullptr, nullptr, sv->q),
+            "query cast");
+  }
+  return PKM_OK;
+}
+
+pkm_status run_score(const pkm_handle_s* h, hipStream_t s, int64_t T, const void* q, const void* C, const void* Cp,
+                     int32_t* sub_idx, float* sub_score) {
+  const pkm_config& c = h->cfg;
+  PKM_HIP(launch_score_topk(s, c.dtype, q, T, c.heads, c.d_query, C, Cp, c.n_keys, c.n_keys2, c.topk, sub_idx,
+                            sub_score),
+          "sub-key scoring / top-k");
+  return PKM_OK;
+}
+
+pkm_status run_merge(const pkm_handle_s* h, hipStream_t s, int64_t T, const int32_t* sub_idx, const float* sub_score,
+                     int32_t* idx, float* w, float* score) {
+  const pkm_config& c = h->cfg;
+  PKM_HIP(launch_merge_softmax(s, sub_idx, sub_score, T * c.heads, c.topk, c.n_keys2, 1.0f / c.temperature, idx, w,
+                               score),
+          "candidate merge / softmax");
+  return PKM_OK;
+}
+
+pkm_status run_gather(const pkm_handle_s* h, hipStream_t s, int64_t T, const int32_t* idx, const float* w,
+                      const void* V, void* y) {
+  const pkm_config& c = h->cfg;
+  PKM_HIP(launch_gather(s, c.dtype, idx, w, V, y, T, c.heads * c.topk, c.d_value), "value gather-sum");
+  return PKM_OK;
+}
+
+pkm_status run_value_grad(const pkm_handle_s* h, hipStream_t s, int64_t T, const int32_t* idx, const float* w,
+                          const void* dY, const void* V, float* dV, int32_t* touched, int64_t* n_touched, float* dw,
+                          void* ws) {
+  const pkm_config& c = h->cfg;
+  const BwdLayout L = bwd_layout(h, T);
+  const int64_t N = T * c.heads * c.topk;
+  bool in1 = false;
+  PKM_HIP(launch_radix_sort_from(s, reinterpret_cast<const uint32_t*>(idx), at<uint32_t>(ws, L.k0),
+                                 at<int32_t>(ws, L.v0), at<uint32_t>(ws, L.k1), at<int32_t>(ws, L.v1), N, h->row_bits,
+                                 at<void>(ws, L.sort_tmp), &in1),
+          "row sort");
+  const uint32_t* sk = at<uint32_t>(ws, in1 ? L.k1 : L.k0);
+  const int32_t* sv = at<int32_t>(ws, in1 ? L.v1 : L.v0);
+  int32_t* seg = at<int32_t>(ws, L.seg);
+  PKM_HIP(launch_segments(s, sk, N, at<uint32_t>(ws, L.flags), at<uint32_t>(ws, L.pos), seg, touched, n_touched,
+                          at<void>(ws, L.scan_tmp)),
+          "row segments");
+  PKM_HIP(launch_value_grad(s, c.dtype, seg, n_touched, N, sk, sv, w, dY, V, dV, dw, c.heads * c.topk, c.d_value,
+                            c.accumulate_dv != 0),
+          "value gradient");
+  return PKM_OK;
+}
+
+pkm_status run_subkey_grad(const pkm_handle_s* h, hipStream_t s, int64_t T, const int32_t* idx, const float* w,
+                           const float* dw, const void* q, const void* C, const void* Cp, float* dq, float* dC,
+                           float* dCp, void* ws) {
+  const pkm_config& c = h->cfg;
+  const BwdLayout L = bwd_layout(h, T);
+  const int64_t N = T * c.heads * c.topk;
+  float* ds = at<float>(ws, L.ds);
+  PKM_HIP(launch_softmax_bwd_dq(s, c.dtype, idx, w, dw, C, Cp, T, c.heads, c.d_query, c.topk, c.n_keys, c.n_keys2,
+                                1.0f / c.temperature, ds, dq),
+          "softmax backward / query gradient");
+  for (int half_sel = 0; half_sel < 2; ++half_sel) {
+    const int nkeys = half_sel ? c.n_keys2 : c.n_keys;
+    float* out = half_sel ? dCp : dC;
+    uint32_t* keys = at<uint32_t>(ws, L.flags);  // scratch: the key array is read only by the first pass
+    PKM_HIP(launch_subkey_keys(s, idx, N, c.heads, c.topk, c.n_keys, c.n_keys2, half_sel, keys), "sub-key ids");
+    int bits = 1;
+    while ((int64_t(1) << bits) < int64_t(c.heads) * nkeys) ++bits;
+    bool in1 = false;
+    PKM_HIP(launch_radix_sort_from(s, keys, at<uint32_t>(ws, L.k0), at<int32_t>(ws, L.v0), at<uint32_t>(ws, L.k1),
+                                   at<int32_t>(ws, L.v1), N, bits, at<void>(ws, L.sort_tmp), &in1),
+            "sub-key sort");
+    const uint32_t* sk = at<uint32_t>(ws, in1 ? L.k1 : L.k0);
+    const int32_t* sv = at<int32_t>(ws, in1 ? L.v1 : L.v0);
+    int32_t* seg = at<int32_t>(ws, L.seg);
+    int64_t* nseg = at<int64_t>(ws, L.nseg) + 1 + half_sel;
+    PKM_HIP(launch_fill_f32(s, out, int64_t(c.heads) * nkeys * h->half, 0.f), "sub-key gradient clear");
+    PKM_HIP(launch_segments(s, sk, N, at<uint32_t>(ws, L.flags), at<uint32_t>(ws, L.pos), seg, nullptr, nseg,
+                            at<void>(ws, L.scan_tmp)),
+            "sub-key segments");
+    PKM_HIP(launch_subkey_grad(s, c.dtype, seg, nseg, N, sk, sv, ds, q, c.heads, c.d_query, c.topk, half_sel, nkeys,
+                               out),
+            "sub-key gradient");
+  }
+  return PKM_OK;
+}
+
+pkm_status run_query_grad(const pkm_handle_s* h, hipStream_t s, int64_t T, const float* dq, const void* x,
+                          const void* Wq, const float* gamma, const pkm_saved* sv, float* dWq, float* dgamma,
+                          float* dbeta, void* dx, void* ws) {
+  const pkm_config& c = h->cfg;
+  const BwdLayout L = bwd_layout(h, T);
+  const bool bn = c.bn == PKM_BN_BATCH;
+  if (bn) {
+    double* part = at<double>(ws, L.bn_part);
+    const int nblk = int((T + kBnRows - 1) / kBnRows);
+    PKM_HIP(launch_bn_bwd_partials(s, dq, sv->q_pre, sv->bn_mean, sv->bn_rstd, T, h->F, part),
+            "BatchNorm backward partial sums");
+    PKM_HIP(launch_bn_bwd_finalize(s, part, nblk, h->F, gamma, dgamma, dbeta, nullptr), "BatchNorm backward finalize");
+  }
+  void* dqpre = at<void>(ws, L.dqpre);
+  void* dqpre_t = at<void>(ws, L.dqpre_t);
+  PKM_HIP(launch_bn_bwd_apply(s, c.dtype, dq, sv->q_pre, sv->bn_mean, sv->bn_rstd, gamma, dgamma, dbeta, T, h->F, bn,
+                              dqpre, dqpre_t, L.tpad),
+          "BatchNorm backward apply");
+  // dWq[F, d] = dq_pre^T x : A = dq_pre^T [F, Tpad], B = x^T [d, Tpad]
+  void* xt = at<void>(ws, L.x_t);
+  PKM_HIP(launch_transpose(s, x, T, c.d_in, c.d_in, xt, L.tpad, L.tpad, h->elem, h->elem), "x transpose");
+  float* split = at<float>(ws, L.split);
+  const int64_t sstride = int64_t(h->F) * c.d_in;
+  if (L.splits == 1) {
+    PKM_HIP(launch_gemm_nt(s, c.dtype, h->F, c.d_in, L.tpad, dqpre_t, L.tpad, xt, L.tpad, dWq, c.d_in, false, 1, 0),
+            "dWq GEMM");
+  } else {
+    PKM_HIP(launch_gemm_nt(s, c.dtype, h->F, c.d_in, L.tpad, dqpre_t, L.tpad, xt, L.tpad, split, c.d_in, false,
+                           L.splits, sstride),
+            "dWq GEMM");
+    PKM_HIP(launch_sum_splits(s, split, L.splits, sstride, h->F, c.d_in, c.d_in, dWq, c.d_in, false), "dWq reduce");
+  }
+  if (dx) {
+    // dx[T, d] = dq_pre Wq : A = dq_pre [T, F], B = Wq^T [d, F]
+    void* wqt = at<void>(ws, L.wq_t);
+    PKM_HIP(launch_transpose(s, Wq, h->F, c.d_in, c.d_in, wqt, h->F, h->F, h->elem, h->elem), "Wq transpose");
+    PKM_HIP(launch_gemm_nt(s, c.dtype, T, c.d_in, h->F, dqpre, h->F, wqt, h->F, dx, c.d_in, c.dtype == PKM_BF16, 1, 0),
+            "dx GEMM");
+  }
+  return PKM_OK;
+}
+
+pkm_status check_saved(const pkm_handle_s* h, const pkm_saved* sv, bool need_sel) {
+  if (sv == nullptr) return fail(PKM_ERR_INVALID_ARG, "saved is NULL");
+  if (need_sel) {
+    PKM_TRY(need(sv->idx, "saved->idx"));
+    PKM_TRY(need(sv->w, "saved->w"));
+  }
+  PKM_TRY(need(sv->q, "saved->q"));
+  PKM_TRY(need(sv->q_pre, "saved->q_pre"));
+  if (h->cfg.bn == PKM_BN_BATCH) {
+    PKM_TRY(need(sv->bn_mean, "saved->bn_mean"));
+    PKM_TRY(need(sv->bn_rstd, "saved->bn_rstd"));
+  }
+  return PKM_OK;
+}
+
+pkm_status zero_grads(const pkm_handle_s* h, hipStream_t s, int64_t* n_touched, float* dC, float* dCp, float* dWq,
+                      float* dgamma, float* dbeta) {
+  const pkm_config& c = h->cfg;
+  if (n_touched) PKM_HIP(hipMemsetAsync(n_touched, 0, sizeof(int64_t), s), "clear n_touched");
+  if (dC) PKM_HIP(launch_fill_f32(s, dC, int64_t(c.heads) * c.n_keys * h->half, 0.f), "clear dC");
+  if (dCp) PKM_HIP(launch_fill_f32(s, dCp, int64_t(c.heads) * c.n_keys2 * h->half, 0.f), "clear dCp");
+  if (dWq) PKM_HIP(launch_fill_f32(s, dWq, int64_t(h->F) * c.d_in, 0.f), "clear dWq");
+  if (dgamma) PKM_HIP(launch_fill_f32(s, dgamma, h->F, 0.f), "clear dgamma");
+  if (dbeta) PKM_HIP(launch_fill_f32(s, dbeta, h->F, 0.f), "clear dbeta");
+  return PKM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkm_status_string(pkm_status s) {
+  switch (s) {
+    case PKM_OK: return "ok";
+    case PKM_ERR_INVALID_ARG: return "invalid argument";
+    case PKM_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PKM_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKM_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* pkm_last_error(void) { return g_err.c_str(); }
+
+pkm_status pkm_create(const pkm_config* cfg, pkm_handle_t* out) {
+  if (cfg == nullptr || out == nullptr) return fail(PKM_ERR_INVALID_ARG, "cfg or out is NULL");
+  *out = nullptr;
+  const pkm_config& c = *cfg;
+  if (c.dtype != PKM_F32 && c.dtype != PKM_BF16) return fail(PKM_ERR_INVALID_ARG, "dtype %d unknown", c.dtype);
+  if (c.bn != PKM_BN_NONE && c.bn != PKM_BN_BATCH) return fail(PKM_ERR_INVALID_ARG, "bn mode %d unknown", c.bn);
+  const int vec = c.dtype == PKM_BF16 ? 8 : 4;  // elements per 16 bytes
+  if (c.d_in < 1) return fail(PKM_ERR_INVALID_ARG, "d_in = %d < 1", c.d_in);
+  if (c.heads < 1) return fail(PKM_ERR_INVALID_ARG, "heads = %d < 1", c.heads);
+  if (c.d_query < 2 || c.d_query % 2) return fail(PKM_ERR_INVALID_ARG, "d_query = %d must be even and >= 2", c.d_query);
+  if (c.n_keys < 1 || c.n_keys2 < 1) return fail(PKM_ERR_INVALID_ARG, "n_keys and n_keys2 must be >= 1");
+  if (c.topk < 1) return fail(PKM_ERR_INVALID_ARG, "topk = %d < 1", c.topk);
+  if (c.topk > c.n_keys || c.topk > c.n_keys2)
+    return fail(PKM_ERR_INVALID_ARG, "topk = %d exceeds a codebook size (%d, %d)", c.topk, c.n_keys, c.n_keys2);
+  if (c.d_value < 1) return fail(PKM_ERR_INVALID_ARG, "d_value = %d < 1", c.d_value);
+  if (!(c.temperature > 0.0f)) return fail(PKM_ERR_INVALID_ARG, "temperature must be > 0");
+  if (c.bn == PKM_BN_BATCH && !(c.bn_eps >= 0.0f)) return fail(PKM_ERR_INVALID_ARG, "bn_eps must be >= 0");
+  if (int64_t(c.n_keys) * c.n_keys2 >= (int64_t(1) << 31))
+    return fail(PKM_ERR_INVALID_ARG, "n_keys * n_keys2 = %lld does not fit int32 row ids",
+                (long long)(int64_t(c.n_keys) * c.n_keys2));
+  // limits of the kernels
+  if (c.topk > 32) return fail(PKM_ERR_UNSUPPORTED, "topk = %d > 32", c.topk);
+  if (c.n_keys > 2048 || c.n_keys2 > 2048) return fail(PKM_ERR_UNSUPPORTED, "codebooks larger than 2048 sub-keys");
+  if (c.d_in % vec) return fail(PKM_ERR_UNSUPPORTED, "d_in must be a multiple of %d for this dtype", vec);
+  if ((c.d_query / 2) % vec)
+    return fail(PKM_ERR_UNSUPPORTED, "d_query/2 must be a multiple of %d for this dtype", vec);
+  if (c.d_value % vec) return fail(PKM_ERR_UNSUPPORTED, "d_value must be a multiple of %d for this dtype", vec);
+  if (c.d_value / vec > 256)
+    return fail(PKM_ERR_UNSUPPORTED, "d_value rows above 4096 bytes are not supported");
+  const int maxk = c.n_keys > c.n_keys2 ? c.n_keys : c.n_keys2;
+  if (!score_topk_supported(c.dtype, c.d_query / 2, maxk))
+    return fail(PKM_ERR_UNSUPPORTED, "d_query/2 = %d with %d sub-keys does not fit the scoring tile", c.d_query / 2,
+                maxk);
+  pkm_handle_s* h = new (std::nothrow) pkm_handle_s;
+  if (!h) return fail(PKM_ERR_INVALID_ARG, "out of host memory");
+  h->cfg = c;
+  h->half = c.d_query / 2;
+  h->F = c.heads * c.d_query;
+  h->elem = c.dtype == PKM_BF16 ? 2 : 4;
+  int bits = 0;
+  while ((int64_t(1) << bits) < int64_t(c.n_keys) * c.n_keys2) ++bits;
+  h->row_bits = bits;
+  *out = h;
+  return PKM_OK;
+}
+
+pkm_status pkm_destroy(pkm_handle_t handle) {
+  delete handle;
+  return PKM_OK;
+}
+
+pkm_status pkm_get_config(pkm_handle_t handle, pkm_config* out) {
+  PKM_TRY(check_handle(handle));
+  if (!out) return fail(PKM_ERR_INVALID_ARG, "out is NULL");
+  *out = handle->cfg;
+  return PKM_OK;
+}
+
+pkm_status pkm_workspace_size(pkm_handle_t handle, int64_t T, int with_backward, size_t* bytes) {
+  PKM_TRY(check_handle(handle));
+  if (!bytes) return fail(PKM_ERR_INVALID_ARG, "bytes is NULL");
+  PKM_TRY(check_T(handle, T));
+  *bytes = ws_size(handle, T, with_backward);
+  return PKM_OK;
+}
+
+pkm_status pkm_forward(pkm_handle_t handle, void* stream, int64_t T, const void* x, const void* Wq,
+                       const float* bn_gamma, const float* bn_beta, const void* C, const void* Cp, const void* V,
+                       void* y, const pkm_saved* saved, void* ws, size_t ws_bytes) {
+  PKM_TRY(check_handle(handle));
+  PKM_TRY(check_T(handle, T));
+  PKM_TRY(need(x, "x"));
+  PKM_TRY(need(Wq, "Wq"));
+  PKM_TRY(need(C, "C"));
+  PKM_TRY(need(Cp, "Cp"));
+  PKM_TRY(need(V, "V"));
+  PKM_TRY(need(y, "y"));
+  if (handle->cfg.bn == PKM_BN_BATCH) {
+    PKM_TRY(need(bn_gamma, "bn_gamma"));
+    PKM_TRY(need(bn_beta, "bn_beta"));
+  }
+  PKM_TRY(check_saved(handle, saved, true));
+  PKM_TRY(check_ws(handle, T, 0, ws, ws_bytes));
+  if (T == 0) return PKM_OK;
+  hipStream_t s = as_stream(stream);
+  const FwdLayout L = fwd_layout(handle, T);
+  int32_t* sub_idx = at<int32_t>(ws, L.sub_idx);
+  float* sub_score = at<float>(ws, L.sub_score);
+  PKM_TRY(run_query(handle, s, T, x, Wq, bn_gamma, bn_beta, saved, ws));
+  PKM_TRY(run_score(handle, s, T, saved->q, C, Cp, sub_idx, sub_score));
+  PKM_TRY(run_merge(handle, s, T, sub_idx, sub_score, saved->idx, saved->w, nullptr));
+  PKM_TRY(run_gather(handle, s, T, saved->idx, saved->w, V, y));
+  return PKM_OK;
+}
+
+pkm_status pkm_backward(pkm_handle_t handle, void* stream, int64_t T, const void* dY, const void* x, const void* Wq,
+                        const float* bn_gamma, const void* C, const void* Cp, const void* V, const pkm_saved* saved,
+                        float* dV, int32_t* touched, int64_t* n_touched, float* dC, float* dCp, float* dWq,
+                        float* dgamma, float* dbeta, void* dx, void* ws, size_t ws_bytes) {
+  PKM_TRY(check_handle(handle));
+  PKM_TRY(check_T(handle, T));
+  const bool bn = handle->cfg.bn == PKM_BN_BATCH;
+  PKM_TRY(need(dY, "dY"));
+  PKM_TRY(need(x, "x"));
+  PKM_TRY(need(Wq, "Wq"));
+  PKM_TRY(need(C, "C"));
+  PKM_TRY(need(Cp, "Cp"));
+  PKM_TRY(need(V, "V"));
+  PKM_TRY(check_saved(handle, saved, true));
+  PKM_TRY(need(dV, "dV"));
+  PKM_TRY(need(touched, "touched"));
+  if (n_touched == nullptr) return fail(PKM_ERR_INVALID_ARG, "n_touched is NULL");
+  PKM_TRY(need(dC, "dC"));
+  PKM_TRY(need(dCp, "dCp"));
+  PKM_TRY(need(dWq, "dWq"));
+  if (bn) {
+    PKM_TRY(need(bn_gamma, "bn_gamma"));
+    PKM_TRY(need(dgamma, "dgamma"));
+    PKM_TRY(need(dbeta, "dbeta"));
+  }
+  if (dx) PKM_TRY(need(dx, "dx"));
+  PKM_TRY(check_ws(handle, T, 1, ws, ws_bytes));
+  hipStream_t s = as_stream(stream);
+  if (T == 0) return zero_grads(handle, s, n_touched, dC, dCp, dWq, bn ? dgamma : nullptr, bn ? dbeta : nullptr);
+  const BwdLayout L = bwd_layout(handle, T);
+  float* dw = at<float>(ws, L.dw);
+  float* dq = at<float>(ws, L.dq);
+  PKM_TRY(run_value_grad(handle, s, T, saved->idx, saved->w, dY, V, dV, touched, n_touched, dw, ws));
+  PKM_TRY(run_subkey_grad(handle, s, T, saved->idx, saved->w, dw, saved->q, C, Cp, dq, dC, dCp, ws));
+  PKM_TRY(run_query_grad(handle, s, T, dq, x, Wq, bn_gamma, saved, dWq, bn ? dgamma : nullptr, bn ? dbeta : nullptr,
+                         dx, ws));
+  return PKM_OK;
+}
+
+pkm_status pkm_stage_query(pkm_handle_t handle, void* stream, int64_t T, const void* x, const void* Wq,
+                           const float* bn_gamma, const float* bn_beta, const pkm_saved* saved, void* ws,
+                           size_t ws_bytes) {
+  PKM_TRY(check_handle(handle));
+  PKM_TRY(check_T(handle, T));
+  PKM_TRY(need(x, "x"));
+  PKM_TRY(need(Wq, "Wq"));
+  if (handle->cfg.bn == PKM_BN_BATCH) {
+    PKM_TRY(need(bn_gamma, "bn_gamma"));
+    PKM_TRY(need(bn_beta, "bn_beta"));
+  }
+  PKM_TRY(check_saved(handle, saved, false));
+  PKM_TRY(check_ws(handle, T, 0, ws, ws_bytes));
+  if (T == 0) return PKM_OK;
+  return run_query(handle, as_stream(stream), T, x, Wq, bn_gamma, bn_beta, saved, ws);
+}
+
+pkm_status pkm_stage_score_topk(pkm_handle_t handle, void* stream, int64_t T, const void* q, const void* C,
+                                const void* Cp, int32_t* sub_idx, float* sub_score) {
+  PKM_TRY(check_handle(handle));
+  PKM_TRY(check_T(handle, T));
+  PKM_TRY(need(q, "q"));
+  PKM_TRY(need(C, "C"));
+  PKM_TRY(need(Cp, "Cp"));
+  PKM_TRY(need(sub_idx, "sub_idx"));
+  PKM_TRY(need(sub_score, "sub_score"));
+  if (T == 0) return PKM_OK;
+  return run_score(handle, as_stream(stream), T, q, C, Cp, sub_idx, sub_score);
+}
+
+pkm_status pkm_stage_merge_softmax(pkm_handle_t handle, void* stream, int64_t T, const int32_t* sub_idx,
+                                   const float* sub_score, int32_t* idx, float* w, float* score) {
+  PKM_TRY(check_handle(handle));
+  PKM_TRY(check_T(handle, T));
+  PKM_TRY(need(sub_idx, "sub_idx"));
+  PKM_TRY(need(sub_score, "sub_score"));
+  PKM_TRY(need(idx, "idx"));
+  PKM_TRY(need(w, "w"));
+  if (score) PKM_TRY(need(score, "score"));
+  if (T == 0) return PKM_OK;
+  return run_merge(handle, as_stream(stream), T, sub_idx, sub_score, idx, w, score);
+}
+
+pkm_status pkm_stage_gather(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx, const float* w,
+                            const void* V, void* y) {
+  PKM_TRY(check_handle(handle));
+  PKM_TRY(check_T(handle, T));
+  PKM_TRY(need(idx, "idx"));
+  PKM_TRY(need(w, "w"));
+  PKM_TRY(need(V, "V"));
+  PKM_TRY(need(y, "y"));
+  if (T == 0) return PKM_OK;
+  return run_gather(handle, as_stream(stream), T, idx, w, V, y);
+}
+
+pkm_status pkm_stage_value_grad(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx, const float* w,
+                                const void* dY, const void* V, float* dV, int32_t* touched, int64_t* n_touched,
+                                float* dw, void* ws, size_t ws_bytes) {
+  PKM_TRY(check_handle(handle));
+  PKM_TRY(check_T(handle, T));
+  PKM_TRY(need(idx, "idx"));
+  PKM_TRY(need(w, "w"));
+  PKM_TRY(need(dY, "dY"));
+  PKM_TRY(need(V, "V"));
+  PKM_TRY(need(dV, "dV"));
+  PKM_TRY(need(touched, "touched"));
+  if (n_touched == nullptr) return fail(PKM_ERR_INVALID_ARG, "n_touched is NULL");
+  PKM_TRY(need(dw, "dw"));
+  PKM_TRY(check_ws(handle, T, 1, ws, ws_bytes));
+  hipStream_t s = as_stream(stream);
+  if (T == 0) return zero_grads(handle, s, n_touched, nullptr, nullptr, nullptr, nullptr, nullptr);
+  return run_value_grad(handle, s, T, idx, w, dY, V, dV, touched, n_touched, dw, ws);
+}
+
+pkm_status pkm_stage_subkey_grad(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx, const float* w,
+                                 const float* dw, const void* q, const void* C, const void* Cp, float* dq, float* dC,
+                                 float* dCp, void* ws, size_t ws_bytes) {
+  PKM_TRY(check_handle(handle));
+  PKM_TRY(check_T(handle, T));
+  PKM_TRY(need(idx, "idx"));
+  PKM_TRY(need(w, "w"));
+  PKM_TRY(need(dw, "dw"));
+  PKM_TRY(need(q, "q"));
+  PKM_TRY(need(C, "C"));
+  PKM_TRY(need(Cp, "Cp"));
+  PKM_TRY(need(dq, "dq"));
+  PKM_TRY(need(dC, "dC"));
+  PKM_TRY(need(dCp, "dCp"));
+  PKM_TRY(check_ws(handle, T, 1, ws, ws_bytes));
+  hipStream_t s = as_stream(stream);
+  if (T == 0) return zero_grads(handle, s, nullptr, dC, dCp, nullptr, nullptr, nullptr);
+  return run_subkey_grad(handle, s, T, idx, w, dw, q, C, Cp, dq, dC, dCp, ws);
+}
+
+pkm_status pkm_stage_query_grad(pkm_handle_t handle, void* stream, int64_t T, const float* dq, const void* x,
+                                const void* Wq, const float* bn_gamma, const pkm_saved* saved, float* dWq,
+                                float* dgamma, float* dbeta, void* dx, void* ws, size_t ws_bytes) {
+  PKM_TRY(check_handle(handle));
+  PKM_TRY(check_T(handle, T));
+  const bool bn = handle->cfg.bn == PKM_BN_BATCH;
+  PKM_TRY(need(dq, "dq"));
+  PKM_TRY(need(x, "x"));
+  PKM_TRY(need(Wq, "Wq"));
+  PKM_TRY(check_saved(handle, saved, false));
+  PKM_TRY(need(dWq, "dWq"));
+  if (bn) {
+    PKM_TRY(need(bn_gamma, "bn_gamma"));
+    PKM_TRY(need(dgamma, "dgamma"));
+    PKM_TRY(need(dbeta, "dbeta"));
+  }
+  if (dx) PKM_TRY(need(dx, "dx"));
+  PKM_TRY(check_ws(handle, T, 1, ws, ws_bytes));
+  hipStream_t s = as_stream(stream);
+  if (T == 0) return zero_grads(handle, s, nullptr, nullptr, nullptr, dWq, bn ? dgamma : nullptr, bn ? dbeta : nullptr);
+  return run_query_grad(handle, s, T, dq, x, Wq, bn_gamma, saved, dWq, bn ? dgamma : nullptr, bn ? dbeta : nullptr,
+                        dx, ws);
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Host-side launchers of the PKM kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkm {
+
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+
+// a6: y[t] = sum_r w[t, r] V[idx[t, r]] over R = h*k rows per token.
+hipError_t launch_gather(hipStream_t s, int dtype, const int32_t* idx, const float* w, const void* V,
+                         void* y, int64_t ntok, int R, int d_value);
+
+// a3 + a4: per (token, head, half) scores against the half's sub-keys and top-k.
+// Returns hipErrorInvalidValue when the shape does not fit the kernel's LDS plan.
+bool score_topk_supported(int dtype, int half, int nkeys);
+hipError_t launch_score_topk(hipStream_t s, int dtype, const void* q, int64_t ntok, int heads, int dq,
+                             const void* C, const void* Cp, int nk, int nk2, int k, int32_t* sub_idx,
+                             float* sub_score);
+
+// a5: k x k candidates -> top-k -> softmax, per (token, head).
+hipError_t launch_merge_softmax(hipStream_t s, const int32_t* sub_idx, const float* sub_score,
+                                int64_t nitems, int k, int nk2, float inv_tau, int32_t* idx, float* w,
+                                float* score);
+
+// C[M, N] = A[M, K] * B[N, K]^T; A, B storage dtype, C fp32 (or bf16 when out_bf16).
+// splits > 1: blockIdx.z handles a slice of K and writes C + z * split_stride.
+hipError_t launch_gemm_nt(hipStream_t s, int dtype, int64_t M, int64_t N, int64_t K, const void* A,
+                          int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, bool out_bf16,
+                          int splits, int64_t split_stride);
+// out[i] = sum_z part[z * stride + i] for i < n (fixed order), optional bf16 output.
+hipError_t launch_sum_splits(hipStream_t s, const float* part, int splits, int64_t stride, int64_t rows,
+                             int64_t cols, int64_t ld_part, void* out, int64_t ld_out, bool out_bf16);
+// out[c, r] = in[r, c] for r < rows, c < cols; zero for r in [rows, rows_pad).
+// Element size 2 or 4 bytes; in_f32_to_bf16 converts fp32 input to bf16 output.
+hipError_t launch_transpose(hipStream_t s, const void* in, int64_t rows, int64_t cols, int64_t ld_in,
+                            void* out, int64_t ld_out, int64_t rows_pad, int in_elem, int out_elem);
+
+// a2: BatchNorm.
+// Per-block partial sums (fp64) of q_pre columns over row blocks of kBnRows.
+constexpr int kBnRows = 256;
+hipError_t launch_bn_partials(hipStream_t s, const float* q_pre, int64_t ntok, int F, double* part);
+hipError_t launch_bn_finalize(hipStream_t s, const double* part, int nblk, int64_t ntok, int F, float eps,
+                              float* mean, float* rstd);
+hipError_t launch_bn_apply(hipStream_t s, int dtype, const float* q_pre, int64_t ntok, int F,
+                           const float* mean, const float* rstd, const float* gamma, const float* beta,
+                           void* q);
+// a10: partial sums of dq and dq * xhat per column block.
+hipError_t launch_bn_bwd_partials(hipStream_t s, const float* dq, const float* q_pre, const float* mean,
+                                  const float* rstd, int64_t ntok, int F, double* part);
+hipError_t launch_bn_bwd_finalize(hipStream_t s, const double* part, int nblk, int F, const float* gamma,
+                                  float* dgamma, float* dbeta, float* coef);
+// dq_pre = gamma*rstd*(dq - dbeta/T - xhat*dgamma/T); written row-major (out_rm) and
+// transposed (out_tr, [F, ld_tr]), each as fp32 or bf16 per dtype.
+hipError_t launch_bn_bwd_apply(hipStream_t s, int dtype, const float* dq, const float* q_pre,
+                               const float* mean, const float* rstd, const float* gamma,
+                               const float* dgamma, const float* dbeta, int64_t ntok, int F, bool bn,
+                               void* out_rm, void* out_tr, int64_t ld_tr);
+
+// Stable radix sort by key of n keys (< 2^key_bits) paired with their indices 0..n-1.
+// keys_in is read only; the passes ping-pong between (k0, v0) and (k1, v1) and
+// *result_in_1 tells which pair holds the sorted result.
+size_t radix_sort_temp_bytes(int64_t n);
+hipError_t launch_radix_sort_from(hipStream_t s, const uint32_t* keys_in, uint32_t* k0, int32_t* v0,
+                                  uint32_t* k1, int32_t* v1, int64_t n, int key_bits, void* temp,
+                                  bool* result_in_1);
+// Exclusive scan of n uint32 values (n <= 2^31); temp of scan_temp_bytes(n).
+size_t scan_temp_bytes(int64_t n);
+hipError_t launch_exclusive_scan(hipStream_t s, const uint32_t* in, uint32_t* out, int64_t n, void* temp,
+                                 uint32_t* total /*device, may be null*/);
+
+// Segments of a sorted key array: seg_start[u] for every distinct key run, and
+// count (device int64).  Also touched[u] = key of run u (may be null).
+hipError_t launch_segments(hipStream_t s, const uint32_t* sorted_keys, int64_t n, uint32_t* flags,
+                           uint32_t* pos, int32_t* seg_start, int32_t* touched, int64_t* count,
+                           void* scan_temp);
+
+// a7 + a8: per touched row, dw for every lookup of it and the row's dV.
+hipError_t launch_value_grad(hipStream_t s, int dtype, const int32_t* seg_start, const int64_t* nseg,
+                             int64_t nitems, const uint32_t* sorted_rows, const int32_t* sorted_c,
+                             const float* w, const void* dY, const void* V, float* dV, float* dw,
+                             int R, int d_value, bool accumulate);
+
+// a7: ds = w (dw - sum w dw) / tau ; a9: dq from the selected sub-keys.
+hipError_t launch_softmax_bwd_dq(hipStream_t s, int dtype, const int32_t* idx, const float* w,
+                                 const float* dw, const void* C, const void* Cp, int64_t ntok, int heads,
+                                 int dq, int k, int nk, int nk2, float inv_tau, float* ds, float* dq_out);
+// keys for the sub-key sort: key = h*nk + (row / nk2) (half 0) or h*nk2 + row % nk2 (half 1).
+hipError_t launch_subkey_keys(hipStream_t s, const int32_t* idx, int64_t n, int heads, int k, int nk, int nk2,
+                              int half_sel, uint32_t* keys);
+// dC[seg key] = sum over its contributions of ds[c] * q_half[t(c), h]; untouched rows zeroed.
+hipError_t launch_subkey_grad(hipStream_t s, int dtype, const int32_t* seg_start, const int64_t* nseg,
+                              int64_t nitems, const uint32_t* sorted_keys, const int32_t* sorted_c,
+                              const float* ds, const void* q, int heads, int dq, int k, int half_sel,
+                              int nkeys, float* dC);
+
+hipError_t launch_fill_f32(hipStream_t s, float* p, int64_t n, float v);
+
+}  // namespace pkm

@@ -1,0 +1,330 @@
+// Steps a3 + a4: sub-key scores of each query half and the per-half top-k.
+//
+//   s1[t,h,i] = q1[t,h] . C[h,i],   s2[t,h,j] = q2[t,h] . C'[h,j]
+//   I1 = the k largest s1 (score desc, index asc on ties), likewise I2.
+//
+// ("Meta AI 可扩展内存层", sections 4.3-4.4: each half is scored against its own
+// codebook as a matrix product and only its top-k survive; product-key paper
+// summary, method details: q split into q1, q2, top-k search in each half.)
+//
+// One workgroup = 8 waves = (TM tokens, one head, one half).
+//  1. The TM x dq/2 query tile is staged in LDS.
+//  2. MFMA (bf16 16x16x32 or fp32 16x16x4, fp32 accumulation): each wave owns
+//     16-column tiles of the TM x |C| score tile and streams its sub-key rows
+//     from global memory (the codebooks are small and stay in L2); the scores
+//     land in LDS and never reach HBM.
+//  3. Selection, one wave per token row: every lane takes |C|/64 scores as
+//     order-preserving 32-bit keys; the k-th largest of the 64 lane maxima
+//     (bisection with ballots) is a lower bound of the row's k-th largest
+//     score, so every key below it is dropped; the <= 64 survivors are
+//     compacted and bitonic-sorted as (key, ~index) 64-bit words, which orders
+//     them by score and then lowest index.  Rows where more than 64 keys pass
+//     the bound (heavy ties) take an exact bisection over all keys instead.
+#include "common.h"
+#include "kernels.h"
+
+namespace pkm {
+
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr size_t kLdsLimit = 160 * 1024;
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+}
+
+template <typename T>
+struct ScoreTraits;
+template <>
+struct ScoreTraits<bf16_t> {
+  static constexpr int VE = 8;   // elements per 16-byte lane vector
+  static constexpr int KC = 32;  // k covered by one 16-byte vector per lane (4 lane groups)
+  __device__ __forceinline__ static f32x4 mma(const u32x4& a, const u32x4& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+template <>
+struct ScoreTraits<float> {
+  static constexpr int VE = 4;
+  static constexpr int KC = 16;
+  __device__ __forceinline__ static f32x4 mma(const u32x4& a, const u32x4& b, f32x4 c) {
+    // Lane group g holds k = 4g..4g+3 of this 16-wide slice for both operands;
+    // MFMA step e consumes element e, so the 4 steps cover all 16 k.
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+    return c;
+  }
+};
+
+struct Plan {
+  int TM;
+  int half_pad;
+  int qstride;  // elements
+  int ncols_pad;
+  int sstride;  // floats
+  int npl;
+  size_t lds;
+};
+
+inline int round_up(int a, int b) { return (a + b - 1) / b * b; }
+
+Plan make_plan(int dtype, int half, int ncols) {
+  Plan p{};
+  const int VE = dtype == kBF16 ? 8 : 4;
+  const int KC = dtype == kBF16 ? 32 : 16;
+  const int e = dtype == kBF16 ? 2 : 4;
+  p.half_pad = round_up(half, KC);
+  p.qstride = p.half_pad + VE;
+  p.ncols_pad = round_up(ncols, 64);
+  p.sstride = p.ncols_pad + 4;
+  int npl = 1;
+  while (npl * 64 < ncols) npl *= 2;
+  p.npl = npl;
+  p.TM = 0;
+  for (int tm = 64; tm >= 16; tm /= 2) {
+    size_t lds = size_t(tm) * p.qstride * e + size_t(tm) * p.sstride * 4 + kWaves * 64 * 8;
+    if (lds <= kLdsLimit) {
+      p.TM = tm;
+      p.lds = lds;
+      break;
+    }
+  }
+  return p;
+}
+
+template <typename T, int TM, int NPL>
+__global__ __launch_bounds__(kThreads) void score_topk_kernel(
+    const T* __restrict__ q, int64_t ntok, int F, int dq, int half, int half_pad, int qstride,
+    const T* __restrict__ C, const T* __restrict__ Cp, int nk, int nk2, int k, int sstride,
+    int32_t* __restrict__ sub_idx, float* __restrict__ sub_score) {
+  using TR = ScoreTraits<T>;
+  constexpr int VE = TR::VE;
+  constexpr int KC = TR::KC;
+  constexpr int RT = TM / 16;
+  constexpr int CT = 256 / TM;  // column tiles per pass: RT*CT*4 = 64 accumulator registers
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  T* qt = reinterpret_cast<T*>(smem);
+  float* S = reinterpret_cast<float*>(smem + size_t(TM) * qstride * sizeof(T));
+  uint64_t* scratch = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(S) + size_t(TM) * sstride * 4);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int hh = blockIdx.y;
+  const int p = blockIdx.z;
+  const int heads = gridDim.y;
+  const int ncols = p ? nk2 : nk;
+  const T* keys = (p ? Cp : C) + size_t(hh) * ncols * half;
+  const int64_t t0 = int64_t(blockIdx.x) * TM;
+
+  // 1. query tile -> LDS (zero rows past the last token and k past dq/2)
+  {
+    const int vpr = half_pad / VE;
+    const T* qsrc = q + size_t(hh) * dq + size_t(p) * half;
+    for (int e = tid; e < TM * vpr; e += kThreads) {
+      const int r = e / vpr;
+      const int kk = (e - r * vpr) * VE;
+      u32x4 v = {0, 0, 0, 0};
+      if (t0 + r < ntok && kk < half) v = ld16(qsrc + size_t(t0 + r) * F + kk);
+      st16(qt + size_t(r) * qstride + kk, v);
+    }
+  }
+  __syncthreads();
+
+  // 2. scores -> LDS
+  const int nct = (ncols + 15) / 16;
+  const int lrow = lane & 15;
+  const int lgrp = lane >> 4;
+  for (int g0 = wave * CT; g0 < nct; g0 += kWaves * CT) {
+    f32x4 acc[RT][CT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int c = 0; c < CT; ++c) acc[rt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const T* kb[CT];
+    bool colok[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      const int col = (g0 + c) * 16 + lrow;
+      colok[c] = col < ncols;
+      kb[c] = keys + size_t(colok[c] ? col : 0) * half;
+    }
+    u32x4 bcur[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      const int kk = lgrp * VE;
+      bcur[c] = (colok[c] && kk < half) ? ld16(kb[c] + kk) : u32x4{0, 0, 0, 0};
+    }
+    for (int kc = 0; kc < half_pad; kc += KC) {
+      u32x4 bnext[CT];
+      const int kn = kc + KC + lgrp * VE;
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+        bnext[c] = (kc + KC < half_pad && colok[c] && kn < half) ? ld16(kb[c] + kn) : u32x4{0, 0, 0, 0};
+      u32x4 a[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) a[rt] = ld16(qt + size_t(rt * 16 + lrow) * qstride + kc + lgrp * VE);
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[rt][c] = TR::mma(a[rt], bcur[c], acc[rt][c]);
+#pragma unroll
+      for (int c = 0; c < CT; ++c) bcur[c] = bnext[c];
+    }
+    // D layout of a 16x16 MFMA tile: lane l holds column l%16, rows 4*(l/16)+i.
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        if (g0 + c < nct) {
+          const int col = (g0 + c) * 16 + lrow;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[size_t(rt * 16 + lgrp * 4 + i) * sstride + col] = acc[rt][c][i];
+        }
+      }
+  }
+  __syncthreads();
+
+  // 3. per-row top-k, one wave per row
+  uint64_t* scr = scratch + wave * 64;
+  for (int r = wave; r < TM; r += kWaves) {
+    const int64_t t = t0 + r;
+    if (t >= ntok) break;  // wave-uniform
+    const float* srow = S + size_t(r) * sstride;
+    uint32_t key[NPL];
+    uint32_t lmax = 0;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int col = j * 64 + lane;
+      key[j] = col < ncols ? float_key(srow[col]) : 0u;
+      lmax = key[j] > lmax ? key[j] : lmax;
+    }
+    // k lanes hold real keys (k <= ncols), so the bound below is attained.
+    const uint32_t thr = wave_kth_largest_u32(lmax, k);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) cnt += key[j] >= thr;
+    int total;
+    int pos = wave_excl_scan(cnt, &total);
+    if (total <= 64) {
+#pragma unroll
+      for (int j = 0; j < NPL; ++j)
+        if (key[j] >= thr) scr[pos++] = (uint64_t(key[j]) << 32) | uint32_t(~uint32_t(j * 64 + lane));
+    } else {
+      // Exact k-th largest key over all columns.
+      uint32_t res = 0;
+      for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = res | (1u << b);
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) c += key[j] >= cand;
+        if (wave_sum_i(c) >= k) res = cand;
+      }
+      int gt = 0;
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) gt += key[j] > res;
+      int gt_total;
+      int gpos = wave_excl_scan(gt, &gt_total);
+#pragma unroll
+      for (int j = 0; j < NPL; ++j)
+        if (key[j] > res) scr[gpos++] = (uint64_t(key[j]) << 32) | uint32_t(~uint32_t(j * 64 + lane));
+      // ties at the k-th key: lowest columns first (column = j*64 + lane)
+      int remaining = k - gt_total;
+      int base = gt_total;
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) {
+        const bool eq = key[j] == res;
+        const uint64_t m = ballot(eq);
+        const int rk = lanes_below(m);
+        if (eq && rk < remaining) scr[base + rk] = (uint64_t(key[j]) << 32) | uint32_t(~uint32_t(j * 64 + lane));
+        const int taken = min(popc64(m), remaining);
+        base += taken;
+        remaining -= taken;
+      }
+      total = k;
+    }
+    wave_lds_sync();
+    uint64_t v = lane < total ? scr[lane] : 0ull;
+    wave_lds_sync();
+    v = wave_sort_desc_u64(v);
+    if (lane < k) {
+      const size_t o = ((size_t(t) * heads + hh) * 2 + p) * k + lane;
+      sub_idx[o] = int32_t(~uint32_t(v));
+      sub_score[o] = key_float(uint32_t(v >> 32));
+    }
+  }
+}
+
+template <typename T, int TM>
+void launch_tm(hipStream_t s, const Plan& pl, const void* q, int64_t ntok, int heads, int dq, const void* C,
+               const void* Cp, int nk, int nk2, int k, int32_t* sub_idx, float* sub_score) {
+  const int half = dq / 2;
+  const int F = heads * dq;
+  dim3 grid(unsigned((ntok + TM - 1) / TM), unsigned(heads), 2u);
+#define PKM_SCORE_CASE(NPLV)                                                                          \
+  case NPLV: {                                                                                        \
+    auto fn = score_topk_kernel<T, TM, NPLV>;                                                         \
+    hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, \
+                        int(pl.lds));                                                                 \
+    hipLaunchKernelGGL(fn, grid, dim3(kThreads), pl.lds, s, static_cast<const T*>(q), ntok, F, dq, half, \
+                       pl.half_pad, pl.qstride, static_cast<const T*>(C), static_cast<const T*>(Cp), nk, \
+                       nk2, k, pl.sstride, sub_idx, sub_score);                                      \
+  } break;
+  switch (pl.npl) {
+    PKM_SCORE_CASE(1)
+    PKM_SCORE_CASE(2)
+    PKM_SCORE_CASE(4)
+    PKM_SCORE_CASE(8)
+    PKM_SCORE_CASE(16)
+    PKM_SCORE_CASE(32)
+    default:
+      break;
+  }
+#undef PKM_SCORE_CASE
+}
+
+template <typename T>
+void launch_t(hipStream_t s, const Plan& pl, const void* q, int64_t ntok, int heads, int dq, const void* C,
+              const void* Cp, int nk, int nk2, int k, int32_t* sub_idx, float* sub_score) {
+  if (pl.TM == 64)
+    launch_tm<T, 64>(s, pl, q, ntok, heads, dq, C, Cp, nk, nk2, k, sub_idx, sub_score);
+  else if (pl.TM == 32)
+    launch_tm<T, 32>(s, pl, q, ntok, heads, dq, C, Cp, nk, nk2, k, sub_idx, sub_score);
+  else
+    launch_tm<T, 16>(s, pl, q, ntok, heads, dq, C, Cp, nk, nk2, k, sub_idx, sub_score);
+}
+
+}  // namespace
+
+bool score_topk_supported(int dtype, int half, int nkeys) {
+  if (nkeys < 1 || nkeys > 2048) return false;
+  Plan p = make_plan(dtype, half, nkeys);
+  return p.TM != 0;
+}
+
+hipError_t launch_score_topk(hipStream_t s, int dtype, const void* q, int64_t ntok, int heads, int dq,
+                             const void* C, const void* Cp, int nk, int nk2, int k, int32_t* sub_idx,
+                             float* sub_score) {
+  const Plan pl = make_plan(dtype, dq / 2, nk > nk2 ? nk : nk2);
+  if (pl.TM == 0 || pl.npl > 32) return hipErrorInvalidValue;
+  if (dtype == kBF16)
+    launch_t<bf16_t>(s, pl, q, ntok, heads, dq, C, Cp, nk, nk2, k, sub_idx, sub_score);
+  else
+    launch_t<float>(s, pl, q, ntok, heads, dq, C, Cp, nk, nk2, k, sub_idx, sub_score);
+  return hipGetLastError();
+}
+
+}  // namespace pkm

@@ -1,0 +1,274 @@
+// Deterministic grouping for the sparse backward: a stable LSD radix sort of
+// (key, lookup id) pairs, an exclusive scan, and the segment table of the
+// sorted keys.  Only the selected rows / sub-keys receive gradient
+// ("Meta AI 可扩展内存层", sections 6.1 and 9.2: sparse gradients at the
+// selected positions; product-key paper summary: only a few memory slots are
+// updated per step); grouping by a stable sort makes every per-row sum run in
+// lookup order, so the backward is bit-identical from run to run without
+// floating-point atomics.
+//
+// Radix pass (8-bit digit): per 4096-key tile a digit histogram, one exclusive
+// scan over the digit-major (digit, tile) table, then a scatter in which each
+// key's rank among equal digits of its tile is found round by round (256 keys
+// per round, in index order): within a wave by matching the 8 digit bits with
+// ballots, across the 4 waves through LDS counters.
+#include "common.h"
+#include "kernels.h"
+
+namespace pkm {
+
+namespace {
+
+constexpr int kTile = 4096;     // keys per tile (256 threads x 16)
+constexpr int kScanBlock = 4096;
+
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+}
+
+// Exclusive scan over the 256 threads of a block; returns the block total in *tot.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh /*[4]*/, uint32_t* tot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    uint32_t y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  uint32_t pre = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (w < wave) pre += sh[w];
+    all += sh[w];
+  }
+  __syncthreads();
+  *tot = all;
+  return pre + x - v;
+}
+
+__global__ __launch_bounds__(256) void scan_reduce_kernel(const uint32_t* __restrict__ in, int64_t n,
+                                                          uint32_t* __restrict__ part) {
+  __shared__ uint32_t sh[4];
+  const int64_t base = int64_t(blockIdx.x) * kScanBlock + threadIdx.x * 16;
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (base + i < n) s += in[base + i];
+  uint32_t tot;
+  block_excl_scan(s, sh, &tot);
+  if (threadIdx.x == 0) part[blockIdx.x] = tot;
+}
+
+// Single block: exclusive scan of nb block totals (nb <= 256 * 64).
+__global__ __launch_bounds__(256) void scan_top_kernel(uint32_t* __restrict__ part, int nb,
+                                                       uint32_t* __restrict__ total) {
+  __shared__ uint32_t sh[4];
+  const int per = (nb + 255) / 256;
+  const int b0 = threadIdx.x * per;
+  uint32_t s = 0;
+  for (int i = 0; i < per; ++i)
+    if (b0 + i < nb) s += part[b0 + i];
+  uint32_t tot;
+  uint32_t run = block_excl_scan(s, sh, &tot);
+  for (int i = 0; i < per; ++i)
+    if (b0 + i < nb) {
+      uint32_t v = part[b0 + i];
+      part[b0 + i] = run;
+      run += v;
+    }
+  if (threadIdx.x == 0 && total) *total = tot;
+}
+
+__global__ __launch_bounds__(256) void scan_apply_kernel(const uint32_t* __restrict__ in, int64_t n,
+                                                         const uint32_t* __restrict__ part,
+                                                         uint32_t* __restrict__ out) {
+  __shared__ uint32_t sh[4];
+  const int64_t base = int64_t(blockIdx.x) * kScanBlock + threadIdx.x * 16;
+  uint32_t v[16];
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[i] = base + i < n ? in[base + i] : 0u;
+    s += v[i];
+  }
+  uint32_t tot;
+  uint32_t run = block_excl_scan(s, sh, &tot) + part[blockIdx.x];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (base + i < n) {
+      out[base + i] = run;
+      run += v[i];
+    }
+}
+
+__global__ __launch_bounds__(256) void radix_hist_kernel(const uint32_t* __restrict__ keys, int64_t n, int shift,
+                                                         int nb, uint32_t* __restrict__ hist) {
+  __shared__ uint32_t cnt[256];
+  cnt[threadIdx.x] = 0;
+  __syncthreads();
+  const int64_t base = int64_t(blockIdx.x) * kTile;
+#pragma unroll 4
+  for (int i = 0; i < kTile / 256; ++i) {
+    const int64_t e = base + i * 256 + threadIdx.x;
+    if (e < n) atomicAdd(&cnt[(keys[e] >> shift) & 0xFF], 1u);
+  }
+  __syncthreads();
+  hist[int64_t(threadIdx.x) * nb + blockIdx.x] = cnt[threadIdx.x];
+}
+
+// Stable scatter of one tile.  vals_in == nullptr: the value is the key's index.
+__global__ __launch_bounds__(256) void radix_scatter_kernel(const uint32_t* __restrict__ keys_in,
+                                                            const int32_t* __restrict__ vals_in, int64_t n,
+                                                            int shift, int nb, const uint32_t* __restrict__ offs,
+                                                            uint32_t* __restrict__ keys_out,
+                                                            int32_t* __restrict__ vals_out) {
+  __shared__ uint32_t run[256];
+  __shared__ uint32_t wcnt[4][256];
+  __shared__ uint32_t goff[256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  run[tid] = 0;
+  goff[tid] = offs[int64_t(tid) * nb + blockIdx.x];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) wcnt[w][tid] = 0;
+  __syncthreads();
+  const int64_t base = int64_t(blockIdx.x) * kTile;
+  for (int i = 0; i < kTile / 256; ++i) {
+    const int64_t e = base + i * 256 + tid;
+    const bool ok = e < n;
+    const uint32_t key = ok ? keys_in[e] : 0u;
+    const int32_t val = ok ? (vals_in ? vals_in[e] : int32_t(e)) : 0;
+    const uint32_t d = (key >> shift) & 0xFF;
+    uint64_t peers = ballot(ok);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool bit = (d >> b) & 1u;
+      const uint64_t m = ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const int rk = lanes_below(peers);
+    if (ok && rk == 0) wcnt[wave][d] = uint32_t(popc64(peers));
+    __syncthreads();
+    if (ok) {
+      uint32_t pre = run[d];
+      for (int w = 0; w < wave; ++w) pre += wcnt[w][d];
+      const uint32_t pos = goff[d] + pre + uint32_t(rk);
+      keys_out[pos] = key;
+      vals_out[pos] = val;
+    }
+    __syncthreads();
+    run[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) wcnt[w][tid] = 0;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void seg_flags_kernel(const uint32_t* __restrict__ k, int64_t n,
+                                                        uint32_t* __restrict__ flags) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256)
+    flags[i] = (i == 0 || k[i] != k[i - 1]) ? 1u : 0u;
+}
+
+__global__ __launch_bounds__(256) void seg_write_kernel(const uint32_t* __restrict__ k, int64_t n,
+                                                        const uint32_t* __restrict__ flags,
+                                                        const uint32_t* __restrict__ pos,
+                                                        const uint32_t* __restrict__ total,
+                                                        int32_t* __restrict__ seg_start, int32_t* __restrict__ touched,
+                                                        int64_t* __restrict__ count) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
+    if (flags[i]) {
+      seg_start[pos[i]] = int32_t(i);
+      if (touched) touched[pos[i]] = int32_t(k[i]);
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    seg_start[*total] = int32_t(n);
+    *count = int64_t(*total);
+  }
+}
+
+inline unsigned grid1d(int64_t n, int64_t cap = 16384) {
+  int64_t b = (n + 255) / 256;
+  if (b > cap) b = cap;
+  if (b < 1) b = 1;
+  return unsigned(b);
+}
+
+}  // namespace
+
+size_t scan_temp_bytes(int64_t n) {
+  const int64_t nb = (n + kScanBlock - 1) / kScanBlock;
+  return size_t((nb + 64) * 4);
+}
+
+hipError_t launch_exclusive_scan(hipStream_t s, const uint32_t* in, uint32_t* out, int64_t n, void* temp,
+                                 uint32_t* total) {
+  const int64_t nb = (n + kScanBlock - 1) / kScanBlock;
+  if (nb > 256 * 64) return hipErrorInvalidValue;
+  uint32_t* part = static_cast<uint32_t*>(temp);
+  if (nb > 0) {
+    hipLaunchKernelGGL(scan_reduce_kernel, dim3(unsigned(nb)), dim3(256), 0, s, in, n, part);
+  }
+  hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(256), 0, s, part, int(nb), total);
+  if (nb > 0) {
+    hipLaunchKernelGGL(scan_apply_kernel, dim3(unsigned(nb)), dim3(256), 0, s, in, n, part, out);
+  }
+  return hipGetLastError();
+}
+
+size_t radix_sort_temp_bytes(int64_t n) {
+  const int64_t nb = (n + kTile - 1) / kTile;
+  const int64_t h = 256 * nb;
+  return size_t(h * 4 * 2) + scan_temp_bytes(h) + 256;
+}
+
+hipError_t launch_radix_sort_from(hipStream_t s, const uint32_t* keys_in, uint32_t* k0, int32_t* v0, uint32_t* k1,
+                                  int32_t* v1, int64_t n, int key_bits, void* temp, bool* result_in_1) {
+  const int64_t nb = (n + kTile - 1) / kTile;
+  uint32_t* hist = static_cast<uint32_t*>(temp);
+  uint32_t* offs = hist + 256 * nb;
+  void* stemp = offs + 256 * nb;
+  int passes = (key_bits + 7) / 8;
+  if (passes < 1) passes = 1;
+  const uint32_t* kin = keys_in;
+  const int32_t* vin = nullptr;
+  uint32_t* kout = k0;
+  int32_t* vout = v0;
+  for (int p = 0; p < passes; ++p) {
+    const int shift = 8 * p;
+    if (nb > 0) {
+      hipLaunchKernelGGL(radix_hist_kernel, dim3(unsigned(nb)), dim3(256), 0, s, kin, n, shift, int(nb), hist);
+      hipError_t e = launch_exclusive_scan(s, hist, offs, 256 * nb, stemp, nullptr);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(radix_scatter_kernel, dim3(unsigned(nb)), dim3(256), 0, s, kin, vin, n, shift, int(nb),
+                         offs, kout, vout);
+    }
+    kin = kout;
+    vin = vout;
+    if (kout == k0) {
+      kout = k1;
+      vout = v1;
+    } else {
+      kout = k0;
+      vout = v0;
+    }
+  }
+  *result_in_1 = (kin == k1);
+  return hipGetLastError();
+}
+
+hipError_t launch_segments(hipStream_t s, const uint32_t* sorted_keys, int64_t n, uint32_t* flags, uint32_t* pos,
+                           int32_t* seg_start, int32_t* touched, int64_t* count, void* scan_temp) {
+  hipLaunchKernelGGL(seg_flags_kernel, dim3(grid1d(n)), dim3(256), 0, s, sorted_keys, n, flags);
+  uint32_t* total = static_cast<uint32_t*>(scan_temp);
+  void* stemp = total + 64;
+  hipError_t e = launch_exclusive_scan(s, flags, pos, n, stemp, total);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(seg_write_kernel, dim3(grid1d(n)), dim3(256), 0, s, sorted_keys, n, flags, pos, total,
+                     seg_start, touched, count);
+  return hipGetLastError();
+}
+
+}  // namespace pkm

@@ -1,0 +1,78 @@
+"""Convenience wrapper: allocates the caller-owned buffers of the C ABI with torch.
+
+Nothing here computes: ``forward`` / ``backward`` allocate outputs, saved state
+and workspace, then call ``pkm_forward`` / ``pkm_backward``.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as L
+
+
+class ProductKeyMemory:
+    """Product-key memory layer shape + handle.
+
+    Parameters follow the C ABI (``pkm_config``): input width ``d_in``, ``heads``,
+    per-head query width ``d_query``, codebook sizes ``n_keys`` / ``n_keys2``,
+    ``topk``, value width ``d_value``, storage dtype ``"f32"`` or ``"bf16"``.
+    """
+
+    def __init__(self, d_in, heads, d_query, n_keys, n_keys2, topk, d_value, dtype="bf16", bn=True, bn_eps=1e-5,
+                 temperature=1.0, accumulate_dv=True, device="cuda"):
+        self.cfg = L.make_config(d_in, heads, d_query, n_keys, n_keys2, topk, d_value, dtype, bn, bn_eps,
+                                 temperature, accumulate_dv)
+        self.handle = L.pkm_create(self.cfg)
+        self.device = torch.device(device)
+        self._ws = None
+
+    @property
+    def storage(self) -> torch.dtype:
+        return self.handle.storage
+
+    def workspace(self, T: int, with_backward: bool) -> torch.Tensor:
+        n = L.pkm_workspace_size(self.handle, T, with_backward)
+        if self._ws is None or self._ws.numel() < n:
+            self._ws = torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def alloc_saved(self, T: int) -> dict:
+        c = self.cfg
+        F = c.heads * c.d_query
+        dev = self.device
+        sv = {"idx": torch.empty((T, c.heads, c.topk), dtype=torch.int32, device=dev),
+              "w": torch.empty((T, c.heads, c.topk), dtype=torch.float32, device=dev),
+              "q": torch.empty((T, F), dtype=self.storage, device=dev),
+              "q_pre": torch.empty((T, F), dtype=torch.float32, device=dev)}
+        if c.bn:
+            sv["bn_mean"] = torch.empty(F, dtype=torch.float32, device=dev)
+            sv["bn_rstd"] = torch.empty(F, dtype=torch.float32, device=dev)
+        return sv
+
+    def forward(self, x, Wq, gamma, beta, C, Cp, V, saved=None, y=None):
+        T = x.shape[0]
+        saved = saved if saved is not None else self.alloc_saved(T)
+        y = y if y is not None else torch.empty((T, self.cfg.d_value), dtype=self.storage, device=self.device)
+        ws = self.workspace(T, False)
+        L.pkm_forward(self.handle, T, x, Wq, gamma, beta, C, Cp, V, y, saved, ws)
+        return y, saved
+
+    def backward(self, dY, x, Wq, gamma, C, Cp, V, saved, dV, want_dx=True, out=None):
+        c = self.cfg
+        T = x.shape[0]
+        F = c.heads * c.d_query
+        dev = self.device
+        g = out if out is not None else {
+            "touched": torch.empty(max(1, T * c.heads * c.topk), dtype=torch.int32, device=dev),
+            "n_touched": torch.zeros(1, dtype=torch.int64, device=dev),
+            "dC": torch.empty((c.heads, c.n_keys, c.d_query // 2), dtype=torch.float32, device=dev),
+            "dCp": torch.empty((c.heads, c.n_keys2, c.d_query // 2), dtype=torch.float32, device=dev),
+            "dWq": torch.empty((F, c.d_in), dtype=torch.float32, device=dev),
+            "dgamma": torch.empty(F, dtype=torch.float32, device=dev) if c.bn else None,
+            "dbeta": torch.empty(F, dtype=torch.float32, device=dev) if c.bn else None,
+            "dx": torch.empty((T, c.d_in), dtype=self.storage, device=dev) if want_dx else None,
+        }
+        ws = self.workspace(T, True)
+        L.pkm_backward(self.handle, T, dY, x, Wq, gamma, C, Cp, V, saved, dV, g["touched"], g["n_touched"], g["dC"],
+                       g["dCp"], g["dWq"], g["dgamma"], g["dbeta"], g["dx"], ws)
+        return g

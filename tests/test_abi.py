@@ -1,0 +1,170 @@
+"""The C ABI on the CPU: the library loads, exports what include/pkm.h declares,
+and rejects bad arguments before any HIP call.
+
+No test here reaches a kernel launch: every call below fails validation, so the
+file is safe with or without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkm.h")
+
+
+def _lib():
+    from product_key_memory_pkm_amd import _lib as L
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("libpkm.so not built")
+    return L
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkm_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("pkm_create", "pkm_destroy", "pkm_workspace_size", "pkm_forward", "pkm_backward",
+              "pkm_stage_score_topk", "pkm_stage_merge_softmax", "pkm_stage_gather", "pkm_stage_value_grad"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    lib = L.lib()
+    for n in _declared():
+        assert hasattr(lib, n), n
+    assert sorted(_declared()) == sorted(L.EXPORTED)
+
+
+def _cfg(L, **kw):
+    base = dict(d_in=64, heads=2, d_query=32, n_keys=32, n_keys2=32, topk=8, d_value=64, dtype="f32", bn=True)
+    base.update(kw)
+    return L.make_config(**base)
+
+
+BAD_CONFIGS = [
+    (dict(d_in=0), 1), (dict(heads=0), 1), (dict(d_query=7), 1), (dict(n_keys=0), 1), (dict(topk=0), 1),
+    (dict(topk=40, n_keys=64, n_keys2=64), 2),      # above the 32 the kernels implement
+    (dict(topk=16, n_keys=8), 1),                   # k larger than a codebook
+    (dict(d_value=0), 1), (dict(temperature=0.0), 1), (dict(temperature=-1.0), 1),
+    (dict(n_keys=4096, n_keys2=8), 2),              # codebook above 2048
+    (dict(d_in=6), 2), (dict(d_query=6), 2), (dict(d_value=6), 2),   # fp32 needs multiples of 4
+    (dict(dtype="bf16", d_in=12), 2), (dict(dtype="bf16", d_query=24), 2),
+    (dict(d_value=8192), 2),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_CONFIGS)
+def test_create_rejects(kw, status):
+    L = _lib()
+    with pytest.raises(L.PkmError) as e:
+        L.pkm_create(_cfg(L, **kw))
+    assert e.value.status == status
+
+
+def test_create_row_id_overflow_and_limits():
+    L = _lib()
+    c = _cfg(L)
+    h = L.pkm_create(c)
+    got = L.pkm_get_config(h)
+    assert (got.d_in, got.heads, got.topk) == (64, 2, 8)
+    # unknown enums
+    for field, val in (("dtype", 7), ("bn", 5)):
+        c2 = _cfg(L)
+        setattr(c2, field, val)
+        with pytest.raises(L.PkmError):
+            L.pkm_create(c2)
+
+
+def test_workspace_sizes_grow_with_tokens():
+    L = _lib()
+    h = L.pkm_create(_cfg(L))
+    a = L.pkm_workspace_size(h, 100, False)
+    b = L.pkm_workspace_size(h, 1000, False)
+    c = L.pkm_workspace_size(h, 1000, True)
+    assert 0 < a < b <= c
+    assert L.pkm_workspace_size(h, 0, True) >= 0
+    with pytest.raises(L.PkmError):
+        L.pkm_workspace_size(h, -1, False)
+    with pytest.raises(L.PkmError) as e:
+        L.pkm_workspace_size(h, 1 << 30, False)
+    assert e.value.status == L.PKM_ERR_UNSUPPORTED
+
+
+# Raw calls with fake, 16-byte aligned addresses: validation must fail before they are used.
+FAKE = 0x100000
+
+
+def _fake(n=0):
+    return ctypes.c_void_p(FAKE + 256 * n)
+
+
+def _fwd(L, h, T=10, **over):
+    args = dict(x=_fake(1), Wq=_fake(2), g=_fake(3), b=_fake(4), C=_fake(5), Cp=_fake(6), V=_fake(7), y=_fake(8))
+    args.update(over)
+    sv = over.get("saved", L.pkm_saved(_fake(9), _fake(10), _fake(11), _fake(12), _fake(13), _fake(14)))
+    ws = over.get("ws", _fake(15))
+    ws_bytes = over.get("ws_bytes", 16)
+    return L.lib().pkm_forward(h.ptr, None, T, args["x"], args["Wq"], args["g"], args["b"], args["C"], args["Cp"],
+                               args["V"], args["y"], ctypes.byref(sv), ws, ws_bytes)
+
+
+def test_forward_argument_errors():
+    L = _lib()
+    h = L.pkm_create(_cfg(L))
+    assert _fwd(L, h, x=None) == L.PKM_ERR_INVALID_ARG
+    assert "x is NULL" in L.lib().pkm_last_error().decode()
+    assert _fwd(L, h, V=ctypes.c_void_p(FAKE + 8)) == L.PKM_ERR_INVALID_ARG     # misaligned
+    assert "aligned" in L.lib().pkm_last_error().decode()
+    assert _fwd(L, h, g=None) == L.PKM_ERR_INVALID_ARG                           # BN needs gamma
+    assert _fwd(L, h, T=-5) == L.PKM_ERR_INVALID_ARG
+    assert _fwd(L, h, ws=None) == L.PKM_ERR_WORKSPACE
+    assert _fwd(L, h, ws_bytes=16) == L.PKM_ERR_WORKSPACE                       # too small
+    assert "needed" in L.lib().pkm_last_error().decode()
+    bad_saved = L.pkm_saved(_fake(9), None, _fake(11), _fake(12), _fake(13), _fake(14))
+    assert _fwd(L, h, saved=bad_saved) == L.PKM_ERR_INVALID_ARG
+    assert L.lib().pkm_forward(None, None, 1, *([None] * 8), None, None, 0) == L.PKM_ERR_INVALID_ARG
+
+
+def test_backward_and_stage_argument_errors():
+    L = _lib()
+    lib = L.lib()
+    h = L.pkm_create(_cfg(L))
+    sv = L.pkm_saved(_fake(9), _fake(10), _fake(11), _fake(12), _fake(13), _fake(14))
+    ok = [_fake(i) for i in range(30)]
+    # backward: NULL n_touched, then a too-small workspace
+    st = lib.pkm_backward(h.ptr, None, 10, ok[1], ok[2], ok[3], ok[4], ok[5], ok[6], ok[7], ctypes.byref(sv), ok[8],
+                          ok[9], None, ok[11], ok[12], ok[13], ok[14], ok[15], None, ok[16], 16)
+    assert st == L.PKM_ERR_INVALID_ARG
+    st = lib.pkm_backward(h.ptr, None, 10, ok[1], ok[2], ok[3], ok[4], ok[5], ok[6], ok[7], ctypes.byref(sv), ok[8],
+                          ok[9], ok[10], ok[11], ok[12], ok[13], ok[14], ok[15], None, ok[16], 16)
+    assert st == L.PKM_ERR_WORKSPACE
+    assert lib.pkm_stage_gather(h.ptr, None, 4, ok[1], None, ok[3], ok[4]) == L.PKM_ERR_INVALID_ARG
+    assert lib.pkm_stage_score_topk(h.ptr, None, 4, ok[1], ok[2], None, ok[4], ok[5]) == L.PKM_ERR_INVALID_ARG
+    assert lib.pkm_stage_merge_softmax(h.ptr, None, 4, ok[1], ok[2], ok[3], ctypes.c_void_p(FAKE + 4),
+                                       None) == L.PKM_ERR_INVALID_ARG
+    assert lib.pkm_stage_value_grad(h.ptr, None, 4, ok[1], ok[2], ok[3], ok[4], ok[5], ok[6], ok[7], ok[8], ok[9],
+                                    16) == L.PKM_ERR_WORKSPACE
+    assert lib.pkm_stage_subkey_grad(h.ptr, None, 4, ok[1], ok[2], ok[3], ok[4], ok[5], ok[6], ok[7], ok[8], ok[9],
+                                     None, 0) == L.PKM_ERR_WORKSPACE
+    assert lib.pkm_stage_query_grad(h.ptr, None, 4, ok[1], ok[2], ok[3], ok[4], ctypes.byref(sv), ok[5], None,
+                                    ok[7], None, ok[9], 1 << 30) == L.PKM_ERR_INVALID_ARG   # BN needs dgamma
+    assert lib.pkm_stage_query(h.ptr, None, 4, ok[1], ok[2], ok[3], ok[4], ctypes.byref(sv), ok[5],
+                               16) == L.PKM_ERR_WORKSPACE
+    for s in range(5):
+        assert lib.pkm_status_string(s)
+
+
+def test_binding_rejects_host_tensors():
+    L = _lib()
+    import torch
+    h = L.pkm_create(_cfg(L))
+    with pytest.raises(ValueError):
+        L.pkm_stage_gather(h, 1, torch.zeros(8, dtype=torch.int32), torch.zeros(8), torch.zeros(64),
+                           torch.zeros(64))
