@@ -58,6 +58,18 @@ def bf16_ulp(v: np.ndarray) -> np.ndarray:
     return np.ldexp(1.0, np.maximum(e - 8, -133))
 
 
+def q_allowed(q_g: np.ndarray, q_o: np.ndarray) -> np.ndarray:
+    """Largest allowed |q_gpu - q_oracle| per element for a bf16 query.
+
+    q is the nearest bf16 of a value the GPU computes in fp32 and the oracle in
+    fp64: the two may land on neighbouring bf16 values (one ulp), and where
+    q_pre sits near its batch mean the fp32 cancellation error (about 1e-5 of
+    the feature's scale) can exceed the ulp of the tiny result.
+    """
+    scale = np.abs(q_o).max(axis=0, keepdims=True)
+    return bf16_ulp(np.maximum(np.abs(q_g), np.abs(q_o))) * 1.0001 + 1e-5 * scale
+
+
 def full_scores(rows: np.ndarray, s1: np.ndarray, s2: np.ndarray, nk2: int) -> np.ndarray:
     """Oracle score of each row id in rows[n, h, m] from the per-half tables s1[n, h, |C|], s2[n, h, |C'|]."""
     i = rows // nk2

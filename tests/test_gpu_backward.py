@@ -1,0 +1,268 @@
+"""GPU parity of the backward steps (a7-a10) against the fp64 CPU oracle.
+
+Stage tests feed both sides the same seeded selections, weights and upstream
+gradients; end-to-end tests run the GPU forward + backward and the oracle's on
+the same seeded layer.  Rules and tolerances: tests/parity.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import pkm_inputs as pi
+from oracle import pkm_oracle as O
+from tests import parity as P
+from tests.gpu_util import layer_for, note, require_lib, to_dev, upload
+from tests.test_gpu_forward import FWD_CASES, run_gpu_forward
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0.25
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    require_lib()
+
+
+def _cfg(**kw):
+    base = dict(T=64, d=16, heads=1, dq=32, n_keys=32, n_keys2=32, topk=8, d_value=64, dtype="f32", bn=False,
+                seed=3)
+    base.update(kw)
+    return pi.custom(**base)
+
+
+# ---------------------------------------------------------------------------
+# a7 (dw) + a8 (sparse dV)
+# ---------------------------------------------------------------------------
+VG_CASES = [
+    # T, heads, k, nk (slots = nk^2), d_value, dtype, zipf, accumulate
+    (40, 2, 8, 16, 64, "f32", 0.0, True),
+    (300, 4, 32, 64, 512, "f32", 0.0, True),
+    (300, 4, 32, 64, 512, "f32", 1.2, False),      # skewed: long runs of one row
+    (128, 4, 32, 128, 1600, "bf16", 0.0, True),
+    (64, 8, 32, 64, 1024, "bf16", 1.0, True),
+    (1, 1, 1, 4, 8, "bf16", 0.0, True),
+    (2000, 2, 16, 16, 16, "f32", 0.0, True),       # 256 rows, ~250 lookups per row
+]
+
+
+@pytest.mark.parametrize("T,h,k,nk,dv,dtype,zipf,acc", VG_CASES)
+def test_value_grad_stage(T, h, k, nk, dv, dtype, zipf, acc):
+    note(f"value_grad T={T} h={h} k={k} slots={nk * nk} dv={dv} {dtype} zipf={zipf} acc={acc}")
+    nrows = nk * nk
+    rows, w = pi.random_selection(T * 3 + 1, T, h, k, nrows, zipf=zipf)
+    V = pi.random_array(8, 1, (nrows, dv), dtype=dtype, std=0.05)
+    dY = pi.random_array(8, 2, (T, dv), dtype=dtype)
+    cfg = _cfg(T=T, heads=h, topk=k, n_keys=nk, n_keys2=nk, d_value=dv, dtype=dtype)
+    layer = layer_for(cfg, accumulate_dv=acc)
+    from product_key_memory_pkm_amd import pkm_stage_value_grad
+    outs = []
+    for rep in range(2):
+        dV = torch.full((nrows, dv), SENTINEL, dtype=torch.float32, device="cuda")
+        touched = torch.full((T * h * k,), -1, dtype=torch.int32, device="cuda")
+        nt = torch.zeros(1, dtype=torch.int64, device="cuda")
+        dw = torch.empty((T, h, k), dtype=torch.float32, device="cuda")
+        pkm_stage_value_grad(layer.handle, T, to_dev(rows), to_dev(w), to_dev(dY), to_dev(V), dV, touched, nt, dw,
+                             layer.workspace(T, True))
+        torch.cuda.synchronize()
+        outs.append((dV.cpu().numpy(), touched.cpu().numpy(), int(nt.item()), dw.cpu().numpy()))
+    dV, touched, nt, dw = outs[0]
+    # bit-identical on a second run (sorted grouping, no atomics)
+    np.testing.assert_array_equal(outs[1][0], dV)
+    np.testing.assert_array_equal(outs[1][3], dw)
+    uniq = np.unique(rows)
+    assert nt == len(uniq)
+    np.testing.assert_array_equal(touched[:nt], uniq)
+    untouched = np.setdiff1d(np.arange(nrows), uniq)
+    assert (dV[untouched] == SENTINEL).all(), "an untouched row was written"
+    ref_dw = O.weight_grad(rows, dY, V, dtype)
+    tol = P.TOL["f32"]
+    assert P.row_rel_err(dw.reshape(T, -1), ref_dw.reshape(T, -1)).max() <= (tol if dtype == "f32" else 1e-5)
+    ref_dv = O.value_grad_rows(rows, w.astype(np.float64), dY, dtype, uniq)
+    got = dV[uniq].astype(np.float64) - (SENTINEL if acc else 0.0)
+    sent_ulp = 2.0 ** -24 * SENTINEL if acc else 0.0
+    err = np.abs(got - ref_dv).max(1)
+    assert (err <= 1e-5 * np.abs(ref_dv).max(1) + 2 * sent_ulp).all()
+
+
+# ---------------------------------------------------------------------------
+# a7 (softmax backward) + a9 (query and sub-key gradients)
+# ---------------------------------------------------------------------------
+SK_CASES = [
+    # T, heads, dq, nk, nk2, k, dtype, tau
+    (50, 2, 32, 16, 24, 8, "f32", 1.0),
+    (400, 4, 256, 256, 256, 32, "f32", 1.0),
+    (300, 4, 512, 1024, 1024, 32, "bf16", 1.0),
+    (77, 3, 16, 9, 40, 9, "bf16", 0.5),
+]
+
+
+@pytest.mark.parametrize("T,h,dq,nk,nk2,k,dtype,tau", SK_CASES)
+def test_subkey_grad_stage(T, h, dq, nk, nk2, k, dtype, tau):
+    note(f"subkey_grad T={T} h={h} dq={dq} nk={nk}/{nk2} k={k} {dtype}")
+    cfg = _cfg(T=T, heads=h, dq=dq, n_keys=nk, n_keys2=nk2, topk=k, dtype=dtype, temperature=tau)
+    rows, w = pi.random_selection(T + 5, T, h, k, nk * nk2)
+    dw = pi.random_array(9, 3, (T, h, k))
+    q = pi.random_array(9, 4, (T, h * dq), dtype=dtype)
+    C = pi.random_array(9, 5, (h, nk, dq // 2), dtype=dtype, std=0.1)
+    Cp = pi.random_array(9, 6, (h, nk2, dq // 2), dtype=dtype, std=0.1)
+    layer = layer_for(cfg)
+    from product_key_memory_pkm_amd import pkm_stage_subkey_grad
+    dq_g = torch.empty((T, h * dq), dtype=torch.float32, device="cuda")
+    dC = torch.full((h, nk, dq // 2), 3.0, dtype=torch.float32, device="cuda")
+    dCp = torch.full((h, nk2, dq // 2), 3.0, dtype=torch.float32, device="cuda")
+    pkm_stage_subkey_grad(layer.handle, T, to_dev(rows), to_dev(w), to_dev(dw), to_dev(q), to_dev(C), to_dev(Cp),
+                          dq_g, dC, dCp, layer.workspace(T, True))
+    torch.cuda.synchronize()
+    ds = O.softmax_backward(w.astype(np.float64), dw.astype(np.float64), tau)
+    ref_dq, ref_dC, ref_dCp = O.subkey_backward(cfg, rows.astype(np.int64), ds, O.decode(q, dtype),
+                                                O.decode(C, dtype), O.decode(Cp, dtype))
+    assert P.row_rel_err(dq_g.cpu().double().numpy(), ref_dq).max() <= 1e-5
+    for got, ref in ((dC, ref_dC), (dCp, ref_dCp)):
+        g = got.cpu().double().numpy()
+        assert P.fro_rel_err(g, ref) <= 1e-5
+        assert (g[np.abs(ref).sum(-1) == 0] == 0).all()     # never-selected sub-keys: exactly zero
+
+
+# ---------------------------------------------------------------------------
+# a10: BatchNorm backward and the projection gradients
+# ---------------------------------------------------------------------------
+QG_CASES = [
+    # T, d, heads, dq, dtype, bn
+    (64, 64, 1, 32, "f32", False),
+    (500, 128, 2, 64, "f32", True),
+    (1000, 1600, 4, 512, "bf16", True),
+    (37, 24, 3, 16, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("T,d,h,dq,dtype,bn", QG_CASES)
+def test_query_grad_stage(T, d, h, dq, dtype, bn):
+    note(f"query_grad T={T} d={d} h={h} dq={dq} {dtype} bn={bn}")
+    cfg = _cfg(T=T, d=d, heads=h, dq=dq, dtype=dtype, bn=bn, n_keys=8, n_keys2=8, topk=4, d_value=16, seed=T + 1)
+    inp = pi.make_inputs(cfg)
+    F = cfg.F
+    gamma = np.linspace(0.5, 1.5, F).astype(np.float32)
+    dq_in = pi.random_array(10, 0, (T, F), std=0.1)
+    # saved state as the forward would leave it: q_pre, batch mean and 1/sqrt(var+eps), all fp32
+    ref = O.query(cfg, dict(inp, gamma=gamma))
+    q_pre32 = ref["q_pre"].astype(np.float32)
+    if bn:
+        mean32 = q_pre32.astype(np.float64).mean(0).astype(np.float32)
+        var = ((q_pre32.astype(np.float64) - mean32) ** 2).mean(0)
+        rstd32 = (1.0 / np.sqrt(var + cfg.bn_eps)).astype(np.float32)
+    layer = layer_for(cfg)
+    saved = layer.alloc_saved(T)
+    saved["q_pre"].copy_(torch.from_numpy(q_pre32))
+    if bn:
+        saved["bn_mean"].copy_(torch.from_numpy(mean32))
+        saved["bn_rstd"].copy_(torch.from_numpy(rstd32))
+    dev = upload(inp)
+    dWq = torch.empty((F, d), dtype=torch.float32, device="cuda")
+    dgamma = torch.empty(F, dtype=torch.float32, device="cuda") if bn else None
+    dbeta = torch.empty(F, dtype=torch.float32, device="cuda") if bn else None
+    dx = torch.empty((T, d), dtype=layer.storage, device="cuda")
+    from product_key_memory_pkm_amd import pkm_stage_query_grad
+    pkm_stage_query_grad(layer.handle, T, to_dev(dq_in), dev["x"], dev["Wq"], to_dev(gamma), saved, dWq, dgamma, dbeta,
+                         dx, layer.workspace(T, True))
+    torch.cuda.synchronize()
+    dq64 = dq_in.astype(np.float64)
+    if bn:
+        xhat = (q_pre32.astype(np.float64) - mean32) * rstd32.astype(np.float64)
+        var_eff = 1.0 / rstd32.astype(np.float64) ** 2 - cfg.bn_eps
+        dq_pre, dg, db = O.batchnorm_backward(dq64, xhat, gamma.astype(np.float64), var_eff, cfg.bn_eps)
+        assert P.fro_rel_err(P.to_f64(dgamma), dg) <= 1e-5
+        assert P.fro_rel_err(P.to_f64(dbeta), db) <= 1e-5
+    else:
+        dq_pre = dq64
+    x = O.decode(inp["x"], dtype)
+    Wq = O.decode(inp["Wq"], dtype)
+    # bf16 storage: dq_pre enters the MFMA products as bf16 (2^-9 relative per element)
+    tol = 1e-5 if dtype == "f32" else 1e-2
+    assert P.fro_rel_err(P.to_f64(dWq), dq_pre.T @ x) <= tol
+    assert P.fro_rel_err(P.to_f64(dx), dq_pre @ Wq) <= tol
+
+
+# ---------------------------------------------------------------------------
+# whole backward
+# ---------------------------------------------------------------------------
+def backward_check(cfg, inp, gpu, g, dV_np, dY):
+    """Compare a GPU backward with the oracle's for the same upstream gradient dY."""
+    ref = O.forward(cfg, inp)
+    gb = O.backward(cfg, inp, ref, dY)
+    tol = P.TOL[cfg.dtype]
+    uniq = np.unique(gpu["idx"])
+    nt = int(g["n_touched"].item())
+    assert nt == len(uniq)
+    np.testing.assert_array_equal(g["touched"].cpu().numpy()[:nt], uniq)
+    untouched = np.setdiff1d(np.arange(cfg.slots), uniq)
+    assert (dV_np[untouched] == SENTINEL).all()
+    rows = np.union1d(uniq, np.unique(ref["rows"]))
+    ref_dv = O.value_grad_rows(ref["rows"], ref["w"], dY, cfg.dtype, rows)
+    # a row sums w*dY over its lookups; the weights carry the forward's relative error, so the
+    # bound is relative to the sum of |w*dY| (rows whose terms cancel would otherwise be held
+    # to far less than the inputs' own accuracy)
+    dY_abs = (dY & np.uint16(0x7FFF)) if cfg.dtype == "bf16" else np.abs(dY)
+    mag = O.value_grad_rows(ref["rows"], ref["w"], dY_abs, cfg.dtype, rows)
+    got = dV_np[rows].astype(np.float64) - SENTINEL
+    err = np.abs(got - ref_dv).max(1)
+    assert (err <= tol * mag.max(1) + 2.0 ** -23 * (SENTINEL + np.abs(got).max(1))).all()
+    assert P.fro_rel_err(P.to_f64(g["dC"]), gb["dC"]) <= tol
+    assert P.fro_rel_err(P.to_f64(g["dCp"]), gb["dCp"]) <= tol
+    assert P.fro_rel_err(P.to_f64(g["dWq"]), gb["dWq"]) <= tol
+    if cfg.bn:
+        assert P.fro_rel_err(P.to_f64(g["dgamma"]), gb["dgamma"]) <= tol
+        assert P.fro_rel_err(P.to_f64(g["dbeta"]), gb["dbeta"]) <= tol
+    if g.get("dx") is not None:
+        assert P.fro_rel_err(P.to_f64(g["dx"]), gb["dx"]) <= tol
+
+
+BWD_CASES = ["tiny", "small", "bf16_mid", "ragged", "one_token", "k1", "tau", "int_ties"]
+
+
+def masked_dy(inp, gpu_idx, ref_rows):
+    """dY with the rows of near-tie tokens zeroed.
+
+    Where a token's selection validly differs from the oracle's (a near tie),
+    its gradients differ too; with a zero upstream gradient such a token adds
+    nothing to any gradient on either side, so every remaining value has one
+    correct answer.  The selections themselves are checked by the forward tests.
+    """
+    exact = (np.sort(gpu_idx, -1) == np.sort(ref_rows, -1)).all(-1).all(-1)
+    dY = inp["dY"].copy()
+    dY[~exact] = 0
+    return dY, exact
+
+
+@pytest.mark.parametrize("name", BWD_CASES)
+def test_backward_end_to_end(name):
+    cfg = FWD_CASES[name]
+    note(f"backward {name}: {cfg}")
+    inp = pi.make_inputs(cfg, with_dy=True)
+    gpu, (layer, dev, saved, y) = run_gpu_forward(cfg, inp)
+    ref = O.forward(cfg, inp)
+    dY, exact = masked_dy(inp, gpu["idx"], ref["rows"])
+    assert exact.mean() > (0.999 if cfg.dtype == "f32" else 0.95)
+    dV = torch.full((cfg.slots, cfg.d_value), SENTINEL, dtype=torch.float32, device="cuda")
+    g = layer.backward(to_dev(dY), dev["x"], dev["Wq"], dev["gamma"], dev["C"], dev["Cp"], dev["V"], saved, dV)
+    torch.cuda.synchronize()
+    backward_check(cfg, inp, gpu, g, dV.cpu().numpy(), dY)
+
+
+def test_backward_is_deterministic():
+    cfg = FWD_CASES["bf16_mid"]
+    note("backward determinism")
+    inp = pi.make_inputs(cfg, with_dy=True)
+    res = []
+    for _ in range(2):
+        gpu, (layer, dev, saved, y) = run_gpu_forward(cfg, inp)
+        dV = torch.zeros((cfg.slots, cfg.d_value), dtype=torch.float32, device="cuda")
+        g = layer.backward(to_dev(inp["dY"]), dev["x"], dev["Wq"], dev["gamma"], dev["C"], dev["Cp"], dev["V"],
+                           saved, dV)
+        torch.cuda.synchronize()
+        out = {k: v.cpu().clone() for k, v in g.items() if v is not None}
+        out["touched"] = out["touched"][: int(out["n_touched"].item())]
+        out["dV"] = dV.cpu()
+        res.append(out)
+    for k in res[0]:
+        assert torch.equal(res[0][k], res[1][k]), k

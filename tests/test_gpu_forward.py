@@ -221,8 +221,7 @@ def test_query_stage(T, d, h, dq, dtype, bn):
         np.testing.assert_allclose(P.to_f64(saved["bn_rstd"]), 1 / np.sqrt(ref["var"] + cfg.bn_eps), rtol=2e-5)
     if dtype == "bf16":
         # q is the nearest bf16 of a value the two sides compute in different precision: equal or one ulp apart
-        ulp = P.bf16_ulp(np.maximum(np.abs(q), np.abs(ref["q"])))
-        assert (np.abs(q - ref["q"]) <= ulp * 1.0001).all()
+        assert (np.abs(q - ref["q"]) <= P.q_allowed(q, ref["q"])).all()
         assert (q != ref["q"]).mean() < 0.01
     else:
         assert P.row_rel_err(q, ref["q"]).max() <= 1e-5
@@ -241,9 +240,9 @@ def forward_check(cfg, inp, gpu: dict, tokens=None):
     half = cfg.dq // 2
     slack = None
     if cfg.dtype == "bf16":
-        ulp = P.bf16_ulp(np.maximum(np.abs(q_g), np.abs(ref["q"])))
         dq_abs = np.abs(q_g - ref["q"])
-        assert (dq_abs <= ulp * 1.0001).all(), "q differs by more than one bf16 ulp"
+        assert (dq_abs <= P.q_allowed(q_g, ref["q"])).all(), "q differs by more than one bf16 ulp + fp32 error"
+        assert (dq_abs > 0).mean() < 0.01
         dqh = dq_abs.reshape(len(tok), cfg.heads, 2, half)
         cmax = np.abs(C).max(axis=1)    # [h, half]
         cpmax = np.abs(Cp).max(axis=1)
