@@ -1,0 +1,213 @@
+"""Benchmark of the product-key memory lookup on one MI355X.
+
+One step = the whole hot path over one batch: forward (projection, BatchNorm,
+per-half scores and top-k, k x k merge + softmax, value gather-sum) and
+backward (value gradient into the touched rows, softmax backward, sub-key
+gradients, BatchNorm backward, dWq, dx).  Workload: the paper-scale memory
+layer (32,768 tokens of width 1600, h=4, dq=512, 1024 x 1024 = 1,048,576 slots,
+k=32, bf16 storage, fp32 accumulation, BatchNorm), seeded synthetic inputs.
+
+Prints one JSON line (see the design doc for every field).  ``--gpus`` above 1 is
+not supported: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+# HBM bytes per launch of the gather kernel at the paper-scale workload, from two rocprofv3 --pmc
+# passes (FETCH_SIZE, WRITE_SIZE) scaled by a plain 1 GiB copy (profiles/gather_paper_hbm_counters.md).
+# They hold for the kernel source whose sha256 prefix is given; any change to it voids them.
+GATHER_TRAFFIC = {"bytes": 13552185344, "source_sha256_16": "53a5257d0d80a76c"}
+
+
+def gather_traffic():
+    import hashlib
+    src = os.path.join(ROOT, "product_key_memory_pkm_amd", "csrc", "gather.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    return GATHER_TRAFFIC["bytes"] if digest == GATHER_TRAFFIC["source_sha256_16"] else None
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="paper", choices=["paper", "skewed", "small"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=6144, help="tokens in the oracle's timed sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (for HBM counter calibration)")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="run this many steps and nothing else (for profilers)")
+    return ap.parse_args()
+
+
+def alg_bytes(cfg):
+    """Algorithmic HBM bytes per launch of the forward gather and of the value-gradient pass."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    L = cfg.T * cfg.heads * cfg.topk
+    gather = L * (cfg.d_value * e + 8) + cfg.T * cfg.d_value * e
+    return {"gather": gather}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1"}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import pkm_inputs as pi
+    from product_key_memory_pkm_amd import ProductKeyMemory, pkm_stage_gather
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 5}), flush=True)
+        return
+
+    cfg = pi.CONFIGS[args.workload]
+    t0 = time.time()
+    inp = pi.make_inputs(cfg, with_dy=True)
+    gen_s = time.time() - t0
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    x, Wq, C, Cp, V, dY = (dev(inp[k]) for k in ("x", "Wq", "C", "Cp", "V", "dY"))
+    gamma, beta = dev(inp["gamma"]), dev(inp["beta"])
+    m = ProductKeyMemory(cfg.d, cfg.heads, cfg.dq, cfg.n_keys, cfg.n_keys2, cfg.topk, cfg.d_value, dtype=cfg.dtype,
+                         bn=cfg.bn, bn_eps=cfg.bn_eps, temperature=cfg.temperature, accumulate_dv=True)
+    T = cfg.T
+    saved = m.alloc_saved(T)
+    y = torch.empty((T, cfg.d_value), dtype=m.storage, device="cuda")
+    dV = torch.zeros((cfg.slots, cfg.d_value), dtype=torch.float32, device="cuda")
+    grads = None
+
+    def step():
+        nonlocal grads
+        m.forward(x, Wq, gamma, beta, C, Cp, V, saved=saved, y=y)
+        grads = m.backward(dY, x, Wq, gamma, C, Cp, V, saved, dV, want_dx=True, out=grads)
+
+    # first call allocates the outputs and the workspace outside the timed region
+    step()
+    torch.cuda.synchronize()
+    if args.profile_steps:
+        for _ in range(args.profile_steps):
+            step()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_steps": args.profile_steps}), flush=True)
+        return
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.time()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.time() - t_wall
+    ms = start.elapsed_time(end) / args.steps
+
+    # forward alone
+    for _ in range(2):
+        m.forward(x, Wq, gamma, beta, C, Cp, V, saved=saved, y=y)
+    torch.cuda.synchronize()
+    start.record()
+    nf = max(3, args.steps)
+    for _ in range(nf):
+        m.forward(x, Wq, gamma, beta, C, Cp, V, saved=saved, y=y)
+    end.record()
+    torch.cuda.synchronize()
+    ms_fwd = start.elapsed_time(end) / nf
+
+    # the gather kernel alone (the forward's pkm_stage_gather launches exactly that kernel),
+    # timed with events on the stream it runs on
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nf)]
+    for a, b in evs:
+        a.record()
+        pkm_stage_gather(m.handle, T, saved["idx"], saved["w"], V, y)
+        b.record()
+    torch.cuda.synchronize()
+    gather_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ab = alg_bytes(cfg)
+    achieved = ab["gather"] / (gather_ms * 1e-3) / 1e9
+
+    out = {
+        "metric": "PKM lookup tokens/sec (fwd+bwd) at 1024^2 slots h=4 k=32",
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": (f"{cfg.name}: T={T}, d={cfg.d}, heads={cfg.heads}, dq={cfg.dq}, "
+                                f"|C|=|C'|={cfg.n_keys} ({cfg.slots} slots), k={cfg.topk}, d_value={cfg.d_value}, "
+                                f"{cfg.dtype} storage, fp32 accumulation, BatchNorm, dV accumulated in fp32"),
+                   "tokens_per_step": T, "step": "forward + backward (all steps a1-a10)"},
+        "fwd_tokens_per_s": T / (ms_fwd * 1e-3),
+        "fwd_ms": ms_fwd,
+        "wall_s_timed_region": wall,
+        "roofline": {"kernel": "gather_sum (a6)", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": gather_traffic(),
+                     "alg_bytes_per_launch": ab["gather"], "avg_launch_ms": gather_ms},
+        "input_generation_s": gen_s,
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, inp, ntok):
+    """The fp64 oracle, as it stands, on a bounded sample: the first ``ntok`` tokens as their own batch."""
+    import numpy as np
+
+    from oracle import pkm_oracle as O
+    import pkm_inputs as pi
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    sub = pi.with_tokens(cfg, ntok)
+    sinp = dict(inp)
+    sinp["x"] = inp["x"][:ntok]
+    sinp["dY"] = inp["dY"][:ntok]
+    t0 = time.time()
+    fwd = O.forward(sub, sinp)
+    bwd = O.backward(sub, sinp, fwd, sinp["dY"], dv_rows=np.unique(fwd["rows"]))
+    dt = time.time() - t0
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"first {ntok} tokens of the benchmark batch as one batch (BatchNorm over the sample), "
+                       f"full forward + backward in fp64 numpy, {dt:.1f} s"),
+            "seconds": dt}
+
+
+if __name__ == "__main__":
+    main()
