@@ -66,8 +66,8 @@ struct FwdLayout {
   size_t sub_idx, sub_score, bn_part, total;
 };
 struct BwdLayout {
-  size_t k0, v0, k1, v1, sort_tmp, flags, pos, seg, scan_tmp, nseg, dw, ds, dq, bn_part, dqpre, dqpre_t, x_t, wq_t,
-      split, total;
+  size_t k0, v0, k1, v1, sort_tmp, flags, pos, seg_flags, seg_pos, seg, scan_tmp, nseg, dw, ds, coef2, dq, bn_part,
+      dqpre, dqpre_t, x_t, wq_t, split, total;
   int splits;
   int64_t tpad;
 };
@@ -107,11 +107,14 @@ BwdLayout bwd_layout(const pkm_handle_s* h, int64_t T) {
   L.sort_tmp = o; o += al(radix_sort_temp_bytes(int64_t(N)));
   L.flags = o; o += al(N * 4);
   L.pos = o; o += al(N * 4);
+  L.seg_flags = o; o += al(N * 4);
+  L.seg_pos = o; o += al(N * 4);
   L.seg = o; o += al((N + 1) * 4);
   L.scan_tmp = o; o += al(256 + scan_temp_bytes(int64_t(N)));
   L.nseg = o; o += al(4 * sizeof(int64_t));
   L.dw = o; o += al(N * 4);
   L.ds = o; o += al(N * 4);
+  L.coef2 = o; o += al(N * 4);
   L.dq = o; o += al(size_t(T) * h->F * 4);
   const size_t nblk = size_t((T + kBnRows - 1) / kBnRows);
   L.bn_part = o; o += al(nblk * 2 * h->F * sizeof(double));
@@ -237,17 +240,21 @@ pkm_status run_subkey_grad(const pkm_handle_s* h, hipStream_t s, int64_t T, cons
   const pkm_config& c = h->cfg;
   const BwdLayout L = bwd_layout(h, T);
   const int64_t N = T * c.heads * c.topk;
-  float* ds = at<float>(ws, L.ds);
+  // per-slot sort keys and coefficients of the two halves (the forward-only regions are free here)
+  uint32_t* key1 = at<uint32_t>(ws, L.flags);
+  uint32_t* key2 = at<uint32_t>(ws, L.pos);
+  float* coef1 = at<float>(ws, L.ds);
+  float* coef2 = at<float>(ws, L.coef2);
   PKM_HIP(launch_softmax_bwd_dq(s, c.dtype, idx, w, dw, C, Cp, T, c.heads, c.d_query, c.topk, c.n_keys, c.n_keys2,
-                                1.0f / c.temperature, ds, dq),
+                                1.0f / c.temperature, dq, key1, coef1, key2, coef2),
           "softmax backward / query gradient");
   for (int half_sel = 0; half_sel < 2; ++half_sel) {
     const int nkeys = half_sel ? c.n_keys2 : c.n_keys;
     float* out = half_sel ? dCp : dC;
-    uint32_t* keys = at<uint32_t>(ws, L.flags);  // scratch: the key array is read only by the first pass
-    PKM_HIP(launch_subkey_keys(s, idx, N, c.heads, c.topk, c.n_keys, c.n_keys2, half_sel, keys), "sub-key ids");
+    const uint32_t* keys = half_sel ? key2 : key1;
+    const float* coef = half_sel ? coef2 : coef1;
     int bits = 1;
-    while ((int64_t(1) << bits) < int64_t(c.heads) * nkeys) ++bits;
+    while ((int64_t(1) << bits) <= int64_t(c.heads) * nkeys) ++bits;  // keys <= heads*nkeys (sentinel)
     bool in1 = false;
     PKM_HIP(launch_radix_sort_from(s, keys, at<uint32_t>(ws, L.k0), at<int32_t>(ws, L.v0), at<uint32_t>(ws, L.k1),
                                    at<int32_t>(ws, L.v1), N, bits, at<void>(ws, L.sort_tmp), &in1),
@@ -257,11 +264,11 @@ pkm_status run_subkey_grad(const pkm_handle_s* h, hipStream_t s, int64_t T, cons
     int32_t* seg = at<int32_t>(ws, L.seg);
     int64_t* nseg = at<int64_t>(ws, L.nseg) + 1 + half_sel;
     PKM_HIP(launch_fill_f32(s, out, int64_t(c.heads) * nkeys * h->half, 0.f), "sub-key gradient clear");
-    PKM_HIP(launch_segments(s, sk, N, at<uint32_t>(ws, L.flags), at<uint32_t>(ws, L.pos), seg, nullptr, nseg,
+    PKM_HIP(launch_segments(s, sk, N, at<uint32_t>(ws, L.seg_flags), at<uint32_t>(ws, L.seg_pos), seg, nullptr, nseg,
                             at<void>(ws, L.scan_tmp)),
             "sub-key segments");
-    PKM_HIP(launch_subkey_grad(s, c.dtype, seg, nseg, N, sk, sv, ds, q, c.heads, c.d_query, c.topk, half_sel, nkeys,
-                               out),
+    PKM_HIP(launch_subkey_grad(s, c.dtype, seg, nseg, int64_t(c.heads) * nkeys, sk, sv, coef, q, c.heads, c.d_query,
+                               c.topk, half_sel, nkeys, out),
             "sub-key gradient");
   }
   return PKM_OK;

@@ -84,17 +84,18 @@ hipError_t launch_value_grad(hipStream_t s, int dtype, const int32_t* seg_start,
                              const float* w, const void* dY, const void* V, float* dV, float* dw,
                              int R, int d_value, bool accumulate);
 
-// a7: ds = w (dw - sum w dw) / tau ; a9: dq from the selected sub-keys.
+// a7 + a9: per (token, head) softmax backward, dq from the distinct selected
+// sub-keys, and per slot the sub-key sort key (h*|C|+i / h*|C'|+j, or the
+// sentinel h*|C| / h*|C'| for a repeated sub-key) with the summed coefficient.
 hipError_t launch_softmax_bwd_dq(hipStream_t s, int dtype, const int32_t* idx, const float* w,
                                  const float* dw, const void* C, const void* Cp, int64_t ntok, int heads,
-                                 int dq, int k, int nk, int nk2, float inv_tau, float* ds, float* dq_out);
-// keys for the sub-key sort: key = h*nk + (row / nk2) (half 0) or h*nk2 + row % nk2 (half 1).
-hipError_t launch_subkey_keys(hipStream_t s, const int32_t* idx, int64_t n, int heads, int k, int nk, int nk2,
-                              int half_sel, uint32_t* keys);
-// dC[seg key] = sum over its contributions of ds[c] * q_half[t(c), h]; untouched rows zeroed.
+                                 int dq, int k, int nk, int nk2, float inv_tau, float* dq_out, uint32_t* key1,
+                                 float* coef1, uint32_t* key2, float* coef2);
+// dC[key] = sum over its sorted entries of coef[c] * q_half[t(c), h], one block per sub-key;
+// sub-keys without entries are left alone (the caller clears dC first).
 hipError_t launch_subkey_grad(hipStream_t s, int dtype, const int32_t* seg_start, const int64_t* nseg,
-                              int64_t nitems, const uint32_t* sorted_keys, const int32_t* sorted_c,
-                              const float* ds, const void* q, int heads, int dq, int k, int half_sel,
+                              int64_t nsub, const uint32_t* sorted_keys, const int32_t* sorted_c,
+                              const float* coef, const void* q, int heads, int dq, int k, int half_sel,
                               int nkeys, float* dC);
 
 hipError_t launch_fill_f32(hipStream_t s, float* p, int64_t n, float v);
