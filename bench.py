@@ -23,17 +23,22 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 
-# HBM bytes per launch of the gather kernel at the paper-scale workload, from two rocprofv3 --pmc
-# passes (FETCH_SIZE, WRITE_SIZE) scaled by a plain 1 GiB copy (profiles/gather_paper_hbm_counters.md).
-# They hold for the kernel source whose sha256 prefix is given; any change to it voids them.
-GATHER_TRAFFIC = {"bytes": 13552185344, "source_sha256_16": "53a5257d0d80a76c"}
+# HBM bytes per launch measured with two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) at the paper-scale
+# workload, scaled by the same counters for a plain 1 GiB copy (profiles/*_hbm_counters.md).  Each figure
+# holds for the kernel source whose sha256 prefix is given; any change to that file voids it (traffic null).
+KERNEL_TRAFFIC = {
+    "gather": {"bytes": 13552185344, "source": "gather.hip", "source_sha256_16": "53a5257d0d80a76c"},
+}
 
 
-def gather_traffic():
+def measured_traffic(name):
     import hashlib
-    src = os.path.join(ROOT, "product_key_memory_pkm_amd", "csrc", "gather.hip")
+    ent = KERNEL_TRAFFIC.get(name)
+    if ent is None:
+        return None
+    src = os.path.join(ROOT, "product_key_memory_pkm_amd", "csrc", ent["source"])
     digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    return GATHER_TRAFFIC["bytes"] if digest == GATHER_TRAFFIC["source_sha256_16"] else None
+    return ent["bytes"] if digest == ent["source_sha256_16"] else None
 
 
 def parse():
@@ -51,12 +56,20 @@ def parse():
     return ap.parse_args()
 
 
-def alg_bytes(cfg):
-    """Algorithmic HBM bytes per launch of the forward gather and of the value-gradient pass."""
+def alg_bytes(cfg, touched):
+    """Algorithmic HBM bytes per launch of the forward gather and of the value-gradient kernel.
+
+    gather: every lookup reads its value row, index and weight; y is written once.
+    value gradient: every touched row of V is read once, its fp32 dV row read and
+    written (accumulating), dY is needed once per token, and per lookup the sorted
+    lookup id, its weight and its dw (4 bytes each) plus one row id per touched row.
+    """
     e = 2 if cfg.dtype == "bf16" else 4
     L = cfg.T * cfg.heads * cfg.topk
-    gather = L * (cfg.d_value * e + 8) + cfg.T * cfg.d_value * e
-    return {"gather": gather}
+    dv = cfg.d_value
+    gather = L * (dv * e + 8) + cfg.T * dv * e
+    value_grad = touched * (dv * e + 2 * dv * 4 + 4) + cfg.T * dv * e + L * 12
+    return {"gather": gather, "value_grad": value_grad}
 
 
 def main():
@@ -69,7 +82,8 @@ def main():
     import torch
 
     import pkm_inputs as pi
-    from product_key_memory_pkm_amd import ProductKeyMemory, pkm_stage_gather
+    from product_key_memory_pkm_amd import (ProductKeyMemory, pkm_stage_gather, pkm_stage_row_groups,
+                                            pkm_stage_value_grad_grouped)
 
     if args.copy_calibration:
         n = 1 << 30
@@ -141,17 +155,42 @@ def main():
     torch.cuda.synchronize()
     ms_fwd = start.elapsed_time(end) / nf
 
-    # the gather kernel alone (the forward's pkm_stage_gather launches exactly that kernel),
-    # timed with events on the stream it runs on
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nf)]
-    for a, b in evs:
-        a.record()
-        pkm_stage_gather(m.handle, T, saved["idx"], saved["w"], V, y)
-        b.record()
+    # The two HBM-bound kernels alone, each timed with events on the stream it runs on:
+    # pkm_stage_gather launches exactly the forward's gather kernel, and
+    # pkm_stage_value_grad_grouped exactly the backward's value-gradient kernel
+    # (on a grouping made beforehand by pkm_stage_row_groups).
+    def timed(fn, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    gather_ms = timed(lambda: pkm_stage_gather(m.handle, T, saved["idx"], saved["w"], V, y), nf)
+    ws = m.workspace(T, True)
+    touched = torch.empty(T * cfg.heads * cfg.topk, dtype=torch.int32, device="cuda")
+    nt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    dw = torch.empty(T * cfg.heads * cfg.topk, dtype=torch.float32, device="cuda")
+    pkm_stage_row_groups(m.handle, T, saved["idx"], touched, nt, ws)
     torch.cuda.synchronize()
-    gather_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    ab = alg_bytes(cfg)
-    achieved = ab["gather"] / (gather_ms * 1e-3) / 1e9
+    vg_ms = timed(lambda: pkm_stage_value_grad_grouped(m.handle, T, saved["w"], dY, V, dV, dw, nt, ws), nf)
+    n_touched = int(nt.item())
+    ab = alg_bytes(cfg, n_touched)
+    kern = {
+        "gather": {"kernel": "gather_sum (a6)", "ms": gather_ms, "alg": ab["gather"]},
+        "value_grad": {"kernel": "value_grad (a7 dw + a8 dV)", "ms": vg_ms, "alg": ab["value_grad"]},
+    }
+    for k_ in kern.values():
+        k_["achieved"] = k_["alg"] / (k_["ms"] * 1e-3) / 1e9
+    dom = max(kern, key=lambda n: kern[n]["ms"])
+
+    def roof(name):
+        k_ = kern[name]
+        return {"kernel": k_["kernel"], "bound": "hbm", "achieved": k_["achieved"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": k_["achieved"] / HBM_PEAK_GBS, "traffic": measured_traffic(name),
+                "alg_bytes_per_launch": k_["alg"], "avg_launch_ms": k_["ms"]}
 
     out = {
         "metric": "PKM lookup tokens/sec (fwd+bwd) at 1024^2 slots h=4 k=32",
@@ -173,9 +212,10 @@ def main():
         "fwd_tokens_per_s": T / (ms_fwd * 1e-3),
         "fwd_ms": ms_fwd,
         "wall_s_timed_region": wall,
-        "roofline": {"kernel": "gather_sum (a6)", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": gather_traffic(),
-                     "alg_bytes_per_launch": ab["gather"], "avg_launch_ms": gather_ms},
+        "roofline": roof(dom),
+        "roofline_other": {n: roof(n) for n in kern if n != dom},
+        "touched_rows": n_touched,
+        "memory_usage": n_touched / cfg.slots,
         "input_generation_s": gen_s,
     }
 

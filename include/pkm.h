@@ -68,12 +68,14 @@ typedef enum {
 typedef enum { PKM_F32 = 0, PKM_BF16 = 1 } pkm_dtype;
 typedef enum { PKM_BN_NONE = 0, PKM_BN_BATCH = 1 } pkm_bn_mode;
 
-/* Layer shape.  Limits checked by pkm_create:
- *   d_in >= 1, d_in % 8 == 0; heads >= 1; d_query even, 2 <= d_query, (d_query/2) % 8 == 0 ... see below;
- *   1 <= topk <= 32, topk <= n_keys, topk <= n_keys2; 1 <= n_keys, n_keys2 <= 2048;
- *   n_keys * n_keys2 < 2^31; d_value >= 1, d_value % 8 == 0; heads * topk <= 1024;
- *   temperature > 0; bn_eps >= 0.
- * (d_query/2 must be a multiple of 16 for bf16 and of 4 for fp32 storage.) */
+/* Layer shape.  pkm_create checks (v = 8 elements for bf16, 4 for fp32 storage,
+ * i.e. 16 bytes):
+ *   d_in >= 1, d_in % v == 0;  heads >= 1;  d_query >= 2, even, (d_query/2) % v == 0;
+ *   1 <= topk <= 32, topk <= n_keys, topk <= n_keys2;  1 <= n_keys, n_keys2 <= 2048;
+ *   n_keys * n_keys2 < 2^31;  d_value >= 1, d_value % v == 0, d_value * elem <= 4096 bytes;
+ *   temperature > 0;  bn_eps >= 0 (BN_BATCH).
+ * Per call: T >= 0 (T = 0 is a no-op; the backward then zeroes its gradients)
+ * and T * heads * topk <= 2^26 lookups. */
 typedef struct {
   int32_t d_in;          /* d: width of x */
   int32_t heads;         /* h */
@@ -177,6 +179,19 @@ pkm_status pkm_stage_value_grad(pkm_handle_t handle, void* stream, int64_t T, co
                                 const float* w, const void* dY, const void* V, float* dV,
                                 int32_t* touched, int64_t* n_touched, float* dw, void* ws,
                                 size_t ws_bytes);
+
+/* Step a8's grouping alone: the lookups of idx [T, h, k] stably sorted by row,
+ * written into the workspace (for pkm_stage_value_grad_grouped), plus touched
+ * and *n_touched as in pkm_backward.  ws >= pkm_workspace_size(handle, T, 1). */
+pkm_status pkm_stage_row_groups(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx,
+                                int32_t* touched, int64_t* n_touched, void* ws, size_t ws_bytes);
+
+/* Steps a7 (dw) and a8 on a grouping already in ws (pkm_stage_row_groups with
+ * the same handle, T, idx and n_touched): launches the value-gradient kernel only.
+ * w, dY, V, dV, dw as in pkm_stage_value_grad; n_touched is read on the device. */
+pkm_status pkm_stage_value_grad_grouped(pkm_handle_t handle, void* stream, int64_t T, const float* w,
+                                        const void* dY, const void* V, float* dV, float* dw,
+                                        const int64_t* n_touched, void* ws, size_t ws_bytes);
 
 /* Steps a7 (softmax backward) and a9: ds = w (dw - sum_s w dw) / tau; then
  * dq[t, h*dq] fp32 (both halves of each head) and dC, dCp (overwritten) through

@@ -57,6 +57,8 @@ _SIGS = {
     "pkm_stage_merge_softmax": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP],
     "pkm_stage_gather": [_VP, _VP, _I64, _VP, _VP, _VP, _VP],
     "pkm_stage_value_grad": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
+    "pkm_stage_row_groups": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _SZ],
+    "pkm_stage_value_grad_grouped": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
     "pkm_stage_subkey_grad": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
     "pkm_stage_query_grad": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_saved), _VP, _VP, _VP, _VP,
                              _VP, _SZ],
@@ -216,6 +218,18 @@ def pkm_stage_value_grad(h, T, idx, w, dY, V, dV, touched, n_touched, dw, ws):
     _check(_invoke("pkm_stage_value_grad", h, T, _ptr(idx), _ptr(w), _ptr(dY), _ptr(V), _ptr(dV),
                                       _ptr(touched), _ptr(n_touched), _ptr(dw), _ptr(ws), _nbytes(ws)),
            "pkm_stage_value_grad")
+
+
+def pkm_stage_row_groups(h, T, idx, touched, n_touched, ws):
+    _dt(idx, torch.int32, "idx")
+    _dt(n_touched, torch.int64, "n_touched")
+    _check(_invoke("pkm_stage_row_groups", h, T, _ptr(idx), _ptr(touched), _ptr(n_touched), _ptr(ws), _nbytes(ws)),
+           "pkm_stage_row_groups")
+
+
+def pkm_stage_value_grad_grouped(h, T, w, dY, V, dV, dw, n_touched, ws):
+    _check(_invoke("pkm_stage_value_grad_grouped", h, T, _ptr(w), _ptr(dY), _ptr(V), _ptr(dV), _ptr(dw),
+                   _ptr(n_touched), _ptr(ws), _nbytes(ws)), "pkm_stage_value_grad_grouped")
 
 
 def pkm_stage_subkey_grad(h, T, idx, w, dw, q, C, Cp, dq, dC, dCp, ws):

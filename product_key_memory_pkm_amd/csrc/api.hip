@@ -211,9 +211,10 @@ pkm_status run_gather(const pkm_handle_s* h, hipStream_t s, int64_t T, const int
   return PKM_OK;
 }
 
-pkm_status run_value_grad(const pkm_handle_s* h, hipStream_t s, int64_t T, const int32_t* idx, const float* w,
-                          const void* dY, const void* V, float* dV, int32_t* touched, int64_t* n_touched, float* dw,
-                          void* ws) {
+// Grouping of the lookups by row.  The sorted (row, lookup) pairs land in
+// (k0, v0) or (k1, v1) depending on the number of radix passes.
+pkm_status run_row_groups(const pkm_handle_s* h, hipStream_t s, int64_t T, const int32_t* idx, int32_t* touched,
+                          int64_t* n_touched, void* ws) {
   const pkm_config& c = h->cfg;
   const BwdLayout L = bwd_layout(h, T);
   const int64_t N = T * c.heads * c.topk;
@@ -223,15 +224,36 @@ pkm_status run_value_grad(const pkm_handle_s* h, hipStream_t s, int64_t T, const
                                  at<void>(ws, L.sort_tmp), &in1),
           "row sort");
   const uint32_t* sk = at<uint32_t>(ws, in1 ? L.k1 : L.k0);
-  const int32_t* sv = at<int32_t>(ws, in1 ? L.v1 : L.v0);
-  int32_t* seg = at<int32_t>(ws, L.seg);
-  PKM_HIP(launch_segments(s, sk, N, at<uint32_t>(ws, L.flags), at<uint32_t>(ws, L.pos), seg, touched, n_touched,
-                          at<void>(ws, L.scan_tmp)),
+  PKM_HIP(launch_segments(s, sk, N, at<uint32_t>(ws, L.flags), at<uint32_t>(ws, L.pos), at<int32_t>(ws, L.seg),
+                          touched, n_touched, at<void>(ws, L.scan_tmp)),
           "row segments");
-  PKM_HIP(launch_value_grad(s, c.dtype, seg, n_touched, N, sk, sv, w, dY, V, dV, dw, c.heads * c.topk, c.d_value,
-                            c.accumulate_dv != 0),
+  return PKM_OK;
+}
+
+int row_sort_passes(const pkm_handle_s* h) {
+  const int p = (h->row_bits + 7) / 8;
+  return p < 1 ? 1 : p;
+}
+
+pkm_status run_value_grad_grouped(const pkm_handle_s* h, hipStream_t s, int64_t T, const float* w, const void* dY,
+                                  const void* V, float* dV, float* dw, const int64_t* n_touched, void* ws) {
+  const pkm_config& c = h->cfg;
+  const BwdLayout L = bwd_layout(h, T);
+  const int64_t N = T * c.heads * c.topk;
+  const bool in1 = row_sort_passes(h) % 2 == 0;  // passes alternate (k0,v0), (k1,v1), ...
+  const uint32_t* sk = at<uint32_t>(ws, in1 ? L.k1 : L.k0);
+  const int32_t* sv = at<int32_t>(ws, in1 ? L.v1 : L.v0);
+  PKM_HIP(launch_value_grad(s, c.dtype, at<int32_t>(ws, L.seg), n_touched, N, sk, sv, w, dY, V, dV, dw,
+                            c.heads * c.topk, c.d_value, c.accumulate_dv != 0),
           "value gradient");
   return PKM_OK;
+}
+
+pkm_status run_value_grad(const pkm_handle_s* h, hipStream_t s, int64_t T, const int32_t* idx, const float* w,
+                          const void* dY, const void* V, float* dV, int32_t* touched, int64_t* n_touched, float* dw,
+                          void* ws) {
+  PKM_TRY(run_row_groups(h, s, T, idx, touched, n_touched, ws));
+  return run_value_grad_grouped(h, s, T, w, dY, V, dV, dw, n_touched, ws);
 }
 
 pkm_status run_subkey_grad(const pkm_handle_s* h, hipStream_t s, int64_t T, const int32_t* idx, const float* w,
@@ -566,6 +588,35 @@ pkm_status pkm_stage_value_grad(pkm_handle_t handle, void* stream, int64_t T, co
   hipStream_t s = as_stream(stream);
   if (T == 0) return zero_grads(handle, s, n_touched, nullptr, nullptr, nullptr, nullptr, nullptr);
   return run_value_grad(handle, s, T, idx, w, dY, V, dV, touched, n_touched, dw, ws);
+}
+
+pkm_status pkm_stage_row_groups(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx, int32_t* touched,
+                                int64_t* n_touched, void* ws, size_t ws_bytes) {
+  PKM_TRY(check_handle(handle));
+  PKM_TRY(check_T(handle, T));
+  PKM_TRY(need(idx, "idx"));
+  PKM_TRY(need(touched, "touched"));
+  if (n_touched == nullptr) return fail(PKM_ERR_INVALID_ARG, "n_touched is NULL");
+  PKM_TRY(check_ws(handle, T, 1, ws, ws_bytes));
+  hipStream_t s = as_stream(stream);
+  if (T == 0) return zero_grads(handle, s, n_touched, nullptr, nullptr, nullptr, nullptr, nullptr);
+  return run_row_groups(handle, s, T, idx, touched, n_touched, ws);
+}
+
+pkm_status pkm_stage_value_grad_grouped(pkm_handle_t handle, void* stream, int64_t T, const float* w, const void* dY,
+                                        const void* V, float* dV, float* dw, const int64_t* n_touched, void* ws,
+                                        size_t ws_bytes) {
+  PKM_TRY(check_handle(handle));
+  PKM_TRY(check_T(handle, T));
+  PKM_TRY(need(w, "w"));
+  PKM_TRY(need(dY, "dY"));
+  PKM_TRY(need(V, "V"));
+  PKM_TRY(need(dV, "dV"));
+  PKM_TRY(need(dw, "dw"));
+  if (n_touched == nullptr) return fail(PKM_ERR_INVALID_ARG, "n_touched is NULL");
+  PKM_TRY(check_ws(handle, T, 1, ws, ws_bytes));
+  if (T == 0) return PKM_OK;
+  return run_value_grad_grouped(handle, as_stream(stream), T, w, dY, V, dV, dw, n_touched, ws);
 }
 
 pkm_status pkm_stage_subkey_grad(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx, const float* w,

@@ -13,13 +13,15 @@
 //     16-column tiles of the TM x |C| score tile and streams its sub-key rows
 //     from global memory (the codebooks are small and stay in L2); the scores
 //     land in LDS and never reach HBM.
-//  3. Selection, one wave per token row: every lane takes |C|/64 scores as
-//     order-preserving 32-bit keys; the k-th largest of the 64 lane maxima
-//     (bisection with ballots) is a lower bound of the row's k-th largest
-//     score, so every key below it is dropped; the <= 64 survivors are
-//     compacted and bitonic-sorted as (key, ~index) 64-bit words, which orders
-//     them by score and then lowest index.  Rows where more than 64 keys pass
-//     the bound (heavy ties) take an exact bisection over all keys instead.
+//  3. Selection: each wave owns TM/8 rows and works on them together (their
+//     dependency chains overlap).  A lane holds |C|/64 scores of a row; the
+//     k-th largest of the 64 lane maxima (bisection on order-preserving keys,
+//     with ballots) is a lower bound of the row's k-th largest score, so every
+//     score below it is dropped by a plain float compare; the <= 64 survivors
+//     are compacted (DPP prefix sum) into the row's own LDS slot and
+//     bitonic-sorted as (key, ~index) 64-bit words, which orders them by score
+//     and then lowest index.  Rows where more than 64 scores pass the bound
+//     (heavy ties) take an exact bisection over all scores instead.
 #include "common.h"
 #include "kernels.h"
 
@@ -67,6 +69,88 @@ struct ScoreTraits<float> {
   }
 };
 
+
+// Exclusive prefix sum of one int per lane (DPP row shifts inside rows of 16,
+// then row broadcasts across rows); *total gets the wave total.
+__device__ __forceinline__ int wave_excl_scan_dpp(int v, int* total) {
+  int x = v;
+  const int lane = lane_id();
+  int y;
+  y = __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += y;
+  y = __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += y;
+  y = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += y;
+  y = __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += y;
+  // inclusive within rows of 16; add the totals of earlier rows
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+            r2 = __builtin_amdgcn_readlane(x, 47), r3 = __builtin_amdgcn_readlane(x, 63);
+  const int row = lane >> 4;
+  x += (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+  *total = r0 + r1 + r2 + r3;
+  return x - v;
+}
+
+// Bitonic sort, descending, of N independent uint64 values per lane across the wave.
+template <int N>
+__device__ __forceinline__ void wave_sort_desc_u64_n(uint64_t* v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const bool take_max = ((lane & stride) == 0) == ((lane & size) == 0);
+#pragma unroll
+      for (int q = 0; q < N; ++q) {
+        const uint64_t o = shfl_xor_u64(v[q], stride);
+        const uint64_t mx = v[q] > o ? v[q] : o;
+        const uint64_t mn = v[q] > o ? o : v[q];
+        v[q] = take_max ? mx : mn;
+      }
+    }
+  }
+}
+
+// Exact top-k of one row held as NPL scores per lane (column j*64 + lane),
+// written as (key, ~column) words into slot[0..k): the k-th largest key by
+// bisection over all columns, every larger key, then equal keys by lowest column.
+template <int NPL>
+__device__ __forceinline__ void exact_topk(const float* v, int k, int lane, uint64_t* slot) {
+  uint32_t key[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) key[j] = v[j] == -INFINITY ? 0u : float_key(v[j]);
+  uint32_t res = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = res | (1u << b);
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) c += key[j] >= cand;
+    if (wave_sum_i(c) >= k) res = cand;
+  }
+  int gt = 0;
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) gt += key[j] > res;
+  int gt_total;
+  int gpos = wave_excl_scan(gt, &gt_total);
+#pragma unroll
+  for (int j = 0; j < NPL; ++j)
+    if (key[j] > res) slot[gpos++] = (uint64_t(key[j]) << 32) | uint32_t(~uint32_t(j * 64 + lane));
+  int remaining = k - gt_total;
+  int base = gt_total;
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const bool eq = key[j] == res;
+    const uint64_t m = ballot(eq);
+    const int rk = lanes_below(m);
+    if (eq && rk < remaining) slot[base + rk] = (uint64_t(key[j]) << 32) | uint32_t(~uint32_t(j * 64 + lane));
+    const int taken = min(popc64(m), remaining);
+    base += taken;
+    remaining -= taken;
+  }
+}
+
 struct Plan {
   int TM;
   int half_pad;
@@ -87,14 +171,15 @@ Plan make_plan(int dtype, int half, int ncols) {
   p.half_pad = round_up(half, KC);
   p.qstride = p.half_pad + VE;
   p.ncols_pad = round_up(ncols, 64);
-  p.sstride = p.ncols_pad + 4;
+  // a row's slot also takes up to 64 compacted (key, ~column) words: >= 128 floats
+  p.sstride = (p.ncols_pad > 128 ? p.ncols_pad : 128) + 4;
   int npl = 1;
   while (npl * 64 < ncols) npl *= 2;
   p.npl = npl;
   p.TM = 0;
   for (int tm = 64; tm >= 16; tm /= 2) {
-    size_t lds = size_t(tm) * p.qstride * e + size_t(tm) * p.sstride * 4 + kWaves * 64 * 8;
-    if (lds <= kLdsLimit) {
+    size_t lds = size_t(tm) * p.qstride * e + size_t(tm) * p.sstride * 4;
+    if (lds <= kLdsLimit && (tm / kWaves) * npl <= 64) {
       p.TM = tm;
       p.lds = lds;
       break;
@@ -117,7 +202,6 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(
   extern __shared__ __attribute__((aligned(16))) char smem[];
   T* qt = reinterpret_cast<T*>(smem);
   float* S = reinterpret_cast<float*>(smem + size_t(TM) * qstride * sizeof(T));
-  uint64_t* scratch = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(S) + size_t(TM) * sstride * 4);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -198,72 +282,78 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(
   }
   __syncthreads();
 
-  // 3. per-row top-k, one wave per row
-  uint64_t* scr = scratch + wave * 64;
-  for (int r = wave; r < TM; r += kWaves) {
-    const int64_t t = t0 + r;
-    if (t >= ntok) break;  // wave-uniform
-    const float* srow = S + size_t(r) * sstride;
-    uint32_t key[NPL];
-    uint32_t lmax = 0;
+  // 3. per-row top-k.  Each wave owns rows wave, wave+8, ... (RPW of them) and
+  // works on all of them at once, so the latency chains of the rows overlap.
+  constexpr int RPW = TM / kWaves;
+  float v[RPW][NPL];
+  float lmax[RPW];
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) {
+    const float* srow = S + size_t(q * kWaves + wave) * sstride;
+    lmax[q] = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
       const int col = j * 64 + lane;
-      key[j] = col < ncols ? float_key(srow[col]) : 0u;
-      lmax = key[j] > lmax ? key[j] : lmax;
+      v[q][j] = col < ncols ? srow[col] : -INFINITY;
+      lmax[q] = fmaxf(lmax[q], v[q][j]);
     }
-    // k lanes hold real keys (k <= ncols), so the bound below is attained.
-    const uint32_t thr = wave_kth_largest_u32(lmax, k);
-    int cnt = 0;
+  }
+  // k-th largest lane maximum (a lower bound of the row's k-th largest score):
+  // bisection on order-preserving keys, with ballots
+  uint32_t lk[RPW], res[RPW];
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) cnt += key[j] >= thr;
-    int total;
-    int pos = wave_excl_scan(cnt, &total);
-    if (total <= 64) {
+  for (int q = 0; q < RPW; ++q) {
+    lk[q] = float_key(lmax[q]);
+    res[q] = 0;
+  }
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+      const uint32_t cand = res[q] | (1u << b);
+      if (popc64(ballot(lk[q] >= cand)) >= k) res[q] = cand;
+    }
+  }
+  int cnt[RPW], total[RPW], pos[RPW];
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) {
+    const float thr = key_float(res[q]);
+    cnt[q] = 0;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) cnt[q] += v[q][j] >= thr;
+    pos[q] = wave_excl_scan_dpp(cnt[q], &total[q]);
+  }
+  // compaction into the row's own LDS slot (its scores are in registers now);
+  // rows with more than 64 survivors (heavy ties) take the exact path below
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) {
+    uint64_t* slot = reinterpret_cast<uint64_t*>(S + size_t(q * kWaves + wave) * sstride);
+    const float thr = key_float(res[q]);
+    if (total[q] <= 64) {
 #pragma unroll
       for (int j = 0; j < NPL; ++j)
-        if (key[j] >= thr) scr[pos++] = (uint64_t(key[j]) << 32) | uint32_t(~uint32_t(j * 64 + lane));
+        if (v[q][j] >= thr) slot[pos[q]++] = (uint64_t(float_key(v[q][j])) << 32) | uint32_t(~uint32_t(j * 64 + lane));
     } else {
-      // Exact k-th largest key over all columns.
-      uint32_t res = 0;
-      for (int b = 31; b >= 0; --b) {
-        const uint32_t cand = res | (1u << b);
-        int c = 0;
-#pragma unroll
-        for (int j = 0; j < NPL; ++j) c += key[j] >= cand;
-        if (wave_sum_i(c) >= k) res = cand;
-      }
-      int gt = 0;
-#pragma unroll
-      for (int j = 0; j < NPL; ++j) gt += key[j] > res;
-      int gt_total;
-      int gpos = wave_excl_scan(gt, &gt_total);
-#pragma unroll
-      for (int j = 0; j < NPL; ++j)
-        if (key[j] > res) scr[gpos++] = (uint64_t(key[j]) << 32) | uint32_t(~uint32_t(j * 64 + lane));
-      // ties at the k-th key: lowest columns first (column = j*64 + lane)
-      int remaining = k - gt_total;
-      int base = gt_total;
-#pragma unroll
-      for (int j = 0; j < NPL; ++j) {
-        const bool eq = key[j] == res;
-        const uint64_t m = ballot(eq);
-        const int rk = lanes_below(m);
-        if (eq && rk < remaining) scr[base + rk] = (uint64_t(key[j]) << 32) | uint32_t(~uint32_t(j * 64 + lane));
-        const int taken = min(popc64(m), remaining);
-        base += taken;
-        remaining -= taken;
-      }
-      total = k;
+      exact_topk<NPL>(v[q], k, lane, slot);
+      total[q] = k;
     }
-    wave_lds_sync();
-    uint64_t v = lane < total ? scr[lane] : 0ull;
-    wave_lds_sync();
-    v = wave_sort_desc_u64(v);
-    if (lane < k) {
+  }
+  wave_lds_sync();
+  uint64_t key[RPW];
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) {
+    const uint64_t* slot = reinterpret_cast<const uint64_t*>(S + size_t(q * kWaves + wave) * sstride);
+    key[q] = lane < total[q] ? slot[lane] : 0ull;
+  }
+  wave_sort_desc_u64_n<RPW>(key);
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) {
+    const int64_t t = t0 + q * kWaves + wave;
+    if (lane < k && t < ntok) {
       const size_t o = ((size_t(t) * heads + hh) * 2 + p) * k + lane;
-      sub_idx[o] = int32_t(~uint32_t(v));
-      sub_score[o] = key_float(uint32_t(v >> 32));
+      sub_idx[o] = int32_t(~uint32_t(key[q]));
+      sub_score[o] = key_float(uint32_t(key[q] >> 32));
     }
   }
 }
@@ -276,12 +366,14 @@ void launch_tm(hipStream_t s, const Plan& pl, const void* q, int64_t ntok, int h
   dim3 grid(unsigned((ntok + TM - 1) / TM), unsigned(heads), 2u);
 #define PKM_SCORE_CASE(NPLV)                                                                          \
   case NPLV: {                                                                                        \
-    auto fn = score_topk_kernel<T, TM, NPLV>;                                                         \
-    hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, \
-                        int(pl.lds));                                                                 \
-    hipLaunchKernelGGL(fn, grid, dim3(kThreads), pl.lds, s, static_cast<const T*>(q), ntok, F, dq, half, \
-                       pl.half_pad, pl.qstride, static_cast<const T*>(C), static_cast<const T*>(Cp), nk, \
-                       nk2, k, pl.sstride, sub_idx, sub_score);                                      \
+    if constexpr ((TM / kWaves) * NPLV <= 64) { /* the plan never pairs a tall tile with wide rows */ \
+      auto fn = score_topk_kernel<T, TM, NPLV>;                                                       \
+      hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, \
+                          int(pl.lds));                                                               \
+      hipLaunchKernelGGL(fn, grid, dim3(kThreads), pl.lds, s, static_cast<const T*>(q), ntok, F, dq, half, \
+                         pl.half_pad, pl.qstride, static_cast<const T*>(C), static_cast<const T*>(Cp), nk, \
+                         nk2, k, pl.sstride, sub_idx, sub_score);                                    \
+    }                                                                                                 \
   } break;
   switch (pl.npl) {
     PKM_SCORE_CASE(1)

@@ -157,6 +157,12 @@ def test_backward_and_stage_argument_errors():
                                     ok[7], None, ok[9], 1 << 30) == L.PKM_ERR_INVALID_ARG   # BN needs dgamma
     assert lib.pkm_stage_query(h.ptr, None, 4, ok[1], ok[2], ok[3], ok[4], ctypes.byref(sv), ok[5],
                                16) == L.PKM_ERR_WORKSPACE
+    assert lib.pkm_stage_row_groups(h.ptr, None, 4, ok[1], ok[2], None, ok[3], 1 << 30) == L.PKM_ERR_INVALID_ARG
+    assert lib.pkm_stage_row_groups(h.ptr, None, 4, ok[1], ok[2], ok[3], ok[4], 16) == L.PKM_ERR_WORKSPACE
+    assert lib.pkm_stage_value_grad_grouped(h.ptr, None, 4, ok[1], ok[2], ok[3], ok[4], ok[5], None, ok[6],
+                                            1 << 30) == L.PKM_ERR_INVALID_ARG
+    assert lib.pkm_stage_value_grad_grouped(h.ptr, None, 4, ok[1], ok[2], ok[3], ok[4], ok[5], ok[6], ok[7],
+                                            16) == L.PKM_ERR_WORKSPACE
     for s in range(5):
         assert lib.pkm_status_string(s)
 

@@ -266,3 +266,32 @@ def test_backward_is_deterministic():
         res.append(out)
     for k in res[0]:
         assert torch.equal(res[0][k], res[1][k]), k
+
+
+def test_row_groups_then_grouped_value_grad_equals_value_grad_stage():
+    note("row groups + grouped value grad")
+    T, h, k, nk, dv = 300, 4, 32, 64, 1024
+    rows, w = pi.random_selection(77, T, h, k, nk * nk)
+    V = pi.random_array(8, 1, (nk * nk, dv), dtype="bf16", std=0.05)
+    dY = pi.random_array(8, 2, (T, dv), dtype="bf16")
+    cfg = _cfg(T=T, heads=h, topk=k, n_keys=nk, n_keys2=nk, d_value=dv, dtype="bf16")
+    layer = layer_for(cfg)
+    from product_key_memory_pkm_amd import pkm_stage_row_groups, pkm_stage_value_grad, pkm_stage_value_grad_grouped
+    outs = []
+    for split in (False, True):
+        dV = torch.full((nk * nk, dv), SENTINEL, dtype=torch.float32, device="cuda")
+        touched = torch.empty(T * h * k, dtype=torch.int32, device="cuda")
+        nt = torch.zeros(1, dtype=torch.int64, device="cuda")
+        dw = torch.empty((T, h, k), dtype=torch.float32, device="cuda")
+        ws = layer.workspace(T, True)
+        if split:
+            pkm_stage_row_groups(layer.handle, T, to_dev(rows), touched, nt, ws)
+            pkm_stage_value_grad_grouped(layer.handle, T, to_dev(w), to_dev(dY), to_dev(V), dV, dw, nt, ws)
+        else:
+            pkm_stage_value_grad(layer.handle, T, to_dev(rows), to_dev(w), to_dev(dY), to_dev(V), dV, touched, nt, dw,
+                                 ws)
+        torch.cuda.synchronize()
+        n = int(nt.item())
+        outs.append((dV.cpu(), touched.cpu()[:n], dw.cpu()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
