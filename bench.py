@@ -7,7 +7,8 @@ gradients, BatchNorm backward, dWq, dx).  Workload: the paper-scale memory
 layer (32,768 tokens of width 1600, h=4, dq=512, 1024 x 1024 = 1,048,576 slots,
 k=32, bf16 storage, fp32 accumulation, BatchNorm), seeded synthetic inputs.
 
-Prints one JSON line (see the design doc for every field).  ``--gpus`` above 1 is
+Prints one JSON line: tokens/s, the roofline of the step's dominant kernel and the
+CPU oracle's rate on a bounded sample.  ``--gpus`` above 1 is
 not supported: this path runs on one GPU.
 """
 from __future__ import annotations

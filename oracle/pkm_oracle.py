@@ -23,7 +23,7 @@ Every step is the plain definition, in float64, written from the pages:
   heads; all parameters trained by back-propagation), "关键结果" (BatchNorm on
   the query, h = 4, k = 32), abstract (the product-key search is exact).
 
-Readings where the pages leave a step open (each also listed in the design doc):
+Readings where the pages leave a step open:
 heads each own a W_q slice, a C and a C'; they share V and their outputs are
 summed.  BatchNorm uses the batch statistics of the call (biased variance,
 eps), no bias on the projection, softmax of the raw full-key scores divided
