@@ -72,14 +72,18 @@ def _threads() -> int:
     return max(1, min(16, n))
 
 
-def _fill(seed: int, tensor_id: int, n: int, kind: str, a: float, b: float) -> np.ndarray:
-    out = np.empty(n, dtype=np.float32)
+def _fill(seed: int, tensor_id: int, n: int, kind: str, a: float, b: float, dtype: str = F32) -> np.ndarray:
+    """n fp32 draws (chunk c from its own stream), or their bf16 bits when dtype is bf16.
+
+    The bf16 case rounds chunk by chunk, so large tensors never exist in fp32.
+    """
+    out = np.empty(n, dtype=np.uint16 if dtype == BF16 else np.float32)
     nchunks = (n + CHUNK - 1) // CHUNK
 
     def work(c: int) -> None:
         g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(tensor_id, c))))
         lo, hi = c * CHUNK, min(n, (c + 1) * CHUNK)
-        view = out[lo:hi]
+        view = out[lo:hi] if dtype != BF16 else np.empty(hi - lo, dtype=np.float32)
         if kind == "normal":
             g.standard_normal(out=view, dtype=np.float32)
             if a != 0.0 or b != 1.0:
@@ -93,6 +97,8 @@ def _fill(seed: int, tensor_id: int, n: int, kind: str, a: float, b: float) -> n
             view[:] = g.integers(int(a), int(b) + 1, size=hi - lo).astype(np.float32)
         else:
             raise ValueError(kind)
+        if dtype == BF16:
+            out[lo:hi] = f32_to_bf16_bits(view)
 
     if nchunks == 1:
         work(0)
@@ -219,15 +225,15 @@ def make_inputs(cfg: Config, with_dy: bool = False) -> dict:
     # values
     K = cfg.slots
     if cfg.x_kind == "int" and cfg.key_kind == "int":
-        v = _fill(s, 4, K * cfg.d_value, "int", -ir, ir)
+        v = _fill(s, 4, K * cfg.d_value, "int", -ir, ir, cfg.dtype)
     else:
         std = cfg.v_std if cfg.v_std > 0 else cfg.d_value ** -0.5
-        v = _fill(s, 4, K * cfg.d_value, "normal", 0.0, std)
-    out["V"] = _encode(v.reshape(K, cfg.d_value), cfg.dtype)
+        v = _fill(s, 4, K * cfg.d_value, "normal", 0.0, std, cfg.dtype)
+    out["V"] = v.reshape(K, cfg.d_value)
 
     if with_dy:
-        dy = _fill(s, 5, T * cfg.d_value, "normal", 0.0, 1.0)
-        out["dY"] = _encode(dy.reshape(T, cfg.d_value), cfg.dtype)
+        dy = _fill(s, 5, T * cfg.d_value, "normal", 0.0, 1.0, cfg.dtype)
+        out["dY"] = dy.reshape(T, cfg.d_value)
 
     out["gamma"] = np.ones(F, dtype=np.float32)
     out["beta"] = np.zeros(F, dtype=np.float32)

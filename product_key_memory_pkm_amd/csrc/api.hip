@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <new>
 #include <string>
 
@@ -67,7 +68,7 @@ struct FwdLayout {
 };
 struct BwdLayout {
   size_t k0, v0, k1, v1, sort_tmp, flags, pos, seg_flags, seg_pos, seg, scan_tmp, nseg, dw, ds, coef2, dq, bn_part,
-      dqpre, dqpre_t, x_t, wq_t, split, total;
+      dqpre, dqpre_t, x_t, wq_t, split, aux, total;
   int splits;
   int64_t tpad;
 };
@@ -125,6 +126,8 @@ BwdLayout bwd_layout(const pkm_handle_s* h, int64_t T) {
   L.wq_t = o; o += al(size_t(c.d_in) * h->F * h->elem);
   L.splits = dwq_splits(h, L.tpad);
   L.split = o; o += al(size_t(L.splits) * h->F * c.d_in * 4);
+  // long-run lists and partial sums of the value and sub-key gradients (used one after the other)
+  L.aux = o; o += al(std::max(value_grad_aux_bytes(int64_t(N), c.d_value), subkey_grad_aux_bytes(int64_t(N), c.d_query)));
   L.total = o;
   return L;
 }
@@ -244,7 +247,7 @@ pkm_status run_value_grad_grouped(const pkm_handle_s* h, hipStream_t s, int64_t 
   const uint32_t* sk = at<uint32_t>(ws, in1 ? L.k1 : L.k0);
   const int32_t* sv = at<int32_t>(ws, in1 ? L.v1 : L.v0);
   PKM_HIP(launch_value_grad(s, c.dtype, at<int32_t>(ws, L.seg), n_touched, N, sk, sv, w, dY, V, dV, dw,
-                            c.heads * c.topk, c.d_value, c.accumulate_dv != 0),
+                            c.heads * c.topk, c.d_value, c.accumulate_dv != 0, at<void>(ws, L.aux)),
           "value gradient");
   return PKM_OK;
 }
@@ -289,8 +292,8 @@ pkm_status run_subkey_grad(const pkm_handle_s* h, hipStream_t s, int64_t T, cons
     PKM_HIP(launch_segments(s, sk, N, at<uint32_t>(ws, L.seg_flags), at<uint32_t>(ws, L.seg_pos), seg, nullptr, nseg,
                             at<void>(ws, L.scan_tmp)),
             "sub-key segments");
-    PKM_HIP(launch_subkey_grad(s, c.dtype, seg, nseg, int64_t(c.heads) * nkeys, sk, sv, coef, q, c.heads, c.d_query,
-                               c.topk, half_sel, nkeys, out),
+    PKM_HIP(launch_subkey_grad(s, c.dtype, seg, nseg, int64_t(c.heads) * nkeys, N, sk, sv, coef, q, c.heads,
+                               c.d_query, c.topk, half_sel, nkeys, out, at<void>(ws, L.aux)),
             "sub-key gradient");
   }
   return PKM_OK;

@@ -78,11 +78,14 @@ hipError_t launch_segments(hipStream_t s, const uint32_t* sorted_keys, int64_t n
                            uint32_t* pos, int32_t* seg_start, int32_t* touched, int64_t* count,
                            void* scan_temp);
 
-// a7 + a8: per touched row, dw for every lookup of it and the row's dV.
+// a7 + a8: per touched row, dw for every lookup of it and the row's dV.  Rows
+// with more lookups than a chunk are split over several waves; aux (of
+// value_grad_aux_bytes) holds their lists and partial sums.
+size_t value_grad_aux_bytes(int64_t nitems, int d_value);
 hipError_t launch_value_grad(hipStream_t s, int dtype, const int32_t* seg_start, const int64_t* nseg,
                              int64_t nitems, const uint32_t* sorted_rows, const int32_t* sorted_c,
                              const float* w, const void* dY, const void* V, float* dV, float* dw,
-                             int R, int d_value, bool accumulate);
+                             int R, int d_value, bool accumulate, void* aux);
 
 // a7 + a9: per (token, head) softmax backward, dq from the distinct selected
 // sub-keys, and per slot the sub-key sort key (h*|C|+i / h*|C'|+j, or the
@@ -91,12 +94,15 @@ hipError_t launch_softmax_bwd_dq(hipStream_t s, int dtype, const int32_t* idx, c
                                  const float* dw, const void* C, const void* Cp, int64_t ntok, int heads,
                                  int dq, int k, int nk, int nk2, float inv_tau, float* dq_out, uint32_t* key1,
                                  float* coef1, uint32_t* key2, float* coef2);
-// dC[key] = sum over its sorted entries of coef[c] * q_half[t(c), h], one block per sub-key;
-// sub-keys without entries are left alone (the caller clears dC first).
+// dC[key] = sum over its sorted entries of coef[c] * q_half[t(c), h], one block per
+// sub-key, sub-keys with more entries than a chunk split over several blocks;
+// aux (of subkey_grad_aux_bytes) holds their lists and partial sums.  Sub-keys
+// without entries are left alone (the caller clears dC first).
+size_t subkey_grad_aux_bytes(int64_t nitems, int dq);
 hipError_t launch_subkey_grad(hipStream_t s, int dtype, const int32_t* seg_start, const int64_t* nseg,
-                              int64_t nsub, const uint32_t* sorted_keys, const int32_t* sorted_c,
+                              int64_t nsub, int64_t nitems, const uint32_t* sorted_keys, const int32_t* sorted_c,
                               const float* coef, const void* q, int heads, int dq, int k, int half_sel,
-                              int nkeys, float* dC);
+                              int nkeys, float* dC, void* aux);
 
 hipError_t launch_fill_f32(hipStream_t s, float* p, int64_t n, float v);
 

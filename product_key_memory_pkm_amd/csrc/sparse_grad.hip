@@ -14,8 +14,13 @@
 // one wave per touched row: V[r] is read once and kept in registers, every
 // lookup of r reads its dY row, produces dw with one wave reduction and adds
 // w*dY into the row's fp32 gradient, which is written (or added) once.  The
-// sub-key gradients use the same grouping keyed by sub-key.  Sums run in
-// lookup order, so results are bit-identical from run to run.
+// sub-key gradients use the same grouping keyed by sub-key.  A skewed workload
+// makes some runs very long (thousands of lookups of one row, 10^5 of one
+// sub-key); those are cut into fixed chunks that run in parallel, each chunk's
+// partial sum landing in a slot named by its start position (distinct for all
+// chunks), and one wave or block per long run adds them up in chunk order.
+// Every sum thus has a fixed order, so results are bit-identical from run to
+// run.
 #include "common.h"
 #include "kernels.h"
 
@@ -50,95 +55,205 @@ __device__ __forceinline__ float dot16<float>(const u32x4& a, const u32x4& v, fl
   return c;
 }
 
-// One wave per touched row (grid-stride over rows).  Lane l owns 16-byte
-// vectors l, l+64, ... of the row; the first NVL-1 are in range for every lane
-// (the launcher picks NVL so), only the last one is predicated: out-of-range
-// lanes read vector 0 instead (discarded), so every load is issued unconditionally.  The value row stays in
-// its storage format; each lookup costs one dY row read, NVL dot products, one
-// DPP wave reduction and the fp32 FMAs of w*dY.
+// Lookups of one row longer than this many entries are cut into chunks that
+// separate waves process; their partial sums meet in a fixed order.
+constexpr int kVgChunk = 256;
+
+struct VgArgs {
+  const int32_t* seg_start;
+  const int64_t* nseg;
+  const uint32_t* sorted_rows;
+  const int32_t* sorted_c;
+  const float* w;
+  const void* dY;
+  const void* V;
+  float* dV;
+  float* dw;
+  uint32_t R;  // lookups per token (h*k)
+  int nvec;    // 16-byte vectors per row
+  int accumulate;
+  // long rows
+  const int2* chunk_list;   // (row run u, chunk j >= 1)
+  const int32_t* long_list; // row runs longer than kVgChunk
+  const uint32_t* counts;   // [0] chunks listed, [1] long runs listed
+  float* partial;           // [N / kVgChunk + 1, d_v]: slot of the chunk starting at s is s / kVgChunk
+};
+
+// The wave's lanes own 16-byte vectors l, l+64, ... of a row; the first NVL-1
+// are in range for every lane (the launcher picks NVL so), only the last one is
+// predicated: out-of-range lanes read vector 0 instead (discarded), so every
+// load is issued unconditionally.
+template <int NVL>
+struct LaneVecs {
+  int voff[NVL];
+  bool last_ok;
+  __device__ __forceinline__ LaneVecs(int nvec, int lane) {
+    last_ok = (NVL - 1) * 64 + lane < nvec;
+#pragma unroll
+    for (int m = 0; m < NVL; ++m) voff[m] = (m < NVL - 1 || last_ok) ? (m * 64 + lane) * 16 : 0;
+  }
+};
+
+// g += sum over sorted lookups [lo, hi) of w * dY[t]; dw of each lookup = <dY[t], V[r]>.
+// Each lookup costs one dY row read, NVL dot products, one DPP wave reduction and
+// the fp32 FMAs of w*dY; two lookups are in flight per step.
 template <typename T, int NVL>
-__global__ __launch_bounds__(256) void value_grad_kernel(const int32_t* __restrict__ seg_start,
-                                                         const int64_t* __restrict__ nseg_p,
-                                                         const uint32_t* __restrict__ sorted_rows,
-                                                         const int32_t* __restrict__ sorted_c,
-                                                         const float* __restrict__ w, const T* __restrict__ dY,
-                                                         const T* __restrict__ V, float* __restrict__ dV,
-                                                         float* __restrict__ dw, uint32_t R, int nvec, int accumulate) {
+__device__ __forceinline__ void vg_accumulate(const VgArgs& a, const LaneVecs<NVL>& lv, const u32x4* vr, int lo,
+                                              int hi, float (*g)[Vec16<T>::N]) {
   constexpr int E = Vec16<T>::N;
   const int lane = lane_id();
-  const int64_t nseg = *nseg_p;
-  const int64_t gw = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
-  const int64_t nw = (int64_t(gridDim.x) * blockDim.x) >> 6;
-  const size_t row_bytes = size_t(nvec) * 16;
-  const int dv = nvec * E;
-  const char* Vb = reinterpret_cast<const char*>(V);
-  const char* Yb = reinterpret_cast<const char*>(dY);
-  const bool last_ok = (NVL - 1) * 64 + lane < nvec;
-  int voff[NVL];
+  const size_t row_bytes = size_t(a.nvec) * 16;
+  const char* Yb = reinterpret_cast<const char*>(a.dY);
+  for (int c0 = lo; c0 < hi; c0 += 64) {
+    const int n = min(64, hi - c0);
+    const int my_c = lane < n ? a.sorted_c[c0 + lane] : 0;
+    const float my_w = lane < n ? a.w[my_c] : 0.f;
+    float my_dw = 0.f;
+    for (int j = 0; j < n; j += kVgU) {
+      u32x4 buf[kVgU][NVL];
 #pragma unroll
-  for (int m = 0; m < NVL; ++m) voff[m] = (m < NVL - 1 || last_ok) ? (m * 64 + lane) * 16 : 0;  // clamp to vector 0
-
-  for (int64_t u = gw; u < nseg; u += nw) {
-    const int lo = seg_start[u], hi = seg_start[u + 1];
-    const uint32_t r = sorted_rows[lo];
-    const char* vrow = Vb + size_t(r) * row_bytes;
-    u32x4 vr[NVL];
-    float g[NVL][E];
+      for (int uu = 0; uu < kVgU; ++uu) {
+        const int jj = j + uu < n ? j + uu : n - 1;
+        const uint32_t c = uint32_t(__builtin_amdgcn_readlane(my_c, jj));
+        const char* yrow = Yb + size_t(c / a.R) * row_bytes;
 #pragma unroll
-    for (int m = 0; m < NVL; ++m) {
-      vr[m] = ld16_nt(vrow + voff[m]);
+        for (int m = 0; m < NVL; ++m) buf[uu][m] = ld16(yrow + lv.voff[m]);
+      }
 #pragma unroll
-      for (int e = 0; e < E; ++e) g[m][e] = 0.f;
-    }
-    if (!last_ok) vr[NVL - 1] = u32x4{0, 0, 0, 0};
-    for (int c0 = lo; c0 < hi; c0 += 64) {
-      const int n = min(64, hi - c0);
-      const int my_c = lane < n ? sorted_c[c0 + lane] : 0;
-      const float my_w = lane < n ? w[my_c] : 0.f;
-      float my_dw = 0.f;
-      for (int j = 0; j < n; j += kVgU) {
-        u32x4 buf[kVgU][NVL];
+      for (int uu = 0; uu < kVgU; ++uu) {
+        if (j + uu < n) {  // wave-uniform
+          const float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j + uu));
+          float part = 0.f;
 #pragma unroll
-        for (int uu = 0; uu < kVgU; ++uu) {
-          const int jj = j + uu < n ? j + uu : n - 1;
-          const uint32_t c = uint32_t(__builtin_amdgcn_readlane(my_c, jj));
-          const char* yrow = Yb + size_t(c / R) * row_bytes;
+          for (int m = 0; m < NVL; ++m) {
+            part = dot16<T>(buf[uu][m], vr[m], part);
+            float f[E];
+            Vec16<T>::widen(buf[uu][m], f);
 #pragma unroll
-          for (int m = 0; m < NVL; ++m) buf[uu][m] = ld16(yrow + voff[m]);
-        }
-#pragma unroll
-        for (int uu = 0; uu < kVgU; ++uu) {
-          if (j + uu < n) {  // wave-uniform
-            const float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j + uu));
-            float part = 0.f;
-#pragma unroll
-            for (int m = 0; m < NVL; ++m) {
-              part = dot16<T>(buf[uu][m], vr[m], part);
-              float f[E];
-              Vec16<T>::widen(buf[uu][m], f);
-#pragma unroll
-              for (int e = 0; e < E; ++e) g[m][e] = fmaf(wt, f[e], g[m][e]);
-            }
-            const float s = wave_sum_dpp(part);
-            if (lane == j + uu) my_dw = s;
+            for (int e = 0; e < E; ++e) g[m][e] = fmaf(wt, f[e], g[m][e]);
           }
+          const float sm = wave_sum_dpp(part);
+          if (lane == j + uu) my_dw = sm;
         }
       }
-      if (lane < n) dw[my_c] = my_dw;
     }
-    float* drow = dV + size_t(r) * dv;
+    if (lane < n) a.dw[my_c] = my_dw;
+  }
+}
+
+template <typename T, int NVL>
+__device__ __forceinline__ void vg_load_row(const VgArgs& a, const LaneVecs<NVL>& lv, uint32_t r, u32x4* vr) {
+  const char* vrow = reinterpret_cast<const char*>(a.V) + size_t(r) * size_t(a.nvec) * 16;
 #pragma unroll
-    for (int m = 0; m < NVL; ++m) {
-      if (m == NVL - 1 && !last_ok) continue;
-      float* p = drow + (voff[m] / 16) * E;
+  for (int m = 0; m < NVL; ++m) vr[m] = ld16_nt(vrow + lv.voff[m]);
+  if (!lv.last_ok) vr[NVL - 1] = u32x4{0, 0, 0, 0};
+}
+
+// dst[lane's part] = g (+ old dst when add_old)
+template <typename T, int NVL>
+__device__ __forceinline__ void vg_store(const LaneVecs<NVL>& lv, float* drow, const float (*g)[Vec16<T>::N],
+                                         bool add_old) {
+  constexpr int E = Vec16<T>::N;
 #pragma unroll
-      for (int q4 = 0; q4 < E / 4; ++q4) {
-        f32x4 o = {g[m][q4 * 4 + 0], g[m][q4 * 4 + 1], g[m][q4 * 4 + 2], g[m][q4 * 4 + 3]};
-        if (accumulate) o += *reinterpret_cast<const f32x4*>(p + q4 * 4);
-        *reinterpret_cast<f32x4*>(p + q4 * 4) = o;
-      }
+  for (int m = 0; m < NVL; ++m) {
+    if (m == NVL - 1 && !lv.last_ok) continue;
+    float* p = drow + (lv.voff[m] / 16) * E;
+#pragma unroll
+    for (int q4 = 0; q4 < E / 4; ++q4) {
+      f32x4 o = {g[m][q4 * 4 + 0], g[m][q4 * 4 + 1], g[m][q4 * 4 + 2], g[m][q4 * 4 + 3]};
+      if (add_old) o += *reinterpret_cast<const f32x4*>(p + q4 * 4);
+      *reinterpret_cast<f32x4*>(p + q4 * 4) = o;
     }
   }
+}
+
+template <typename T, int NVL>
+__device__ __forceinline__ void vg_add_from(const LaneVecs<NVL>& lv, const float* src, float (*g)[Vec16<T>::N]) {
+  constexpr int E = Vec16<T>::N;
+#pragma unroll
+  for (int m = 0; m < NVL; ++m) {
+    const float* p = src + (lv.voff[m] / 16) * E;
+#pragma unroll
+    for (int q4 = 0; q4 < E / 4; ++q4) {
+      const f32x4 o = *reinterpret_cast<const f32x4*>(p + q4 * 4);
+      g[m][q4 * 4 + 0] += o.x;
+      g[m][q4 * 4 + 1] += o.y;
+      g[m][q4 * 4 + 2] += o.z;
+      g[m][q4 * 4 + 3] += o.w;
+    }
+  }
+}
+
+// MODE 0: one wave per row run of at most kVgChunk lookups (grid-stride over
+//         runs): the value row is read once, its gradient written once.
+// MODE 1: chunk j >= 1 of a long run: partial sum into its slot.
+// MODE 2: long run: chunk 0, plus the partial sums of chunks 1.. in order, into dV.
+template <typename T, int NVL, int MODE>
+__global__ __launch_bounds__(256) void value_grad_kernel(VgArgs a) {
+  constexpr int E = Vec16<T>::N;
+  const int lane = lane_id();
+  const int64_t gw = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nw = (int64_t(gridDim.x) * blockDim.x) >> 6;
+  const int dv = a.nvec * E;
+  const LaneVecs<NVL> lv(a.nvec, lane);
+  const int64_t nitems = MODE == 0 ? *a.nseg : int64_t(a.counts[MODE - 1]);
+  for (int64_t it = gw; it < nitems; it += nw) {
+    int u, j = 0;
+    if (MODE == 1) {
+      const int2 e = a.chunk_list[it];
+      u = e.x;
+      j = e.y;
+    } else {
+      u = MODE == 0 ? int(it) : a.long_list[it];
+    }
+    const int lo = a.seg_start[u], hi = a.seg_start[u + 1];
+    if (MODE == 0 && hi - lo > kVgChunk) continue;  // wave-uniform: long runs go through MODE 1/2
+    const uint32_t r = a.sorted_rows[lo];
+    u32x4 vr[NVL];
+    vg_load_row<T, NVL>(a, lv, r, vr);
+    float g[NVL][E];
+#pragma unroll
+    for (int m = 0; m < NVL; ++m)
+#pragma unroll
+      for (int e = 0; e < E; ++e) g[m][e] = 0.f;
+    const int clo = lo + j * kVgChunk;
+    const int chi = MODE == 0 ? hi : min(hi, clo + kVgChunk);
+    vg_accumulate<T, NVL>(a, lv, vr, clo, chi, g);
+    if (MODE == 1) {
+      vg_store<T, NVL>(lv, a.partial + size_t(clo / kVgChunk) * dv, g, false);
+    } else {
+      if (MODE == 2)
+        for (int s = lo + kVgChunk; s < hi; s += kVgChunk) vg_add_from<T, NVL>(lv, a.partial + size_t(s / kVgChunk) * dv, g);
+      vg_store<T, NVL>(lv, a.dV + size_t(r) * dv, g, a.accumulate != 0);
+    }
+  }
+}
+
+// Lists the runs longer than `chunk` entries and their chunks j >= 1 (list
+// order is free: every chunk's output slot and the combine order depend only on
+// the run itself).  Runs whose key is >= nvalid are skipped (keys == nullptr:
+// none is).
+__global__ __launch_bounds__(256) void long_run_plan_kernel(const int32_t* __restrict__ seg_start,
+                                                            const int64_t* __restrict__ nseg_p, int chunk,
+                                                            const uint32_t* __restrict__ keys, uint32_t nvalid,
+                                                            int2* __restrict__ chunk_list,
+                                                            int32_t* __restrict__ long_list,
+                                                            uint32_t* __restrict__ counts) {
+  const int64_t nseg = *nseg_p;
+  for (int64_t u = int64_t(blockIdx.x) * 256 + threadIdx.x; u < nseg; u += int64_t(gridDim.x) * 256) {
+    const int lo = seg_start[u];
+    const int len = seg_start[u + 1] - lo;
+    if (len > chunk && (keys == nullptr || keys[lo] < nvalid)) {
+      const int nch = (len + chunk - 1) / chunk;
+      const uint32_t base = atomicAdd(&counts[0], uint32_t(nch - 1));
+      for (int j = 1; j < nch; ++j) chunk_list[base + j - 1] = make_int2(int(u), j);
+      long_list[atomicAdd(&counts[1], 1u)] = int(u);
+    }
+  }
+}
+
+__global__ void zero_u32_kernel(uint32_t* p, int n) {
+  if (threadIdx.x < n) p[threadIdx.x] = 0u;
 }
 
 // 4 consecutive storage elements widened to fp32.
@@ -248,41 +363,67 @@ __global__ __launch_bounds__(256) void softmax_bwd_dq_kernel(const int32_t* __re
 
 constexpr int kSkU = 8;
 constexpr int kSkWaves = 4;
+// Sub-keys with more entries than this are cut into chunks processed by
+// separate blocks; their partial sums meet in a fixed order.
+constexpr int kSkChunk = 2048;
 
-// One 4-wave block per sub-key (grid-stride): dC[key] = sum over its entries of
-// coef * q_half[t, h].  Wave v takes entries v, v+4, ... in batches of 8 rows,
-// and the four partial sums are added in wave order through LDS.
-template <typename T>
-__global__ __launch_bounds__(256) void subkey_grad_kernel(const int32_t* __restrict__ seg_start,
-                                                          const int64_t* __restrict__ nseg_p,
-                                                          const uint32_t* __restrict__ sorted_keys,
-                                                          const int32_t* __restrict__ sorted_c,
-                                                          const float* __restrict__ coef, const T* __restrict__ q,
-                                                          int heads, int dq, int k, int half_sel, int nkeys,
-                                                          float* __restrict__ dC) {
+struct SkArgs {
+  const int32_t* seg_start;
+  const int64_t* nseg;
+  const uint32_t* sorted_keys;
+  const int32_t* sorted_c;
+  const float* coef;
+  const void* q;
+  float* dC;
+  int heads, dq, k, half_sel, nkeys;
+  const int2* chunk_list;    // (run u, chunk j >= 1)
+  const int32_t* long_list;  // runs longer than kSkChunk
+  const uint32_t* counts;    // [0] chunks listed, [1] long runs listed
+  float* partial;            // [N / kSkChunk + 1, dq/2]: slot of the chunk starting at s is s / kSkChunk
+};
+
+// One 4-wave block per work item (grid-stride): dC[key] = sum over the key's
+// entries of coef * q_half[t, h].  Wave v takes entries v, v+4, ... in batches
+// of 8 rows, and the four partial sums are added in wave order through LDS.
+// MODE 0: a whole run of at most kSkChunk entries, written to dC.
+// MODE 1: chunk j >= 1 of a long run, written to its partial slot.
+// MODE 2: chunk 0 of a long run plus the partial sums of chunks 1.., in order, into dC.
+template <typename T, int MODE>
+__global__ __launch_bounds__(256) void subkey_grad_kernel(SkArgs a) {
   __shared__ f32x4 part[kSkWaves][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t nseg = *nseg_p;
-  const int half = dq / 2;
+  const int64_t nitems = MODE == 0 ? *a.nseg : int64_t(a.counts[MODE - 1]);
+  const int half = a.dq / 2;
   const int nch = half / 4;
-  const int F = heads * dq;
-  const uint32_t nvalid = uint32_t(heads) * uint32_t(nkeys);
-  const int kh = k * heads;
-  for (int64_t u = blockIdx.x; u < nseg; u += gridDim.x) {
-    const int lo = seg_start[u], hi = seg_start[u + 1];
-    const uint32_t key = sorted_keys[lo];
-    if (key >= nvalid) continue;  // block-uniform: the sentinel run (repeated sub-keys)
-    const int hh = int(key / uint32_t(nkeys));
-    const T* qh = q + size_t(hh) * dq + size_t(half_sel) * half;
+  const int F = a.heads * a.dq;
+  const uint32_t nvalid = uint32_t(a.heads) * uint32_t(a.nkeys);
+  const int kh = a.k * a.heads;
+  for (int64_t it = blockIdx.x; it < nitems; it += gridDim.x) {
+    int u, j = 0;
+    if (MODE == 1) {
+      const int2 e = a.chunk_list[it];
+      u = e.x;
+      j = e.y;
+    } else {
+      u = MODE == 0 ? int(it) : a.long_list[it];
+    }
+    const int lo = a.seg_start[u], hi = a.seg_start[u + 1];
+    const uint32_t key = a.sorted_keys[lo];
+    if (key >= nvalid) continue;                      // block-uniform: the sentinel run (repeated sub-keys)
+    if (MODE == 0 && hi - lo > kSkChunk) continue;    // block-uniform: long runs go through MODE 1/2
+    const int clo = lo + j * kSkChunk;
+    const int chi = MODE == 0 ? hi : min(hi, clo + kSkChunk);
+    const int hh = int(key / uint32_t(a.nkeys));
+    const T* qh = static_cast<const T*>(a.q) + size_t(hh) * a.dq + size_t(a.half_sel) * half;
     for (int chb = 0; chb < nch; chb += 64) {
       const int ch = min(chb + lane, nch - 1);
-      float a[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int c0 = lo + wave; c0 < hi; c0 += kSkWaves * 64) {
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int c0 = clo + wave; c0 < chi; c0 += kSkWaves * 64) {
         // entries c0, c0+4, ..., one per lane
         const int e = c0 + lane * kSkWaves;
-        const int my_c = e < hi ? sorted_c[e] : 0;
-        const float my_d = e < hi ? coef[my_c] : 0.f;
-        const int n = min(64, (hi - c0 + kSkWaves - 1) / kSkWaves);
+        const int my_c = e < chi ? a.sorted_c[e] : 0;
+        const float my_d = e < chi ? a.coef[my_c] : 0.f;
+        const int n = min(64, (chi - c0 + kSkWaves - 1) / kSkWaves);
         for (int jb = 0; jb < n; jb += kSkU) {
           float f[kSkU][4];
 #pragma unroll
@@ -296,18 +437,25 @@ __global__ __launch_bounds__(256) void subkey_grad_kernel(const int32_t* __restr
             if (jb + uu < n) {
               const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_d), jb + uu));
 #pragma unroll
-              for (int q4 = 0; q4 < 4; ++q4) a[q4] = fmaf(d, f[uu][q4], a[q4]);
+              for (int q4 = 0; q4 < 4; ++q4) acc[q4] = fmaf(d, f[uu][q4], acc[q4]);
             }
           }
         }
       }
-      part[wave][lane] = f32x4{a[0], a[1], a[2], a[3]};
+      part[wave][lane] = f32x4{acc[0], acc[1], acc[2], acc[3]};
       __syncthreads();
       if (wave == 0 && chb + lane < nch) {
         f32x4 tot = part[0][lane];
 #pragma unroll
         for (int v = 1; v < kSkWaves; ++v) tot += part[v][lane];
-        *reinterpret_cast<f32x4*>(dC + size_t(key) * half + ch * 4) = tot;
+        if (MODE == 1) {
+          *reinterpret_cast<f32x4*>(a.partial + size_t(clo / kSkChunk) * half + ch * 4) = tot;
+        } else {
+          if (MODE == 2)
+            for (int s = lo + kSkChunk; s < hi; s += kSkChunk)
+              tot += *reinterpret_cast<const f32x4*>(a.partial + size_t(s / kSkChunk) * half + ch * 4);
+          *reinterpret_cast<f32x4*>(a.dC + size_t(key) * half + ch * 4) = tot;
+        }
       }
       __syncthreads();
     }
@@ -323,18 +471,53 @@ inline unsigned grid_waves(int64_t items, int64_t cap_blocks = 4096) {
 
 }  // namespace
 
+size_t value_grad_aux_bytes(int64_t nitems, int d_value) {
+  const int64_t slots = nitems / kVgChunk + 1;
+  return size_t(slots) * (size_t(d_value) * 4 + 8 + 4) + 64;
+}
+
 hipError_t launch_value_grad(hipStream_t s, int dtype, const int32_t* seg_start, const int64_t* nseg,
                              int64_t nitems, const uint32_t* sorted_rows, const int32_t* sorted_c, const float* w,
                              const void* dY, const void* V, float* dV, float* dw, int R, int d_value,
-                             bool accumulate) {
+                             bool accumulate, void* aux) {
   const int elem = dtype == kBF16 ? 2 : 4;
   const int nvec = d_value * elem / 16;
   const int per_lane = (nvec + 63) / 64;
+  const int64_t slots = nitems / kVgChunk + 1;
+  char* ap = static_cast<char*>(aux);
+  VgArgs a;
+  a.seg_start = seg_start;
+  a.nseg = nseg;
+  a.sorted_rows = sorted_rows;
+  a.sorted_c = sorted_c;
+  a.w = w;
+  a.dY = dY;
+  a.V = V;
+  a.dV = dV;
+  a.dw = dw;
+  a.R = uint32_t(R);
+  a.nvec = nvec;
+  a.accumulate = int(accumulate);
+  uint32_t* counts = reinterpret_cast<uint32_t*>(ap);
+  a.counts = counts;
+  a.partial = reinterpret_cast<float*>(ap + 64);
+  a.chunk_list = reinterpret_cast<int2*>(ap + 64 + size_t(slots) * d_value * 4);
+  a.long_list = reinterpret_cast<const int32_t*>(ap + 64 + size_t(slots) * (size_t(d_value) * 4 + 8));
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, s, counts, 2);
+  int64_t pb = (nitems + 255) / 256;
+  if (pb > 4096) pb = 4096;
+  if (pb < 1) pb = 1;
+  hipLaunchKernelGGL(long_run_plan_kernel, dim3(unsigned(pb)), dim3(256), 0, s, seg_start, nseg, kVgChunk,
+                     static_cast<const uint32_t*>(nullptr), 0u, const_cast<int2*>(a.chunk_list),
+                     const_cast<int32_t*>(a.long_list), counts);
   const dim3 grid(grid_waves(nitems)), block(256);
-#define PKM_VG(TT, NV)                                                                                        \
-  hipLaunchKernelGGL((value_grad_kernel<TT, NV>), grid, block, 0, s, seg_start, nseg, sorted_rows, sorted_c, w, \
-                     static_cast<const TT*>(dY), static_cast<const TT*>(V), dV, dw, uint32_t(R), nvec,          \
-                     int(accumulate))
+  const dim3 grid_long(grid_waves(slots, 1024));
+#define PKM_VG(TT, NV)                                                                                    \
+  do {                                                                                                    \
+    hipLaunchKernelGGL((value_grad_kernel<TT, NV, 0>), grid, block, 0, s, a);                             \
+    hipLaunchKernelGGL((value_grad_kernel<TT, NV, 1>), grid_long, block, 0, s, a);                        \
+    hipLaunchKernelGGL((value_grad_kernel<TT, NV, 2>), grid_long, block, 0, s, a);                        \
+  } while (0)
   if (dtype == kBF16) {
     if (per_lane <= 1) PKM_VG(bf16_t, 1);
     else if (per_lane == 2) PKM_VG(bf16_t, 2);
@@ -369,18 +552,55 @@ hipError_t launch_softmax_bwd_dq(hipStream_t s, int dtype, const int32_t* idx, c
   return hipGetLastError();
 }
 
+size_t subkey_grad_aux_bytes(int64_t nitems, int dq) {
+  const int64_t slots = nitems / kSkChunk + 1;
+  return size_t(slots) * (size_t(dq / 2) * 4 + 8 + 4) + 64;
+}
+
 hipError_t launch_subkey_grad(hipStream_t s, int dtype, const int32_t* seg_start, const int64_t* nseg, int64_t nsub,
-                              const uint32_t* sorted_keys, const int32_t* sorted_c, const float* coef, const void* q,
-                              int heads, int dq, int k, int half_sel, int nkeys, float* dC) {
-  int64_t blocks = nsub + 1;  // at most one block per distinct sub-key (+ the sentinel run)
+                              int64_t nitems, const uint32_t* sorted_keys, const int32_t* sorted_c, const float* coef,
+                              const void* q, int heads, int dq, int k, int half_sel, int nkeys, float* dC, void* aux) {
+  const int64_t slots = nitems / kSkChunk + 1;
+  const int half = dq / 2;
+  char* ap = static_cast<char*>(aux);
+  SkArgs a;
+  a.seg_start = seg_start;
+  a.nseg = nseg;
+  a.sorted_keys = sorted_keys;
+  a.sorted_c = sorted_c;
+  a.coef = coef;
+  a.q = q;
+  a.dC = dC;
+  a.heads = heads;
+  a.dq = dq;
+  a.k = k;
+  a.half_sel = half_sel;
+  a.nkeys = nkeys;
+  uint32_t* counts = reinterpret_cast<uint32_t*>(ap);
+  a.counts = counts;
+  a.partial = reinterpret_cast<float*>(ap + 64);
+  int2* chunk_list = reinterpret_cast<int2*>(ap + 64 + size_t(slots) * half * 4);
+  int32_t* long_list = reinterpret_cast<int32_t*>(ap + 64 + size_t(slots) * (size_t(half) * 4 + 8));
+  a.chunk_list = chunk_list;
+  a.long_list = long_list;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, s, counts, 2);
+  int64_t pb = (nsub + 1 + 255) / 256;  // at most one run per distinct sub-key (+ the sentinel run)
+  if (pb > 4096) pb = 4096;
+  hipLaunchKernelGGL(long_run_plan_kernel, dim3(unsigned(pb)), dim3(256), 0, s, seg_start, nseg, kSkChunk,
+                     sorted_keys, uint32_t(heads) * uint32_t(nkeys), chunk_list, long_list, counts);
+  int64_t blocks = nsub + 1;
   if (blocks > 8192) blocks = 8192;
-  const dim3 grid{unsigned(blocks), 1, 1}, block{256, 1, 1};
-  if (dtype == kBF16)
-    hipLaunchKernelGGL(subkey_grad_kernel<bf16_t>, grid, block, 0, s, seg_start, nseg, sorted_keys, sorted_c, coef,
-                       static_cast<const bf16_t*>(q), heads, dq, k, half_sel, nkeys, dC);
-  else
-    hipLaunchKernelGGL(subkey_grad_kernel<float>, grid, block, 0, s, seg_start, nseg, sorted_keys, sorted_c, coef,
-                       static_cast<const float*>(q), heads, dq, k, half_sel, nkeys, dC);
+  int64_t lblocks = slots < 8192 ? slots : 8192;
+  const dim3 grid{unsigned(blocks), 1, 1}, lgrid{unsigned(lblocks), 1, 1}, block{256, 1, 1};
+  if (dtype == kBF16) {
+    hipLaunchKernelGGL((subkey_grad_kernel<bf16_t, 0>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((subkey_grad_kernel<bf16_t, 1>), lgrid, block, 0, s, a);
+    hipLaunchKernelGGL((subkey_grad_kernel<bf16_t, 2>), lgrid, block, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((subkey_grad_kernel<float, 0>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((subkey_grad_kernel<float, 1>), lgrid, block, 0, s, a);
+    hipLaunchKernelGGL((subkey_grad_kernel<float, 2>), lgrid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

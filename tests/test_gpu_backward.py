@@ -85,6 +85,45 @@ def test_value_grad_stage(T, h, k, nk, dv, dtype, zipf, acc):
     assert (err <= 1e-5 * np.abs(ref_dv).max(1) + 2 * sent_ulp).all()
 
 
+def test_value_grad_run_length_edges():
+    """Rows looked up exactly 1, 255, 256, 257, 512, 513 and 3000 times.
+
+    Runs longer than the kernel's chunk are split over several waves and their
+    partial sums combined in order; the lengths straddle the chunk boundaries.
+    """
+    T, h, k, dv, nrows = 600, 2, 8, 96, 64
+    lens = [1, 255, 256, 257, 512, 513, 3000]
+    n = T * h * k
+    g = np.random.Generator(np.random.PCG64(77))
+    fixed = np.concatenate([np.full(c, r, np.int64) for r, c in enumerate(lens)])
+    rest = g.integers(len(lens), nrows, size=n - fixed.size)
+    rows = g.permutation(np.concatenate([fixed, rest])).astype(np.int32).reshape(T, h, k)
+    _, w = pi.random_selection(5, T, h, k, nrows)
+    V = pi.random_array(12, 1, (nrows, dv), std=0.05)
+    dY = pi.random_array(12, 2, (T, dv))
+    cfg = _cfg(T=T, heads=h, topk=k, n_keys=8, n_keys2=8, d_value=dv)
+    note(f"value_grad run-length edges {lens}")
+    from product_key_memory_pkm_amd import pkm_stage_value_grad
+    layer = layer_for(cfg, accumulate_dv=True)
+    dV = torch.full((nrows, dv), SENTINEL, dtype=torch.float32, device="cuda")
+    touched = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+    nt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    dw = torch.empty((T, h, k), dtype=torch.float32, device="cuda")
+    pkm_stage_value_grad(layer.handle, T, to_dev(rows), to_dev(w), to_dev(dY), to_dev(V), dV, touched, nt, dw,
+                         layer.workspace(T, True))
+    torch.cuda.synchronize()
+    counts = np.bincount(rows.reshape(-1), minlength=nrows)
+    assert list(counts[:len(lens)]) == lens
+    uniq = np.unique(rows)
+    assert int(nt.item()) == len(uniq)
+    ref_dv = O.value_grad_rows(rows, w.astype(np.float64), dY, "f32", uniq)
+    got = dV.cpu().double().numpy()[uniq] - SENTINEL
+    err = np.abs(got - ref_dv).max(1)
+    assert (err <= 1e-5 * np.abs(ref_dv).max(1) + 2 * 2.0 ** -24 * SENTINEL).all()
+    ref_dw = O.weight_grad(rows, dY, V, "f32")
+    assert P.row_rel_err(dw.cpu().numpy().reshape(T, -1), ref_dw.reshape(T, -1)).max() <= 1e-5
+
+
 # ---------------------------------------------------------------------------
 # a7 (softmax backward) + a9 (query and sub-key gradients)
 # ---------------------------------------------------------------------------
@@ -94,6 +133,7 @@ SK_CASES = [
     (400, 4, 256, 256, 256, 32, "f32", 1.0),
     (300, 4, 512, 1024, 1024, 32, "bf16", 1.0),
     (77, 3, 16, 9, 40, 9, "bf16", 0.5),
+    (4000, 1, 64, 32, 64, 32, "f32", 1.0),     # first-half sub-keys: ~2550 entries each (split runs)
 ]
 
 

@@ -1,0 +1,212 @@
+"""GPU parity at the full workload sizes (paper scale and the skewed workload).
+
+Same kernels and launch shapes as bench.py.  The oracle computes sampled
+outputs one by one (BatchNorm statistics always over every token); properties
+that hold at any size cover the rest: touched rows equal the distinct selected
+rows bit for bit, untouched dV rows keep their sentinel, and the value gradient
+conserves sum_r dV[r] = sum over lookups of w * dY[t].
+"""
+import numpy as np
+import pytest
+import torch
+
+import pkm_inputs as pi
+from oracle import pkm_oracle as O
+from tests import parity as P
+from tests.gpu_util import layer_for, note, require_lib, to_dev, upload
+from tests.test_gpu_forward import forward_check
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0.25
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    require_lib()
+
+
+_INPUTS = {}
+
+
+def _inputs(name):
+    """Seeded inputs of a named workload (with dY), generated once per module."""
+    if name not in _INPUTS:
+        _INPUTS[name] = pi.make_inputs(pi.CONFIGS[name], with_dy=True)
+    return _INPUTS[name]
+
+
+def _sample(n, count, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    return np.sort(g.choice(n, size=min(n, count), replace=False))
+
+
+@pytest.mark.parametrize("name", ["paper", "skewed"])
+def test_forward_full_size_sampled(name):
+    cfg = pi.CONFIGS[name]
+    note(f"full-size forward {name}")
+    inp = _inputs(name)
+    layer = layer_for(cfg)
+    dev = upload({k: inp[k] for k in ('x', 'Wq', 'gamma', 'beta', 'C', 'Cp', 'V')})
+    y, saved = layer.forward(dev["x"], dev["Wq"], dev["gamma"], dev["beta"], dev["C"], dev["Cp"], dev["V"])
+    torch.cuda.synchronize()
+    tok = _sample(cfg.T, 192, 5)
+    tk = torch.from_numpy(tok).cuda()
+    gpu = {"q": P.to_f64(saved["q"][tk]), "idx": saved["idx"][tk].cpu().numpy(), "w": saved["w"][tk].cpu().numpy(),
+           "y": P.to_f64(y[tk])}
+    del dev
+    stats = forward_check(cfg, inp, gpu, tokens=tok)
+    assert stats["exact_set"] > 0.95
+    # BatchNorm statistics over all tokens
+    ref_q = O.query(cfg, inp)
+    np.testing.assert_allclose(saved["bn_mean"].cpu().double().numpy(), ref_q["mean"], rtol=1e-4,
+                               atol=1e-5 * np.abs(ref_q["q_pre"]).max())
+    np.testing.assert_allclose(saved["bn_rstd"].cpu().double().numpy(), 1 / np.sqrt(ref_q["var"] + cfg.bn_eps),
+                               rtol=1e-4)
+
+
+def _row_chunks(n, step=1 << 18):
+    for lo in range(0, n, step):
+        yield lo, min(n, lo + step)
+
+
+# zipf 0.6 over 4.19M rows puts ~15k lookups on the hottest row, about twice
+# what the mixture-query workload selects for its hottest row.
+@pytest.mark.parametrize("name,zipf", [("paper", 0.0), ("skewed", 0.6)])
+def test_value_grad_full_size(name, zipf):
+    cfg = pi.CONFIGS[name]
+    note(f"full-size value gradient {name} zipf={zipf}")
+    T, h, k = cfg.T, cfg.heads, cfg.topk
+    rows, w = pi.random_selection(31, T, h, k, cfg.slots, zipf=zipf)
+    inp = _inputs(name)
+    V, dY = inp["V"], inp["dY"]
+    layer = layer_for(cfg)
+    from product_key_memory_pkm_amd import pkm_stage_value_grad
+    dV = torch.full((cfg.slots, cfg.d_value), SENTINEL, dtype=torch.float32, device="cuda")
+    touched = torch.empty(T * h * k, dtype=torch.int32, device="cuda")
+    nt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    dw = torch.empty((T, h, k), dtype=torch.float32, device="cuda")
+    pkm_stage_value_grad(layer.handle, T, to_dev(rows), to_dev(w), to_dev(dY), to_dev(V), dV, touched, nt, dw,
+                         layer.workspace(T, True))
+    torch.cuda.synchronize()
+    uniq = np.unique(rows)
+    n = int(nt.item())
+    assert n == len(uniq)
+    np.testing.assert_array_equal(touched[:n].cpu().numpy(), uniq)
+    # untouched rows keep the sentinel (checked on the device, in row blocks)
+    mask = torch.ones(cfg.slots, dtype=torch.bool, device="cuda")
+    mask[torch.from_numpy(uniq).cuda().long()] = False
+    tot = torch.zeros(cfg.d_value, dtype=torch.float64, device="cuda")
+    for lo, hi in _row_chunks(cfg.slots):
+        blk, m = dV[lo:hi], mask[lo:hi]
+        assert bool((blk[m] == SENTINEL).all().item()), f"untouched row written in [{lo}, {hi})"
+        tot += (blk[~m].double() - SENTINEL).sum(0)
+    # sampled touched rows: every lookup of the row, from the oracle
+    which = uniq[_sample(len(uniq), 400, 9)]
+    if zipf > 0:   # include the hottest rows
+        vals, cnt = np.unique(rows, return_counts=True)
+        which = np.union1d(which, vals[np.argsort(-cnt)[:8]])
+    ref = O.value_grad_rows(rows, w.astype(np.float64), dY, cfg.dtype, which)
+    dY_abs = dY & np.uint16(0x7FFF)
+    mag = O.value_grad_rows(rows, w.astype(np.float64), dY_abs, cfg.dtype, which)
+    got = dV[torch.from_numpy(which).cuda().long()].cpu().double().numpy() - SENTINEL
+    err = np.abs(got - ref).max(1)
+    assert (err <= 1e-5 * mag.max(1) + 2.0 ** -23 * (SENTINEL + np.abs(got).max(1))).all()
+    # sampled dw
+    tok = _sample(T, 128, 11)
+    ref_dw = O.weight_grad(rows[tok], dY[tok], V, cfg.dtype)
+    assert P.row_rel_err(dw[torch.from_numpy(tok).cuda()].cpu().double().numpy().reshape(len(tok), -1),
+                         ref_dw.reshape(len(tok), -1)).max() <= 1e-5
+    # conservation over all rows: sum_r (dV[r] - sentinel) = sum_t (sum_{h,s} w) dY[t]
+    tot = tot.cpu().numpy()
+    wt = w.astype(np.float64).reshape(T, -1).sum(1)
+    expect = wt @ O.decode(dY, cfg.dtype)
+    assert np.abs(tot - expect).max() <= 1e-3 * np.abs(expect).max() + 1e-3
+
+
+@pytest.mark.parametrize("name,zipf", [("paper", 0.0), ("skewed", 0.6)])
+def test_subkey_grad_full_size_sampled(name, zipf):
+    cfg = pi.CONFIGS[name]
+    note(f"full-size sub-key gradient {name} zipf={zipf}")
+    T, h, k, dq = cfg.T, cfg.heads, cfg.topk, cfg.dq
+    rows, w = pi.random_selection(41, T, h, k, cfg.slots, zipf=zipf)
+    dw = pi.random_array(41, 3, (T, h, k))
+    q = pi.random_array(41, 4, (T, h * dq), dtype="bf16")
+    inp = _inputs(name)
+    C, Cp = inp["C"], inp["Cp"]
+    layer = layer_for(cfg)
+    from product_key_memory_pkm_amd import pkm_stage_subkey_grad
+    dq_g = torch.empty((T, h * dq), dtype=torch.float32, device="cuda")
+    dC = torch.full(C.shape, 3.0, dtype=torch.float32, device="cuda")
+    dCp = torch.full(Cp.shape, 3.0, dtype=torch.float32, device="cuda")
+    pkm_stage_subkey_grad(layer.handle, T, to_dev(rows), to_dev(w), to_dev(dw), to_dev(q), to_dev(C), to_dev(Cp),
+                          dq_g, dC, dCp, layer.workspace(T, True))
+    torch.cuda.synchronize()
+    ds = O.softmax_backward(w.astype(np.float64), dw.astype(np.float64), cfg.temperature)
+    Cd, Cpd, qd = O.decode(C, "bf16"), O.decode(Cp, "bf16"), O.decode(q, "bf16")
+    # dq on sampled tokens
+    tok = _sample(T, 256, 13)
+    ref_dq, _, _ = O.subkey_backward(cfg, rows[tok].astype(np.int64), ds[tok], qd[tok], Cd, Cpd)
+    assert P.row_rel_err(dq_g[torch.from_numpy(tok).cuda()].cpu().double().numpy(), ref_dq).max() <= 1e-5
+    # dC / dC' rows of sampled sub-keys: every lookup of that sub-key
+    g1, g2 = dC.cpu().double().numpy(), dCp.cpu().double().numpy()
+    half = dq // 2
+    hh = np.broadcast_to(np.arange(h)[None, :, None], rows.shape)
+    for half_sel, G, nk in ((0, g1, cfg.n_keys), (1, g2, cfg.n_keys2)):
+        sub = rows // cfg.n_keys2 if half_sel == 0 else rows % cfg.n_keys2
+        picks = [(0, 0), (1, 17), (h - 1, nk - 1), (2, nk // 2 - 1), (0, 700)]
+        # the most used sub-keys (the longest runs)
+        flat = (hh * nk + sub).reshape(-1)
+        cnt = np.bincount(flat, minlength=h * nk)
+        picks += [(int(f // nk), int(f % nk)) for f in np.argsort(-cnt)[:3]]
+        for (h0, i0) in picks:
+            sel = (hh == h0) & (sub == i0)
+            t_idx = np.nonzero(sel)[0]
+            qh = qd.reshape(T, h, 2, half)[t_idx, h0, half_sel, :]
+            ref = (ds[sel][:, None] * qh).sum(0)
+            got = G[h0, i0]
+            scale = (np.abs(ds[sel])[:, None] * np.abs(qh)).sum(0).max() + 1e-30
+            assert np.abs(got - ref).max() <= 1e-5 * scale, (half_sel, h0, i0)
+    # sub-keys never selected: exactly zero
+    used = np.zeros((h, cfg.n_keys), bool)
+    used[hh.reshape(-1), (rows // cfg.n_keys2).reshape(-1)] = True
+    assert (g1[~used] == 0).all()
+
+
+def test_query_grad_full_size():
+    cfg = pi.CONFIGS["paper"]
+    note("full-size query gradient (paper)")
+    T, F = cfg.T, cfg.F
+    inp = _inputs("paper")
+    ref = O.query(cfg, inp)
+    q_pre32 = ref["q_pre"].astype(np.float32)
+    mean32 = q_pre32.astype(np.float64).mean(0).astype(np.float32)
+    var = ((q_pre32.astype(np.float64) - mean32) ** 2).mean(0)
+    rstd32 = (1.0 / np.sqrt(var + cfg.bn_eps)).astype(np.float32)
+    dq_in = pi.random_array(51, 0, (T, F), std=0.1)
+    gamma = np.linspace(0.5, 1.5, F).astype(np.float32)
+    layer = layer_for(cfg)
+    saved = layer.alloc_saved(T)
+    saved["q_pre"].copy_(torch.from_numpy(q_pre32))
+    saved["bn_mean"].copy_(torch.from_numpy(mean32))
+    saved["bn_rstd"].copy_(torch.from_numpy(rstd32))
+    dev = upload({"x": inp["x"], "Wq": inp["Wq"]})
+    dWq = torch.empty((F, cfg.d), dtype=torch.float32, device="cuda")
+    dg = torch.empty(F, dtype=torch.float32, device="cuda")
+    db = torch.empty(F, dtype=torch.float32, device="cuda")
+    dx = torch.empty((T, cfg.d), dtype=torch.bfloat16, device="cuda")
+    from product_key_memory_pkm_amd import pkm_stage_query_grad
+    pkm_stage_query_grad(layer.handle, T, to_dev(dq_in), dev["x"], dev["Wq"], to_dev(gamma), saved, dWq, dg, db, dx,
+                         layer.workspace(T, True))
+    torch.cuda.synchronize()
+    xhat = (q_pre32.astype(np.float64) - mean32) * rstd32.astype(np.float64)
+    var_eff = 1.0 / rstd32.astype(np.float64) ** 2 - cfg.bn_eps
+    dq_pre, dgr, dbr = O.batchnorm_backward(dq_in.astype(np.float64), xhat, gamma.astype(np.float64), var_eff,
+                                            cfg.bn_eps)
+    assert P.fro_rel_err(P.to_f64(dg), dgr) <= 1e-5
+    assert P.fro_rel_err(P.to_f64(db), dbr) <= 1e-5
+    x = O.decode(inp["x"], "bf16")
+    assert P.fro_rel_err(P.to_f64(dWq), dq_pre.T @ x) <= 1e-2
+    tok = _sample(T, 512, 17)
+    Wq = O.decode(inp["Wq"], "bf16")
+    assert P.fro_rel_err(P.to_f64(dx[torch.from_numpy(tok).cuda()]), dq_pre[tok] @ Wq) <= 1e-2
