@@ -23,18 +23,20 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# dense MFMA peaks of the MI355X by operand type
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 
 # HBM bytes per launch measured with two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) at the paper-scale
 # workload, scaled by the same counters for a plain 1 GiB copy (profiles/*_hbm_counters.md).  Each figure
 # holds for the kernel source whose sha256 prefix is given; any change to that file voids it (traffic null).
 KERNEL_TRAFFIC = {
-    "gather": {"bytes": 13552185344, "source": "gather.hip", "source_sha256_16": "53a5257d0d80a76c"},
+    ("gather", "paper"): {"bytes": 13552185344, "source": "gather.hip", "source_sha256_16": "53a5257d0d80a76c"},
 }
 
 
-def measured_traffic(name):
+def measured_traffic(name, workload):
     import hashlib
-    ent = KERNEL_TRAFFIC.get(name)
+    ent = KERNEL_TRAFFIC.get((name, workload))
     if ent is None:
         return None
     src = os.path.join(ROOT, "product_key_memory_pkm_amd", "csrc", ent["source"])
@@ -84,7 +86,7 @@ def main():
 
     import pkm_inputs as pi
     from product_key_memory_pkm_amd import (ProductKeyMemory, pkm_stage_gather, pkm_stage_row_groups,
-                                            pkm_stage_value_grad_grouped)
+                                            pkm_stage_score_topk, pkm_stage_value_grad_grouped)
 
     if args.copy_calibration:
         n = 1 << 30
@@ -178,6 +180,13 @@ def main():
     torch.cuda.synchronize()
     vg_ms = timed(lambda: pkm_stage_value_grad_grouped(m.handle, T, saved["w"], dY, V, dV, dw, nt, ws), nf)
     n_touched = int(nt.item())
+    # the per-half scoring + top-k kernel alone (its MFMA roofline)
+    sub_idx = torch.empty((T, cfg.heads, 2, cfg.topk), dtype=torch.int32, device="cuda")
+    sub_score = torch.empty((T, cfg.heads, 2, cfg.topk), dtype=torch.float32, device="cuda")
+    score_ms = timed(lambda: pkm_stage_score_topk(m.handle, T, saved["q"], C, Cp, sub_idx, sub_score), nf)
+    score_flops = 2.0 * T * cfg.heads * (cfg.n_keys + cfg.n_keys2) * (cfg.dq // 2)
+    score_peak = MFMA_PEAK_TFLOPS[cfg.dtype]
+    score_tf = score_flops / (score_ms * 1e-3) / 1e12
     ab = alg_bytes(cfg, n_touched)
     kern = {
         "gather": {"kernel": "gather_sum (a6)", "ms": gather_ms, "alg": ab["gather"]},
@@ -190,11 +199,11 @@ def main():
     def roof(name):
         k_ = kern[name]
         return {"kernel": k_["kernel"], "bound": "hbm", "achieved": k_["achieved"], "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": k_["achieved"] / HBM_PEAK_GBS, "traffic": measured_traffic(name),
+                "unit": "GB/s", "frac": k_["achieved"] / HBM_PEAK_GBS, "traffic": measured_traffic(name, args.workload),
                 "alg_bytes_per_launch": k_["alg"], "avg_launch_ms": k_["ms"]}
 
     out = {
-        "metric": "PKM lookup tokens/sec (fwd+bwd) at 1024^2 slots h=4 k=32",
+        "metric": f"PKM lookup tokens/sec (fwd+bwd) at {cfg.n_keys}^2 slots h={cfg.heads} k={cfg.topk}",
         "value": T / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -214,7 +223,11 @@ def main():
         "fwd_ms": ms_fwd,
         "wall_s_timed_region": wall,
         "roofline": roof(dom),
-        "roofline_other": {n: roof(n) for n in kern if n != dom},
+        "roofline_other": dict({n: roof(n) for n in kern if n != dom},
+                               score_topk={"kernel": "score_topk (a2 MFMA scores + a3 per-half top-k)", "bound": "mfma",
+                                           "achieved": score_tf, "peak": score_peak, "unit": "TFLOP/s",
+                                           "frac": score_tf / score_peak, "traffic": None,
+                                           "alg_flops_per_launch": score_flops, "avg_launch_ms": score_ms}),
         "touched_rows": n_touched,
         "memory_usage": n_touched / cfg.slots,
         "input_generation_s": gen_s,

@@ -117,7 +117,7 @@ __device__ __forceinline__ void wave_sort_desc_u64_n(uint64_t* v) {
 // written as (key, ~column) words into slot[0..k): the k-th largest key by
 // bisection over all columns, every larger key, then equal keys by lowest column.
 template <int NPL>
-__device__ __forceinline__ void exact_topk(const float* v, int k, int lane, uint64_t* slot) {
+__device__ __forceinline__ void exact_topk(const float* v, int k, int lane, uint32_t col0, uint64_t* slot) {
   uint32_t key[NPL];
 #pragma unroll
   for (int j = 0; j < NPL; ++j) key[j] = v[j] == -INFINITY ? 0u : float_key(v[j]);
@@ -136,7 +136,7 @@ __device__ __forceinline__ void exact_topk(const float* v, int k, int lane, uint
   int gpos = wave_excl_scan(gt, &gt_total);
 #pragma unroll
   for (int j = 0; j < NPL; ++j)
-    if (key[j] > res) slot[gpos++] = (uint64_t(key[j]) << 32) | uint32_t(~uint32_t(j * 64 + lane));
+    if (key[j] > res) slot[gpos++] = (uint64_t(key[j]) << 32) | uint32_t(~(col0 + uint32_t(j * 64 + lane)));
   int remaining = k - gt_total;
   int base = gt_total;
 #pragma unroll
@@ -144,7 +144,7 @@ __device__ __forceinline__ void exact_topk(const float* v, int k, int lane, uint
     const bool eq = key[j] == res;
     const uint64_t m = ballot(eq);
     const int rk = lanes_below(m);
-    if (eq && rk < remaining) slot[base + rk] = (uint64_t(key[j]) << 32) | uint32_t(~uint32_t(j * 64 + lane));
+    if (eq && rk < remaining) slot[base + rk] = (uint64_t(key[j]) << 32) | uint32_t(~(col0 + uint32_t(j * 64 + lane)));
     const int taken = min(popc64(m), remaining);
     base += taken;
     remaining -= taken;
@@ -155,7 +155,7 @@ struct Plan {
   int TM;
   int half_pad;
   int qstride;  // elements
-  int ncols_pad;
+  int cw;       // columns per chunk (multiple of 64); rows wider than this are done chunk by chunk
   int sstride;  // floats
   int npl;
   size_t lds;
@@ -163,6 +163,10 @@ struct Plan {
 
 inline int round_up(int a, int b) { return (a + b - 1) / b * b; }
 
+constexpr int kMaxChunk = 1024;
+
+// Widest chunk first (one selection per row and chunk), then the tallest tile
+// (a sub-key row read from L2 serves TM queries).
 Plan make_plan(int dtype, int half, int ncols) {
   Plan p{};
   const int VE = dtype == kBF16 ? 8 : 4;
@@ -170,34 +174,73 @@ Plan make_plan(int dtype, int half, int ncols) {
   const int e = dtype == kBF16 ? 2 : 4;
   p.half_pad = round_up(half, KC);
   p.qstride = p.half_pad + VE;
-  p.ncols_pad = round_up(ncols, 64);
-  // a row's slot also takes up to 64 compacted (key, ~column) words: >= 128 floats
-  p.sstride = (p.ncols_pad > 128 ? p.ncols_pad : 128) + 4;
-  int npl = 1;
-  while (npl * 64 < ncols) npl *= 2;
-  p.npl = npl;
   p.TM = 0;
-  for (int tm = 64; tm >= 16; tm /= 2) {
-    size_t lds = size_t(tm) * p.qstride * e + size_t(tm) * p.sstride * 4;
-    if (lds <= kLdsLimit && (tm / kWaves) * npl <= 64) {
-      p.TM = tm;
+  const int full = round_up(ncols, 64);
+  for (int cw = full < kMaxChunk ? full : kMaxChunk; cw >= 64 && p.TM == 0; cw = round_up(cw / 2, 64)) {
+    int npl = 1;
+    while (npl * 64 < cw) npl *= 2;
+    // a row's slot also takes up to 64 compacted (key, ~column) words: >= 128 floats
+    const int sstride = (cw > 128 ? cw : 128) + 4;
+    for (int tm = 64; tm >= 16; tm /= 2) {
+      const size_t lds = size_t(tm) * p.qstride * e + size_t(tm) * sstride * 4;
+      if (lds <= kLdsLimit && (tm / kWaves) * npl <= 64 && tm >= (cw > 256 ? 32 : 16)) {
+        p.TM = tm;
+        p.cw = cw;
+        p.npl = npl;
+        p.sstride = sstride;
+        p.lds = lds;
+        break;
+      }
+    }
+    if (cw == 64) break;
+  }
+  if (p.TM == 0) {  // small tiles as a last resort
+    const int cw = full < 256 ? full : 256;
+    int npl = 1;
+    while (npl * 64 < cw) npl *= 2;
+    const int sstride = (cw > 128 ? cw : 128) + 4;
+    const size_t lds = size_t(16) * p.qstride * e + size_t(16) * sstride * 4;
+    if (lds <= kLdsLimit) {
+      p.TM = 16;
+      p.cw = cw;
+      p.npl = npl;
+      p.sstride = sstride;
       p.lds = lds;
-      break;
     }
   }
   return p;
 }
 
+// Top-k of the union of two lists held one word per lane, each sorted
+// descending in lanes 0..31 (lanes 32..63 of a are zero): the lane-wise maximum
+// of a and reversed b is a bitonic sequence holding the 32 largest words of
+// both, which five half-cleaner steps sort.
+__device__ __forceinline__ uint64_t merge_top32(uint64_t a, uint64_t b, int lane) {
+  const int src = lane < 32 ? 31 - lane : lane;
+  const uint64_t br = (uint64_t(uint32_t(__shfl(int(uint32_t(b >> 32)), src, 64))) << 32) |
+                      uint32_t(__shfl(int(uint32_t(b)), src, 64));
+  uint64_t x = lane < 32 ? (a > br ? a : br) : 0ull;
+#pragma unroll
+  for (int stride = 16; stride > 0; stride >>= 1) {
+    const uint64_t o = shfl_xor_u64(x, stride);
+    const bool take_max = (lane & stride) == 0;
+    const uint64_t mx = x > o ? x : o;
+    const uint64_t mn = x > o ? o : x;
+    x = take_max ? mx : mn;
+  }
+  return x;
+}
+
 template <typename T, int TM, int NPL>
 __global__ __launch_bounds__(kThreads) void score_topk_kernel(
     const T* __restrict__ q, int64_t ntok, int F, int dq, int half, int half_pad, int qstride,
-    const T* __restrict__ C, const T* __restrict__ Cp, int nk, int nk2, int k, int sstride,
+    const T* __restrict__ C, const T* __restrict__ Cp, int nk, int nk2, int k, int cw, int sstride,
     int32_t* __restrict__ sub_idx, float* __restrict__ sub_score) {
   using TR = ScoreTraits<T>;
   constexpr int VE = TR::VE;
   constexpr int KC = TR::KC;
   constexpr int RT = TM / 16;
-  constexpr int CT = 256 / TM;  // column tiles per pass: RT*CT*4 = 64 accumulator registers
+  constexpr int CT = TM >= 32 ? 256 / TM : 8;  // column tiles per pass: RT*CT*4 <= 64 accumulator registers
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
   T* qt = reinterpret_cast<T*>(smem);
@@ -227,133 +270,147 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(
   }
   __syncthreads();
 
-  // 2. scores -> LDS
-  const int nct = (ncols + 15) / 16;
+  constexpr int RPW = TM / kWaves;
+  uint64_t run[RPW];  // running top-k of the chunks done so far (lanes 0..31, descending)
   const int lrow = lane & 15;
   const int lgrp = lane >> 4;
-  for (int g0 = wave * CT; g0 < nct; g0 += kWaves * CT) {
-    f32x4 acc[RT][CT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int c = 0; c < CT; ++c) acc[rt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int cb = 0; cb < ncols; cb += cw) {
+    const int cwe = ncols - cb < cw ? ncols - cb : cw;  // columns in this chunk
 
-    const T* kb[CT];
-    bool colok[CT];
+    // 2. scores of the chunk -> LDS
+    const int nct = (cwe + 15) / 16;
+    for (int g0 = wave * CT; g0 < nct; g0 += kWaves * CT) {
+      f32x4 acc[RT][CT];
 #pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      const int col = (g0 + c) * 16 + lrow;
-      colok[c] = col < ncols;
-      kb[c] = keys + size_t(colok[c] ? col : 0) * half;
-    }
-    u32x4 bcur[CT];
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      const int kk = lgrp * VE;
-      bcur[c] = (colok[c] && kk < half) ? ld16(kb[c] + kk) : u32x4{0, 0, 0, 0};
-    }
-    for (int kc = 0; kc < half_pad; kc += KC) {
-      u32x4 bnext[CT];
-      const int kn = kc + KC + lgrp * VE;
-#pragma unroll
-      for (int c = 0; c < CT; ++c)
-        bnext[c] = (kc + KC < half_pad && colok[c] && kn < half) ? ld16(kb[c] + kn) : u32x4{0, 0, 0, 0};
-      u32x4 a[RT];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) a[rt] = ld16(qt + size_t(rt * 16 + lrow) * qstride + kc + lgrp * VE);
-#pragma unroll
-      for (int c = 0; c < CT; ++c)
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) acc[rt][c] = TR::mma(a[rt], bcur[c], acc[rt][c]);
-#pragma unroll
-      for (int c = 0; c < CT; ++c) bcur[c] = bnext[c];
-    }
-    // D layout of a 16x16 MFMA tile: lane l holds column l%16, rows 4*(l/16)+i.
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+        for (int c = 0; c < CT; ++c) acc[rt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+      const T* kb[CT];
+      bool colok[CT];
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
-        if (g0 + c < nct) {
-          const int col = (g0 + c) * 16 + lrow;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) S[size_t(rt * 16 + lgrp * 4 + i) * sstride + col] = acc[rt][c][i];
-        }
+        const int col = (g0 + c) * 16 + lrow;
+        colok[c] = col < cwe;
+        kb[c] = keys + size_t(cb + (colok[c] ? col : 0)) * half;
       }
-  }
-  __syncthreads();
-
-  // 3. per-row top-k.  Each wave owns rows wave, wave+8, ... (RPW of them) and
-  // works on all of them at once, so the latency chains of the rows overlap.
-  constexpr int RPW = TM / kWaves;
-  float v[RPW][NPL];
-  float lmax[RPW];
+      u32x4 bcur[CT];
 #pragma unroll
-  for (int q = 0; q < RPW; ++q) {
-    const float* srow = S + size_t(q * kWaves + wave) * sstride;
-    lmax[q] = -INFINITY;
+      for (int c = 0; c < CT; ++c) {
+        const int kk = lgrp * VE;
+        bcur[c] = (colok[c] && kk < half) ? ld16(kb[c] + kk) : u32x4{0, 0, 0, 0};
+      }
+      for (int kc = 0; kc < half_pad; kc += KC) {
+        u32x4 bnext[CT];
+        const int kn = kc + KC + lgrp * VE;
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-      const int col = j * 64 + lane;
-      v[q][j] = col < ncols ? srow[col] : -INFINITY;
-      lmax[q] = fmaxf(lmax[q], v[q][j]);
+        for (int c = 0; c < CT; ++c)
+          bnext[c] = (kc + KC < half_pad && colok[c] && kn < half) ? ld16(kb[c] + kn) : u32x4{0, 0, 0, 0};
+        u32x4 a[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) a[rt] = ld16(qt + size_t(rt * 16 + lrow) * qstride + kc + lgrp * VE);
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) acc[rt][c] = TR::mma(a[rt], bcur[c], acc[rt][c]);
+#pragma unroll
+        for (int c = 0; c < CT; ++c) bcur[c] = bnext[c];
+      }
+      // D layout of a 16x16 MFMA tile: lane l holds column l%16, rows 4*(l/16)+i.
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+          if (g0 + c < nct) {
+            const int col = (g0 + c) * 16 + lrow;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[size_t(rt * 16 + lgrp * 4 + i) * sstride + col] = acc[rt][c][i];
+          }
+        }
     }
-  }
-  // k-th largest lane maximum (a lower bound of the row's k-th largest score):
-  // bisection on order-preserving keys, with ballots
-  uint32_t lk[RPW], res[RPW];
-#pragma unroll
-  for (int q = 0; q < RPW; ++q) {
-    lk[q] = float_key(lmax[q]);
-    res[q] = 0;
-  }
-#pragma unroll
-  for (int b = 31; b >= 0; --b) {
+    __syncthreads();
+
+    // 3. per-row top-k of the chunk.  Each wave owns rows wave, wave+8, ... (RPW
+    // of them) and works on all of them at once, so the latency chains overlap.
+    float v[RPW][NPL];
+    float lmax[RPW];
 #pragma unroll
     for (int q = 0; q < RPW; ++q) {
-      const uint32_t cand = res[q] | (1u << b);
-      if (popc64(ballot(lk[q] >= cand)) >= k) res[q] = cand;
+      const float* srow = S + size_t(q * kWaves + wave) * sstride;
+      lmax[q] = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) {
+        const int col = j * 64 + lane;
+        v[q][j] = col < cwe ? srow[col] : -INFINITY;
+        lmax[q] = fmaxf(lmax[q], v[q][j]);
+      }
     }
-  }
-  int cnt[RPW], total[RPW], pos[RPW];
+    // k-th largest lane maximum (a lower bound of the row's k-th largest score):
+    // bisection on order-preserving keys, with ballots
+    uint32_t lk[RPW], res[RPW];
 #pragma unroll
-  for (int q = 0; q < RPW; ++q) {
-    const float thr = key_float(res[q]);
-    cnt[q] = 0;
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) cnt[q] += v[q][j] >= thr;
-    pos[q] = wave_excl_scan_dpp(cnt[q], &total[q]);
-  }
-  // compaction into the row's own LDS slot (its scores are in registers now);
-  // rows with more than 64 survivors (heavy ties) take the exact path below
-  __builtin_amdgcn_wave_barrier();
-#pragma unroll
-  for (int q = 0; q < RPW; ++q) {
-    uint64_t* slot = reinterpret_cast<uint64_t*>(S + size_t(q * kWaves + wave) * sstride);
-    const float thr = key_float(res[q]);
-    if (total[q] <= 64) {
-#pragma unroll
-      for (int j = 0; j < NPL; ++j)
-        if (v[q][j] >= thr) slot[pos[q]++] = (uint64_t(float_key(v[q][j])) << 32) | uint32_t(~uint32_t(j * 64 + lane));
-    } else {
-      exact_topk<NPL>(v[q], k, lane, slot);
-      total[q] = k;
+    for (int q = 0; q < RPW; ++q) {
+      lk[q] = float_key(lmax[q]);
+      res[q] = 0;
     }
-  }
-  wave_lds_sync();
-  uint64_t key[RPW];
+    const int kc_ = k < cwe ? k : cwe;  // a chunk narrower than k keeps all its columns
 #pragma unroll
-  for (int q = 0; q < RPW; ++q) {
-    const uint64_t* slot = reinterpret_cast<const uint64_t*>(S + size_t(q * kWaves + wave) * sstride);
-    key[q] = lane < total[q] ? slot[lane] : 0ull;
+    for (int b = 31; b >= 0; --b) {
+#pragma unroll
+      for (int q = 0; q < RPW; ++q) {
+        const uint32_t cand = res[q] | (1u << b);
+        if (popc64(ballot(lk[q] >= cand)) >= kc_) res[q] = cand;
+      }
+    }
+    int cnt[RPW], total[RPW], pos[RPW];
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+      const float thr = key_float(res[q]);
+      cnt[q] = 0;
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) cnt[q] += v[q][j] >= thr;
+      pos[q] = wave_excl_scan_dpp(cnt[q], &total[q]);
+    }
+    // compaction into the row's own LDS slot (its scores are in registers now);
+    // rows with more than 64 survivors (heavy ties) take the exact path below
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+      uint64_t* slot = reinterpret_cast<uint64_t*>(S + size_t(q * kWaves + wave) * sstride);
+      const float thr = key_float(res[q]);
+      if (total[q] <= 64) {
+#pragma unroll
+        for (int j = 0; j < NPL; ++j)
+          if (v[q][j] >= thr)
+            slot[pos[q]++] = (uint64_t(float_key(v[q][j])) << 32) | uint32_t(~(uint32_t(cb) + uint32_t(j * 64 + lane)));
+      } else {
+        exact_topk<NPL>(v[q], kc_, lane, uint32_t(cb), slot);
+        total[q] = kc_;
+      }
+    }
+    wave_lds_sync();
+    uint64_t key[RPW];
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+      const uint64_t* slot = reinterpret_cast<const uint64_t*>(S + size_t(q * kWaves + wave) * sstride);
+      key[q] = lane < total[q] ? slot[lane] : 0ull;
+    }
+    wave_sort_desc_u64_n<RPW>(key);
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+      // the chunk's 32 largest words contain its top k (k <= 32)
+      const uint64_t top = lane < 32 ? key[q] : 0ull;
+      run[q] = cb == 0 ? top : merge_top32(run[q], top, lane);
+    }
+    __syncthreads();  // the next chunk's scores overwrite S
   }
-  wave_sort_desc_u64_n<RPW>(key);
 #pragma unroll
   for (int q = 0; q < RPW; ++q) {
     const int64_t t = t0 + q * kWaves + wave;
     if (lane < k && t < ntok) {
       const size_t o = ((size_t(t) * heads + hh) * 2 + p) * k + lane;
-      sub_idx[o] = int32_t(~uint32_t(key[q]));
-      sub_score[o] = key_float(uint32_t(key[q] >> 32));
+      sub_idx[o] = int32_t(~uint32_t(run[q]));
+      sub_score[o] = key_float(uint32_t(run[q] >> 32));
     }
   }
 }
@@ -372,7 +429,7 @@ void launch_tm(hipStream_t s, const Plan& pl, const void* q, int64_t ntok, int h
                           int(pl.lds));                                                               \
       hipLaunchKernelGGL(fn, grid, dim3(kThreads), pl.lds, s, static_cast<const T*>(q), ntok, F, dq, half, \
                          pl.half_pad, pl.qstride, static_cast<const T*>(C), static_cast<const T*>(Cp), nk, \
-                         nk2, k, pl.sstride, sub_idx, sub_score);                                    \
+                         nk2, k, pl.cw, pl.sstride, sub_idx, sub_score);                             \
     }                                                                                                 \
   } break;
   switch (pl.npl) {
@@ -381,7 +438,6 @@ void launch_tm(hipStream_t s, const Plan& pl, const void* q, int64_t ntok, int h
     PKM_SCORE_CASE(4)
     PKM_SCORE_CASE(8)
     PKM_SCORE_CASE(16)
-    PKM_SCORE_CASE(32)
     default:
       break;
   }
@@ -411,7 +467,7 @@ hipError_t launch_score_topk(hipStream_t s, int dtype, const void* q, int64_t nt
                              const void* C, const void* Cp, int nk, int nk2, int k, int32_t* sub_idx,
                              float* sub_score) {
   const Plan pl = make_plan(dtype, dq / 2, nk > nk2 ? nk : nk2);
-  if (pl.TM == 0 || pl.npl > 32) return hipErrorInvalidValue;
+  if (pl.TM == 0 || pl.npl > 16) return hipErrorInvalidValue;
   if (dtype == kBF16)
     launch_t<bf16_t>(s, pl, q, ntok, heads, dq, C, Cp, nk, nk2, k, sub_idx, sub_score);
   else

@@ -79,6 +79,10 @@ SCORE_CASES = [
     (33, 3, 32, 40, 40, 32, "f32", True),      # small integers: many exact ties
     (31, 2, 64, 100, 37, 32, "bf16", True),
     (17, 1, 8, 5, 3, 3, "f32", False),         # k = |C'|
+    # rows wider than one chunk of 1024 columns: the chunk top-k lists are merged
+    (60, 2, 256, 1040, 1100, 32, "bf16", False),  # last chunk narrower than k
+    (30, 2, 32, 1300, 40, 32, "f32", True),       # ties across chunks: lowest index wins
+    (20, 1, 512, 1024, 1024, 16, "f32", False),   # fp32 with wide halves: 512-column chunks
 ]
 
 
