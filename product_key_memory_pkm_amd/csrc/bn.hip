@@ -16,20 +16,47 @@ namespace pkm {
 
 namespace {
 
+// Thread (ty, tx) of a block sums features 4*tx.. of the block's 256-feature
+// slice over rows ty, ty+4, ... of its row block (fp64, four features at
+// once); the four row groups are then added in a fixed order through LDS.
+__device__ __forceinline__ void bn_combine_store(double (*acc)[4], double* __restrict__ part, int F, int f4) {
+  __shared__ double red[4][2][4][64];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[ty][a][e][tx] = acc[a][e];
+  __syncthreads();
+  if (ty == 0 && f4 < F) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double v = ((red[0][a][e][tx] + red[1][a][e][tx]) + red[2][a][e][tx]) + red[3][a][e][tx];
+        part[(int64_t(blockIdx.y) * 2 + a) * F + f4 + e] = v;
+      }
+  }
+}
+
 __global__ __launch_bounds__(256) void bn_partials_kernel(const float* __restrict__ q_pre, int64_t ntok, int F,
                                                           double* __restrict__ part) {
-  const int f = blockIdx.x * 256 + threadIdx.x;
-  if (f >= F) return;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int f4 = (blockIdx.x * 64 + tx) * 4;
   const int64_t r0 = int64_t(blockIdx.y) * kBnRows;
   const int64_t r1 = r0 + kBnRows < ntok ? r0 + kBnRows : ntok;
-  double s = 0.0, ss = 0.0;
-  for (int64_t r = r0; r < r1; ++r) {
-    const double v = q_pre[r * F + f];
-    s += v;
-    ss += v * v;
+  double acc[2][4] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
+  if (f4 < F) {
+    for (int64_t r = r0 + ty; r < r1; r += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(q_pre + r * F + f4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double d = v[e];
+        acc[0][e] += d;
+        acc[1][e] += d * d;
+      }
+    }
   }
-  part[(int64_t(blockIdx.y) * 2 + 0) * F + f] = s;
-  part[(int64_t(blockIdx.y) * 2 + 1) * F + f] = ss;
+  bn_combine_store(acc, part, F, f4);
 }
 
 __global__ __launch_bounds__(256) void bn_finalize_kernel(const double* __restrict__ part, int nblk, int64_t ntok,
@@ -49,22 +76,52 @@ __global__ __launch_bounds__(256) void bn_finalize_kernel(const double* __restri
   rstd[f] = float(1.0 / sqrt(var + double(eps)));
 }
 
+// Thread tx of a block normalises features 4*tx.. of a 1024-feature slice for
+// kApplyRows consecutive rows (no per-element index arithmetic).
+constexpr int kApplyRows = 8;
+
 template <typename T>
-__global__ __launch_bounds__(256) void bn_apply_kernel(const float* __restrict__ q_pre, int64_t n4, int F,
+__device__ __forceinline__ void store4(T* p, const float* o);
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const float* o) {
+  const uint32_t lo = uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16);
+  const uint32_t hi = uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16);
+  *reinterpret_cast<u32x2*>(p) = u32x2{lo, hi};
+}
+template <>
+__device__ __forceinline__ void store4<float>(float* p, const float* o) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{o[0], o[1], o[2], o[3]};
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void bn_apply_kernel(const float* __restrict__ q_pre, int64_t ntok, int F,
                                                        const float* __restrict__ mean,
                                                        const float* __restrict__ rstd,
                                                        const float* __restrict__ gamma,
                                                        const float* __restrict__ beta, int bn, T* __restrict__ q) {
-  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n4; i += int64_t(gridDim.x) * 256) {
-    const float4 v = reinterpret_cast<const float4*>(q_pre)[i];
-    const int f = int((i * 4) % F);
+  const int f4 = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (f4 >= F) return;
+  float mu[4] = {0.f, 0.f, 0.f, 0.f}, rs[4] = {1.f, 1.f, 1.f, 1.f}, ga[4] = {1.f, 1.f, 1.f, 1.f},
+        be[4] = {0.f, 0.f, 0.f, 0.f};
+  if (bn) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mu[e] = mean[f4 + e];
+      rs[e] = rstd[f4 + e];
+      ga[e] = gamma[f4 + e];
+      be[e] = beta[f4 + e];
+    }
+  }
+  const int64_t r0 = int64_t(blockIdx.y) * kApplyRows;
+  const int64_t r1 = r0 + kApplyRows < ntok ? r0 + kApplyRows : ntok;
+  for (int64_t r = r0; r < r1; ++r) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(q_pre + r * F + f4);
     float o[4] = {v.x, v.y, v.z, v.w};
     if (bn) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = gamma[f + e] * ((o[e] - mean[f + e]) * rstd[f + e]) + beta[f + e];
+      for (int e = 0; e < 4; ++e) o[e] = ga[e] * ((o[e] - mu[e]) * rs[e]) + be[e];
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) q[i * 4 + e] = to_storage<T>(o[e]);
+    store4<T>(q + r * F + f4, o);
   }
 }
 
@@ -73,20 +130,30 @@ __global__ __launch_bounds__(256) void bn_bwd_partials_kernel(const float* __res
                                                               const float* __restrict__ mean,
                                                               const float* __restrict__ rstd, int64_t ntok, int F,
                                                               double* __restrict__ part) {
-  const int f = blockIdx.x * 256 + threadIdx.x;
-  if (f >= F) return;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int f4 = (blockIdx.x * 64 + tx) * 4;
   const int64_t r0 = int64_t(blockIdx.y) * kBnRows;
   const int64_t r1 = r0 + kBnRows < ntok ? r0 + kBnRows : ntok;
-  const float mu = mean[f], rs = rstd[f];
-  double s = 0.0, sx = 0.0;
-  for (int64_t r = r0; r < r1; ++r) {
-    const float g = dq[r * F + f];
-    const float xh = (q_pre[r * F + f] - mu) * rs;
-    s += double(g);
-    sx += double(g) * double(xh);
+  double acc[2][4] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
+  if (f4 < F) {
+    float mu[4], rs[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mu[e] = mean[f4 + e];
+      rs[e] = rstd[f4 + e];
+    }
+    for (int64_t r = r0 + ty; r < r1; r += 4) {
+      const f32x4 g = *reinterpret_cast<const f32x4*>(dq + r * F + f4);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(q_pre + r * F + f4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float xh = (x[e] - mu[e]) * rs[e];
+        acc[0][e] += double(g[e]);
+        acc[1][e] += double(g[e]) * double(xh);
+      }
+    }
   }
-  part[(int64_t(blockIdx.y) * 2 + 0) * F + f] = s;
-  part[(int64_t(blockIdx.y) * 2 + 1) * F + f] = sx;
+  bn_combine_store(acc, part, F, f4);
 }
 
 __global__ __launch_bounds__(256) void bn_bwd_finalize_kernel(const double* __restrict__ part, int nblk, int F,
@@ -161,7 +228,7 @@ inline unsigned grid1d(int64_t n, int64_t cap = 8192) {
 }  // namespace
 
 hipError_t launch_bn_partials(hipStream_t s, const float* q_pre, int64_t ntok, int F, double* part) {
-  dim3 grid(unsigned((F + 255) / 256), unsigned((ntok + kBnRows - 1) / kBnRows));
+  dim3 grid(unsigned((F + 255) / 256), unsigned((ntok + kBnRows - 1) / kBnRows));  // F % 4 == 0
   hipLaunchKernelGGL(bn_partials_kernel, grid, dim3(256), 0, s, q_pre, ntok, F, part);
   return hipGetLastError();
 }
@@ -175,14 +242,15 @@ hipError_t launch_bn_finalize(hipStream_t s, const double* part, int nblk, int64
 
 hipError_t launch_bn_apply(hipStream_t s, int dtype, const float* q_pre, int64_t ntok, int F, const float* mean,
                            const float* rstd, const float* gamma, const float* beta, void* q) {
-  const int64_t n4 = ntok * F / 4;  // F % 4 == 0
+  if (ntok == 0) return hipSuccess;
   const int bn = mean != nullptr;
+  const dim3 grid(unsigned((F / 4 + 255) / 256), unsigned((ntok + kApplyRows - 1) / kApplyRows));  // F % 4 == 0
   if (dtype == kBF16)
-    hipLaunchKernelGGL(bn_apply_kernel<bf16_t>, dim3(grid1d(n4)), dim3(256), 0, s, q_pre, n4, F, mean, rstd, gamma,
-                       beta, bn, static_cast<bf16_t*>(q));
+    hipLaunchKernelGGL(bn_apply_kernel<bf16_t>, grid, dim3(256), 0, s, q_pre, ntok, F, mean, rstd, gamma, beta, bn,
+                       static_cast<bf16_t*>(q));
   else
-    hipLaunchKernelGGL(bn_apply_kernel<float>, dim3(grid1d(n4)), dim3(256), 0, s, q_pre, n4, F, mean, rstd, gamma,
-                       beta, bn, static_cast<float*>(q));
+    hipLaunchKernelGGL(bn_apply_kernel<float>, grid, dim3(256), 0, s, q_pre, ntok, F, mean, rstd, gamma, beta, bn,
+                       static_cast<float*>(q));
   return hipGetLastError();
 }
 

@@ -184,8 +184,9 @@ __device__ __forceinline__ void vg_add_from(const LaneVecs<NVL>& lv, const float
   }
 }
 
-// MODE 0: one wave per row run of at most kVgChunk lookups (grid-stride over
-//         runs): the value row is read once, its gradient written once.
+// MODE 0: one wave per row run of at most kVgChunk lookups (a resident grid
+//         striding over the runs): the value row is read once, its gradient
+//         written once.
 // MODE 1: chunk j >= 1 of a long run: partial sum into its slot.
 // MODE 2: long run: chunk 0, plus the partial sums of chunks 1.. in order, into dV.
 template <typename T, int NVL, int MODE>
@@ -462,6 +463,23 @@ __global__ __launch_bounds__(256) void subkey_grad_kernel(SkArgs a) {
   }
 }
 
+// As many 256-thread blocks as the device holds at once, but no more than one
+// wave per item.
+unsigned resident_grid(const void* fn, int64_t items) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) != hipSuccess || per_cu < 1 || cus < 1) {
+    cus = 256;
+    per_cu = 2;
+  }
+  int64_t b = int64_t(cus) * per_cu;
+  const int64_t need = (items + 3) / 4;
+  if (b > need) b = need;
+  if (b < 1) b = 1;
+  return unsigned(b);
+}
+
 inline unsigned grid_waves(int64_t items, int64_t cap_blocks = 4096) {
   int64_t b = (items + 3) / 4;
   if (b > cap_blocks) b = cap_blocks;
@@ -510,10 +528,11 @@ hipError_t launch_value_grad(hipStream_t s, int dtype, const int32_t* seg_start,
   hipLaunchKernelGGL(long_run_plan_kernel, dim3(unsigned(pb)), dim3(256), 0, s, seg_start, nseg, kVgChunk,
                      static_cast<const uint32_t*>(nullptr), 0u, const_cast<int2*>(a.chunk_list),
                      const_cast<int32_t*>(a.long_list), counts);
-  const dim3 grid(grid_waves(nitems)), block(256);
+  const dim3 block(256);
   const dim3 grid_long(grid_waves(slots, 1024));
 #define PKM_VG(TT, NV)                                                                                    \
   do {                                                                                                    \
+    const dim3 grid(resident_grid(reinterpret_cast<const void*>(value_grad_kernel<TT, NV, 0>), nitems));  \
     hipLaunchKernelGGL((value_grad_kernel<TT, NV, 0>), grid, block, 0, s, a);                             \
     hipLaunchKernelGGL((value_grad_kernel<TT, NV, 1>), grid_long, block, 0, s, a);                        \
     hipLaunchKernelGGL((value_grad_kernel<TT, NV, 2>), grid_long, block, 0, s, a);                        \
