@@ -183,7 +183,7 @@ def main():
     # the per-half scoring + top-k kernel alone (its MFMA roofline)
     sub_idx = torch.empty((T, cfg.heads, 2, cfg.topk), dtype=torch.int32, device="cuda")
     sub_score = torch.empty((T, cfg.heads, 2, cfg.topk), dtype=torch.float32, device="cuda")
-    score_ms = timed(lambda: pkm_stage_score_topk(m.handle, T, saved["q"], C, Cp, sub_idx, sub_score), nf)
+    score_ms = timed(lambda: pkm_stage_score_topk(m.handle, T, saved["q"], C, Cp, sub_idx, sub_score, ws), nf)
     score_flops = 2.0 * T * cfg.heads * (cfg.n_keys + cfg.n_keys2) * (cfg.dq // 2)
     score_peak = MFMA_PEAK_TFLOPS[cfg.dtype]
     score_tf = score_flops / (score_ms * 1e-3) / 1e12

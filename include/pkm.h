@@ -154,9 +154,11 @@ pkm_status pkm_stage_query(pkm_handle_t handle, void* stream, int64_t T, const v
 /* Steps a3-a4: per head and half, scores of q's half against C (C') and the top-k.
  * q [T, h*dq] storage dtype.  Outputs sub_idx int32 and sub_score fp32, both
  * [T, h, 2, k]: [..., 0, :] from C, [..., 1, :] from C', each ordered by
- * (score desc, index asc). */
+ * (score desc, index asc).  ws >= pkm_workspace_size(handle, T, 0) (holds the
+ * sub-keys repacked for the matrix cores). */
 pkm_status pkm_stage_score_topk(pkm_handle_t handle, void* stream, int64_t T, const void* q,
-                                const void* C, const void* Cp, int32_t* sub_idx, float* sub_score);
+                                const void* C, const void* Cp, int32_t* sub_idx, float* sub_score,
+                                void* ws, size_t ws_bytes);
 
 /* Step a5: from sorted per-half lists [T, h, 2, k] (as written by the stage
  * above), the k best of the k x k candidates and their softmax weights:

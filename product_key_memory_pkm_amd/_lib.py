@@ -53,7 +53,7 @@ _SIGS = {
     "pkm_backward": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_saved), _VP, _VP, _VP,
                      _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
     "pkm_stage_query": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_saved), _VP, _SZ],
-    "pkm_stage_score_topk": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP],
+    "pkm_stage_score_topk": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
     "pkm_stage_merge_softmax": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP],
     "pkm_stage_gather": [_VP, _VP, _I64, _VP, _VP, _VP, _VP],
     "pkm_stage_value_grad": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
@@ -196,11 +196,11 @@ def pkm_stage_query(h, T, x, Wq, bn_gamma, bn_beta, saved: dict, ws):
                                  ctypes.byref(sv), _ptr(ws), _nbytes(ws)), "pkm_stage_query")
 
 
-def pkm_stage_score_topk(h, T, q, C, Cp, sub_idx, sub_score):
+def pkm_stage_score_topk(h, T, q, C, Cp, sub_idx, sub_score, ws):
     _dt(sub_idx, torch.int32, "sub_idx")
     _dt(sub_score, torch.float32, "sub_score")
     _check(_invoke("pkm_stage_score_topk", h, T, _ptr(q), _ptr(C), _ptr(Cp), _ptr(sub_idx),
-                                      _ptr(sub_score)), "pkm_stage_score_topk")
+                   _ptr(sub_score), _ptr(ws), _nbytes(ws)), "pkm_stage_score_topk")
 
 
 def pkm_stage_merge_softmax(h, T, sub_idx, sub_score, idx, w, score=None):

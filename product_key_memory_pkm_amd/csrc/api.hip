@@ -64,7 +64,7 @@ int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 // backward layout never needs the forward's regions, so one buffer of the
 // larger size serves both.
 struct FwdLayout {
-  size_t sub_idx, sub_score, bn_part, total;
+  size_t sub_idx, sub_score, bn_part, keys, total;
 };
 struct BwdLayout {
   size_t k0, v0, k1, v1, sort_tmp, flags, pos, seg_flags, seg_pos, seg, scan_tmp, nseg, dw, ds, coef2, dq, bn_part,
@@ -82,6 +82,7 @@ FwdLayout fwd_layout(const pkm_handle_s* h, int64_t T) {
   L.sub_score = o; o += al(nsub * 4);
   const size_t nblk = size_t((T + kBnRows - 1) / kBnRows);
   L.bn_part = o;  o += al(nblk * 2 * h->F * sizeof(double));
+  L.keys = o;     o += al(score_topk_packed_bytes(c.dtype, c.heads, h->half, c.n_keys, c.n_keys2));
   L.total = o;
   return L;
 }
@@ -190,10 +191,11 @@ pkm_status run_query(const pkm_handle_s* h, hipStream_t s, int64_t T, const void
 }
 
 pkm_status run_score(const pkm_handle_s* h, hipStream_t s, int64_t T, const void* q, const void* C, const void* Cp,
-                     int32_t* sub_idx, float* sub_score) {
+                     int32_t* sub_idx, float* sub_score, void* ws) {
   const pkm_config& c = h->cfg;
+  const FwdLayout L = fwd_layout(h, T);
   PKM_HIP(launch_score_topk(s, c.dtype, q, T, c.heads, c.d_query, C, Cp, c.n_keys, c.n_keys2, c.topk, sub_idx,
-                            sub_score),
+                            sub_score, at<void>(ws, L.keys)),
           "sub-key scoring / top-k");
   return PKM_OK;
 }
@@ -474,7 +476,7 @@ pkm_status pkm_forward(pkm_handle_t handle, void* stream, int64_t T, const void*
   int32_t* sub_idx = at<int32_t>(ws, L.sub_idx);
   float* sub_score = at<float>(ws, L.sub_score);
   PKM_TRY(run_query(handle, s, T, x, Wq, bn_gamma, bn_beta, saved, ws));
-  PKM_TRY(run_score(handle, s, T, saved->q, C, Cp, sub_idx, sub_score));
+  PKM_TRY(run_score(handle, s, T, saved->q, C, Cp, sub_idx, sub_score, ws));
   PKM_TRY(run_merge(handle, s, T, sub_idx, sub_score, saved->idx, saved->w, nullptr));
   PKM_TRY(run_gather(handle, s, T, saved->idx, saved->w, V, y));
   return PKM_OK;
@@ -537,7 +539,7 @@ pkm_status pkm_stage_query(pkm_handle_t handle, void* stream, int64_t T, const v
 }
 
 pkm_status pkm_stage_score_topk(pkm_handle_t handle, void* stream, int64_t T, const void* q, const void* C,
-                                const void* Cp, int32_t* sub_idx, float* sub_score) {
+                                const void* Cp, int32_t* sub_idx, float* sub_score, void* ws, size_t ws_bytes) {
   PKM_TRY(check_handle(handle));
   PKM_TRY(check_T(handle, T));
   PKM_TRY(need(q, "q"));
@@ -545,8 +547,9 @@ pkm_status pkm_stage_score_topk(pkm_handle_t handle, void* stream, int64_t T, co
   PKM_TRY(need(Cp, "Cp"));
   PKM_TRY(need(sub_idx, "sub_idx"));
   PKM_TRY(need(sub_score, "sub_score"));
+  PKM_TRY(check_ws(handle, T, 0, ws, ws_bytes));
   if (T == 0) return PKM_OK;
-  return run_score(handle, as_stream(stream), T, q, C, Cp, sub_idx, sub_score);
+  return run_score(handle, as_stream(stream), T, q, C, Cp, sub_idx, sub_score, ws);
 }
 
 pkm_status pkm_stage_merge_softmax(pkm_handle_t handle, void* stream, int64_t T, const int32_t* sub_idx,

@@ -15,11 +15,13 @@ hipError_t launch_gather(hipStream_t s, int dtype, const int32_t* idx, const flo
                          void* y, int64_t ntok, int R, int d_value);
 
 // a3 + a4: per (token, head, half) scores against the half's sub-keys and top-k.
+// packed: score_topk_packed_bytes of scratch for the repacked sub-keys.
 // Returns hipErrorInvalidValue when the shape does not fit the kernel's LDS plan.
 bool score_topk_supported(int dtype, int half, int nkeys);
+size_t score_topk_packed_bytes(int dtype, int heads, int half, int nk, int nk2);
 hipError_t launch_score_topk(hipStream_t s, int dtype, const void* q, int64_t ntok, int heads, int dq,
                              const void* C, const void* Cp, int nk, int nk2, int k, int32_t* sub_idx,
-                             float* sub_score);
+                             float* sub_score, void* packed);
 
 // a5: k x k candidates -> top-k -> softmax, per (token, head).
 hipError_t launch_merge_softmax(hipStream_t s, const int32_t* sub_idx, const float* sub_score,

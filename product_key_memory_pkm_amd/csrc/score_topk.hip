@@ -11,8 +11,12 @@
 //  1. The TM x dq/2 query tile is staged in LDS.
 //  2. MFMA (bf16 16x16x32 or fp32 16x16x4, fp32 accumulation): each wave owns
 //     16-column tiles of the TM x |C| score tile and streams its sub-key rows
-//     from global memory (the codebooks are small and stay in L2); the scores
-//     land in LDS and never reach HBM.
+//     from L2 (the codebooks are small); the scores land in LDS and never
+//     reach HBM.  The sub-keys are first repacked so that the 64 lane
+//     fragments of one (16-key tile, k step) operand are one contiguous 1 KB
+//     block: the operand read in MFMA order would touch 16 half-used cache
+//     lines per instruction, which the texture path serves at about a third
+//     of the rate of a contiguous read.
 //  3. Selection: each wave owns TM/8 rows and works on them together (their
 //     dependency chains overlap).  A lane holds |C|/64 scores of a row; the
 //     k-th largest of the 64 lane maxima (bisection on order-preserving keys,
@@ -231,10 +235,34 @@ __device__ __forceinline__ uint64_t merge_top32(uint64_t a, uint64_t b, int lane
   return x;
 }
 
+// Packed operand layout, per codebook: [h][ceil(n/16) tiles][ksteps][64 lanes]
+// 16-byte fragments; lane (r, g) of (tile, kstep) holds row tile*16 + r,
+// elements kstep*KC + g*VE .. +VE (zeros past the last row or element).
+template <typename T>
+__global__ __launch_bounds__(256) void pack_keys_kernel(const T* __restrict__ C, int heads, int n, int half,
+                                                        int nks, u32x4* __restrict__ out) {
+  using TR = ScoreTraits<T>;
+  const int ntile = (n + 15) / 16;
+  const int64_t total = int64_t(heads) * ntile * nks * 64;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < total; i += int64_t(gridDim.x) * 256) {
+    const int lane = int(i & 63);
+    const int64_t fr = i >> 6;
+    const int ks = int(fr % nks);
+    const int64_t tl = fr / nks;
+    const int tile = int(tl % ntile);
+    const int hh = int(tl / ntile);
+    const int row = tile * 16 + (lane & 15);
+    const int kk = ks * TR::KC + (lane >> 4) * TR::VE;
+    u32x4 v = {0, 0, 0, 0};
+    if (row < n && kk < half) v = ld16(C + (size_t(hh) * n + row) * half + kk);
+    out[i] = v;
+  }
+}
+
 template <typename T, int TM, int NPL>
 __global__ __launch_bounds__(kThreads) void score_topk_kernel(
     const T* __restrict__ q, int64_t ntok, int F, int dq, int half, int half_pad, int qstride,
-    const T* __restrict__ C, const T* __restrict__ Cp, int nk, int nk2, int k, int cw, int sstride,
+    const u32x4* __restrict__ P1, const u32x4* __restrict__ P2, int nk, int nk2, int k, int cw, int sstride,
     int32_t* __restrict__ sub_idx, float* __restrict__ sub_score) {
   using TR = ScoreTraits<T>;
   constexpr int VE = TR::VE;
@@ -253,7 +281,9 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(
   const int p = blockIdx.z;
   const int heads = gridDim.y;
   const int ncols = p ? nk2 : nk;
-  const T* keys = (p ? Cp : C) + size_t(hh) * ncols * half;
+  const int ntile = (ncols + 15) / 16;
+  const int nks = half_pad / KC;
+  const u32x4* keys = (p ? P2 : P1) + size_t(hh) * ntile * nks * 64;
   const int64_t t0 = int64_t(blockIdx.x) * TM;
 
   // 1. query tile -> LDS (zero rows past the last token and k past dq/2)
@@ -286,29 +316,25 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(
 #pragma unroll
         for (int c = 0; c < CT; ++c) acc[rt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-      const T* kb[CT];
-      bool colok[CT];
+      // this wave's tiles; tiles past the chunk are clamped (their columns are never stored)
+      const u32x4* kb[CT];
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
-        const int col = (g0 + c) * 16 + lrow;
-        colok[c] = col < cwe;
-        kb[c] = keys + size_t(cb + (colok[c] ? col : 0)) * half;
+        int tile = cb / 16 + g0 + c;
+        tile = tile < ntile ? tile : ntile - 1;
+        kb[c] = keys + size_t(tile) * nks * 64 + lane;
       }
       u32x4 bcur[CT];
 #pragma unroll
-      for (int c = 0; c < CT; ++c) {
-        const int kk = lgrp * VE;
-        bcur[c] = (colok[c] && kk < half) ? ld16(kb[c] + kk) : u32x4{0, 0, 0, 0};
-      }
-      for (int kc = 0; kc < half_pad; kc += KC) {
+      for (int c = 0; c < CT; ++c) bcur[c] = kb[c][0];
+      for (int ks = 0; ks < nks; ++ks) {
         u32x4 bnext[CT];
-        const int kn = kc + KC + lgrp * VE;
+        const int kn = ks + 1 < nks ? ks + 1 : ks;
 #pragma unroll
-        for (int c = 0; c < CT; ++c)
-          bnext[c] = (kc + KC < half_pad && colok[c] && kn < half) ? ld16(kb[c] + kn) : u32x4{0, 0, 0, 0};
+        for (int c = 0; c < CT; ++c) bnext[c] = kb[c][size_t(kn) * 64];
         u32x4 a[RT];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) a[rt] = ld16(qt + size_t(rt * 16 + lrow) * qstride + kc + lgrp * VE);
+        for (int rt = 0; rt < RT; ++rt) a[rt] = ld16(qt + size_t(rt * 16 + lrow) * qstride + ks * KC + lgrp * VE);
 #pragma unroll
         for (int c = 0; c < CT; ++c)
 #pragma unroll
@@ -416,8 +442,8 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(
 }
 
 template <typename T, int TM>
-void launch_tm(hipStream_t s, const Plan& pl, const void* q, int64_t ntok, int heads, int dq, const void* C,
-               const void* Cp, int nk, int nk2, int k, int32_t* sub_idx, float* sub_score) {
+void launch_tm(hipStream_t s, const Plan& pl, const void* q, int64_t ntok, int heads, int dq, const u32x4* C,
+               const u32x4* Cp, int nk, int nk2, int k, int32_t* sub_idx, float* sub_score) {
   const int half = dq / 2;
   const int F = heads * dq;
   dim3 grid(unsigned((ntok + TM - 1) / TM), unsigned(heads), 2u);
@@ -428,7 +454,7 @@ void launch_tm(hipStream_t s, const Plan& pl, const void* q, int64_t ntok, int h
       hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, \
                           int(pl.lds));                                                               \
       hipLaunchKernelGGL(fn, grid, dim3(kThreads), pl.lds, s, static_cast<const T*>(q), ntok, F, dq, half, \
-                         pl.half_pad, pl.qstride, static_cast<const T*>(C), static_cast<const T*>(Cp), nk, \
+                         pl.half_pad, pl.qstride, C, Cp, nk,                                           \
                          nk2, k, pl.cw, pl.sstride, sub_idx, sub_score);                             \
     }                                                                                                 \
   } break;
@@ -445,8 +471,8 @@ void launch_tm(hipStream_t s, const Plan& pl, const void* q, int64_t ntok, int h
 }
 
 template <typename T>
-void launch_t(hipStream_t s, const Plan& pl, const void* q, int64_t ntok, int heads, int dq, const void* C,
-              const void* Cp, int nk, int nk2, int k, int32_t* sub_idx, float* sub_score) {
+void launch_t(hipStream_t s, const Plan& pl, const void* q, int64_t ntok, int heads, int dq, const u32x4* C,
+              const u32x4* Cp, int nk, int nk2, int k, int32_t* sub_idx, float* sub_score) {
   if (pl.TM == 64)
     launch_tm<T, 64>(s, pl, q, ntok, heads, dq, C, Cp, nk, nk2, k, sub_idx, sub_score);
   else if (pl.TM == 32)
@@ -463,15 +489,39 @@ bool score_topk_supported(int dtype, int half, int nkeys) {
   return p.TM != 0;
 }
 
+size_t score_topk_packed_bytes(int dtype, int heads, int half, int nk, int nk2) {
+  const int KC = dtype == kBF16 ? 32 : 16;
+  const size_t nks = size_t(round_up(half, KC) / KC);
+  return size_t(heads) * (size_t((nk + 15) / 16) + size_t((nk2 + 15) / 16)) * nks * 64 * 16;
+}
+
 hipError_t launch_score_topk(hipStream_t s, int dtype, const void* q, int64_t ntok, int heads, int dq,
                              const void* C, const void* Cp, int nk, int nk2, int k, int32_t* sub_idx,
-                             float* sub_score) {
-  const Plan pl = make_plan(dtype, dq / 2, nk > nk2 ? nk : nk2);
+                             float* sub_score, void* packed) {
+  const int half = dq / 2;
+  const Plan pl = make_plan(dtype, half, nk > nk2 ? nk : nk2);
   if (pl.TM == 0 || pl.npl > 16) return hipErrorInvalidValue;
+  const int KC = dtype == kBF16 ? 32 : 16;
+  const int nks = pl.half_pad / KC;
+  u32x4* P1 = static_cast<u32x4*>(packed);
+  u32x4* P2 = P1 + size_t(heads) * ((nk + 15) / 16) * nks * 64;
+  auto pack = [&](const void* src, int n, u32x4* dst) {
+    const int64_t total = int64_t(heads) * ((n + 15) / 16) * nks * 64;
+    int64_t b = (total + 255) / 256;
+    if (b > 4096) b = 4096;
+    if (dtype == kBF16)
+      hipLaunchKernelGGL(pack_keys_kernel<bf16_t>, dim3(unsigned(b)), dim3(256), 0, s,
+                         static_cast<const bf16_t*>(src), heads, n, half, nks, dst);
+    else
+      hipLaunchKernelGGL(pack_keys_kernel<float>, dim3(unsigned(b)), dim3(256), 0, s,
+                         static_cast<const float*>(src), heads, n, half, nks, dst);
+  };
+  pack(C, nk, P1);
+  pack(Cp, nk2, P2);
   if (dtype == kBF16)
-    launch_t<bf16_t>(s, pl, q, ntok, heads, dq, C, Cp, nk, nk2, k, sub_idx, sub_score);
+    launch_t<bf16_t>(s, pl, q, ntok, heads, dq, P1, P2, nk, nk2, k, sub_idx, sub_score);
   else
-    launch_t<float>(s, pl, q, ntok, heads, dq, C, Cp, nk, nk2, k, sub_idx, sub_score);
+    launch_t<float>(s, pl, q, ntok, heads, dq, P1, P2, nk, nk2, k, sub_idx, sub_score);
   return hipGetLastError();
 }
 

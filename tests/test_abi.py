@@ -146,7 +146,8 @@ def test_backward_and_stage_argument_errors():
                           ok[9], ok[10], ok[11], ok[12], ok[13], ok[14], ok[15], None, ok[16], 16)
     assert st == L.PKM_ERR_WORKSPACE
     assert lib.pkm_stage_gather(h.ptr, None, 4, ok[1], None, ok[3], ok[4]) == L.PKM_ERR_INVALID_ARG
-    assert lib.pkm_stage_score_topk(h.ptr, None, 4, ok[1], ok[2], None, ok[4], ok[5]) == L.PKM_ERR_INVALID_ARG
+    assert lib.pkm_stage_score_topk(h.ptr, None, 4, ok[1], ok[2], None, ok[4], ok[5], ok[6], 1 << 30) == \
+        L.PKM_ERR_INVALID_ARG
     assert lib.pkm_stage_merge_softmax(h.ptr, None, 4, ok[1], ok[2], ok[3], ctypes.c_void_p(FAKE + 4),
                                        None) == L.PKM_ERR_INVALID_ARG
     assert lib.pkm_stage_value_grad(h.ptr, None, 4, ok[1], ok[2], ok[3], ok[4], ok[5], ok[6], ok[7], ok[8], ok[9],

@@ -108,7 +108,7 @@ def test_score_topk_stage(T, h, dq, nk, nk2, k, dtype, integer):
     from product_key_memory_pkm_amd import pkm_stage_score_topk
     si = torch.empty((T, h, 2, k), dtype=torch.int32, device="cuda")
     ss = torch.empty((T, h, 2, k), dtype=torch.float32, device="cuda")
-    pkm_stage_score_topk(layer.handle, T, to_dev(q), to_dev(C), to_dev(Cp), si, ss)
+    pkm_stage_score_topk(layer.handle, T, to_dev(q), to_dev(C), to_dev(Cp), si, ss, layer.workspace(T, False))
     torch.cuda.synchronize()
     si, ss = si.cpu().numpy(), ss.cpu().numpy()
     qd, Cd, Cpd = O.decode(q, dtype), O.decode(C, dtype), O.decode(Cp, dtype)
