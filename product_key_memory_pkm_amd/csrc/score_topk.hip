@@ -97,6 +97,23 @@ __device__ __forceinline__ int wave_excl_scan_dpp(int v, int* total) {
   return x - v;
 }
 
+// Value of lane (lane ^ stride): DPP quad permutes for strides 1 and 2,
+// ds_swizzle (xor within 32 lanes, no address register) for 4..16, a
+// bpermute for 32.  stride is a constant once the callers' loops unroll.
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v, int stride) {
+  switch (stride) {
+    case 1: return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+    case 2: return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+    case 4: return uint32_t(__builtin_amdgcn_ds_swizzle(int(v), (4 << 10) | 0x1F));
+    case 8: return uint32_t(__builtin_amdgcn_ds_swizzle(int(v), (8 << 10) | 0x1F));
+    case 16: return uint32_t(__builtin_amdgcn_ds_swizzle(int(v), (16 << 10) | 0x1F));
+    default: return uint32_t(__shfl_xor(int(v), stride, 64));
+  }
+}
+__device__ __forceinline__ uint64_t xor_lane_u64(uint64_t v, int stride) {
+  return (uint64_t(xor_lane(uint32_t(v >> 32), stride)) << 32) | xor_lane(uint32_t(v), stride);
+}
+
 // Bitonic sort, descending, of N independent uint64 values per lane across the wave.
 template <int N>
 __device__ __forceinline__ void wave_sort_desc_u64_n(uint64_t* v) {
@@ -108,51 +125,50 @@ __device__ __forceinline__ void wave_sort_desc_u64_n(uint64_t* v) {
       const bool take_max = ((lane & stride) == 0) == ((lane & size) == 0);
 #pragma unroll
       for (int q = 0; q < N; ++q) {
-        const uint64_t o = shfl_xor_u64(v[q], stride);
-        const uint64_t mx = v[q] > o ? v[q] : o;
-        const uint64_t mn = v[q] > o ? o : v[q];
-        v[q] = take_max ? mx : mn;
+        const uint64_t o = xor_lane_u64(v[q], stride);
+        const bool gt = v[q] > o;
+        v[q] = (gt == take_max) ? v[q] : o;
       }
     }
   }
 }
 
-// Exact top-k of one row held as NPL scores per lane (column j*64 + lane),
-// written as (key, ~column) words into slot[0..k): the k-th largest key by
-// bisection over all columns, every larger key, then equal keys by lowest column.
+// Column of a row's j-th value in a lane: 16-byte runs of 4 consecutive
+// columns per lane when a lane holds at least 4 values (one ds_read_b128 per
+// run), else one column per 64.
+template <int NPL>
+__device__ __forceinline__ int col_of(int j, int lane) {
+  return NPL >= 4 ? 256 * (j >> 2) + 4 * lane + (j & 3) : j * 64 + lane;
+}
+
+// Exact top-k of one row held as NPL scores per lane (column col0 +
+// col_of(j, lane)), written as (key, ~column) words into slot[0..k): the
+// words are distinct, so the k-th largest word (bisection over all 64 bits,
+// counts by ballot) splits off exactly the k best, ties going to the lowest
+// column.  The fallback for rows where heavy ties defeat the cheap bound.
 template <int NPL>
 __device__ __forceinline__ void exact_topk(const float* v, int k, int lane, uint32_t col0, uint64_t* slot) {
-  uint32_t key[NPL];
-#pragma unroll
-  for (int j = 0; j < NPL; ++j) key[j] = v[j] == -INFINITY ? 0u : float_key(v[j]);
-  uint32_t res = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t cand = res | (1u << b);
-    int c = 0;
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) c += key[j] >= cand;
-    if (wave_sum_i(c) >= k) res = cand;
-  }
-  int gt = 0;
-#pragma unroll
-  for (int j = 0; j < NPL; ++j) gt += key[j] > res;
-  int gt_total;
-  int gpos = wave_excl_scan(gt, &gt_total);
+  uint64_t key[NPL];
 #pragma unroll
   for (int j = 0; j < NPL; ++j)
-    if (key[j] > res) slot[gpos++] = (uint64_t(key[j]) << 32) | uint32_t(~(col0 + uint32_t(j * 64 + lane)));
-  int remaining = k - gt_total;
-  int base = gt_total;
+    key[j] = v[j] == -INFINITY ? 0ull
+                               : (uint64_t(float_key(v[j])) << 32) | uint32_t(~(col0 + uint32_t(col_of<NPL>(j, lane))));
+  uint64_t res = 0;
+  for (int b = 63; b >= 0; --b) {
+    const uint64_t cand = res | (1ull << b);
+    int c = 0;
 #pragma unroll
-  for (int j = 0; j < NPL; ++j) {
-    const bool eq = key[j] == res;
-    const uint64_t m = ballot(eq);
-    const int rk = lanes_below(m);
-    if (eq && rk < remaining) slot[base + rk] = (uint64_t(key[j]) << 32) | uint32_t(~(col0 + uint32_t(j * 64 + lane)));
-    const int taken = min(popc64(m), remaining);
-    base += taken;
-    remaining -= taken;
+    for (int j = 0; j < NPL; ++j) c += popc64(ballot(key[j] >= cand));
+    if (c >= k) res = cand;
   }
+  int mine = 0;
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) mine += key[j] >= res;
+  int tot;
+  int pos = wave_excl_scan(mine, &tot);
+#pragma unroll
+  for (int j = 0; j < NPL; ++j)
+    if (key[j] >= res) slot[pos++] = key[j];
 }
 
 struct Plan {
@@ -226,11 +242,10 @@ __device__ __forceinline__ uint64_t merge_top32(uint64_t a, uint64_t b, int lane
   uint64_t x = lane < 32 ? (a > br ? a : br) : 0ull;
 #pragma unroll
   for (int stride = 16; stride > 0; stride >>= 1) {
-    const uint64_t o = shfl_xor_u64(x, stride);
+    const uint64_t o = xor_lane_u64(x, stride);
     const bool take_max = (lane & stride) == 0;
-    const uint64_t mx = x > o ? x : o;
-    const uint64_t mn = x > o ? o : x;
-    x = take_max ? mx : mn;
+    const bool gt = x > o;
+    x = (gt == take_max) ? x : o;
   }
   return x;
 }
@@ -364,12 +379,24 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(
     for (int q = 0; q < RPW; ++q) {
       const float* srow = S + size_t(q * kWaves + wave) * sstride;
       lmax[q] = -INFINITY;
+      if constexpr (NPL >= 4) {
 #pragma unroll
-      for (int j = 0; j < NPL; ++j) {
-        const int col = j * 64 + lane;
-        v[q][j] = col < cwe ? srow[col] : -INFINITY;
-        lmax[q] = fmaxf(lmax[q], v[q][j]);
+        for (int jj = 0; jj < NPL / 4; ++jj) {
+          const int c0 = 256 * jj + 4 * lane;  // a run starting below cwe ends inside the row (sstride >= cw + 4)
+          f32x4 t = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+          if (c0 < cwe) t = *reinterpret_cast<const f32x4*>(srow + c0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[q][4 * jj + e] = c0 + e < cwe ? t[e] : -INFINITY;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) {
+          const int col = j * 64 + lane;
+          v[q][j] = col < cwe ? srow[col] : -INFINITY;
+        }
       }
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) lmax[q] = fmaxf(lmax[q], v[q][j]);
     }
     // k-th largest lane maximum (a lower bound of the row's k-th largest score):
     // bisection on order-preserving keys, with ballots
@@ -397,29 +424,35 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(
       for (int j = 0; j < NPL; ++j) cnt[q] += v[q][j] >= thr;
       pos[q] = wave_excl_scan_dpp(cnt[q], &total[q]);
     }
-    // compaction into the row's own LDS slot (its scores are in registers now);
-    // rows with more than 64 survivors (heavy ties) take the exact path below
+    // compaction into the row's own LDS slot (its scores are in registers now)
+    // as (score bits, column) pairs; rows with more than 64 survivors (heavy
+    // ties) take the exact path, which writes finished (key, ~column) words
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int q = 0; q < RPW; ++q) {
-      uint64_t* slot = reinterpret_cast<uint64_t*>(S + size_t(q * kWaves + wave) * sstride);
       const float thr = key_float(res[q]);
       if (total[q] <= 64) {
+        u32x2* slot = reinterpret_cast<u32x2*>(S + size_t(q * kWaves + wave) * sstride);
 #pragma unroll
         for (int j = 0; j < NPL; ++j)
-          if (v[q][j] >= thr)
-            slot[pos[q]++] = (uint64_t(float_key(v[q][j])) << 32) | uint32_t(~(uint32_t(cb) + uint32_t(j * 64 + lane)));
+          if (v[q][j] >= thr) slot[pos[q]++] = u32x2{__float_as_uint(v[q][j]), uint32_t(col_of<NPL>(j, lane))};
       } else {
-        exact_topk<NPL>(v[q], kc_, lane, uint32_t(cb), slot);
-        total[q] = kc_;
+        exact_topk<NPL>(v[q], kc_, lane, uint32_t(cb), reinterpret_cast<uint64_t*>(S + size_t(q * kWaves + wave) * sstride));
       }
     }
     wave_lds_sync();
     uint64_t key[RPW];
 #pragma unroll
     for (int q = 0; q < RPW; ++q) {
-      const uint64_t* slot = reinterpret_cast<const uint64_t*>(S + size_t(q * kWaves + wave) * sstride);
-      key[q] = lane < total[q] ? slot[lane] : 0ull;
+      const u32x2* slot = reinterpret_cast<const u32x2*>(S + size_t(q * kWaves + wave) * sstride);
+      if (total[q] <= 64) {
+        const u32x2 e = lane < total[q] ? slot[lane] : u32x2{0u, 0u};
+        key[q] = lane < total[q]
+                     ? (uint64_t(float_key(__uint_as_float(e.x))) << 32) | uint32_t(~(uint32_t(cb) + e.y))
+                     : 0ull;
+      } else {
+        key[q] = lane < kc_ ? reinterpret_cast<const uint64_t*>(slot)[lane] : 0ull;
+      }
     }
     wave_sort_desc_u64_n<RPW>(key);
 #pragma unroll
