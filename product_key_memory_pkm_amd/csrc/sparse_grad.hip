@@ -16,11 +16,11 @@
 // w*dY into the row's fp32 gradient, which is written (or added) once.  The
 // sub-key gradients use the same grouping keyed by sub-key.  A skewed workload
 // makes some runs very long (thousands of lookups of one row, 10^5 of one
-// sub-key); those are cut into fixed chunks that run in parallel, each chunk's
-// partial sum landing in a slot named by its start position (distinct for all
-// chunks), and one wave or block per long run adds them up in chunk order.
-// Every sum thus has a fixed order, so results are bit-identical from run to
-// run.
+// sub-key); a plan kernel cuts those into fixed chunks, which the main launch
+// processes first and in parallel with the short runs, each chunk's partial
+// sum landing in its own slot; a short combine pass then adds each long run's
+// slots in chunk order.  Every sum thus has a fixed order, so results are
+// bit-identical from run to run.
 #include "common.h"
 #include "kernels.h"
 
@@ -73,10 +73,10 @@ struct VgArgs {
   int nvec;    // 16-byte vectors per row
   int accumulate;
   // long rows
-  const int2* chunk_list;   // (row run u, chunk j >= 1)
-  const int32_t* long_list; // row runs longer than kVgChunk
+  const int2* chunk_list;   // (row run u, chunk j): list entry i owns partial slot i
+  const int2* long_list;    // (row run u, first slot) of every run longer than kVgChunk
   const uint32_t* counts;   // [0] chunks listed, [1] long runs listed
-  float* partial;           // [N / kVgChunk + 1, d_v]: slot of the chunk starting at s is s / kVgChunk
+  float* partial;           // [2 N / kVgChunk + 2, d_v] partial sums
 };
 
 // The wave's lanes own 16-byte vectors l, l+64, ... of a row; the first NVL-1
@@ -184,11 +184,11 @@ __device__ __forceinline__ void vg_add_from(const LaneVecs<NVL>& lv, const float
   }
 }
 
-// MODE 0: one wave per row run of at most kVgChunk lookups (a resident grid
-//         striding over the runs): the value row is read once, its gradient
-//         written once.
-// MODE 1: chunk j >= 1 of a long run: partial sum into its slot.
-// MODE 2: long run: chunk 0, plus the partial sums of chunks 1.. in order, into dV.
+// MODE 0: one wave per work item, a resident grid striding over the items:
+//         first the chunks of the long runs (partial sums into their slots),
+//         then the runs of at most kVgChunk lookups, whose value row is read
+//         once and gradient row written (or added) once.
+// MODE 1: one wave per long run: its slots added in chunk order into dV.
 template <typename T, int NVL, int MODE>
 __global__ __launch_bounds__(256) void value_grad_kernel(VgArgs a) {
   constexpr int E = Vec16<T>::N;
@@ -197,18 +197,37 @@ __global__ __launch_bounds__(256) void value_grad_kernel(VgArgs a) {
   const int64_t nw = (int64_t(gridDim.x) * blockDim.x) >> 6;
   const int dv = a.nvec * E;
   const LaneVecs<NVL> lv(a.nvec, lane);
-  const int64_t nitems = MODE == 0 ? *a.nseg : int64_t(a.counts[MODE - 1]);
+  if (MODE == 1) {
+    const int64_t nlong = a.counts[1];
+    for (int64_t it = gw; it < nlong; it += nw) {
+      const int2 e = a.long_list[it];
+      const int lo = a.seg_start[e.x], hi = a.seg_start[e.x + 1];
+      const uint32_t r = a.sorted_rows[lo];
+      float g[NVL][E];
+#pragma unroll
+      for (int m = 0; m < NVL; ++m)
+#pragma unroll
+        for (int q = 0; q < E; ++q) g[m][q] = 0.f;
+      const int nch = (hi - lo + kVgChunk - 1) / kVgChunk;
+      for (int j = 0; j < nch; ++j) vg_add_from<T, NVL>(lv, a.partial + size_t(e.y + j) * dv, g);
+      vg_store<T, NVL>(lv, a.dV + size_t(r) * dv, g, a.accumulate != 0);
+    }
+    return;
+  }
+  const int64_t nchunks = a.counts[0];
+  const int64_t nitems = nchunks + *a.nseg;
   for (int64_t it = gw; it < nitems; it += nw) {
+    const bool chunk = it < nchunks;  // wave-uniform
     int u, j = 0;
-    if (MODE == 1) {
+    if (chunk) {
       const int2 e = a.chunk_list[it];
       u = e.x;
       j = e.y;
     } else {
-      u = MODE == 0 ? int(it) : a.long_list[it];
+      u = int(it - nchunks);
     }
     const int lo = a.seg_start[u], hi = a.seg_start[u + 1];
-    if (MODE == 0 && hi - lo > kVgChunk) continue;  // wave-uniform: long runs go through MODE 1/2
+    if (!chunk && hi - lo > kVgChunk) continue;  // wave-uniform: listed as chunks
     const uint32_t r = a.sorted_rows[lo];
     u32x4 vr[NVL];
     vg_load_row<T, NVL>(a, lv, r, vr);
@@ -216,29 +235,27 @@ __global__ __launch_bounds__(256) void value_grad_kernel(VgArgs a) {
 #pragma unroll
     for (int m = 0; m < NVL; ++m)
 #pragma unroll
-      for (int e = 0; e < E; ++e) g[m][e] = 0.f;
+      for (int q = 0; q < E; ++q) g[m][q] = 0.f;
     const int clo = lo + j * kVgChunk;
-    const int chi = MODE == 0 ? hi : min(hi, clo + kVgChunk);
+    const int chi = chunk ? min(hi, clo + kVgChunk) : hi;
     vg_accumulate<T, NVL>(a, lv, vr, clo, chi, g);
-    if (MODE == 1) {
-      vg_store<T, NVL>(lv, a.partial + size_t(clo / kVgChunk) * dv, g, false);
-    } else {
-      if (MODE == 2)
-        for (int s = lo + kVgChunk; s < hi; s += kVgChunk) vg_add_from<T, NVL>(lv, a.partial + size_t(s / kVgChunk) * dv, g);
+    if (chunk)
+      vg_store<T, NVL>(lv, a.partial + size_t(it) * dv, g, false);
+    else
       vg_store<T, NVL>(lv, a.dV + size_t(r) * dv, g, a.accumulate != 0);
-    }
   }
 }
 
-// Lists the runs longer than `chunk` entries and their chunks j >= 1 (list
-// order is free: every chunk's output slot and the combine order depend only on
-// the run itself).  Runs whose key is >= nvalid are skipped (keys == nullptr:
-// none is).
+// Lists the runs longer than `chunk` entries, every chunk of them (run u,
+// chunk j) in chunk_list and (u, first list entry) in long_list.  List order
+// is free: a chunk's partial sum goes to the slot of its list entry and a long
+// run adds its slots in chunk order, so results do not depend on it.  Runs
+// whose key is >= nvalid are skipped (keys == nullptr: none is).
 __global__ __launch_bounds__(256) void long_run_plan_kernel(const int32_t* __restrict__ seg_start,
                                                             const int64_t* __restrict__ nseg_p, int chunk,
                                                             const uint32_t* __restrict__ keys, uint32_t nvalid,
                                                             int2* __restrict__ chunk_list,
-                                                            int32_t* __restrict__ long_list,
+                                                            int2* __restrict__ long_list,
                                                             uint32_t* __restrict__ counts) {
   const int64_t nseg = *nseg_p;
   for (int64_t u = int64_t(blockIdx.x) * 256 + threadIdx.x; u < nseg; u += int64_t(gridDim.x) * 256) {
@@ -246,9 +263,9 @@ __global__ __launch_bounds__(256) void long_run_plan_kernel(const int32_t* __res
     const int len = seg_start[u + 1] - lo;
     if (len > chunk && (keys == nullptr || keys[lo] < nvalid)) {
       const int nch = (len + chunk - 1) / chunk;
-      const uint32_t base = atomicAdd(&counts[0], uint32_t(nch - 1));
-      for (int j = 1; j < nch; ++j) chunk_list[base + j - 1] = make_int2(int(u), j);
-      long_list[atomicAdd(&counts[1], 1u)] = int(u);
+      const uint32_t base = atomicAdd(&counts[0], uint32_t(nch));
+      for (int j = 0; j < nch; ++j) chunk_list[base + j] = make_int2(int(u), j);
+      long_list[atomicAdd(&counts[1], 1u)] = make_int2(int(u), int(base));
     }
   }
 }
@@ -377,43 +394,60 @@ struct SkArgs {
   const void* q;
   float* dC;
   int heads, dq, k, half_sel, nkeys;
-  const int2* chunk_list;    // (run u, chunk j >= 1)
-  const int32_t* long_list;  // runs longer than kSkChunk
+  const int2* chunk_list;    // (run u, chunk j): list entry i owns partial slot i
+  const int2* long_list;     // (run u, first slot) of every run longer than kSkChunk
   const uint32_t* counts;    // [0] chunks listed, [1] long runs listed
-  float* partial;            // [N / kSkChunk + 1, dq/2]: slot of the chunk starting at s is s / kSkChunk
+  float* partial;            // [2 N / kSkChunk + 2, dq/2] partial sums
 };
 
 // One 4-wave block per work item (grid-stride): dC[key] = sum over the key's
 // entries of coef * q_half[t, h].  Wave v takes entries v, v+4, ... in batches
 // of 8 rows, and the four partial sums are added in wave order through LDS.
-// MODE 0: a whole run of at most kSkChunk entries, written to dC.
-// MODE 1: chunk j >= 1 of a long run, written to its partial slot.
-// MODE 2: chunk 0 of a long run plus the partial sums of chunks 1.., in order, into dC.
+// MODE 0: first the chunks of the long runs (into their partial slots), then
+//         the runs of at most kSkChunk entries (into dC).
+// MODE 1: one block per long run: its slots added in chunk order into dC.
 template <typename T, int MODE>
 __global__ __launch_bounds__(256) void subkey_grad_kernel(SkArgs a) {
   __shared__ f32x4 part[kSkWaves][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t nitems = MODE == 0 ? *a.nseg : int64_t(a.counts[MODE - 1]);
   const int half = a.dq / 2;
   const int nch = half / 4;
   const int F = a.heads * a.dq;
   const uint32_t nvalid = uint32_t(a.heads) * uint32_t(a.nkeys);
   const int kh = a.k * a.heads;
+  if (MODE == 1) {
+    const int64_t nlong = a.counts[1];
+    for (int64_t it = blockIdx.x; it < nlong; it += gridDim.x) {
+      const int2 e = a.long_list[it];
+      const int lo = a.seg_start[e.x], hi = a.seg_start[e.x + 1];
+      const uint32_t key = a.sorted_keys[lo];
+      const int nchk = (hi - lo + kSkChunk - 1) / kSkChunk;
+      for (int ch = threadIdx.x; ch < nch; ch += blockDim.x) {
+        f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < nchk; ++j) tot += *reinterpret_cast<const f32x4*>(a.partial + size_t(e.y + j) * half + ch * 4);
+        *reinterpret_cast<f32x4*>(a.dC + size_t(key) * half + ch * 4) = tot;
+      }
+    }
+    return;
+  }
+  const int64_t nchunks = a.counts[0];
+  const int64_t nitems = nchunks + *a.nseg;
   for (int64_t it = blockIdx.x; it < nitems; it += gridDim.x) {
+    const bool chunk = it < nchunks;  // block-uniform
     int u, j = 0;
-    if (MODE == 1) {
+    if (chunk) {
       const int2 e = a.chunk_list[it];
       u = e.x;
       j = e.y;
     } else {
-      u = MODE == 0 ? int(it) : a.long_list[it];
+      u = int(it - nchunks);
     }
     const int lo = a.seg_start[u], hi = a.seg_start[u + 1];
     const uint32_t key = a.sorted_keys[lo];
     if (key >= nvalid) continue;                      // block-uniform: the sentinel run (repeated sub-keys)
-    if (MODE == 0 && hi - lo > kSkChunk) continue;    // block-uniform: long runs go through MODE 1/2
+    if (!chunk && hi - lo > kSkChunk) continue;       // block-uniform: listed as chunks
     const int clo = lo + j * kSkChunk;
-    const int chi = MODE == 0 ? hi : min(hi, clo + kSkChunk);
+    const int chi = chunk ? min(hi, clo + kSkChunk) : hi;
     const int hh = int(key / uint32_t(a.nkeys));
     const T* qh = static_cast<const T*>(a.q) + size_t(hh) * a.dq + size_t(a.half_sel) * half;
     for (int chb = 0; chb < nch; chb += 64) {
@@ -449,14 +483,8 @@ __global__ __launch_bounds__(256) void subkey_grad_kernel(SkArgs a) {
         f32x4 tot = part[0][lane];
 #pragma unroll
         for (int v = 1; v < kSkWaves; ++v) tot += part[v][lane];
-        if (MODE == 1) {
-          *reinterpret_cast<f32x4*>(a.partial + size_t(clo / kSkChunk) * half + ch * 4) = tot;
-        } else {
-          if (MODE == 2)
-            for (int s = lo + kSkChunk; s < hi; s += kSkChunk)
-              tot += *reinterpret_cast<const f32x4*>(a.partial + size_t(s / kSkChunk) * half + ch * 4);
-          *reinterpret_cast<f32x4*>(a.dC + size_t(key) * half + ch * 4) = tot;
-        }
+        float* dst = chunk ? a.partial + size_t(it) * half : a.dC + size_t(key) * half;
+        *reinterpret_cast<f32x4*>(dst + ch * 4) = tot;
       }
       __syncthreads();
     }
@@ -490,8 +518,8 @@ inline unsigned grid_waves(int64_t items, int64_t cap_blocks = 4096) {
 }  // namespace
 
 size_t value_grad_aux_bytes(int64_t nitems, int d_value) {
-  const int64_t slots = nitems / kVgChunk + 1;
-  return size_t(slots) * (size_t(d_value) * 4 + 8 + 4) + 64;
+  const int64_t slots = 2 * (nitems / kVgChunk) + 2;  // chunks of runs longer than a chunk: < 2 N / kVgChunk
+  return size_t(slots) * (size_t(d_value) * 4 + 8 + 8) + 64;
 }
 
 hipError_t launch_value_grad(hipStream_t s, int dtype, const int32_t* seg_start, const int64_t* nseg,
@@ -501,7 +529,7 @@ hipError_t launch_value_grad(hipStream_t s, int dtype, const int32_t* seg_start,
   const int elem = dtype == kBF16 ? 2 : 4;
   const int nvec = d_value * elem / 16;
   const int per_lane = (nvec + 63) / 64;
-  const int64_t slots = nitems / kVgChunk + 1;
+  const int64_t slots = 2 * (nitems / kVgChunk) + 2;
   char* ap = static_cast<char*>(aux);
   VgArgs a;
   a.seg_start = seg_start;
@@ -519,15 +547,16 @@ hipError_t launch_value_grad(hipStream_t s, int dtype, const int32_t* seg_start,
   uint32_t* counts = reinterpret_cast<uint32_t*>(ap);
   a.counts = counts;
   a.partial = reinterpret_cast<float*>(ap + 64);
-  a.chunk_list = reinterpret_cast<int2*>(ap + 64 + size_t(slots) * d_value * 4);
-  a.long_list = reinterpret_cast<const int32_t*>(ap + 64 + size_t(slots) * (size_t(d_value) * 4 + 8));
+  int2* chunk_list = reinterpret_cast<int2*>(ap + 64 + size_t(slots) * d_value * 4);
+  int2* long_list = chunk_list + slots;
+  a.chunk_list = chunk_list;
+  a.long_list = long_list;
   hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, s, counts, 2);
   int64_t pb = (nitems + 255) / 256;
   if (pb > 4096) pb = 4096;
   if (pb < 1) pb = 1;
   hipLaunchKernelGGL(long_run_plan_kernel, dim3(unsigned(pb)), dim3(256), 0, s, seg_start, nseg, kVgChunk,
-                     static_cast<const uint32_t*>(nullptr), 0u, const_cast<int2*>(a.chunk_list),
-                     const_cast<int32_t*>(a.long_list), counts);
+                     static_cast<const uint32_t*>(nullptr), 0u, chunk_list, long_list, counts);
   const dim3 block(256);
   const dim3 grid_long(grid_waves(slots, 1024));
 #define PKM_VG(TT, NV)                                                                                    \
@@ -535,7 +564,6 @@ hipError_t launch_value_grad(hipStream_t s, int dtype, const int32_t* seg_start,
     const dim3 grid(resident_grid(reinterpret_cast<const void*>(value_grad_kernel<TT, NV, 0>), nitems));  \
     hipLaunchKernelGGL((value_grad_kernel<TT, NV, 0>), grid, block, 0, s, a);                             \
     hipLaunchKernelGGL((value_grad_kernel<TT, NV, 1>), grid_long, block, 0, s, a);                        \
-    hipLaunchKernelGGL((value_grad_kernel<TT, NV, 2>), grid_long, block, 0, s, a);                        \
   } while (0)
   if (dtype == kBF16) {
     if (per_lane <= 1) PKM_VG(bf16_t, 1);
@@ -572,14 +600,14 @@ hipError_t launch_softmax_bwd_dq(hipStream_t s, int dtype, const int32_t* idx, c
 }
 
 size_t subkey_grad_aux_bytes(int64_t nitems, int dq) {
-  const int64_t slots = nitems / kSkChunk + 1;
-  return size_t(slots) * (size_t(dq / 2) * 4 + 8 + 4) + 64;
+  const int64_t slots = 2 * (nitems / kSkChunk) + 2;  // chunks of runs longer than a chunk: < 2 N / kSkChunk
+  return size_t(slots) * (size_t(dq / 2) * 4 + 8 + 8) + 64;
 }
 
 hipError_t launch_subkey_grad(hipStream_t s, int dtype, const int32_t* seg_start, const int64_t* nseg, int64_t nsub,
                               int64_t nitems, const uint32_t* sorted_keys, const int32_t* sorted_c, const float* coef,
                               const void* q, int heads, int dq, int k, int half_sel, int nkeys, float* dC, void* aux) {
-  const int64_t slots = nitems / kSkChunk + 1;
+  const int64_t slots = 2 * (nitems / kSkChunk) + 2;
   const int half = dq / 2;
   char* ap = static_cast<char*>(aux);
   SkArgs a;
@@ -599,7 +627,7 @@ hipError_t launch_subkey_grad(hipStream_t s, int dtype, const int32_t* seg_start
   a.counts = counts;
   a.partial = reinterpret_cast<float*>(ap + 64);
   int2* chunk_list = reinterpret_cast<int2*>(ap + 64 + size_t(slots) * half * 4);
-  int32_t* long_list = reinterpret_cast<int32_t*>(ap + 64 + size_t(slots) * (size_t(half) * 4 + 8));
+  int2* long_list = chunk_list + slots;
   a.chunk_list = chunk_list;
   a.long_list = long_list;
   hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, s, counts, 2);
@@ -607,18 +635,17 @@ hipError_t launch_subkey_grad(hipStream_t s, int dtype, const int32_t* seg_start
   if (pb > 4096) pb = 4096;
   hipLaunchKernelGGL(long_run_plan_kernel, dim3(unsigned(pb)), dim3(256), 0, s, seg_start, nseg, kSkChunk,
                      sorted_keys, uint32_t(heads) * uint32_t(nkeys), chunk_list, long_list, counts);
-  int64_t blocks = nsub + 1;
+  // one block per run (at most one per sub-key, plus the sentinel) or chunk (< 2 N / kSkChunk)
+  int64_t blocks = nsub + 1 + slots;
   if (blocks > 8192) blocks = 8192;
-  int64_t lblocks = slots < 8192 ? slots : 8192;
+  int64_t lblocks = slots < 4096 ? slots : 4096;
   const dim3 grid{unsigned(blocks), 1, 1}, lgrid{unsigned(lblocks), 1, 1}, block{256, 1, 1};
   if (dtype == kBF16) {
     hipLaunchKernelGGL((subkey_grad_kernel<bf16_t, 0>), grid, block, 0, s, a);
     hipLaunchKernelGGL((subkey_grad_kernel<bf16_t, 1>), lgrid, block, 0, s, a);
-    hipLaunchKernelGGL((subkey_grad_kernel<bf16_t, 2>), lgrid, block, 0, s, a);
   } else {
     hipLaunchKernelGGL((subkey_grad_kernel<float, 0>), grid, block, 0, s, a);
     hipLaunchKernelGGL((subkey_grad_kernel<float, 1>), lgrid, block, 0, s, a);
-    hipLaunchKernelGGL((subkey_grad_kernel<float, 2>), lgrid, block, 0, s, a);
   }
   return hipGetLastError();
 }
