@@ -7,12 +7,20 @@
 // projection; product-key paper summary, method details: every parameter is
 // trained by back-propagation.)
 //
-// 128x128 output tile per 256-thread workgroup, 2x2 waves of 64x64, K staged
-// through double-buffered LDS in 128-byte slices (64 bf16 or 32 fp32); bf16
-// uses v_mfma_f32_16x16x32_bf16 and fp32 uses v_mfma_f32_16x16x4f32, both with
-// fp32 accumulation.  The next K slice is fetched into registers while the
-// current one feeds the MFMAs.  Rows padded in LDS by 16 bytes so the 16-byte
-// fragment reads of 16 consecutive rows hit distinct banks.
+// bf16 (K a multiple of 32, operands under 4 GB): 256x256 output tile per
+// 8-wave workgroup (4 x 2 waves of 64 x 128), v_mfma_f32_16x16x32_bf16 with
+// fp32 accumulation.  Operands go straight from memory into LDS with
+// buffer_load ... lds (no register staging), four 32-deep K stages in flight;
+// rows past the matrix read as zero through the buffer range check.  Each
+// 16-row x 64-byte LDS block keeps its 16-byte chunks XOR-swizzled by row so
+// the MFMA fragment reads of 16 rows spread over all banks.  Tiles are
+// assigned so that each XCD (workgroups b with equal b % 8) walks a
+// contiguous range of output rows, sharing the A panel in its L2.
+//
+// Otherwise: 128x128 output tile per 256-thread workgroup, 2x2 waves of
+// 64x64, K staged through double-buffered LDS in 128-byte slices (64 bf16 or
+// 32 fp32; fp32 uses v_mfma_f32_16x16x4f32); the next slice is fetched into
+// registers while the current one feeds the MFMAs; rows padded by 16 bytes.
 #include "common.h"
 #include "kernels.h"
 
@@ -142,6 +150,134 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(int64_t M, int64_t N, int6
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// bf16 path with LDS-DMA operand staging
+// ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+
+// Buffer resource of `bytes` bytes at base (raw buffer: stride 0; reads at or
+// beyond `bytes` return zero).
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{int(uint32_t(a)), int(uint32_t(a >> 32) & 0xFFFF), int(bytes), 0x00020000};
+}
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
+}
+// 16 bytes per lane from buffer offset voff into LDS at lds_base + lane * 16.
+// Written as asm because the compiler, seeing the builtin's LDS write, waits for
+// every outstanding load before any later LDS read, which would drain the
+// pipeline each K stage; the caller waits with s_waitcnt vmcnt instead.  The
+// instruction has no register results (the data lands in LDS), and its address
+// operands are read at issue.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+// Workgroup barrier that orders LDS only (leaves later stages' loads in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+// s_waitcnt vmcnt(n) (n < 64), other counters untouched
+#define PKM_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 0xF) | (((n) >> 4) << 14))
+
+constexpr int kDmaStages = 4;
+constexpr int kDmaStage = 32768;  // bytes per stage: A and B blocks of 256 rows x 64 bytes
+constexpr int kDmaWM = 4, kDmaWN = 2;
+
+__global__ __launch_bounds__(512) void gemm_nt_dma_kernel(int64_t M, int64_t N, const bf16_t* __restrict__ A,
+                                                          int64_t lda, const bf16_t* __restrict__ B, int64_t ldb,
+                                                          void* __restrict__ Cout, int64_t ldc, int out_bf16,
+                                                          int64_t K, int64_t kchunk, int64_t split_stride) {
+  constexpr int BM = 256, BN = 256, NW = kDmaWM * kDmaWN, TI = BM / kDmaWM / 16, TJ = BN / kDmaWN / 16;
+  constexpr int BPW = 16 / NW;        // 1 KB blocks per operand, stage and wave
+  constexpr int PER = 2 * BPW;        // DMA instructions per stage and wave
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave / kDmaWN, wn = wave % kDmaWN;
+  const int64_t gx = (N + BN - 1) / BN, total = gx * ((M + BM - 1) / BM);
+  int64_t t = blockIdx.x;
+  if (total % 8 == 0) t = (t % 8) * (total / 8) + t / 8;  // XCD b % 8 gets a contiguous run of tiles
+  const int64_t m0 = (t / gx) * BM, n0 = (t % gx) * BN;
+  const int64_t kbeg = int64_t(blockIdx.y) * kchunk;
+  const int64_t kend = kbeg + kchunk < K ? kbeg + kchunk : K;
+  const i32x4 ra = make_rsrc(A, uint32_t(M * lda * 2));
+  const i32x4 rb = make_rsrc(B, uint32_t(N * ldb * 2));
+  // lane slot in a 1 KB block (16 rows x 64 bytes): row r, chunk position lane & 3, source chunk c
+  const int r = lane >> 2, c = (lane & 3) ^ ((r >> 2) & 3);
+  constexpr uint32_t kOut = 0xFFFFFFF0u;  // offset past any buffer: reads zero
+  uint32_t aoff[BPW], boff[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int64_t ar = m0 + (wave + NW * i) * 16 + r, br = n0 + (wave + NW * i) * 16 + r;
+    aoff[i] = ar < M ? uint32_t((ar * lda + kbeg + c * 8) * 2) : kOut;
+    boff[i] = br < N ? uint32_t((br * ldb + kbeg + c * 8) * 2) : kOut;
+  }
+  const int nkt = kend > kbeg ? int((kend - kbeg) / 32) : 0;
+  auto issue = [&](int kt) {
+    char* st = smem + (kt % kDmaStages) * kDmaStage;
+    const uint32_t kb = uint32_t(kt) * 64;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      dma16(ra, aoff[i] == kOut ? kOut : aoff[i] + kb, lds_addr(st + (wave + NW * i) * 1024));
+      dma16(rb, boff[i] == kOut ? kOut : boff[i] + kb, lds_addr(st + 16384 + (wave + NW * i) * 1024));
+    }
+  };
+  f32x4 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int lrow = lane & 15, lgrp = lane >> 4;
+  const int fr = lrow * 64 + ((lgrp ^ ((lrow >> 2) & 3)) * 16);  // this lane's fragment in a block
+#pragma unroll
+  for (int st = 0; st < kDmaStages - 1; ++st)
+    if (st < nkt) issue(st);
+  for (int kt = 0; kt < nkt; ++kt) {
+    if (kt + kDmaStages - 1 < nkt) {
+      issue(kt + kDmaStages - 1);
+      PKM_WAIT_VM(PER * (kDmaStages - 1));  // stage kt landed; the next three stay in flight
+    } else {
+      PKM_WAIT_VM(0);
+    }
+    lds_barrier();
+    const char* st = smem + (kt % kDmaStages) * kDmaStage;
+    u32x4 b[TJ];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) b[j] = *reinterpret_cast<const u32x4*>(st + 16384 + (wn * TJ + j) * 1024 + fr);
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(st + (wm * TI + i) * 1024 + fr);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) acc[i][j] = GemmTraits<bf16_t>::mma(a, b[j], acc[i][j]);
+    }
+    lds_barrier();  // stage kt's buffer is refilled by the next iteration's issue
+  }
+  char* Cb = reinterpret_cast<char*>(Cout) + int64_t(blockIdx.y) * split_stride * (out_bf16 ? 2 : 4);
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int64_t col = n0 + (wn * TJ + j) * 16 + lrow;
+      if (col >= N) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t row = m0 + (wm * TI + i) * 16 + lgrp * 4 + q;
+        if (row < M) {
+          if (out_bf16)
+            reinterpret_cast<uint16_t*>(Cb)[row * ldc + col] = f32_to_bf16(acc[i][j][q]);
+          else
+            reinterpret_cast<float*>(Cb)[row * ldc + col] = acc[i][j][q];
+        }
+      }
+    }
+}
+
 __global__ __launch_bounds__(256) void sum_splits_kernel(const float* __restrict__ part, int splits,
                                                          int64_t stride, int64_t rows, int64_t cols,
                                                          int64_t ld_part, void* __restrict__ out,
@@ -199,6 +335,23 @@ hipError_t launch_gemm_nt(hipStream_t s, int dtype, int64_t M, int64_t N, int64_
                           int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, bool out_bf16,
                           int splits, int64_t split_stride) {
   if (splits < 1) splits = 1;
+  if (dtype == kBF16 && K % 32 == 0 && M * lda * 2 < (int64_t(1) << 32) - 64 &&
+      N * ldb * 2 < (int64_t(1) << 32) - 64) {
+    int64_t kchunk = (K + splits - 1) / splits;
+    kchunk = (kchunk + 31) / 32 * 32;
+    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    const size_t lds = size_t(kDmaStages) * kDmaStage;
+    static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
+    if (!attr_set) {
+      hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_nt_dma_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+      attr_set = true;
+    }
+    hipLaunchKernelGGL(gemm_nt_dma_kernel, dim3(unsigned(tiles), unsigned(splits)), dim3(512), lds, s, M, N,
+                       static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(B), ldb, C, ldc,
+                       int(out_bf16), K, kchunk, split_stride);
+    return hipGetLastError();
+  }
   const int64_t bk = dtype == kBF16 ? 64 : 32;
   int64_t kchunk = (K + splits - 1) / splits;
   kchunk = (kchunk + bk - 1) / bk * bk;
