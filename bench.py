@@ -31,6 +31,7 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 # holds for the kernel source whose sha256 prefix is given; any change to that file voids it (traffic null).
 KERNEL_TRAFFIC = {
     ("gather", "paper"): {"bytes": 13552185344, "source": "gather.hip", "source_sha256_16": "53a5257d0d80a76c"},
+    ("value_grad", "paper"): {"bytes": 29733489152, "source": "sparse_grad.hip", "source_sha256_16": "081749a54f6290be"},
 }
 
 
