@@ -67,7 +67,7 @@ struct FwdLayout {
   size_t sub_idx, sub_score, bn_part, keys, total;
 };
 struct BwdLayout {
-  size_t k0, v0, k1, v1, sort_tmp, flags, pos, seg_flags, seg_pos, seg, scan_tmp, nseg, dw, ds, coef2, dq, bn_part,
+  size_t k0, v0, k1, v1, sort_tmp, key1, key2, seg, scan_tmp, nseg, dw, ds, coef2, dq, bn_part,
       dqpre, dqpre_t, x_t, wq_t, split, aux, total;
   int splits;
   int64_t tpad;
@@ -107,10 +107,8 @@ BwdLayout bwd_layout(const pkm_handle_s* h, int64_t T) {
   L.k1 = o; o += al(N * 4);
   L.v1 = o; o += al(N * 4);
   L.sort_tmp = o; o += al(radix_sort_temp_bytes(int64_t(N)));
-  L.flags = o; o += al(N * 4);
-  L.pos = o; o += al(N * 4);
-  L.seg_flags = o; o += al(N * 4);
-  L.seg_pos = o; o += al(N * 4);
+  L.key1 = o; o += al(N * 4);  // per-slot sub-key sort keys of the two halves
+  L.key2 = o; o += al(N * 4);
   L.seg = o; o += al((N + 1) * 4);
   L.scan_tmp = o; o += al(256 + scan_temp_bytes(int64_t(N)));
   L.nseg = o; o += al(4 * sizeof(int64_t));
@@ -229,8 +227,7 @@ pkm_status run_row_groups(const pkm_handle_s* h, hipStream_t s, int64_t T, const
                                  at<void>(ws, L.sort_tmp), &in1),
           "row sort");
   const uint32_t* sk = at<uint32_t>(ws, in1 ? L.k1 : L.k0);
-  PKM_HIP(launch_segments(s, sk, N, at<uint32_t>(ws, L.flags), at<uint32_t>(ws, L.pos), at<int32_t>(ws, L.seg),
-                          touched, n_touched, at<void>(ws, L.scan_tmp)),
+  PKM_HIP(launch_segments(s, sk, N, at<int32_t>(ws, L.seg), touched, n_touched, at<void>(ws, L.scan_tmp)),
           "row segments");
   return PKM_OK;
 }
@@ -267,9 +264,9 @@ pkm_status run_subkey_grad(const pkm_handle_s* h, hipStream_t s, int64_t T, cons
   const pkm_config& c = h->cfg;
   const BwdLayout L = bwd_layout(h, T);
   const int64_t N = T * c.heads * c.topk;
-  // per-slot sort keys and coefficients of the two halves (the forward-only regions are free here)
-  uint32_t* key1 = at<uint32_t>(ws, L.flags);
-  uint32_t* key2 = at<uint32_t>(ws, L.pos);
+  // per-slot sort keys and coefficients of the two halves
+  uint32_t* key1 = at<uint32_t>(ws, L.key1);
+  uint32_t* key2 = at<uint32_t>(ws, L.key2);
   float* coef1 = at<float>(ws, L.ds);
   float* coef2 = at<float>(ws, L.coef2);
   PKM_HIP(launch_softmax_bwd_dq(s, c.dtype, idx, w, dw, C, Cp, T, c.heads, c.d_query, c.topk, c.n_keys, c.n_keys2,
@@ -291,8 +288,7 @@ pkm_status run_subkey_grad(const pkm_handle_s* h, hipStream_t s, int64_t T, cons
     int32_t* seg = at<int32_t>(ws, L.seg);
     int64_t* nseg = at<int64_t>(ws, L.nseg) + 1 + half_sel;
     PKM_HIP(launch_fill_f32(s, out, int64_t(c.heads) * nkeys * h->half, 0.f), "sub-key gradient clear");
-    PKM_HIP(launch_segments(s, sk, N, at<uint32_t>(ws, L.seg_flags), at<uint32_t>(ws, L.seg_pos), seg, nullptr, nseg,
-                            at<void>(ws, L.scan_tmp)),
+    PKM_HIP(launch_segments(s, sk, N, seg, nullptr, nseg, at<void>(ws, L.scan_tmp)),
             "sub-key segments");
     PKM_HIP(launch_subkey_grad(s, c.dtype, seg, nseg, int64_t(c.heads) * nkeys, N, sk, sv, coef, q, c.heads,
                                c.d_query, c.topk, half_sel, nkeys, out, at<void>(ws, L.aux)),

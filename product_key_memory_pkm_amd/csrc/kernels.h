@@ -76,9 +76,9 @@ hipError_t launch_exclusive_scan(hipStream_t s, const uint32_t* in, uint32_t* ou
 
 // Segments of a sorted key array: seg_start[u] for every distinct key run, and
 // count (device int64).  Also touched[u] = key of run u (may be null).
-hipError_t launch_segments(hipStream_t s, const uint32_t* sorted_keys, int64_t n, uint32_t* flags,
-                           uint32_t* pos, int32_t* seg_start, int32_t* touched, int64_t* count,
-                           void* scan_temp);
+// seg_start needs room for count + 1 entries (the last one is n).
+hipError_t launch_segments(hipStream_t s, const uint32_t* sorted_keys, int64_t n, int32_t* seg_start,
+                           int32_t* touched, int64_t* count, void* scan_temp);
 
 // a7 + a8: per touched row, dw for every lookup of it and the row's dV.  Rows
 // with more lookups than a chunk are split over several waves; aux (of

@@ -8,10 +8,16 @@
 // floating-point atomics.
 //
 // Radix pass (8-bit digit): per 4096-key tile a digit histogram, one exclusive
-// scan over the digit-major (digit, tile) table, then a scatter in which each
-// key's rank among equal digits of its tile is found round by round (256 keys
-// per round, in index order): within a wave by matching the 8 digit bits with
-// ballots, across the 4 waves through LDS counters.
+// scan over the digit-major (digit, tile) table, then a scatter.  In the
+// scatter each wave owns 1024 consecutive keys of the tile and walks them 64 at
+// a time, ranking every key among equal digits by matching the 8 digit bits
+// with ballots and keeping per-digit counts in its own LDS row (no barrier per
+// round); one barrier then turns the four waves' counts into per-wave bases,
+// and the keys, still in registers, are written out in index order per digit.
+//
+// Segments of a sorted key array are found in one scan over "key differs from
+// its predecessor" computed on the fly: the apply pass writes each segment's
+// start (and key) at its rank directly.
 #include "common.h"
 #include "kernels.h"
 
@@ -119,27 +125,35 @@ __global__ __launch_bounds__(256) void radix_hist_kernel(const uint32_t* __restr
 }
 
 // Stable scatter of one tile.  vals_in == nullptr: the value is the key's index.
+constexpr int kWaveKeys = kTile / 4;     // keys per wave and tile
+constexpr int kRounds = kWaveKeys / 64;  // 64 keys per round
+
 __global__ __launch_bounds__(256) void radix_scatter_kernel(const uint32_t* __restrict__ keys_in,
                                                             const int32_t* __restrict__ vals_in, int64_t n,
                                                             int shift, int nb, const uint32_t* __restrict__ offs,
                                                             uint32_t* __restrict__ keys_out,
                                                             int32_t* __restrict__ vals_out) {
-  __shared__ uint32_t run[256];
-  __shared__ uint32_t wcnt[4][256];
-  __shared__ uint32_t goff[256];
+  __shared__ uint32_t cnt[4][256];  // per-wave digit counts, then per-wave write bases
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  run[tid] = 0;
-  goff[tid] = offs[int64_t(tid) * nb + blockIdx.x];
 #pragma unroll
-  for (int w = 0; w < 4; ++w) wcnt[w][tid] = 0;
+  for (int w = 0; w < 4; ++w) cnt[w][tid] = 0;
   __syncthreads();
-  const int64_t base = int64_t(blockIdx.x) * kTile;
-  for (int i = 0; i < kTile / 256; ++i) {
-    const int64_t e = base + i * 256 + tid;
+  const int64_t base = int64_t(blockIdx.x) * kTile + int64_t(wave) * kWaveKeys;
+  uint32_t key[kRounds];
+  int32_t val[kRounds];
+  uint32_t lpos[kRounds];
+#pragma unroll
+  for (int i = 0; i < kRounds; ++i) {
+    const int64_t e = base + i * 64 + lane;
     const bool ok = e < n;
-    const uint32_t key = ok ? keys_in[e] : 0u;
-    const int32_t val = ok ? (vals_in ? vals_in[e] : int32_t(e)) : 0;
-    const uint32_t d = (key >> shift) & 0xFF;
+    key[i] = ok ? keys_in[e] : 0u;
+    val[i] = ok ? (vals_in ? vals_in[e] : int32_t(e)) : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < kRounds; ++i) {
+    const int64_t e = base + i * 64 + lane;
+    const bool ok = e < n;
+    const uint32_t d = (key[i] >> shift) & 0xFF;
     uint64_t peers = ballot(ok);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
@@ -148,44 +162,83 @@ __global__ __launch_bounds__(256) void radix_scatter_kernel(const uint32_t* __re
       peers &= bit ? m : ~m;
     }
     const int rk = lanes_below(peers);
-    if (ok && rk == 0) wcnt[wave][d] = uint32_t(popc64(peers));
-    __syncthreads();
-    if (ok) {
-      uint32_t pre = run[d];
-      for (int w = 0; w < wave; ++w) pre += wcnt[w][d];
-      const uint32_t pos = goff[d] + pre + uint32_t(rk);
-      keys_out[pos] = key;
-      vals_out[pos] = val;
-    }
-    __syncthreads();
-    run[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
+    const uint32_t before = ok ? cnt[wave][d] : 0u;  // every lane reads before the leader writes
+    lpos[i] = before + uint32_t(rk);
+    if (ok && rk == 0) cnt[wave][d] = before + uint32_t(popc64(peers));
+  }
+  __syncthreads();
+  {  // bases: tile offset of digit tid, then the earlier waves' counts
+    uint32_t run = offs[int64_t(tid) * nb + blockIdx.x];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) wcnt[w][tid] = 0;
-    __syncthreads();
-  }
-}
-
-__global__ __launch_bounds__(256) void seg_flags_kernel(const uint32_t* __restrict__ k, int64_t n,
-                                                        uint32_t* __restrict__ flags) {
-  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256)
-    flags[i] = (i == 0 || k[i] != k[i - 1]) ? 1u : 0u;
-}
-
-__global__ __launch_bounds__(256) void seg_write_kernel(const uint32_t* __restrict__ k, int64_t n,
-                                                        const uint32_t* __restrict__ flags,
-                                                        const uint32_t* __restrict__ pos,
-                                                        const uint32_t* __restrict__ total,
-                                                        int32_t* __restrict__ seg_start, int32_t* __restrict__ touched,
-                                                        int64_t* __restrict__ count) {
-  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
-    if (flags[i]) {
-      seg_start[pos[i]] = int32_t(i);
-      if (touched) touched[pos[i]] = int32_t(k[i]);
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t c = cnt[w][tid];
+      cnt[w][tid] = run;
+      run += c;
     }
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kRounds; ++i) {
+    const int64_t e = base + i * 64 + lane;
+    if (e < n) {
+      const uint32_t d = (key[i] >> shift) & 0xFF;
+      const uint32_t pos = cnt[wave][d] + lpos[i];
+      keys_out[pos] = key[i];
+      vals_out[pos] = val[i];
+    }
+  }
+}
+
+// Segment scan over flag(i) = (i == 0 || k[i] != k[i-1]): per-block flag counts.
+__global__ __launch_bounds__(256) void seg_reduce_kernel(const uint32_t* __restrict__ k, int64_t n,
+                                                         uint32_t* __restrict__ part) {
+  __shared__ uint32_t sh[4];
+  const int64_t b0 = int64_t(blockIdx.x) * kScanBlock + threadIdx.x * 16;
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t e = b0 + i;
+    if (e < n) s += (e == 0 || k[e] != k[e - 1]) ? 1u : 0u;
+  }
+  uint32_t tot;
+  block_excl_scan(s, sh, &tot);
+  if (threadIdx.x == 0) part[blockIdx.x] = tot;
+}
+
+// Writes seg_start[rank] = i (and touched[rank] = k[i]) for every segment start
+// i; the last block also closes the table: seg_start[total] = n, *count = total.
+__global__ __launch_bounds__(256) void seg_apply_kernel(const uint32_t* __restrict__ k, int64_t n,
+                                                        const uint32_t* __restrict__ part,
+                                                        const uint32_t* __restrict__ total,
+                                                        int32_t* __restrict__ seg_start,
+                                                        int32_t* __restrict__ touched, int64_t* __restrict__ count) {
+  __shared__ uint32_t sh[4];
+  const int64_t b0 = int64_t(blockIdx.x) * kScanBlock + threadIdx.x * 16;
+  uint32_t f = 0;  // flag bits of this thread's 16 elements
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t e = b0 + i;
+    if (e < n && (e == 0 || k[e] != k[e - 1])) f |= 1u << i;
+  }
+  uint32_t tot;
+  uint32_t rank = block_excl_scan(uint32_t(__popc(f)), sh, &tot) + part[blockIdx.x];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (f & (1u << i)) {
+      seg_start[rank] = int32_t(b0 + i);
+      if (touched) touched[rank] = int32_t(k[b0 + i]);
+      ++rank;
+    }
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) {
     seg_start[*total] = int32_t(n);
     *count = int64_t(*total);
+  }
+}
+
+__global__ void seg_empty_kernel(int32_t* seg_start, int64_t* count) {
+  if (threadIdx.x == 0) {
+    seg_start[0] = 0;
+    *count = 0;
   }
 }
 
@@ -259,15 +312,20 @@ hipError_t launch_radix_sort_from(hipStream_t s, const uint32_t* keys_in, uint32
   return hipGetLastError();
 }
 
-hipError_t launch_segments(hipStream_t s, const uint32_t* sorted_keys, int64_t n, uint32_t* flags, uint32_t* pos,
-                           int32_t* seg_start, int32_t* touched, int64_t* count, void* scan_temp) {
-  hipLaunchKernelGGL(seg_flags_kernel, dim3(grid1d(n)), dim3(256), 0, s, sorted_keys, n, flags);
+hipError_t launch_segments(hipStream_t s, const uint32_t* sorted_keys, int64_t n, int32_t* seg_start,
+                           int32_t* touched, int64_t* count, void* scan_temp) {
   uint32_t* total = static_cast<uint32_t*>(scan_temp);
-  void* stemp = total + 64;
-  hipError_t e = launch_exclusive_scan(s, flags, pos, n, stemp, total);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(seg_write_kernel, dim3(grid1d(n)), dim3(256), 0, s, sorted_keys, n, flags, pos, total,
-                     seg_start, touched, count);
+  uint32_t* part = total + 64;
+  const int64_t nb = (n + kScanBlock - 1) / kScanBlock;
+  if (nb > 256 * 64) return hipErrorInvalidValue;
+  if (nb > 0) hipLaunchKernelGGL(seg_reduce_kernel, dim3(unsigned(nb)), dim3(256), 0, s, sorted_keys, n, part);
+  hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(256), 0, s, part, int(nb), total);
+  if (nb > 0) {
+    hipLaunchKernelGGL(seg_apply_kernel, dim3(unsigned(nb)), dim3(256), 0, s, sorted_keys, n, part, total,
+                       seg_start, touched, count);
+  } else {
+    hipLaunchKernelGGL(seg_empty_kernel, dim3(1), dim3(64), 0, s, seg_start, count);
+  }
   return hipGetLastError();
 }
 
