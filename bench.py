@@ -26,23 +26,28 @@ HBM_PEAK_GBS = 8000.0
 # dense MFMA peaks of the MI355X by operand type
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 
-# HBM bytes per launch measured with two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) at the paper-scale
+# HBM bytes per launch measured with two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) at the named
 # workload, scaled by the same counters for a plain 1 GiB copy (profiles/*_hbm_counters.md).  Each figure
-# holds for the kernel source whose sha256 prefix is given; any change to that file voids it (traffic null).
+# holds for the kernel sources whose combined sha256 prefix is given; any change to them voids it (traffic null).
 KERNEL_TRAFFIC = {
-    ("gather", "paper"): {"bytes": 13552185344, "source": "gather.hip", "source_sha256_16": "53a5257d0d80a76c"},
-    ("value_grad", "paper"): {"bytes": 29733489152, "source": "sparse_grad.hip", "source_sha256_16": "081749a54f6290be"},
+    ("gather", "paper"): {"bytes": 13552399360, "sources": ["gather.hip", "common.h"], "sources_sha256_16": "130545acf7a0c23f"},
+    ("value_grad", "paper"): {"bytes": 29721798656, "sources": ["value_grad.hip", "sparse_common.h", "common.h"], "sources_sha256_16": "8e0c2d1075f27797"},
 }
 
 
-def measured_traffic(name, workload):
+def sources_digest(names):
     import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        h.update(open(os.path.join(ROOT, "product_key_memory_pkm_amd", "csrc", n), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name, workload):
     ent = KERNEL_TRAFFIC.get((name, workload))
     if ent is None:
         return None
-    src = os.path.join(ROOT, "product_key_memory_pkm_amd", "csrc", ent["source"])
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    return ent["bytes"] if digest == ent["source_sha256_16"] else None
+    return ent["bytes"] if sources_digest(ent["sources"]) == ent["sources_sha256_16"] else None
 
 
 def parse():
