@@ -16,6 +16,7 @@
 // with a 32-lane bitonic network, and the softmax runs on the sorted lanes.
 #include "common.h"
 #include "kernels.h"
+#include "lane_ops.h"
 
 namespace pkm {
 
@@ -31,20 +32,18 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Bitonic sort, descending, of one uint64 per lane within aligned groups of 32 lanes.
+// Bitonic sort, descending, of one uint64 per lane within aligned groups of 32
+// lanes (every exchange stays inside 32 lanes: DPP or ds_swizzle).
 __device__ __forceinline__ uint64_t sort32_desc_u64(uint64_t v) {
   const int lane = lane_id();
 #pragma unroll
   for (int size = 2; size <= 32; size <<= 1) {
 #pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      uint64_t o = shfl_xor_u64(v, stride);
-      bool lower = (lane & stride) == 0;
-      bool desc = (lane & size) == 0 || size == 32;
-      bool take_max = (lower == desc);
-      uint64_t mx = v > o ? v : o;
-      uint64_t mn = v > o ? o : v;
-      v = take_max ? mx : mn;
+      const uint64_t o = xor_lane_u64(v, stride);
+      const bool take_max = ((lane & stride) == 0) == ((lane & size) == 0 || size == 32);
+      const bool gt = v > o;
+      v = (gt == take_max) ? v : o;
     }
   }
   return v;
@@ -95,10 +94,15 @@ __global__ __launch_bounds__(256) void merge_softmax_kernel(const int32_t* __res
     const uint32_t h1 = ok1 ? float_key(s1) : 0u;
     const uint32_t l0 = ~uint32_t(r0), l1 = ~uint32_t(r1);
 
-    // k-th largest score key
-    uint32_t thr = 0;
-#pragma unroll
-    for (int b = 31; b >= 0; --b) {
+    // k-th largest score key, by bisection between a lower bound and the
+    // largest key: the k candidates (a, 0), a < k, are all in the set, so the
+    // k-th largest key is at least that of (k-1, 0), and the bits above the
+    // highest one where the two bounds differ are fixed.
+    const uint32_t hi = float_key(shfl_f32(v1, 0) + shfl_f32(v2, 0));
+    const uint32_t lo = float_key(shfl_f32(v1, k - 1) + shfl_f32(v2, 0));
+    const int top = hi == lo ? -1 : 31 - __builtin_clz(hi ^ lo);
+    uint32_t thr = top < 0 ? lo : (lo & ~((2u << top) - 1u));
+    for (int b = top; b >= 0; --b) {
       const uint32_t c = thr | (1u << b);
       if (popc64(ballot(h0 >= c)) + popc64(ballot(h1 >= c)) >= k) thr = c;
     }
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(256) void merge_softmax_kernel(const int32_t* __res
     const int row = int(~uint32_t(v));
     const float smax = shfl_f32(sc, 0);
     const float e = lane < k ? expf((sc - smax) * inv_tau) : 0.f;
-    const float sum = wave_sum(e);
+    const float sum = wave_sum_dpp(e);
     if (lane < k) {
       const int64_t o = it * k + lane;
       idx[o] = row;

@@ -28,6 +28,7 @@
 //     (heavy ties) take an exact bisection over all scores instead.
 #include "common.h"
 #include "kernels.h"
+#include "lane_ops.h"
 
 namespace pkm {
 
@@ -95,23 +96,6 @@ __device__ __forceinline__ int wave_excl_scan_dpp(int v, int* total) {
   x += (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
   *total = r0 + r1 + r2 + r3;
   return x - v;
-}
-
-// Value of lane (lane ^ stride): DPP quad permutes for strides 1 and 2,
-// ds_swizzle (xor within 32 lanes, no address register) for 4..16, a
-// bpermute for 32.  stride is a constant once the callers' loops unroll.
-__device__ __forceinline__ uint32_t xor_lane(uint32_t v, int stride) {
-  switch (stride) {
-    case 1: return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
-    case 2: return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
-    case 4: return uint32_t(__builtin_amdgcn_ds_swizzle(int(v), (4 << 10) | 0x1F));
-    case 8: return uint32_t(__builtin_amdgcn_ds_swizzle(int(v), (8 << 10) | 0x1F));
-    case 16: return uint32_t(__builtin_amdgcn_ds_swizzle(int(v), (16 << 10) | 0x1F));
-    default: return uint32_t(__shfl_xor(int(v), stride, 64));
-  }
-}
-__device__ __forceinline__ uint64_t xor_lane_u64(uint64_t v, int stride) {
-  return (uint64_t(xor_lane(uint32_t(v >> 32), stride)) << 32) | xor_lane(uint32_t(v), stride);
 }
 
 // Bitonic sort, descending, of N independent uint64 values per lane across the wave.
