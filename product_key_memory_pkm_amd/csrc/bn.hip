@@ -8,7 +8,8 @@
 //             dq_pre = gamma_f rstd_f (dq - dbeta_f/T - xhat dgamma_f/T)
 //
 // Column sums are taken in fp64 over fixed blocks of 256 rows, then combined in
-// block order by one thread per feature: no atomics, bit-identical across runs.
+// a fixed order (four strided groups of blocks, added group by group): no
+// atomics, bit-identical across runs.
 #include "common.h"
 #include "kernels.h"
 
@@ -59,18 +60,34 @@ __global__ __launch_bounds__(256) void bn_partials_kernel(const float* __restric
   bn_combine_store(acc, part, F, f4);
 }
 
+// Thread (ty, tx) of a block adds partial blocks ty, ty+4, ... of feature
+// 64 * blockIdx.x + tx; the four row-group sums are combined in a fixed order.
+__device__ __forceinline__ void bn_sum_partials(const double* __restrict__ part, int nblk, int F, double* out2) {
+  __shared__ double red[4][2][64];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int f = blockIdx.x * 64 + tx;
+  double a = 0.0, b = 0.0;
+  if (f < F)
+    for (int k = ty; k < nblk; k += 4) {
+      a += part[(int64_t(k) * 2 + 0) * F + f];
+      b += part[(int64_t(k) * 2 + 1) * F + f];
+    }
+  red[ty][0][tx] = a;
+  red[ty][1][tx] = b;
+  __syncthreads();
+  out2[0] = ((red[0][0][tx] + red[1][0][tx]) + red[2][0][tx]) + red[3][0][tx];
+  out2[1] = ((red[0][1][tx] + red[1][1][tx]) + red[2][1][tx]) + red[3][1][tx];
+}
+
 __global__ __launch_bounds__(256) void bn_finalize_kernel(const double* __restrict__ part, int nblk, int64_t ntok,
                                                           int F, float eps, float* __restrict__ mean,
                                                           float* __restrict__ rstd) {
-  const int f = blockIdx.x * 256 + threadIdx.x;
-  if (f >= F) return;
-  double s = 0.0, ss = 0.0;
-  for (int b = 0; b < nblk; ++b) {
-    s += part[(int64_t(b) * 2 + 0) * F + f];
-    ss += part[(int64_t(b) * 2 + 1) * F + f];
-  }
-  const double m = s / double(ntok);
-  double var = ss / double(ntok) - m * m;
+  double sums[2];
+  bn_sum_partials(part, nblk, F, sums);
+  const int f = blockIdx.x * 64 + (threadIdx.x & 63);
+  if (threadIdx.x >= 64 || f >= F) return;
+  const double m = sums[0] / double(ntok);
+  double var = sums[1] / double(ntok) - m * m;
   if (var < 0.0) var = 0.0;
   mean[f] = float(m);
   rstd[f] = float(1.0 / sqrt(var + double(eps)));
@@ -159,15 +176,12 @@ __global__ __launch_bounds__(256) void bn_bwd_partials_kernel(const float* __res
 __global__ __launch_bounds__(256) void bn_bwd_finalize_kernel(const double* __restrict__ part, int nblk, int F,
                                                               float* __restrict__ dgamma,
                                                               float* __restrict__ dbeta) {
-  const int f = blockIdx.x * 256 + threadIdx.x;
-  if (f >= F) return;
-  double s = 0.0, sx = 0.0;
-  for (int b = 0; b < nblk; ++b) {
-    s += part[(int64_t(b) * 2 + 0) * F + f];
-    sx += part[(int64_t(b) * 2 + 1) * F + f];
-  }
-  dbeta[f] = float(s);
-  dgamma[f] = float(sx);
+  double sums[2];
+  bn_sum_partials(part, nblk, F, sums);
+  const int f = blockIdx.x * 64 + (threadIdx.x & 63);
+  if (threadIdx.x >= 64 || f >= F) return;
+  dbeta[f] = float(sums[0]);
+  dgamma[f] = float(sums[1]);
 }
 
 // 64 x 64 tiles: dq_pre written row-major and, through LDS, transposed.
@@ -235,7 +249,7 @@ hipError_t launch_bn_partials(hipStream_t s, const float* q_pre, int64_t ntok, i
 
 hipError_t launch_bn_finalize(hipStream_t s, const double* part, int nblk, int64_t ntok, int F, float eps,
                               float* mean, float* rstd) {
-  hipLaunchKernelGGL(bn_finalize_kernel, dim3(unsigned((F + 255) / 256)), dim3(256), 0, s, part, nblk, ntok, F,
+  hipLaunchKernelGGL(bn_finalize_kernel, dim3(unsigned((F + 63) / 64)), dim3(256), 0, s, part, nblk, ntok, F,
                      eps, mean, rstd);
   return hipGetLastError();
 }
@@ -265,7 +279,7 @@ hipError_t launch_bn_bwd_finalize(hipStream_t s, const double* part, int nblk, i
                                   float* dgamma, float* dbeta, float* coef) {
   (void)gamma;
   (void)coef;
-  hipLaunchKernelGGL(bn_bwd_finalize_kernel, dim3(unsigned((F + 255) / 256)), dim3(256), 0, s, part, nblk, F,
+  hipLaunchKernelGGL(bn_bwd_finalize_kernel, dim3(unsigned((F + 63) / 64)), dim3(256), 0, s, part, nblk, F,
                      dgamma, dbeta);
   return hipGetLastError();
 }

@@ -325,6 +325,43 @@ __global__ __launch_bounds__(256) void transpose_kernel(const void* __restrict__
   }
 }
 
+// 64x64 tile transpose of 2-byte elements with 16-byte global accesses: rows
+// read 8 elements per thread, LDS tile padded by one dword per row, output rows
+// written 8 elements per thread.  Needs ld_in, ld_out, cols and rows_pad
+// multiples of 8 (rows in [rows, rows_pad) come out zero).
+__global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* __restrict__ in, int64_t rows, int64_t cols,
+                                                          int64_t ld_in, uint16_t* __restrict__ out, int64_t ld_out,
+                                                          int64_t rows_pad) {
+  __shared__ uint16_t tile[64][66];
+  const int64_t r0 = int64_t(blockIdx.y) * 64, c0 = int64_t(blockIdx.x) * 64;
+  const int t = threadIdx.x, tr = t >> 3, tc = (t & 7) * 8;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int rr = tr + pass * 32;
+    const int64_t r = r0 + rr, c = c0 + tc;
+    u32x4 v = {0, 0, 0, 0};
+    if (r < rows && c < cols) v = *reinterpret_cast<const u32x4*>(in + r * ld_in + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[rr][tc + 2 * e] = uint16_t(w[e] & 0xFFFFu);
+      tile[rr][tc + 2 * e + 1] = uint16_t(w[e] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int oc = tr + pass * 32;  // output row = input column c0 + oc
+    const int64_t orow = c0 + oc, ocol = r0 + tc;
+    if (orow < cols && ocol < rows_pad) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = uint32_t(tile[tc + 2 * e][oc]) | (uint32_t(tile[tc + 2 * e + 1][oc]) << 16);
+      *reinterpret_cast<u32x4*>(out + orow * ld_out + ocol) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+  }
+}
+
 __global__ void fill_f32_kernel(float* p, int64_t n, float v) {
   for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) p[i] = v;
 }
@@ -378,6 +415,11 @@ hipError_t launch_sum_splits(hipStream_t s, const float* part, int splits, int64
 hipError_t launch_transpose(hipStream_t s, const void* in, int64_t rows, int64_t cols, int64_t ld_in, void* out,
                             int64_t ld_out, int64_t rows_pad, int in_elem, int out_elem) {
   dim3 grid(unsigned((cols + 63) / 64), unsigned((rows_pad + 63) / 64));
+  if (in_elem == 2 && out_elem == 2 && ld_in % 8 == 0 && ld_out % 8 == 0 && cols % 8 == 0 && rows_pad % 8 == 0) {
+    hipLaunchKernelGGL(transpose16_kernel, grid, dim3(256), 0, s, static_cast<const uint16_t*>(in), rows, cols, ld_in,
+                       static_cast<uint16_t*>(out), ld_out, rows_pad);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, s, in, rows, cols, ld_in, out, ld_out, rows_pad,
                      in_elem, out_elem);
   return hipGetLastError();
