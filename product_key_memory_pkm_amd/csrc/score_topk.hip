@@ -258,6 +258,108 @@ __global__ __launch_bounds__(256) void pack_keys_kernel(const T* __restrict__ C,
   }
 }
 
+// Top-k of one score chunk for RPW rows of S (rows row0, row0 + rstep, ...),
+// merged into the running lists run[] (cb == 0: the chunk starts the row).
+// Columns [0, cwe) of each row hold the scores of columns cb + c; each row's
+// slot is reused as compaction scratch.  Selection: the k-th largest lane
+// maximum (a lower bound of the row's k-th largest score, bisection on
+// order-preserving keys with ballots) drops most scores by a float compare;
+// the <= 64 survivors are compacted and bitonic-sorted as (key, ~column) words;
+// rows with more survivors (heavy ties) take the exact path.  The rows are
+// worked on together so that their latency chains overlap.
+template <int NPL, int RPW>
+__device__ __forceinline__ void select_chunk(float* S, int sstride, int row0, int rstep, int cwe, int cb, int k,
+                                             int lane, uint64_t* run) {
+  float v[RPW][NPL];
+  float lmax[RPW];
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) {
+    const float* srow = S + size_t(row0 + q * rstep) * sstride;
+    lmax[q] = -INFINITY;
+    if constexpr (NPL >= 4) {
+#pragma unroll
+      for (int jj = 0; jj < NPL / 4; ++jj) {
+        const int c0 = 256 * jj + 4 * lane;  // a run starting below cwe ends inside the row (sstride >= cw + 4)
+        f32x4 t = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        if (c0 < cwe) t = *reinterpret_cast<const f32x4*>(srow + c0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[q][4 * jj + e] = c0 + e < cwe ? t[e] : -INFINITY;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) {
+        const int col = j * 64 + lane;
+        v[q][j] = col < cwe ? srow[col] : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) lmax[q] = fmaxf(lmax[q], v[q][j]);
+  }
+  // k-th largest lane maximum (a lower bound of the row's k-th largest score):
+  // bisection on order-preserving keys, with ballots
+  uint32_t lk[RPW], res[RPW];
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) {
+    lk[q] = float_key(lmax[q]);
+    res[q] = 0;
+  }
+  const int kc_ = k < cwe ? k : cwe;  // a chunk narrower than k keeps all its columns
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+      const uint32_t cand = res[q] | (1u << b);
+      if (popc64(ballot(lk[q] >= cand)) >= kc_) res[q] = cand;
+    }
+  }
+  int cnt[RPW], total[RPW], pos[RPW];
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) {
+    const float thr = key_float(res[q]);
+    cnt[q] = 0;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) cnt[q] += v[q][j] >= thr;
+    pos[q] = wave_excl_scan_dpp(cnt[q], &total[q]);
+  }
+  // compaction into the row's own LDS slot (its scores are in registers now)
+  // as (score bits, column) pairs; rows with more than 64 survivors (heavy
+  // ties) take the exact path, which writes finished (key, ~column) words
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) {
+    const float thr = key_float(res[q]);
+    if (total[q] <= 64) {
+      u32x2* slot = reinterpret_cast<u32x2*>(S + size_t(row0 + q * rstep) * sstride);
+#pragma unroll
+      for (int j = 0; j < NPL; ++j)
+        if (v[q][j] >= thr) slot[pos[q]++] = u32x2{__float_as_uint(v[q][j]), uint32_t(col_of<NPL>(j, lane))};
+    } else {
+      exact_topk<NPL>(v[q], kc_, lane, uint32_t(cb), reinterpret_cast<uint64_t*>(S + size_t(row0 + q * rstep) * sstride));
+    }
+  }
+  wave_lds_sync();
+  uint64_t key[RPW];
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) {
+    const u32x2* slot = reinterpret_cast<const u32x2*>(S + size_t(row0 + q * rstep) * sstride);
+    if (total[q] <= 64) {
+      const u32x2 e = lane < total[q] ? slot[lane] : u32x2{0u, 0u};
+      key[q] = lane < total[q]
+                   ? (uint64_t(float_key(__uint_as_float(e.x))) << 32) | uint32_t(~(uint32_t(cb) + e.y))
+                   : 0ull;
+    } else {
+      key[q] = lane < kc_ ? reinterpret_cast<const uint64_t*>(slot)[lane] : 0ull;
+    }
+  }
+  wave_sort_desc_u64_n<RPW>(key);
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) {
+    // the chunk's 32 largest words contain its top k (k <= 32)
+    const uint64_t top = lane < 32 ? key[q] : 0ull;
+    run[q] = cb == 0 ? top : merge_top32(run[q], top, lane);
+  }
+}
+
 template <typename T, int TM, int NPL>
 __global__ __launch_bounds__(kThreads) void score_topk_kernel(
     const T* __restrict__ q, int64_t ntok, int F, int dq, int half, int half_pad, int qstride,
@@ -355,96 +457,8 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(
     }
     __syncthreads();
 
-    // 3. per-row top-k of the chunk.  Each wave owns rows wave, wave+8, ... (RPW
-    // of them) and works on all of them at once, so the latency chains overlap.
-    float v[RPW][NPL];
-    float lmax[RPW];
-#pragma unroll
-    for (int q = 0; q < RPW; ++q) {
-      const float* srow = S + size_t(q * kWaves + wave) * sstride;
-      lmax[q] = -INFINITY;
-      if constexpr (NPL >= 4) {
-#pragma unroll
-        for (int jj = 0; jj < NPL / 4; ++jj) {
-          const int c0 = 256 * jj + 4 * lane;  // a run starting below cwe ends inside the row (sstride >= cw + 4)
-          f32x4 t = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-          if (c0 < cwe) t = *reinterpret_cast<const f32x4*>(srow + c0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[q][4 * jj + e] = c0 + e < cwe ? t[e] : -INFINITY;
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < NPL; ++j) {
-          const int col = j * 64 + lane;
-          v[q][j] = col < cwe ? srow[col] : -INFINITY;
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < NPL; ++j) lmax[q] = fmaxf(lmax[q], v[q][j]);
-    }
-    // k-th largest lane maximum (a lower bound of the row's k-th largest score):
-    // bisection on order-preserving keys, with ballots
-    uint32_t lk[RPW], res[RPW];
-#pragma unroll
-    for (int q = 0; q < RPW; ++q) {
-      lk[q] = float_key(lmax[q]);
-      res[q] = 0;
-    }
-    const int kc_ = k < cwe ? k : cwe;  // a chunk narrower than k keeps all its columns
-#pragma unroll
-    for (int b = 31; b >= 0; --b) {
-#pragma unroll
-      for (int q = 0; q < RPW; ++q) {
-        const uint32_t cand = res[q] | (1u << b);
-        if (popc64(ballot(lk[q] >= cand)) >= kc_) res[q] = cand;
-      }
-    }
-    int cnt[RPW], total[RPW], pos[RPW];
-#pragma unroll
-    for (int q = 0; q < RPW; ++q) {
-      const float thr = key_float(res[q]);
-      cnt[q] = 0;
-#pragma unroll
-      for (int j = 0; j < NPL; ++j) cnt[q] += v[q][j] >= thr;
-      pos[q] = wave_excl_scan_dpp(cnt[q], &total[q]);
-    }
-    // compaction into the row's own LDS slot (its scores are in registers now)
-    // as (score bits, column) pairs; rows with more than 64 survivors (heavy
-    // ties) take the exact path, which writes finished (key, ~column) words
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int q = 0; q < RPW; ++q) {
-      const float thr = key_float(res[q]);
-      if (total[q] <= 64) {
-        u32x2* slot = reinterpret_cast<u32x2*>(S + size_t(q * kWaves + wave) * sstride);
-#pragma unroll
-        for (int j = 0; j < NPL; ++j)
-          if (v[q][j] >= thr) slot[pos[q]++] = u32x2{__float_as_uint(v[q][j]), uint32_t(col_of<NPL>(j, lane))};
-      } else {
-        exact_topk<NPL>(v[q], kc_, lane, uint32_t(cb), reinterpret_cast<uint64_t*>(S + size_t(q * kWaves + wave) * sstride));
-      }
-    }
-    wave_lds_sync();
-    uint64_t key[RPW];
-#pragma unroll
-    for (int q = 0; q < RPW; ++q) {
-      const u32x2* slot = reinterpret_cast<const u32x2*>(S + size_t(q * kWaves + wave) * sstride);
-      if (total[q] <= 64) {
-        const u32x2 e = lane < total[q] ? slot[lane] : u32x2{0u, 0u};
-        key[q] = lane < total[q]
-                     ? (uint64_t(float_key(__uint_as_float(e.x))) << 32) | uint32_t(~(uint32_t(cb) + e.y))
-                     : 0ull;
-      } else {
-        key[q] = lane < kc_ ? reinterpret_cast<const uint64_t*>(slot)[lane] : 0ull;
-      }
-    }
-    wave_sort_desc_u64_n<RPW>(key);
-#pragma unroll
-    for (int q = 0; q < RPW; ++q) {
-      // the chunk's 32 largest words contain its top k (k <= 32)
-      const uint64_t top = lane < 32 ? key[q] : 0ull;
-      run[q] = cb == 0 ? top : merge_top32(run[q], top, lane);
-    }
+    // 3. per-row top-k of the chunk; wave w owns rows w, w+8, ...
+    select_chunk<NPL, RPW>(S, sstride, wave, kWaves, cwe, cb, k, lane, run);
     __syncthreads();  // the next chunk's scores overwrite S
   }
 #pragma unroll
@@ -457,6 +471,7 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(
     }
   }
 }
+
 
 template <typename T, int TM>
 void launch_tm(hipStream_t s, const Plan& pl, const void* q, int64_t ntok, int heads, int dq, const u32x4* C,
