@@ -257,7 +257,7 @@ def backward_check(cfg, inp, gpu, g, dV_np, dY):
         assert P.fro_rel_err(P.to_f64(g["dx"]), gb["dx"]) <= tol
 
 
-BWD_CASES = ["tiny", "small", "bf16_mid", "ragged", "one_token", "k1", "tau", "int_ties"]
+BWD_CASES = ["tiny", "small", "bf16_mid", "ragged", "one_token", "k1", "tau", "int_ties", "hot", "hot_bf16"]
 
 
 def masked_dy(inp, gpu_idx, ref_rows):

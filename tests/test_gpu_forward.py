@@ -301,6 +301,12 @@ FWD_CASES = {
                 seed=25, temperature=0.25),
     "int_ties": _cfg(T=40, d=8, heads=2, dq=8, n_keys=12, n_keys2=9, topk=6, d_value=8, dtype="f32", bn=False,
                      seed=26, x_kind="int", wq_kind="int", key_kind="int", int_range=1),
+    # few slots, many tokens: every value row gets hundreds of lookups and every
+    # sub-key thousands, so the backward splits them into chunks
+    "hot": _cfg(T=6000, d=32, heads=2, dq=32, n_keys=8, n_keys2=8, topk=8, d_value=40, dtype="f32", bn=True,
+                seed=27),
+    "hot_bf16": _cfg(T=6000, d=64, heads=2, dq=64, n_keys=16, n_keys2=16, topk=16, d_value=64, dtype="bf16",
+                     bn=True, seed=28),
 }
 
 
