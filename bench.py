@@ -230,7 +230,7 @@ def main():
         "wall_s_timed_region": wall,
         "roofline": roof(dom),
         "roofline_other": dict({n: roof(n) for n in kern if n != dom},
-                               score_topk={"kernel": "score_topk (a2 MFMA scores + a3 per-half top-k)", "bound": "mfma",
+                               score_topk={"kernel": "score_topk (a3 MFMA scores + a4 per-half top-k)", "bound": "mfma",
                                            "achieved": score_tf, "peak": score_peak, "unit": "TFLOP/s",
                                            "frac": score_tf / score_peak, "traffic": None,
                                            "alg_flops_per_launch": score_flops, "avg_launch_ms": score_ms}),

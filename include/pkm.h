@@ -12,6 +12,13 @@
  *   y[t]  = sum_h sum_s w[t,h,s] * V[row[t,h,s], :]
  * The residual add (x + y) belongs to the caller.
  *
+ * Steps, as named by the stage entry points and the kernels' comments:
+ *   a1 projection, a2 BatchNorm, a3 sub-key scores, a4 per-half top-k,
+ *   a5 candidate merge, top-k and softmax, a6 weighted sum of value rows;
+ *   backward: a7 dw and the softmax backward, a8 value-row gradient (touched
+ *   rows only), a9 query and sub-key gradients, a10 BatchNorm backward and the
+ *   projection gradients (dW_q, dx).
+ *
  * Sources (web pages on product-key memory layers):
  *  - "Meta AI 可扩展内存层" (zskr.cn article on Meta AI's scalable memory layers):
  *    section 3.2 (query projection, top-k similarity, softmax, weighted sum),
