@@ -48,8 +48,10 @@
  *    returns a non-zero pkm_status, touches nothing, and pkm_last_error() gives a
  *    message.  PKM_ERR_HIP reports a failed launch; a device-side fault shows up
  *    at the caller's next synchronisation.  No C++ exception crosses the ABI.
- *  - Threads: a handle is immutable after pkm_create; concurrent calls on one
- *    handle are safe when they use distinct workspaces and outputs.
+ *  - Threads: a handle's configuration is immutable after pkm_create;
+ *    concurrent calls on one handle are safe when they use distinct workspaces
+ *    and outputs (pkm_backward serialises only the enqueueing of its side-stream
+ *    part).
  *  - Inputs must be finite (not checked on the device).
  */
 #ifndef PKM_H_
@@ -108,7 +110,12 @@ typedef struct {
   float* bn_rstd; /* [h*dq] 1/sqrt(var + eps) (BN_BATCH; may be NULL with BN_NONE) */
 } pkm_saved;
 
-/* Validate cfg and build a handle (host memory only, no HIP call). */
+/* Validate cfg and build a handle.  Besides host state, the handle owns one
+ * HIP stream (default priority, non-blocking) and two events created on the
+ * device current at this call; pkm_backward uses them to run the sub-key
+ * gradients beside the projection gradients.  If they cannot be created (no
+ * device), pkm_backward runs on the caller's stream alone.  No device memory
+ * is allocated.  pkm_destroy releases them. */
 pkm_status pkm_create(const pkm_config* cfg, pkm_handle_t* out);
 pkm_status pkm_destroy(pkm_handle_t handle);
 /* The config the handle was created with. */
@@ -135,7 +142,11 @@ pkm_status pkm_forward(pkm_handle_t handle, void* stream, int64_t T, const void*
  *   dC [h, |C|, dq/2], dCp [h, |C'|, dq/2], dWq [h*dq, d_in] fp32 (overwritten);
  *   dgamma, dbeta [h*dq] fp32 (BN_BATCH; may be NULL with BN_NONE);
  *   dx [T, d_in] storage dtype, may be NULL (not computed).
- *   ws: workspace of ws_bytes >= pkm_workspace_size(handle, T, 1). */
+ *   ws: workspace of ws_bytes >= pkm_workspace_size(handle, T, 1).
+ * On the device current at pkm_create, part of the work (dC, dC') runs on the
+ * handle's side stream, forked from and joined back into `stream` with events,
+ * so all outputs are complete once `stream` has reached the end of this call
+ * (also under stream capture: the side stream joins the capture). */
 pkm_status pkm_backward(pkm_handle_t handle, void* stream, int64_t T, const void* dY, const void* x,
                         const void* Wq, const float* bn_gamma, const void* C, const void* Cp,
                         const void* V, const pkm_saved* saved, float* dV, int32_t* touched,

@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -20,6 +21,12 @@ struct pkm_handle_s {
   int F;      // heads * dq
   int elem;   // bytes per storage element
   int row_bits;
+  // second stream of pkm_backward (sub-key gradients beside the projection
+  // gradients), with its fork/join events; absent (null) if creation failed
+  int device;
+  hipStream_t side;
+  hipEvent_t fork, join;
+  std::mutex side_mu;  // one backward at a time enqueues on the side stream
 };
 
 namespace {
@@ -258,12 +265,12 @@ pkm_status run_value_grad(const pkm_handle_s* h, hipStream_t s, int64_t T, const
   return run_value_grad_grouped(h, s, T, w, dY, V, dV, dw, n_touched, ws);
 }
 
-pkm_status run_subkey_grad(const pkm_handle_s* h, hipStream_t s, int64_t T, const int32_t* idx, const float* w,
-                           const float* dw, const void* q, const void* C, const void* Cp, float* dq, float* dC,
-                           float* dCp, void* ws) {
+// Softmax backward and dq; per-slot sub-key sort keys and coefficients of
+// the two halves for the sub-key gradients.
+pkm_status run_softmax_bwd(const pkm_handle_s* h, hipStream_t s, int64_t T, const int32_t* idx, const float* w,
+                           const float* dw, const void* C, const void* Cp, float* dq, void* ws) {
   const pkm_config& c = h->cfg;
   const BwdLayout L = bwd_layout(h, T);
-  const int64_t N = T * c.heads * c.topk;
   // per-slot sort keys and coefficients of the two halves
   uint32_t* key1 = at<uint32_t>(ws, L.key1);
   uint32_t* key2 = at<uint32_t>(ws, L.key2);
@@ -272,6 +279,21 @@ pkm_status run_subkey_grad(const pkm_handle_s* h, hipStream_t s, int64_t T, cons
   PKM_HIP(launch_softmax_bwd_dq(s, c.dtype, idx, w, dw, C, Cp, T, c.heads, c.d_query, c.topk, c.n_keys, c.n_keys2,
                                 1.0f / c.temperature, dq, key1, coef1, key2, coef2),
           "softmax backward / query gradient");
+  return PKM_OK;
+}
+
+// Sub-key gradients dC, dC' from the per-slot keys and coefficients written by
+// run_softmax_bwd.  Touches only its own workspace regions (sort arrays,
+// segments, long-run lists), so it may run beside run_query_grad.
+pkm_status run_subkey_halves(const pkm_handle_s* h, hipStream_t s, int64_t T, const void* q, float* dC, float* dCp,
+                             void* ws) {
+  const pkm_config& c = h->cfg;
+  const BwdLayout L = bwd_layout(h, T);
+  const int64_t N = T * c.heads * c.topk;
+  const uint32_t* key1 = at<uint32_t>(ws, L.key1);
+  const uint32_t* key2 = at<uint32_t>(ws, L.key2);
+  const float* coef1 = at<float>(ws, L.ds);
+  const float* coef2 = at<float>(ws, L.coef2);
   for (int half_sel = 0; half_sel < 2; ++half_sel) {
     const int nkeys = half_sel ? c.n_keys2 : c.n_keys;
     float* out = half_sel ? dCp : dC;
@@ -295,6 +317,13 @@ pkm_status run_subkey_grad(const pkm_handle_s* h, hipStream_t s, int64_t T, cons
             "sub-key gradient");
   }
   return PKM_OK;
+}
+
+pkm_status run_subkey_grad(const pkm_handle_s* h, hipStream_t s, int64_t T, const int32_t* idx, const float* w,
+                           const float* dw, const void* q, const void* C, const void* Cp, float* dq, float* dC,
+                           float* dCp, void* ws) {
+  PKM_TRY(run_softmax_bwd(h, s, T, idx, w, dw, C, Cp, dq, ws));
+  return run_subkey_halves(h, s, T, q, dC, dCp, ws);
 }
 
 pkm_status run_query_grad(const pkm_handle_s* h, hipStream_t s, int64_t T, const float* dq, const void* x,
@@ -425,11 +454,43 @@ pkm_status pkm_create(const pkm_config* cfg, pkm_handle_t* out) {
   int bits = 0;
   while ((int64_t(1) << bits) < int64_t(c.n_keys) * c.n_keys2) ++bits;
   h->row_bits = bits;
+  // side stream on the current device (default priority); without a device the
+  // backward simply stays on the caller's stream
+  h->device = -1;
+  h->side = nullptr;
+  h->fork = h->join = nullptr;
+  int dev = -1;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    hipStream_t st = nullptr;
+    hipEvent_t e1 = nullptr, e2 = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) == hipSuccess &&
+        hipEventCreateWithFlags(&e1, hipEventDisableTiming) == hipSuccess &&
+        hipEventCreateWithFlags(&e2, hipEventDisableTiming) == hipSuccess) {
+      h->device = dev;
+      h->side = st;
+      h->fork = e1;
+      h->join = e2;
+    } else {
+      if (st) (void)hipStreamDestroy(st);
+      if (e1) (void)hipEventDestroy(e1);
+      if (e2) (void)hipEventDestroy(e2);
+    }
+  }
+  (void)hipGetLastError();  // a failed creation above must not surface in a later call's status
   *out = h;
   return PKM_OK;
 }
 
 pkm_status pkm_destroy(pkm_handle_t handle) {
+  if (handle != nullptr && handle->side != nullptr) {
+    int prev = -1;
+    const bool switched = hipGetDevice(&prev) == hipSuccess && prev != handle->device &&
+                          hipSetDevice(handle->device) == hipSuccess;
+    (void)hipStreamDestroy(handle->side);
+    (void)hipEventDestroy(handle->fork);
+    (void)hipEventDestroy(handle->join);
+    if (switched) (void)hipSetDevice(prev);
+  }
   delete handle;
   return PKM_OK;
 }
@@ -511,7 +572,23 @@ pkm_status pkm_backward(pkm_handle_t handle, void* stream, int64_t T, const void
   float* dw = at<float>(ws, L.dw);
   float* dq = at<float>(ws, L.dq);
   PKM_TRY(run_value_grad(handle, s, T, saved->idx, saved->w, dY, V, dV, touched, n_touched, dw, ws));
-  PKM_TRY(run_subkey_grad(handle, s, T, saved->idx, saved->w, dw, saved->q, C, Cp, dq, dC, dCp, ws));
+  PKM_TRY(run_softmax_bwd(handle, s, T, saved->idx, saved->w, dw, C, Cp, dq, ws));
+  // The sub-key gradients (sorts, L2 gathers) and the projection gradients
+  // (BatchNorm backward, MFMA GEMMs) only share inputs: run them side by side.
+  int dev = -1;
+  pkm_handle_s* hm = const_cast<pkm_handle_s*>(handle);
+  if (hm->side != nullptr && hipGetDevice(&dev) == hipSuccess && dev == hm->device) {
+    std::lock_guard<std::mutex> lock(hm->side_mu);
+    PKM_HIP(hipEventRecord(hm->fork, s), "fork event");
+    PKM_HIP(hipStreamWaitEvent(hm->side, hm->fork, 0), "side stream wait");
+    PKM_TRY(run_subkey_halves(handle, hm->side, T, saved->q, dC, dCp, ws));
+    PKM_HIP(hipEventRecord(hm->join, hm->side), "join event");
+    PKM_TRY(run_query_grad(handle, s, T, dq, x, Wq, bn_gamma, saved, dWq, bn ? dgamma : nullptr,
+                           bn ? dbeta : nullptr, dx, ws));
+    PKM_HIP(hipStreamWaitEvent(s, hm->join, 0), "join wait");
+    return PKM_OK;
+  }
+  PKM_TRY(run_subkey_halves(handle, s, T, saved->q, dC, dCp, ws));
   PKM_TRY(run_query_grad(handle, s, T, dq, x, Wq, bn_gamma, saved, dWq, bn ? dgamma : nullptr, bn ? dbeta : nullptr,
                          dx, ws));
   return PKM_OK;
