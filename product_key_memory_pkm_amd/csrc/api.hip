@@ -386,7 +386,8 @@ pkm_status check_saved(const pkm_handle_s* h, const pkm_saved* sv, bool need_sel
 pkm_status zero_grads(const pkm_handle_s* h, hipStream_t s, int64_t* n_touched, float* dC, float* dCp, float* dWq,
                       float* dgamma, float* dbeta) {
   const pkm_config& c = h->cfg;
-  if (n_touched) PKM_HIP(hipMemsetAsync(n_touched, 0, sizeof(int64_t), s), "clear n_touched");
+  // a fill kernel rather than a memset node (safe under stream capture)
+  if (n_touched) PKM_HIP(launch_fill_f32(s, reinterpret_cast<float*>(n_touched), 2, 0.f), "clear n_touched");
   if (dC) PKM_HIP(launch_fill_f32(s, dC, int64_t(c.heads) * c.n_keys * h->half, 0.f), "clear dC");
   if (dCp) PKM_HIP(launch_fill_f32(s, dCp, int64_t(c.heads) * c.n_keys2 * h->half, 0.f), "clear dCp");
   if (dWq) PKM_HIP(launch_fill_f32(s, dWq, int64_t(h->F) * c.d_in, 0.f), "clear dWq");
