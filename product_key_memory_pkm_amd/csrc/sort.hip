@@ -109,16 +109,33 @@ __global__ __launch_bounds__(256) void scan_apply_kernel(const uint32_t* __restr
     }
 }
 
+// Digit histogram of one tile.  Lanes holding the same digit are matched with
+// ballots first, so each distinct digit of a wave takes one LDS atomic: skewed
+// keys (a few hot sub-keys) would otherwise serialise on one counter.
 __global__ __launch_bounds__(256) void radix_hist_kernel(const uint32_t* __restrict__ keys, int64_t n, int shift,
                                                          int nb, uint32_t* __restrict__ hist) {
   __shared__ uint32_t cnt[256];
   cnt[threadIdx.x] = 0;
   __syncthreads();
   const int64_t base = int64_t(blockIdx.x) * kTile;
-#pragma unroll 4
+  uint32_t key[kTile / 256];
+#pragma unroll
   for (int i = 0; i < kTile / 256; ++i) {
     const int64_t e = base + i * 256 + threadIdx.x;
-    if (e < n) atomicAdd(&cnt[(keys[e] >> shift) & 0xFF], 1u);
+    key[i] = e < n ? keys[e] : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < kTile / 256; ++i) {
+    const bool ok = base + i * 256 + threadIdx.x < n;
+    const uint32_t d = (key[i] >> shift) & 0xFF;
+    uint64_t peers = ballot(ok);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool bit = (d >> b) & 1u;
+      const uint64_t m = ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    if (ok && lanes_below(peers) == 0) atomicAdd(&cnt[d], uint32_t(popc64(peers)));
   }
   __syncthreads();
   hist[int64_t(threadIdx.x) * nb + blockIdx.x] = cnt[threadIdx.x];
@@ -189,19 +206,42 @@ __global__ __launch_bounds__(256) void radix_scatter_kernel(const uint32_t* __re
   }
 }
 
+// Flag bits of the 16 sorted keys k[b0 .. b0+15] (bit i set when b0+i starts a
+// segment: the first key or one that differs from its predecessor).  A full
+// group is read with four 16-byte loads; the ragged tail element by element.
+__device__ __forceinline__ uint32_t seg_flags16(const uint32_t* __restrict__ k, int64_t n, int64_t b0) {
+  uint32_t v[16];
+  if (b0 + 16 <= n && (reinterpret_cast<uintptr_t>(k) & 15u) == 0) {
+    const uint4* p = reinterpret_cast<const uint4*>(k + b0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 q = p[j];
+      v[4 * j] = q.x;
+      v[4 * j + 1] = q.y;
+      v[4 * j + 2] = q.z;
+      v[4 * j + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = b0 + i < n ? k[b0 + i] : 0u;
+  }
+  uint32_t prev = b0 > 0 && b0 < n ? k[b0 - 1] : ~v[0];
+  uint32_t f = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (b0 + i < n && v[i] != prev) f |= 1u << i;
+    prev = v[i];
+  }
+  return f;
+}
+
 // Segment scan over flag(i) = (i == 0 || k[i] != k[i-1]): per-block flag counts.
 __global__ __launch_bounds__(256) void seg_reduce_kernel(const uint32_t* __restrict__ k, int64_t n,
                                                          uint32_t* __restrict__ part) {
   __shared__ uint32_t sh[4];
   const int64_t b0 = int64_t(blockIdx.x) * kScanBlock + threadIdx.x * 16;
-  uint32_t s = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t e = b0 + i;
-    if (e < n) s += (e == 0 || k[e] != k[e - 1]) ? 1u : 0u;
-  }
   uint32_t tot;
-  block_excl_scan(s, sh, &tot);
+  block_excl_scan(uint32_t(__popc(seg_flags16(k, n, b0))), sh, &tot);
   if (threadIdx.x == 0) part[blockIdx.x] = tot;
 }
 
@@ -214,12 +254,7 @@ __global__ __launch_bounds__(256) void seg_apply_kernel(const uint32_t* __restri
                                                         int32_t* __restrict__ touched, int64_t* __restrict__ count) {
   __shared__ uint32_t sh[4];
   const int64_t b0 = int64_t(blockIdx.x) * kScanBlock + threadIdx.x * 16;
-  uint32_t f = 0;  // flag bits of this thread's 16 elements
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t e = b0 + i;
-    if (e < n && (e == 0 || k[e] != k[e - 1])) f |= 1u << i;
-  }
+  const uint32_t f = seg_flags16(k, n, b0);
   uint32_t tot;
   uint32_t rank = block_excl_scan(uint32_t(__popc(f)), sh, &tot) + part[blockIdx.x];
 #pragma unroll
