@@ -44,6 +44,20 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Wave-wide maximum / minimum, the result in every lane (xor butterfly).
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int st = 1; st < 64; st <<= 1) v = fmaxf(v, __uint_as_float(xor_lane(__float_as_uint(v), st)));
+  return v;
+}
+__device__ __forceinline__ float wave_min_f32(float v) {
+#pragma unroll
+  for (int st = 1; st < 64; st <<= 1) v = fminf(v, __uint_as_float(xor_lane(__float_as_uint(v), st)));
+  return v;
+}
+
+constexpr int kBoundSteps = 12;  // halvings of the selection bound's search range
+
 __device__ __forceinline__ int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
 }
@@ -183,8 +197,10 @@ Plan make_plan(int dtype, int half, int ncols) {
   for (int cw = full < kMaxChunk ? full : kMaxChunk; cw >= 64 && p.TM == 0; cw = round_up(cw / 2, 64)) {
     int npl = 1;
     while (npl * 64 < cw) npl *= 2;
-    // a row's slot also takes up to 64 compacted (key, ~column) words: >= 128 floats
-    const int sstride = (cw > 128 ? cw : 128) + 4;
+    // a row's slot also takes the compacted (score, column) pairs: 64 of them,
+    // plus 64 spare entries when a lane holds >= 4 values (>= 128 / 256 floats)
+    const int smin = npl >= 4 ? 256 : 128;
+    const int sstride = (cw > smin ? cw : smin) + 4;
     for (int tm = 64; tm >= 16; tm /= 2) {
       const size_t lds = size_t(tm) * p.qstride * e + size_t(tm) * sstride * 4;
       if (lds <= kLdsLimit && (tm / kWaves) * npl <= 64 && tm >= (cw > 256 ? 32 : 16)) {
@@ -202,7 +218,8 @@ Plan make_plan(int dtype, int half, int ncols) {
     const int cw = full < 256 ? full : 256;
     int npl = 1;
     while (npl * 64 < cw) npl *= 2;
-    const int sstride = (cw > 128 ? cw : 128) + 4;
+    const int smin = npl >= 4 ? 256 : 128;
+    const int sstride = (cw > smin ? cw : smin) + 4;
     const size_t lds = size_t(16) * p.qstride * e + size_t(16) * sstride * 4;
     if (lds <= kLdsLimit) {
       p.TM = 16;
@@ -295,27 +312,41 @@ __device__ __forceinline__ void select_chunk(float* S, int sstride, int row0, in
 #pragma unroll
     for (int j = 0; j < NPL; ++j) lmax[q] = fmaxf(lmax[q], v[q][j]);
   }
-  // k-th largest lane maximum (a lower bound of the row's k-th largest score):
-  // bisection on order-preserving keys, with ballots
-  uint32_t lk[RPW], res[RPW];
+  // A lower bound of the row's k-th largest score: any value b with at least k
+  // lane maxima >= b (k distinct lanes then hold a score >= b).  Bisection on
+  // the value between the smallest and the largest finite lane maximum keeps
+  // that invariant at the low end; kBoundSteps halvings leave the bound within
+  // 1/4096 of that range below the k-th largest lane maximum, which lets a few
+  // more scores through than the exact value would at a third of the
+  // dependent ballot steps.  With fewer than k finite lane maxima the bound is
+  // -inf (every score survives and the row takes the exact path).
+  const int kc_ = k < cwe ? k : cwe;  // a chunk narrower than k keeps all its columns
+  float lo[RPW], hi[RPW];
 #pragma unroll
   for (int q = 0; q < RPW; ++q) {
-    lk[q] = float_key(lmax[q]);
-    res[q] = 0;
+    hi[q] = wave_max_f32(lmax[q]);
+    lo[q] = wave_min_f32(lmax[q] == -INFINITY ? INFINITY : lmax[q]);
   }
-  const int kc_ = k < cwe ? k : cwe;  // a chunk narrower than k keeps all its columns
+  bool few[RPW];
 #pragma unroll
-  for (int b = 31; b >= 0; --b) {
+  for (int q = 0; q < RPW; ++q) few[q] = popc64(ballot(lmax[q] != -INFINITY)) < kc_;
+#pragma unroll
+  for (int it = 0; it < kBoundSteps; ++it) {
 #pragma unroll
     for (int q = 0; q < RPW; ++q) {
-      const uint32_t cand = res[q] | (1u << b);
-      if (popc64(ballot(lk[q] >= cand)) >= kc_) res[q] = cand;
+      const float mid = lo[q] + (hi[q] - lo[q]) * 0.5f;
+      const bool ok = popc64(ballot(lmax[q] >= mid)) >= kc_;
+      lo[q] = ok ? mid : lo[q];
+      hi[q] = ok ? hi[q] : mid;
     }
   }
+  float thrv[RPW];
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) thrv[q] = few[q] ? -INFINITY : lo[q];
   int cnt[RPW], total[RPW], pos[RPW];
 #pragma unroll
   for (int q = 0; q < RPW; ++q) {
-    const float thr = key_float(res[q]);
+    const float thr = thrv[q];
     cnt[q] = 0;
 #pragma unroll
     for (int j = 0; j < NPL; ++j) cnt[q] += v[q][j] >= thr;
@@ -327,12 +358,23 @@ __device__ __forceinline__ void select_chunk(float* S, int sstride, int row0, in
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int q = 0; q < RPW; ++q) {
-    const float thr = key_float(res[q]);
+    const float thr = thrv[q];
     if (total[q] <= 64) {
       u32x2* slot = reinterpret_cast<u32x2*>(S + size_t(row0 + q * rstep) * sstride);
+      if constexpr (NPL >= 4) {
+        // every value is stored: survivors at their rank, the rest into the
+        // lane's own spare entry 64 + lane (no per-value branch)
 #pragma unroll
-      for (int j = 0; j < NPL; ++j)
-        if (v[q][j] >= thr) slot[pos[q]++] = u32x2{__float_as_uint(v[q][j]), uint32_t(col_of<NPL>(j, lane))};
+        for (int j = 0; j < NPL; ++j) {
+          const bool keep = v[q][j] >= thr;
+          slot[keep ? pos[q] : 64 + lane] = u32x2{__float_as_uint(v[q][j]), uint32_t(col_of<NPL>(j, lane))};
+          pos[q] += keep ? 1 : 0;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NPL; ++j)
+          if (v[q][j] >= thr) slot[pos[q]++] = u32x2{__float_as_uint(v[q][j]), uint32_t(col_of<NPL>(j, lane))};
+      }
     } else {
       exact_topk<NPL>(v[q], kc_, lane, uint32_t(cb), reinterpret_cast<uint64_t*>(S + size_t(row0 + q * rstep) * sstride));
     }
@@ -439,20 +481,19 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(
 #pragma unroll
         for (int c = 0; c < CT; ++c)
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) acc[rt][c] = TR::mma(a[rt], bcur[c], acc[rt][c]);
+          for (int rt = 0; rt < RT; ++rt) acc[rt][c] = TR::mma(bcur[c], a[rt], acc[rt][c]);
 #pragma unroll
         for (int c = 0; c < CT; ++c) bcur[c] = bnext[c];
       }
-      // D layout of a 16x16 MFMA tile: lane l holds column l%16, rows 4*(l/16)+i.
+      // The sub-keys are the MFMA's first operand, so the 16x16 tile is
+      // D[key][token]: lane l holds token l%16 and keys 4*(l/16)+i, i.e. four
+      // consecutive scores of one query row, stored with one 16-byte write.
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
-          if (g0 + c < nct) {
-            const int col = (g0 + c) * 16 + lrow;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) S[size_t(rt * 16 + lgrp * 4 + i) * sstride + col] = acc[rt][c][i];
-          }
+          if (g0 + c < nct)
+            *reinterpret_cast<f32x4*>(S + size_t(rt * 16 + lrow) * sstride + (g0 + c) * 16 + lgrp * 4) = acc[rt][c];
         }
     }
     __syncthreads();
