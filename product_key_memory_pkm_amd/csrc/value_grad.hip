@@ -23,7 +23,7 @@ namespace pkm {
 
 namespace {
 
-constexpr int kVgU = 2;
+constexpr int kVgU = 4;  // dY rows in flight per wave
 // <a, v> over one 16-byte vector, accumulated into c.  bf16: v_dot2_f32_bf16 on
 // packed pairs (products exact in fp32); fp32: four FMAs.
 template <typename T>
@@ -89,7 +89,7 @@ struct LaneVecs {
 
 // g += sum over sorted lookups [lo, hi) of w * dY[t]; dw of each lookup = <dY[t], V[r]>.
 // Each lookup costs one dY row read, NVL dot products, one DPP wave reduction and
-// the fp32 FMAs of w*dY; two lookups are in flight per step.
+// the fp32 FMAs of w*dY; kVgU lookups are in flight per step.
 template <typename T, int NVL>
 __device__ __forceinline__ void vg_accumulate(const VgArgs& a, const LaneVecs<NVL>& lv, const u32x4* vr, int lo,
                                               int hi, float (*g)[Vec16<T>::N]) {
@@ -160,6 +160,25 @@ __device__ __forceinline__ void vg_store(const LaneVecs<NVL>& lv, float* drow, c
   }
 }
 
+// dst = the lane's part of an fp32 row (zeros for the out-of-range last vector)
+template <typename T, int NVL>
+__device__ __forceinline__ void vg_load_f32(const LaneVecs<NVL>& lv, const float* src, float (*dst)[Vec16<T>::N]) {
+  constexpr int E = Vec16<T>::N;
+#pragma unroll
+  for (int m = 0; m < NVL; ++m) {
+    const bool ok = m < NVL - 1 || lv.last_ok;
+    const float* p = src + (lv.voff[m] / 16) * E;
+#pragma unroll
+    for (int q4 = 0; q4 < E / 4; ++q4) {
+      const f32x4 o = ok ? *reinterpret_cast<const f32x4*>(p + q4 * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      dst[m][q4 * 4 + 0] = o.x;
+      dst[m][q4 * 4 + 1] = o.y;
+      dst[m][q4 * 4 + 2] = o.z;
+      dst[m][q4 * 4 + 3] = o.w;
+    }
+  }
+}
+
 template <typename T, int NVL>
 __device__ __forceinline__ void vg_add_from(const LaneVecs<NVL>& lv, const float* src, float (*g)[Vec16<T>::N]) {
   constexpr int E = Vec16<T>::N;
@@ -224,6 +243,12 @@ __global__ __launch_bounds__(256) void value_grad_kernel(VgArgs a) {
     const uint32_t r = a.sorted_rows[lo];
     u32x4 vr[NVL];
     vg_load_row<T, NVL>(a, lv, r, vr);
+    // the old gradient row of a short run is fetched now, beside the value
+    // row, so that its latency overlaps the lookups; it is added to the sum at
+    // the end (the same order of additions as reading it there)
+    const bool add_old = !chunk && a.accumulate != 0;  // wave-uniform
+    float old[NVL][E];
+    if (add_old) vg_load_f32<T, NVL>(lv, a.dV + size_t(r) * dv, old);
     float g[NVL][E];
 #pragma unroll
     for (int m = 0; m < NVL; ++m)
@@ -232,10 +257,17 @@ __global__ __launch_bounds__(256) void value_grad_kernel(VgArgs a) {
     const int clo = lo + j * kVgChunk;
     const int chi = chunk ? min(hi, clo + kVgChunk) : hi;
     vg_accumulate<T, NVL>(a, lv, vr, clo, chi, g);
-    if (chunk)
+    if (chunk) {
       vg_store<T, NVL>(lv, a.partial + size_t(it) * dv, g, false);
-    else
-      vg_store<T, NVL>(lv, a.dV + size_t(r) * dv, g, a.accumulate != 0);
+    } else {
+      if (add_old) {
+#pragma unroll
+        for (int m = 0; m < NVL; ++m)
+#pragma unroll
+          for (int q = 0; q < E; ++q) g[m][q] += old[m][q];
+      }
+      vg_store<T, NVL>(lv, a.dV + size_t(r) * dv, g, false);
+    }
   }
 }
 
