@@ -24,6 +24,7 @@ struct pkm_handle_s {
   // second stream of pkm_backward (sub-key gradients beside the projection
   // gradients), with its fork/join events; absent (null) if creation failed
   int device;
+  int cus;  // compute units of the device (split-K sizing)
   hipStream_t side;
   hipEvent_t fork, join;
   std::mutex side_mu;  // one backward at a time enqueues on the side stream
@@ -78,6 +79,11 @@ struct BwdLayout {
       dqpre, dqpre_t, x_t, wq_t, split, aux, total;
   int splits;
   int64_t tpad;
+  // leading dimensions of the GEMM operands written here: 64 elements past a
+  // multiple of 64 so that a tile's rows do not all start at the same offset
+  // modulo a large power of two
+  int64_t ldt;  // dqpre_t, x_t: [F | d_in, ldt], columns [0, tpad) used
+  int64_t ldf;  // dqpre: [T, ldf]; wq_t: [d_in, ldf]
 };
 
 FwdLayout fwd_layout(const pkm_handle_s* h, int64_t T) {
@@ -95,13 +101,9 @@ FwdLayout fwd_layout(const pkm_handle_s* h, int64_t T) {
 }
 
 int dwq_splits(const pkm_handle_s* h, int64_t tpad) {
-  const int64_t tiles = ((h->F + 127) / 128) * ((h->cfg.d_in + 127) / 128);
-  int64_t s = (2048 + tiles - 1) / tiles;
-  const int64_t maxs = tpad / 256 > 1 ? tpad / 256 : 1;
-  if (s > maxs) s = maxs;
-  if (s > 32) s = 32;
-  if (s < 1) s = 1;
-  return int(s);
+  int64_t maxs = tpad / 256 > 1 ? tpad / 256 : 1;
+  if (maxs > 32) maxs = 32;
+  return gemm_nt_splits(h->cfg.dtype, h->F, h->cfg.d_in, tpad, h->cus, int(maxs));
 }
 
 BwdLayout bwd_layout(const pkm_handle_s* h, int64_t T) {
@@ -126,10 +128,12 @@ BwdLayout bwd_layout(const pkm_handle_s* h, int64_t T) {
   const size_t nblk = size_t((T + kBnRows - 1) / kBnRows);
   L.bn_part = o; o += al(nblk * 2 * h->F * sizeof(double));
   L.tpad = round_up(T, 64);
-  L.dqpre = o; o += al(size_t(T) * h->F * h->elem);
-  L.dqpre_t = o; o += al(size_t(h->F) * L.tpad * h->elem);
-  L.x_t = o; o += al(size_t(c.d_in) * L.tpad * h->elem);
-  L.wq_t = o; o += al(size_t(c.d_in) * h->F * h->elem);
+  L.ldt = L.tpad + 64;
+  L.ldf = round_up(h->F, 64) + 64;
+  L.dqpre = o; o += al(size_t(T) * L.ldf * h->elem);
+  L.dqpre_t = o; o += al(size_t(h->F) * L.ldt * h->elem);
+  L.x_t = o; o += al(size_t(c.d_in) * L.ldt * h->elem);
+  L.wq_t = o; o += al(size_t(c.d_in) * L.ldf * h->elem);
   L.splits = dwq_splits(h, L.tpad);
   L.split = o; o += al(size_t(L.splits) * h->F * c.d_in * 4);
   // long-run lists and partial sums of the value and sub-key gradients (used one after the other)
@@ -342,18 +346,18 @@ pkm_status run_query_grad(const pkm_handle_s* h, hipStream_t s, int64_t T, const
   void* dqpre = at<void>(ws, L.dqpre);
   void* dqpre_t = at<void>(ws, L.dqpre_t);
   PKM_HIP(launch_bn_bwd_apply(s, c.dtype, dq, sv->q_pre, sv->bn_mean, sv->bn_rstd, gamma, dgamma, dbeta, T, h->F, bn,
-                              dqpre, dqpre_t, L.tpad),
+                              dqpre, L.ldf, dqpre_t, L.ldt, L.tpad),
           "BatchNorm backward apply");
   // dWq[F, d] = dq_pre^T x : A = dq_pre^T [F, Tpad], B = x^T [d, Tpad]
   void* xt = at<void>(ws, L.x_t);
-  PKM_HIP(launch_transpose(s, x, T, c.d_in, c.d_in, xt, L.tpad, L.tpad, h->elem, h->elem), "x transpose");
+  PKM_HIP(launch_transpose(s, x, T, c.d_in, c.d_in, xt, L.ldt, L.tpad, h->elem, h->elem), "x transpose");
   float* split = at<float>(ws, L.split);
   const int64_t sstride = int64_t(h->F) * c.d_in;
   if (L.splits == 1) {
-    PKM_HIP(launch_gemm_nt(s, c.dtype, h->F, c.d_in, L.tpad, dqpre_t, L.tpad, xt, L.tpad, dWq, c.d_in, false, 1, 0),
+    PKM_HIP(launch_gemm_nt(s, c.dtype, h->F, c.d_in, L.tpad, dqpre_t, L.ldt, xt, L.ldt, dWq, c.d_in, false, 1, 0),
             "dWq GEMM");
   } else {
-    PKM_HIP(launch_gemm_nt(s, c.dtype, h->F, c.d_in, L.tpad, dqpre_t, L.tpad, xt, L.tpad, split, c.d_in, false,
+    PKM_HIP(launch_gemm_nt(s, c.dtype, h->F, c.d_in, L.tpad, dqpre_t, L.ldt, xt, L.ldt, split, c.d_in, false,
                            L.splits, sstride),
             "dWq GEMM");
     PKM_HIP(launch_sum_splits(s, split, L.splits, sstride, h->F, c.d_in, c.d_in, dWq, c.d_in, false), "dWq reduce");
@@ -361,8 +365,8 @@ pkm_status run_query_grad(const pkm_handle_s* h, hipStream_t s, int64_t T, const
   if (dx) {
     // dx[T, d] = dq_pre Wq : A = dq_pre [T, F], B = Wq^T [d, F]
     void* wqt = at<void>(ws, L.wq_t);
-    PKM_HIP(launch_transpose(s, Wq, h->F, c.d_in, c.d_in, wqt, h->F, h->F, h->elem, h->elem), "Wq transpose");
-    PKM_HIP(launch_gemm_nt(s, c.dtype, T, c.d_in, h->F, dqpre, h->F, wqt, h->F, dx, c.d_in, c.dtype == PKM_BF16, 1, 0),
+    PKM_HIP(launch_transpose(s, Wq, h->F, c.d_in, c.d_in, wqt, L.ldf, h->F, h->elem, h->elem), "Wq transpose");
+    PKM_HIP(launch_gemm_nt(s, c.dtype, T, c.d_in, h->F, dqpre, L.ldf, wqt, L.ldf, dx, c.d_in, c.dtype == PKM_BF16, 1, 0),
             "dx GEMM");
   }
   return PKM_OK;
@@ -458,10 +462,14 @@ pkm_status pkm_create(const pkm_config* cfg, pkm_handle_t* out) {
   // side stream on the current device (default priority); without a device the
   // backward simply stays on the caller's stream
   h->device = -1;
+  h->cus = 256;
   h->side = nullptr;
   h->fork = h->join = nullptr;
   int dev = -1;
   if (hipGetDevice(&dev) == hipSuccess) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+      h->cus = cus;
     hipStream_t st = nullptr;
     hipEvent_t e1 = nullptr, e2 = nullptr;
     if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) == hipSuccess &&

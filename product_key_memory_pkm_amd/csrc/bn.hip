@@ -193,8 +193,8 @@ __global__ __launch_bounds__(256) void bn_bwd_apply_kernel(const float* __restri
                                                            const float* __restrict__ gamma,
                                                            const float* __restrict__ dgamma,
                                                            const float* __restrict__ dbeta, int64_t ntok, int F,
-                                                           int bn, T* __restrict__ out_rm, T* __restrict__ out_tr,
-                                                           int64_t ld_tr, int64_t rows_pad) {
+                                                           int bn, T* __restrict__ out_rm, int64_t ld_rm,
+                                                           T* __restrict__ out_tr, int64_t ld_tr, int64_t rows_pad) {
   __shared__ float tile[64][65];
   const int64_t r0 = int64_t(blockIdx.y) * 64;
   const int f0 = blockIdx.x * 64;
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(256) void bn_bwd_apply_kernel(const float* __restri
       } else {
         v = g;
       }
-      out_rm[r * F + f] = to_storage<T>(v);
+      out_rm[r * ld_rm + f] = to_storage<T>(v);
     }
     tile[i][tx] = v;
   }
@@ -286,16 +286,17 @@ hipError_t launch_bn_bwd_finalize(hipStream_t s, const double* part, int nblk, i
 
 hipError_t launch_bn_bwd_apply(hipStream_t s, int dtype, const float* dq, const float* q_pre, const float* mean,
                                const float* rstd, const float* gamma, const float* dgamma, const float* dbeta,
-                               int64_t ntok, int F, bool bn, void* out_rm, void* out_tr, int64_t ld_tr) {
-  dim3 grid(unsigned((F + 63) / 64), unsigned((ld_tr + 63) / 64));
+                               int64_t ntok, int F, bool bn, void* out_rm, int64_t ld_rm, void* out_tr, int64_t ld_tr,
+                               int64_t rows_pad) {
+  dim3 grid(unsigned((F + 63) / 64), unsigned((rows_pad + 63) / 64));
   if (dtype == kBF16)
     hipLaunchKernelGGL(bn_bwd_apply_kernel<bf16_t>, grid, dim3(256), 0, s, dq, q_pre, mean, rstd, gamma, dgamma,
-                       dbeta, ntok, F, int(bn), static_cast<bf16_t*>(out_rm), static_cast<bf16_t*>(out_tr), ld_tr,
-                       ld_tr);
+                       dbeta, ntok, F, int(bn), static_cast<bf16_t*>(out_rm), ld_rm, static_cast<bf16_t*>(out_tr),
+                       ld_tr, rows_pad);
   else
     hipLaunchKernelGGL(bn_bwd_apply_kernel<float>, grid, dim3(256), 0, s, dq, q_pre, mean, rstd, gamma, dgamma,
-                       dbeta, ntok, F, int(bn), static_cast<float*>(out_rm), static_cast<float*>(out_tr), ld_tr,
-                       ld_tr);
+                       dbeta, ntok, F, int(bn), static_cast<float*>(out_rm), ld_rm, static_cast<float*>(out_tr),
+                       ld_tr, rows_pad);
   return hipGetLastError();
 }
 

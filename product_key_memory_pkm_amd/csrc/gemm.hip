@@ -294,6 +294,29 @@ __global__ __launch_bounds__(256) void sum_splits_kernel(const float* __restrict
   }
 }
 
+// Same as sum_splits_kernel, four consecutive columns per thread (16-byte
+// loads); cols, ld_part, stride and ld_out are multiples of 4 and the pointers
+// 16-byte aligned.
+__global__ __launch_bounds__(256) void sum_splits4_kernel(const float* __restrict__ part, int splits,
+                                                          int64_t stride, int64_t rows, int64_t cols,
+                                                          int64_t ld_part, void* __restrict__ out,
+                                                          int64_t ld_out, int out_bf16) {
+  const int64_t n4 = rows * cols / 4;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n4; i += int64_t(gridDim.x) * 256) {
+    const int64_t r = (i * 4) / cols, c = i * 4 - r * cols;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int z = 0; z < splits; ++z) acc += *reinterpret_cast<const f32x4*>(part + z * stride + r * ld_part + c);
+    if (out_bf16) {
+      uint16_t* o = reinterpret_cast<uint16_t*>(out) + r * ld_out + c;
+      const uint32_t lo = uint32_t(f32_to_bf16(acc.x)) | (uint32_t(f32_to_bf16(acc.y)) << 16);
+      const uint32_t hi = uint32_t(f32_to_bf16(acc.z)) | (uint32_t(f32_to_bf16(acc.w)) << 16);
+      *reinterpret_cast<u32x2*>(o) = u32x2{lo, hi};
+    } else {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + r * ld_out + c) = acc;
+    }
+  }
+}
+
 // 64x64 tile transpose through LDS.  in_elem/out_elem in {2, 4}; 4 -> 2 rounds fp32 to bf16.
 __global__ __launch_bounds__(256) void transpose_kernel(const void* __restrict__ in, int64_t rows, int64_t cols,
                                                         int64_t ld_in, void* __restrict__ out, int64_t ld_out,
@@ -368,6 +391,35 @@ __global__ void fill_f32_kernel(float* p, int64_t n, float v) {
 
 }  // namespace
 
+int gemm_nt_splits(int dtype, int64_t M, int64_t N, int64_t K, int cus, int max_splits) {
+  if (max_splits < 1) max_splits = 1;
+  if (cus < 1) cus = 256;
+  if (!(dtype == kBF16 && K % 32 == 0)) {  // the 128x128 kernel, several blocks per CU
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    int64_t sp = (int64_t(8) * cus + tiles - 1) / tiles;
+    return int(sp < 1 ? 1 : sp > max_splits ? max_splits : sp);
+  }
+  // The 256x256 kernel holds one block per CU: blocks run in rounds of cus.
+  // Time ~ rounds * K-slice (tile work) + the partial sums written and read
+  // back (in units of one tile's K step: 256*256*2 flops at ~3 TFLOP/s per CU
+  // against ~5 TB/s for the reduction).
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  const double kstep_s = 256.0 * 256.0 * 2.0 / 3.0e12;
+  int best = 1;
+  double best_t = 0.0;
+  for (int sp = 1; sp <= max_splits; ++sp) {
+    const int64_t kchunk = ((K + sp - 1) / sp + 31) / 32 * 32;
+    const int64_t rounds = (tiles * sp + cus - 1) / cus;
+    const double t = double(rounds) * double(kchunk) * kstep_s +
+                     (sp > 1 ? double(sp + 1) * double(M) * double(N) * 4.0 / 5.0e12 : 0.0);
+    if (sp == 1 || t < best_t * 0.98) {
+      best = sp;
+      best_t = t;
+    }
+  }
+  return best;
+}
+
 hipError_t launch_gemm_nt(hipStream_t s, int dtype, int64_t M, int64_t N, int64_t K, const void* A,
                           int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, bool out_bf16,
                           int splits, int64_t split_stride) {
@@ -404,6 +456,16 @@ hipError_t launch_gemm_nt(hipStream_t s, int dtype, int64_t M, int64_t N, int64_
 
 hipError_t launch_sum_splits(hipStream_t s, const float* part, int splits, int64_t stride, int64_t rows,
                              int64_t cols, int64_t ld_part, void* out, int64_t ld_out, bool out_bf16) {
+  const bool v4 = cols % 4 == 0 && ld_part % 4 == 0 && stride % 4 == 0 && ld_out % 4 == 0 &&
+                  (reinterpret_cast<uintptr_t>(part) & 15) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+  if (v4) {
+    int64_t blocks = (rows * cols / 4 + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(sum_splits4_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, part, splits, stride, rows, cols,
+                       ld_part, out, ld_out, int(out_bf16));
+    return hipGetLastError();
+  }
   int64_t blocks = (rows * cols + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;

@@ -33,6 +33,9 @@ hipError_t launch_merge_softmax(hipStream_t s, const int32_t* sub_idx, const flo
 hipError_t launch_gemm_nt(hipStream_t s, int dtype, int64_t M, int64_t N, int64_t K, const void* A,
                           int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, bool out_bf16,
                           int splits, int64_t split_stride);
+// Split-K count for launch_gemm_nt on a device with cus compute units: whole
+// rounds of resident blocks, the partial-sum traffic counted against it.
+int gemm_nt_splits(int dtype, int64_t M, int64_t N, int64_t K, int cus, int max_splits);
 // out[i] = sum_z part[z * stride + i] for i < n (fixed order), optional bf16 output.
 hipError_t launch_sum_splits(hipStream_t s, const float* part, int splits, int64_t stride, int64_t rows,
                              int64_t cols, int64_t ld_part, void* out, int64_t ld_out, bool out_bf16);
@@ -55,12 +58,13 @@ hipError_t launch_bn_bwd_partials(hipStream_t s, const float* dq, const float* q
                                   const float* rstd, int64_t ntok, int F, double* part);
 hipError_t launch_bn_bwd_finalize(hipStream_t s, const double* part, int nblk, int F, const float* gamma,
                                   float* dgamma, float* dbeta, float* coef);
-// dq_pre = gamma*rstd*(dq - dbeta/T - xhat*dgamma/T); written row-major (out_rm) and
-// transposed (out_tr, [F, ld_tr]), each as fp32 or bf16 per dtype.
+// dq_pre = gamma*rstd*(dq - dbeta/T - xhat*dgamma/T); written row-major (out_rm,
+// [ntok, ld_rm]) and transposed (out_tr, [F, ld_tr], zero in columns [ntok, rows_pad)),
+// each as fp32 or bf16 per dtype.
 hipError_t launch_bn_bwd_apply(hipStream_t s, int dtype, const float* dq, const float* q_pre,
                                const float* mean, const float* rstd, const float* gamma,
                                const float* dgamma, const float* dbeta, int64_t ntok, int F, bool bn,
-                               void* out_rm, void* out_tr, int64_t ld_tr);
+                               void* out_rm, int64_t ld_rm, void* out_tr, int64_t ld_tr, int64_t rows_pad);
 
 // Stable radix sort by key of n keys (< 2^key_bits) paired with their indices 0..n-1.
 // keys_in is read only; the passes ping-pong between (k0, v0) and (k1, v1) and
