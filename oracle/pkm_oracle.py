@@ -32,6 +32,9 @@ add is left to the caller.  For bf16 storage the BatchNorm output q is
 rounded to the nearest bf16 (the value the scores are computed from) and the
 rounding is passed straight through in the backward.
 
+Beyond the lookup, ``sparse_adam_rows`` is the optimizer step on the touched
+value rows that [Blog] §6.3 describes (moments only for rows with gradient).
+
 Parity pins (all in ``tests/test_oracle_pins.py``): brute force over every
 full key, integer-valued exact ties, numpy cross-checks against dense
 formulations, closed forms of BatchNorm and softmax, finite differences of
@@ -293,6 +296,30 @@ def value_grad_dense(rows: np.ndarray, w: np.ndarray, dY: np.ndarray, y_dtype: s
         c = np.arange(lo, min(flat.size, lo + step))
         np.add.at(dV, flat[c], wf[c][:, None] * dYf[c // per_tok])
     return dV
+
+
+def sparse_adam_rows(V_rows: np.ndarray, m_rows: np.ndarray, v_rows: np.ndarray, g: np.ndarray, lr: float,
+                     beta1: float, beta2: float, eps: float, step: int, v_dtype: str):
+    """One Adam step on the value rows that received gradient in this step.
+
+    ([Blog] §6.3: the optimizer keeps first and second moments only for the
+    parameters that actually got gradient, and the value table gets its own
+    learning rate; §6.1: only the activated value rows have gradient.)
+    Inputs are the touched rows only: their current values ``V_rows`` (stored
+    tensor, decoded here), moments ``m_rows``, ``v_rows`` and this step's
+    gradient ``g`` (all [n, d]).  Rows that got no gradient are not passed and
+    keep value and moments.  Readings: Adam's bias corrections use the global
+    step count ``step`` (1 for the first step), and the stored value is rounded
+    to the storage type after the update.  Returns (V', m', v') in float64,
+    V' holding storage-precision values.
+    """
+    g = np.asarray(g, dtype=np.float64)
+    m1 = beta1 * np.asarray(m_rows, dtype=np.float64) + (1.0 - beta1) * g
+    v1 = beta2 * np.asarray(v_rows, dtype=np.float64) + (1.0 - beta2) * g * g
+    m_hat = m1 / (1.0 - beta1 ** step)
+    v_hat = v1 / (1.0 - beta2 ** step)
+    V1 = decode(V_rows, v_dtype) - lr * m_hat / (np.sqrt(v_hat) + eps)
+    return round_to_storage(V1, v_dtype), m1, v1
 
 
 def weight_grad(rows: np.ndarray, dY: np.ndarray, V: np.ndarray, dtype: str, chunk: int = 256) -> np.ndarray:

@@ -387,3 +387,82 @@ def test_value_grad_rows_sampled_matches_dense_on_small_workload_shape():
     which = np.unique(rows)[::37]
     np.testing.assert_allclose(O.value_grad_rows(rows, w.astype(np.float64), dY, "bf16", which),
                                dense[which], rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Sparse Adam on the touched value rows ([Blog] §6.3)
+# ---------------------------------------------------------------------------
+
+def _adam_iterate(V0, steps, lr, b1, b2, eps):
+    """Run O.sparse_adam_rows over ``steps`` = [(rows, grad_rows)], carrying the dense state."""
+    V = V0.copy()
+    m = np.zeros_like(V)
+    v = np.zeros_like(V)
+    for n, (rows, g) in enumerate(steps, start=1):
+        V[rows], m[rows], v[rows] = O.sparse_adam_rows(V[rows], m[rows], v[rows], g, lr, b1, b2, eps, n, O.F64)
+    return V, m, v
+
+
+def test_sparse_adam_all_rows_touched_matches_dense_adam():
+    # every row gets gradient at every step: lazy Adam and torch's dense Adam coincide
+    rng = np.random.default_rng(5)
+    V0 = rng.standard_normal((6, 5))
+    grads = [rng.standard_normal((6, 5)) * (0.1 + n) for n in range(5)]
+    lr, b1, b2, eps = 1e-2, 0.9, 0.999, 1e-8
+    V, m, v = _adam_iterate(V0, [(np.arange(6), g) for g in grads], lr, b1, b2, eps)
+    p = torch.nn.Parameter(torch.tensor(V0))
+    opt = torch.optim.Adam([p], lr=lr, betas=(b1, b2), eps=eps)
+    for g in grads:
+        p.grad = torch.tensor(g)
+        opt.step()
+    st = opt.state[p]
+    np.testing.assert_allclose(V, p.detach().numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(m, st["exp_avg"].numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(v, st["exp_avg_sq"].numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_sparse_adam_lazy_rows_match_torch_sparse_adam():
+    # rows without gradient keep value and moments; bias correction counts global
+    # steps.  torch's SparseAdam adds eps before its bias correction, so with a
+    # negligible eps (it rejects 0) the two forms agree to rounding.
+    rng = np.random.default_rng(6)
+    n_rows, d = 40, 3
+    V0 = rng.standard_normal((n_rows, d))
+    steps = []
+    for n in range(6):
+        rows = np.sort(rng.choice(n_rows, size=rng.integers(1, n_rows), replace=False))
+        steps.append((rows, rng.standard_normal((rows.size, d))))
+    lr, b1, b2 = 3e-2, 0.8, 0.95
+    V, m, v = _adam_iterate(V0, steps, lr, b1, b2, 1e-30)
+    p = torch.nn.Parameter(torch.tensor(V0))
+    opt = torch.optim.SparseAdam([p], lr=lr, betas=(b1, b2), eps=1e-30)
+    for rows, g in steps:
+        p.grad = torch.sparse_coo_tensor(torch.tensor(rows)[None], torch.tensor(g), (n_rows, d))
+        opt.step()
+    st = opt.state[p]
+    np.testing.assert_allclose(V, p.detach().numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(m, st["exp_avg"].to_dense().numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(v, st["exp_avg_sq"].to_dense().numpy(), rtol=1e-12, atol=1e-14)
+    untouched = np.setdiff1d(np.arange(n_rows), np.concatenate([r for r, _ in steps]))
+    np.testing.assert_array_equal(V[untouched], V0[untouched])
+
+
+def test_sparse_adam_first_step_closed_form_and_bf16_rounding():
+    # from zero moments the first step moves each element by lr * g / (|g| + eps)
+    rng = np.random.default_rng(7)
+    g = rng.standard_normal((4, 9))
+    g[0, 0] = 0.0
+    V0 = rng.standard_normal((4, 9))
+    lr, eps = 1e-3, 1e-6
+    V1, m1, v1 = O.sparse_adam_rows(V0, np.zeros_like(g), np.zeros_like(g), g, lr, 0.9, 0.999, eps, 1, O.F64)
+    np.testing.assert_allclose(V1, V0 - lr * g / (np.abs(g) + eps), rtol=1e-13, atol=1e-16)
+    np.testing.assert_allclose(m1, 0.1 * g, rtol=1e-15)
+    np.testing.assert_allclose(v1, 0.001 * g * g, rtol=1e-14)
+    assert V1[0, 0] == V0[0, 0]
+    # bf16 storage: the stored value is the nearest bf16 of the exact update (torch's cast)
+    Vb = torch.tensor(V0, dtype=torch.float32).to(torch.bfloat16)
+    bits = Vb.view(torch.int16).numpy().view(np.uint16)
+    Vb1, _, _ = O.sparse_adam_rows(bits, np.zeros_like(g), np.zeros_like(g), g, lr, 0.9, 0.999, eps, 1, O.BF16)
+    exact = Vb.double().numpy() - lr * g / (np.abs(g) + eps)
+    want = torch.tensor(exact).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(Vb1, want)
