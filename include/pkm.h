@@ -110,6 +110,19 @@ typedef struct {
   float* bn_rstd; /* [h*dq] 1/sqrt(var + eps) (BN_BATCH; may be NULL with BN_NONE) */
 } pkm_saved;
 
+/* Adam hyper-parameters of the value table's optimizer step (pkm_backward_adam,
+ * pkm_stage_value_adam).  "Meta AI 可扩展内存层", section 6.3: moments only for
+ * the parameters that received gradient, and a learning rate of the value
+ * table's own.  Checked on the host: lr finite >= 0, beta1 and beta2 in [0, 1),
+ * eps finite > 0, step >= 1. */
+typedef struct {
+  float lr;
+  float beta1;
+  float beta2;
+  float eps;
+  int64_t step; /* 1-based global count of optimizer steps, this one included (bias correction) */
+} pkm_adam;
+
 /* Validate cfg and build a handle.  Besides host state, the handle owns one
  * HIP stream (default priority, non-blocking) and two events created on the
  * device current at this call; pkm_backward uses them to run the sub-key
@@ -152,6 +165,24 @@ pkm_status pkm_backward(pkm_handle_t handle, void* stream, int64_t T, const void
                         const void* V, const pkm_saved* saved, float* dV, int32_t* touched,
                         int64_t* n_touched, float* dC, float* dCp, float* dWq, float* dgamma,
                         float* dbeta, void* dx, void* ws, size_t ws_bytes);
+
+/* pkm_backward with the value table's optimizer step fused into the value
+ * gradient: no dV.  For every touched row r (the rows of saved->idx; all other
+ * rows of V, adam_m and adam_v are neither read nor written), with g_r the
+ * row's gradient of this call (what pkm_backward would write into dV with
+ * accumulate_dv = 0) and t = adam->step:
+ *   m_r = beta1 m_r + (1 - beta1) g_r,   v_r = beta2 v_r + (1 - beta2) g_r^2,
+ *   V_r = V_r - lr * (m_r / (1 - beta1^t)) / (sqrt(v_r / (1 - beta2^t)) + eps),
+ * elementwise in fp32, V_r rounded to the storage dtype.  dw and everything
+ * after it use the rows of V before this step.  V [|C|*|C'|, d_value] storage
+ * dtype (updated in place); adam_m, adam_v [|C|*|C'|, d_value] fp32 (caller
+ * allocated, zero before the first step).  The other arguments, outputs and the
+ * workspace are those of pkm_backward; cfg.accumulate_dv is ignored. */
+pkm_status pkm_backward_adam(pkm_handle_t handle, void* stream, int64_t T, const void* dY, const void* x,
+                             const void* Wq, const float* bn_gamma, const void* C, const void* Cp, void* V,
+                             const pkm_saved* saved, float* adam_m, float* adam_v, const pkm_adam* adam,
+                             int32_t* touched, int64_t* n_touched, float* dC, float* dCp, float* dWq,
+                             float* dgamma, float* dbeta, void* dx, void* ws, size_t ws_bytes);
 
 const char* pkm_status_string(pkm_status s);
 /* Message of the last failed call on this thread ("" if none). */
@@ -199,6 +230,15 @@ pkm_status pkm_stage_value_grad(pkm_handle_t handle, void* stream, int64_t T, co
                                 const float* w, const void* dY, const void* V, float* dV,
                                 int32_t* touched, int64_t* n_touched, float* dw, void* ws,
                                 size_t ws_bytes);
+
+/* Steps a7 (dw) and a8 with the Adam step of pkm_backward_adam in place of
+ * dV: dw [T, h, k] fp32 from the rows of V before the step; V, adam_m, adam_v
+ * updated at the touched rows; touched, n_touched as in pkm_backward.
+ * ws >= pkm_workspace_size(handle, T, 1). */
+pkm_status pkm_stage_value_adam(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx,
+                                const float* w, const void* dY, void* V, float* adam_m, float* adam_v,
+                                const pkm_adam* adam, int32_t* touched, int64_t* n_touched, float* dw,
+                                void* ws, size_t ws_bytes);
 
 /* Step a8's grouping alone: the lookups of idx [T, h, k] stably sorted by row,
  * written into the workspace (for pkm_stage_value_grad_grouped), plus touched

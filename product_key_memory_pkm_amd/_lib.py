@@ -40,6 +40,11 @@ class pkm_saved(ctypes.Structure):
                 ("q_pre", ctypes.c_void_p), ("bn_mean", ctypes.c_void_p), ("bn_rstd", ctypes.c_void_p)]
 
 
+class pkm_adam(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("step", ctypes.c_int64)]
+
+
 _lib = None
 
 # name -> argument types (all return pkm_status as int)
@@ -52,11 +57,15 @@ _SIGS = {
     "pkm_forward": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_saved), _VP, _SZ],
     "pkm_backward": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_saved), _VP, _VP, _VP,
                      _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
+    "pkm_backward_adam": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_saved), _VP, _VP,
+                          ctypes.POINTER(pkm_adam), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
     "pkm_stage_query": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_saved), _VP, _SZ],
     "pkm_stage_score_topk": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
     "pkm_stage_merge_softmax": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP],
     "pkm_stage_gather": [_VP, _VP, _I64, _VP, _VP, _VP, _VP],
     "pkm_stage_value_grad": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
+    "pkm_stage_value_adam": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_adam), _VP, _VP, _VP,
+                             _VP, _SZ],
     "pkm_stage_row_groups": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _SZ],
     "pkm_stage_value_grad_grouped": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
     "pkm_stage_subkey_grad": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
@@ -188,6 +197,42 @@ def pkm_backward(h, T, dY, x, Wq, bn_gamma, C, Cp, V, saved: dict, dV, touched, 
                               _ptr(V), ctypes.byref(sv), _ptr(dV), _ptr(touched), _ptr(n_touched), _ptr(dC),
                               _ptr(dCp), _ptr(dWq), _ptr(dgamma), _ptr(dbeta), _ptr(dx), _ptr(ws), _nbytes(ws)),
            "pkm_backward")
+
+
+def _adam_struct(adam: dict) -> pkm_adam:
+    return pkm_adam(float(adam["lr"]), float(adam["beta1"]), float(adam["beta2"]), float(adam["eps"]),
+                    int(adam["step"]))
+
+
+def pkm_backward_adam(h, T, dY, x, Wq, bn_gamma, C, Cp, V, saved: dict, adam_m, adam_v, adam: dict, touched,
+                      n_touched, dC, dCp, dWq, dgamma, dbeta, dx, ws):
+    """pkm_backward with the Adam step of the touched value rows in place of dV.
+
+    ``adam``: {"lr", "beta1", "beta2", "eps", "step"}; V, adam_m, adam_v are updated in place."""
+    st = h.storage
+    for n, t in (("dY", dY), ("x", x), ("Wq", Wq), ("C", C), ("Cp", Cp), ("V", V), ("dx", dx)):
+        _dt(t, st, n)
+    _dt(adam_m, torch.float32, "adam_m")
+    _dt(adam_v, torch.float32, "adam_v")
+    _dt(n_touched, torch.int64, "n_touched")
+    sv = _saved_struct(saved)
+    hp = _adam_struct(adam)
+    _check(_invoke("pkm_backward_adam", h, T, _ptr(dY), _ptr(x), _ptr(Wq), _ptr(bn_gamma), _ptr(C), _ptr(Cp),
+                   _ptr(V), ctypes.byref(sv), _ptr(adam_m), _ptr(adam_v), ctypes.byref(hp), _ptr(touched),
+                   _ptr(n_touched), _ptr(dC), _ptr(dCp), _ptr(dWq), _ptr(dgamma), _ptr(dbeta), _ptr(dx), _ptr(ws),
+                   _nbytes(ws)), "pkm_backward_adam")
+
+
+def pkm_stage_value_adam(h, T, idx, w, dY, V, adam_m, adam_v, adam: dict, touched, n_touched, dw, ws):
+    _dt(idx, torch.int32, "idx")
+    _dt(w, torch.float32, "w")
+    _dt(adam_m, torch.float32, "adam_m")
+    _dt(adam_v, torch.float32, "adam_v")
+    _dt(dw, torch.float32, "dw")
+    hp = _adam_struct(adam)
+    _check(_invoke("pkm_stage_value_adam", h, T, _ptr(idx), _ptr(w), _ptr(dY), _ptr(V), _ptr(adam_m), _ptr(adam_v),
+                   ctypes.byref(hp), _ptr(touched), _ptr(n_touched), _ptr(dw), _ptr(ws), _nbytes(ws)),
+           "pkm_stage_value_adam")
 
 
 def pkm_stage_query(h, T, x, Wq, bn_gamma, bn_beta, saved: dict, ws):

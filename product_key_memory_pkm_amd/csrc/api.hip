@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <cmath>
 #include <mutex>
 #include <new>
 #include <string>
@@ -249,7 +250,8 @@ int row_sort_passes(const pkm_handle_s* h) {
 }
 
 pkm_status run_value_grad_grouped(const pkm_handle_s* h, hipStream_t s, int64_t T, const float* w, const void* dY,
-                                  const void* V, float* dV, float* dw, const int64_t* n_touched, void* ws) {
+                                  const void* V, float* dV, float* dw, const int64_t* n_touched, void* ws,
+                                  const VgAdam* adam = nullptr) {
   const pkm_config& c = h->cfg;
   const BwdLayout L = bwd_layout(h, T);
   const int64_t N = T * c.heads * c.topk;
@@ -257,16 +259,37 @@ pkm_status run_value_grad_grouped(const pkm_handle_s* h, hipStream_t s, int64_t 
   const uint32_t* sk = at<uint32_t>(ws, in1 ? L.k1 : L.k0);
   const int32_t* sv = at<int32_t>(ws, in1 ? L.v1 : L.v0);
   PKM_HIP(launch_value_grad(s, c.dtype, at<int32_t>(ws, L.seg), n_touched, N, sk, sv, w, dY, V, dV, dw,
-                            c.heads * c.topk, c.d_value, c.accumulate_dv != 0, at<void>(ws, L.aux)),
-          "value gradient");
+                            c.heads * c.topk, c.d_value, c.accumulate_dv != 0, at<void>(ws, L.aux), adam),
+          adam ? "value gradient with Adam step" : "value gradient");
   return PKM_OK;
 }
 
 pkm_status run_value_grad(const pkm_handle_s* h, hipStream_t s, int64_t T, const int32_t* idx, const float* w,
                           const void* dY, const void* V, float* dV, int32_t* touched, int64_t* n_touched, float* dw,
-                          void* ws) {
+                          void* ws, const VgAdam* adam = nullptr) {
   PKM_TRY(run_row_groups(h, s, T, idx, touched, n_touched, ws));
-  return run_value_grad_grouped(h, s, T, w, dY, V, dV, dw, n_touched, ws);
+  return run_value_grad_grouped(h, s, T, w, dY, V, dV, dw, n_touched, ws, adam);
+}
+
+// Adam hyper-parameters -> the kernel's constants (bias corrections in double).
+pkm_status adam_args(const pkm_adam* hp, void* V, float* m, float* v, VgAdam* out) {
+  if (hp == nullptr) return fail(PKM_ERR_INVALID_ARG, "adam is NULL");
+  if (!(std::isfinite(hp->lr) && hp->lr >= 0.f)) return fail(PKM_ERR_INVALID_ARG, "adam.lr must be finite and >= 0");
+  if (!(hp->beta1 >= 0.f && hp->beta1 < 1.f)) return fail(PKM_ERR_INVALID_ARG, "adam.beta1 must lie in [0, 1)");
+  if (!(hp->beta2 >= 0.f && hp->beta2 < 1.f)) return fail(PKM_ERR_INVALID_ARG, "adam.beta2 must lie in [0, 1)");
+  if (!(std::isfinite(hp->eps) && hp->eps > 0.f)) return fail(PKM_ERR_INVALID_ARG, "adam.eps must be finite and > 0");
+  if (hp->step < 1) return fail(PKM_ERR_INVALID_ARG, "adam.step must be >= 1");
+  const double bc1 = 1.0 - std::pow(double(hp->beta1), double(hp->step));
+  const double bc2 = 1.0 - std::pow(double(hp->beta2), double(hp->step));
+  out->V = V;
+  out->m = m;
+  out->v = v;
+  out->beta1 = hp->beta1;
+  out->beta2 = hp->beta2;
+  out->eps = hp->eps;
+  out->step_size = float(double(hp->lr) / bc1);
+  out->inv_sqrt_bc2 = float(1.0 / std::sqrt(bc2));
+  return PKM_OK;
 }
 
 // Softmax backward and dq; per-slot sub-key sort keys and coefficients of
@@ -548,10 +571,13 @@ pkm_status pkm_forward(pkm_handle_t handle, void* stream, int64_t T, const void*
   return PKM_OK;
 }
 
-pkm_status pkm_backward(pkm_handle_t handle, void* stream, int64_t T, const void* dY, const void* x, const void* Wq,
-                        const float* bn_gamma, const void* C, const void* Cp, const void* V, const pkm_saved* saved,
-                        float* dV, int32_t* touched, int64_t* n_touched, float* dC, float* dCp, float* dWq,
-                        float* dgamma, float* dbeta, void* dx, void* ws, size_t ws_bytes) {
+// pkm_backward (adam == null: dV written) and pkm_backward_adam (Adam step on
+// the touched rows of V instead of dV).
+static pkm_status backward_impl(pkm_handle_t handle, void* stream, int64_t T, const void* dY, const void* x,
+                                const void* Wq, const float* bn_gamma, const void* C, const void* Cp, const void* V,
+                                const pkm_saved* saved, float* dV, const VgAdam* adam, int32_t* touched,
+                                int64_t* n_touched, float* dC, float* dCp, float* dWq, float* dgamma, float* dbeta,
+                                void* dx, void* ws, size_t ws_bytes) {
   PKM_TRY(check_handle(handle));
   PKM_TRY(check_T(handle, T));
   const bool bn = handle->cfg.bn == PKM_BN_BATCH;
@@ -562,7 +588,7 @@ pkm_status pkm_backward(pkm_handle_t handle, void* stream, int64_t T, const void
   PKM_TRY(need(Cp, "Cp"));
   PKM_TRY(need(V, "V"));
   PKM_TRY(check_saved(handle, saved, true));
-  PKM_TRY(need(dV, "dV"));
+  if (adam == nullptr) PKM_TRY(need(dV, "dV"));
   PKM_TRY(need(touched, "touched"));
   if (n_touched == nullptr) return fail(PKM_ERR_INVALID_ARG, "n_touched is NULL");
   PKM_TRY(need(dC, "dC"));
@@ -580,7 +606,7 @@ pkm_status pkm_backward(pkm_handle_t handle, void* stream, int64_t T, const void
   const BwdLayout L = bwd_layout(handle, T);
   float* dw = at<float>(ws, L.dw);
   float* dq = at<float>(ws, L.dq);
-  PKM_TRY(run_value_grad(handle, s, T, saved->idx, saved->w, dY, V, dV, touched, n_touched, dw, ws));
+  PKM_TRY(run_value_grad(handle, s, T, saved->idx, saved->w, dY, V, dV, touched, n_touched, dw, ws, adam));
   PKM_TRY(run_softmax_bwd(handle, s, T, saved->idx, saved->w, dw, C, Cp, dq, ws));
   // The sub-key gradients (sorts, L2 gathers) and the projection gradients
   // (BatchNorm backward, MFMA GEMMs) only share inputs: run them side by side.
@@ -601,6 +627,29 @@ pkm_status pkm_backward(pkm_handle_t handle, void* stream, int64_t T, const void
   PKM_TRY(run_query_grad(handle, s, T, dq, x, Wq, bn_gamma, saved, dWq, bn ? dgamma : nullptr, bn ? dbeta : nullptr,
                          dx, ws));
   return PKM_OK;
+}
+
+pkm_status pkm_backward(pkm_handle_t handle, void* stream, int64_t T, const void* dY, const void* x, const void* Wq,
+                        const float* bn_gamma, const void* C, const void* Cp, const void* V, const pkm_saved* saved,
+                        float* dV, int32_t* touched, int64_t* n_touched, float* dC, float* dCp, float* dWq,
+                        float* dgamma, float* dbeta, void* dx, void* ws, size_t ws_bytes) {
+  return backward_impl(handle, stream, T, dY, x, Wq, bn_gamma, C, Cp, V, saved, dV, nullptr, touched, n_touched, dC,
+                       dCp, dWq, dgamma, dbeta, dx, ws, ws_bytes);
+}
+
+pkm_status pkm_backward_adam(pkm_handle_t handle, void* stream, int64_t T, const void* dY, const void* x,
+                             const void* Wq, const float* bn_gamma, const void* C, const void* Cp, void* V,
+                             const pkm_saved* saved, float* adam_m, float* adam_v, const pkm_adam* adam,
+                             int32_t* touched, int64_t* n_touched, float* dC, float* dCp, float* dWq, float* dgamma,
+                             float* dbeta, void* dx, void* ws, size_t ws_bytes) {
+  PKM_TRY(check_handle(handle));
+  PKM_TRY(need(V, "V"));
+  PKM_TRY(need(adam_m, "adam_m"));
+  PKM_TRY(need(adam_v, "adam_v"));
+  VgAdam ad;
+  PKM_TRY(adam_args(adam, V, adam_m, adam_v, &ad));
+  return backward_impl(handle, stream, T, dY, x, Wq, bn_gamma, C, Cp, V, saved, nullptr, &ad, touched, n_touched, dC,
+                       dCp, dWq, dgamma, dbeta, dx, ws, ws_bytes);
 }
 
 pkm_status pkm_stage_query(pkm_handle_t handle, void* stream, int64_t T, const void* x, const void* Wq,
@@ -676,6 +725,28 @@ pkm_status pkm_stage_value_grad(pkm_handle_t handle, void* stream, int64_t T, co
   hipStream_t s = as_stream(stream);
   if (T == 0) return zero_grads(handle, s, n_touched, nullptr, nullptr, nullptr, nullptr, nullptr);
   return run_value_grad(handle, s, T, idx, w, dY, V, dV, touched, n_touched, dw, ws);
+}
+
+pkm_status pkm_stage_value_adam(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx, const float* w,
+                                const void* dY, void* V, float* adam_m, float* adam_v, const pkm_adam* adam,
+                                int32_t* touched, int64_t* n_touched, float* dw, void* ws, size_t ws_bytes) {
+  PKM_TRY(check_handle(handle));
+  PKM_TRY(check_T(handle, T));
+  PKM_TRY(need(idx, "idx"));
+  PKM_TRY(need(w, "w"));
+  PKM_TRY(need(dY, "dY"));
+  PKM_TRY(need(V, "V"));
+  PKM_TRY(need(adam_m, "adam_m"));
+  PKM_TRY(need(adam_v, "adam_v"));
+  VgAdam ad;
+  PKM_TRY(adam_args(adam, V, adam_m, adam_v, &ad));
+  PKM_TRY(need(touched, "touched"));
+  if (n_touched == nullptr) return fail(PKM_ERR_INVALID_ARG, "n_touched is NULL");
+  PKM_TRY(need(dw, "dw"));
+  PKM_TRY(check_ws(handle, T, 1, ws, ws_bytes));
+  hipStream_t s = as_stream(stream);
+  if (T == 0) return zero_grads(handle, s, n_touched, nullptr, nullptr, nullptr, nullptr, nullptr);
+  return run_value_grad(handle, s, T, idx, w, dY, V, nullptr, touched, n_touched, dw, ws, &ad);
 }
 
 pkm_status pkm_stage_row_groups(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx, int32_t* touched,

@@ -87,11 +87,21 @@ hipError_t launch_segments(hipStream_t s, const uint32_t* sorted_keys, int64_t n
 // a7 + a8: per touched row, dw for every lookup of it and the row's dV.  Rows
 // with more lookups than a chunk are split over several waves; aux (of
 // value_grad_aux_bytes) holds their lists and partial sums.
+// adam != null: no dV; every touched row's gradient takes an Adam step on
+// (V, m, v) instead (V is then the same buffer as adam->V, updated in place).
+struct VgAdam {
+  void* V;
+  float* m;
+  float* v;
+  float beta1, beta2, eps;
+  float step_size;     // lr / (1 - beta1^step)
+  float inv_sqrt_bc2;  // 1 / sqrt(1 - beta2^step)
+};
 size_t value_grad_aux_bytes(int64_t nitems, int d_value);
 hipError_t launch_value_grad(hipStream_t s, int dtype, const int32_t* seg_start, const int64_t* nseg,
                              int64_t nitems, const uint32_t* sorted_rows, const int32_t* sorted_c,
                              const float* w, const void* dY, const void* V, float* dV, float* dw,
-                             int R, int d_value, bool accumulate, void* aux);
+                             int R, int d_value, bool accumulate, void* aux, const VgAdam* adam = nullptr);
 
 // a7 + a9: per (token, head) softmax backward, dq from the distinct selected
 // sub-keys, and per slot the sub-key sort key (h*|C|+i / h*|C'|+j, or the

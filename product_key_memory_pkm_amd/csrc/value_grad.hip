@@ -17,6 +17,16 @@
 // own slot; a short combine pass then adds each long run's slots in chunk
 // order.  Every sum thus has a fixed order, so results are bit-identical from
 // run to run.
+//
+// Optional fused optimizer step ("Meta AI 可扩展内存层", section 6.3: Adam
+// moments kept only for the parameters that got gradient, a learning rate of
+// its own for the value table): instead of writing dV, each touched row's
+// gradient g of this call updates its moments m, v and the row itself,
+//   m = b1 m + (1-b1) g,  v = b2 v + (1-b2) g^2,
+//   V = V - lr/(1-b1^t) * m / (sqrt(v)/sqrt(1-b2^t) + eps)   (t: global step),
+// in the same pass that read the row for dw (so dw always sees the old row);
+// rows cut into chunks are updated by the combine launch, after every chunk
+// has read the old row.
 #include "sparse_common.h"
 
 namespace pkm {
@@ -70,6 +80,13 @@ struct VgArgs {
   const int2* long_list;    // (row run u, first slot) of every run longer than kVgChunk
   const uint32_t* counts;   // [0] chunks listed, [1] long runs listed
   float* partial;           // [2 N / kVgChunk + 2, d_v] partial sums
+  // fused Adam step (value_grad_kernel<..., ADAM = true>): V is written in place
+  void* Vout;
+  float* am;
+  float* av;
+  float b1, b2, eps;
+  float step_size;     // lr / (1 - b1^t)
+  float inv_sqrt_bc2;  // 1 / sqrt(1 - b2^t)
 };
 
 // The wave's lanes own 16-byte vectors l, l+64, ... of a row; the first NVL-1
@@ -196,12 +213,46 @@ __device__ __forceinline__ void vg_add_from(const LaneVecs<NVL>& lv, const float
   }
 }
 
+// Adam step of row r from its gradient g: moments read, updated and written
+// back, the row (old value in vr, storage packing) moved and stored.
+template <typename T, int NVL>
+__device__ __forceinline__ void vg_adam_row(const VgArgs& a, const LaneVecs<NVL>& lv, uint32_t r, const u32x4* vr,
+                                            const float (*g)[Vec16<T>::N]) {
+  constexpr int E = Vec16<T>::N;
+  const size_t dv = size_t(a.nvec) * E;
+  float* mrow = a.am + size_t(r) * dv;
+  float* vrow = a.av + size_t(r) * dv;
+  char* Vrow = reinterpret_cast<char*>(a.Vout) + size_t(r) * size_t(a.nvec) * 16;
+  float m0[NVL][E], v0[NVL][E];
+  vg_load_f32<T, NVL>(lv, mrow, m0);
+  vg_load_f32<T, NVL>(lv, vrow, v0);
+#pragma unroll
+  for (int m = 0; m < NVL; ++m) {
+    if (m == NVL - 1 && !lv.last_ok) continue;
+    float old[E], nv[E];
+    Vec16<T>::widen(vr[m], old);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float gm = g[m][e];
+      const float m1 = a.b1 * m0[m][e] + (1.0f - a.b1) * gm;
+      const float v1 = a.b2 * v0[m][e] + (1.0f - a.b2) * (gm * gm);
+      m0[m][e] = m1;
+      v0[m][e] = v1;
+      nv[e] = old[e] - a.step_size * m1 / (__builtin_sqrtf(v1) * a.inv_sqrt_bc2 + a.eps);
+    }
+    st16(Vrow + lv.voff[m], Vec16<T>::narrow(nv));
+  }
+  vg_store<T, NVL>(lv, mrow, m0, false);
+  vg_store<T, NVL>(lv, vrow, v0, false);
+}
+
 // MODE 0: one wave per work item, a resident grid striding over the items:
 //         first the chunks of the long runs (partial sums into their slots),
 //         then the runs of at most kVgChunk lookups, whose value row is read
 //         once and gradient row written (or added) once.
 // MODE 1: one wave per long run: its slots added in chunk order into dV.
-template <typename T, int NVL, int MODE>
+// ADAM: the row's gradient drives the Adam step (vg_adam_row) instead of dV.
+template <typename T, int NVL, int MODE, bool ADAM>
 __global__ __launch_bounds__(256) void value_grad_kernel(VgArgs a) {
   constexpr int E = Vec16<T>::N;
   const int lane = lane_id();
@@ -222,7 +273,13 @@ __global__ __launch_bounds__(256) void value_grad_kernel(VgArgs a) {
         for (int q = 0; q < E; ++q) g[m][q] = 0.f;
       const int nch = (hi - lo + kVgChunk - 1) / kVgChunk;
       for (int j = 0; j < nch; ++j) vg_add_from<T, NVL>(lv, a.partial + size_t(e.y + j) * dv, g);
-      vg_store<T, NVL>(lv, a.dV + size_t(r) * dv, g, a.accumulate != 0);
+      if constexpr (ADAM) {
+        u32x4 vr[NVL];
+        vg_load_row<T, NVL>(a, lv, r, vr);
+        vg_adam_row<T, NVL>(a, lv, r, vr, g);
+      } else {
+        vg_store<T, NVL>(lv, a.dV + size_t(r) * dv, g, a.accumulate != 0);
+      }
     }
     return;
   }
@@ -246,7 +303,7 @@ __global__ __launch_bounds__(256) void value_grad_kernel(VgArgs a) {
     // the old gradient row of a short run is fetched now, beside the value
     // row, so that its latency overlaps the lookups; it is added to the sum at
     // the end (the same order of additions as reading it there)
-    const bool add_old = !chunk && a.accumulate != 0;  // wave-uniform
+    const bool add_old = !ADAM && !chunk && a.accumulate != 0;  // wave-uniform
     float old[NVL][E];
     if (add_old) vg_load_f32<T, NVL>(lv, a.dV + size_t(r) * dv, old);
     float g[NVL][E];
@@ -259,6 +316,8 @@ __global__ __launch_bounds__(256) void value_grad_kernel(VgArgs a) {
     vg_accumulate<T, NVL>(a, lv, vr, clo, chi, g);
     if (chunk) {
       vg_store<T, NVL>(lv, a.partial + size_t(it) * dv, g, false);
+    } else if constexpr (ADAM) {
+      vg_adam_row<T, NVL>(a, lv, r, vr, g);
     } else {
       if (add_old) {
 #pragma unroll
@@ -281,7 +340,7 @@ size_t value_grad_aux_bytes(int64_t nitems, int d_value) {
 hipError_t launch_value_grad(hipStream_t s, int dtype, const int32_t* seg_start, const int64_t* nseg,
                              int64_t nitems, const uint32_t* sorted_rows, const int32_t* sorted_c, const float* w,
                              const void* dY, const void* V, float* dV, float* dw, int R, int d_value,
-                             bool accumulate, void* aux) {
+                             bool accumulate, void* aux, const VgAdam* adam) {
   const int elem = dtype == kBF16 ? 2 : 4;
   const int nvec = d_value * elem / 16;
   const int per_lane = (nvec + 63) / 64;
@@ -300,6 +359,19 @@ hipError_t launch_value_grad(hipStream_t s, int dtype, const int32_t* seg_start,
   a.R = uint32_t(R);
   a.nvec = nvec;
   a.accumulate = int(accumulate);
+  a.Vout = nullptr;
+  a.am = a.av = nullptr;
+  a.b1 = a.b2 = a.eps = a.step_size = a.inv_sqrt_bc2 = 0.f;
+  if (adam) {
+    a.Vout = adam->V;
+    a.am = adam->m;
+    a.av = adam->v;
+    a.b1 = adam->beta1;
+    a.b2 = adam->beta2;
+    a.eps = adam->eps;
+    a.step_size = adam->step_size;
+    a.inv_sqrt_bc2 = adam->inv_sqrt_bc2;
+  }
   uint32_t* counts = reinterpret_cast<uint32_t*>(ap);
   a.counts = counts;
   a.partial = reinterpret_cast<float*>(ap + 64);
@@ -315,11 +387,18 @@ hipError_t launch_value_grad(hipStream_t s, int dtype, const int32_t* seg_start,
                      static_cast<const uint32_t*>(nullptr), 0u, chunk_list, long_list, counts);
   const dim3 block(256);
   const dim3 grid_long(grid_waves(slots, 1024));
-#define PKM_VG(TT, NV)                                                                                    \
-  do {                                                                                                    \
-    const dim3 grid(resident_grid(reinterpret_cast<const void*>(value_grad_kernel<TT, NV, 0>), nitems));  \
-    hipLaunchKernelGGL((value_grad_kernel<TT, NV, 0>), grid, block, 0, s, a);                             \
-    hipLaunchKernelGGL((value_grad_kernel<TT, NV, 1>), grid_long, block, 0, s, a);                        \
+#define PKM_VG_AD(TT, NV, AD)                                                                                \
+  do {                                                                                                       \
+    const dim3 grid(resident_grid(reinterpret_cast<const void*>(value_grad_kernel<TT, NV, 0, AD>), nitems)); \
+    hipLaunchKernelGGL((value_grad_kernel<TT, NV, 0, AD>), grid, block, 0, s, a);                            \
+    hipLaunchKernelGGL((value_grad_kernel<TT, NV, 1, AD>), grid_long, block, 0, s, a);                       \
+  } while (0)
+#define PKM_VG(TT, NV)            \
+  do {                            \
+    if (adam)                     \
+      PKM_VG_AD(TT, NV, true);    \
+    else                          \
+      PKM_VG_AD(TT, NV, false);   \
   } while (0)
   if (dtype == kBF16) {
     if (per_lane <= 1) PKM_VG(bf16_t, 1);
@@ -335,6 +414,7 @@ hipError_t launch_value_grad(hipStream_t s, int dtype, const int32_t* seg_start,
     else return hipErrorInvalidValue;
   }
 #undef PKM_VG
+#undef PKM_VG_AD
   return hipGetLastError();
 }
 

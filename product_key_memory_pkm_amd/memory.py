@@ -76,3 +76,26 @@ class ProductKeyMemory:
         L.pkm_backward(self.handle, T, dY, x, Wq, gamma, C, Cp, V, saved, dV, g["touched"], g["n_touched"], g["dC"],
                        g["dCp"], g["dWq"], g["dgamma"], g["dbeta"], g["dx"], ws)
         return g
+
+    def backward_adam(self, dY, x, Wq, gamma, C, Cp, V, saved, adam_m, adam_v, adam: dict, want_dx=True, out=None):
+        """Backward with the Adam step of the touched value rows fused in (V, adam_m, adam_v updated in place).
+
+        ``adam``: {"lr", "beta1", "beta2", "eps", "step"} (step counts from 1).  Returns the other gradients."""
+        c = self.cfg
+        T = x.shape[0]
+        F = c.heads * c.d_query
+        dev = self.device
+        g = out if out is not None else {
+            "touched": torch.empty(max(1, T * c.heads * c.topk), dtype=torch.int32, device=dev),
+            "n_touched": torch.zeros(1, dtype=torch.int64, device=dev),
+            "dC": torch.empty((c.heads, c.n_keys, c.d_query // 2), dtype=torch.float32, device=dev),
+            "dCp": torch.empty((c.heads, c.n_keys2, c.d_query // 2), dtype=torch.float32, device=dev),
+            "dWq": torch.empty((F, c.d_in), dtype=torch.float32, device=dev),
+            "dgamma": torch.empty(F, dtype=torch.float32, device=dev) if c.bn else None,
+            "dbeta": torch.empty(F, dtype=torch.float32, device=dev) if c.bn else None,
+            "dx": torch.empty((T, c.d_in), dtype=self.storage, device=dev) if want_dx else None,
+        }
+        ws = self.workspace(T, True)
+        L.pkm_backward_adam(self.handle, T, dY, x, Wq, gamma, C, Cp, V, saved, adam_m, adam_v, adam, g["touched"],
+                            g["n_touched"], g["dC"], g["dCp"], g["dWq"], g["dgamma"], g["dbeta"], g["dx"], ws)
+        return g

@@ -168,6 +168,36 @@ def test_backward_and_stage_argument_errors():
         assert lib.pkm_status_string(s)
 
 
+def test_adam_argument_errors():
+    L = _lib()
+    lib = L.lib()
+    h = L.pkm_create(_cfg(L))
+    sv = L.pkm_saved(_fake(9), _fake(10), _fake(11), _fake(12), _fake(13), _fake(14))
+    ok = [_fake(i) for i in range(30)]
+
+    def stage(hp, ws_bytes=16):
+        ref = ctypes.byref(hp) if hp is not None else None
+        return lib.pkm_stage_value_adam(h.ptr, None, 4, ok[1], ok[2], ok[3], ok[4], ok[5], ok[6], ref, ok[7], ok[8],
+                                        ok[9], ok[10], ws_bytes)
+
+    good = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, step=1)
+    assert stage(L.pkm_adam(**good)) == L.PKM_ERR_WORKSPACE       # every other check passes
+    assert stage(None) == L.PKM_ERR_INVALID_ARG
+    for field, bad in (("lr", float("nan")), ("lr", -1.0), ("beta1", 1.0), ("beta2", -0.1), ("eps", 0.0),
+                       ("step", 0)):
+        hp = L.pkm_adam(**{**good, field: bad})
+        assert stage(hp) == L.PKM_ERR_INVALID_ARG, field
+        assert field in lib.pkm_last_error().decode()
+    st = lib.pkm_backward_adam(h.ptr, None, 10, ok[1], ok[2], ok[3], ok[4], ok[5], ok[6], ok[7], ctypes.byref(sv),
+                               ok[8], ok[9], ctypes.byref(L.pkm_adam(**good)), ok[10], ok[11], ok[12], ok[13],
+                               ok[14], ok[15], ok[16], None, ok[17], 16)
+    assert st == L.PKM_ERR_WORKSPACE
+    st = lib.pkm_backward_adam(h.ptr, None, 10, ok[1], ok[2], ok[3], ok[4], ok[5], ok[6], ok[7], ctypes.byref(sv),
+                               None, ok[9], ctypes.byref(L.pkm_adam(**good)), ok[10], ok[11], ok[12], ok[13],
+                               ok[14], ok[15], ok[16], None, ok[17], 1 << 40)
+    assert st == L.PKM_ERR_INVALID_ARG and "adam_m" in lib.pkm_last_error().decode()
+
+
 def test_binding_rejects_host_tensors():
     L = _lib()
     import torch

@@ -335,3 +335,129 @@ def test_row_groups_then_grouped_value_grad_equals_value_grad_stage():
         outs.append((dV.cpu(), touched.cpu()[:n], dw.cpu()))
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# Adam step on the touched value rows, fused into a8 ([Blog] §6.3)
+# ---------------------------------------------------------------------------
+ADAM = dict(lr=1e-2, beta1=0.9, beta2=0.999, eps=1e-8, step=5)
+
+
+def _adam_state(nrows, dv, seed):
+    """Moments as after a few earlier steps: m ~ N(0, 1e-3), v ~ U(1e-5, 1e-4)."""
+    m0 = pi.random_array(seed, 1, (nrows, dv), dtype="f32", std=1e-3).astype(np.float32)
+    v0 = (1e-5 + 9e-5 * np.abs(pi.random_array(seed, 2, (nrows, dv), dtype="f32", std=0.5))).astype(np.float32)
+    v0 = np.minimum(v0, np.float32(1e-4))
+    return m0, v0
+
+
+def adam_check(dtype, V0, m0, v0, uniq, g_ref, V1, m1, v1, untouched=None):
+    """Rows ``uniq`` against the oracle's Adam step with gradient ``g_ref``; the rows ``untouched`` (default: all
+    others) bit-identical to the input."""
+    # the boundary carries the hyper-parameters as fp32 (pkm_adam): the oracle gets those values
+    hp = {k: (float(np.float32(v)) if k != "step" else v) for k, v in ADAM.items()}
+    Vr, mr, vr = O.sparse_adam_rows(V0[uniq], m0[uniq], v0[uniq], g_ref, hp["lr"], hp["beta1"], hp["beta2"],
+                                    hp["eps"], hp["step"], dtype)
+    nrows = V0.shape[0]
+    if untouched is None:
+        untouched = np.setdiff1d(np.arange(nrows), uniq)
+    np.testing.assert_array_equal(V1[untouched], V0[untouched])
+    np.testing.assert_array_equal(m1[untouched], m0[untouched])
+    np.testing.assert_array_equal(v1[untouched], v0[untouched])
+    gm, gv = m1[uniq].astype(np.float64), v1[uniq].astype(np.float64)
+    assert (np.abs(gm - mr).max(1) <= 1e-5 * np.abs(mr).max(1) + 1e-12).all(), "adam m"
+    assert (np.abs(gv - vr).max(1) <= 1e-5 * np.abs(vr).max(1) + 1e-15).all(), "adam v"
+    gV = O.decode(V1[uniq], dtype)
+    err = np.abs(gV - Vr)
+    if dtype == "bf16":
+        # both sides round to bf16; they may land one bf16 step apart
+        assert (err <= P.bf16_ulp(Vr)).all(), "adam V (bf16)"
+    else:
+        assert (err <= 2.0 ** -22 * np.abs(Vr) + 1e-4 * hp["lr"]).all(), "adam V (f32)"
+
+
+ADAM_CASES = [
+    # T, heads, k, nk (slots = nk^2), d_value, dtype, zipf
+    (40, 2, 8, 16, 64, "f32", 0.0),
+    (300, 4, 32, 64, 512, "f32", 1.2),       # long runs: chunks, update in the combine launch
+    (128, 4, 32, 128, 1600, "bf16", 0.0),
+    (64, 8, 32, 64, 1024, "bf16", 1.0),
+    (2000, 2, 16, 16, 16, "f32", 0.0),       # ~250 lookups per row, around the chunk size
+    (1, 1, 1, 4, 8, "bf16", 0.0),
+]
+
+
+@pytest.mark.parametrize("T,h,k,nk,dv,dtype,zipf", ADAM_CASES)
+def test_value_adam_stage(T, h, k, nk, dv, dtype, zipf):
+    note(f"value_adam T={T} h={h} k={k} slots={nk * nk} dv={dv} {dtype} zipf={zipf}")
+    nrows = nk * nk
+    rows, w = pi.random_selection(T * 3 + 1, T, h, k, nrows, zipf=zipf)
+    V = pi.random_array(8, 1, (nrows, dv), dtype=dtype, std=0.05)
+    dY = pi.random_array(8, 2, (T, dv), dtype=dtype)
+    m0, v0 = _adam_state(nrows, dv, 9)
+    cfg = _cfg(T=T, heads=h, topk=k, n_keys=nk, n_keys2=nk, d_value=dv, dtype=dtype)
+    layer = layer_for(cfg)
+    from product_key_memory_pkm_amd import pkm_stage_value_adam
+    outs = []
+    for rep in range(2):
+        Vd, md, vd = to_dev(V), to_dev(m0), to_dev(v0)
+        touched = torch.full((T * h * k,), -1, dtype=torch.int32, device="cuda")
+        nt = torch.zeros(1, dtype=torch.int64, device="cuda")
+        dw = torch.empty((T, h, k), dtype=torch.float32, device="cuda")
+        pkm_stage_value_adam(layer.handle, T, to_dev(rows), to_dev(w), to_dev(dY), Vd, md, vd, ADAM, touched, nt, dw,
+                             layer.workspace(T, True))
+        torch.cuda.synchronize()
+        Vh = Vd.cpu().view(torch.int16).numpy().view(np.uint16) if dtype == "bf16" else Vd.cpu().numpy()
+        outs.append((Vh, md.cpu().numpy(), vd.cpu().numpy(), touched.cpu().numpy(), int(nt.item()),
+                     dw.cpu().numpy()))
+    V1, m1, v1, touched, nt, dw = outs[0]
+    for a, b in zip(outs[0], outs[1]):    # bit-identical from run to run
+        np.testing.assert_array_equal(np.asarray(a), np.asarray(b))
+    uniq = np.unique(rows)
+    assert nt == len(uniq)
+    np.testing.assert_array_equal(touched[:nt], uniq)
+    # dw comes from the rows before the step
+    ref_dw = O.weight_grad(rows, dY, V, dtype)
+    assert P.row_rel_err(dw.reshape(T, -1), ref_dw.reshape(T, -1)).max() <= 1e-5
+    g_ref = O.value_grad_rows(rows, w.astype(np.float64), dY, dtype, uniq)
+    adam_check(dtype, V, m0, v0, uniq, g_ref, V1, m1, v1)
+
+
+@pytest.mark.parametrize("name", ["small", "hot"])
+def test_backward_adam_end_to_end(name):
+    """pkm_backward_adam: the Adam step on the oracle's touched rows, and every other output bit-identical
+    to pkm_backward's on the same inputs."""
+    cfg = FWD_CASES[name]
+    note(f"backward_adam {name}: {cfg}")
+    inp = pi.make_inputs(cfg, with_dy=True)
+    gpu, (layer, dev, saved, y) = run_gpu_forward(cfg, inp)
+    ref = O.forward(cfg, inp)
+    dY, exact = masked_dy(inp, gpu["idx"], ref["rows"])
+    assert exact.mean() > 0.999
+    dYd = to_dev(dY)
+    dV = torch.zeros((cfg.slots, cfg.d_value), dtype=torch.float32, device="cuda")
+    g_plain = layer.backward(dYd, dev["x"], dev["Wq"], dev["gamma"], dev["C"], dev["Cp"], dev["V"], saved, dV)
+    torch.cuda.synchronize()
+    plain = {k: v.cpu().clone() for k, v in g_plain.items() if v is not None}
+    m0, v0 = _adam_state(cfg.slots, cfg.d_value, 10)
+    V0 = inp["V"]
+    Vd, md, vd = to_dev(V0), to_dev(m0), to_dev(v0)
+    g_adam = layer.backward_adam(dYd, dev["x"], dev["Wq"], dev["gamma"], dev["C"], dev["Cp"], Vd, saved, md, vd,
+                                 ADAM)
+    torch.cuda.synchronize()
+    n = int(plain["n_touched"].item())
+    assert int(g_adam["n_touched"].item()) == n
+    for k, v in plain.items():
+        got = g_adam[k].cpu()
+        if k == "touched":
+            assert torch.equal(got[:n], v[:n])
+        else:
+            assert torch.equal(got, v), k
+    # Tokens whose selection differs from the oracle's (near-ties) have dY masked to zero; the rows they pick
+    # on either side are left out of the comparison (lazy Adam moves a touched row even at zero gradient).
+    bad = np.union1d(ref["rows"][~exact].reshape(-1), gpu["idx"][~exact].reshape(-1))
+    uniq = np.setdiff1d(np.unique(ref["rows"]), bad)
+    untouched = np.setdiff1d(np.arange(cfg.slots), np.union1d(np.unique(ref["rows"]), np.unique(gpu["idx"])))
+    g_ref = O.value_grad_rows(ref["rows"], ref["w"], dY, cfg.dtype, uniq)
+    Vh = Vd.cpu().view(torch.int16).numpy().view(np.uint16) if cfg.dtype == "bf16" else Vd.cpu().numpy()
+    adam_check(cfg.dtype, V0, m0, v0, uniq, g_ref, Vh, md.cpu().numpy(), vd.cpu().numpy(), untouched)
