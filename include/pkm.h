@@ -253,6 +253,14 @@ pkm_status pkm_stage_value_grad_grouped(pkm_handle_t handle, void* stream, int64
                                         const void* dY, const void* V, float* dV, float* dw,
                                         const int64_t* n_touched, void* ws, size_t ws_bytes);
 
+/* pkm_stage_value_adam on a grouping already in ws (pkm_stage_row_groups with
+ * the same handle, T, idx and n_touched): launches the value-gradient kernel
+ * with the Adam step only.  Arguments as in pkm_stage_value_adam. */
+pkm_status pkm_stage_value_adam_grouped(pkm_handle_t handle, void* stream, int64_t T, const float* w,
+                                        const void* dY, void* V, float* adam_m, float* adam_v,
+                                        const pkm_adam* adam, float* dw, const int64_t* n_touched, void* ws,
+                                        size_t ws_bytes);
+
 /* Steps a7 (softmax backward) and a9: ds = w (dw - sum_s w dw) / tau; then
  * dq[t, h*dq] fp32 (both halves of each head) and dC, dCp (overwritten) through
  * the selected sub-keys only.  q is the saved query (storage dtype).

@@ -66,6 +66,8 @@ _SIGS = {
     "pkm_stage_value_grad": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
     "pkm_stage_value_adam": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_adam), _VP, _VP, _VP,
                              _VP, _SZ],
+    "pkm_stage_value_adam_grouped": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_adam), _VP, _VP,
+                                     _VP, _SZ],
     "pkm_stage_row_groups": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _SZ],
     "pkm_stage_value_grad_grouped": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
     "pkm_stage_subkey_grad": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
@@ -275,6 +277,15 @@ def pkm_stage_row_groups(h, T, idx, touched, n_touched, ws):
 def pkm_stage_value_grad_grouped(h, T, w, dY, V, dV, dw, n_touched, ws):
     _check(_invoke("pkm_stage_value_grad_grouped", h, T, _ptr(w), _ptr(dY), _ptr(V), _ptr(dV), _ptr(dw),
                    _ptr(n_touched), _ptr(ws), _nbytes(ws)), "pkm_stage_value_grad_grouped")
+
+
+def pkm_stage_value_adam_grouped(h, T, w, dY, V, adam_m, adam_v, adam: dict, dw, n_touched, ws):
+    _dt(adam_m, torch.float32, "adam_m")
+    _dt(adam_v, torch.float32, "adam_v")
+    hp = _adam_struct(adam)
+    _check(_invoke("pkm_stage_value_adam_grouped", h, T, _ptr(w), _ptr(dY), _ptr(V), _ptr(adam_m), _ptr(adam_v),
+                   ctypes.byref(hp), _ptr(dw), _ptr(n_touched), _ptr(ws), _nbytes(ws)),
+           "pkm_stage_value_adam_grouped")
 
 
 def pkm_stage_subkey_grad(h, T, idx, w, dw, q, C, Cp, dq, dC, dCp, ws):

@@ -778,6 +778,25 @@ pkm_status pkm_stage_value_grad_grouped(pkm_handle_t handle, void* stream, int64
   return run_value_grad_grouped(handle, as_stream(stream), T, w, dY, V, dV, dw, n_touched, ws);
 }
 
+pkm_status pkm_stage_value_adam_grouped(pkm_handle_t handle, void* stream, int64_t T, const float* w, const void* dY,
+                                        void* V, float* adam_m, float* adam_v, const pkm_adam* adam, float* dw,
+                                        const int64_t* n_touched, void* ws, size_t ws_bytes) {
+  PKM_TRY(check_handle(handle));
+  PKM_TRY(check_T(handle, T));
+  PKM_TRY(need(w, "w"));
+  PKM_TRY(need(dY, "dY"));
+  PKM_TRY(need(V, "V"));
+  PKM_TRY(need(adam_m, "adam_m"));
+  PKM_TRY(need(adam_v, "adam_v"));
+  VgAdam ad;
+  PKM_TRY(adam_args(adam, V, adam_m, adam_v, &ad));
+  PKM_TRY(need(dw, "dw"));
+  if (n_touched == nullptr) return fail(PKM_ERR_INVALID_ARG, "n_touched is NULL");
+  PKM_TRY(check_ws(handle, T, 1, ws, ws_bytes));
+  if (T == 0) return PKM_OK;
+  return run_value_grad_grouped(handle, as_stream(stream), T, w, dY, V, nullptr, dw, n_touched, ws, &ad);
+}
+
 pkm_status pkm_stage_subkey_grad(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx, const float* w,
                                  const float* dw, const void* q, const void* C, const void* Cp, float* dq, float* dC,
                                  float* dCp, void* ws, size_t ws_bytes) {

@@ -192,6 +192,11 @@ def test_adam_argument_errors():
                                ok[8], ok[9], ctypes.byref(L.pkm_adam(**good)), ok[10], ok[11], ok[12], ok[13],
                                ok[14], ok[15], ok[16], None, ok[17], 16)
     assert st == L.PKM_ERR_WORKSPACE
+    grouped = lib.pkm_stage_value_adam_grouped
+    assert grouped(h.ptr, None, 4, ok[1], ok[2], ok[3], ok[4], ok[5], ctypes.byref(L.pkm_adam(**good)), ok[6], ok[7],
+                   ok[8], 16) == L.PKM_ERR_WORKSPACE
+    assert grouped(h.ptr, None, 4, ok[1], ok[2], ok[3], ok[4], ok[5], ctypes.byref(L.pkm_adam(**{**good, "step": 0})),
+                   ok[6], ok[7], ok[8], 1 << 40) == L.PKM_ERR_INVALID_ARG
     st = lib.pkm_backward_adam(h.ptr, None, 10, ok[1], ok[2], ok[3], ok[4], ok[5], ok[6], ok[7], ctypes.byref(sv),
                                None, ok[9], ctypes.byref(L.pkm_adam(**good)), ok[10], ok[11], ok[12], ok[13],
                                ok[14], ok[15], ok[16], None, ok[17], 1 << 40)

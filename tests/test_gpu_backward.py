@@ -423,6 +423,36 @@ def test_value_adam_stage(T, h, k, nk, dv, dtype, zipf):
     adam_check(dtype, V, m0, v0, uniq, g_ref, V1, m1, v1)
 
 
+def test_row_groups_then_grouped_adam_equals_adam_stage():
+    note("row groups + grouped adam")
+    T, h, k, nk, dv = 300, 4, 32, 64, 1024
+    rows, w = pi.random_selection(78, T, h, k, nk * nk, zipf=1.2)
+    V = pi.random_array(8, 1, (nk * nk, dv), dtype="bf16", std=0.05)
+    dY = pi.random_array(8, 2, (T, dv), dtype="bf16")
+    m0, v0 = _adam_state(nk * nk, dv, 11)
+    cfg = _cfg(T=T, heads=h, topk=k, n_keys=nk, n_keys2=nk, d_value=dv, dtype="bf16")
+    layer = layer_for(cfg)
+    from product_key_memory_pkm_amd import pkm_stage_row_groups, pkm_stage_value_adam, pkm_stage_value_adam_grouped
+    outs = []
+    for split in (False, True):
+        Vd, md, vd = to_dev(V), to_dev(m0), to_dev(v0)
+        touched = torch.empty(T * h * k, dtype=torch.int32, device="cuda")
+        nt = torch.zeros(1, dtype=torch.int64, device="cuda")
+        dw = torch.empty((T, h, k), dtype=torch.float32, device="cuda")
+        ws = layer.workspace(T, True)
+        if split:
+            pkm_stage_row_groups(layer.handle, T, to_dev(rows), touched, nt, ws)
+            pkm_stage_value_adam_grouped(layer.handle, T, to_dev(w), to_dev(dY), Vd, md, vd, ADAM, dw, nt, ws)
+        else:
+            pkm_stage_value_adam(layer.handle, T, to_dev(rows), to_dev(w), to_dev(dY), Vd, md, vd, ADAM, touched, nt,
+                                 dw, ws)
+        torch.cuda.synchronize()
+        n = int(nt.item())
+        outs.append((Vd.cpu(), md.cpu(), vd.cpu(), touched.cpu()[:n], dw.cpu()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("name", ["small", "hot"])
 def test_backward_adam_end_to_end(name):
     """pkm_backward_adam: the Adam step on the oracle's touched rows, and every other output bit-identical
