@@ -31,7 +31,8 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 # holds for the kernel sources whose combined sha256 prefix is given; any change to them voids it (traffic null).
 KERNEL_TRAFFIC = {
     ("gather", "paper"): {"bytes": 13552399360, "sources": ["gather.hip", "common.h"], "sources_sha256_16": "130545acf7a0c23f"},
-    ("value_grad", "paper"): {"bytes": 29557937904, "sources": ["value_grad.hip", "sparse_common.h", "common.h"], "sources_sha256_16": "536a4ec8832f849f"},
+    ("value_grad", "paper"): {"bytes": 29565939616, "sources": ["value_grad.hip", "sparse_common.h", "common.h"], "sources_sha256_16": "d5350ce721b14972"},
+    ("value_adam", "paper"): {"bytes": 46449338752, "sources": ["value_grad.hip", "sparse_common.h", "common.h"], "sources_sha256_16": "d5350ce721b14972"},
 }
 
 
@@ -62,6 +63,8 @@ def parse():
                     help="only run a plain device copy of known size (for HBM counter calibration)")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="run this many steps and nothing else (for profilers)")
+    ap.add_argument("--profile-adam", action="store_true",
+                    help="after one step, one launch of the Adam-fused value kernel and nothing else (for profilers)")
     return ap.parse_args()
 
 
@@ -137,6 +140,20 @@ def main():
     # first call allocates the outputs and the workspace outside the timed region
     step()
     torch.cuda.synchronize()
+    if args.profile_adam:
+        # one launch of the Adam-fused value kernel on this step's grouping (for kernel counters)
+        ws = m.workspace(T, True)
+        touched = torch.empty(T * cfg.heads * cfg.topk, dtype=torch.int32, device="cuda")
+        nt = torch.zeros(1, dtype=torch.int64, device="cuda")
+        dw = torch.empty(T * cfg.heads * cfg.topk, dtype=torch.float32, device="cuda")
+        pkm_stage_row_groups(m.handle, T, saved["idx"], touched, nt, ws)
+        adam_m = torch.zeros((cfg.slots, cfg.d_value), dtype=torch.float32, device="cuda")
+        adam_v = torch.zeros_like(adam_m)
+        hp = {"lr": 1e-3, "beta1": 0.9, "beta2": 0.999, "eps": 1e-8, "step": 1}
+        pkm_stage_value_adam_grouped(m.handle, T, saved["w"], dY, V, adam_m, adam_v, hp, dw, nt, ws)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_adam": 1, "touched_rows": int(nt.item())}), flush=True)
+        return
     if args.profile_steps:
         for _ in range(args.profile_steps):
             step()
