@@ -33,7 +33,8 @@ rounded to the nearest bf16 (the value the scores are computed from) and the
 rounding is passed straight through in the backward.
 
 Beyond the lookup, ``sparse_adam_rows`` is the optimizer step on the touched
-value rows that [Blog] §6.3 describes (moments only for rows with gradient).
+value rows that [Blog] §6.3 describes (moments only for rows with gradient),
+and ``diagnostics`` the monitoring signals of [Blog] §9.3 and §11.2.
 
 Parity pins (all in ``tests/test_oracle_pins.py``): brute force over every
 full key, integer-valued exact ties, numpy cross-checks against dense
@@ -320,6 +321,34 @@ def sparse_adam_rows(V_rows: np.ndarray, m_rows: np.ndarray, v_rows: np.ndarray,
     v_hat = v1 / (1.0 - beta2 ** step)
     V1 = decode(V_rows, v_dtype) - lr * m_hat / (np.sqrt(v_hat) + eps)
     return round_to_storage(V1, v_dtype), m1, v1
+
+
+def diagnostics(rows: np.ndarray, w: np.ndarray, n_keys: int, n_keys2: int):
+    """Monitoring signals of one batch's selection ``rows`` [T, h, k] with weights ``w``.
+
+    ([Blog] §11.2: the codebook hit distribution, each sub-key's hit count and
+    the candidate softmax entropy are the signals to watch; §9.3: per-sub-key
+    hit counts and gradient density; [PKM-summary] key results: memory usage,
+    the share of slots in use, rises above 80% with BatchNorm.)  Returns
+    ``hits_c`` [h, |C|] and ``hits_cp`` [h, |C'|]: how many selected slots of
+    head h use sub-key i of C (row // |C'| == i) or j of C' (row % |C'| == j);
+    ``used`` [1 + h]: distinct rows selected over all heads, then per head;
+    ``entropy`` [T, h]: -sum_s w log w (terms with w = 0 count 0), float64.
+    """
+    T, h, k = rows.shape
+    hits_c = np.zeros((h, n_keys), dtype=np.int64)
+    hits_cp = np.zeros((h, n_keys2), dtype=np.int64)
+    used = np.zeros(1 + h, dtype=np.int64)
+    for hh in range(h):
+        r = rows[:, hh, :].reshape(-1).astype(np.int64)
+        hits_c[hh] = np.bincount(r // n_keys2, minlength=n_keys)
+        hits_cp[hh] = np.bincount(r % n_keys2, minlength=n_keys2)
+        used[1 + hh] = np.unique(r).size
+    used[0] = np.unique(rows).size
+    wf = np.asarray(w, dtype=np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        terms = np.where(wf > 0, -wf * np.log(np.where(wf > 0, wf, 1.0)), 0.0)
+    return hits_c, hits_cp, used, terms.sum(axis=-1)
 
 
 def weight_grad(rows: np.ndarray, dY: np.ndarray, V: np.ndarray, dtype: str, chunk: int = 256) -> np.ndarray:

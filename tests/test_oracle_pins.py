@@ -14,6 +14,7 @@ import os
 import numpy as np
 import pytest
 import scipy.special
+import scipy.stats
 import torch
 
 import pkm_inputs as pi
@@ -466,3 +467,42 @@ def test_sparse_adam_first_step_closed_form_and_bf16_rounding():
     exact = Vb.double().numpy() - lr * g / (np.abs(g) + eps)
     want = torch.tensor(exact).to(torch.bfloat16).double().numpy()
     np.testing.assert_array_equal(Vb1, want)
+
+
+# ---------------------------------------------------------------------------
+# Monitoring signals ([Blog] §9.3, §11.2; [PKM-summary] key results)
+# ---------------------------------------------------------------------------
+
+def test_diagnostics_against_python_loops():
+    rng = np.random.default_rng(8)
+    T, h, k, nk, nk2 = 13, 3, 4, 5, 7
+    rows = rng.integers(0, nk * nk2, size=(T, h, k)).astype(np.int32)
+    w = rng.random((T, h, k))
+    w /= w.sum(-1, keepdims=True)
+    hc, hcp, used, ent = O.diagnostics(rows, w, nk, nk2)
+    for hh in range(h):
+        for i in range(nk):
+            assert hc[hh, i] == sum(1 for t in range(T) for s in range(k) if rows[t, hh, s] // nk2 == i)
+        for j in range(nk2):
+            assert hcp[hh, j] == sum(1 for t in range(T) for s in range(k) if rows[t, hh, s] % nk2 == j)
+        assert used[1 + hh] == len({int(rows[t, hh, s]) for t in range(T) for s in range(k)})
+    assert used[0] == len({int(r) for r in rows.reshape(-1)})
+    assert (hc.sum(1) == T * k).all() and (hcp.sum(1) == T * k).all()
+    for t in range(T):
+        for hh in range(h):
+            want = -sum(float(x) * math.log(float(x)) for x in w[t, hh])
+            assert abs(ent[t, hh] - want) <= 1e-13
+
+
+def test_diagnostics_entropy_closed_forms():
+    k = 8
+    rows = np.arange(3 * 2 * k, dtype=np.int32).reshape(3, 2, k)
+    w = np.zeros((3, 2, k))
+    w[0] = 1.0 / k                       # uniform: log k
+    w[1, :, 0] = 1.0                     # one-hot: 0 (w = 0 terms count 0)
+    w[2] = scipy.special.softmax(np.arange(k, dtype=np.float64))
+    _, _, used, ent = O.diagnostics(rows, w, 8, 8)
+    np.testing.assert_allclose(ent[0], math.log(k), rtol=1e-15)
+    assert (ent[1] == 0.0).all()
+    np.testing.assert_allclose(ent[2], scipy.stats.entropy(w[2, 0]), rtol=1e-13)
+    assert used[0] == 3 * 2 * k and (used[1:] == 3 * k).all()
