@@ -240,6 +240,23 @@ pkm_status pkm_stage_value_adam(pkm_handle_t handle, void* stream, int64_t T, co
                                 const pkm_adam* adam, int32_t* touched, int64_t* n_touched, float* dw,
                                 void* ws, size_t ws_bytes);
 
+/* Monitoring signals of a batch's selection ("Meta AI 可扩展内存层", section 11.2:
+ * codebook hit distribution, per-sub-key hit counts, candidate softmax entropy;
+ * section 9.3: per-sub-key hits and gradient density; product-key paper summary,
+ * key results: memory usage, the share of slots in use).  From idx, w [T, h, k]
+ * (as the forward saves them), all outputs on the device:
+ *   hits_c [h, |C|], hits_cp [h, |C'|] int32: selected slots of head h whose row
+ *     has first-half sub-key i (row / |C'| == i), second-half sub-key j (row % |C'|);
+ *   used [1 + h] int64 (8-byte aligned): distinct rows over all heads, then per head;
+ *   entropy [T, h] fp32 (may be NULL): -sum_s w log w (w = 0 terms count 0);
+ *   entropy_sum [1] fp64 (may be NULL, 8-byte aligned): the sum of entropy over
+ *     (t, h), in a fixed order.
+ * Integer outputs are exact; rows outside [0, |C|*|C'|) are not counted.
+ * ws >= pkm_workspace_size(handle, T, 1). */
+pkm_status pkm_diagnostics(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx, const float* w,
+                           int32_t* hits_c, int32_t* hits_cp, int64_t* used, float* entropy, double* entropy_sum,
+                           void* ws, size_t ws_bytes);
+
 /* Step a8's grouping alone: the lookups of idx [T, h, k] stably sorted by row,
  * written into the workspace (for pkm_stage_value_grad_grouped), plus touched
  * and *n_touched as in pkm_backward.  ws >= pkm_workspace_size(handle, T, 1). */

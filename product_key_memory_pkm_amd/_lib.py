@@ -68,6 +68,7 @@ _SIGS = {
                              _VP, _SZ],
     "pkm_stage_value_adam_grouped": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_adam), _VP, _VP,
                                      _VP, _SZ],
+    "pkm_diagnostics": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
     "pkm_stage_row_groups": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _SZ],
     "pkm_stage_value_grad_grouped": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
     "pkm_stage_subkey_grad": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
@@ -286,6 +287,19 @@ def pkm_stage_value_adam_grouped(h, T, w, dY, V, adam_m, adam_v, adam: dict, dw,
     _check(_invoke("pkm_stage_value_adam_grouped", h, T, _ptr(w), _ptr(dY), _ptr(V), _ptr(adam_m), _ptr(adam_v),
                    ctypes.byref(hp), _ptr(dw), _ptr(n_touched), _ptr(ws), _nbytes(ws)),
            "pkm_stage_value_adam_grouped")
+
+
+def pkm_diagnostics(h, T, idx, w, hits_c, hits_cp, used, entropy, entropy_sum, ws):
+    """Monitoring signals of a selection: sub-key hit counts, slots in use, softmax entropy (see pkm.h)."""
+    _dt(idx, torch.int32, "idx")
+    _dt(w, torch.float32, "w")
+    _dt(hits_c, torch.int32, "hits_c")
+    _dt(hits_cp, torch.int32, "hits_cp")
+    _dt(used, torch.int64, "used")
+    _dt(entropy, torch.float32, "entropy")
+    _dt(entropy_sum, torch.float64, "entropy_sum")
+    _check(_invoke("pkm_diagnostics", h, T, _ptr(idx), _ptr(w), _ptr(hits_c), _ptr(hits_cp), _ptr(used),
+                   _ptr(entropy), _ptr(entropy_sum), _ptr(ws), _nbytes(ws)), "pkm_diagnostics")
 
 
 def pkm_stage_subkey_grad(h, T, idx, w, dw, q, C, Cp, dq, dC, dCp, ws):

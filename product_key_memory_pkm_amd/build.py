@@ -13,7 +13,7 @@ OUT = os.path.join(PKG, "libpkm.so")
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.hip", "gather.hip", "score_topk.hip", "merge_softmax.hip", "gemm.hip", "bn.hip", "sort.hip",
-           "value_grad.hip", "subkey_grad.hip"]
+           "value_grad.hip", "subkey_grad.hip", "diagnostics.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

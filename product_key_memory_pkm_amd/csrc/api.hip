@@ -146,7 +146,8 @@ BwdLayout bwd_layout(const pkm_handle_s* h, int64_t T) {
 size_t ws_size(const pkm_handle_s* h, int64_t T, int with_backward) {
   const size_t f = fwd_layout(h, T).total;
   if (!with_backward) return f;
-  const size_t b = bwd_layout(h, T).total;
+  const size_t b = std::max(bwd_layout(h, T).total,
+                            diagnostics_ws_bytes(T, h->cfg.heads, int64_t(h->cfg.n_keys) * h->cfg.n_keys2));
   return f > b ? f : b;
 }
 
@@ -747,6 +748,28 @@ pkm_status pkm_stage_value_adam(pkm_handle_t handle, void* stream, int64_t T, co
   hipStream_t s = as_stream(stream);
   if (T == 0) return zero_grads(handle, s, n_touched, nullptr, nullptr, nullptr, nullptr, nullptr);
   return run_value_grad(handle, s, T, idx, w, dY, V, nullptr, touched, n_touched, dw, ws, &ad);
+}
+
+pkm_status pkm_diagnostics(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx, const float* w,
+                           int32_t* hits_c, int32_t* hits_cp, int64_t* used, float* entropy, double* entropy_sum,
+                           void* ws, size_t ws_bytes) {
+  PKM_TRY(check_handle(handle));
+  PKM_TRY(check_T(handle, T));
+  PKM_TRY(need(idx, "idx"));
+  PKM_TRY(need(w, "w"));
+  PKM_TRY(need(hits_c, "hits_c"));
+  PKM_TRY(need(hits_cp, "hits_cp"));
+  if (used == nullptr) return fail(PKM_ERR_INVALID_ARG, "used is NULL");
+  if (reinterpret_cast<uintptr_t>(used) % 8 != 0) return fail(PKM_ERR_INVALID_ARG, "used is not 8-byte aligned");
+  if (entropy) PKM_TRY(need(entropy, "entropy"));
+  if (entropy_sum && reinterpret_cast<uintptr_t>(entropy_sum) % 8 != 0)
+    return fail(PKM_ERR_INVALID_ARG, "entropy_sum is not 8-byte aligned");
+  PKM_TRY(check_ws(handle, T, 1, ws, ws_bytes));
+  const pkm_config& c = handle->cfg;
+  PKM_HIP(launch_diagnostics(as_stream(stream), idx, w, T, c.heads, c.topk, c.n_keys, c.n_keys2, hits_c, hits_cp,
+                             used, entropy, entropy_sum, ws),
+          "diagnostics");
+  return PKM_OK;
 }
 
 pkm_status pkm_stage_row_groups(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx, int32_t* touched,

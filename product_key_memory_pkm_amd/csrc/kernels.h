@@ -122,4 +122,12 @@ hipError_t launch_subkey_grad(hipStream_t s, int dtype, const int32_t* seg_start
 
 hipError_t launch_fill_f32(hipStream_t s, float* p, int64_t n, float v);
 
+// Monitoring signals of a selection (idx, w [ntok, heads, k]): sub-key hit
+// counts, slots in use (all heads, then per head), entropy per (t, h) (may be
+// null) and its fp64 sum (may be null).  ws: diagnostics_ws_bytes.
+size_t diagnostics_ws_bytes(int64_t ntok, int heads, int64_t nrows);
+hipError_t launch_diagnostics(hipStream_t s, const int32_t* idx, const float* w, int64_t ntok, int heads, int k,
+                              int nk, int nk2, int32_t* hits_c, int32_t* hits_cp, int64_t* used, float* entropy,
+                              double* entropy_sum, void* ws);
+
 }  // namespace pkm

@@ -203,6 +203,21 @@ def test_adam_argument_errors():
     assert st == L.PKM_ERR_INVALID_ARG and "adam_m" in lib.pkm_last_error().decode()
 
 
+def test_diagnostics_argument_errors():
+    L = _lib()
+    lib = L.lib()
+    h = L.pkm_create(_cfg(L))
+    ok = [_fake(i) for i in range(12)]
+    d = lib.pkm_diagnostics
+    assert d(h.ptr, None, 4, ok[1], ok[2], ok[3], ok[4], ok[5], None, None, ok[6], 16) == L.PKM_ERR_WORKSPACE
+    assert d(h.ptr, None, 4, ok[1], None, ok[3], ok[4], ok[5], None, None, ok[6], 1 << 30) == L.PKM_ERR_INVALID_ARG
+    assert d(h.ptr, None, 4, ok[1], ok[2], ok[3], ok[4], None, None, None, ok[6], 1 << 30) == L.PKM_ERR_INVALID_ARG
+    assert "used" in lib.pkm_last_error().decode()
+    assert d(h.ptr, None, 4, ok[1], ok[2], ok[3], ok[4], ctypes.c_void_p(FAKE + 4), None, None, ok[6],
+             1 << 30) == L.PKM_ERR_INVALID_ARG                                              # misaligned used
+    assert d(h.ptr, None, -1, ok[1], ok[2], ok[3], ok[4], ok[5], None, None, ok[6], 1 << 30) == L.PKM_ERR_INVALID_ARG
+
+
 def test_binding_rejects_host_tensors():
     L = _lib()
     import torch

@@ -331,3 +331,48 @@ def test_forward_is_deterministic():
     b, _ = run_gpu_forward(cfg, inp)
     for k in a:
         np.testing.assert_array_equal(a[k], b[k])
+
+
+# ---------------------------------------------------------------------------
+# Monitoring signals of a selection ([Blog] §9.3, §11.2; [PKM-summary] key results)
+# ---------------------------------------------------------------------------
+DIAG_CASES = [
+    # T, heads, k, nk, nk2, zipf
+    (100, 2, 8, 16, 24, 0.0),
+    (3000, 4, 32, 64, 64, 1.1),       # skewed: hot rows and sub-keys
+    (1, 1, 1, 4, 4, 0.0),
+    (0, 3, 4, 8, 8, 0.0),             # empty batch: zero counts
+    (700, 8, 16, 2048, 2048, 0.0),    # the largest codebooks
+]
+
+
+@pytest.mark.parametrize("T,h,k,nk,nk2,zipf", DIAG_CASES)
+def test_diagnostics_stage(T, h, k, nk, nk2, zipf):
+    note(f"diagnostics T={T} h={h} k={k} nk={nk}/{nk2} zipf={zipf}")
+    if T > 0:
+        rows, w = pi.random_selection(T * 5 + 3, T, h, k, nk * nk2, zipf=zipf)
+        w = w.copy()
+        w[::7, :, -1] = 0.0          # some zero weights: their terms count 0
+    else:
+        rows = np.zeros((0, h, k), dtype=np.int32)
+        w = np.zeros((0, h, k), dtype=np.float32)
+    cfg = _cfg(T=max(T, 1), heads=h, dq=16, n_keys=nk, n_keys2=nk2, topk=k, dtype="f32", d=16, d_value=16)
+    layer = layer_for(cfg)
+    from product_key_memory_pkm_amd import pkm_diagnostics
+    hc = torch.full((h, nk), -1, dtype=torch.int32, device="cuda")
+    hcp = torch.full((h, nk2), -1, dtype=torch.int32, device="cuda")
+    used = torch.full((1 + h,), -1, dtype=torch.int64, device="cuda")
+    ent = torch.empty((max(T, 1), h), dtype=torch.float32, device="cuda")
+    ent_sum = torch.full((1,), -1.0, dtype=torch.float64, device="cuda")
+    rd = to_dev(rows) if T > 0 else torch.zeros(1, dtype=torch.int32, device="cuda")
+    wd = to_dev(w.astype(np.float32)) if T > 0 else torch.zeros(1, dtype=torch.float32, device="cuda")
+    pkm_diagnostics(layer.handle, T, rd, wd, hc, hcp, used, ent, ent_sum, layer.workspace(max(T, 1), True))
+    torch.cuda.synchronize()
+    r_hc, r_hcp, r_used, r_ent = O.diagnostics(rows, w.astype(np.float32).astype(np.float64), nk, nk2)
+    np.testing.assert_array_equal(hc.cpu().numpy(), r_hc)
+    np.testing.assert_array_equal(hcp.cpu().numpy(), r_hcp)
+    np.testing.assert_array_equal(used.cpu().numpy(), r_used)
+    got = ent.cpu().numpy()[:T].astype(np.float64)
+    assert np.all(np.abs(got - r_ent) <= 1e-5 * np.abs(r_ent) + 1e-6)
+    total = float(ent_sum.cpu().item())
+    assert abs(total - r_ent.sum()) <= 1e-5 * abs(r_ent.sum()) + 1e-6
