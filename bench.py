@@ -85,7 +85,10 @@ def alg_bytes(cfg, touched):
     # the same kernel with the Adam step of the touched rows instead of dV: the
     # value row read and written, both fp32 moment rows read and written
     value_adam = touched * (2 * dv * e + 4 * dv * 4 + 4) + cfg.T * dv * e + L * 12
-    return {"gather": gather, "value_grad": value_grad, "value_adam": value_adam}
+    # monitoring signals: idx and w read once, entropy written, the per-head
+    # slot byte maps cleared and counted (read twice: per head and OR)
+    diagnostics = L * 8 + cfg.T * cfg.heads * 4 + cfg.heads * cfg.slots * 3
+    return {"gather": gather, "value_grad": value_grad, "value_adam": value_adam, "diagnostics": diagnostics}
 
 
 def main():
@@ -99,7 +102,7 @@ def main():
 
     import pkm_inputs as pi
     from product_key_memory_pkm_amd import (ProductKeyMemory, pkm_stage_gather, pkm_stage_row_groups,
-                                            pkm_stage_score_topk, pkm_stage_value_adam_grouped,
+                                            pkm_diagnostics, pkm_stage_score_topk, pkm_stage_value_adam_grouped,
                                             pkm_stage_value_grad_grouped)
 
     if args.copy_calibration:
@@ -217,6 +220,18 @@ def main():
                                                        ws), nf)
     del V_opt, adam_m, adam_v
     torch.cuda.empty_cache()
+    # monitoring signals of the step's selection
+    hits_c = torch.empty((cfg.heads, cfg.n_keys), dtype=torch.int32, device="cuda")
+    hits_cp = torch.empty((cfg.heads, cfg.n_keys2), dtype=torch.int32, device="cuda")
+    used = torch.empty(1 + cfg.heads, dtype=torch.int64, device="cuda")
+    ent = torch.empty((T, cfg.heads), dtype=torch.float32, device="cuda")
+    ent_sum = torch.empty(1, dtype=torch.float64, device="cuda")
+    dg_ms = timed(lambda: pkm_diagnostics(m.handle, T, saved["idx"], saved["w"], hits_c, hits_cp, used, ent, ent_sum,
+                                          ws), nf)
+    diag = {"slots_in_use": int(used[0].item()), "slots_in_use_fraction": int(used[0].item()) / cfg.slots,
+            "mean_softmax_entropy": float(ent_sum.item()) / (T * cfg.heads),
+            "max_subkey_hits": int(max(hits_c.max().item(), hits_cp.max().item())),
+            "mean_subkey_hits": T * cfg.topk / cfg.n_keys}
     # the per-half scoring + top-k kernel alone (its MFMA roofline)
     sub_idx = torch.empty((T, cfg.heads, 2, cfg.topk), dtype=torch.int32, device="cuda")
     sub_score = torch.empty((T, cfg.heads, 2, cfg.topk), dtype=torch.float32, device="cuda")
@@ -233,6 +248,8 @@ def main():
     # not a step of the lookup itself: the optimizer step fused into a8 (reported beside it)
     kern["value_adam"] = {"kernel": "value_grad with the Adam step of the touched value rows (a7 dw + a8 + optimizer)",
                           "ms": va_ms, "alg": ab["value_adam"]}
+    kern["diagnostics"] = {"kernel": "diagnostics (hit counts, slots in use, softmax entropy)", "ms": dg_ms,
+                           "alg": ab["diagnostics"]}
     for k_ in kern.values():
         k_["achieved"] = k_["alg"] / (k_["ms"] * 1e-3) / 1e9
 
@@ -269,6 +286,7 @@ def main():
                                            "frac": score_tf / score_peak, "traffic": None,
                                            "alg_flops_per_launch": score_flops, "avg_launch_ms": score_ms}),
         "touched_rows": n_touched,
+        "diagnostics": diag,
         "memory_usage": n_touched / cfg.slots,
         "input_generation_s": gen_s,
     }

@@ -10,9 +10,12 @@
 //   entropy[t, h] = -sum_s w log w,  entropy_sum = sum over (t, h), fp64 in a fixed order
 //
 // Counts are integers (atomics give exact, order-free results): per (head,
-// token slice) the sub-key hits are counted in LDS and added once per sub-key;
-// every selected row sets its bit in an all-heads and a per-head slot bitmap,
-// whose popcounts are the slots in use.
+// token slice) the sub-key hits are counted in LDS, one thread per token (a
+// token's k slots share few sub-keys, so lanes of different tokens rarely hit
+// the same counter at once), and added once per sub-key; every selected row
+// stores 1 into its byte of its head's slot map (a plain store: writing the
+// same value needs no atomic).  The non-zero bytes of the head maps, and of
+// their OR for all heads, are the slots in use.
 #include "common.h"
 #include "kernels.h"
 
@@ -20,31 +23,54 @@ namespace pkm {
 
 namespace {
 
-constexpr int kDiagTokens = 256;  // tokens per hit-count block
+constexpr int kDiagTokens = 256;  // tokens per hit-count block (one per thread)
+
+// Clears up to four buffers (n32[i] 32-bit words each) in one launch.
+struct ZeroList {
+  uint32_t* p[4];
+  int64_t n32[4];
+};
+__global__ __launch_bounds__(256) void diag_zero_kernel(ZeroList z) {
+  for (int b = 0; b < 4; ++b)
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < z.n32[b]; i += int64_t(gridDim.x) * 256)
+      z.p[b][i] = 0u;
+}
 
 __global__ __launch_bounds__(256) void diag_hits_kernel(const int32_t* __restrict__ idx, int64_t ntok, int heads,
                                                         int k, int nk, int nk2, int32_t* __restrict__ hits_c,
-                                                        int32_t* __restrict__ hits_cp, uint32_t* __restrict__ bitmaps,
-                                                        int64_t bm_words) {
+                                                        int32_t* __restrict__ hits_cp, uint8_t* __restrict__ maps,
+                                                        int64_t map_bytes) {
   extern __shared__ int32_t cnt[];  // [nk + nk2]
   const int hh = blockIdx.y;
   for (int i = threadIdx.x; i < nk + nk2; i += 256) cnt[i] = 0;
   __syncthreads();
-  const int64_t t0 = int64_t(blockIdx.x) * kDiagTokens;
-  const int64_t t1 = t0 + kDiagTokens < ntok ? t0 + kDiagTokens : ntok;
-  const int64_t n = (t1 - t0) * k;
+  const int64_t t = int64_t(blockIdx.x) * kDiagTokens + threadIdx.x;
   const uint32_t nrows = uint32_t(nk) * uint32_t(nk2);
-  uint32_t* bm_all = bitmaps;
-  uint32_t* bm_h = bitmaps + int64_t(1 + hh) * bm_words;
-  for (int64_t e = threadIdx.x; e < n; e += 256) {
-    const int64_t t = t0 + e / k;
-    const int s = int(e % k);
-    const uint32_t row = uint32_t(idx[(t * heads + hh) * k + s]);
-    if (row < nrows) {  // rows outside the table are not counted
-      atomicAdd(&cnt[row / uint32_t(nk2)], 1);
-      atomicAdd(&cnt[nk + int(row % uint32_t(nk2))], 1);
-      atomicOr(&bm_all[row >> 5], 1u << (row & 31));
-      atomicOr(&bm_h[row >> 5], 1u << (row & 31));
+  uint8_t* map = maps + int64_t(hh) * map_bytes;
+  if (t < ntok) {
+    const int32_t* it = idx + (t * heads + hh) * k;
+    auto count = [&](uint32_t row) {
+      if (row < nrows) {  // rows outside the table are not counted
+        atomicAdd(&cnt[row / uint32_t(nk2)], 1);
+        atomicAdd(&cnt[nk + int(row % uint32_t(nk2))], 1);
+        map[row] = 1;
+      }
+    };
+    if ((k & 3) == 0) {  // the token's row ids with 16-byte loads, 4 at a time
+      for (int s = 0; s < k; s += 8) {
+        const int4 a = *reinterpret_cast<const int4*>(it + s);
+        const int4 b = s + 4 < k ? *reinterpret_cast<const int4*>(it + s + 4) : make_int4(-1, -1, -1, -1);
+        count(uint32_t(a.x));
+        count(uint32_t(a.y));
+        count(uint32_t(a.z));
+        count(uint32_t(a.w));
+        count(uint32_t(b.x));
+        count(uint32_t(b.y));
+        count(uint32_t(b.z));
+        count(uint32_t(b.w));
+      }
+    } else {
+      for (int s = 0; s < k; ++s) count(uint32_t(it[s]));
     }
   }
   __syncthreads();
@@ -54,15 +80,32 @@ __global__ __launch_bounds__(256) void diag_hits_kernel(const int32_t* __restric
     if (cnt[nk + j]) atomicAdd(&hits_cp[int64_t(hh) * nk2 + j], cnt[nk + j]);
 }
 
-// used[b] += set bits of bitmap b (grid.y = bitmap)
-__global__ __launch_bounds__(256) void diag_popc_kernel(const uint32_t* __restrict__ bitmaps, int64_t bm_words,
-                                                        unsigned long long* __restrict__ used) {
-  const uint32_t* bm = bitmaps + int64_t(blockIdx.y) * bm_words;
+// Non-zero bytes of a 32-bit word of a 0/1 byte map.
+__device__ __forceinline__ int bytes_set(uint32_t x) { return __popc(x & 0x01010101u); }
+
+// used[0] += set bytes of the OR of the head maps (grid.y = 0), used[y] += set
+// bytes of head y - 1's map (grid.y >= 1); one atomic per block.
+__global__ __launch_bounds__(256) void diag_count_kernel(const uint32_t* __restrict__ maps, int64_t map_words,
+                                                         int heads, unsigned long long* __restrict__ used) {
+  __shared__ int wsum[4];
+  const int y = blockIdx.y;
   int c = 0;
-  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < bm_words; i += int64_t(gridDim.x) * 256)
-    c += __popc(bm[i]);
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < map_words; i += int64_t(gridDim.x) * 256) {
+    uint32_t x = 0;
+    if (y == 0) {
+      for (int hh = 0; hh < heads; ++hh) x |= maps[int64_t(hh) * map_words + i];
+    } else {
+      x = maps[int64_t(y - 1) * map_words + i];
+    }
+    c += bytes_set(x);
+  }
   c = wave_sum_i(c);
-  if (lane_id() == 0 && c) atomicAdd(&used[blockIdx.y], (unsigned long long)c);
+  if (lane_id() == 0) wsum[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int tot = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    if (tot) atomicAdd(&used[y], (unsigned long long)tot);
+  }
 }
 
 // Fixed-order sum of the 256 values of a block (tree over LDS); result in sh[0].
@@ -74,21 +117,36 @@ __device__ __forceinline__ void block_sum_f64(double* sh) {
   __syncthreads();
 }
 
-// entropy of every (t, h) item (n = T*h) and per-block fp64 partial sums
+// Entropy of every (t, h) item (n = T*h): eight lanes per item, lane j taking
+// weights 4j.. (16-byte loads when k is a multiple of 4), a fixed xor-tree sum
+// over the eight; per-block fp64 partial sums of the 32 items of the block.
 __global__ __launch_bounds__(256) void diag_entropy_kernel(const float* __restrict__ w, int64_t n, int k,
                                                            float* __restrict__ ent, double* __restrict__ part) {
   __shared__ double sh[256];
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int sub = threadIdx.x & 7;
+  const int64_t i = int64_t(blockIdx.x) * 32 + (threadIdx.x >> 3);
   float e = 0.f;
   if (i < n) {
     const float* wi = w + i * k;
-    for (int s = 0; s < k; ++s) {
-      const float x = wi[s];
-      if (x > 0.f) e -= x * logf(x);
+    if ((k & 3) == 0) {
+      for (int s = 4 * sub; s < k; s += 32) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(wi + s);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (x[q] > 0.f) e -= x[q] * logf(x[q]);
+      }
+    } else {
+      for (int s = sub; s < k; s += 8) {
+        const float x = wi[s];
+        if (x > 0.f) e -= x * logf(x);
+      }
     }
-    if (ent) ent[i] = e;
   }
-  sh[threadIdx.x] = double(e);
+  e += __shfl_xor(e, 1, 64);
+  e += __shfl_xor(e, 2, 64);
+  e += __shfl_xor(e, 4, 64);
+  if (sub == 0 && i < n && ent) ent[i] = e;
+  sh[threadIdx.x] = sub == 0 ? double(e) : 0.0;
   block_sum_f64(sh);
   if (threadIdx.x == 0) part[blockIdx.x] = sh[0];
 }
@@ -104,40 +162,56 @@ __global__ __launch_bounds__(256) void diag_sum_kernel(const double* __restrict_
 }
 
 inline size_t al256(size_t b) { return (b + 255) / 256 * 256; }
+inline int64_t map_bytes_of(int64_t nrows) { return (nrows + 255) / 256 * 256; }  // whole 32-bit words, aligned
 
 }  // namespace
 
 size_t diagnostics_ws_bytes(int64_t ntok, int heads, int64_t nrows) {
-  const int64_t words = (nrows + 31) / 32;
-  const int64_t nblk = (ntok * heads + 255) / 256;
-  return al256(size_t(1 + heads) * size_t(words) * 4) + al256(size_t(nblk > 0 ? nblk : 1) * 8);
+  const int64_t nblk = (ntok * heads + 31) / 32;
+  return al256(size_t(heads) * size_t(map_bytes_of(nrows))) + al256(size_t(nblk > 0 ? nblk : 1) * 8);
 }
 
 hipError_t launch_diagnostics(hipStream_t s, const int32_t* idx, const float* w, int64_t ntok, int heads, int k,
                               int nk, int nk2, int32_t* hits_c, int32_t* hits_cp, int64_t* used, float* entropy,
                               double* entropy_sum, void* ws) {
   const int64_t nrows = int64_t(nk) * nk2;
-  const int64_t words = (nrows + 31) / 32;
-  uint32_t* bitmaps = static_cast<uint32_t*>(ws);
-  double* part = reinterpret_cast<double*>(static_cast<char*>(ws) + al256(size_t(1 + heads) * size_t(words) * 4));
-  hipError_t e;
-  // every fill writes zero bits (int32 / int64 / uint32 zeros)
-  if ((e = launch_fill_f32(s, reinterpret_cast<float*>(hits_c), int64_t(heads) * nk, 0.f)) != hipSuccess) return e;
-  if ((e = launch_fill_f32(s, reinterpret_cast<float*>(hits_cp), int64_t(heads) * nk2, 0.f)) != hipSuccess) return e;
-  if ((e = launch_fill_f32(s, reinterpret_cast<float*>(used), 2 * int64_t(1 + heads), 0.f)) != hipSuccess) return e;
-  if ((e = launch_fill_f32(s, reinterpret_cast<float*>(bitmaps), int64_t(1 + heads) * words, 0.f)) != hipSuccess)
-    return e;
-  if (entropy_sum && (e = launch_fill_f32(s, reinterpret_cast<float*>(entropy_sum), 2, 0.f)) != hipSuccess) return e;
-  if (ntok == 0) return hipGetLastError();
+  const int64_t mb = map_bytes_of(nrows);
+  uint8_t* maps = static_cast<uint8_t*>(ws);
+  double* part = reinterpret_cast<double*>(static_cast<char*>(ws) + al256(size_t(heads) * size_t(mb)));
+  ZeroList z;
+  z.p[0] = reinterpret_cast<uint32_t*>(hits_c);
+  z.n32[0] = int64_t(heads) * nk;
+  z.p[1] = reinterpret_cast<uint32_t*>(hits_cp);
+  z.n32[1] = int64_t(heads) * nk2;
+  z.p[2] = reinterpret_cast<uint32_t*>(used);
+  z.n32[2] = 2 * int64_t(1 + heads);
+  z.p[3] = reinterpret_cast<uint32_t*>(maps);
+  z.n32[3] = int64_t(heads) * mb / 4;
+  int64_t zb = (z.n32[3] + 255) / 256;
+  if (zb > 2048) zb = 2048;
+  if (zb < 1) zb = 1;
+  hipLaunchKernelGGL(diag_zero_kernel, dim3(unsigned(zb)), dim3(256), 0, s, z);
+  if (ntok == 0) {
+    if (entropy_sum) {
+      ZeroList z2 = {};
+      z2.p[0] = reinterpret_cast<uint32_t*>(entropy_sum);
+      z2.n32[0] = 2;
+      for (int b = 1; b < 4; ++b) z2.p[b] = nullptr;
+      hipLaunchKernelGGL(diag_zero_kernel, dim3(1), dim3(256), 0, s, z2);
+    }
+    return hipGetLastError();
+  }
   const dim3 gh(unsigned((ntok + kDiagTokens - 1) / kDiagTokens), unsigned(heads));
   hipLaunchKernelGGL(diag_hits_kernel, gh, dim3(256), size_t(nk + nk2) * 4, s, idx, ntok, heads, k, nk, nk2, hits_c,
-                     hits_cp, bitmaps, words);
-  int64_t pb = (words + 255) / 256;
-  if (pb > 1024) pb = 1024;
-  hipLaunchKernelGGL(diag_popc_kernel, dim3(unsigned(pb), unsigned(1 + heads)), dim3(256), 0, s, bitmaps, words,
+                     hits_cp, maps, mb);
+  const int64_t words = mb / 4;
+  int64_t cb = (words + 256 * 16 - 1) / (256 * 16);  // ~16 words per thread
+  if (cb < 1) cb = 1;
+  hipLaunchKernelGGL(diag_count_kernel, dim3(unsigned(cb), unsigned(1 + heads)), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t*>(maps), words, heads,
                      reinterpret_cast<unsigned long long*>(used));
   const int64_t n = ntok * heads;
-  const int64_t nblk = (n + 255) / 256;
+  const int64_t nblk = (n + 31) / 32;
   hipLaunchKernelGGL(diag_entropy_kernel, dim3(unsigned(nblk)), dim3(256), 0, s, w, n, k, entropy, part);
   if (entropy_sum) hipLaunchKernelGGL(diag_sum_kernel, dim3(1), dim3(256), 0, s, part, nblk, entropy_sum);
   return hipGetLastError();
