@@ -63,6 +63,8 @@ def parse():
                     help="only run a plain device copy of known size (for HBM counter calibration)")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="run this many steps and nothing else (for profilers)")
+    ap.add_argument("--profile-diag", action="store_true",
+                    help="after one step, five launches of the diagnostics on its selection and nothing else")
     ap.add_argument("--profile-adam", action="store_true",
                     help="after one step, one launch of the Adam-fused value kernel and nothing else (for profilers)")
     return ap.parse_args()
@@ -143,6 +145,18 @@ def main():
     # first call allocates the outputs and the workspace outside the timed region
     step()
     torch.cuda.synchronize()
+    if args.profile_diag:
+        hits_c = torch.empty((cfg.heads, cfg.n_keys), dtype=torch.int32, device="cuda")
+        hits_cp = torch.empty((cfg.heads, cfg.n_keys2), dtype=torch.int32, device="cuda")
+        used = torch.empty(1 + cfg.heads, dtype=torch.int64, device="cuda")
+        ent = torch.empty((T, cfg.heads), dtype=torch.float32, device="cuda")
+        ent_sum = torch.empty(1, dtype=torch.float64, device="cuda")
+        for _ in range(5):
+            pkm_diagnostics(m.handle, T, saved["idx"], saved["w"], hits_c, hits_cp, used, ent, ent_sum,
+                            m.workspace(T, True))
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_diag": 5, "slots_in_use": int(used[0].item())}), flush=True)
+        return
     if args.profile_adam:
         # one launch of the Adam-fused value kernel on this step's grouping (for kernel counters)
         ws = m.workspace(T, True)

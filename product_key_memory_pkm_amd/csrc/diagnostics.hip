@@ -83,29 +83,43 @@ __global__ __launch_bounds__(256) void diag_hits_kernel(const int32_t* __restric
 // Non-zero bytes of a 32-bit word of a 0/1 byte map.
 __device__ __forceinline__ int bytes_set(uint32_t x) { return __popc(x & 0x01010101u); }
 
-// used[0] += set bytes of the OR of the head maps (grid.y = 0), used[y] += set
-// bytes of head y - 1's map (grid.y >= 1); one atomic per block.
+constexpr int kCountWords = 16;  // map words per thread in the count pass
+
+// One pass over the head maps: per head the set bytes of its words (used[1 + h])
+// and of their OR over the heads (used[0]); one atomic per block and counter.
 __global__ __launch_bounds__(256) void diag_count_kernel(const uint32_t* __restrict__ maps, int64_t map_words,
                                                          int heads, unsigned long long* __restrict__ used) {
   __shared__ int wsum[4];
-  const int y = blockIdx.y;
-  int c = 0;
-  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < map_words; i += int64_t(gridDim.x) * 256) {
-    uint32_t x = 0;
-    if (y == 0) {
-      for (int hh = 0; hh < heads; ++hh) x |= maps[int64_t(hh) * map_words + i];
-    } else {
-      x = maps[int64_t(y - 1) * map_words + i];
+  const int64_t base = int64_t(blockIdx.x) * 256 * kCountWords + threadIdx.x;
+  uint32_t orw[kCountWords];
+#pragma unroll
+  for (int j = 0; j < kCountWords; ++j) orw[j] = 0u;
+  auto block_add = [&](int c, unsigned long long* dst) {
+    c = wave_sum_i(c);
+    __syncthreads();
+    if (lane_id() == 0) wsum[threadIdx.x >> 6] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int tot = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+      if (tot) atomicAdd(dst, (unsigned long long)tot);
     }
-    c += bytes_set(x);
+  };
+  for (int hh = 0; hh < heads; ++hh) {
+    const uint32_t* m = maps + int64_t(hh) * map_words;
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < kCountWords; ++j) {
+      const int64_t i = base + int64_t(j) * 256;
+      const uint32_t x = i < map_words ? m[i] : 0u;
+      orw[j] |= x;
+      c += bytes_set(x);
+    }
+    block_add(c, &used[1 + hh]);
   }
-  c = wave_sum_i(c);
-  if (lane_id() == 0) wsum[threadIdx.x >> 6] = c;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int tot = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    if (tot) atomicAdd(&used[y], (unsigned long long)tot);
-  }
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < kCountWords; ++j) c += bytes_set(orw[j]);
+  block_add(c, &used[0]);
 }
 
 // Fixed-order sum of the 256 values of a block (tree over LDS); result in sh[0].
@@ -124,29 +138,35 @@ __global__ __launch_bounds__(256) void diag_entropy_kernel(const float* __restri
                                                            float* __restrict__ ent, double* __restrict__ part) {
   __shared__ double sh[256];
   const int sub = threadIdx.x & 7;
-  const int64_t i = int64_t(blockIdx.x) * 32 + (threadIdx.x >> 3);
-  float e = 0.f;
-  if (i < n) {
-    const float* wi = w + i * k;
-    if ((k & 3) == 0) {
-      for (int s = 4 * sub; s < k; s += 32) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(wi + s);
+  double acc = 0.0;  // this lane group's items, in a fixed order
+  // every lane of the block takes the same number of steps (the test is on the
+  // block's first item), so the shuffles below always see the whole wave
+  for (int64_t i = int64_t(blockIdx.x) * 32 + (threadIdx.x >> 3); i - (threadIdx.x >> 3) < n;
+       i += int64_t(gridDim.x) * 32) {
+    float e = 0.f;
+    if (i < n) {
+      const float* wi = w + i * k;
+      if ((k & 3) == 0) {
+        for (int s = 4 * sub; s < k; s += 32) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(wi + s);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (x[q] > 0.f) e -= x[q] * logf(x[q]);
-      }
-    } else {
-      for (int s = sub; s < k; s += 8) {
-        const float x = wi[s];
-        if (x > 0.f) e -= x * logf(x);
+          for (int q = 0; q < 4; ++q)
+            if (x[q] > 0.f) e -= x[q] * logf(x[q]);
+        }
+      } else {
+        for (int s = sub; s < k; s += 8) {
+          const float x = wi[s];
+          if (x > 0.f) e -= x * logf(x);
+        }
       }
     }
+    e += __shfl_xor(e, 1, 64);
+    e += __shfl_xor(e, 2, 64);
+    e += __shfl_xor(e, 4, 64);
+    if (sub == 0 && i < n && ent) ent[i] = e;
+    if (sub == 0 && i < n) acc += double(e);
   }
-  e += __shfl_xor(e, 1, 64);
-  e += __shfl_xor(e, 2, 64);
-  e += __shfl_xor(e, 4, 64);
-  if (sub == 0 && i < n && ent) ent[i] = e;
-  sh[threadIdx.x] = sub == 0 ? double(e) : 0.0;
+  sh[threadIdx.x] = acc;
   block_sum_f64(sh);
   if (threadIdx.x == 0) part[blockIdx.x] = sh[0];
 }
@@ -162,13 +182,17 @@ __global__ __launch_bounds__(256) void diag_sum_kernel(const double* __restrict_
 }
 
 inline size_t al256(size_t b) { return (b + 255) / 256 * 256; }
+// entropy launch: groups of 32 items, at most 1024 blocks (one fp64 partial each)
+inline int64_t entropy_blocks(int64_t n) {
+  const int64_t b = (n + 31) / 32;
+  return b < 1 ? 1 : b > 1024 ? 1024 : b;
+}
 inline int64_t map_bytes_of(int64_t nrows) { return (nrows + 255) / 256 * 256; }  // whole 32-bit words, aligned
 
 }  // namespace
 
 size_t diagnostics_ws_bytes(int64_t ntok, int heads, int64_t nrows) {
-  const int64_t nblk = (ntok * heads + 31) / 32;
-  return al256(size_t(heads) * size_t(map_bytes_of(nrows))) + al256(size_t(nblk > 0 ? nblk : 1) * 8);
+  return al256(size_t(heads) * size_t(map_bytes_of(nrows))) + al256(size_t(entropy_blocks(ntok * heads)) * 8);
 }
 
 hipError_t launch_diagnostics(hipStream_t s, const int32_t* idx, const float* w, int64_t ntok, int heads, int k,
@@ -205,13 +229,11 @@ hipError_t launch_diagnostics(hipStream_t s, const int32_t* idx, const float* w,
   hipLaunchKernelGGL(diag_hits_kernel, gh, dim3(256), size_t(nk + nk2) * 4, s, idx, ntok, heads, k, nk, nk2, hits_c,
                      hits_cp, maps, mb);
   const int64_t words = mb / 4;
-  int64_t cb = (words + 256 * 16 - 1) / (256 * 16);  // ~16 words per thread
-  if (cb < 1) cb = 1;
-  hipLaunchKernelGGL(diag_count_kernel, dim3(unsigned(cb), unsigned(1 + heads)), dim3(256), 0, s,
-                     reinterpret_cast<const uint32_t*>(maps), words, heads,
-                     reinterpret_cast<unsigned long long*>(used));
+  const int64_t cb = (words + 256 * kCountWords - 1) / (256 * kCountWords);
+  hipLaunchKernelGGL(diag_count_kernel, dim3(unsigned(cb)), dim3(256), 0, s, reinterpret_cast<const uint32_t*>(maps),
+                     words, heads, reinterpret_cast<unsigned long long*>(used));
   const int64_t n = ntok * heads;
-  const int64_t nblk = (n + 31) / 32;
+  const int64_t nblk = entropy_blocks(n);
   hipLaunchKernelGGL(diag_entropy_kernel, dim3(unsigned(nblk)), dim3(256), 0, s, w, n, k, entropy, part);
   if (entropy_sum) hipLaunchKernelGGL(diag_sum_kernel, dim3(1), dim3(256), 0, s, part, nblk, entropy_sum);
   return hipGetLastError();
