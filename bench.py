@@ -88,8 +88,8 @@ def alg_bytes(cfg, touched):
     # value row read and written, both fp32 moment rows read and written
     value_adam = touched * (2 * dv * e + 4 * dv * 4 + 4) + cfg.T * dv * e + L * 12
     # monitoring signals: idx and w read once, entropy written, the per-head
-    # slot byte maps cleared and counted (read twice: per head and OR)
-    diagnostics = L * 8 + cfg.T * cfg.heads * 4 + cfg.heads * cfg.slots * 3
+    # slot byte maps cleared and read once by the count pass
+    diagnostics = L * 8 + cfg.T * cfg.heads * 4 + cfg.heads * cfg.slots * 2
     return {"gather": gather, "value_grad": value_grad, "value_adam": value_adam, "diagnostics": diagnostics}
 
 
