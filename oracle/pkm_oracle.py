@@ -34,7 +34,8 @@ rounding is passed straight through in the backward.
 
 Beyond the lookup, ``sparse_adam_rows`` is the optimizer step on the touched
 value rows that [Blog] §6.3 describes (moments only for rows with gradient),
-and ``diagnostics`` the monitoring signals of [Blog] §9.3 and §11.2.
+``diagnostics`` the monitoring signals of [Blog] §9.3 and §11.2, and
+``quantize_rows_fp8`` / ``e4m3_*`` the fp8 value storage of [Blog] §16.3.
 
 Parity pins (all in ``tests/test_oracle_pins.py``): brute force over every
 full key, integer-valued exact ties, numpy cross-checks against dense
@@ -321,6 +322,68 @@ def sparse_adam_rows(V_rows: np.ndarray, m_rows: np.ndarray, v_rows: np.ndarray,
     v_hat = v1 / (1.0 - beta2 ** step)
     V1 = decode(V_rows, v_dtype) - lr * m_hat / (np.sqrt(v_hat) + eps)
     return round_to_storage(V1, v_dtype), m1, v1
+
+
+# ---------------------------------------------------------------------------
+# fp8 value storage ([Blog] §16.3: the value table compressed to a low-bit
+# format with little loss of retrieval quality)
+# ---------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Values of fp8 E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa
+    bits; exponent 0 is subnormal, exponent 15 with mantissa 7 is NaN, no
+    infinities), float64."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 code of each finite value (ties to the even code), saturated
+    at +-448.  Brute force over the 254 finite codes: the candidates are sorted by
+    value and the nearest found with a search; an exact tie takes the code with
+    a zero last mantissa bit."""
+    finite = np.array([c for c in range(256) if not np.isnan(e4m3_decode(np.array([c]))[0])], dtype=np.int64)
+    vals = e4m3_decode(finite)
+    pos = finite[(vals >= 0) & ~((vals == 0) & (finite == 0x80))]       # +0 .. 448
+    pv = e4m3_decode(pos)
+    order = np.argsort(pv)
+    pos, pv = pos[order], pv[order]
+    a = np.minimum(np.abs(np.asarray(x, dtype=np.float64)), E4M3_MAX)
+    i = np.clip(np.searchsorted(pv, a), 1, len(pv) - 1)
+    lo, hi = pv[i - 1], pv[i]
+    d_lo, d_hi = a - lo, hi - a
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((pos[i] & 1) == 0))
+    code = np.where(take_hi, pos[i], pos[i - 1])
+    code = np.where(a == 0, 0, code)
+    neg = np.signbit(np.asarray(x, dtype=np.float64)) & (code != 0)
+    return (code | np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+def quantize_rows_fp8(V: np.ndarray, v_dtype: str):
+    """Per-row fp8 storage of a value table: scale s_r = max_j |V[r, j]| / 448 and
+    codes c = E4M3(V[r, j] * (448 / max_j |V[r, j]|)); a zero row gets s = 0 and
+    zero codes.  The scale, its reciprocal factor and the product are rounded to
+    fp32, as the library computes them (they decide the integer codes).  Returns
+    (scales fp32 [n], codes uint8 [n, d])."""
+    Vf = decode(V, v_dtype).astype(np.float32)
+    mx = np.abs(Vf).max(axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        scale = np.where(mx > 0, mx / np.float32(E4M3_MAX), np.float32(0)).astype(np.float32)
+        inv = np.where(mx > 0, np.float32(E4M3_MAX) / mx, np.float32(0)).astype(np.float32)
+    q = (Vf * inv[:, None]).astype(np.float32)
+    return scale, e4m3_encode(q)
+
+
+def dequantize_rows_fp8(scale: np.ndarray, codes: np.ndarray) -> np.ndarray:
+    """V[r, j] = s_r * value(c[r, j]), float64."""
+    return np.asarray(scale, dtype=np.float64)[:, None] * e4m3_decode(codes)
 
 
 def diagnostics(rows: np.ndarray, w: np.ndarray, n_keys: int, n_keys2: int):

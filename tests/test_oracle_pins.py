@@ -506,3 +506,53 @@ def test_diagnostics_entropy_closed_forms():
     assert (ent[1] == 0.0).all()
     np.testing.assert_allclose(ent[2], scipy.stats.entropy(w[2, 0]), rtol=1e-13)
     assert used[0] == 3 * 2 * k and (used[1:] == 3 * k).all()
+
+
+# ---------------------------------------------------------------------------
+# fp8 value storage ([Blog] §16.3)
+# ---------------------------------------------------------------------------
+
+def test_e4m3_decode_matches_torch_float8_on_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = O.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(ours[ok], ref[ok])
+    assert O.e4m3_decode(np.array([0x7E]))[0] == 448.0 and O.e4m3_decode(np.array([0x01]))[0] == 2.0 ** -9
+
+
+def test_e4m3_encode_matches_torch_cast_including_ties():
+    rng = np.random.default_rng(9)
+    codes = np.array([c for c in range(256) if not np.isnan(O.e4m3_decode(np.array([c]))[0])], dtype=np.uint8)
+    vals = np.unique(O.e4m3_decode(codes))
+    mids = (vals[1:] + vals[:-1]) / 2                              # exact ties: the even code wins
+    xs = np.concatenate([vals, mids, rng.uniform(-448, 448, 20000), rng.uniform(-0.02, 0.02, 5000),
+                         np.array([0.0, -0.0, 2.0 ** -10, -(2.0 ** -10), 447.99])]).astype(np.float32)
+    ours = O.e4m3_encode(xs)
+    ref = torch.from_numpy(xs).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(O.e4m3_decode(ours), O.e4m3_decode(ref))
+    # beyond the range the encoder saturates (the row scale keeps quotients inside it)
+    assert O.e4m3_decode(O.e4m3_encode(np.array([1e6, -500.0])))[0] == 448.0
+    assert O.e4m3_decode(O.e4m3_encode(np.array([1e6, -500.0])))[1] == -448.0
+
+
+def test_quantize_rows_fp8_closed_forms_and_error_bound():
+    rng = np.random.default_rng(10)
+    V = rng.standard_normal((50, 64)).astype(np.float32) * np.exp(rng.uniform(-6, 3, (50, 1))).astype(np.float32)
+    V[3] = 0.0
+    V[4, :] = 0.0
+    V[4, 5] = -2.5                                                 # one non-zero element: it maps to -448
+    scale, codes = O.quantize_rows_fp8(V, O.F32)
+    assert scale[3] == 0 and (codes[3] == 0).all()
+    assert codes[4, 5] == 0xFE and (codes[4, np.arange(64) != 5] == 0).all()
+    mx = np.abs(V).max(1)
+    np.testing.assert_array_equal(scale, (mx / np.float32(448)).astype(np.float32))
+    # every row's largest element lands on +-448 (code 0x7E / 0xFE)
+    j = np.abs(V).argmax(1)
+    r = np.arange(50)[mx > 0]
+    assert np.all((codes[r, j[r]] & 0x7F) == 0x7E)
+    deq = O.dequantize_rows_fp8(scale, codes)
+    # half a unit in the last place of e4m3 (3 mantissa bits) or of its subnormal step, plus fp32 slack
+    bound = np.maximum(np.abs(V) * 2.0 ** -4, scale[:, None] * 2.0 ** -10) * (1 + 1e-6) + 1e-30
+    assert np.all(np.abs(deq - V) <= bound)
