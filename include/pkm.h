@@ -76,13 +76,24 @@ typedef enum {
 
 typedef enum { PKM_F32 = 0, PKM_BF16 = 1 } pkm_dtype;
 typedef enum { PKM_BN_NONE = 0, PKM_BN_BATCH = 1 } pkm_bn_mode;
+/* How the value table V is stored.  PKM_VALUES_FP8 ("Meta AI 可扩展内存层",
+ * section 16.3: the value matrix compressed to a low-bit format): row r takes
+ * d_value + 16 bytes, a 16-byte header whose first 4 bytes are the fp32 scale
+ * s_r (the other 12 bytes zero), then d_value E4M3 codes (1 sign bit, 4 exponent
+ * bits with bias 7, 3 mantissa bits, no infinities); the value is s_r * code.
+ * pkm_quantize_values writes such a table.  It is a forward (inference)
+ * format: pkm_forward and pkm_stage_gather read it; the entry points that need
+ * V in the backward return PKM_ERR_UNSUPPORTED (train a table in the storage
+ * dtype and quantize it). */
+typedef enum { PKM_VALUES_STORAGE = 0, PKM_VALUES_FP8 = 1 } pkm_value_format;
 
 /* Layer shape.  pkm_create checks (v = 8 elements for bf16, 4 for fp32 storage,
  * i.e. 16 bytes):
  *   d_in >= 1, d_in % v == 0;  heads >= 1;  d_query >= 2, even, (d_query/2) % v == 0;
  *   1 <= topk <= 32, topk <= n_keys, topk <= n_keys2;  1 <= n_keys, n_keys2 <= 2048;
  *   n_keys * n_keys2 < 2^31;  d_value >= 1, d_value % v == 0, d_value * elem <= 4096 bytes;
- *   temperature > 0;  bn_eps >= 0 (BN_BATCH).
+ *   temperature > 0;  bn_eps >= 0 (BN_BATCH);
+ *   value_format PKM_VALUES_FP8: d_value % 16 == 0 and d_value <= 4096.
  * Per call: T >= 0 (T = 0 is a no-op; the backward then zeroes its gradients)
  * and T * heads * topk <= 2^26 lookups. */
 typedef struct {
@@ -98,6 +109,7 @@ typedef struct {
   float bn_eps;          /* BatchNorm epsilon (1e-5) */
   float temperature;     /* tau: w = softmax(score / tau) (1.0) */
   int32_t accumulate_dv; /* pkm_backward: 1 -> dV[r] += g_r, 0 -> dV[r] = g_r (touched rows only) */
+  int32_t value_format;  /* pkm_value_format: PKM_VALUES_STORAGE (V in the storage dtype) or PKM_VALUES_FP8 */
 } pkm_config;
 
 /* State the forward saves for the backward; every buffer is caller-allocated device memory. */
@@ -256,6 +268,15 @@ pkm_status pkm_stage_value_adam(pkm_handle_t handle, void* stream, int64_t T, co
 pkm_status pkm_diagnostics(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx, const float* w,
                            int32_t* hits_c, int32_t* hits_cp, int64_t* used, float* entropy, double* entropy_sum,
                            void* ws, size_t ws_bytes);
+
+/* The fp8 value table of PKM_VALUES_FP8 from rows in the storage dtype: for
+ * each of the `rows` rows of V_src [rows, d_value], s_r = max_j |V_src[r, j]| / 448
+ * and code j = the E4M3 value nearest to V_src[r, j] * (448 / max_j |V_src[r, j]|)
+ * (ties to the even code; scale, factor and product rounded to fp32); a zero
+ * row gets s_r = 0 and zero codes.  V_fp8: rows * (d_value + 16) bytes, layout
+ * as described at pkm_value_format.  The handle must have value_format =
+ * PKM_VALUES_FP8.  rows >= 0. */
+pkm_status pkm_quantize_values(pkm_handle_t handle, void* stream, const void* V_src, int64_t rows, void* V_fp8);
 
 /* Step a8's grouping alone: the lookups of idx [T, h, k] stably sorted by row,
  * written into the workspace (for pkm_stage_value_grad_grouped), plus touched

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libpkm.so")
 PKM_OK, PKM_ERR_INVALID_ARG, PKM_ERR_UNSUPPORTED, PKM_ERR_WORKSPACE, PKM_ERR_HIP = range(5)
 PKM_F32, PKM_BF16 = 0, 1
 PKM_BN_NONE, PKM_BN_BATCH = 0, 1
+PKM_VALUES_STORAGE, PKM_VALUES_FP8 = 0, 1
 
 _STORAGE = {PKM_F32: torch.float32, PKM_BF16: torch.bfloat16}
 
@@ -32,7 +33,8 @@ class pkm_config(ctypes.Structure):
     _fields_ = [("d_in", ctypes.c_int32), ("heads", ctypes.c_int32), ("d_query", ctypes.c_int32),
                 ("n_keys", ctypes.c_int32), ("n_keys2", ctypes.c_int32), ("topk", ctypes.c_int32),
                 ("d_value", ctypes.c_int32), ("dtype", ctypes.c_int32), ("bn", ctypes.c_int32),
-                ("bn_eps", ctypes.c_float), ("temperature", ctypes.c_float), ("accumulate_dv", ctypes.c_int32)]
+                ("bn_eps", ctypes.c_float), ("temperature", ctypes.c_float), ("accumulate_dv", ctypes.c_int32),
+                ("value_format", ctypes.c_int32)]
 
 
 class pkm_saved(ctypes.Structure):
@@ -69,6 +71,7 @@ _SIGS = {
     "pkm_stage_value_adam_grouped": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_adam), _VP, _VP,
                                      _VP, _SZ],
     "pkm_diagnostics": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
+    "pkm_quantize_values": [_VP, _VP, _VP, _I64, _VP],
     "pkm_stage_row_groups": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _SZ],
     "pkm_stage_value_grad_grouped": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
     "pkm_stage_subkey_grad": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
@@ -140,6 +143,11 @@ class Handle:
     def storage(self) -> torch.dtype:
         return _STORAGE[self.cfg.dtype]
 
+    @property
+    def value_dtype(self) -> torch.dtype:
+        """dtype of the value table tensor: the storage dtype, or uint8 bytes for fp8 rows."""
+        return torch.uint8 if self.cfg.value_format == PKM_VALUES_FP8 else self.storage
+
     def __del__(self):
         if _lib is not None and self.ptr:
             _lib.pkm_destroy(self.ptr)
@@ -147,10 +155,14 @@ class Handle:
 
 
 def make_config(d_in, heads, d_query, n_keys, n_keys2, topk, d_value, dtype="f32", bn=True, bn_eps=1e-5,
-                temperature=1.0, accumulate_dv=True) -> pkm_config:
+                temperature=1.0, accumulate_dv=True, values="storage") -> pkm_config:
+    """``values``: "storage" (V in the storage dtype) or "fp8" (rows of a fp32 scale + E4M3 codes)."""
+    if values not in ("storage", "fp8"):
+        raise ValueError(f"values must be 'storage' or 'fp8', got {values!r}")
     return pkm_config(d_in, heads, d_query, n_keys, n_keys2, topk, d_value,
                       PKM_BF16 if dtype in ("bf16", PKM_BF16, torch.bfloat16) else PKM_F32,
-                      PKM_BN_BATCH if bn else PKM_BN_NONE, bn_eps, temperature, 1 if accumulate_dv else 0)
+                      PKM_BN_BATCH if bn else PKM_BN_NONE, bn_eps, temperature, 1 if accumulate_dv else 0,
+                      PKM_VALUES_FP8 if values == "fp8" else PKM_VALUES_STORAGE)
 
 
 def pkm_create(cfg: pkm_config) -> Handle:
@@ -181,8 +193,9 @@ def _nbytes(t):
 
 def pkm_forward(h, T, x, Wq, bn_gamma, bn_beta, C, Cp, V, y, saved: dict, ws):
     st = h.storage
-    for n, t in (("x", x), ("Wq", Wq), ("C", C), ("Cp", Cp), ("V", V), ("y", y)):
+    for n, t in (("x", x), ("Wq", Wq), ("C", C), ("Cp", Cp), ("y", y)):
         _dt(t, st, n)
+    _dt(V, h.value_dtype, "V")
     sv = _saved_struct(saved)
     _check(_invoke("pkm_forward", h, T, _ptr(x), _ptr(Wq), _ptr(bn_gamma), _ptr(bn_beta), _ptr(C),
                              _ptr(Cp), _ptr(V), _ptr(y), ctypes.byref(sv), _ptr(ws), _nbytes(ws)), "pkm_forward")
@@ -256,9 +269,20 @@ def pkm_stage_merge_softmax(h, T, sub_idx, sub_score, idx, w, score=None):
                                          _ptr(score)), "pkm_stage_merge_softmax")
 
 
+def pkm_quantize_values(h, V_src, V_fp8, rows=None):
+    """fp8 rows (fp32 scale + E4M3 codes, pkm.h) of the value table V_src [rows, d_value] into V_fp8 (uint8)."""
+    _dt(V_src, h.storage, "V_src")
+    _dt(V_fp8, torch.uint8, "V_fp8")
+    n = V_src.shape[0] if rows is None else rows
+    if V_fp8.numel() < n * (h.cfg.d_value + 16):
+        raise ValueError("V_fp8 holds fewer than rows * (d_value + 16) bytes")
+    _check(lib().pkm_quantize_values(h.ptr, _stream(), _ptr(V_src), n, _ptr(V_fp8)), "pkm_quantize_values")
+
+
 def pkm_stage_gather(h, T, idx, w, V, y):
     _dt(idx, torch.int32, "idx")
     _dt(w, torch.float32, "w")
+    _dt(V, h.value_dtype, "V")
     _check(_invoke("pkm_stage_gather", h, T, _ptr(idx), _ptr(w), _ptr(V), _ptr(y)), "pkm_stage_gather")
 
 

@@ -156,6 +156,13 @@ pkm_status check_handle(pkm_handle_t h) {
   return PKM_OK;
 }
 
+// Entry points that read V in the backward need it in the storage dtype.
+pkm_status need_storage_values(pkm_handle_t h) {
+  if (h->cfg.value_format == PKM_VALUES_FP8)
+    return fail(PKM_ERR_UNSUPPORTED, "fp8 values are a forward format; the backward needs V in the storage dtype");
+  return PKM_OK;
+}
+
 pkm_status check_T(const pkm_handle_s* h, int64_t T) {
   if (T < 0) return fail(PKM_ERR_INVALID_ARG, "T = %lld is negative", (long long)T);
   const int64_t N = T * h->cfg.heads * h->cfg.topk;
@@ -223,7 +230,8 @@ pkm_status run_merge(const pkm_handle_s* h, hipStream_t s, int64_t T, const int3
 pkm_status run_gather(const pkm_handle_s* h, hipStream_t s, int64_t T, const int32_t* idx, const float* w,
                       const void* V, void* y) {
   const pkm_config& c = h->cfg;
-  PKM_HIP(launch_gather(s, c.dtype, idx, w, V, y, T, c.heads * c.topk, c.d_value), "value gather-sum");
+  PKM_HIP(launch_gather(s, c.dtype, idx, w, V, y, T, c.heads * c.topk, c.d_value, c.value_format == PKM_VALUES_FP8),
+          "value gather-sum");
   return PKM_OK;
 }
 
@@ -470,6 +478,10 @@ pkm_status pkm_create(const pkm_config* cfg, pkm_handle_t* out) {
   if (c.d_value % vec) return fail(PKM_ERR_UNSUPPORTED, "d_value must be a multiple of %d for this dtype", vec);
   if (c.d_value / vec > 256)
     return fail(PKM_ERR_UNSUPPORTED, "d_value rows above 4096 bytes are not supported");
+  if (c.value_format != PKM_VALUES_STORAGE && c.value_format != PKM_VALUES_FP8)
+    return fail(PKM_ERR_INVALID_ARG, "value_format %d unknown", c.value_format);
+  if (c.value_format == PKM_VALUES_FP8 && c.d_value % 16)
+    return fail(PKM_ERR_UNSUPPORTED, "fp8 values need d_value to be a multiple of 16");
   const int maxk = c.n_keys > c.n_keys2 ? c.n_keys : c.n_keys2;
   if (!score_topk_supported(c.dtype, c.d_query / 2, maxk))
     return fail(PKM_ERR_UNSUPPORTED, "d_query/2 = %d with %d sub-keys does not fit the scoring tile", c.d_query / 2,
@@ -580,6 +592,7 @@ static pkm_status backward_impl(pkm_handle_t handle, void* stream, int64_t T, co
                                 int64_t* n_touched, float* dC, float* dCp, float* dWq, float* dgamma, float* dbeta,
                                 void* dx, void* ws, size_t ws_bytes) {
   PKM_TRY(check_handle(handle));
+  PKM_TRY(need_storage_values(handle));
   PKM_TRY(check_T(handle, T));
   const bool bn = handle->cfg.bn == PKM_BN_BATCH;
   PKM_TRY(need(dY, "dY"));
@@ -713,6 +726,7 @@ pkm_status pkm_stage_value_grad(pkm_handle_t handle, void* stream, int64_t T, co
                                 const void* dY, const void* V, float* dV, int32_t* touched, int64_t* n_touched,
                                 float* dw, void* ws, size_t ws_bytes) {
   PKM_TRY(check_handle(handle));
+  PKM_TRY(need_storage_values(handle));
   PKM_TRY(check_T(handle, T));
   PKM_TRY(need(idx, "idx"));
   PKM_TRY(need(w, "w"));
@@ -732,6 +746,7 @@ pkm_status pkm_stage_value_adam(pkm_handle_t handle, void* stream, int64_t T, co
                                 const void* dY, void* V, float* adam_m, float* adam_v, const pkm_adam* adam,
                                 int32_t* touched, int64_t* n_touched, float* dw, void* ws, size_t ws_bytes) {
   PKM_TRY(check_handle(handle));
+  PKM_TRY(need_storage_values(handle));
   PKM_TRY(check_T(handle, T));
   PKM_TRY(need(idx, "idx"));
   PKM_TRY(need(w, "w"));
@@ -772,6 +787,22 @@ pkm_status pkm_diagnostics(pkm_handle_t handle, void* stream, int64_t T, const i
   return PKM_OK;
 }
 
+pkm_status pkm_quantize_values(pkm_handle_t handle, void* stream, const void* V_src, int64_t rows, void* V_fp8) {
+  PKM_TRY(check_handle(handle));
+  const pkm_config& c = handle->cfg;
+  if (c.value_format != PKM_VALUES_FP8)
+    return fail(PKM_ERR_INVALID_ARG, "pkm_quantize_values needs a handle with value_format = PKM_VALUES_FP8");
+  if (rows < 0) return fail(PKM_ERR_INVALID_ARG, "rows = %lld < 0", (long long)rows);
+  if (rows > int64_t(c.n_keys) * c.n_keys2)
+    return fail(PKM_ERR_INVALID_ARG, "rows = %lld exceeds the table (%lld rows)", (long long)rows,
+                (long long)(int64_t(c.n_keys) * c.n_keys2));
+  PKM_TRY(need(V_src, "V_src"));
+  PKM_TRY(need(V_fp8, "V_fp8"));
+  if (rows == 0) return PKM_OK;
+  PKM_HIP(launch_quantize_fp8(as_stream(stream), c.dtype, V_src, rows, c.d_value, V_fp8), "fp8 value quantization");
+  return PKM_OK;
+}
+
 pkm_status pkm_stage_row_groups(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx, int32_t* touched,
                                 int64_t* n_touched, void* ws, size_t ws_bytes) {
   PKM_TRY(check_handle(handle));
@@ -789,6 +820,7 @@ pkm_status pkm_stage_value_grad_grouped(pkm_handle_t handle, void* stream, int64
                                         const void* V, float* dV, float* dw, const int64_t* n_touched, void* ws,
                                         size_t ws_bytes) {
   PKM_TRY(check_handle(handle));
+  PKM_TRY(need_storage_values(handle));
   PKM_TRY(check_T(handle, T));
   PKM_TRY(need(w, "w"));
   PKM_TRY(need(dY, "dY"));
@@ -805,6 +837,7 @@ pkm_status pkm_stage_value_adam_grouped(pkm_handle_t handle, void* stream, int64
                                         void* V, float* adam_m, float* adam_v, const pkm_adam* adam, float* dw,
                                         const int64_t* n_touched, void* ws, size_t ws_bytes) {
   PKM_TRY(check_handle(handle));
+  PKM_TRY(need_storage_values(handle));
   PKM_TRY(check_T(handle, T));
   PKM_TRY(need(w, "w"));
   PKM_TRY(need(dY, "dY"));

@@ -11,8 +11,11 @@ constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 
 // a6: y[t] = sum_r w[t, r] V[idx[t, r]] over R = h*k rows per token.
+// fp8_values: rows of [16-byte header (fp32 scale), d_value E4M3 codes].
 hipError_t launch_gather(hipStream_t s, int dtype, const int32_t* idx, const float* w, const void* V,
-                         void* y, int64_t ntok, int R, int d_value);
+                         void* y, int64_t ntok, int R, int d_value, bool fp8_values);
+// fp8 value rows from rows in the storage dtype (d_value % 16 == 0).
+hipError_t launch_quantize_fp8(hipStream_t s, int dtype, const void* src, int64_t rows, int d_value, void* dst);
 
 // a3 + a4: per (token, head, half) scores against the half's sub-keys and top-k.
 // packed: score_topk_packed_bytes of scratch for the repacked sub-keys.

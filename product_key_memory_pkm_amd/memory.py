@@ -15,13 +15,14 @@ class ProductKeyMemory:
 
     Parameters follow the C ABI (``pkm_config``): input width ``d_in``, ``heads``,
     per-head query width ``d_query``, codebook sizes ``n_keys`` / ``n_keys2``,
-    ``topk``, value width ``d_value``, storage dtype ``"f32"`` or ``"bf16"``.
+    ``topk``, value width ``d_value``, storage dtype ``"f32"`` or ``"bf16"``, value table format ``values``
+    (``"storage"`` or ``"fp8"``: rows of a fp32 scale and E4M3 codes, forward only).
     """
 
     def __init__(self, d_in, heads, d_query, n_keys, n_keys2, topk, d_value, dtype="bf16", bn=True, bn_eps=1e-5,
-                 temperature=1.0, accumulate_dv=True, device="cuda"):
+                 temperature=1.0, accumulate_dv=True, device="cuda", values="storage"):
         self.cfg = L.make_config(d_in, heads, d_query, n_keys, n_keys2, topk, d_value, dtype, bn, bn_eps,
-                                 temperature, accumulate_dv)
+                                 temperature, accumulate_dv, values)
         self.handle = L.pkm_create(self.cfg)
         self.device = torch.device(device)
         self._ws = None
@@ -48,6 +49,12 @@ class ProductKeyMemory:
             sv["bn_mean"] = torch.empty(F, dtype=torch.float32, device=dev)
             sv["bn_rstd"] = torch.empty(F, dtype=torch.float32, device=dev)
         return sv
+
+    def quantize_values(self, V):
+        """fp8 value table (uint8 bytes, rows of a fp32 scale header and E4M3 codes) of V [rows, d_value]."""
+        out = torch.empty(V.shape[0] * (self.cfg.d_value + 16), dtype=torch.uint8, device=self.device)
+        L.pkm_quantize_values(self.handle, V, out)
+        return out
 
     def forward(self, x, Wq, gamma, beta, C, Cp, V, saved=None, y=None):
         T = x.shape[0]

@@ -29,11 +29,21 @@ def to_dev(a: np.ndarray, dtype: str | None = None) -> torch.Tensor:
     return t.cuda()
 
 
-def layer_for(cfg, accumulate_dv=True):
+def layer_for(cfg, accumulate_dv=True, values="storage"):
     from product_key_memory_pkm_amd import ProductKeyMemory
     return ProductKeyMemory(cfg.d, cfg.heads, cfg.dq, cfg.n_keys, cfg.n_keys2, cfg.topk, cfg.d_value,
                             dtype=cfg.dtype, bn=cfg.bn, bn_eps=cfg.bn_eps, temperature=cfg.temperature,
-                            accumulate_dv=accumulate_dv)
+                            accumulate_dv=accumulate_dv, values=values)
+
+
+def fp8_table(scale: np.ndarray, codes: np.ndarray) -> np.ndarray:
+    """Bytes of an fp8 value table (pkm.h, PKM_VALUES_FP8): per row a 16-byte header holding the fp32 scale
+    (other bytes zero), then the row's E4M3 codes."""
+    n, d = codes.shape
+    out = np.zeros((n, d + 16), dtype=np.uint8)
+    out[:, :4] = np.asarray(scale, dtype=np.float32).reshape(n, 1).view(np.uint8)
+    out[:, 16:] = codes
+    return out.reshape(-1)
 
 
 def upload(inp: dict) -> dict:

@@ -57,6 +57,7 @@ BAD_CONFIGS = [
     (dict(d_in=6), 2), (dict(d_query=6), 2), (dict(d_value=6), 2),   # fp32 needs multiples of 4
     (dict(dtype="bf16", d_in=12), 2), (dict(dtype="bf16", d_query=24), 2),
     (dict(d_value=8192), 2),
+    (dict(values="fp8", d_value=40), 2),            # fp8 rows need multiples of 16
 ]
 
 
@@ -216,6 +217,33 @@ def test_diagnostics_argument_errors():
     assert d(h.ptr, None, 4, ok[1], ok[2], ok[3], ok[4], ctypes.c_void_p(FAKE + 4), None, None, ok[6],
              1 << 30) == L.PKM_ERR_INVALID_ARG                                              # misaligned used
     assert d(h.ptr, None, -1, ok[1], ok[2], ok[3], ok[4], ok[5], None, None, ok[6], 1 << 30) == L.PKM_ERR_INVALID_ARG
+
+
+def test_fp8_values_argument_errors():
+    L = _lib()
+    lib = L.lib()
+    cfg = _cfg(L, values="fp8", d_value=64)
+    bad = _cfg(L, values="fp8", d_value=64)
+    bad.value_format = 2
+    assert lib.pkm_create(ctypes.byref(bad), ctypes.byref(ctypes.c_void_p())) == L.PKM_ERR_INVALID_ARG
+    h = L.pkm_create(cfg)
+    ok = [_fake(i) for i in range(30)]
+    q = lib.pkm_quantize_values
+    assert q(h.ptr, None, ok[1], -1, ok[2]) == L.PKM_ERR_INVALID_ARG
+    assert q(h.ptr, None, ok[1], 32 * 32 + 1, ok[2]) == L.PKM_ERR_INVALID_ARG      # more rows than the table
+    assert q(h.ptr, None, None, 4, ok[2]) == L.PKM_ERR_INVALID_ARG
+    assert q(h.ptr, None, ok[1], 0, ok[2]) == L.PKM_OK                              # nothing to do
+    plain = L.pkm_create(_cfg(L))
+    assert q(plain.ptr, None, ok[1], 4, ok[2]) == L.PKM_ERR_INVALID_ARG           # needs an fp8 handle
+    # every entry point that reads V in the backward refuses fp8 values
+    sv = L.pkm_saved(_fake(9), _fake(10), _fake(11), _fake(12), _fake(13), _fake(14))
+    st = lib.pkm_backward(h.ptr, None, 10, ok[1], ok[2], ok[3], ok[4], ok[5], ok[6], ok[7], ctypes.byref(sv), ok[8],
+                          ok[9], ok[10], ok[11], ok[12], ok[13], ok[14], ok[15], None, ok[16], 1 << 40)
+    assert st == L.PKM_ERR_UNSUPPORTED and "fp8" in lib.pkm_last_error().decode()
+    assert lib.pkm_stage_value_grad(h.ptr, None, 4, ok[1], ok[2], ok[3], ok[4], ok[5], ok[6], ok[7], ok[8], ok[9],
+                                    1 << 40) == L.PKM_ERR_UNSUPPORTED
+    assert lib.pkm_stage_value_grad_grouped(h.ptr, None, 4, ok[1], ok[2], ok[3], ok[4], ok[5], ok[6], ok[7],
+                                            1 << 40) == L.PKM_ERR_UNSUPPORTED
 
 
 def test_binding_rejects_host_tensors():

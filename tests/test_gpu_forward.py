@@ -376,3 +376,103 @@ def test_diagnostics_stage(T, h, k, nk, nk2, zipf):
     assert np.all(np.abs(got - r_ent) <= 1e-5 * np.abs(r_ent) + 1e-6)
     total = float(ent_sum.cpu().item())
     assert abs(total - r_ent.sum()) <= 1e-5 * abs(r_ent.sum()) + 1e-6
+
+
+# ---------------------------------------------------------------------------
+# fp8 value storage ([Blog] §16.3): quantization and the fp8 gather
+# ---------------------------------------------------------------------------
+from tests.gpu_util import fp8_table  # noqa: E402
+
+QUANT_CASES = [
+    # rows, d_value, dtype
+    (300, 64, "f32"),
+    (257, 1600, "bf16"),
+    (40, 16, "bf16"),       # one 16-code vector per row
+    (33, 2048, "bf16"),     # 128 vectors per row: 2 per lane
+    (70, 1024, "f32"),
+]
+
+
+def _quant_input(rows, dv, dtype, seed):
+    V = pi.random_array(seed, 1, (rows, dv), dtype="f32").astype(np.float32)
+    V *= np.exp(pi.random_array(seed, 2, (rows, 1), dtype="f32", std=3.0)).astype(np.float32)  # wide row scales
+    V[0] = 0.0                                            # zero row
+    V[1] = 0.0
+    V[1, dv // 2] = -3.5                                  # one non-zero element
+    if dv >= 16:                                          # exact ties: row max 448 (factor 1) and midpoints
+        V[2] = 0.0
+        V[2, 0] = 448.0
+        V[2, 1:8] = [1.0625, 1.1875, -2.125, 0.0029296875, 17.0, 208.0, -1.3125]
+    V[3] *= np.float32(1e-4)                              # tiny values: subnormal codes
+    if dtype == "bf16":
+        return torch.from_numpy(V).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return V
+
+
+@pytest.mark.parametrize("rows,dv,dtype", QUANT_CASES)
+def test_quantize_values_bit_exact(rows, dv, dtype):
+    note(f"quantize rows={rows} dv={dv} {dtype}")
+    V = _quant_input(rows, dv, dtype, 21)
+    cfg = _cfg(d_value=dv, dtype=dtype, n_keys=32, n_keys2=32, d=16, dq=32)
+    layer = layer_for(cfg, values="fp8")
+    from product_key_memory_pkm_amd import pkm_quantize_values
+    out = torch.full((rows * (dv + 16),), 0xAB, dtype=torch.uint8, device="cuda")
+    pkm_quantize_values(layer.handle, to_dev(V), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(rows, dv + 16)
+    scale, codes = O.quantize_rows_fp8(V, dtype)
+    np.testing.assert_array_equal(got[:, :4].copy().view(np.float32).reshape(-1), scale)
+    assert (got[:, 4:16] == 0).all()
+    np.testing.assert_array_equal(got[:, 16:], codes)
+
+
+FP8_GATHER_CASES = [
+    # T, heads, k, rows, d_value, dtype
+    (64, 4, 32, 5000, 1600, "bf16"),
+    (37, 3, 5, 100, 32, "f32"),
+    (33, 1, 3, 50, 2048, "bf16"),      # 4 vectors per lane
+    (70, 4, 32, 4096, 768, "f32"),     # 3 vectors per lane
+]
+
+
+@pytest.mark.parametrize("T,h,k,nrows,dv,dtype", FP8_GATHER_CASES)
+def test_gather_fp8_values(T, h, k, nrows, dv, dtype):
+    note(f"gather fp8 T={T} h={h} k={k} rows={nrows} dv={dv} {dtype}")
+    rows, w = pi.random_selection(T + nrows + 1, T, h, k, nrows)
+    V = pi.random_array(7, 3, (nrows, dv), dtype="f32", std=dv ** -0.5)
+    scale, codes = O.quantize_rows_fp8(V, "f32")       # the table comes from the oracle
+    nk = int(np.ceil(np.sqrt(nrows)))
+    cfg = _cfg(heads=h, topk=k, n_keys=max(nk, k), n_keys2=max(nk, k), d_value=dv, dtype=dtype,
+               d=16 if dtype == "bf16" else 8, dq=32)
+    layer = layer_for(cfg, values="fp8")
+    from product_key_memory_pkm_amd import pkm_stage_gather
+    y = torch.empty((T, dv), dtype=layer.storage, device="cuda")
+    pkm_stage_gather(layer.handle, T, to_dev(rows), to_dev(w), torch.from_numpy(fp8_table(scale, codes)).cuda(), y)
+    torch.cuda.synchronize()
+    ref = O.gather_sum(rows, w.astype(np.float64), O.dequantize_rows_fp8(scale, codes), O.F64)
+    err = P.row_rel_err(P.to_f64(y), ref)
+    assert err.max() <= (1e-5 if dtype == "f32" else 8e-3), err.max()
+
+
+def test_forward_with_fp8_values_end_to_end():
+    """A bf16 layer whose value table is stored as fp8 rows: the selection is the storage-value layer's, y the
+    weighted sum of the dequantized rows."""
+    cfg = FWD_CASES["bf16_mid"]
+    note(f"forward fp8 values: {cfg}")
+    inp = pi.make_inputs(cfg)
+    scale, codes = O.quantize_rows_fp8(inp["V"], cfg.dtype)
+    layer = layer_for(cfg, values="fp8")
+    dev = upload(inp)
+    table = torch.from_numpy(fp8_table(scale, codes)).cuda()
+    y, saved = layer.forward(dev["x"], dev["Wq"], dev["gamma"], dev["beta"], dev["C"], dev["Cp"], table)
+    torch.cuda.synchronize()
+    ref = O.forward(cfg, inp)
+    idx = saved["idx"].cpu().numpy()
+    exact = (np.sort(idx, -1) == np.sort(ref["rows"], -1)).all(-1).all(-1)
+    assert exact.mean() > 0.95
+    y_ref = O.gather_sum(ref["rows"], ref["w"], O.dequantize_rows_fp8(scale, codes), O.F64)
+    err = P.row_rel_err(P.to_f64(y)[exact], y_ref[exact])
+    assert err.max() <= 8e-3, err.max()
+    # the fp8 table reproduces the storage-value output to within its rounding (E4M3: 2^-4 relative per element)
+    y_bf16 = O.gather_sum(ref["rows"], ref["w"], inp["V"], cfg.dtype)
+    assert P.row_rel_err(y_ref, y_bf16).max() <= 0.1
