@@ -90,7 +90,10 @@ def alg_bytes(cfg, touched):
     # monitoring signals: idx and w read once, entropy written, the per-head
     # slot byte maps cleared and read once by the count pass
     diagnostics = L * 8 + cfg.T * cfg.heads * 4 + cfg.heads * cfg.slots * 2
-    return {"gather": gather, "value_grad": value_grad, "value_adam": value_adam, "diagnostics": diagnostics}
+    # the gather over fp8 value rows (16-byte header + one byte per element)
+    gather_fp8 = L * (dv + 16 + 8) + cfg.T * dv * e
+    return {"gather": gather, "value_grad": value_grad, "value_adam": value_adam, "diagnostics": diagnostics,
+            "gather_fp8": gather_fp8}
 
 
 def main():
@@ -103,8 +106,8 @@ def main():
     import torch
 
     import pkm_inputs as pi
-    from product_key_memory_pkm_amd import (ProductKeyMemory, pkm_stage_gather, pkm_stage_row_groups,
-                                            pkm_diagnostics, pkm_stage_score_topk, pkm_stage_value_adam_grouped,
+    from product_key_memory_pkm_amd import (ProductKeyMemory, pkm_diagnostics, pkm_quantize_values, pkm_stage_gather,
+                                            pkm_stage_row_groups, pkm_stage_score_topk, pkm_stage_value_adam_grouped,
                                             pkm_stage_value_grad_grouped)
 
     if args.copy_calibration:
@@ -246,6 +249,28 @@ def main():
             "mean_softmax_entropy": float(ent_sum.item()) / (T * cfg.heads),
             "max_subkey_hits": int(max(hits_c.max().item(), hits_cp.max().item())),
             "mean_subkey_hits": T * cfg.topk / cfg.n_keys}
+    # the forward with the value table stored as fp8 rows (a forward format)
+    m8 = ProductKeyMemory(cfg.d, cfg.heads, cfg.dq, cfg.n_keys, cfg.n_keys2, cfg.topk, cfg.d_value, dtype=cfg.dtype,
+                          bn=cfg.bn, bn_eps=cfg.bn_eps, temperature=cfg.temperature, values="fp8")
+    V8 = torch.empty(cfg.slots * (cfg.d_value + 16), dtype=torch.uint8, device="cuda")
+    quant_ms = timed(lambda: pkm_quantize_values(m8.handle, V, V8), 3)
+    saved8 = m8.alloc_saved(T)
+    y8 = torch.empty_like(y)
+    for _ in range(2):
+        m8.forward(x, Wq, gamma, beta, C, Cp, V8, saved=saved8, y=y8)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(nf):
+        m8.forward(x, Wq, gamma, beta, C, Cp, V8, saved=saved8, y=y8)
+    end.record()
+    torch.cuda.synchronize()
+    ms_fwd8 = start.elapsed_time(end) / nf
+    g8_ms = timed(lambda: pkm_stage_gather(m8.handle, T, saved8["idx"], saved8["w"], V8, y8), nf)
+    y_rel = float(((y8.float() - y.float()).norm() / y.float().norm()).item())
+    fp8 = {"fwd_tokens_per_s": T / (ms_fwd8 * 1e-3), "fwd_ms": ms_fwd8, "quantize_ms": quant_ms,
+           "table_bytes": V8.numel(), "y_rel_diff_vs_storage_values": y_rel}
+    del V8, y8, saved8, m8
+    torch.cuda.empty_cache()
     # the per-half scoring + top-k kernel alone (its MFMA roofline)
     sub_idx = torch.empty((T, cfg.heads, 2, cfg.topk), dtype=torch.int32, device="cuda")
     sub_score = torch.empty((T, cfg.heads, 2, cfg.topk), dtype=torch.float32, device="cuda")
@@ -264,6 +289,8 @@ def main():
                           "ms": va_ms, "alg": ab["value_adam"]}
     kern["diagnostics"] = {"kernel": "diagnostics (hit counts, slots in use, softmax entropy)", "ms": dg_ms,
                            "alg": ab["diagnostics"]}
+    kern["gather_fp8"] = {"kernel": "gather_sum over fp8 value rows (a6, value_format fp8)", "ms": g8_ms,
+                          "alg": ab["gather_fp8"]}
     for k_ in kern.values():
         k_["achieved"] = k_["alg"] / (k_["ms"] * 1e-3) / 1e9
 
@@ -301,6 +328,7 @@ def main():
                                            "alg_flops_per_launch": score_flops, "avg_launch_ms": score_ms}),
         "touched_rows": n_touched,
         "diagnostics": diag,
+        "fp8_values": fp8,
         "memory_usage": n_touched / cfg.slots,
         "input_generation_s": gen_s,
     }
