@@ -35,7 +35,10 @@ rounding is passed straight through in the backward.
 Beyond the lookup, ``sparse_adam_rows`` is the optimizer step on the touched
 value rows that [Blog] §6.3 describes (moments only for rows with gradient),
 ``diagnostics`` the monitoring signals of [Blog] §9.3 and §11.2, and
-``quantize_rows_fp8`` / ``e4m3_*`` the fp8 value storage of [Blog] §16.3.
+``quantize_rows_fp8`` / ``e4m3_*`` the fp8 value storage of [Blog] §16.3,
+``subkey_scores_idw`` and ``fwpkm_chunk`` the fast-weight memorization of the
+FwPKM page (fourth source page: "Fast-weight Product Key Memory" summary,
+sections 2.1-2.2).
 
 Parity pins (all in ``tests/test_oracle_pins.py``): brute force over every
 full key, integer-valued exact ties, numpy cross-checks against dense
@@ -121,6 +124,19 @@ def subkey_scores(q1: np.ndarray, q2: np.ndarray, C: np.ndarray, Cp: np.ndarray)
     return s1, s2
 
 
+IDW_FLOOR = 1e-12  # squared distances below this count as this (a query on a key)
+
+
+def subkey_scores_idw(q1: np.ndarray, q2: np.ndarray, C: np.ndarray, Cp: np.ndarray):
+    """s1[t,h,i] = -log ||q1[t,h] - C[h,i]||, likewise s2 against C' (FwPKM page, section 2.2: the
+    negative log of the Euclidean distance replaces the dot product).  Squared distances are floored
+    at IDW_FLOOR; computed from the differences, float64."""
+    def idw(qh, K):
+        d2 = ((qh[:, :, None, :] - K[None, :, :, :]) ** 2).sum(-1)
+        return -0.5 * np.log(np.maximum(d2, IDW_FLOOR))
+    return idw(q1, C), idw(q2, Cp)
+
+
 def topk_sorted(s: np.ndarray, k: int):
     """Indices and values of the k largest entries along the last axis.
 
@@ -194,15 +210,17 @@ def query(cfg, inp: dict):
     return {"q_pre": q_pre, "mean": mean, "var": var, "xhat": xhat, "q": q}
 
 
-def lookup(cfg, q: np.ndarray, C: np.ndarray, Cp: np.ndarray, keep_tables: bool = False):
+def lookup(cfg, q: np.ndarray, C: np.ndarray, Cp: np.ndarray, keep_tables: bool = False, score: str = "dot"):
     """Product-key selection and weights for the tokens whose queries are ``q`` [n, h*dq].
 
     Returns rows/scores/w [n, h, k] (rows ordered by score desc, row asc), the
     per-half top-k lists and, for the gap rule, the per-half (k+1)-th values.
+    ``score``: "dot" (sub-key dot products) or "idw" (negative log distances,
+    subkey_scores_idw); either way a full key scores the sum of its halves.
     """
     k = cfg.topk
     q1, q2 = split_heads(q, cfg.heads, cfg.dq)
-    s1, s2 = subkey_scores(q1, q2, C, Cp)
+    s1, s2 = (subkey_scores_idw if score == "idw" else subkey_scores)(q1, q2, C, Cp)
     k1 = min(k + 1, s1.shape[-1])
     k2 = min(k + 1, s2.shape[-1])
     i1, v1 = topk_sorted(s1, k1)
@@ -224,10 +242,10 @@ def lookup(cfg, q: np.ndarray, C: np.ndarray, Cp: np.ndarray, keep_tables: bool 
     return out
 
 
-def forward(cfg, inp: dict, tokens=None, keep_tables: bool = False, chunk: int = 1024):
+def forward(cfg, inp: dict, tokens=None, keep_tables: bool = False, chunk: int = 1024, score: str = "dot"):
     """The memory output m(x) (no residual) for ``tokens`` (default all).
 
-    BatchNorm statistics always use all T tokens of the call.
+    BatchNorm statistics always use all T tokens of the call.  ``score`` as in lookup.
     """
     qs = query(cfg, inp)
     C = decode(inp["C"], cfg.dtype)
@@ -235,7 +253,7 @@ def forward(cfg, inp: dict, tokens=None, keep_tables: bool = False, chunk: int =
     tok = np.arange(cfg.T) if tokens is None else np.asarray(tokens)
     parts = []
     for lo in range(0, len(tok), chunk):
-        parts.append(lookup(cfg, qs["q"][tok[lo:lo + chunk]], C, Cp, keep_tables))
+        parts.append(lookup(cfg, qs["q"][tok[lo:lo + chunk]], C, Cp, keep_tables, score))
     sel = {key: (None if parts[0][key] is None else np.concatenate([p[key] for p in parts]))
            for key in parts[0]}
     y = gather_sum(sel["rows"], sel["w"], inp["V"], cfg.dtype)
@@ -384,6 +402,28 @@ def quantize_rows_fp8(V: np.ndarray, v_dtype: str):
 def dequantize_rows_fp8(scale: np.ndarray, codes: np.ndarray) -> np.ndarray:
     """V[r, j] = s_r * value(c[r, j]), float64."""
     return np.asarray(scale, dtype=np.float64)[:, None] * e4m3_decode(codes)
+
+
+def fwpkm_chunk(cfg, q: np.ndarray, C: np.ndarray, Cp: np.ndarray, V: np.ndarray, target: np.ndarray, lr: float):
+    """One chunk of FwPKM memorization (FwPKM page, sections 2.1-2.2: the value table is a fast weight,
+    written during inference by gradient descent on a local reconstruction loss toward lookahead
+    targets v_{t+1}; sparse retrieval with IDW scores).
+
+    Readings: the call's queries ``q`` [T, h*dq] (storage values) and targets [T, d_v] (the caller's
+    v_{t+1}) are given; lookup with IDW scores; y = the weighted sum of the rows read before the write,
+    stored in the storage dtype; loss 1/2 sum_t ||y_t - target_t||^2 with the residual e = y - target
+    also in the storage dtype (as an upstream gradient is); only the value rows are written:
+    V[r] <- V[r] - lr * sum over the lookups of r of w * e_t, rounded to storage.  Returns
+    (y as stored, V after the write, the lookup dict), float64.
+    """
+    sel = lookup(cfg, decode(q, cfg.dtype), decode(C, cfg.dtype), decode(Cp, cfg.dtype), score="idw")
+    y = round_to_storage(gather_sum(sel["rows"], sel["w"], V, cfg.dtype), cfg.dtype)
+    e = round_to_storage(y - decode(target, cfg.dtype), cfg.dtype)
+    uniq = np.unique(sel["rows"])
+    g = value_grad_rows(sel["rows"], sel["w"], e, F64, uniq)
+    Vn = decode(V, cfg.dtype).copy()
+    Vn[uniq] = round_to_storage(Vn[uniq] - lr * g, cfg.dtype)
+    return y, Vn, sel
 
 
 def diagnostics(rows: np.ndarray, w: np.ndarray, n_keys: int, n_keys2: int):

@@ -556,3 +556,71 @@ def test_quantize_rows_fp8_closed_forms_and_error_bound():
     # half a unit in the last place of e4m3 (3 mantissa bits) or of its subnormal step, plus fp32 slack
     bound = np.maximum(np.abs(V) * 2.0 ** -4, scale[:, None] * 2.0 ** -10) * (1 + 1e-6) + 1e-30
     assert np.all(np.abs(deq - V) <= bound)
+
+
+# ---------------------------------------------------------------------------
+# FwPKM: IDW scores and the per-chunk memorization write (FwPKM page §2.1-2.2)
+# ---------------------------------------------------------------------------
+
+class _Cfg:
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
+
+
+def test_idw_scores_closed_forms():
+    q1 = np.zeros((1, 1, 2))
+    C = np.array([[[3.0, 4.0], [0.0, 0.0], [1.0, 0.0]]])
+    s1, _ = O.subkey_scores_idw(q1, q1, C, C)
+    np.testing.assert_allclose(s1[0, 0], [-math.log(5.0), -0.5 * math.log(O.IDW_FLOOR), 0.0], rtol=1e-15)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_idw_product_key_selection_is_exact_topk(seed):
+    # the sum of the halves' -log distances is separable, so the product-key search is exact
+    rng = np.random.default_rng(40 + seed)
+    h, dq, nk, nk2, k, T = 2, 6, 7, 5, 4, 9
+    cfg = _Cfg(heads=h, dq=dq, topk=k, n_keys=nk, n_keys2=nk2, temperature=1.0)
+    q = rng.standard_normal((T, h * dq))
+    C = rng.standard_normal((h, nk, dq // 2))
+    Cp = rng.standard_normal((h, nk2, dq // 2))
+    sel = O.lookup(cfg, q, C, Cp, score="idw")
+    for t in range(T):
+        for hh in range(h):
+            qa, qb = q[t, hh * dq: hh * dq + dq // 2], q[t, hh * dq + dq // 2: (hh + 1) * dq]
+            full = []
+            for i in range(nk):
+                for j in range(nk2):
+                    sc = -math.log(np.linalg.norm(qa - C[hh, i])) - math.log(np.linalg.norm(qb - Cp[hh, j]))
+                    full.append((-sc, i * nk2 + j))
+            full.sort()
+            assert [r for _, r in full[:k]] == list(sel["rows"][t, hh])
+            np.testing.assert_allclose(sel["scores"][t, hh], [-v for v, _ in full[:k]], rtol=1e-12)
+
+
+def test_fwpkm_chunk_write_is_the_gradient_step_of_the_reconstruction_loss():
+    rng = np.random.default_rng(41)
+    h, dq, nk, k, T, dv, lr = 2, 8, 6, 3, 10, 5, 0.3
+    cfg = _Cfg(heads=h, dq=dq, topk=k, n_keys=nk, n_keys2=nk, temperature=1.0, dtype=O.F64)
+    q = rng.standard_normal((T, h * dq))
+    C = rng.standard_normal((h, nk, dq // 2))
+    Cp = rng.standard_normal((h, nk, dq // 2))
+    V = rng.standard_normal((nk * nk, dv))
+    tgt = rng.standard_normal((T, dv))
+    y, Vn, sel = O.fwpkm_chunk(cfg, q, C, Cp, V, tgt, lr)
+    # y reads the rows before the write
+    np.testing.assert_allclose(y, O.gather_sum(sel["rows"], sel["w"], V, O.F64), rtol=1e-15)
+
+    def loss(Vx):
+        yx = O.gather_sum(sel["rows"], sel["w"], Vx, O.F64)
+        return 0.5 * ((yx - tgt) ** 2).sum()
+
+    g = (V - Vn) / lr
+    eps = 1e-6
+    for r in range(nk * nk):
+        for c in range(dv):
+            E = np.zeros_like(V)
+            E[r, c] = eps
+            fd = (loss(V + E) - loss(V - E)) / (2 * eps)
+            assert abs(fd - g[r, c]) <= 1e-6 * max(1.0, abs(fd))
+    untouched = np.setdiff1d(np.arange(nk * nk), np.unique(sel["rows"]))
+    np.testing.assert_array_equal(Vn[untouched], V[untouched])
