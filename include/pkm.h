@@ -86,6 +86,18 @@ typedef enum { PKM_BN_NONE = 0, PKM_BN_BATCH = 1 } pkm_bn_mode;
  * V in the backward return PKM_ERR_UNSUPPORTED (train a table in the storage
  * dtype and quantize it). */
 typedef enum { PKM_VALUES_STORAGE = 0, PKM_VALUES_FP8 = 1 } pkm_value_format;
+/* Sub-key score.  PKM_SCORE_DOT: s1[i] = q1 . C[h,i] (as above).  PKM_SCORE_IDW
+ * ("Fast-weight Product Key Memory", section 2.2: inverse-distance scores):
+ * s1[i] = -log ||q1 - C[h,i]||, computed as -1/2 log(max(||q1||^2 - (2 q1 . C[h,i]
+ * - ||C[h,i]||^2), 1e-12)) in fp32, likewise s2 against C'; the per-half top-k
+ * ranks on 2 q1 . C[h,i] - ||C[h,i]||^2, which orders the sub-keys as the
+ * distance does.  The full-key score stays s1 + s2, so the product-key search is
+ * still exact.  With IDW, pkm_forward, pkm_stage_score_topk and pkm_fwpkm_chunk
+ * score this way; pkm_backward, pkm_backward_adam and pkm_stage_subkey_grad
+ * return PKM_ERR_UNSUPPORTED (their score gradients are the dot product's). */
+typedef enum { PKM_SCORE_DOT = 0, PKM_SCORE_IDW = 1 } pkm_score_fn;
+/* pkm_workspace_size's with_backward: the forward, the backward, or pkm_fwpkm_chunk. */
+typedef enum { PKM_WS_FORWARD = 0, PKM_WS_BACKWARD = 1, PKM_WS_FWPKM_CHUNK = 2 } pkm_ws_kind;
 
 /* Layer shape.  pkm_create checks (v = 8 elements for bf16, 4 for fp32 storage,
  * i.e. 16 bytes):
@@ -110,6 +122,7 @@ typedef struct {
   float temperature;     /* tau: w = softmax(score / tau) (1.0) */
   int32_t accumulate_dv; /* pkm_backward: 1 -> dV[r] += g_r, 0 -> dV[r] = g_r (touched rows only) */
   int32_t value_format;  /* pkm_value_format: PKM_VALUES_STORAGE (V in the storage dtype) or PKM_VALUES_FP8 */
+  int32_t score_fn;      /* pkm_score_fn: PKM_SCORE_DOT or PKM_SCORE_IDW */
 } pkm_config;
 
 /* State the forward saves for the backward; every buffer is caller-allocated device memory. */
@@ -146,8 +159,9 @@ pkm_status pkm_destroy(pkm_handle_t handle);
 /* The config the handle was created with. */
 pkm_status pkm_get_config(pkm_handle_t handle, pkm_config* out);
 
-/* Device workspace (bytes) that pkm_forward (with_backward = 0) or pkm_backward
- * (with_backward = 1) needs for T tokens.  The caller allocates it. */
+/* Device workspace (bytes) that pkm_forward (with_backward = PKM_WS_FORWARD),
+ * pkm_backward (PKM_WS_BACKWARD) or pkm_fwpkm_chunk (PKM_WS_FWPKM_CHUNK) needs
+ * for T tokens; any other value is PKM_ERR_INVALID_ARG.  The caller allocates it. */
 pkm_status pkm_workspace_size(pkm_handle_t handle, int64_t T, int with_backward, size_t* bytes);
 
 /* Forward m(x) for T >= 1 tokens.  Device pointers:
@@ -316,6 +330,27 @@ pkm_status pkm_stage_query_grad(pkm_handle_t handle, void* stream, int64_t T, co
                                 const void* x, const void* Wq, const float* bn_gamma,
                                 const pkm_saved* saved, float* dWq, float* dgamma, float* dbeta,
                                 void* dx, void* ws, size_t ws_bytes);
+
+/* One chunk of FwPKM memorization ("Fast-weight Product Key Memory", sections
+ * 2.1 and 2.2: the value table is a fast weight that the layer itself writes
+ * while it reads, by a gradient step on a local reconstruction loss toward the
+ * caller's lookahead targets).  For the T tokens of the chunk, with the
+ * handle's IDW scores (score_fn must be PKM_SCORE_IDW, else
+ * PKM_ERR_UNSUPPORTED; value_format must be PKM_VALUES_STORAGE):
+ *   idx, w  = the selection of q (as pkm_stage_score_topk + pkm_stage_merge_softmax);
+ *   y[t]    = sum over (h, s) of w V[idx] from V BEFORE the write, rounded to storage;
+ *   e[t]    = y[t] - target[t], rounded to storage (the gradient of 1/2 ||y - target||^2);
+ *   V[r]    = V[r] - lr * sum over the lookups c of r of w[c] e[t(c)], fp32, rounded
+ *             to storage, for every selected row r (no other row is read or written).
+ * The per-row sums run in a fixed order, so the result is deterministic.
+ * Device pointers: q [T, h*dq], C [h, |C|, dq/2], Cp [h, |C'|, dq/2], V [|C|*|C'|,
+ * d_value] (updated in place), target and y [T, d_value]: storage dtype;
+ * idx int32 and w fp32 [T, h, k] (outputs, ordered as in pkm_saved).  lr finite
+ * >= 0.  ws >= pkm_workspace_size(handle, T, PKM_WS_FWPKM_CHUNK).  Chunks that
+ * follow one another are calls that follow one another on the stream. */
+pkm_status pkm_fwpkm_chunk(pkm_handle_t handle, void* stream, int64_t T, const void* q, const void* C,
+                           const void* Cp, void* V, const void* target, float lr, void* y, int32_t* idx,
+                           float* w, void* ws, size_t ws_bytes);
 
 #ifdef __cplusplus
 }

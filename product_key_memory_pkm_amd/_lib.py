@@ -19,6 +19,8 @@ PKM_OK, PKM_ERR_INVALID_ARG, PKM_ERR_UNSUPPORTED, PKM_ERR_WORKSPACE, PKM_ERR_HIP
 PKM_F32, PKM_BF16 = 0, 1
 PKM_BN_NONE, PKM_BN_BATCH = 0, 1
 PKM_VALUES_STORAGE, PKM_VALUES_FP8 = 0, 1
+PKM_SCORE_DOT, PKM_SCORE_IDW = 0, 1
+PKM_WS_FORWARD, PKM_WS_BACKWARD, PKM_WS_FWPKM_CHUNK = 0, 1, 2
 
 _STORAGE = {PKM_F32: torch.float32, PKM_BF16: torch.bfloat16}
 
@@ -34,7 +36,7 @@ class pkm_config(ctypes.Structure):
                 ("n_keys", ctypes.c_int32), ("n_keys2", ctypes.c_int32), ("topk", ctypes.c_int32),
                 ("d_value", ctypes.c_int32), ("dtype", ctypes.c_int32), ("bn", ctypes.c_int32),
                 ("bn_eps", ctypes.c_float), ("temperature", ctypes.c_float), ("accumulate_dv", ctypes.c_int32),
-                ("value_format", ctypes.c_int32)]
+                ("value_format", ctypes.c_int32), ("score_fn", ctypes.c_int32)]
 
 
 class pkm_saved(ctypes.Structure):
@@ -77,6 +79,7 @@ _SIGS = {
     "pkm_stage_subkey_grad": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
     "pkm_stage_query_grad": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_saved), _VP, _VP, _VP, _VP,
                              _VP, _SZ],
+    "pkm_fwpkm_chunk": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP, _VP, _VP, _VP, _SZ],
 }
 EXPORTED = sorted(list(_SIGS) + ["pkm_status_string", "pkm_last_error"])
 
@@ -155,14 +158,18 @@ class Handle:
 
 
 def make_config(d_in, heads, d_query, n_keys, n_keys2, topk, d_value, dtype="f32", bn=True, bn_eps=1e-5,
-                temperature=1.0, accumulate_dv=True, values="storage") -> pkm_config:
-    """``values``: "storage" (V in the storage dtype) or "fp8" (rows of a fp32 scale + E4M3 codes)."""
+                temperature=1.0, accumulate_dv=True, values="storage", score="dot") -> pkm_config:
+    """``values``: "storage" (V in the storage dtype) or "fp8" (rows of a fp32 scale + E4M3 codes);
+    ``score``: "dot" (q . c) or "idw" (-log ||q - c||, the fast-weight memory's scores)."""
     if values not in ("storage", "fp8"):
         raise ValueError(f"values must be 'storage' or 'fp8', got {values!r}")
+    if score not in ("dot", "idw"):
+        raise ValueError(f"score must be 'dot' or 'idw', got {score!r}")
     return pkm_config(d_in, heads, d_query, n_keys, n_keys2, topk, d_value,
                       PKM_BF16 if dtype in ("bf16", PKM_BF16, torch.bfloat16) else PKM_F32,
                       PKM_BN_BATCH if bn else PKM_BN_NONE, bn_eps, temperature, 1 if accumulate_dv else 0,
-                      PKM_VALUES_FP8 if values == "fp8" else PKM_VALUES_STORAGE)
+                      PKM_VALUES_FP8 if values == "fp8" else PKM_VALUES_STORAGE,
+                      PKM_SCORE_IDW if score == "idw" else PKM_SCORE_DOT)
 
 
 def pkm_create(cfg: pkm_config) -> Handle:
@@ -177,9 +184,12 @@ def pkm_get_config(h: Handle) -> pkm_config:
     return c
 
 
-def pkm_workspace_size(h: Handle, T: int, with_backward: bool) -> int:
+def pkm_workspace_size(h: Handle, T: int, with_backward) -> int:
+    """``with_backward``: False/True (forward / backward) or one of PKM_WS_FORWARD, PKM_WS_BACKWARD,
+    PKM_WS_FWPKM_CHUNK."""
+    kind = int(with_backward)
     n = ctypes.c_size_t()
-    _check(lib().pkm_workspace_size(h.ptr, T, int(bool(with_backward)), ctypes.byref(n)), "pkm_workspace_size")
+    _check(lib().pkm_workspace_size(h.ptr, T, kind, ctypes.byref(n)), "pkm_workspace_size")
     return n.value
 
 
@@ -337,3 +347,15 @@ def pkm_stage_query_grad(h, T, dq, x, Wq, bn_gamma, saved: dict, dWq, dgamma, db
     _check(_invoke("pkm_stage_query_grad", h, T, _ptr(dq), _ptr(x), _ptr(Wq), _ptr(bn_gamma),
                                       ctypes.byref(sv), _ptr(dWq), _ptr(dgamma), _ptr(dbeta), _ptr(dx), _ptr(ws),
                                       _nbytes(ws)), "pkm_stage_query_grad")
+
+
+def pkm_fwpkm_chunk(h, T, q, C, Cp, V, target, lr, y, idx, w, ws):
+    """One FwPKM memorization chunk (pkm.h): select with IDW scores, y from V before the write, then
+    V[r] -= lr * sum w (y - target) over the lookups of each selected row (V updated in place)."""
+    st = h.storage
+    for n, t in (("q", q), ("C", C), ("Cp", Cp), ("V", V), ("target", target), ("y", y)):
+        _dt(t, st, n)
+    _dt(idx, torch.int32, "idx")
+    _dt(w, torch.float32, "w")
+    _check(_invoke("pkm_fwpkm_chunk", h, T, _ptr(q), _ptr(C), _ptr(Cp), _ptr(V), _ptr(target), float(lr), _ptr(y),
+                   _ptr(idx), _ptr(w), _ptr(ws), _nbytes(ws)), "pkm_fwpkm_chunk")

@@ -143,9 +143,28 @@ BwdLayout bwd_layout(const pkm_handle_s* h, int64_t T) {
   return L;
 }
 
+// FwPKM memorization chunk: the forward's and the backward's regions (used one
+// after the other), then the residual e [T, d_value] (storage dtype), the
+// touched rows and their count.
+struct ChunkLayout {
+  size_t e, touched, n_touched, total;
+};
+
+ChunkLayout chunk_layout(const pkm_handle_s* h, int64_t T) {
+  const size_t N = size_t(T) * h->cfg.heads * h->cfg.topk;
+  ChunkLayout L{};
+  size_t o = std::max(fwd_layout(h, T).total, bwd_layout(h, T).total);
+  L.e = o; o += al(size_t(T) * h->cfg.d_value * h->elem);
+  L.touched = o; o += al(N * 4);
+  L.n_touched = o; o += al(sizeof(int64_t));
+  L.total = o;
+  return L;
+}
+
 size_t ws_size(const pkm_handle_s* h, int64_t T, int with_backward) {
   const size_t f = fwd_layout(h, T).total;
-  if (!with_backward) return f;
+  if (with_backward == PKM_WS_FORWARD) return f;
+  if (with_backward == PKM_WS_FWPKM_CHUNK) return chunk_layout(h, T).total;
   const size_t b = std::max(bwd_layout(h, T).total,
                             diagnostics_ws_bytes(T, h->cfg.heads, int64_t(h->cfg.n_keys) * h->cfg.n_keys2));
   return f > b ? f : b;
@@ -160,6 +179,13 @@ pkm_status check_handle(pkm_handle_t h) {
 pkm_status need_storage_values(pkm_handle_t h) {
   if (h->cfg.value_format == PKM_VALUES_FP8)
     return fail(PKM_ERR_UNSUPPORTED, "fp8 values are a forward format; the backward needs V in the storage dtype");
+  return PKM_OK;
+}
+
+// The gradients through the scores are those of the dot product.
+pkm_status need_dot_scores(pkm_handle_t h) {
+  if (h->cfg.score_fn != PKM_SCORE_DOT)
+    return fail(PKM_ERR_UNSUPPORTED, "the sub-key and query gradients are implemented for dot-product scores only");
   return PKM_OK;
 }
 
@@ -213,7 +239,7 @@ pkm_status run_score(const pkm_handle_s* h, hipStream_t s, int64_t T, const void
   const pkm_config& c = h->cfg;
   const FwdLayout L = fwd_layout(h, T);
   PKM_HIP(launch_score_topk(s, c.dtype, q, T, c.heads, c.d_query, C, Cp, c.n_keys, c.n_keys2, c.topk, sub_idx,
-                            sub_score, at<void>(ws, L.keys)),
+                            sub_score, at<void>(ws, L.keys), c.score_fn == PKM_SCORE_IDW),
           "sub-key scoring / top-k");
   return PKM_OK;
 }
@@ -298,6 +324,7 @@ pkm_status adam_args(const pkm_adam* hp, void* V, float* m, float* v, VgAdam* ou
   out->eps = hp->eps;
   out->step_size = float(double(hp->lr) / bc1);
   out->inv_sqrt_bc2 = float(1.0 / std::sqrt(bc2));
+  out->sgd = 0;
   return PKM_OK;
 }
 
@@ -480,6 +507,8 @@ pkm_status pkm_create(const pkm_config* cfg, pkm_handle_t* out) {
     return fail(PKM_ERR_UNSUPPORTED, "d_value rows above 4096 bytes are not supported");
   if (c.value_format != PKM_VALUES_STORAGE && c.value_format != PKM_VALUES_FP8)
     return fail(PKM_ERR_INVALID_ARG, "value_format %d unknown", c.value_format);
+  if (c.score_fn != PKM_SCORE_DOT && c.score_fn != PKM_SCORE_IDW)
+    return fail(PKM_ERR_INVALID_ARG, "score_fn %d unknown", c.score_fn);
   if (c.value_format == PKM_VALUES_FP8 && c.d_value % 16)
     return fail(PKM_ERR_UNSUPPORTED, "fp8 values need d_value to be a multiple of 16");
   const int maxk = c.n_keys > c.n_keys2 ? c.n_keys : c.n_keys2;
@@ -551,6 +580,8 @@ pkm_status pkm_workspace_size(pkm_handle_t handle, int64_t T, int with_backward,
   PKM_TRY(check_handle(handle));
   if (!bytes) return fail(PKM_ERR_INVALID_ARG, "bytes is NULL");
   PKM_TRY(check_T(handle, T));
+  if (with_backward != PKM_WS_FORWARD && with_backward != PKM_WS_BACKWARD && with_backward != PKM_WS_FWPKM_CHUNK)
+    return fail(PKM_ERR_INVALID_ARG, "with_backward = %d is none of 0, 1, 2", with_backward);
   *bytes = ws_size(handle, T, with_backward);
   return PKM_OK;
 }
@@ -593,6 +624,7 @@ static pkm_status backward_impl(pkm_handle_t handle, void* stream, int64_t T, co
                                 void* dx, void* ws, size_t ws_bytes) {
   PKM_TRY(check_handle(handle));
   PKM_TRY(need_storage_values(handle));
+  PKM_TRY(need_dot_scores(handle));
   PKM_TRY(check_T(handle, T));
   const bool bn = handle->cfg.bn == PKM_BN_BATCH;
   PKM_TRY(need(dY, "dY"));
@@ -857,6 +889,7 @@ pkm_status pkm_stage_subkey_grad(pkm_handle_t handle, void* stream, int64_t T, c
                                  const float* dw, const void* q, const void* C, const void* Cp, float* dq, float* dC,
                                  float* dCp, void* ws, size_t ws_bytes) {
   PKM_TRY(check_handle(handle));
+  PKM_TRY(need_dot_scores(handle));
   PKM_TRY(check_T(handle, T));
   PKM_TRY(need(idx, "idx"));
   PKM_TRY(need(w, "w"));
@@ -898,3 +931,42 @@ pkm_status pkm_stage_query_grad(pkm_handle_t handle, void* stream, int64_t T, co
 }
 
 }  // extern "C"
+
+pkm_status pkm_fwpkm_chunk(pkm_handle_t handle, void* stream, int64_t T, const void* q, const void* C, const void* Cp,
+                           void* V, const void* target, float lr, void* y, int32_t* idx, float* w, void* ws,
+                           size_t ws_bytes) {
+  PKM_TRY(check_handle(handle));
+  PKM_TRY(need_storage_values(handle));
+  if (handle->cfg.score_fn != PKM_SCORE_IDW)
+    return fail(PKM_ERR_UNSUPPORTED, "the memorization chunk scores with score_fn = PKM_SCORE_IDW");
+  PKM_TRY(check_T(handle, T));
+  PKM_TRY(need(q, "q"));
+  PKM_TRY(need(C, "C"));
+  PKM_TRY(need(Cp, "Cp"));
+  PKM_TRY(need(V, "V"));
+  PKM_TRY(need(target, "target"));
+  PKM_TRY(need(y, "y"));
+  PKM_TRY(need(idx, "idx"));
+  PKM_TRY(need(w, "w"));
+  if (!(std::isfinite(lr) && lr >= 0.f)) return fail(PKM_ERR_INVALID_ARG, "lr must be finite and >= 0");
+  PKM_TRY(check_ws(handle, T, PKM_WS_FWPKM_CHUNK, ws, ws_bytes));
+  if (T == 0) return PKM_OK;
+  const pkm_config& c = handle->cfg;
+  hipStream_t s = as_stream(stream);
+  const FwdLayout F = fwd_layout(handle, T);
+  const BwdLayout B = bwd_layout(handle, T);
+  const ChunkLayout L = chunk_layout(handle, T);
+  int32_t* sub_idx = at<int32_t>(ws, F.sub_idx);
+  float* sub_score = at<float>(ws, F.sub_score);
+  PKM_TRY(run_score(handle, s, T, q, C, Cp, sub_idx, sub_score, ws));
+  PKM_TRY(run_merge(handle, s, T, sub_idx, sub_score, idx, w, nullptr));
+  PKM_TRY(run_gather(handle, s, T, idx, w, V, y));
+  void* e = at<void>(ws, L.e);
+  PKM_HIP(launch_sub_storage(s, c.dtype, y, target, e, T * c.d_value), "reconstruction residual");
+  VgAdam sgd{};
+  sgd.V = V;
+  sgd.step_size = lr;
+  sgd.sgd = 1;
+  return run_value_grad(handle, s, T, idx, w, e, V, nullptr, at<int32_t>(ws, L.touched), at<int64_t>(ws, L.n_touched),
+                        at<float>(ws, B.dw), ws, &sgd);
+}

@@ -22,9 +22,10 @@ hipError_t launch_quantize_fp8(hipStream_t s, int dtype, const void* src, int64_
 // Returns hipErrorInvalidValue when the shape does not fit the kernel's LDS plan.
 bool score_topk_supported(int dtype, int half, int nkeys);
 size_t score_topk_packed_bytes(int dtype, int heads, int half, int nk, int nk2);
+// idw: scores -log |q_half - c| (squared distance floored at 1e-12) instead of q_half . c.
 hipError_t launch_score_topk(hipStream_t s, int dtype, const void* q, int64_t ntok, int heads, int dq,
                              const void* C, const void* Cp, int nk, int nk2, int k, int32_t* sub_idx,
-                             float* sub_score, void* packed);
+                             float* sub_score, void* packed, bool idw = false);
 
 // a5: k x k candidates -> top-k -> softmax, per (token, head).
 hipError_t launch_merge_softmax(hipStream_t s, const int32_t* sub_idx, const float* sub_score,
@@ -97,8 +98,9 @@ struct VgAdam {
   float* m;
   float* v;
   float beta1, beta2, eps;
-  float step_size;     // lr / (1 - beta1^step)
+  float step_size;     // lr / (1 - beta1^step); with sgd the learning rate
   float inv_sqrt_bc2;  // 1 / sqrt(1 - beta2^step)
+  int sgd;             // 1: plain step V -= step_size * g (m, v unused)
 };
 size_t value_grad_aux_bytes(int64_t nitems, int d_value);
 hipError_t launch_value_grad(hipStream_t s, int dtype, const int32_t* seg_start, const int64_t* nseg,
@@ -124,6 +126,8 @@ hipError_t launch_subkey_grad(hipStream_t s, int dtype, const int32_t* seg_start
                               int nkeys, float* dC, void* aux);
 
 hipError_t launch_fill_f32(hipStream_t s, float* p, int64_t n, float v);
+// e = a - b elementwise in the storage dtype (n elements, fp32 arithmetic, one rounding).
+hipError_t launch_sub_storage(hipStream_t s, int dtype, const void* a, const void* b, void* e, int64_t n);
 
 // Monitoring signals of a selection (idx, w [ntok, heads, k]): sub-key hit
 // counts, slots in use (all heads, then per head), entropy per (t, h) (may be

@@ -56,7 +56,8 @@ __device__ __forceinline__ float wave_min_f32(float v) {
   return v;
 }
 
-constexpr int kBoundSteps = 12;  // halvings of the selection bound's search range
+constexpr int kBoundSteps = 12;
+constexpr float kIdwFloor = 1e-12f;  // squared-distance floor of the IDW scores  // halvings of the selection bound's search range
 
 __device__ __forceinline__ int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
@@ -406,7 +407,8 @@ template <typename T, int TM, int NPL>
 __global__ __launch_bounds__(kThreads) void score_topk_kernel(
     const T* __restrict__ q, int64_t ntok, int F, int dq, int half, int half_pad, int qstride,
     const u32x4* __restrict__ P1, const u32x4* __restrict__ P2, int nk, int nk2, int k, int cw, int sstride,
-    int32_t* __restrict__ sub_idx, float* __restrict__ sub_score) {
+    int32_t* __restrict__ sub_idx, float* __restrict__ sub_score, const float* __restrict__ cc1,
+    const float* __restrict__ cc2) {
   using TR = ScoreTraits<T>;
   constexpr int VE = TR::VE;
   constexpr int KC = TR::KC;
@@ -427,6 +429,9 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(
   const int ntile = (ncols + 15) / 16;
   const int nks = half_pad / KC;
   const u32x4* keys = (p ? P2 : P1) + size_t(hh) * ntile * nks * 64;
+  // IDW scores (cc1 != null): |c|^2 of this head's sub-keys; the tile then
+  // holds 2 q.c - |c|^2, which orders like -|q - c|^2 (|q|^2 is one per row)
+  const float* ccp = cc1 ? (p ? cc2 : cc1) + size_t(hh) * ncols : nullptr;
   const int64_t t0 = int64_t(blockIdx.x) * TM;
 
   // 1. query tile -> LDS (zero rows past the last token and k past dq/2)
@@ -492,8 +497,15 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
-          if (g0 + c < nct)
-            *reinterpret_cast<f32x4*>(S + size_t(rt * 16 + lrow) * sstride + (g0 + c) * 16 + lgrp * 4) = acc[rt][c];
+          if (g0 + c < nct) {
+            f32x4 v = acc[rt][c];
+            if (ccp) {  // wave-uniform
+              const int key0 = cb + (g0 + c) * 16 + lgrp * 4;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) v[i] = fmaf(2.f, v[i], -(key0 + i < ncols ? ccp[key0 + i] : 0.f));
+            }
+            *reinterpret_cast<f32x4*>(S + size_t(rt * 16 + lrow) * sstride + (g0 + c) * 16 + lgrp * 4) = v;
+          }
         }
     }
     __syncthreads();
@@ -502,13 +514,29 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(
     select_chunk<NPL, RPW>(S, sstride, wave, kWaves, cwe, cb, k, lane, run);
     __syncthreads();  // the next chunk's scores overwrite S
   }
+  float qq[RPW];  // |q half|^2 of the wave's rows (IDW only)
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) {
+    qq[q] = 0.f;
+    if (ccp) {
+      const T* qr = qt + size_t(q * kWaves + wave) * qstride;
+      float a = 0.f;
+      for (int e = lane; e < half_pad; e += 64) {
+        const float x = to_f32<T>(qr[e]);
+        a = fmaf(x, x, a);
+      }
+      qq[q] = wave_sum_dpp(a);
+    }
+  }
 #pragma unroll
   for (int q = 0; q < RPW; ++q) {
     const int64_t t = t0 + q * kWaves + wave;
     if (lane < k && t < ntok) {
       const size_t o = ((size_t(t) * heads + hh) * 2 + p) * k + lane;
       sub_idx[o] = int32_t(~uint32_t(run[q]));
-      sub_score[o] = key_float(uint32_t(run[q] >> 32));
+      const float v = key_float(uint32_t(run[q] >> 32));
+      // IDW: -log |q - c| = -1/2 log(|q|^2 - (2 q.c - |c|^2)), squared distance floored
+      sub_score[o] = ccp ? -0.5f * logf(fmaxf(qq[q] - v, kIdwFloor)) : v;
     }
   }
 }
@@ -516,7 +544,8 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(
 
 template <typename T, int TM>
 void launch_tm(hipStream_t s, const Plan& pl, const void* q, int64_t ntok, int heads, int dq, const u32x4* C,
-               const u32x4* Cp, int nk, int nk2, int k, int32_t* sub_idx, float* sub_score) {
+               const u32x4* Cp, int nk, int nk2, int k, int32_t* sub_idx, float* sub_score, const float* cc1,
+               const float* cc2) {
   const int half = dq / 2;
   const int F = heads * dq;
   dim3 grid(unsigned((ntok + TM - 1) / TM), unsigned(heads), 2u);
@@ -528,7 +557,7 @@ void launch_tm(hipStream_t s, const Plan& pl, const void* q, int64_t ntok, int h
                           int(pl.lds));                                                               \
       hipLaunchKernelGGL(fn, grid, dim3(kThreads), pl.lds, s, static_cast<const T*>(q), ntok, F, dq, half, \
                          pl.half_pad, pl.qstride, C, Cp, nk,                                           \
-                         nk2, k, pl.cw, pl.sstride, sub_idx, sub_score);                             \
+                         nk2, k, pl.cw, pl.sstride, sub_idx, sub_score, cc1, cc2);                   \
     }                                                                                                 \
   } break;
   switch (pl.npl) {
@@ -545,13 +574,29 @@ void launch_tm(hipStream_t s, const Plan& pl, const void* q, int64_t ntok, int h
 
 template <typename T>
 void launch_t(hipStream_t s, const Plan& pl, const void* q, int64_t ntok, int heads, int dq, const u32x4* C,
-              const u32x4* Cp, int nk, int nk2, int k, int32_t* sub_idx, float* sub_score) {
+              const u32x4* Cp, int nk, int nk2, int k, int32_t* sub_idx, float* sub_score, const float* cc1,
+              const float* cc2) {
   if (pl.TM == 64)
-    launch_tm<T, 64>(s, pl, q, ntok, heads, dq, C, Cp, nk, nk2, k, sub_idx, sub_score);
+    launch_tm<T, 64>(s, pl, q, ntok, heads, dq, C, Cp, nk, nk2, k, sub_idx, sub_score, cc1, cc2);
   else if (pl.TM == 32)
-    launch_tm<T, 32>(s, pl, q, ntok, heads, dq, C, Cp, nk, nk2, k, sub_idx, sub_score);
+    launch_tm<T, 32>(s, pl, q, ntok, heads, dq, C, Cp, nk, nk2, k, sub_idx, sub_score, cc1, cc2);
   else
-    launch_tm<T, 16>(s, pl, q, ntok, heads, dq, C, Cp, nk, nk2, k, sub_idx, sub_score);
+    launch_tm<T, 16>(s, pl, q, ntok, heads, dq, C, Cp, nk, nk2, k, sub_idx, sub_score, cc1, cc2);
+}
+
+// |C[r]|^2 of every sub-key row r (fp32, in element order), for the IDW scores.
+template <typename T>
+__global__ __launch_bounds__(256) void subkey_norms_kernel(const T* __restrict__ C, int64_t rows, int half,
+                                                           float* __restrict__ out) {
+  for (int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x; r < rows; r += int64_t(gridDim.x) * 256) {
+    const T* c = C + size_t(r) * half;
+    float a = 0.f;
+    for (int j = 0; j < half; ++j) {
+      const float x = to_f32<T>(c[j]);
+      a = fmaf(x, x, a);
+    }
+    out[r] = a;
+  }
 }
 
 }  // namespace
@@ -565,12 +610,14 @@ bool score_topk_supported(int dtype, int half, int nkeys) {
 size_t score_topk_packed_bytes(int dtype, int heads, int half, int nk, int nk2) {
   const int KC = dtype == kBF16 ? 32 : 16;
   const size_t nks = size_t(round_up(half, KC) / KC);
-  return size_t(heads) * (size_t((nk + 15) / 16) + size_t((nk2 + 15) / 16)) * nks * 64 * 16;
+  // packed operands, then the sub-key squared norms of the IDW scores
+  return size_t(heads) * (size_t((nk + 15) / 16) + size_t((nk2 + 15) / 16)) * nks * 64 * 16 +
+         size_t(heads) * size_t(nk + nk2) * 4;
 }
 
 hipError_t launch_score_topk(hipStream_t s, int dtype, const void* q, int64_t ntok, int heads, int dq,
                              const void* C, const void* Cp, int nk, int nk2, int k, int32_t* sub_idx,
-                             float* sub_score, void* packed) {
+                             float* sub_score, void* packed, bool idw) {
   const int half = dq / 2;
   const Plan pl = make_plan(dtype, half, nk > nk2 ? nk : nk2);
   if (pl.TM == 0 || pl.npl > 16) return hipErrorInvalidValue;
@@ -591,10 +638,29 @@ hipError_t launch_score_topk(hipStream_t s, int dtype, const void* q, int64_t nt
   };
   pack(C, nk, P1);
   pack(Cp, nk2, P2);
+  float* cc1 = nullptr;
+  float* cc2 = nullptr;
+  if (idw) {
+    cc1 = reinterpret_cast<float*>(P2 + size_t(heads) * ((nk2 + 15) / 16) * nks * 64);
+    cc2 = cc1 + size_t(heads) * nk;
+    auto norms = [&](const void* src, int n, float* dst) {
+      const int64_t rows = int64_t(heads) * n;
+      int64_t b = (rows + 255) / 256;
+      if (b > 1024) b = 1024;
+      if (dtype == kBF16)
+        hipLaunchKernelGGL(subkey_norms_kernel<bf16_t>, dim3(unsigned(b)), dim3(256), 0, s,
+                           static_cast<const bf16_t*>(src), rows, half, dst);
+      else
+        hipLaunchKernelGGL(subkey_norms_kernel<float>, dim3(unsigned(b)), dim3(256), 0, s,
+                           static_cast<const float*>(src), rows, half, dst);
+    };
+    norms(C, nk, cc1);
+    norms(Cp, nk2, cc2);
+  }
   if (dtype == kBF16)
-    launch_t<bf16_t>(s, pl, q, ntok, heads, dq, P1, P2, nk, nk2, k, sub_idx, sub_score);
+    launch_t<bf16_t>(s, pl, q, ntok, heads, dq, P1, P2, nk, nk2, k, sub_idx, sub_score, cc1, cc2);
   else
-    launch_t<float>(s, pl, q, ntok, heads, dq, P1, P2, nk, nk2, k, sub_idx, sub_score);
+    launch_t<float>(s, pl, q, ntok, heads, dq, P1, P2, nk, nk2, k, sub_idx, sub_score, cc1, cc2);
   return hipGetLastError();
 }
 

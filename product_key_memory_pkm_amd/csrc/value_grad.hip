@@ -85,8 +85,9 @@ struct VgArgs {
   float* am;
   float* av;
   float b1, b2, eps;
-  float step_size;     // lr / (1 - b1^t)
+  float step_size;     // lr / (1 - b1^t); the plain learning rate when sgd
   float inv_sqrt_bc2;  // 1 / sqrt(1 - b2^t)
+  int sgd;             // plain gradient step V -= step_size * g (no moments)
 };
 
 // The wave's lanes own 16-byte vectors l, l+64, ... of a row; the first NVL-1
@@ -220,9 +221,21 @@ __device__ __forceinline__ void vg_adam_row(const VgArgs& a, const LaneVecs<NVL>
                                             const float (*g)[Vec16<T>::N]) {
   constexpr int E = Vec16<T>::N;
   const size_t dv = size_t(a.nvec) * E;
+  char* Vrow = reinterpret_cast<char*>(a.Vout) + size_t(r) * size_t(a.nvec) * 16;
+  if (a.sgd) {  // wave-uniform: V -= lr * g
+#pragma unroll
+    for (int m = 0; m < NVL; ++m) {
+      if (m == NVL - 1 && !lv.last_ok) continue;
+      float old[E], nv[E];
+      Vec16<T>::widen(vr[m], old);
+#pragma unroll
+      for (int e = 0; e < E; ++e) nv[e] = old[e] - a.step_size * g[m][e];
+      st16(Vrow + lv.voff[m], Vec16<T>::narrow(nv));
+    }
+    return;
+  }
   float* mrow = a.am + size_t(r) * dv;
   float* vrow = a.av + size_t(r) * dv;
-  char* Vrow = reinterpret_cast<char*>(a.Vout) + size_t(r) * size_t(a.nvec) * 16;
   float m0[NVL][E], v0[NVL][E];
   vg_load_f32<T, NVL>(lv, mrow, m0);
   vg_load_f32<T, NVL>(lv, vrow, v0);
@@ -362,7 +375,9 @@ hipError_t launch_value_grad(hipStream_t s, int dtype, const int32_t* seg_start,
   a.Vout = nullptr;
   a.am = a.av = nullptr;
   a.b1 = a.b2 = a.eps = a.step_size = a.inv_sqrt_bc2 = 0.f;
+  a.sgd = 0;
   if (adam) {
+    a.sgd = adam->sgd;
     a.Vout = adam->V;
     a.am = adam->m;
     a.av = adam->v;

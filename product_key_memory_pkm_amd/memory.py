@@ -16,13 +16,15 @@ class ProductKeyMemory:
     Parameters follow the C ABI (``pkm_config``): input width ``d_in``, ``heads``,
     per-head query width ``d_query``, codebook sizes ``n_keys`` / ``n_keys2``,
     ``topk``, value width ``d_value``, storage dtype ``"f32"`` or ``"bf16"``, value table format ``values``
-    (``"storage"`` or ``"fp8"``: rows of a fp32 scale and E4M3 codes, forward only).
+    (``"storage"`` or ``"fp8"``: rows of a fp32 scale and E4M3 codes, forward only), sub-key score
+    ``score`` (``"dot"``, or ``"idw"``: -log of the Euclidean distance, as the fast-weight memory scores;
+    forward and ``fwpkm_chunk`` only).
     """
 
     def __init__(self, d_in, heads, d_query, n_keys, n_keys2, topk, d_value, dtype="bf16", bn=True, bn_eps=1e-5,
-                 temperature=1.0, accumulate_dv=True, device="cuda", values="storage"):
+                 temperature=1.0, accumulate_dv=True, device="cuda", values="storage", score="dot"):
         self.cfg = L.make_config(d_in, heads, d_query, n_keys, n_keys2, topk, d_value, dtype, bn, bn_eps,
-                                 temperature, accumulate_dv, values)
+                                 temperature, accumulate_dv, values, score)
         self.handle = L.pkm_create(self.cfg)
         self.device = torch.device(device)
         self._ws = None
@@ -31,7 +33,7 @@ class ProductKeyMemory:
     def storage(self) -> torch.dtype:
         return self.handle.storage
 
-    def workspace(self, T: int, with_backward: bool) -> torch.Tensor:
+    def workspace(self, T: int, with_backward) -> torch.Tensor:
         n = L.pkm_workspace_size(self.handle, T, with_backward)
         if self._ws is None or self._ws.numel() < n:
             self._ws = torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
@@ -106,3 +108,17 @@ class ProductKeyMemory:
         L.pkm_backward_adam(self.handle, T, dY, x, Wq, gamma, C, Cp, V, saved, adam_m, adam_v, adam, g["touched"],
                             g["n_touched"], g["dC"], g["dCp"], g["dWq"], g["dgamma"], g["dbeta"], g["dx"], ws)
         return g
+
+    def fwpkm_chunk(self, q, C, Cp, V, target, lr: float, out=None):
+        """One memorization chunk of the fast-weight memory (``pkm_fwpkm_chunk``): returns (y, idx, w),
+        y read from V before the write; V is updated in place."""
+        T = q.shape[0]
+        c = self.cfg
+        dev = self.device
+        if out is None:
+            out = {"y": torch.empty((T, c.d_value), dtype=self.storage, device=dev),
+                   "idx": torch.empty((T, c.heads, c.topk), dtype=torch.int32, device=dev),
+                   "w": torch.empty((T, c.heads, c.topk), dtype=torch.float32, device=dev)}
+        ws = self.workspace(T, L.PKM_WS_FWPKM_CHUNK)
+        L.pkm_fwpkm_chunk(self.handle, T, q, C, Cp, V, target, lr, out["y"], out["idx"], out["w"], ws)
+        return out["y"], out["idx"], out["w"]

@@ -29,11 +29,11 @@ def to_dev(a: np.ndarray, dtype: str | None = None) -> torch.Tensor:
     return t.cuda()
 
 
-def layer_for(cfg, accumulate_dv=True, values="storage"):
+def layer_for(cfg, accumulate_dv=True, values="storage", score="dot"):
     from product_key_memory_pkm_amd import ProductKeyMemory
     return ProductKeyMemory(cfg.d, cfg.heads, cfg.dq, cfg.n_keys, cfg.n_keys2, cfg.topk, cfg.d_value,
                             dtype=cfg.dtype, bn=cfg.bn, bn_eps=cfg.bn_eps, temperature=cfg.temperature,
-                            accumulate_dv=accumulate_dv, values=values)
+                            accumulate_dv=accumulate_dv, values=values, score=score)
 
 
 def fp8_table(scale: np.ndarray, codes: np.ndarray) -> np.ndarray:

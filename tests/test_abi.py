@@ -61,6 +61,12 @@ BAD_CONFIGS = [
 ]
 
 
+def test_make_config_rejects_unknown_score():
+    L = _lib()
+    with pytest.raises(ValueError):
+        _cfg(L, score="cosine")
+
+
 @pytest.mark.parametrize("kw,status", BAD_CONFIGS)
 def test_create_rejects(kw, status):
     L = _lib()
@@ -244,6 +250,52 @@ def test_fp8_values_argument_errors():
                                     1 << 40) == L.PKM_ERR_UNSUPPORTED
     assert lib.pkm_stage_value_grad_grouped(h.ptr, None, 4, ok[1], ok[2], ok[3], ok[4], ok[5], ok[6], ok[7],
                                             1 << 40) == L.PKM_ERR_UNSUPPORTED
+
+
+def test_idw_scores_and_fwpkm_chunk_argument_errors():
+    L = _lib()
+    lib = L.lib()
+    bad = _cfg(L, score="idw")
+    bad.score_fn = 3
+    assert lib.pkm_create(ctypes.byref(bad), ctypes.byref(ctypes.c_void_p())) == L.PKM_ERR_INVALID_ARG
+    h = L.pkm_create(_cfg(L, score="idw"))
+    dot = L.pkm_create(_cfg(L))
+    assert L.pkm_get_config(h).score_fn == L.PKM_SCORE_IDW
+    # the chunk's workspace holds the forward's and the backward's, plus the residual and the touched rows
+    T = 500
+    fwd, bwd = L.pkm_workspace_size(h, T, L.PKM_WS_FORWARD), L.pkm_workspace_size(h, T, L.PKM_WS_BACKWARD)
+    chunk = L.pkm_workspace_size(h, T, L.PKM_WS_FWPKM_CHUNK)
+    assert chunk >= max(fwd, bwd) + T * 64 * 4 + T * 2 * 8 * 4
+    with pytest.raises(L.PkmError) as e:
+        L.pkm_workspace_size(h, T, 3)
+    assert e.value.status == L.PKM_ERR_INVALID_ARG
+    ok = [_fake(i) for i in range(30)]
+    big = 1 << 40
+    c = lib.pkm_fwpkm_chunk
+
+    def call(handle=h, T=10, lr=0.1, ws_bytes=big, **over):
+        a = [over.get(n, ok[i]) for i, n in enumerate(("q", "C", "Cp", "V", "target", "y", "idx", "w"), 1)]
+        return c(handle.ptr, None, T, a[0], a[1], a[2], a[3], a[4], lr, a[5], a[6], a[7], ok[20], ws_bytes)
+
+    assert call(handle=dot) == L.PKM_ERR_UNSUPPORTED and "IDW" in lib.pkm_last_error().decode()
+    for n in ("q", "C", "Cp", "V", "target", "y", "idx", "w"):
+        assert call(**{n: None}) == L.PKM_ERR_INVALID_ARG, n
+        assert n in lib.pkm_last_error().decode()
+    assert call(q=ctypes.c_void_p(FAKE + 4)) == L.PKM_ERR_INVALID_ARG              # misaligned
+    for lr in (-0.5, float("inf"), float("nan")):
+        assert call(lr=lr) == L.PKM_ERR_INVALID_ARG
+    assert call(ws_bytes=16) == L.PKM_ERR_WORKSPACE
+    assert call(T=-1) == L.PKM_ERR_INVALID_ARG
+    assert call(T=0) == L.PKM_OK                                                     # nothing to do
+    fp8 = L.pkm_create(_cfg(L, score="idw", values="fp8", d_value=64))
+    assert call(handle=fp8) == L.PKM_ERR_UNSUPPORTED
+    # the score gradients are the dot product's: the backward refuses IDW handles
+    sv = L.pkm_saved(_fake(9), _fake(10), _fake(11), _fake(12), _fake(13), _fake(14))
+    st = lib.pkm_backward(h.ptr, None, 10, ok[1], ok[2], ok[3], ok[4], ok[5], ok[6], ok[7], ctypes.byref(sv), ok[8],
+                          ok[9], ok[10], ok[11], ok[12], ok[13], ok[14], ok[15], None, ok[16], big)
+    assert st == L.PKM_ERR_UNSUPPORTED and "dot-product" in lib.pkm_last_error().decode()
+    assert lib.pkm_stage_subkey_grad(h.ptr, None, 4, ok[1], ok[2], ok[3], ok[4], ok[5], ok[6], ok[7], ok[8], ok[9],
+                                     ok[10], big) == L.PKM_ERR_UNSUPPORTED
 
 
 def test_binding_rejects_host_tensors():

@@ -234,10 +234,13 @@ def test_query_stage(T, d, h, dq, dtype, bn):
 # ---------------------------------------------------------------------------
 # whole forward
 # ---------------------------------------------------------------------------
-def forward_check(cfg, inp, gpu: dict, tokens=None):
-    """Compare a GPU forward (q, idx, w, y as numpy) with the oracle on ``tokens`` (default all)."""
+def forward_check(cfg, inp, gpu: dict, tokens=None, score="dot"):
+    """Compare a GPU forward (q, idx, w, y as numpy) with the oracle on ``tokens`` (default all).
+
+    ``score`` "idw" (fp32 storage only: the bf16 slack below is the dot product's)."""
+    assert score == "dot" or cfg.dtype == "f32"
     tok = np.arange(cfg.T) if tokens is None else np.asarray(tokens)
-    ref = O.forward(cfg, inp, tokens=tok, keep_tables=True)
+    ref = O.forward(cfg, inp, tokens=tok, keep_tables=True, score=score)
     tol = P.TOL[cfg.dtype]
     q_g = gpu["q"][tok] if gpu["q"].shape[0] == cfg.T else gpu["q"]
     q_ref = ref["q"][tok]     # the query step covers every token (BatchNorm statistics)
