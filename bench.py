@@ -67,7 +67,35 @@ def parse():
                     help="after one step, five launches of the diagnostics on its selection and nothing else")
     ap.add_argument("--profile-adam", action="store_true",
                     help="after one step, one launch of the Adam-fused value kernel and nothing else (for profilers)")
+    ap.add_argument("--profile-fwpkm", type=int, default=0,
+                    help="run this many fast-weight memorization chunks and nothing else (for profilers)")
+    ap.add_argument("--no-fwpkm", action="store_true", help="skip the fast-weight memorization leg")
     return ap.parse_args()
+
+
+# The fast-weight memory (FwPKM) leg: one token stream memorized in chunks of 512 tokens
+# (the chunking of the fast-weight page) by a single-head memory with IDW scores that reads
+# k = 8 of the 1024 x 1024 slots per token, over the value table of the main workload.
+FWPKM_CHUNK = 512
+FWPKM_CHUNKS = 64
+FWPKM_TOPK = 8
+FWPKM_LR = 0.1
+
+
+def fwpkm_chunk_bytes(chunk, k, dv, e, touched):
+    """Algorithmic HBM bytes of one memorization chunk (heads = 1).
+
+    Read: every lookup's value row, index and weight (gather); y, the target and e for the
+    residual; every touched row once more for its step and the token's e once per touched row
+    group, with the sorted lookup id, weight and dw (4 bytes each).  Written: y, e, idx and w,
+    and every touched row once.  The sub-key scoring reads the chunk's queries (counted) and
+    the sub-keys (small, not counted)."""
+    L = chunk * k
+    gather = L * (dv * e + 8) + chunk * dv * e
+    residual = 3 * chunk * dv * e
+    update = touched * (2 * dv * e + 4) + chunk * dv * e + L * 12
+    select = L * 8
+    return gather + residual + update + select
 
 
 def alg_bytes(cfg, touched):
@@ -106,7 +134,8 @@ def main():
     import torch
 
     import pkm_inputs as pi
-    from product_key_memory_pkm_amd import (ProductKeyMemory, pkm_diagnostics, pkm_quantize_values, pkm_stage_gather,
+    from product_key_memory_pkm_amd import (PKM_WS_FWPKM_CHUNK, ProductKeyMemory, pkm_diagnostics, pkm_fwpkm_chunk,
+                                            pkm_quantize_values, pkm_stage_gather,
                                             pkm_stage_row_groups, pkm_stage_score_topk, pkm_stage_value_adam_grouped,
                                             pkm_stage_value_grad_grouped)
 
@@ -144,6 +173,33 @@ def main():
         nonlocal grads
         m.forward(x, Wq, gamma, beta, C, Cp, V, saved=saved, y=y)
         grads = m.backward(dY, x, Wq, gamma, C, Cp, V, saved, dV, want_dx=True, out=grads)
+
+    def fwpkm_setup():
+        """The fast-weight leg's memory, stream and buffers (allocated outside any timed region)."""
+        mf = ProductKeyMemory(cfg.d, 1, cfg.dq, cfg.n_keys, cfg.n_keys2, FWPKM_TOPK, cfg.d_value, dtype=cfg.dtype,
+                              bn=False, score="idw")
+        n = FWPKM_CHUNK * FWPKM_CHUNKS
+        qn, tn = pi.fwpkm_stream(cfg.seed + 100, n, cfg.dq, cfg.d_value, cfg.dtype)
+        st = {"m": mf, "q": dev(qn), "target": dev(tn), "C": C[:1].contiguous(), "Cp": Cp[:1].contiguous(),
+              "V": V.clone(), "y": torch.empty((n, cfg.d_value), dtype=m.storage, device="cuda"),
+              "idx": torch.empty((FWPKM_CHUNK, 1, FWPKM_TOPK), dtype=torch.int32, device="cuda"),
+              "w": torch.empty((FWPKM_CHUNK, 1, FWPKM_TOPK), dtype=torch.float32, device="cuda"),
+              "ws": mf.workspace(FWPKM_CHUNK, PKM_WS_FWPKM_CHUNK)}
+        return st
+
+    def fwpkm_run(st, nchunks):
+        c0 = FWPKM_CHUNK
+        for c in range(nchunks):
+            sl = slice(c * c0, (c + 1) * c0)
+            pkm_fwpkm_chunk(st["m"].handle, c0, st["q"][sl], st["C"], st["Cp"], st["V"], st["target"][sl],
+                            FWPKM_LR, st["y"][sl], st["idx"], st["w"], st["ws"])
+
+    if args.profile_fwpkm:
+        st = fwpkm_setup()
+        fwpkm_run(st, min(args.profile_fwpkm, FWPKM_CHUNKS))
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_fwpkm": min(args.profile_fwpkm, FWPKM_CHUNKS)}), flush=True)
+        return
 
     # first call allocates the outputs and the workspace outside the timed region
     step()
@@ -271,6 +327,33 @@ def main():
            "table_bytes": V8.numel(), "y_rel_diff_vs_storage_values": y_rel}
     del V8, y8, saved8, m8
     torch.cuda.empty_cache()
+    fw = None
+    if not args.no_fwpkm:
+        # the fast-weight memorization of one stream, chunk after chunk (each chunk reads what the
+        # chunks before it wrote); a second pass over the same stream is timed
+        st = fwpkm_setup()
+        fwpkm_run(st, FWPKM_CHUNKS)
+        torch.cuda.synchronize()
+        t_host = time.time()
+        start.record()
+        fwpkm_run(st, FWPKM_CHUNKS)
+        end.record()
+        host_s = time.time() - t_host
+        torch.cuda.synchronize()
+        ms_fw = start.elapsed_time(end)
+        touched_c = int(torch.unique(st["idx"]).numel())   # the last chunk's distinct rows
+        e_ = 2 if cfg.dtype == "bf16" else 4
+        cb = fwpkm_chunk_bytes(FWPKM_CHUNK, FWPKM_TOPK, cfg.d_value, e_, touched_c)
+        ms_chunk = ms_fw / FWPKM_CHUNKS
+        fw = {"workload": (f"one stream of {FWPKM_CHUNKS} x {FWPKM_CHUNK} tokens, heads=1, dq={cfg.dq}, "
+                           f"|C|=|C'|={cfg.n_keys} ({cfg.slots} slots), k={FWPKM_TOPK}, IDW scores, "
+                           f"d_value={cfg.d_value}, {cfg.dtype} storage, lr={FWPKM_LR}"),
+              "tokens_per_s": FWPKM_CHUNK * FWPKM_CHUNKS / (ms_fw * 1e-3), "ms_per_chunk": ms_chunk,
+              "host_enqueue_ms_per_chunk": host_s * 1e3 / FWPKM_CHUNKS,
+              "touched_rows_last_chunk": touched_c, "alg_bytes_per_chunk": cb,
+              "achieved_GBs_whole_chunk": cb / (ms_chunk * 1e-3) / 1e9}
+        del st
+        torch.cuda.empty_cache()
     # the per-half scoring + top-k kernel alone (its MFMA roofline)
     sub_idx = torch.empty((T, cfg.heads, 2, cfg.topk), dtype=torch.int32, device="cuda")
     sub_score = torch.empty((T, cfg.heads, 2, cfg.topk), dtype=torch.float32, device="cuda")
@@ -329,6 +412,7 @@ def main():
         "touched_rows": n_touched,
         "diagnostics": diag,
         "fp8_values": fp8,
+        "fwpkm": fw,
         "memory_usage": n_touched / cfg.slots,
         "input_generation_s": gen_s,
     }

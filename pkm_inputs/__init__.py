@@ -296,3 +296,19 @@ def random_sublists(seed: int, T: int, heads: int, k: int, nk: int, nk2: int, in
         idx[:, :, p, :] = np.take_along_axis(ids, order, axis=1).reshape(T, heads, k)
         sc[:, :, p, :] = np.take_along_axis(s, order, axis=1).reshape(T, heads, k)
     return idx, sc
+
+
+# --------------------------------------------------------------------------
+# fast-weight memory (FwPKM) stream
+# --------------------------------------------------------------------------
+def fwpkm_stream(seed: int, n_tokens: int, width: int, d_value: int, dtype: str = F32):
+    """Queries and lookahead targets of one token stream for the fast-weight memory.
+
+    q [n_tokens, width] ~ N(0, 2/width) (each half-query has unit expected norm, like the
+    uniform sub-keys); the stream's value vectors v [n_tokens + 1, d_value] ~ N(0, 1) and
+    the target of token t is v[t + 1] (the next token's value: the lookahead target of the
+    fast-weight page).  Both encoded in ``dtype``.
+    """
+    q = _fill(seed, 600, n_tokens * width, "normal", 0.0, math.sqrt(2.0 / width))
+    v = _fill(seed, 601, (n_tokens + 1) * d_value, "normal", 0.0, 1.0).reshape(n_tokens + 1, d_value)
+    return _encode(q.reshape(n_tokens, width), dtype), _encode(np.ascontiguousarray(v[1:]), dtype)

@@ -261,13 +261,27 @@ pkm_status run_gather(const pkm_handle_s* h, hipStream_t s, int64_t T, const int
   return PKM_OK;
 }
 
+int row_sort_passes(const pkm_handle_s* h) {
+  const int p = (h->row_bits + 7) / 8;
+  return p < 1 ? 1 : p;
+}
+
 // Grouping of the lookups by row.  The sorted (row, lookup) pairs land in
-// (k0, v0) or (k1, v1) depending on the number of radix passes.
+// (k0, v0) or (k1, v1) depending on the number of radix passes; a small batch
+// is sorted and segmented in one workgroup, straight into the same place.
 pkm_status run_row_groups(const pkm_handle_s* h, hipStream_t s, int64_t T, const int32_t* idx, int32_t* touched,
                           int64_t* n_touched, void* ws) {
   const pkm_config& c = h->cfg;
   const BwdLayout L = bwd_layout(h, T);
   const int64_t N = T * c.heads * c.topk;
+  if (N <= kSmallSortMax) {
+    const bool out1 = row_sort_passes(h) % 2 == 0;
+    PKM_HIP(launch_sort_segments_small(s, reinterpret_cast<const uint32_t*>(idx), N, h->row_bits,
+                                       at<uint32_t>(ws, out1 ? L.k1 : L.k0), at<int32_t>(ws, out1 ? L.v1 : L.v0),
+                                       at<int32_t>(ws, L.seg), touched, n_touched),
+            "row sort and segments (one workgroup)");
+    return PKM_OK;
+  }
   bool in1 = false;
   PKM_HIP(launch_radix_sort_from(s, reinterpret_cast<const uint32_t*>(idx), at<uint32_t>(ws, L.k0),
                                  at<int32_t>(ws, L.v0), at<uint32_t>(ws, L.k1), at<int32_t>(ws, L.v1), N, h->row_bits,
@@ -277,11 +291,6 @@ pkm_status run_row_groups(const pkm_handle_s* h, hipStream_t s, int64_t T, const
   PKM_HIP(launch_segments(s, sk, N, at<int32_t>(ws, L.seg), touched, n_touched, at<void>(ws, L.scan_tmp)),
           "row segments");
   return PKM_OK;
-}
-
-int row_sort_passes(const pkm_handle_s* h) {
-  const int p = (h->row_bits + 7) / 8;
-  return p < 1 ? 1 : p;
 }
 
 pkm_status run_value_grad_grouped(const pkm_handle_s* h, hipStream_t s, int64_t T, const float* w, const void* dY,

@@ -82,6 +82,14 @@ size_t scan_temp_bytes(int64_t n);
 hipError_t launch_exclusive_scan(hipStream_t s, const uint32_t* in, uint32_t* out, int64_t n, void* temp,
                                  uint32_t* total /*device, may be null*/);
 
+// Both of the above for n <= kSmallSortMax pairs in one launch: keys_in (< 2^key_bits)
+// stably sorted into keys_out with their indices in vals_out, and the segment
+// table (seg_start, touched (may be null), count) of the sorted keys.
+constexpr int kSmallSortMax = 8192;
+hipError_t launch_sort_segments_small(hipStream_t s, const uint32_t* keys_in, int64_t n, int key_bits,
+                                      uint32_t* keys_out, int32_t* vals_out, int32_t* seg_start, int32_t* touched,
+                                      int64_t* count);
+
 // Segments of a sorted key array: seg_start[u] for every distinct key run, and
 // count (device int64).  Also touched[u] = key of run u (may be null).
 // seg_start needs room for count + 1 entries (the last one is n).

@@ -584,18 +584,30 @@ void launch_t(hipStream_t s, const Plan& pl, const void* q, int64_t ntok, int he
     launch_tm<T, 16>(s, pl, q, ntok, heads, dq, C, Cp, nk, nk2, k, sub_idx, sub_score, cc1, cc2);
 }
 
-// |C[r]|^2 of every sub-key row r (fp32, in element order), for the IDW scores.
+// |c|^2 of every sub-key row, for the IDW scores: rows [0, rows1) of C, then
+// rows [rows1, rows1 + rows2) of C', into out[] in that order.  One wave per
+// row; lane l squares the 16-byte vectors l, l + 64, ... of the row, and a DPP
+// reduction adds the lanes in a fixed order (the result does not change from
+// run to run).
 template <typename T>
-__global__ __launch_bounds__(256) void subkey_norms_kernel(const T* __restrict__ C, int64_t rows, int half,
+__global__ __launch_bounds__(256) void subkey_norms_kernel(const T* __restrict__ C, int64_t rows1,
+                                                           const T* __restrict__ Cp, int64_t rows2, int half,
                                                            float* __restrict__ out) {
-  for (int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x; r < rows; r += int64_t(gridDim.x) * 256) {
-    const T* c = C + size_t(r) * half;
+  constexpr int VE = Vec16<T>::N;
+  const int lane = lane_id();
+  const int vpr = half / VE;
+  const int64_t nw = int64_t(gridDim.x) * (blockDim.x >> 6);
+  for (int64_t r = int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6); r < rows1 + rows2; r += nw) {
+    const T* c = r < rows1 ? C + size_t(r) * half : Cp + size_t(r - rows1) * half;
     float a = 0.f;
-    for (int j = 0; j < half; ++j) {
-      const float x = to_f32<T>(c[j]);
-      a = fmaf(x, x, a);
+    for (int v = lane; v < vpr; v += 64) {
+      float x[VE];
+      Vec16<T>::widen(ld16(c + size_t(v) * VE), x);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) a = fmaf(x[e], x[e], a);
     }
-    out[r] = a;
+    a = wave_sum_dpp(a);
+    if (lane == 0) out[r] = a;
   }
 }
 
@@ -643,19 +655,15 @@ hipError_t launch_score_topk(hipStream_t s, int dtype, const void* q, int64_t nt
   if (idw) {
     cc1 = reinterpret_cast<float*>(P2 + size_t(heads) * ((nk2 + 15) / 16) * nks * 64);
     cc2 = cc1 + size_t(heads) * nk;
-    auto norms = [&](const void* src, int n, float* dst) {
-      const int64_t rows = int64_t(heads) * n;
-      int64_t b = (rows + 255) / 256;
-      if (b > 1024) b = 1024;
-      if (dtype == kBF16)
-        hipLaunchKernelGGL(subkey_norms_kernel<bf16_t>, dim3(unsigned(b)), dim3(256), 0, s,
-                           static_cast<const bf16_t*>(src), rows, half, dst);
-      else
-        hipLaunchKernelGGL(subkey_norms_kernel<float>, dim3(unsigned(b)), dim3(256), 0, s,
-                           static_cast<const float*>(src), rows, half, dst);
-    };
-    norms(C, nk, cc1);
-    norms(Cp, nk2, cc2);
+    const int64_t rows1 = int64_t(heads) * nk, rows2 = int64_t(heads) * nk2;
+    int64_t b = (rows1 + rows2 + 3) / 4;  // four waves (rows) per block
+    if (b > 8192) b = 8192;
+    if (dtype == kBF16)
+      hipLaunchKernelGGL(subkey_norms_kernel<bf16_t>, dim3(unsigned(b)), dim3(256), 0, s,
+                         static_cast<const bf16_t*>(C), rows1, static_cast<const bf16_t*>(Cp), rows2, half, cc1);
+    else
+      hipLaunchKernelGGL(subkey_norms_kernel<float>, dim3(unsigned(b)), dim3(256), 0, s,
+                         static_cast<const float*>(C), rows1, static_cast<const float*>(Cp), rows2, half, cc1);
   }
   if (dtype == kBF16)
     launch_t<bf16_t>(s, pl, q, ntok, heads, dq, P1, P2, nk, nk2, k, sub_idx, sub_score, cc1, cc2);

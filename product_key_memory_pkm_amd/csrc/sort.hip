@@ -277,6 +277,147 @@ __global__ void seg_empty_kernel(int32_t* seg_start, int64_t* count) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small batches (n <= kSmallSortMax): the whole grouping in one workgroup of
+// 1024 threads, so a few thousand lookups cost one launch instead of a
+// histogram, a scan and a scatter per digit plus the segment passes.  The
+// (key, lookup id) pairs, packed as key << 32 | id, ping-pong between two LDS
+// buffers.  Per 8-bit digit each of the 16 waves owns a contiguous run of
+// pairs, ranks them among equal digits with ballots and counts them in its own
+// LDS row (as radix_scatter_kernel does per tile); one scan over (digit, wave)
+// turns the counts into bases, and the pairs, still in registers, are written
+// to the other buffer.  The order is stable, so equal keys keep their lookup
+// order.  Then the segment table is built from the sorted keys in the same
+// workgroup.
+// ---------------------------------------------------------------------------
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallWaves = kSmallThreads / 64;
+constexpr int kSmallRounds = kSmallSortMax / kSmallWaves / 64;  // 64-pair rounds per wave at most
+
+size_t small_sort_lds_bytes(int64_t n) {
+  return size_t(n) * 16 + size_t(kSmallWaves) * 256 * 4 + 64 * 4;
+}
+
+__global__ __launch_bounds__(kSmallThreads) void small_sort_segments_kernel(
+    const uint32_t* __restrict__ keys_in, int n, int passes, uint32_t* __restrict__ keys_out,
+    int32_t* __restrict__ vals_out, int32_t* __restrict__ seg_start, int32_t* __restrict__ touched,
+    int64_t* __restrict__ count) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  uint64_t* bufA = reinterpret_cast<uint64_t*>(smem);
+  uint64_t* bufB = bufA + n;
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(bufB + n);  // [kSmallWaves][256]
+  uint32_t* wsum = cnt + kSmallWaves * 256;                 // [64]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < n; i += kSmallThreads) bufA[i] = (uint64_t(keys_in[i]) << 32) | uint32_t(i);
+  // wave w owns pairs [w * per, (w + 1) * per), per a multiple of 64
+  const int per = ((n + kSmallWaves - 1) / kSmallWaves + 63) / 64 * 64;
+  const int rounds = per / 64;
+  uint64_t* src = bufA;
+  uint64_t* dst = bufB;
+  for (int p = 0; p < passes; ++p) {
+    const int shift = 32 + 8 * p;
+    for (int d = lane; d < 256; d += 64) cnt[wave * 256 + d] = 0;
+    __syncthreads();  // bufA filled / previous scatter done; counters cleared
+    uint64_t kv[kSmallRounds];
+    uint32_t lpos[kSmallRounds];
+#pragma unroll
+    for (int r = 0; r < kSmallRounds; ++r) {
+      if (r < rounds) {  // wave-uniform
+        const int e = wave * per + r * 64 + lane;
+        const bool ok = e < n;
+        kv[r] = ok ? src[e] : 0ull;
+        const uint32_t d = uint32_t(kv[r] >> shift) & 0xFFu;
+        uint64_t peers = ballot(ok);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          const bool bit = (d >> b) & 1u;
+          const uint64_t m = ballot(bit);
+          peers &= bit ? m : ~m;
+        }
+        const int rk = lanes_below(peers);
+        const uint32_t before = ok ? cnt[wave * 256 + d] : 0u;  // every lane reads before the leader writes
+        lpos[r] = before + uint32_t(rk);
+        if (ok && rk == 0) cnt[wave * 256 + d] = before + uint32_t(popc64(peers));
+      }
+    }
+    __syncthreads();
+    // bases in (digit, wave) order: digit tid's total, scanned over the 256 digits
+    uint32_t tot = 0, incl = 0;
+    if (tid < 256) {
+      for (int w = 0; w < kSmallWaves; ++w) tot += cnt[w * 256 + tid];
+      incl = tot;
+#pragma unroll
+      for (int dd = 1; dd < 64; dd <<= 1) {
+        const uint32_t y = __shfl_up(incl, dd, 64);
+        if (lane >= dd) incl += y;
+      }
+      if (lane == 63) wsum[wave] = incl;
+    }
+    __syncthreads();
+    if (tid < 256) {
+      uint32_t run = incl - tot;
+      for (int w = 0; w < wave; ++w) run += wsum[w];
+      for (int w = 0; w < kSmallWaves; ++w) {
+        const uint32_t c = cnt[w * 256 + tid];
+        cnt[w * 256 + tid] = run;
+        run += c;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kSmallRounds; ++r) {
+      if (r < rounds) {
+        const int e = wave * per + r * 64 + lane;
+        if (e < n) {
+          const uint32_t d = uint32_t(kv[r] >> shift) & 0xFFu;
+          dst[cnt[wave * 256 + d] + lpos[r]] = kv[r];
+        }
+      }
+    }
+    uint64_t* t = src;
+    src = dst;
+    dst = t;
+  }
+  __syncthreads();
+  // sorted pairs out; segment starts: the first key and every key that differs from its predecessor
+  for (int i = tid; i < n; i += kSmallThreads) {
+    keys_out[i] = uint32_t(src[i] >> 32);
+    vals_out[i] = int32_t(uint32_t(src[i]));
+  }
+  const int ipt = (n + kSmallThreads - 1) / kSmallThreads;
+  const int i0 = tid * ipt;
+  uint32_t flags = 0;
+  for (int j = 0; j < ipt; ++j) {
+    const int i = i0 + j;
+    if (i < n && (i == 0 || uint32_t(src[i] >> 32) != uint32_t(src[i - 1] >> 32))) flags |= 1u << j;
+  }
+  const uint32_t c = uint32_t(__popc(flags));
+  uint32_t x = c;
+#pragma unroll
+  for (int dd = 1; dd < 64; dd <<= 1) {
+    const uint32_t y = __shfl_up(x, dd, 64);
+    if (lane >= dd) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  uint32_t rank = x - c, total = 0;
+  for (int w = 0; w < kSmallWaves; ++w) {
+    if (w < wave) rank += wsum[w];
+    total += wsum[w];
+  }
+  for (int j = 0; j < ipt; ++j) {
+    if (flags & (1u << j)) {
+      seg_start[rank] = i0 + j;
+      if (touched) touched[rank] = int32_t(src[i0 + j] >> 32);
+      ++rank;
+    }
+  }
+  if (tid == 0) {
+    seg_start[total] = n;
+    *count = int64_t(total);
+  }
+}
+
 inline unsigned grid1d(int64_t n, int64_t cap = 16384) {
   int64_t b = (n + 255) / 256;
   if (b > cap) b = cap;
@@ -344,6 +485,26 @@ hipError_t launch_radix_sort_from(hipStream_t s, const uint32_t* keys_in, uint32
     }
   }
   *result_in_1 = (kin == k1);
+  return hipGetLastError();
+}
+
+hipError_t launch_sort_segments_small(hipStream_t s, const uint32_t* keys_in, int64_t n, int key_bits,
+                                      uint32_t* keys_out, int32_t* vals_out, int32_t* seg_start, int32_t* touched,
+                                      int64_t* count) {
+  if (n < 0 || n > kSmallSortMax) return hipErrorInvalidValue;
+  static bool attr_set = false;  // the attribute is per function; setting it again is harmless
+  const size_t lds = small_sort_lds_bytes(kSmallSortMax);
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(small_sort_segments_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  int passes = (key_bits + 7) / 8;
+  if (passes < 1) passes = 1;
+  if (passes > 4) passes = 4;
+  hipLaunchKernelGGL(small_sort_segments_kernel, dim3(1), dim3(kSmallThreads), small_sort_lds_bytes(n), s, keys_in,
+                     int(n), passes, keys_out, vals_out, seg_start, touched, count);
   return hipGetLastError();
 }
 

@@ -43,6 +43,10 @@ VG_CASES = [
     (64, 8, 32, 64, 1024, "bf16", 1.0, True),
     (1, 1, 1, 4, 8, "bf16", 0.0, True),
     (2000, 2, 16, 16, 16, "f32", 0.0, True),       # 256 rows, ~250 lookups per row
+    # up to 8192 lookups are grouped by one workgroup; one more takes the multi-launch radix sort
+    (256, 2, 16, 32, 64, "f32", 1.2, True),        # 8192 lookups, skewed: long runs
+    (257, 2, 16, 32, 64, "f32", 1.2, True),        # 8224 lookups
+    (1000, 2, 4, 4, 32, "bf16", 0.0, False),       # 8000 lookups over 16 rows: every row split in chunks
 ]
 
 
@@ -384,6 +388,7 @@ ADAM_CASES = [
     (64, 8, 32, 64, 1024, "bf16", 1.0),
     (2000, 2, 16, 16, 16, "f32", 0.0),       # ~250 lookups per row, around the chunk size
     (1, 1, 1, 4, 8, "bf16", 0.0),
+    (1000, 2, 4, 4, 32, "f32", 0.0),         # one-workgroup grouping, every row split in chunks
 ]
 
 

@@ -249,6 +249,8 @@ FWPKM_CASES = {
     "int_keys": (_cfg(T=64, heads=1, dq=16, n_keys=32, n_keys2=32, topk=4, d_value=32, seed=43), True, 1.0),
     # every row gets hundreds of lookups: the per-row sums run in chunks and a combine pass
     "hot": (_cfg(T=2048, heads=2, dq=32, n_keys=8, n_keys2=8, topk=8, d_value=40, seed=44), False, 0.01),
+    # 8000 lookups (one-workgroup grouping) over 16 rows: every row's sum runs in chunks
+    "hot_small": (_cfg(T=2000, heads=1, dq=16, n_keys=4, n_keys2=4, topk=4, d_value=32, seed=49), False, 0.01),
     "one_token": (_cfg(T=1, heads=1, dq=16, n_keys=8, n_keys2=8, topk=4, d_value=16, dtype="bf16", seed=45),
                   False, 1.0),
     "lr_zero": (_cfg(T=50, heads=1, dq=32, n_keys=16, n_keys2=16, topk=8, d_value=32, seed=46), False, 0.0),
