@@ -186,7 +186,11 @@ constexpr int kMaxChunk = 1024;
 
 // Widest chunk first (one selection per row and chunk), then the tallest tile
 // (a sub-key row read from L2 serves TM queries).
-Plan make_plan(int dtype, int half, int ncols) {
+// Row tiles: the tallest that fits, at least 32 rows for chunks wider than 256
+// columns (32 rows share each sub-key operand between two MFMA row tiles).
+// small_tiles: a launch with too few 32-row tiles to fill the chip takes
+// 16-row tiles (twice the blocks, each with half the work).
+Plan make_plan(int dtype, int half, int ncols, bool small_tiles = false) {
   Plan p{};
   const int VE = dtype == kBF16 ? 8 : 4;
   const int KC = dtype == kBF16 ? 32 : 16;
@@ -202,9 +206,9 @@ Plan make_plan(int dtype, int half, int ncols) {
     // plus 64 spare entries when a lane holds >= 4 values (>= 128 / 256 floats)
     const int smin = npl >= 4 ? 256 : 128;
     const int sstride = (cw > smin ? cw : smin) + 4;
-    for (int tm = 64; tm >= 16; tm /= 2) {
+    for (int tm = small_tiles ? 16 : 64; tm >= 16; tm /= 2) {
       const size_t lds = size_t(tm) * p.qstride * e + size_t(tm) * sstride * 4;
-      if (lds <= kLdsLimit && (tm / kWaves) * npl <= 64 && tm >= (cw > 256 ? 32 : 16)) {
+      if (lds <= kLdsLimit && (tm / kWaves) * npl <= 64 && tm >= (cw > 256 && !small_tiles ? 32 : 16)) {
         p.TM = tm;
         p.cw = cw;
         p.npl = npl;
@@ -631,7 +635,13 @@ hipError_t launch_score_topk(hipStream_t s, int dtype, const void* q, int64_t nt
                              const void* C, const void* Cp, int nk, int nk2, int k, int32_t* sub_idx,
                              float* sub_score, void* packed, bool idw) {
   const int half = dq / 2;
-  const Plan pl = make_plan(dtype, half, nk > nk2 ? nk : nk2);
+  int cus = 256;
+  {
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  }
+  const bool few_tiles = (ntok + 31) / 32 * heads * 2 < cus;
+  const Plan pl = make_plan(dtype, half, nk > nk2 ? nk : nk2, few_tiles);
   if (pl.TM == 0 || pl.npl > 16) return hipErrorInvalidValue;
   const int KC = dtype == kBF16 ? 32 : 16;
   const int nks = pl.half_pad / KC;
