@@ -30,9 +30,9 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 # workload, scaled by the same counters for a plain 1 GiB copy (profiles/*_hbm_counters.md).  Each figure
 # holds for the kernel sources whose combined sha256 prefix is given; any change to them voids it (traffic null).
 KERNEL_TRAFFIC = {
-    ("gather", "paper"): {"bytes": 13552399360, "sources": ["gather.hip", "common.h"], "sources_sha256_16": "130545acf7a0c23f"},
-    ("value_grad", "paper"): {"bytes": 29565939616, "sources": ["value_grad.hip", "sparse_common.h", "common.h"], "sources_sha256_16": "d5350ce721b14972"},
-    ("value_adam", "paper"): {"bytes": 46449338752, "sources": ["value_grad.hip", "sparse_common.h", "common.h"], "sources_sha256_16": "d5350ce721b14972"},
+    ("gather", "paper"): {"bytes": 13552071360, "sources": ["gather.hip", "common.h"], "sources_sha256_16": "993549f60bba5340"},
+    ("value_grad", "paper"): {"bytes": 29570266960, "sources": ["value_grad.hip", "sparse_common.h", "common.h"], "sources_sha256_16": "4cdc242cda6a10c3"},
+    ("value_adam", "paper"): {"bytes": 46072883456, "sources": ["value_grad.hip", "sparse_common.h", "common.h"], "sources_sha256_16": "4cdc242cda6a10c3"},
 }
 
 

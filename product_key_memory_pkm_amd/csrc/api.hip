@@ -969,9 +969,9 @@ pkm_status pkm_fwpkm_chunk(pkm_handle_t handle, void* stream, int64_t T, const v
   float* sub_score = at<float>(ws, F.sub_score);
   PKM_TRY(run_score(handle, s, T, q, C, Cp, sub_idx, sub_score, ws));
   PKM_TRY(run_merge(handle, s, T, sub_idx, sub_score, idx, w, nullptr));
-  PKM_TRY(run_gather(handle, s, T, idx, w, V, y));
   void* e = at<void>(ws, L.e);
-  PKM_HIP(launch_sub_storage(s, c.dtype, y, target, e, T * c.d_value), "reconstruction residual");
+  PKM_HIP(launch_gather(s, c.dtype, idx, w, V, y, T, c.heads * c.topk, c.d_value, false, target, e),
+          "value gather-sum and reconstruction residual");
   VgAdam sgd{};
   sgd.V = V;
   sgd.step_size = lr;

@@ -14,7 +14,9 @@
 //  * U rows are issued back to back before any FMA, keeping U*NVL 16-byte
 //    loads per lane in flight; V is read with non-temporal loads since random
 //    rows of a multi-GB table are not reused through the caches;
-//  * fp32 accumulation in registers, one rounding to the storage type.
+//  * fp32 accumulation in registers, one rounding to the storage type;
+//  * optionally (the fast-weight memorization) the residual y - target, from y
+//    as stored and rounded once more, written beside y.
 #include "common.h"
 #include "kernels.h"
 
@@ -24,7 +26,8 @@ template <typename T, int NVL, int U>
 __global__ __launch_bounds__(256) void gather_sum_kernel(const int32_t* __restrict__ idx,
                                                          const float* __restrict__ w,
                                                          const T* __restrict__ V, T* __restrict__ y,
-                                                         int64_t ntok, int R, int nvec) {
+                                                         int64_t ntok, int R, int nvec,
+                                                         const T* __restrict__ target, T* __restrict__ resid) {
   constexpr int E = Vec16<T>::N;  // elements per 16-byte vector
   const int lane = lane_id();
   const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -95,6 +98,20 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const int32_t* __restri
 #pragma unroll
   for (int m = 0; m < NVL; ++m)
     if (valid[m]) st16(yb + voff[m], Vec16<T>::narrow(acc[m]));
+  if (resid) {  // wave-uniform
+    const char* tb = reinterpret_cast<const char*>(target) + size_t(t) * row_bytes;
+    char* eb = reinterpret_cast<char*>(resid) + size_t(t) * row_bytes;
+#pragma unroll
+    for (int m = 0; m < NVL; ++m)
+      if (valid[m]) {
+        float yf[E], tf[E];
+        Vec16<T>::widen(Vec16<T>::narrow(acc[m]), yf);
+        Vec16<T>::widen(ld16(tb + voff[m]), tf);
+#pragma unroll
+        for (int e = 0; e < E; ++e) yf[e] -= tf[e];
+        st16(eb + voff[m], Vec16<T>::narrow(yf));
+      }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -259,27 +276,28 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const T* __restrict__
 
 template <typename T, int NVL>
 static void launch_gather_nvl(hipStream_t s, const int32_t* idx, const float* w, const void* V, void* y,
-                              int64_t ntok, int R, int nvec) {
+                              int64_t ntok, int R, int nvec, const void* target, void* resid) {
   constexpr int U = NVL <= 2 ? 8 : 4;
   dim3 grid(unsigned((ntok + 3) / 4), unsigned((nvec + 64 * NVL - 1) / (64 * NVL)));
   hipLaunchKernelGGL((gather_sum_kernel<T, NVL, U>), grid, dim3(256), 0, s, idx, w,
-                     static_cast<const T*>(V), static_cast<T*>(y), ntok, R, nvec);
+                     static_cast<const T*>(V), static_cast<T*>(y), ntok, R, nvec, static_cast<const T*>(target),
+                     static_cast<T*>(resid));
 }
 
 template <typename T>
 static void launch_gather_t(hipStream_t s, const int32_t* idx, const float* w, const void* V, void* y,
-                            int64_t ntok, int R, int nvec) {
+                            int64_t ntok, int R, int nvec, const void* target, void* resid) {
   // Vectors per lane: enough to cover a row in one column block when the row
   // is at most 256 vectors (4 KB); wider rows use several column blocks.
   const int per_lane = (nvec + 63) / 64;
   if (per_lane <= 1)
-    launch_gather_nvl<T, 1>(s, idx, w, V, y, ntok, R, nvec);
+    launch_gather_nvl<T, 1>(s, idx, w, V, y, ntok, R, nvec, target, resid);
   else if (per_lane == 2)
-    launch_gather_nvl<T, 2>(s, idx, w, V, y, ntok, R, nvec);
+    launch_gather_nvl<T, 2>(s, idx, w, V, y, ntok, R, nvec, target, resid);
   else if (per_lane == 3)
-    launch_gather_nvl<T, 3>(s, idx, w, V, y, ntok, R, nvec);
+    launch_gather_nvl<T, 3>(s, idx, w, V, y, ntok, R, nvec, target, resid);
   else
-    launch_gather_nvl<T, 4>(s, idx, w, V, y, ntok, R, nvec);
+    launch_gather_nvl<T, 4>(s, idx, w, V, y, ntok, R, nvec, target, resid);
 }
 
 template <typename T>
@@ -300,8 +318,10 @@ static void launch_gather_fp8_t(hipStream_t s, const int32_t* idx, const float* 
 }
 
 hipError_t launch_gather(hipStream_t s, int dtype, const int32_t* idx, const float* w, const void* V,
-                         void* y, int64_t ntok, int R, int d_value, bool fp8_values) {
+                         void* y, int64_t ntok, int R, int d_value, bool fp8_values, const void* target,
+                         void* resid) {
   if (fp8_values) {
+    if (resid) return hipErrorInvalidValue;
     const int nvec = d_value / 16;
     if (dtype == kBF16)
       launch_gather_fp8_t<bf16_t>(s, idx, w, V, y, ntok, R, nvec);
@@ -312,9 +332,9 @@ hipError_t launch_gather(hipStream_t s, int dtype, const int32_t* idx, const flo
   const int elem = dtype == kBF16 ? 2 : 4;
   const int nvec = d_value * elem / 16;
   if (dtype == kBF16)
-    launch_gather_t<bf16_t>(s, idx, w, V, y, ntok, R, nvec);
+    launch_gather_t<bf16_t>(s, idx, w, V, y, ntok, R, nvec, target, resid);
   else
-    launch_gather_t<float>(s, idx, w, V, y, ntok, R, nvec);
+    launch_gather_t<float>(s, idx, w, V, y, ntok, R, nvec, target, resid);
   return hipGetLastError();
 }
 

@@ -487,26 +487,6 @@ hipError_t launch_transpose(hipStream_t s, const void* in, int64_t rows, int64_t
   return hipGetLastError();
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void sub_storage_kernel(const T* __restrict__ a, const T* __restrict__ b,
-                                                          T* __restrict__ e, int64_t n) {
-  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256)
-    e[i] = to_storage<T>(to_f32<T>(a[i]) - to_f32<T>(b[i]));
-}
-
-hipError_t launch_sub_storage(hipStream_t s, int dtype, const void* a, const void* b, void* e, int64_t n) {
-  int64_t blocks = (n + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
-  if (blocks < 1) return hipGetLastError();
-  if (dtype == kBF16)
-    hipLaunchKernelGGL(sub_storage_kernel<bf16_t>, dim3(unsigned(blocks)), dim3(256), 0, s,
-                       static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b), static_cast<bf16_t*>(e), n);
-  else
-    hipLaunchKernelGGL(sub_storage_kernel<float>, dim3(unsigned(blocks)), dim3(256), 0, s,
-                       static_cast<const float*>(a), static_cast<const float*>(b), static_cast<float*>(e), n);
-  return hipGetLastError();
-}
-
 hipError_t launch_fill_f32(hipStream_t s, float* p, int64_t n, float v) {
   int64_t blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;

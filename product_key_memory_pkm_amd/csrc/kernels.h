@@ -12,8 +12,11 @@ constexpr int kBF16 = 1;
 
 // a6: y[t] = sum_r w[t, r] V[idx[t, r]] over R = h*k rows per token.
 // fp8_values: rows of [16-byte header (fp32 scale), d_value E4M3 codes].
+// resid (storage values only; may be null): resid[t] = y[t] as stored - target[t],
+// rounded to the storage type.
 hipError_t launch_gather(hipStream_t s, int dtype, const int32_t* idx, const float* w, const void* V,
-                         void* y, int64_t ntok, int R, int d_value, bool fp8_values);
+                         void* y, int64_t ntok, int R, int d_value, bool fp8_values,
+                         const void* target = nullptr, void* resid = nullptr);
 // fp8 value rows from rows in the storage dtype (d_value % 16 == 0).
 hipError_t launch_quantize_fp8(hipStream_t s, int dtype, const void* src, int64_t rows, int d_value, void* dst);
 
@@ -134,8 +137,6 @@ hipError_t launch_subkey_grad(hipStream_t s, int dtype, const int32_t* seg_start
                               int nkeys, float* dC, void* aux);
 
 hipError_t launch_fill_f32(hipStream_t s, float* p, int64_t n, float v);
-// e = a - b elementwise in the storage dtype (n elements, fp32 arithmetic, one rounding).
-hipError_t launch_sub_storage(hipStream_t s, int dtype, const void* a, const void* b, void* e, int64_t n);
 
 // Monitoring signals of a selection (idx, w [ntok, heads, k]): sub-key hit
 // counts, slots in use (all heads, then per head), entropy per (t, h) (may be

@@ -258,16 +258,49 @@ __device__ __forceinline__ uint64_t merge_top32(uint64_t a, uint64_t b, int lane
 
 // Packed operand layout, per codebook: [h][ceil(n/16) tiles][ksteps][64 lanes]
 // 16-byte fragments; lane (r, g) of (tile, kstep) holds row tile*16 + r,
-// elements kstep*KC + g*VE .. +VE (zeros past the last row or element).
+// elements kstep*KC + g*VE .. +VE (zeros past the last row or element).  The
+// packed C' follows the packed C in memory, so one index space covers both.
+//
+// For the IDW scores (norms != null) the blocks from pack_blocks on compute
+// |c|^2 of every sub-key row instead: C's rows, then C''s, into norms[] in
+// that order.  One wave per row; lane l squares the 16-byte vectors l, l + 64,
+// ... of the row, and a DPP reduction adds the lanes in a fixed order (the
+// result does not change from run to run).
 template <typename T>
-__global__ __launch_bounds__(256) void pack_keys_kernel(const T* __restrict__ C, int heads, int n, int half,
-                                                        int nks, u32x4* __restrict__ out) {
+__global__ __launch_bounds__(256) void pack_keys_kernel(const T* __restrict__ C, int n1, const T* __restrict__ Cp,
+                                                        int n2, int heads, int half, int nks, int pack_blocks,
+                                                        u32x4* __restrict__ out, float* __restrict__ norms) {
   using TR = ScoreTraits<T>;
-  const int ntile = (n + 15) / 16;
-  const int64_t total = int64_t(heads) * ntile * nks * 64;
-  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < total; i += int64_t(gridDim.x) * 256) {
-    const int lane = int(i & 63);
-    const int64_t fr = i >> 6;
+  if (int(blockIdx.x) >= pack_blocks) {  // block-uniform
+    constexpr int VE = Vec16<T>::N;
+    const int lane = lane_id();
+    const int vpr = half / VE;
+    const int64_t rows1 = int64_t(heads) * n1, rows = rows1 + int64_t(heads) * n2;
+    const int64_t nw = int64_t(gridDim.x - pack_blocks) * 4;
+    for (int64_t r = int64_t(blockIdx.x - pack_blocks) * 4 + (threadIdx.x >> 6); r < rows; r += nw) {
+      const T* c = r < rows1 ? C + size_t(r) * half : Cp + size_t(r - rows1) * half;
+      float a = 0.f;
+      for (int v = lane; v < vpr; v += 64) {
+        float x[VE];
+        Vec16<T>::widen(ld16(c + size_t(v) * VE), x);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) a = fmaf(x[e], x[e], a);
+      }
+      a = wave_sum_dpp(a);
+      if (lane == 0) norms[r] = a;
+    }
+    return;
+  }
+  const int64_t total1 = int64_t(heads) * ((n1 + 15) / 16) * nks * 64;
+  const int64_t total = total1 + int64_t(heads) * ((n2 + 15) / 16) * nks * 64;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < total; i += int64_t(pack_blocks) * 256) {
+    const bool second = i >= total1;
+    const T* src = second ? Cp : C;
+    const int n = second ? n2 : n1;
+    const int64_t j = second ? i - total1 : i;
+    const int ntile = (n + 15) / 16;
+    const int lane = int(j & 63);
+    const int64_t fr = j >> 6;
     const int ks = int(fr % nks);
     const int64_t tl = fr / nks;
     const int tile = int(tl % ntile);
@@ -275,7 +308,7 @@ __global__ __launch_bounds__(256) void pack_keys_kernel(const T* __restrict__ C,
     const int row = tile * 16 + (lane & 15);
     const int kk = ks * TR::KC + (lane >> 4) * TR::VE;
     u32x4 v = {0, 0, 0, 0};
-    if (row < n && kk < half) v = ld16(C + (size_t(hh) * n + row) * half + kk);
+    if (row < n && kk < half) v = ld16(src + (size_t(hh) * n + row) * half + kk);
     out[i] = v;
   }
 }
@@ -588,33 +621,6 @@ void launch_t(hipStream_t s, const Plan& pl, const void* q, int64_t ntok, int he
     launch_tm<T, 16>(s, pl, q, ntok, heads, dq, C, Cp, nk, nk2, k, sub_idx, sub_score, cc1, cc2);
 }
 
-// |c|^2 of every sub-key row, for the IDW scores: rows [0, rows1) of C, then
-// rows [rows1, rows1 + rows2) of C', into out[] in that order.  One wave per
-// row; lane l squares the 16-byte vectors l, l + 64, ... of the row, and a DPP
-// reduction adds the lanes in a fixed order (the result does not change from
-// run to run).
-template <typename T>
-__global__ __launch_bounds__(256) void subkey_norms_kernel(const T* __restrict__ C, int64_t rows1,
-                                                           const T* __restrict__ Cp, int64_t rows2, int half,
-                                                           float* __restrict__ out) {
-  constexpr int VE = Vec16<T>::N;
-  const int lane = lane_id();
-  const int vpr = half / VE;
-  const int64_t nw = int64_t(gridDim.x) * (blockDim.x >> 6);
-  for (int64_t r = int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6); r < rows1 + rows2; r += nw) {
-    const T* c = r < rows1 ? C + size_t(r) * half : Cp + size_t(r - rows1) * half;
-    float a = 0.f;
-    for (int v = lane; v < vpr; v += 64) {
-      float x[VE];
-      Vec16<T>::widen(ld16(c + size_t(v) * VE), x);
-#pragma unroll
-      for (int e = 0; e < VE; ++e) a = fmaf(x[e], x[e], a);
-    }
-    a = wave_sum_dpp(a);
-    if (lane == 0) out[r] = a;
-  }
-}
-
 }  // namespace
 
 bool score_topk_supported(int dtype, int half, int nkeys) {
@@ -647,34 +653,26 @@ hipError_t launch_score_topk(hipStream_t s, int dtype, const void* q, int64_t nt
   const int nks = pl.half_pad / KC;
   u32x4* P1 = static_cast<u32x4*>(packed);
   u32x4* P2 = P1 + size_t(heads) * ((nk + 15) / 16) * nks * 64;
-  auto pack = [&](const void* src, int n, u32x4* dst) {
-    const int64_t total = int64_t(heads) * ((n + 15) / 16) * nks * 64;
-    int64_t b = (total + 255) / 256;
-    if (b > 4096) b = 4096;
-    if (dtype == kBF16)
-      hipLaunchKernelGGL(pack_keys_kernel<bf16_t>, dim3(unsigned(b)), dim3(256), 0, s,
-                         static_cast<const bf16_t*>(src), heads, n, half, nks, dst);
-    else
-      hipLaunchKernelGGL(pack_keys_kernel<float>, dim3(unsigned(b)), dim3(256), 0, s,
-                         static_cast<const float*>(src), heads, n, half, nks, dst);
-  };
-  pack(C, nk, P1);
-  pack(Cp, nk2, P2);
+  const int64_t total = int64_t(heads) * ((nk + 15) / 16 + (nk2 + 15) / 16) * nks * 64;
+  int64_t pb = (total + 255) / 256;
+  if (pb > 4096) pb = 4096;
   float* cc1 = nullptr;
   float* cc2 = nullptr;
-  if (idw) {
-    cc1 = reinterpret_cast<float*>(P2 + size_t(heads) * ((nk2 + 15) / 16) * nks * 64);
+  int64_t nb = 0;
+  if (idw) {  // |c|^2 after the packed operands: C's rows, then C''s
+    cc1 = reinterpret_cast<float*>(P1 + total);
     cc2 = cc1 + size_t(heads) * nk;
-    const int64_t rows1 = int64_t(heads) * nk, rows2 = int64_t(heads) * nk2;
-    int64_t b = (rows1 + rows2 + 3) / 4;  // four waves (rows) per block
-    if (b > 8192) b = 8192;
-    if (dtype == kBF16)
-      hipLaunchKernelGGL(subkey_norms_kernel<bf16_t>, dim3(unsigned(b)), dim3(256), 0, s,
-                         static_cast<const bf16_t*>(C), rows1, static_cast<const bf16_t*>(Cp), rows2, half, cc1);
-    else
-      hipLaunchKernelGGL(subkey_norms_kernel<float>, dim3(unsigned(b)), dim3(256), 0, s,
-                         static_cast<const float*>(C), rows1, static_cast<const float*>(Cp), rows2, half, cc1);
+    nb = (int64_t(heads) * (nk + nk2) + 3) / 4;  // four waves (rows) per block
+    if (nb > 4096) nb = 4096;
   }
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(pack_keys_kernel<bf16_t>, dim3(unsigned(pb + nb)), dim3(256), 0, s,
+                       static_cast<const bf16_t*>(C), nk, static_cast<const bf16_t*>(Cp), nk2, heads, half, nks,
+                       int(pb), P1, cc1);
+  else
+    hipLaunchKernelGGL(pack_keys_kernel<float>, dim3(unsigned(pb + nb)), dim3(256), 0, s,
+                       static_cast<const float*>(C), nk, static_cast<const float*>(Cp), nk2, heads, half, nks,
+                       int(pb), P1, cc1);
   if (dtype == kBF16)
     launch_t<bf16_t>(s, pl, q, ntok, heads, dq, P1, P2, nk, nk2, k, sub_idx, sub_score, cc1, cc2);
   else
