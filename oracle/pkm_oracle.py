@@ -404,7 +404,8 @@ def dequantize_rows_fp8(scale: np.ndarray, codes: np.ndarray) -> np.ndarray:
     return np.asarray(scale, dtype=np.float64)[:, None] * e4m3_decode(codes)
 
 
-def fwpkm_chunk(cfg, q: np.ndarray, C: np.ndarray, Cp: np.ndarray, V: np.ndarray, target: np.ndarray, lr: float):
+def fwpkm_chunk(cfg, q: np.ndarray, C: np.ndarray, Cp: np.ndarray, V: np.ndarray, target: np.ndarray, lr: float,
+                dense: bool = True):
     """One chunk of FwPKM memorization (FwPKM page, sections 2.1-2.2: the value table is a fast weight,
     written during inference by gradient descent on a local reconstruction loss toward lookahead
     targets v_{t+1}; sparse retrieval with IDW scores).
@@ -414,15 +415,20 @@ def fwpkm_chunk(cfg, q: np.ndarray, C: np.ndarray, Cp: np.ndarray, V: np.ndarray
     stored in the storage dtype; loss 1/2 sum_t ||y_t - target_t||^2 with the residual e = y - target
     also in the storage dtype (as an upstream gradient is); only the value rows are written:
     V[r] <- V[r] - lr * sum over the lookups of r of w * e_t, rounded to storage.  Returns
-    (y as stored, V after the write, the lookup dict), float64.
+    (y as stored, V after the write, the lookup dict), float64.  ``dense=False`` (large tables):
+    only the selected rows are read and returned, as (y, (their ids ascending, their new values),
+    the lookup dict).
     """
     sel = lookup(cfg, decode(q, cfg.dtype), decode(C, cfg.dtype), decode(Cp, cfg.dtype), score="idw")
     y = round_to_storage(gather_sum(sel["rows"], sel["w"], V, cfg.dtype), cfg.dtype)
     e = round_to_storage(y - decode(target, cfg.dtype), cfg.dtype)
     uniq = np.unique(sel["rows"])
     g = value_grad_rows(sel["rows"], sel["w"], e, F64, uniq)
+    new_rows = round_to_storage(decode(V[uniq], cfg.dtype) - lr * g, cfg.dtype)
+    if not dense:
+        return y, (uniq, new_rows), sel
     Vn = decode(V, cfg.dtype).copy()
-    Vn[uniq] = round_to_storage(Vn[uniq] - lr * g, cfg.dtype)
+    Vn[uniq] = new_rows
     return y, Vn, sel
 
 

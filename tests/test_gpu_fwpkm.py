@@ -307,3 +307,49 @@ def test_fwpkm_chunk_is_deterministic():
         outs.append((y, G, w, P.to_f64(V_dev)))
     for a, b in zip(*outs):
         np.testing.assert_array_equal(a, b)
+
+
+def test_fwpkm_chunk_at_the_benchmark_configuration():
+    # the launch configuration bench.py times: 512 tokens, one head, dq = 512, 1024 x 1024 slots,
+    # k = 8, 1600-wide bf16 value rows; the oracle reads only the selected rows (dense=False)
+    cfg = _cfg(T=512, heads=1, dq=512, n_keys=1024, n_keys2=1024, topk=8, d_value=1600, dtype="bf16", seed=50)
+    lr = 0.1
+    note(f"fwpkm chunk at the benchmark configuration: {cfg}")
+    half = cfg.dq // 2
+    q, target = pi.fwpkm_stream(cfg.seed, cfg.T, cfg.dq, cfg.d_value, cfg.dtype)
+    C = pi.random_array(cfg.seed, 11, (1, cfg.n_keys, half), dtype=cfg.dtype, std=half ** -0.5)
+    Cp = pi.random_array(cfg.seed, 12, (1, cfg.n_keys2, half), dtype=cfg.dtype, std=half ** -0.5)
+    V = _values(cfg)
+    layer = layer_for(cfg, score="idw")
+    V_dev = to_dev(V)
+    y_g, G, w_g = _run_chunk(layer, q, C, Cp, V_dev, target, lr)
+    y_o, (ids, rows_new), sel = O.fwpkm_chunk(cfg, q, C, Cp, V, target, lr, dense=False)
+    qd, Cd, Cpd = O.decode(q, cfg.dtype), O.decode(C, cfg.dtype), O.decode(Cp, cfg.dtype)
+    q1, q2 = O.split_heads(qd, 1, cfg.dq)
+    s1, s2 = O.subkey_scores_idw(q1, q2, Cd, Cpd)
+
+    def score_of(r):
+        return P.full_scores(r.astype(np.int64), s1, s2, cfg.n_keys2)
+
+    slack = 2 * (_score_err(q1, Cd, sel["sub_val1"]) + _score_err(q2, Cpd, sel["sub_val2"]))
+    valid, exact_set, _ = P.check_selection(G, sel["rows_k1"], sel["scores_k1"], score_of, cfg.slots, cfg.topk,
+                                            slack)
+    assert valid.all()
+    tol = P.TOL[cfg.dtype]
+    w_ref = O.softmax(score_of(G), cfg.temperature)
+    assert np.abs(w_g - w_ref).max() <= tol * max(1e-3, float(np.abs(w_ref).max()))
+    same = exact_set.all(-1)
+    assert same.mean() > 0.98
+    assert P.row_rel_err(y_g[same], y_o[same]).max() <= tol
+    # value rows: the written rows (those of tokens whose sets agree), and untouched rows unchanged
+    bad = np.union1d(G[~same].reshape(-1), sel["rows"][~same].reshape(-1))
+    good = ~np.isin(ids, bad)
+    assert good.mean() > 0.98
+    V_after = V_dev[torch.from_numpy(ids[good]).cuda()]
+    err = P.row_rel_err(P.to_f64(V_after), rows_new[good])
+    assert err.max() <= tol, err.max()
+    assert (rows_new[good] != O.decode(V[ids[good]], cfg.dtype)).any(axis=1).mean() > 0.9
+    g = np.random.default_rng(0)
+    sample = np.setdiff1d(g.integers(0, cfg.slots, 200_000), np.union1d(ids, G.reshape(-1)))
+    np.testing.assert_array_equal(V_dev[torch.from_numpy(sample).cuda()].cpu().view(torch.int16).numpy(),
+                                  V[sample].view(np.int16))

@@ -624,3 +624,20 @@ def test_fwpkm_chunk_write_is_the_gradient_step_of_the_reconstruction_loss():
             assert abs(fd - g[r, c]) <= 1e-6 * max(1.0, abs(fd))
     untouched = np.setdiff1d(np.arange(nk * nk), np.unique(sel["rows"]))
     np.testing.assert_array_equal(Vn[untouched], V[untouched])
+
+
+def test_fwpkm_chunk_sparse_output_is_the_dense_table_at_the_selected_rows():
+    rng = np.random.default_rng(42)
+    h, dq, nk, k, T, dv, lr = 2, 16, 12, 4, 30, 8, 0.7
+    cfg = _Cfg(heads=h, dq=dq, topk=k, n_keys=nk, n_keys2=nk, temperature=1.0, dtype=O.BF16)
+    q = pi.f32_to_bf16_bits(rng.standard_normal((T, h * dq)).astype(np.float32))
+    C = pi.f32_to_bf16_bits(rng.standard_normal((h, nk, dq // 2)).astype(np.float32))
+    Cp = pi.f32_to_bf16_bits(rng.standard_normal((h, nk, dq // 2)).astype(np.float32))
+    V = pi.f32_to_bf16_bits(rng.standard_normal((nk * nk, dv)).astype(np.float32))
+    tgt = pi.f32_to_bf16_bits(rng.standard_normal((T, dv)).astype(np.float32))
+    y, Vn, sel = O.fwpkm_chunk(cfg, q, C, Cp, V, tgt, lr)
+    y2, (ids, rows_new), sel2 = O.fwpkm_chunk(cfg, q, C, Cp, V, tgt, lr, dense=False)
+    np.testing.assert_array_equal(y2, y)
+    np.testing.assert_array_equal(ids, np.unique(sel["rows"]))
+    np.testing.assert_array_equal(rows_new, Vn[ids])
+    assert (Vn[ids] != O.decode(V, O.BF16)[ids]).any()
