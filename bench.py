@@ -5,7 +5,8 @@ per-half scores and top-k, k x k merge + softmax, value gather-sum) and
 backward (value gradient into the touched rows, softmax backward, sub-key
 gradients, BatchNorm backward, dWq, dx).  Workload: the paper-scale memory
 layer (32,768 tokens of width 1600, h=4, dq=512, 1024 x 1024 = 1,048,576 slots,
-k=32, bf16 storage, fp32 accumulation, BatchNorm), seeded synthetic inputs.
+k=32, bf16 storage, fp32 accumulation, BatchNorm), seeded synthetic inputs.  Beside
+it, the fast-weight memorization (FwPKM) of one stream and of a batch of streams.
 
 Prints one JSON line: tokens/s, the roofline of the step's dominant kernel and the
 CPU oracle's rate on a bounded sample.  ``--gpus`` above 1 is
@@ -69,7 +70,9 @@ def parse():
                     help="after one step, one launch of the Adam-fused value kernel and nothing else (for profilers)")
     ap.add_argument("--profile-fwpkm", type=int, default=0,
                     help="run this many fast-weight memorization chunks and nothing else (for profilers)")
-    ap.add_argument("--no-fwpkm", action="store_true", help="skip the fast-weight memorization leg")
+    ap.add_argument("--profile-fwpkm-batch", action="store_true",
+                    help="run the batched fast-weight memorization calls once and nothing else (for profilers)")
+    ap.add_argument("--no-fwpkm", action="store_true", help="skip the fast-weight memorization legs")
     return ap.parse_args()
 
 
@@ -80,6 +83,9 @@ FWPKM_CHUNK = 512
 FWPKM_CHUNKS = 64
 FWPKM_TOPK = 8
 FWPKM_LR = 0.1
+# and a batch of independent streams, each with its own copy of the table, one chunk of each per call
+FWPKM_STREAMS = 8
+FWPKM_BATCH_CHUNKS = 16
 
 
 def fwpkm_chunk_bytes(chunk, k, dv, e, touched):
@@ -194,6 +200,40 @@ def main():
             pkm_fwpkm_chunk(st["m"].handle, c0, st["q"][sl], st["C"], st["Cp"], st["V"], st["target"][sl],
                             FWPKM_LR, st["y"][sl], st["idx"], st["w"], st["ws"])
 
+    def fwpkm_batch_setup():
+        """A batch of FWPKM_STREAMS streams: per call one chunk of each, stream-major (pkm_fwpkm_chunk)."""
+        nb, c0, nc = FWPKM_STREAMS, FWPKM_CHUNK, FWPKM_BATCH_CHUNKS
+        mf = ProductKeyMemory(cfg.d, 1, cfg.dq, cfg.n_keys, cfg.n_keys2, FWPKM_TOPK, cfg.d_value, dtype=cfg.dtype,
+                              bn=False, score="idw")
+        qs, ts = [], []
+        for b in range(nb):
+            qn, tn = pi.fwpkm_stream(cfg.seed + 200 + b, nc * c0, cfg.dq, cfg.d_value, cfg.dtype)
+            qs.append(qn.reshape(nc, c0, -1))
+            ts.append(tn.reshape(nc, c0, -1))
+        # [chunk call, stream, token, feature]: the call's tokens stream-major
+        qa = np.ascontiguousarray(np.stack(qs, axis=1)).reshape(nc, nb * c0, -1)
+        ta = np.ascontiguousarray(np.stack(ts, axis=1)).reshape(nc, nb * c0, -1)
+        Vb = torch.empty((nb * cfg.slots, cfg.d_value), dtype=m.storage, device="cuda")
+        for b in range(nb):
+            Vb[b * cfg.slots:(b + 1) * cfg.slots].copy_(V)
+        return {"m": mf, "q": dev(qa), "target": dev(ta), "C": C[:1].contiguous(), "Cp": Cp[:1].contiguous(),
+                "V": Vb, "y": torch.empty((nc, nb * c0, cfg.d_value), dtype=m.storage, device="cuda"),
+                "idx": torch.empty((nb * c0, 1, FWPKM_TOPK), dtype=torch.int32, device="cuda"),
+                "w": torch.empty((nb * c0, 1, FWPKM_TOPK), dtype=torch.float32, device="cuda"),
+                "ws": mf.workspace(nb * c0, PKM_WS_FWPKM_CHUNK)}
+
+    def fwpkm_batch_run(st, ncalls):
+        for c in range(ncalls):
+            pkm_fwpkm_chunk(st["m"].handle, FWPKM_STREAMS * FWPKM_CHUNK, st["q"][c], st["C"], st["Cp"], st["V"],
+                            st["target"][c], FWPKM_LR, st["y"][c], st["idx"], st["w"], st["ws"],
+                            streams=FWPKM_STREAMS)
+
+    if args.profile_fwpkm_batch:
+        st = fwpkm_batch_setup()
+        fwpkm_batch_run(st, FWPKM_BATCH_CHUNKS)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_fwpkm_batch": FWPKM_BATCH_CHUNKS}), flush=True)
+        return
     if args.profile_fwpkm:
         st = fwpkm_setup()
         fwpkm_run(st, min(args.profile_fwpkm, FWPKM_CHUNKS))
@@ -352,6 +392,27 @@ def main():
               "host_enqueue_ms_per_chunk": host_s * 1e3 / FWPKM_CHUNKS,
               "touched_rows_last_chunk": touched_c, "alg_bytes_per_chunk": cb,
               "achieved_GBs_whole_chunk": cb / (ms_chunk * 1e-3) / 1e9}
+        del st
+        torch.cuda.empty_cache()
+        # a batch of independent streams: one chunk of each per call
+        st = fwpkm_batch_setup()
+        fwpkm_batch_run(st, FWPKM_BATCH_CHUNKS)
+        torch.cuda.synchronize()
+        start.record()
+        fwpkm_batch_run(st, FWPKM_BATCH_CHUNKS)
+        end.record()
+        torch.cuda.synchronize()
+        ms_b = start.elapsed_time(end)
+        ntok_b = FWPKM_STREAMS * FWPKM_CHUNK * FWPKM_BATCH_CHUNKS
+        touched_b = int(torch.unique(st["idx"]).numel())
+        cb_b = fwpkm_chunk_bytes(FWPKM_STREAMS * FWPKM_CHUNK, FWPKM_TOPK, cfg.d_value, e_, touched_b)
+        ms_call = ms_b / FWPKM_BATCH_CHUNKS
+        fw["batch"] = {"workload": (f"{FWPKM_STREAMS} streams x {FWPKM_BATCH_CHUNKS} chunks of {FWPKM_CHUNK} tokens, "
+                                    f"one chunk of each stream per call, each stream on its own table "
+                                    f"({FWPKM_STREAMS} x {cfg.slots} slots); otherwise as above"),
+                       "tokens_per_s": ntok_b / (ms_b * 1e-3), "ms_per_call": ms_call,
+                       "touched_rows_last_call": touched_b, "alg_bytes_per_call": cb_b,
+                       "achieved_GBs_whole_call": cb_b / (ms_call * 1e-3) / 1e9}
         del st
         torch.cuda.empty_cache()
     # the per-half scoring + top-k kernel alone (its MFMA roofline)

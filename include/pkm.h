@@ -334,23 +334,29 @@ pkm_status pkm_stage_query_grad(pkm_handle_t handle, void* stream, int64_t T, co
 /* One chunk of FwPKM memorization ("Fast-weight Product Key Memory", sections
  * 2.1 and 2.2: the value table is a fast weight that the layer itself writes
  * while it reads, by a gradient step on a local reconstruction loss toward the
- * caller's lookahead targets).  For the T tokens of the chunk, with the
- * handle's IDW scores (score_fn must be PKM_SCORE_IDW, else
- * PKM_ERR_UNSUPPORTED; value_format must be PKM_VALUES_STORAGE):
- *   idx, w  = the selection of q (as pkm_stage_score_topk + pkm_stage_merge_softmax);
+ * caller's lookahead targets).  The call holds one chunk of each of `streams`
+ * independent streams (a batch of sequences, each with its own value table;
+ * the sub-keys are shared): T = streams * chunk tokens, stream b's tokens are
+ * rows [b*T/streams, (b+1)*T/streams) of q, target and y, and its table is rows
+ * [b*|C|*|C'|, (b+1)*|C|*|C'|) of V.  For every token, with the handle's IDW
+ * scores (score_fn must be PKM_SCORE_IDW, else PKM_ERR_UNSUPPORTED;
+ * value_format must be PKM_VALUES_STORAGE):
+ *   idx, w  = the selection of q (as pkm_stage_score_topk + pkm_stage_merge_softmax),
+ *             idx as rows of V (stream b's rows offset by b*|C|*|C'|);
  *   y[t]    = sum over (h, s) of w V[idx] from V BEFORE the write, rounded to storage;
  *   e[t]    = y[t] - target[t], rounded to storage (the gradient of 1/2 ||y - target||^2);
  *   V[r]    = V[r] - lr * sum over the lookups c of r of w[c] e[t(c)], fp32, rounded
  *             to storage, for every selected row r (no other row is read or written).
  * The per-row sums run in a fixed order, so the result is deterministic.
- * Device pointers: q [T, h*dq], C [h, |C|, dq/2], Cp [h, |C'|, dq/2], V [|C|*|C'|,
- * d_value] (updated in place), target and y [T, d_value]: storage dtype;
- * idx int32 and w fp32 [T, h, k] (outputs, ordered as in pkm_saved).  lr finite
- * >= 0.  ws >= pkm_workspace_size(handle, T, PKM_WS_FWPKM_CHUNK).  Chunks that
- * follow one another are calls that follow one another on the stream. */
-pkm_status pkm_fwpkm_chunk(pkm_handle_t handle, void* stream, int64_t T, const void* q, const void* C,
-                           const void* Cp, void* V, const void* target, float lr, void* y, int32_t* idx,
-                           float* w, void* ws, size_t ws_bytes);
+ * Device pointers: q [T, h*dq], C [h, |C|, dq/2], Cp [h, |C'|, dq/2], V
+ * [streams*|C|*|C'|, d_value] (updated in place), target and y [T, d_value]:
+ * storage dtype; idx int32 and w fp32 [T, h, k] (outputs, ordered as in
+ * pkm_saved).  streams >= 1 dividing T, streams*|C|*|C'| < 2^31; lr finite >= 0.
+ * ws >= pkm_workspace_size(handle, T, PKM_WS_FWPKM_CHUNK).  Chunks that follow
+ * one another are calls that follow one another on the stream. */
+pkm_status pkm_fwpkm_chunk(pkm_handle_t handle, void* stream, int64_t T, int64_t streams, const void* q,
+                           const void* C, const void* Cp, void* V, const void* target, float lr, void* y,
+                           int32_t* idx, float* w, void* ws, size_t ws_bytes);
 
 #ifdef __cplusplus
 }

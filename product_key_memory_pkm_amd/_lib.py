@@ -79,7 +79,7 @@ _SIGS = {
     "pkm_stage_subkey_grad": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
     "pkm_stage_query_grad": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_saved), _VP, _VP, _VP, _VP,
                              _VP, _SZ],
-    "pkm_fwpkm_chunk": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP, _VP, _VP, _VP, _SZ],
+    "pkm_fwpkm_chunk": [_VP, _VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP, _VP, _VP, _VP, _SZ],
 }
 EXPORTED = sorted(list(_SIGS) + ["pkm_status_string", "pkm_last_error"])
 
@@ -349,13 +349,15 @@ def pkm_stage_query_grad(h, T, dq, x, Wq, bn_gamma, saved: dict, dWq, dgamma, db
                                       _nbytes(ws)), "pkm_stage_query_grad")
 
 
-def pkm_fwpkm_chunk(h, T, q, C, Cp, V, target, lr, y, idx, w, ws):
-    """One FwPKM memorization chunk (pkm.h): select with IDW scores, y from V before the write, then
-    V[r] -= lr * sum w (y - target) over the lookups of each selected row (V updated in place)."""
+def pkm_fwpkm_chunk(h, T, q, C, Cp, V, target, lr, y, idx, w, ws, streams=1):
+    """One FwPKM memorization chunk of each of ``streams`` streams (pkm.h): select with IDW scores, y from
+    V before the write, then V[r] -= lr * sum w (y - target) over the lookups of each selected row (V
+    updated in place; stream b owns the b-th block of |C|*|C'| rows of V and the b-th block of T/streams
+    tokens)."""
     st = h.storage
     for n, t in (("q", q), ("C", C), ("Cp", Cp), ("V", V), ("target", target), ("y", y)):
         _dt(t, st, n)
     _dt(idx, torch.int32, "idx")
     _dt(w, torch.float32, "w")
-    _check(_invoke("pkm_fwpkm_chunk", h, T, _ptr(q), _ptr(C), _ptr(Cp), _ptr(V), _ptr(target), float(lr), _ptr(y),
-                   _ptr(idx), _ptr(w), _ptr(ws), _nbytes(ws)), "pkm_fwpkm_chunk")
+    _check(_invoke("pkm_fwpkm_chunk", h, T, int(streams), _ptr(q), _ptr(C), _ptr(Cp), _ptr(V), _ptr(target),
+                   float(lr), _ptr(y), _ptr(idx), _ptr(w), _ptr(ws), _nbytes(ws)), "pkm_fwpkm_chunk")

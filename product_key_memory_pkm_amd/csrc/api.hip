@@ -245,10 +245,10 @@ pkm_status run_score(const pkm_handle_s* h, hipStream_t s, int64_t T, const void
 }
 
 pkm_status run_merge(const pkm_handle_s* h, hipStream_t s, int64_t T, const int32_t* sub_idx, const float* sub_score,
-                     int32_t* idx, float* w, float* score) {
+                     int32_t* idx, float* w, float* score, int64_t group_tokens = 0) {
   const pkm_config& c = h->cfg;
   PKM_HIP(launch_merge_softmax(s, sub_idx, sub_score, T * c.heads, c.topk, c.n_keys2, 1.0f / c.temperature, idx, w,
-                               score),
+                               score, group_tokens * c.heads, int64_t(c.n_keys) * c.n_keys2),
           "candidate merge / softmax");
   return PKM_OK;
 }
@@ -261,8 +261,9 @@ pkm_status run_gather(const pkm_handle_s* h, hipStream_t s, int64_t T, const int
   return PKM_OK;
 }
 
-int row_sort_passes(const pkm_handle_s* h) {
-  const int p = (h->row_bits + 7) / 8;
+// bits < 0: the handle's row ids; otherwise keys below 2^bits (several tables).
+int row_sort_passes(const pkm_handle_s* h, int bits = -1) {
+  const int p = ((bits < 0 ? h->row_bits : bits) + 7) / 8;
   return p < 1 ? 1 : p;
 }
 
@@ -270,21 +271,23 @@ int row_sort_passes(const pkm_handle_s* h) {
 // (k0, v0) or (k1, v1) depending on the number of radix passes; a small batch
 // is sorted and segmented in one workgroup, straight into the same place.
 pkm_status run_row_groups(const pkm_handle_s* h, hipStream_t s, int64_t T, const int32_t* idx, int32_t* touched,
-                          int64_t* n_touched, void* ws) {
+                          int64_t* n_touched, void* ws, int bits = -1) {
   const pkm_config& c = h->cfg;
   const BwdLayout L = bwd_layout(h, T);
   const int64_t N = T * c.heads * c.topk;
+  const int key_bits = bits < 0 ? h->row_bits : bits;
   if (N <= kSmallSortMax) {
-    const bool out1 = row_sort_passes(h) % 2 == 0;
-    PKM_HIP(launch_sort_segments_small(s, reinterpret_cast<const uint32_t*>(idx), N, h->row_bits,
+    const bool out1 = row_sort_passes(h, key_bits) % 2 == 0;
+    const VgPlan plan = value_grad_plan(at<void>(ws, L.aux), N, c.d_value);
+    PKM_HIP(launch_sort_segments_small(s, reinterpret_cast<const uint32_t*>(idx), N, key_bits,
                                        at<uint32_t>(ws, out1 ? L.k1 : L.k0), at<int32_t>(ws, out1 ? L.v1 : L.v0),
-                                       at<int32_t>(ws, L.seg), touched, n_touched),
-            "row sort and segments (one workgroup)");
+                                       at<int32_t>(ws, L.seg), touched, n_touched, &plan),
+            "row sort, segments and long-run plan (one workgroup)");
     return PKM_OK;
   }
   bool in1 = false;
   PKM_HIP(launch_radix_sort_from(s, reinterpret_cast<const uint32_t*>(idx), at<uint32_t>(ws, L.k0),
-                                 at<int32_t>(ws, L.v0), at<uint32_t>(ws, L.k1), at<int32_t>(ws, L.v1), N, h->row_bits,
+                                 at<int32_t>(ws, L.v0), at<uint32_t>(ws, L.k1), at<int32_t>(ws, L.v1), N, key_bits,
                                  at<void>(ws, L.sort_tmp), &in1),
           "row sort");
   const uint32_t* sk = at<uint32_t>(ws, in1 ? L.k1 : L.k0);
@@ -295,24 +298,26 @@ pkm_status run_row_groups(const pkm_handle_s* h, hipStream_t s, int64_t T, const
 
 pkm_status run_value_grad_grouped(const pkm_handle_s* h, hipStream_t s, int64_t T, const float* w, const void* dY,
                                   const void* V, float* dV, float* dw, const int64_t* n_touched, void* ws,
-                                  const VgAdam* adam = nullptr) {
+                                  const VgAdam* adam = nullptr, int bits = -1) {
   const pkm_config& c = h->cfg;
   const BwdLayout L = bwd_layout(h, T);
   const int64_t N = T * c.heads * c.topk;
-  const bool in1 = row_sort_passes(h) % 2 == 0;  // passes alternate (k0,v0), (k1,v1), ...
+  const bool in1 = row_sort_passes(h, bits) % 2 == 0;  // passes alternate (k0,v0), (k1,v1), ...
   const uint32_t* sk = at<uint32_t>(ws, in1 ? L.k1 : L.k0);
   const int32_t* sv = at<int32_t>(ws, in1 ? L.v1 : L.v0);
+  // a grouping of at most kSmallSortMax lookups came with the long-run plan in aux
   PKM_HIP(launch_value_grad(s, c.dtype, at<int32_t>(ws, L.seg), n_touched, N, sk, sv, w, dY, V, dV, dw,
-                            c.heads * c.topk, c.d_value, c.accumulate_dv != 0, at<void>(ws, L.aux), adam),
+                            c.heads * c.topk, c.d_value, c.accumulate_dv != 0, at<void>(ws, L.aux), adam,
+                            N <= kSmallSortMax),
           adam ? "value gradient with Adam step" : "value gradient");
   return PKM_OK;
 }
 
 pkm_status run_value_grad(const pkm_handle_s* h, hipStream_t s, int64_t T, const int32_t* idx, const float* w,
                           const void* dY, const void* V, float* dV, int32_t* touched, int64_t* n_touched, float* dw,
-                          void* ws, const VgAdam* adam = nullptr) {
-  PKM_TRY(run_row_groups(h, s, T, idx, touched, n_touched, ws));
-  return run_value_grad_grouped(h, s, T, w, dY, V, dV, dw, n_touched, ws, adam);
+                          void* ws, const VgAdam* adam = nullptr, int bits = -1) {
+  PKM_TRY(run_row_groups(h, s, T, idx, touched, n_touched, ws, bits));
+  return run_value_grad_grouped(h, s, T, w, dY, V, dV, dw, n_touched, ws, adam, bits);
 }
 
 // Adam hyper-parameters -> the kernel's constants (bias corrections in double).
@@ -941,9 +946,9 @@ pkm_status pkm_stage_query_grad(pkm_handle_t handle, void* stream, int64_t T, co
 
 }  // extern "C"
 
-pkm_status pkm_fwpkm_chunk(pkm_handle_t handle, void* stream, int64_t T, const void* q, const void* C, const void* Cp,
-                           void* V, const void* target, float lr, void* y, int32_t* idx, float* w, void* ws,
-                           size_t ws_bytes) {
+pkm_status pkm_fwpkm_chunk(pkm_handle_t handle, void* stream, int64_t T, int64_t streams, const void* q,
+                           const void* C, const void* Cp, void* V, const void* target, float lr, void* y, int32_t* idx,
+                           float* w, void* ws, size_t ws_bytes) {
   PKM_TRY(check_handle(handle));
   PKM_TRY(need_storage_values(handle));
   if (handle->cfg.score_fn != PKM_SCORE_IDW)
@@ -958,9 +963,17 @@ pkm_status pkm_fwpkm_chunk(pkm_handle_t handle, void* stream, int64_t T, const v
   PKM_TRY(need(idx, "idx"));
   PKM_TRY(need(w, "w"));
   if (!(std::isfinite(lr) && lr >= 0.f)) return fail(PKM_ERR_INVALID_ARG, "lr must be finite and >= 0");
+  if (streams < 1) return fail(PKM_ERR_INVALID_ARG, "streams = %lld < 1", (long long)streams);
+  if (T % streams) return fail(PKM_ERR_INVALID_ARG, "T = %lld is not a multiple of streams = %lld", (long long)T,
+                               (long long)streams);
+  const pkm_config& c = handle->cfg;
+  const int64_t rows = streams * int64_t(c.n_keys) * c.n_keys2;
+  if (rows >= (int64_t(1) << 31))
+    return fail(PKM_ERR_UNSUPPORTED, "streams * |C| * |C'| = %lld does not fit int32 row ids", (long long)rows);
   PKM_TRY(check_ws(handle, T, PKM_WS_FWPKM_CHUNK, ws, ws_bytes));
   if (T == 0) return PKM_OK;
-  const pkm_config& c = handle->cfg;
+  int bits = 0;
+  while ((int64_t(1) << bits) < rows) ++bits;
   hipStream_t s = as_stream(stream);
   const FwdLayout F = fwd_layout(handle, T);
   const BwdLayout B = bwd_layout(handle, T);
@@ -968,7 +981,7 @@ pkm_status pkm_fwpkm_chunk(pkm_handle_t handle, void* stream, int64_t T, const v
   int32_t* sub_idx = at<int32_t>(ws, F.sub_idx);
   float* sub_score = at<float>(ws, F.sub_score);
   PKM_TRY(run_score(handle, s, T, q, C, Cp, sub_idx, sub_score, ws));
-  PKM_TRY(run_merge(handle, s, T, sub_idx, sub_score, idx, w, nullptr));
+  PKM_TRY(run_merge(handle, s, T, sub_idx, sub_score, idx, w, nullptr, streams > 1 ? T / streams : 0));
   void* e = at<void>(ws, L.e);
   PKM_HIP(launch_gather(s, c.dtype, idx, w, V, y, T, c.heads * c.topk, c.d_value, false, target, e),
           "value gather-sum and reconstruction residual");
@@ -977,5 +990,5 @@ pkm_status pkm_fwpkm_chunk(pkm_handle_t handle, void* stream, int64_t T, const v
   sgd.step_size = lr;
   sgd.sgd = 1;
   return run_value_grad(handle, s, T, idx, w, e, V, nullptr, at<int32_t>(ws, L.touched), at<int64_t>(ws, L.n_touched),
-                        at<float>(ws, B.dw), ws, &sgd);
+                        at<float>(ws, B.dw), ws, &sgd, bits);
 }

@@ -31,9 +31,11 @@ hipError_t launch_score_topk(hipStream_t s, int dtype, const void* q, int64_t nt
                              float* sub_score, void* packed, bool idw = false);
 
 // a5: k x k candidates -> top-k -> softmax, per (token, head).
+// group_items > 0: item i's rows are offset by (i / group_items) * group_rows
+// (consecutive groups of items address consecutive tables of group_rows rows).
 hipError_t launch_merge_softmax(hipStream_t s, const int32_t* sub_idx, const float* sub_score,
                                 int64_t nitems, int k, int nk2, float inv_tau, int32_t* idx, float* w,
-                                float* score);
+                                float* score, int64_t group_items = 0, int64_t group_rows = 0);
 
 // C[M, N] = A[M, K] * B[N, K]^T; A, B storage dtype, C fp32 (or bf16 when out_bf16).
 // splits > 1: blockIdx.z handles a slice of K and writes C + z * split_stride.
@@ -85,13 +87,26 @@ size_t scan_temp_bytes(int64_t n);
 hipError_t launch_exclusive_scan(hipStream_t s, const uint32_t* in, uint32_t* out, int64_t n, void* temp,
                                  uint32_t* total /*device, may be null*/);
 
+// The value gradient's long-run plan: every run of more than kVgChunk lookups
+// of one row is cut into chunks, listed as (run, chunk) in chunk_list and
+// (run, first chunk slot) in long_list; counts = {chunks, long runs}.  The
+// lists live in the value gradient's aux buffer.
+constexpr int kVgChunk = 256;
+struct VgPlan {
+  uint32_t* counts;
+  int2* chunk_list;
+  int2* long_list;
+};
+VgPlan value_grad_plan(void* aux, int64_t nitems, int d_value);
+
 // Both of the above for n <= kSmallSortMax pairs in one launch: keys_in (< 2^key_bits)
 // stably sorted into keys_out with their indices in vals_out, and the segment
-// table (seg_start, touched (may be null), count) of the sorted keys.
+// table (seg_start, touched (may be null), count) of the sorted keys; plan
+// (may be null): also the value gradient's long-run plan of those segments.
 constexpr int kSmallSortMax = 8192;
 hipError_t launch_sort_segments_small(hipStream_t s, const uint32_t* keys_in, int64_t n, int key_bits,
                                       uint32_t* keys_out, int32_t* vals_out, int32_t* seg_start, int32_t* touched,
-                                      int64_t* count);
+                                      int64_t* count, const VgPlan* plan = nullptr);
 
 // Segments of a sorted key array: seg_start[u] for every distinct key run, and
 // count (device int64).  Also touched[u] = key of run u (may be null).
@@ -101,7 +116,8 @@ hipError_t launch_segments(hipStream_t s, const uint32_t* sorted_keys, int64_t n
 
 // a7 + a8: per touched row, dw for every lookup of it and the row's dV.  Rows
 // with more lookups than a chunk are split over several waves; aux (of
-// value_grad_aux_bytes) holds their lists and partial sums.
+// value_grad_aux_bytes) holds their lists and partial sums.  plan_ready: the
+// long-run plan is already in aux (launch_sort_segments_small wrote it).
 // adam != null: no dV; every touched row's gradient takes an Adam step on
 // (V, m, v) instead (V is then the same buffer as adam->V, updated in place).
 struct VgAdam {
@@ -117,7 +133,8 @@ size_t value_grad_aux_bytes(int64_t nitems, int d_value);
 hipError_t launch_value_grad(hipStream_t s, int dtype, const int32_t* seg_start, const int64_t* nseg,
                              int64_t nitems, const uint32_t* sorted_rows, const int32_t* sorted_c,
                              const float* w, const void* dY, const void* V, float* dV, float* dw,
-                             int R, int d_value, bool accumulate, void* aux, const VgAdam* adam = nullptr);
+                             int R, int d_value, bool accumulate, void* aux, const VgAdam* adam = nullptr,
+                             bool plan_ready = false);
 
 // a7 + a9: per (token, head) softmax backward, dq from the distinct selected
 // sub-keys, and per slot the sub-key sort key (h*|C|+i / h*|C'|+j, or the

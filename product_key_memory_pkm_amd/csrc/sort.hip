@@ -288,7 +288,10 @@ __global__ void seg_empty_kernel(int32_t* seg_start, int64_t* count) {
 // turns the counts into bases, and the pairs, still in registers, are written
 // to the other buffer.  The order is stable, so equal keys keep their lookup
 // order.  Then the segment table is built from the sorted keys in the same
-// workgroup.
+// workgroup, and (plan_counts != null) the value gradient's long-run plan of
+// those segments, from a copy of the segment starts in the free LDS buffer
+// (LDS atomics hand out the chunk slots; the sums over a run's chunks are
+// taken in chunk order, so the slot order does not matter).
 // ---------------------------------------------------------------------------
 constexpr int kSmallThreads = 1024;
 constexpr int kSmallWaves = kSmallThreads / 64;
@@ -301,13 +304,15 @@ size_t small_sort_lds_bytes(int64_t n) {
 __global__ __launch_bounds__(kSmallThreads) void small_sort_segments_kernel(
     const uint32_t* __restrict__ keys_in, int n, int passes, uint32_t* __restrict__ keys_out,
     int32_t* __restrict__ vals_out, int32_t* __restrict__ seg_start, int32_t* __restrict__ touched,
-    int64_t* __restrict__ count) {
+    int64_t* __restrict__ count, int chunk, int2* __restrict__ chunk_list, int2* __restrict__ long_list,
+    uint32_t* __restrict__ plan_counts) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   uint64_t* bufA = reinterpret_cast<uint64_t*>(smem);
   uint64_t* bufB = bufA + n;
   uint32_t* cnt = reinterpret_cast<uint32_t*>(bufB + n);  // [kSmallWaves][256]
   uint32_t* wsum = cnt + kSmallWaves * 256;                 // [64]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) wsum[32] = wsum[33] = 0u;  // long-run plan counters
   for (int i = tid; i < n; i += kSmallThreads) bufA[i] = (uint64_t(keys_in[i]) << 32) | uint32_t(i);
   // wave w owns pairs [w * per, (w + 1) * per), per a multiple of 64
   const int per = ((n + kSmallWaves - 1) / kSmallWaves + 63) / 64 * 64;
@@ -405,16 +410,37 @@ __global__ __launch_bounds__(kSmallThreads) void small_sort_segments_kernel(
     if (w < wave) rank += wsum[w];
     total += wsum[w];
   }
+  int32_t* segl = reinterpret_cast<int32_t*>(dst);  // free after the passes: room for 2n ints
+  const bool plan = plan_counts != nullptr && n > 0;
   for (int j = 0; j < ipt; ++j) {
     if (flags & (1u << j)) {
       seg_start[rank] = i0 + j;
       if (touched) touched[rank] = int32_t(src[i0 + j] >> 32);
+      if (plan) segl[rank] = i0 + j;
       ++rank;
     }
   }
   if (tid == 0) {
     seg_start[total] = n;
     *count = int64_t(total);
+    if (plan) segl[total] = n;
+  }
+  if (plan_counts == nullptr) return;  // uniform over the workgroup
+  __syncthreads();
+  for (int u = tid; u < int(total); u += kSmallThreads) {
+    const int lo = segl[u];
+    const int len = segl[u + 1] - lo;
+    if (len > chunk) {
+      const int nch = (len + chunk - 1) / chunk;
+      const uint32_t base = atomicAdd(&wsum[32], uint32_t(nch));
+      for (int j = 0; j < nch; ++j) chunk_list[base + j] = make_int2(u, j);
+      long_list[atomicAdd(&wsum[33], 1u)] = make_int2(u, int(base));
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    plan_counts[0] = wsum[32];
+    plan_counts[1] = wsum[33];
   }
 }
 
@@ -490,7 +516,7 @@ hipError_t launch_radix_sort_from(hipStream_t s, const uint32_t* keys_in, uint32
 
 hipError_t launch_sort_segments_small(hipStream_t s, const uint32_t* keys_in, int64_t n, int key_bits,
                                       uint32_t* keys_out, int32_t* vals_out, int32_t* seg_start, int32_t* touched,
-                                      int64_t* count) {
+                                      int64_t* count, const VgPlan* plan) {
   if (n < 0 || n > kSmallSortMax) return hipErrorInvalidValue;
   static bool attr_set = false;  // the attribute is per function; setting it again is harmless
   const size_t lds = small_sort_lds_bytes(kSmallSortMax);
@@ -504,7 +530,9 @@ hipError_t launch_sort_segments_small(hipStream_t s, const uint32_t* keys_in, in
   if (passes < 1) passes = 1;
   if (passes > 4) passes = 4;
   hipLaunchKernelGGL(small_sort_segments_kernel, dim3(1), dim3(kSmallThreads), small_sort_lds_bytes(n), s, keys_in,
-                     int(n), passes, keys_out, vals_out, seg_start, touched, count);
+                     int(n), passes, keys_out, vals_out, seg_start, touched, count, kVgChunk,
+                     plan ? plan->chunk_list : nullptr, plan ? plan->long_list : nullptr,
+                     plan ? plan->counts : nullptr);
   return hipGetLastError();
 }
 

@@ -58,9 +58,8 @@ __device__ __forceinline__ float dot16<float>(const u32x4& a, const u32x4& v, fl
   return c;
 }
 
-// Lookups of one row longer than this many entries are cut into chunks that
+// Lookups of one row longer than kVgChunk entries are cut into chunks that
 // separate waves process; their partial sums meet in a fixed order.
-constexpr int kVgChunk = 256;
 
 struct VgArgs {
   const int32_t* seg_start;
@@ -350,10 +349,20 @@ size_t value_grad_aux_bytes(int64_t nitems, int d_value) {
   return size_t(slots) * (size_t(d_value) * 4 + 8 + 8) + 64;
 }
 
+VgPlan value_grad_plan(void* aux, int64_t nitems, int d_value) {
+  const int64_t slots = 2 * (nitems / kVgChunk) + 2;
+  char* ap = static_cast<char*>(aux);
+  VgPlan p;
+  p.counts = reinterpret_cast<uint32_t*>(ap);
+  p.chunk_list = reinterpret_cast<int2*>(ap + 64 + size_t(slots) * d_value * 4);
+  p.long_list = p.chunk_list + slots;
+  return p;
+}
+
 hipError_t launch_value_grad(hipStream_t s, int dtype, const int32_t* seg_start, const int64_t* nseg,
                              int64_t nitems, const uint32_t* sorted_rows, const int32_t* sorted_c, const float* w,
                              const void* dY, const void* V, float* dV, float* dw, int R, int d_value,
-                             bool accumulate, void* aux, const VgAdam* adam) {
+                             bool accumulate, void* aux, const VgAdam* adam, bool plan_ready) {
   const int elem = dtype == kBF16 ? 2 : 4;
   const int nvec = d_value * elem / 16;
   const int per_lane = (nvec + 63) / 64;
@@ -387,19 +396,19 @@ hipError_t launch_value_grad(hipStream_t s, int dtype, const int32_t* seg_start,
     a.step_size = adam->step_size;
     a.inv_sqrt_bc2 = adam->inv_sqrt_bc2;
   }
-  uint32_t* counts = reinterpret_cast<uint32_t*>(ap);
-  a.counts = counts;
+  const VgPlan plan = value_grad_plan(aux, nitems, d_value);
+  a.counts = plan.counts;
   a.partial = reinterpret_cast<float*>(ap + 64);
-  int2* chunk_list = reinterpret_cast<int2*>(ap + 64 + size_t(slots) * d_value * 4);
-  int2* long_list = chunk_list + slots;
-  a.chunk_list = chunk_list;
-  a.long_list = long_list;
-  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, s, counts, 2);
-  int64_t pb = (nitems + 255) / 256;
-  if (pb > 4096) pb = 4096;
-  if (pb < 1) pb = 1;
-  hipLaunchKernelGGL(long_run_plan_kernel, dim3(unsigned(pb)), dim3(256), 0, s, seg_start, nseg, kVgChunk,
-                     static_cast<const uint32_t*>(nullptr), 0u, chunk_list, long_list, counts);
+  a.chunk_list = plan.chunk_list;
+  a.long_list = plan.long_list;
+  if (!plan_ready) {
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, s, plan.counts, 2);
+    int64_t pb = (nitems + 255) / 256;
+    if (pb > 4096) pb = 4096;
+    if (pb < 1) pb = 1;
+    hipLaunchKernelGGL(long_run_plan_kernel, dim3(unsigned(pb)), dim3(256), 0, s, seg_start, nseg, kVgChunk,
+                       static_cast<const uint32_t*>(nullptr), 0u, plan.chunk_list, plan.long_list, plan.counts);
+  }
   const dim3 block(256);
   const dim3 grid_long(grid_waves(slots, 1024));
 #define PKM_VG_AD(TT, NV, AD)                                                                                \

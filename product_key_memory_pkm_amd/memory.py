@@ -109,9 +109,9 @@ class ProductKeyMemory:
                             g["n_touched"], g["dC"], g["dCp"], g["dWq"], g["dgamma"], g["dbeta"], g["dx"], ws)
         return g
 
-    def fwpkm_chunk(self, q, C, Cp, V, target, lr: float, out=None):
-        """One memorization chunk of the fast-weight memory (``pkm_fwpkm_chunk``): returns (y, idx, w),
-        y read from V before the write; V is updated in place."""
+    def fwpkm_chunk(self, q, C, Cp, V, target, lr: float, out=None, streams: int = 1):
+        """One memorization chunk of the fast-weight memory (``pkm_fwpkm_chunk``) for each of ``streams``
+        streams: returns (y, idx, w), y read from V before the write; V is updated in place."""
         T = q.shape[0]
         c = self.cfg
         dev = self.device
@@ -120,5 +120,5 @@ class ProductKeyMemory:
                    "idx": torch.empty((T, c.heads, c.topk), dtype=torch.int32, device=dev),
                    "w": torch.empty((T, c.heads, c.topk), dtype=torch.float32, device=dev)}
         ws = self.workspace(T, L.PKM_WS_FWPKM_CHUNK)
-        L.pkm_fwpkm_chunk(self.handle, T, q, C, Cp, V, target, lr, out["y"], out["idx"], out["w"], ws)
+        L.pkm_fwpkm_chunk(self.handle, T, q, C, Cp, V, target, lr, out["y"], out["idx"], out["w"], ws, streams)
         return out["y"], out["idx"], out["w"]

@@ -273,9 +273,9 @@ def test_idw_scores_and_fwpkm_chunk_argument_errors():
     big = 1 << 40
     c = lib.pkm_fwpkm_chunk
 
-    def call(handle=h, T=10, lr=0.1, ws_bytes=big, **over):
+    def call(handle=h, T=10, lr=0.1, ws_bytes=big, streams=1, **over):
         a = [over.get(n, ok[i]) for i, n in enumerate(("q", "C", "Cp", "V", "target", "y", "idx", "w"), 1)]
-        return c(handle.ptr, None, T, a[0], a[1], a[2], a[3], a[4], lr, a[5], a[6], a[7], ok[20], ws_bytes)
+        return c(handle.ptr, None, T, streams, a[0], a[1], a[2], a[3], a[4], lr, a[5], a[6], a[7], ok[20], ws_bytes)
 
     assert call(handle=dot) == L.PKM_ERR_UNSUPPORTED and "IDW" in lib.pkm_last_error().decode()
     for n in ("q", "C", "Cp", "V", "target", "y", "idx", "w"):
@@ -287,6 +287,14 @@ def test_idw_scores_and_fwpkm_chunk_argument_errors():
     assert call(ws_bytes=16) == L.PKM_ERR_WORKSPACE
     assert call(T=-1) == L.PKM_ERR_INVALID_ARG
     assert call(T=0) == L.PKM_OK                                                     # nothing to do
+    # a batch of streams: T a multiple of streams, every stream's rows addressable as int32
+    assert call(streams=0) == L.PKM_ERR_INVALID_ARG
+    assert call(T=10, streams=3) == L.PKM_ERR_INVALID_ARG
+    assert "multiple" in lib.pkm_last_error().decode()
+    assert call(T=12, streams=3, ws_bytes=16) == L.PKM_ERR_WORKSPACE                 # the other checks pass
+    big_keys = L.pkm_create(_cfg(L, score="idw", n_keys=2048, n_keys2=2048))
+    assert call(handle=big_keys, T=1024, streams=512) == L.PKM_ERR_UNSUPPORTED       # 512 * 2^22 = 2^31 rows
+    assert call(handle=big_keys, T=1022, streams=511, ws_bytes=16) == L.PKM_ERR_WORKSPACE  # fits: next check
     fp8 = L.pkm_create(_cfg(L, score="idw", values="fp8", d_value=64))
     assert call(handle=fp8) == L.PKM_ERR_UNSUPPORTED
     # the score gradients are the dot product's: the backward refuses IDW handles

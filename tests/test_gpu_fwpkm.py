@@ -353,3 +353,38 @@ def test_fwpkm_chunk_at_the_benchmark_configuration():
     sample = np.setdiff1d(g.integers(0, cfg.slots, 200_000), np.union1d(ids, G.reshape(-1)))
     np.testing.assert_array_equal(V_dev[torch.from_numpy(sample).cuda()].cpu().view(torch.int16).numpy(),
                                   V[sample].view(np.int16))
+
+
+BATCH_CASES = [
+    # streams, tokens per stream, heads, dq, nk, k, d_value, dtype
+    (3, 40, 2, 16, 12, 4, 24, "f32"),            # 960 lookups: one-workgroup grouping
+    (4, 512, 1, 32, 64, 8, 32, "bf16"),          # 16384 lookups: radix sort, 4 x 4096 slots
+]
+
+
+@pytest.mark.parametrize("streams,tps,h,dq,nk,k,dv,dtype", BATCH_CASES)
+def test_fwpkm_chunk_batch_of_streams(streams, tps, h, dq, nk, k, dv, dtype):
+    # each stream is its own chunk on its own table: compare stream by stream with the oracle
+    cfg = _cfg(T=tps, heads=h, dq=dq, n_keys=nk, n_keys2=nk, topk=k, d_value=dv, dtype=dtype, seed=51)
+    lr = 0.5
+    note(f"fwpkm chunk, {streams} streams of {tps} tokens: {cfg}")
+    half = dq // 2
+    C = pi.random_array(cfg.seed, 11, (h, nk, half), dtype=dtype, std=half ** -0.5)
+    Cp = pi.random_array(cfg.seed, 12, (h, nk, half), dtype=dtype, std=half ** -0.5)
+    qs, ts, Vs = [], [], []
+    for b in range(streams):
+        qs.append(pi.random_array(cfg.seed, 20 + b, (tps, h * dq), dtype=dtype, std=half ** -0.5))
+        ts.append(pi.random_array(cfg.seed, 40 + b, (tps, dv), dtype=dtype))
+        Vs.append(pi.random_array(cfg.seed, 60 + b, (cfg.slots, dv), dtype=dtype, std=dv ** -0.5))
+    layer = layer_for(cfg, score="idw")
+    V_dev = to_dev(np.concatenate(Vs))
+    y, idx, w = layer.fwpkm_chunk(to_dev(np.concatenate(qs)), to_dev(C), to_dev(Cp), V_dev,
+                                  to_dev(np.concatenate(ts)), lr, streams=streams)
+    torch.cuda.synchronize()
+    y, idx, w, V_all = P.to_f64(y), idx.cpu().numpy(), w.cpu().numpy(), P.to_f64(V_dev)
+    for b in range(streams):
+        tok = slice(b * tps, (b + 1) * tps)
+        rows = slice(b * cfg.slots, (b + 1) * cfg.slots)
+        G = idx[tok]
+        assert ((G >= b * cfg.slots) & (G < (b + 1) * cfg.slots)).all(), "a stream addressed another's table"
+        _check_chunk(cfg, qs[b], C, Cp, Vs[b], ts[b], lr, y[tok], G - b * cfg.slots, w[tok], V_all[rows], False)
