@@ -104,6 +104,48 @@ def fwpkm_chunk_bytes(chunk, k, dv, e, touched):
     return gather + residual + update + select
 
 
+def measured_peaks(torch, timed):
+    """What this GPU sustains, measured in this run with libpkm_probe.so: a streaming read of 4 GiB
+    (non-temporal 16-byte loads) and back-to-back bf16 16x16x32 MFMAs on register operands.  None if
+    the probe library is absent (it is not part of the lookup)."""
+    import ctypes
+    path = os.path.join(ROOT, "product_key_memory_pkm_amd", "libpkm_probe.so")
+    if not os.path.exists(path):
+        return None
+    P = ctypes.CDLL(path)
+    P.pkm_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                        ctypes.c_uint32, ctypes.c_void_p]
+    P.pkm_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32,
+                                      ctypes.c_void_p]
+    P.pkm_probe_stream_read.restype = P.pkm_probe_mfma_bf16.restype = ctypes.c_int
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = torch.zeros(4, dtype=torch.int32, device="cuda")
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    best = None
+    for blocks in (2048, 4096, 8192):
+        def rd():
+            assert P.pkm_probe_stream_read(stream, ctypes.c_void_p(buf.data_ptr()), nbytes, blocks, 0xDEADBEEF,
+                                           ctypes.c_void_p(out.data_ptr())) == 0
+        rd()
+        ms = timed(rd, 5)
+        bw = nbytes / (ms * 1e-3) / 1e9
+        best = bw if best is None or bw > best else best
+    del buf
+    blocks, iters = 2048, 4000
+    tf = {}
+    for shape, fl in ((0, 16384), (1, 32768)):
+        def mf():
+            assert P.pkm_probe_mfma_bf16(stream, blocks, iters, shape, 0xDEADBEEF,
+                                         ctypes.c_void_p(out.data_ptr())) == 0
+        mf()
+        ms = timed(mf, 5)
+        tf["16x16x32" if shape == 0 else "32x32x16"] = blocks * 4 * iters * 8 * fl / (ms * 1e-3) / 1e12
+    return {"hbm_read_GBs": best, "mfma_bf16_TFLOPs": max(tf.values()), "mfma_bf16_TFLOPs_by_shape": tf,
+            "method": "streaming read of 4 GiB (best of 2048/4096/8192 blocks), and 2048 blocks x 4 waves x "
+                      "4000 x 8 independent bf16 MFMAs of each shape; 5 event-timed launches each"}
+
+
 def alg_bytes(cfg, touched):
     """Algorithmic HBM bytes per launch of the forward gather and of the value-gradient kernel.
 
@@ -141,7 +183,8 @@ def main():
 
     import pkm_inputs as pi
     from product_key_memory_pkm_amd import (PKM_WS_FWPKM_CHUNK, ProductKeyMemory, pkm_diagnostics, pkm_fwpkm_chunk,
-                                            pkm_quantize_values, pkm_stage_gather,
+                                            pkm_quantize_values, pkm_stage_gather, pkm_stage_merge_softmax,
+                                            pkm_stage_query, pkm_stage_query_grad, pkm_stage_subkey_grad,
                                             pkm_stage_row_groups, pkm_stage_score_topk, pkm_stage_value_adam_grouped,
                                             pkm_stage_value_grad_grouped)
 
@@ -419,10 +462,35 @@ def main():
     sub_idx = torch.empty((T, cfg.heads, 2, cfg.topk), dtype=torch.int32, device="cuda")
     sub_score = torch.empty((T, cfg.heads, 2, cfg.topk), dtype=torch.float32, device="cuda")
     score_ms = timed(lambda: pkm_stage_score_topk(m.handle, T, saved["q"], C, Cp, sub_idx, sub_score, ws), nf)
+    # every step alone, through the stage entry points (each launches exactly the kernels the full calls
+    # launch for that step); inside pkm_backward the sub-key gradients overlap the query gradients
+    F = cfg.heads * cfg.dq
+    dq = torch.empty((T, F), dtype=torch.float32, device="cuda")
+    sdC = torch.empty((cfg.heads, cfg.n_keys, cfg.dq // 2), dtype=torch.float32, device="cuda")
+    sdCp = torch.empty((cfg.heads, cfg.n_keys2, cfg.dq // 2), dtype=torch.float32, device="cuda")
+    sdWq = torch.empty((F, cfg.d), dtype=torch.float32, device="cuda")
+    sdg = torch.empty(F, dtype=torch.float32, device="cuda") if cfg.bn else None
+    sdb = torch.empty(F, dtype=torch.float32, device="cuda") if cfg.bn else None
+    sdx = torch.empty((T, cfg.d), dtype=m.storage, device="cuda")
+    stages = {
+        "a1_a2_query": timed(lambda: pkm_stage_query(m.handle, T, x, Wq, gamma, beta, saved, ws), nf),
+        "a3_a4_score_topk": score_ms,
+        "a5_merge_softmax": timed(lambda: pkm_stage_merge_softmax(m.handle, T, sub_idx, sub_score, saved["idx"],
+                                                                  saved["w"]), nf),
+        "a6_gather": gather_ms,
+        "a8_row_grouping": timed(lambda: pkm_stage_row_groups(m.handle, T, saved["idx"], touched, nt, ws), nf),
+        "a7_a8_value_grad": vg_ms,
+        "a7_a9_subkey_grad": timed(lambda: pkm_stage_subkey_grad(m.handle, T, saved["idx"], saved["w"], dw,
+                                                                 saved["q"], C, Cp, dq, sdC, sdCp, ws), nf),
+        "a10_query_grad": timed(lambda: pkm_stage_query_grad(m.handle, T, dq, x, Wq, gamma, saved, sdWq, sdg, sdb,
+                                                             sdx, ws), nf),
+    }
+    del dq, sdC, sdCp, sdWq, sdg, sdb, sdx
     score_flops = 2.0 * T * cfg.heads * (cfg.n_keys + cfg.n_keys2) * (cfg.dq // 2)
     score_peak = MFMA_PEAK_TFLOPS[cfg.dtype]
     score_tf = score_flops / (score_ms * 1e-3) / 1e12
     ab = alg_bytes(cfg, n_touched)
+    peaks = measured_peaks(torch, timed)
     kern = {
         "gather": {"kernel": "gather_sum (a6)", "ms": gather_ms, "alg": ab["gather"]},
         "value_grad": {"kernel": "value_grad (a7 dw + a8 dV)", "ms": vg_ms, "alg": ab["value_grad"]},
@@ -440,9 +508,12 @@ def main():
 
     def roof(name):
         k_ = kern[name]
-        return {"kernel": k_["kernel"], "bound": "hbm", "achieved": k_["achieved"], "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": k_["achieved"] / HBM_PEAK_GBS, "traffic": measured_traffic(name, args.workload),
-                "alg_bytes_per_launch": k_["alg"], "avg_launch_ms": k_["ms"]}
+        r = {"kernel": k_["kernel"], "bound": "hbm", "achieved": k_["achieved"], "peak": HBM_PEAK_GBS,
+             "unit": "GB/s", "frac": k_["achieved"] / HBM_PEAK_GBS, "traffic": measured_traffic(name, args.workload),
+             "alg_bytes_per_launch": k_["alg"], "avg_launch_ms": k_["ms"]}
+        if peaks:
+            r["frac_of_measured_peak"] = k_["achieved"] / peaks["hbm_read_GBs"]
+        return r
 
     out = {
         "metric": f"PKM lookup tokens/sec (fwd+bwd) at {cfg.n_keys}^2 slots h={cfg.heads} k={cfg.topk}",
@@ -469,7 +540,11 @@ def main():
                                score_topk={"kernel": "score_topk (a3 MFMA scores + a4 per-half top-k)", "bound": "mfma",
                                            "achieved": score_tf, "peak": score_peak, "unit": "TFLOP/s",
                                            "frac": score_tf / score_peak, "traffic": None,
-                                           "alg_flops_per_launch": score_flops, "avg_launch_ms": score_ms}),
+                                           "alg_flops_per_launch": score_flops, "avg_launch_ms": score_ms,
+                                           "frac_of_measured_peak": (score_tf / peaks["mfma_bf16_TFLOPs"]
+                                                                     if peaks and cfg.dtype == "bf16" else None)}),
+        "measured_peaks": peaks,
+        "stages_ms": stages,
         "touched_rows": n_touched,
         "diagnostics": diag,
         "fp8_values": fp8,

@@ -1,4 +1,6 @@
-"""Build libpkm.so (HIP for gfx950) in place: ``python -m product_key_memory_pkm_amd.build``."""
+"""Build libpkm.so (HIP for gfx950) in place: ``python -m product_key_memory_pkm_amd.build``.
+
+Also builds libpkm_probe.so, the benchmark's peak probes (streaming read, MFMA loop), kept out of the library."""
 from __future__ import annotations
 
 import os
@@ -10,6 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libpkm.so")
+PROBE_OUT = os.path.join(PKG, "libpkm_probe.so")
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.hip", "gather.hip", "score_topk.hip", "merge_softmax.hip", "gemm.hip", "bn.hip", "sort.hip",
@@ -42,12 +45,16 @@ def build(verbose: bool = False) -> str:
         return obj
 
     with ThreadPoolExecutor(min(8, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
+        objs = list(ex.map(compile_one, SOURCES + ["probe.hip"]))
+    probe_obj = objs.pop()
     tmp = OUT + ".tmp"
     _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
     os.replace(tmp, OUT)
+    tmp = PROBE_OUT + ".tmp"
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", probe_obj, "-o", tmp])
+    os.replace(tmp, PROBE_OUT)
     if verbose:
-        print("linked", OUT, flush=True)
+        print("linked", OUT, "and", PROBE_OUT, flush=True)
     return OUT
 
 

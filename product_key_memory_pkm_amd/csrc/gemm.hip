@@ -8,9 +8,11 @@
 // trained by back-propagation.)
 //
 // bf16 (K a multiple of 32, operands under 4 GB): 256x256 output tile per
-// 8-wave workgroup (4 x 2 waves of 64 x 128), v_mfma_f32_16x16x32_bf16 with
-// fp32 accumulation.  Operands go straight from memory into LDS with
-// buffer_load ... lds (no register staging), four 32-deep K stages in flight;
+// 8-wave workgroup (4 x 2 waves of 64 x 128), v_mfma_f32_32x32x16_bf16 with
+// fp32 accumulation (gfx950 sustains about twice the bf16 flops with the
+// 32x32x16 shape as with 16x16x32, for the same operand bytes read from LDS).  Operands go straight from memory into LDS with
+// buffer_load ... lds (no register staging), five 32-deep K stages of 32 KB
+// (the whole 160 KB of LDS) so that four are in flight while one is consumed;
 // rows past the matrix read as zero through the buffer range check.  Each
 // 16-row x 64-byte LDS block keeps its 16-byte chunks XOR-swizzled by row so
 // the MFMA fragment reads of 16 rows spread over all banks.  Tiles are
@@ -186,7 +188,7 @@ __device__ __forceinline__ void lds_barrier() {
 // s_waitcnt vmcnt(n) (n < 64), other counters untouched
 #define PKM_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 0xF) | (((n) >> 4) << 14))
 
-constexpr int kDmaStages = 4;
+constexpr int kDmaStages = 5;
 constexpr int kDmaStage = 32768;  // bytes per stage: A and B blocks of 256 rows x 64 bytes
 constexpr int kDmaWM = 4, kDmaWN = 2;
 
@@ -194,7 +196,7 @@ __global__ __launch_bounds__(512) void gemm_nt_dma_kernel(int64_t M, int64_t N, 
                                                           int64_t lda, const bf16_t* __restrict__ B, int64_t ldb,
                                                           void* __restrict__ Cout, int64_t ldc, int out_bf16,
                                                           int64_t K, int64_t kchunk, int64_t split_stride) {
-  constexpr int BM = 256, BN = 256, NW = kDmaWM * kDmaWN, TI = BM / kDmaWM / 16, TJ = BN / kDmaWN / 16;
+  constexpr int BM = 256, BN = 256, NW = kDmaWM * kDmaWN, TI = BM / kDmaWM / 32, TJ = BN / kDmaWN / 32;
   constexpr int BPW = 16 / NW;        // 1 KB blocks per operand, stage and wave
   constexpr int PER = 2 * BPW;        // DMA instructions per stage and wave
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -228,51 +230,65 @@ __global__ __launch_bounds__(512) void gemm_nt_dma_kernel(int64_t M, int64_t N, 
       dma16(rb, boff[i] == kOut ? kOut : boff[i] + kb, lds_addr(st + 16384 + (wave + NW * i) * 1024));
     }
   };
-  f32x4 acc[TI][TJ];
+  f32x16 acc[TI][TJ];
 #pragma unroll
   for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int lrow = lane & 15, lgrp = lane >> 4;
-  const int fr = lrow * 64 + ((lgrp ^ ((lrow >> 2) & 3)) * 16);  // this lane's fragment in a block
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  // 32x32x16 operand fragments: lane l holds row (or column) l % 32 of a 32-row
+  // tile (two 1 KB blocks) and k = 8 (l / 32) .. +8 of the 16-deep half h of the
+  // stage, i.e. 16-byte chunk 2h + l / 32 of that row (swizzled as stored)
+  const int fr_r = lane & 15, fr_hi = lane >> 5;
+  const int fr_base = ((lane >> 4) & 1) * 1024 + fr_r * 64;
+  const int fr0 = fr_base + (((0 + fr_hi) ^ ((fr_r >> 2) & 3)) * 16);
+  const int fr1 = fr_base + (((2 + fr_hi) ^ ((fr_r >> 2) & 3)) * 16);
 #pragma unroll
   for (int st = 0; st < kDmaStages - 1; ++st)
     if (st < nkt) issue(st);
   for (int kt = 0; kt < nkt; ++kt) {
     if (kt + kDmaStages - 1 < nkt) {
       issue(kt + kDmaStages - 1);
-      PKM_WAIT_VM(PER * (kDmaStages - 1));  // stage kt landed; the next three stay in flight
+      PKM_WAIT_VM(PER * (kDmaStages - 1));  // stage kt landed; the next four stay in flight
     } else {
       PKM_WAIT_VM(0);
     }
     lds_barrier();
     const char* st = smem + (kt % kDmaStages) * kDmaStage;
-    u32x4 b[TJ];
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) b[j] = *reinterpret_cast<const u32x4*>(st + 16384 + (wn * TJ + j) * 1024 + fr);
+    for (int h = 0; h < 2; ++h) {
+      const int fr = h ? fr1 : fr0;
+      u32x4 b[TJ], a[TI];
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(st + (wm * TI + i) * 1024 + fr);
+      for (int j = 0; j < TJ; ++j) b[j] = *reinterpret_cast<const u32x4*>(st + 16384 + (wn * TJ + j) * 2048 + fr);
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) acc[i][j] = GemmTraits<bf16_t>::mma(a, b[j], acc[i][j]);
+      for (int i = 0; i < TI; ++i) a[i] = *reinterpret_cast<const u32x4*>(st + (wm * TI + i) * 2048 + fr);
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[i]),
+                                                               __builtin_bit_cast(bf16x8, b[j]), acc[i][j], 0, 0, 0);
     }
     lds_barrier();  // stage kt's buffer is refilled by the next iteration's issue
   }
+  // 32x32 accumulator layout: element e of lane l is row 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32
   char* Cb = reinterpret_cast<char*>(Cout) + int64_t(blockIdx.y) * split_stride * (out_bf16 ? 2 : 4);
 #pragma unroll
   for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
-      const int64_t col = n0 + (wn * TJ + j) * 16 + lrow;
+      const int64_t col = n0 + (wn * TJ + j) * 32 + (lane & 31);
       if (col >= N) continue;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t row = m0 + (wm * TI + i) * 16 + lgrp * 4 + q;
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = m0 + (wm * TI + i) * 32 + 8 * (e / 4) + 4 * fr_hi + (e % 4);
         if (row < M) {
           if (out_bf16)
-            reinterpret_cast<uint16_t*>(Cb)[row * ldc + col] = f32_to_bf16(acc[i][j][q]);
+            reinterpret_cast<uint16_t*>(Cb)[row * ldc + col] = f32_to_bf16(acc[i][j][e]);
           else
-            reinterpret_cast<float*>(Cb)[row * ldc + col] = acc[i][j][q];
+            reinterpret_cast<float*>(Cb)[row * ldc + col] = acc[i][j][e];
         }
       }
     }
