@@ -424,6 +424,24 @@ def main():
         host_s = time.time() - t_host
         torch.cuda.synchronize()
         ms_fw = start.elapsed_time(end)
+        # the same 64 calls captured once in a HIP graph and replayed (no host enqueue per call)
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            fwpkm_run(st, 1)
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fwpkm_run(st, FWPKM_CHUNKS)
+        graph.replay()
+        torch.cuda.synchronize()
+        start.record()
+        graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        ms_fw_graph = start.elapsed_time(end)
+        del graph
         touched_c = int(torch.unique(st["idx"]).numel())   # the last chunk's distinct rows
         e_ = 2 if cfg.dtype == "bf16" else 4
         cb = fwpkm_chunk_bytes(FWPKM_CHUNK, FWPKM_TOPK, cfg.d_value, e_, touched_c)
@@ -433,6 +451,8 @@ def main():
                            f"d_value={cfg.d_value}, {cfg.dtype} storage, lr={FWPKM_LR}"),
               "tokens_per_s": FWPKM_CHUNK * FWPKM_CHUNKS / (ms_fw * 1e-3), "ms_per_chunk": ms_chunk,
               "host_enqueue_ms_per_chunk": host_s * 1e3 / FWPKM_CHUNKS,
+              "tokens_per_s_graph_replay": FWPKM_CHUNK * FWPKM_CHUNKS / (ms_fw_graph * 1e-3),
+              "ms_per_chunk_graph_replay": ms_fw_graph / FWPKM_CHUNKS,
               "touched_rows_last_chunk": touched_c, "alg_bytes_per_chunk": cb,
               "achieved_GBs_whole_chunk": cb / (ms_chunk * 1e-3) / 1e9}
         del st

@@ -73,3 +73,62 @@ def test_forward_backward_graph_replays(name):
         got = snapshot()
         for k_, v_ in ref.items():
             assert torch.equal(got[k_], v_), f"replay {rep}: {k_} differs from the eager run"
+
+
+@pytest.mark.parametrize("streams", [1, 8])
+def test_fwpkm_chunks_graph_replays(streams):
+    # three memorization chunks in sequence (each reads the previous one's write) captured in one graph;
+    # one stream groups its 2048 lookups in one workgroup, eight streams take the radix sort
+    tps, nchunks, lr = 256, 3, 0.5
+    cfg = pi.custom(T=tps * streams, d=16, heads=1, dq=32, n_keys=64, n_keys2=64, topk=8, d_value=64, dtype="bf16",
+                    bn=False, seed=52)
+    note(f"graph capture of {nchunks} fwpkm chunks, {streams} streams")
+    half = cfg.dq // 2
+    T = cfg.T
+    C = to_dev(pi.random_array(cfg.seed, 1, (1, cfg.n_keys, half), dtype="bf16", std=half ** -0.5))
+    Cp = to_dev(pi.random_array(cfg.seed, 2, (1, cfg.n_keys2, half), dtype="bf16", std=half ** -0.5))
+    qs = [to_dev(pi.random_array(cfg.seed, 10 + c, (T, cfg.dq), dtype="bf16", std=half ** -0.5)) for c in range(nchunks)]
+    ts = [to_dev(pi.random_array(cfg.seed, 20 + c, (T, cfg.d_value), dtype="bf16")) for c in range(nchunks)]
+    V0 = to_dev(pi.random_array(cfg.seed, 3, (streams * cfg.slots, cfg.d_value), dtype="bf16", std=0.125))
+    layer = layer_for(cfg, score="idw")
+    outs = [{"y": torch.empty((T, cfg.d_value), dtype=torch.bfloat16, device="cuda"),
+             "idx": torch.empty((T, 1, cfg.topk), dtype=torch.int32, device="cuda"),
+             "w": torch.empty((T, 1, cfg.topk), dtype=torch.float32, device="cuda")} for _ in range(nchunks)]
+    V = V0.clone()
+
+    def run():
+        for c in range(nchunks):
+            layer.fwpkm_chunk(qs[c], C, Cp, V, ts[c], lr, out=outs[c], streams=streams)
+
+    def snapshot():
+        return [{k_: v_.clone() for k_, v_ in o.items()} for o in outs], V.clone()
+
+    run()  # eager reference (also allocates the workspace)
+    torch.cuda.synchronize()
+    ref_outs, ref_V = snapshot()
+    assert not torch.equal(ref_V, V0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        V.copy_(V0)
+        run()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    junk = torch.zeros(1 << 20, device="cuda")
+    for rep in range(3):
+        V.copy_(V0)
+        for o in outs:
+            for v_ in o.values():
+                v_.zero_()
+        junk += torch.randn_like(junk)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got_outs, got_V = snapshot()
+        assert torch.equal(got_V, ref_V), f"replay {rep}: the table differs from the eager run"
+        for c in range(nchunks):
+            for k_ in ("y", "idx", "w"):
+                assert torch.equal(got_outs[c][k_], ref_outs[c][k_]), f"replay {rep}: chunk {c} {k_} differs"
