@@ -83,6 +83,11 @@ SCORE_CASES = [
     (60, 2, 256, 1040, 1100, 32, "bf16", False),  # last chunk narrower than k
     (30, 2, 32, 1300, 40, 32, "f32", True),       # ties across chunks: lowest index wins
     (20, 1, 512, 1024, 1024, 16, "f32", False),   # fp32 with wide halves: 512-column chunks
+    # launches too small for the chip split each half's sub-keys over 2 or 4 blocks and merge their lists
+    (40, 1, 32, 256, 512, 8, "f32", False),       # 4 splits
+    (33, 3, 32, 300, 280, 8, "f32", True),        # 4 splits, ties across splits: lowest index wins
+    (20, 2, 64, 512, 512, 16, "bf16", False),     # 2 splits
+    (25, 1, 16, 130, 129, 4, "bf16", True),       # splits of unequal width
 ]
 
 
@@ -310,6 +315,9 @@ FWD_CASES = {
                 seed=27),
     "hot_bf16": _cfg(T=6000, d=64, heads=2, dq=64, n_keys=16, n_keys2=16, topk=16, d_value=64, dtype="bf16",
                      bn=True, seed=28),
+    # few tokens, wide halves: the scoring splits each half over 4 blocks
+    "split": _cfg(T=100, d=32, heads=1, dq=32, n_keys=256, n_keys2=300, topk=8, d_value=32, dtype="f32", bn=True,
+                  seed=29),
 }
 
 

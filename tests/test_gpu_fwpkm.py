@@ -76,6 +76,8 @@ IDW_SCORE_CASES = [
     (33, 3, 8, 40, 40, 32, "f32", True),            # small integers: exact ties and zero distances
     (31, 2, 16, 100, 37, 16, "bf16", True),
     (17, 1, 8, 5, 3, 3, "f32", False),              # k = |C'|
+    (64, 1, 32, 512, 512, 8, "f32", True),          # 4 split blocks per half, ties across them
+    (50, 2, 64, 600, 520, 16, "bf16", False),       # 2 split blocks per half
 ]
 
 
