@@ -1,6 +1,7 @@
 """GPU parity at the full workload sizes (paper scale and the skewed workload).
 
-Same kernels and launch shapes as bench.py.  The oracle computes sampled
+Same kernels and launch shapes as bench.py, for the lookup's steps and for the
+fp8 value rows, the fused Adam step and the monitoring signals.  The oracle computes sampled
 outputs one by one (BatchNorm statistics always over every token); properties
 that hold at any size cover the rest: touched rows equal the distinct selected
 rows bit for bit, untouched dV rows keep their sentinel, and the value gradient
@@ -210,3 +211,107 @@ def test_query_grad_full_size():
     tok = _sample(T, 512, 17)
     Wq = O.decode(inp["Wq"], "bf16")
     assert P.fro_rel_err(P.to_f64(dx[torch.from_numpy(tok).cuda()]), dq_pre[tok] @ Wq) <= 1e-2
+
+
+# ---------------------------------------------------------------------------
+# The NEXT rows at full size: fp8 value rows, the fused Adam step, diagnostics
+# ---------------------------------------------------------------------------
+def test_fp8_values_full_size_sampled():
+    # the paper-scale table quantized on the GPU (bit-exact on sampled rows), then the fp8 gather of a
+    # paper-shaped selection on sampled tokens against the oracle's own quantization of their rows
+    cfg = pi.CONFIGS["paper"]
+    note("full-size fp8 values (paper)")
+    inp = _inputs("paper")
+    V = inp["V"]
+    layer = layer_for(cfg, values="fp8")
+    from product_key_memory_pkm_amd import pkm_quantize_values, pkm_stage_gather
+    rb = cfg.d_value + 16
+    table = torch.empty(cfg.slots * rb, dtype=torch.uint8, device="cuda")
+    pkm_quantize_values(layer.handle, to_dev(V), table)
+    torch.cuda.synchronize()
+    which = _sample(cfg.slots, 2000, 13)
+    got = table.view(cfg.slots, rb)[torch.from_numpy(which).cuda()].cpu().numpy()
+    scale, codes = O.quantize_rows_fp8(V[which], cfg.dtype)
+    np.testing.assert_array_equal(got[:, :4].copy().view(np.float32).reshape(-1), scale)
+    assert (got[:, 4:16] == 0).all()
+    np.testing.assert_array_equal(got[:, 16:], codes)
+    T, h, k = cfg.T, cfg.heads, cfg.topk
+    rows, w = pi.random_selection(37, T, h, k, cfg.slots)
+    y = torch.empty((T, cfg.d_value), dtype=torch.bfloat16, device="cuda")
+    pkm_stage_gather(layer.handle, T, to_dev(rows), to_dev(w), table, y)
+    torch.cuda.synchronize()
+    tok = _sample(T, 128, 17)
+    r = rows[tok]
+    uniq, inv = np.unique(r, return_inverse=True)
+    s_u, c_u = O.quantize_rows_fp8(V[uniq], cfg.dtype)
+    ref = O.gather_sum(inv.reshape(r.shape), w[tok].astype(np.float64), O.dequantize_rows_fp8(s_u, c_u), O.F64)
+    err = P.row_rel_err(P.to_f64(y[torch.from_numpy(tok).cuda()]), ref)
+    assert err.max() <= 8e-3, err.max()
+
+
+def test_value_adam_full_size_sampled():
+    # the first Adam step (zero moments) of the touched rows of a paper-shaped selection
+    cfg = pi.CONFIGS["paper"]
+    note("full-size value gradient with the Adam step (paper)")
+    T, h, k = cfg.T, cfg.heads, cfg.topk
+    rows, w = pi.random_selection(41, T, h, k, cfg.slots)
+    inp = _inputs("paper")
+    V, dY = inp["V"], inp["dY"]
+    layer = layer_for(cfg)
+    from product_key_memory_pkm_amd import pkm_stage_value_adam
+    hp = dict(lr=1e-2, beta1=0.9, beta2=0.999, eps=1e-8, step=1)
+    V0 = to_dev(V)
+    V1 = V0.clone()
+    m = torch.zeros((cfg.slots, cfg.d_value), dtype=torch.float32, device="cuda")
+    v = torch.zeros_like(m)
+    touched = torch.empty(T * h * k, dtype=torch.int32, device="cuda")
+    nt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    dw = torch.empty((T, h, k), dtype=torch.float32, device="cuda")
+    pkm_stage_value_adam(layer.handle, T, to_dev(rows), to_dev(w), to_dev(dY), V1, m, v, hp, touched, nt, dw,
+                         layer.workspace(T, True))
+    torch.cuda.synchronize()
+    uniq = np.unique(rows)
+    assert int(nt.item()) == len(uniq)
+    # untouched rows: value bits and zero moments kept (checked on the device, in row blocks)
+    mask = torch.ones(cfg.slots, dtype=torch.bool, device="cuda")
+    mask[torch.from_numpy(uniq).cuda().long()] = False
+    for lo, hi in _row_chunks(cfg.slots):
+        mk = mask[lo:hi]
+        assert torch.equal(V1[lo:hi][mk].view(torch.int16), V0[lo:hi][mk].view(torch.int16)), f"[{lo}, {hi})"
+        assert bool((m[lo:hi][mk] == 0).all().item()) and bool((v[lo:hi][mk] == 0).all().item())
+    which = uniq[_sample(len(uniq), 400, 19)]
+    g = O.value_grad_rows(rows, w.astype(np.float64), dY, cfg.dtype, which)
+    f32 = {kk: (float(np.float32(vv)) if kk != "step" else vv) for kk, vv in hp.items()}
+    z = np.zeros((len(which), cfg.d_value), dtype=np.float32)
+    Vr, mr, vr = O.sparse_adam_rows(V[which], z, z, g, f32["lr"], f32["beta1"], f32["beta2"], f32["eps"],
+                                    f32["step"], cfg.dtype)
+    wt = torch.from_numpy(which).cuda().long()
+    gm, gv = m[wt].cpu().double().numpy(), v[wt].cpu().double().numpy()
+    assert (np.abs(gm - mr).max(1) <= 1e-5 * np.abs(mr).max(1) + 1e-12).all(), "adam m"
+    assert (np.abs(gv - vr).max(1) <= 1e-5 * np.abs(vr).max(1) + 1e-15).all(), "adam v"
+    assert (np.abs(P.to_f64(V1[wt]) - Vr) <= P.bf16_ulp(Vr)).all(), "adam V (bf16)"
+
+
+@pytest.mark.parametrize("name,zipf", [("paper", 0.0), ("skewed", 0.8)])
+def test_diagnostics_full_size(name, zipf):
+    # exact integer counts over the whole selection; entropies within fp32 rounding
+    cfg = pi.CONFIGS[name]
+    note(f"full-size diagnostics {name} zipf={zipf}")
+    T, h, k = cfg.T, cfg.heads, cfg.topk
+    rows, w = pi.random_selection(43, T, h, k, cfg.slots, zipf=zipf)
+    layer = layer_for(cfg)
+    from product_key_memory_pkm_amd import pkm_diagnostics
+    hc = torch.full((h, cfg.n_keys), -1, dtype=torch.int32, device="cuda")
+    hcp = torch.full((h, cfg.n_keys2), -1, dtype=torch.int32, device="cuda")
+    used = torch.full((1 + h,), -1, dtype=torch.int64, device="cuda")
+    ent = torch.empty((T, h), dtype=torch.float32, device="cuda")
+    ent_sum = torch.full((1,), -1.0, dtype=torch.float64, device="cuda")
+    pkm_diagnostics(layer.handle, T, to_dev(rows), to_dev(w), hc, hcp, used, ent, ent_sum, layer.workspace(T, True))
+    torch.cuda.synchronize()
+    r_hc, r_hcp, r_used, r_ent = O.diagnostics(rows, w.astype(np.float64), cfg.n_keys, cfg.n_keys2)
+    np.testing.assert_array_equal(hc.cpu().numpy(), r_hc)
+    np.testing.assert_array_equal(hcp.cpu().numpy(), r_hcp)
+    np.testing.assert_array_equal(used.cpu().numpy(), r_used)
+    got = ent.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - r_ent) <= 1e-5 * np.abs(r_ent) + 1e-6)
+    assert abs(float(ent_sum.cpu().item()) - r_ent.sum()) <= 1e-5 * abs(r_ent.sum()) + 1e-6
