@@ -76,7 +76,7 @@ struct FwdLayout {
   size_t sub_idx, sub_score, bn_part, keys, total;
 };
 struct BwdLayout {
-  size_t k0, v0, k1, v1, sort_tmp, key1, key2, seg, scan_tmp, nseg, dw, ds, coef2, dq, bn_part,
+  size_t k0, v0, k1, v1, sort_tmp, grp, key1, key2, seg, scan_tmp, nseg, dw, ds, coef2, dq, bn_part,
       dqpre, dqpre_t, x_t, wq_t, split, aux, total;
   int splits;
   int64_t tpad;
@@ -117,6 +117,7 @@ BwdLayout bwd_layout(const pkm_handle_s* h, int64_t T) {
   L.k1 = o; o += al(N * 4);
   L.v1 = o; o += al(N * 4);
   L.sort_tmp = o; o += al(radix_sort_temp_bytes(int64_t(N)));
+  L.grp = o; o += al(sort_groups_temp_bytes(int64_t(N)));  // per-group segment tables of a grouped sort
   L.key1 = o; o += al(N * 4);  // per-slot sub-key sort keys of the two halves
   L.key2 = o; o += al(N * 4);
   L.seg = o; o += al((N + 1) * 4);
@@ -267,15 +268,32 @@ int row_sort_passes(const pkm_handle_s* h, int bits = -1) {
   return p < 1 ? 1 : p;
 }
 
+// Lookups that come in `groups` equal groups addressing ascending, disjoint
+// row ranges (the streams of a memorization batch) too many for one workgroup
+// but few enough per group are sorted a workgroup per group.
+bool grouped_sort(int64_t N, int groups) {
+  return groups > 1 && N > kSmallSortMax && N % groups == 0 && N / groups <= kSmallSortMax &&
+         groups <= kSortGroupsMax;
+}
+
 // Grouping of the lookups by row.  The sorted (row, lookup) pairs land in
 // (k0, v0) or (k1, v1) depending on the number of radix passes; a small batch
 // is sorted and segmented in one workgroup, straight into the same place.
 pkm_status run_row_groups(const pkm_handle_s* h, hipStream_t s, int64_t T, const int32_t* idx, int32_t* touched,
-                          int64_t* n_touched, void* ws, int bits = -1) {
+                          int64_t* n_touched, void* ws, int bits = -1, int groups = 1) {
   const pkm_config& c = h->cfg;
   const BwdLayout L = bwd_layout(h, T);
   const int64_t N = T * c.heads * c.topk;
   const int key_bits = bits < 0 ? h->row_bits : bits;
+  if (grouped_sort(N, groups)) {  // each group's keys differ only in the handle's row bits
+    const bool out1 = row_sort_passes(h, key_bits) % 2 == 0;
+    const VgPlan plan = value_grad_plan(at<void>(ws, L.aux), N, c.d_value);
+    PKM_HIP(launch_sort_segments_grouped(s, reinterpret_cast<const uint32_t*>(idx), N, groups, h->row_bits,
+                                         at<uint32_t>(ws, out1 ? L.k1 : L.k0), at<int32_t>(ws, out1 ? L.v1 : L.v0),
+                                         at<int32_t>(ws, L.seg), touched, n_touched, &plan, at<void>(ws, L.grp)),
+            "row sort, segments and long-run plan (a workgroup per group)");
+    return PKM_OK;
+  }
   if (N <= kSmallSortMax) {
     const bool out1 = row_sort_passes(h, key_bits) % 2 == 0;
     const VgPlan plan = value_grad_plan(at<void>(ws, L.aux), N, c.d_value);
@@ -298,26 +316,26 @@ pkm_status run_row_groups(const pkm_handle_s* h, hipStream_t s, int64_t T, const
 
 pkm_status run_value_grad_grouped(const pkm_handle_s* h, hipStream_t s, int64_t T, const float* w, const void* dY,
                                   const void* V, float* dV, float* dw, const int64_t* n_touched, void* ws,
-                                  const VgAdam* adam = nullptr, int bits = -1) {
+                                  const VgAdam* adam = nullptr, int bits = -1, int groups = 1) {
   const pkm_config& c = h->cfg;
   const BwdLayout L = bwd_layout(h, T);
   const int64_t N = T * c.heads * c.topk;
   const bool in1 = row_sort_passes(h, bits) % 2 == 0;  // passes alternate (k0,v0), (k1,v1), ...
   const uint32_t* sk = at<uint32_t>(ws, in1 ? L.k1 : L.k0);
   const int32_t* sv = at<int32_t>(ws, in1 ? L.v1 : L.v0);
-  // a grouping of at most kSmallSortMax lookups came with the long-run plan in aux
+  // a grouping made in one workgroup (or one per group) came with the long-run plan in aux
   PKM_HIP(launch_value_grad(s, c.dtype, at<int32_t>(ws, L.seg), n_touched, N, sk, sv, w, dY, V, dV, dw,
                             c.heads * c.topk, c.d_value, c.accumulate_dv != 0, at<void>(ws, L.aux), adam,
-                            N <= kSmallSortMax),
+                            N <= kSmallSortMax || grouped_sort(N, groups)),
           adam ? "value gradient with Adam step" : "value gradient");
   return PKM_OK;
 }
 
 pkm_status run_value_grad(const pkm_handle_s* h, hipStream_t s, int64_t T, const int32_t* idx, const float* w,
                           const void* dY, const void* V, float* dV, int32_t* touched, int64_t* n_touched, float* dw,
-                          void* ws, const VgAdam* adam = nullptr, int bits = -1) {
-  PKM_TRY(run_row_groups(h, s, T, idx, touched, n_touched, ws, bits));
-  return run_value_grad_grouped(h, s, T, w, dY, V, dV, dw, n_touched, ws, adam, bits);
+                          void* ws, const VgAdam* adam = nullptr, int bits = -1, int groups = 1) {
+  PKM_TRY(run_row_groups(h, s, T, idx, touched, n_touched, ws, bits, groups));
+  return run_value_grad_grouped(h, s, T, w, dY, V, dV, dw, n_touched, ws, adam, bits, groups);
 }
 
 // Adam hyper-parameters -> the kernel's constants (bias corrections in double).
@@ -990,5 +1008,5 @@ pkm_status pkm_fwpkm_chunk(pkm_handle_t handle, void* stream, int64_t T, int64_t
   sgd.step_size = lr;
   sgd.sgd = 1;
   return run_value_grad(handle, s, T, idx, w, e, V, nullptr, at<int32_t>(ws, L.touched), at<int64_t>(ws, L.n_touched),
-                        at<float>(ws, B.dw), ws, &sgd, bits);
+                        at<float>(ws, B.dw), ws, &sgd, bits, int(streams));
 }

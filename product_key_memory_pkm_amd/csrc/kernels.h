@@ -107,6 +107,16 @@ constexpr int kSmallSortMax = 8192;
 hipError_t launch_sort_segments_small(hipStream_t s, const uint32_t* keys_in, int64_t n, int key_bits,
                                       uint32_t* keys_out, int32_t* vals_out, int32_t* seg_start, int32_t* touched,
                                       int64_t* count, const VgPlan* plan = nullptr);
+// The same for n pairs in `groups` equal groups of at most kSmallSortMax, every
+// key of a group below every key of the next (groups <= kSortGroupsMax): one
+// workgroup per group, then one that joins their segment tables and builds
+// the plan.  key_bits: the bits in which keys of one group differ (from bit 0).
+// temp: sort_groups_temp_bytes(n).
+constexpr int kSortGroupsMax = 1024;
+size_t sort_groups_temp_bytes(int64_t n);
+hipError_t launch_sort_segments_grouped(hipStream_t s, const uint32_t* keys_in, int64_t n, int groups,
+                                        int key_bits, uint32_t* keys_out, int32_t* vals_out, int32_t* seg_start,
+                                        int32_t* touched, int64_t* count, const VgPlan* plan, void* temp);
 
 // Segments of a sorted key array: seg_start[u] for every distinct key run, and
 // count (device int64).  Also touched[u] = key of run u (may be null).

@@ -301,11 +301,29 @@ size_t small_sort_lds_bytes(int64_t n) {
   return size_t(n) * 16 + size_t(kSmallWaves) * 256 * 4 + 64 * 4;
 }
 
+//
+// Grouped (gridDim.x > 1): workgroup g sorts pairs [g n, (g + 1) n) on their
+// own, the caller guaranteeing that every key of group g is below every key
+// of group g + 1, so the groups' sorted runs side by side are the sorted
+// whole.  Its segment table (n + 1 entries, positions global) and touched
+// keys go to group g's slice of seg_start / touched, its count to count[g];
+// group_segments_kernel then joins them (and builds the long-run plan).
 __global__ __launch_bounds__(kSmallThreads) void small_sort_segments_kernel(
     const uint32_t* __restrict__ keys_in, int n, int passes, uint32_t* __restrict__ keys_out,
     int32_t* __restrict__ vals_out, int32_t* __restrict__ seg_start, int32_t* __restrict__ touched,
     int64_t* __restrict__ count, int chunk, int2* __restrict__ chunk_list, int2* __restrict__ long_list,
     uint32_t* __restrict__ plan_counts) {
+  const int64_t base = int64_t(blockIdx.x) * n;  // this group's first pair
+  if (gridDim.x > 1) {  // grouped: the joining launch lists the long runs, into counters zeroed here
+    if (blockIdx.x == 0 && threadIdx.x == 0 && plan_counts) plan_counts[0] = plan_counts[1] = 0u;
+    plan_counts = nullptr;
+  }
+  keys_in += base;
+  keys_out += base;
+  vals_out += base;
+  seg_start += int64_t(blockIdx.x) * (n + 1);
+  if (touched) touched += base;
+  count += blockIdx.x;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   uint64_t* bufA = reinterpret_cast<uint64_t*>(smem);
   uint64_t* bufB = bufA + n;
@@ -313,7 +331,7 @@ __global__ __launch_bounds__(kSmallThreads) void small_sort_segments_kernel(
   uint32_t* wsum = cnt + kSmallWaves * 256;                 // [64]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) wsum[32] = wsum[33] = 0u;  // long-run plan counters
-  for (int i = tid; i < n; i += kSmallThreads) bufA[i] = (uint64_t(keys_in[i]) << 32) | uint32_t(i);
+  for (int i = tid; i < n; i += kSmallThreads) bufA[i] = (uint64_t(keys_in[i]) << 32) | uint32_t(base + i);
   // wave w owns pairs [w * per, (w + 1) * per), per a multiple of 64
   const int per = ((n + kSmallWaves - 1) / kSmallWaves + 63) / 64 * 64;
   const int rounds = per / 64;
@@ -387,7 +405,7 @@ __global__ __launch_bounds__(kSmallThreads) void small_sort_segments_kernel(
   // sorted pairs out; segment starts: the first key and every key that differs from its predecessor
   for (int i = tid; i < n; i += kSmallThreads) {
     keys_out[i] = uint32_t(src[i] >> 32);
-    vals_out[i] = int32_t(uint32_t(src[i]));
+    vals_out[i] = int32_t(uint32_t(src[i]));  // the pair's global index
   }
   const int ipt = (n + kSmallThreads - 1) / kSmallThreads;
   const int i0 = tid * ipt;
@@ -414,14 +432,14 @@ __global__ __launch_bounds__(kSmallThreads) void small_sort_segments_kernel(
   const bool plan = plan_counts != nullptr && n > 0;
   for (int j = 0; j < ipt; ++j) {
     if (flags & (1u << j)) {
-      seg_start[rank] = i0 + j;
+      seg_start[rank] = int32_t(base + i0 + j);
       if (touched) touched[rank] = int32_t(src[i0 + j] >> 32);
       if (plan) segl[rank] = i0 + j;
       ++rank;
     }
   }
   if (tid == 0) {
-    seg_start[total] = n;
+    seg_start[total] = int32_t(base + n);
     *count = int64_t(total);
     if (plan) segl[total] = n;
   }
@@ -441,6 +459,76 @@ __global__ __launch_bounds__(kSmallThreads) void small_sort_segments_kernel(
   if (tid == 0) {
     plan_counts[0] = wsum[32];
     plan_counts[1] = wsum[33];
+  }
+}
+
+// Joins the groups' segment tables (seg_g: group g's n_per + 1 entries at
+// g (n_per + 1), the last one its end; touched_g at g n_per; cnt_g[g]
+// segments) into one table of all n = groups * n_per pairs, and lists the
+// value gradient's long runs as long_run_plan_kernel does (plan counts zeroed
+// before, by the sorting launch).  Every block scans the group counts itself
+// (groups <= kSortGroupsMax) and takes a grid-stride share of the segments; a
+// run's length comes from its own group's table, so no block reads what
+// another writes.
+constexpr int kJoinThreads = 256;
+__global__ __launch_bounds__(kJoinThreads) void group_segments_kernel(
+    const int32_t* __restrict__ seg_g, const int32_t* __restrict__ touched_g, const int64_t* __restrict__ cnt_g,
+    int groups, int n_per, int32_t* __restrict__ seg_start, int32_t* __restrict__ touched,
+    int64_t* __restrict__ count, int chunk, int2* __restrict__ chunk_list, int2* __restrict__ long_list,
+    uint32_t* __restrict__ plan_counts) {
+  constexpr int kPer = kSortGroupsMax / kJoinThreads;  // group counts per thread
+  __shared__ uint32_t offs[kSortGroupsMax + 1];
+  __shared__ uint32_t wsum[kJoinThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t c[kPer], my = 0;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int g = tid * kPer + q;
+    c[q] = g < groups ? uint32_t(cnt_g[g]) : 0u;
+    my += c[q];
+  }
+  uint32_t x = my;
+#pragma unroll
+  for (int dd = 1; dd < 64; dd <<= 1) {
+    const uint32_t y = __shfl_up(x, dd, 64);
+    if (lane >= dd) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  uint32_t pre = x - my, total = 0;
+  for (int w = 0; w < kJoinThreads / 64; ++w) {
+    if (w < wave) pre += wsum[w];
+    total += wsum[w];
+  }
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    offs[tid * kPer + q] = pre;
+    pre += c[q];
+  }
+  if (tid == 0) offs[kSortGroupsMax] = total;
+  __syncthreads();
+  const uint32_t stride = gridDim.x * kJoinThreads;
+  for (uint32_t u = blockIdx.x * kJoinThreads + tid; u < total; u += stride) {
+    int lo = 0, hi = groups - 1;  // the group holding segment u: the last g with offs[g] <= u
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if (offs[mid] <= u) lo = mid; else hi = mid - 1;
+    }
+    const uint32_t j = u - offs[lo];
+    const int32_t* sg = seg_g + int64_t(lo) * (n_per + 1);
+    const int32_t a = sg[j], len = sg[j + 1] - a;
+    seg_start[u] = a;
+    if (touched) touched[u] = touched_g[int64_t(lo) * n_per + j];
+    if (len > chunk) {
+      const int nch = (len + chunk - 1) / chunk;
+      const uint32_t b = atomicAdd(&plan_counts[0], uint32_t(nch));
+      for (int q = 0; q < nch; ++q) chunk_list[b + q] = make_int2(int(u), q);
+      long_list[atomicAdd(&plan_counts[1], 1u)] = make_int2(int(u), int(b));
+    }
+  }
+  if (blockIdx.x == 0 && tid == 0) {
+    seg_start[total] = int32_t(int64_t(groups) * n_per);
+    *count = int64_t(total);
   }
 }
 
@@ -511,6 +599,41 @@ hipError_t launch_radix_sort_from(hipStream_t s, const uint32_t* keys_in, uint32
     }
   }
   *result_in_1 = (kin == k1);
+  return hipGetLastError();
+}
+
+size_t sort_groups_temp_bytes(int64_t n) {
+  return size_t(n + kSortGroupsMax) * 4 + size_t(n) * 4 + size_t(kSortGroupsMax) * 8 + 64;
+}
+
+hipError_t launch_sort_segments_grouped(hipStream_t s, const uint32_t* keys_in, int64_t n, int groups,
+                                        int key_bits, uint32_t* keys_out, int32_t* vals_out, int32_t* seg_start,
+                                        int32_t* touched, int64_t* count, const VgPlan* plan, void* temp) {
+  if (groups < 1 || groups > kSortGroupsMax || n % groups || n / groups > kSmallSortMax || plan == nullptr)
+    return hipErrorInvalidValue;
+  const int n_per = int(n / groups);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(small_sort_segments_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       int(small_sort_lds_bytes(kSmallSortMax)));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  int passes = (key_bits + 7) / 8;
+  if (passes < 1) passes = 1;
+  if (passes > 4) passes = 4;
+  int32_t* seg_g = static_cast<int32_t*>(temp);             // groups x (n_per + 1)
+  int32_t* touched_g = seg_g + n + kSortGroupsMax;          // groups x n_per
+  int64_t* cnt_g = reinterpret_cast<int64_t*>(touched_g + n);  // groups (8-byte aligned: n + n + 1024 ints)
+  hipLaunchKernelGGL(small_sort_segments_kernel, dim3(unsigned(groups)), dim3(kSmallThreads),
+                     small_sort_lds_bytes(n_per), s, keys_in, n_per, passes, keys_out, vals_out, seg_g, touched_g,
+                     cnt_g, kVgChunk, nullptr, nullptr, plan->counts);
+  int64_t jb = (n + kJoinThreads - 1) / kJoinThreads;
+  if (jb > 1024) jb = 1024;
+  hipLaunchKernelGGL(group_segments_kernel, dim3(unsigned(jb)), dim3(kJoinThreads), 0, s, seg_g, touched_g, cnt_g,
+                     groups, n_per, seg_start, touched, count, kVgChunk, plan->chunk_list, plan->long_list,
+                     plan->counts);
   return hipGetLastError();
 }
 

@@ -360,7 +360,10 @@ def test_fwpkm_chunk_at_the_benchmark_configuration():
 BATCH_CASES = [
     # streams, tokens per stream, heads, dq, nk, k, d_value, dtype
     (3, 40, 2, 16, 12, 4, 24, "f32"),            # 960 lookups: one-workgroup grouping
-    (4, 512, 1, 32, 64, 8, 32, "bf16"),          # 16384 lookups: radix sort, 4 x 4096 slots
+    (4, 512, 1, 32, 64, 8, 32, "bf16"),          # 16384 lookups: a workgroup per stream, 4 x 4096 slots
+    (3, 2000, 1, 16, 4, 4, 32, "f32"),           # a workgroup per stream, ~500 lookups per row: long runs
+    (64, 64, 2, 16, 16, 8, 16, "f32"),           # 64 streams of 1024 lookups
+    (2, 4608, 1, 16, 64, 2, 16, "f32"),          # 9216 lookups per stream: above one workgroup, radix sort
 ]
 
 
