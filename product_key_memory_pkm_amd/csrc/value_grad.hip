@@ -142,12 +142,14 @@ __device__ __forceinline__ void vg_accumulate(const VgArgs& a, const LaneVecs<NV
 #pragma unroll
             for (int e = 0; e < E; ++e) g[m][e] = fmaf(wt, f[e], g[m][e]);
           }
-          const float sm = wave_sum_dpp(part);
-          if (lane == j + uu) my_dw = sm;
+          if (!a.sgd) {  // wave-uniform: the plain step has no use for dw
+            const float sm = wave_sum_dpp(part);
+            if (lane == j + uu) my_dw = sm;
+          }
         }
       }
     }
-    if (lane < n) a.dw[my_c] = my_dw;
+    if (!a.sgd && lane < n) a.dw[my_c] = my_dw;
   }
 }
 
