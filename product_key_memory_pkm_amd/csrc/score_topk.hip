@@ -56,8 +56,8 @@ __device__ __forceinline__ float wave_min_f32(float v) {
   return v;
 }
 
-constexpr int kBoundSteps = 12;
-constexpr float kIdwFloor = 1e-12f;  // squared-distance floor of the IDW scores  // halvings of the selection bound's search range
+constexpr int kBoundSteps = 12;       // halvings of the selection bound's search range
+constexpr float kIdwFloor = 1e-12f;  // squared-distance floor of the IDW scores
 
 __device__ __forceinline__ int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
