@@ -446,12 +446,9 @@ hipError_t launch_gemm_nt(hipStream_t s, int dtype, int64_t M, int64_t N, int64_
     kchunk = (kchunk + 31) / 32 * 32;
     const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
     const size_t lds = size_t(kDmaStages) * kDmaStage;
-    static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
-    if (!attr_set) {
-      hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_nt_dma_kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-      attr_set = true;
-    }
+    static LdsLimit lim;
+    const hipError_t e = lim.ensure(reinterpret_cast<const void*>(gemm_nt_dma_kernel), int(lds));
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(gemm_nt_dma_kernel, dim3(unsigned(tiles), unsigned(splits)), dim3(512), lds, s, M, N,
                        static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(B), ldb, C, ldc,
                        int(out_bf16), K, kchunk, split_stride);

@@ -5,7 +5,30 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace pkm {
+
+// Raises one kernel's dynamic LDS limit (hipFuncAttributeMaxDynamicSharedMemorySize)
+// to `bytes` the first time it is launched on each device: devices 0..63 are
+// remembered, others set it on every launch.  Safe to call from several host
+// threads (two first launches may both set it, which is harmless).
+class LdsLimit {
+ public:
+  hipError_t ensure(const void* fn, int bytes) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t(1) << dev : 0;
+    if (bit != 0 && (done_.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) done_.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
+  }
+
+ private:
+  std::atomic<uint64_t> done_{0};
+};
 
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;

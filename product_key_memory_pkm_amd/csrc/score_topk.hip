@@ -580,7 +580,7 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(
 
 
 template <typename T, int TM>
-void launch_tm(hipStream_t s, const Plan& pl, const void* q, int64_t ntok, int heads, int dq, const u32x4* C,
+hipError_t launch_tm(hipStream_t s, const Plan& pl, const void* q, int64_t ntok, int heads, int dq, const u32x4* C,
                const u32x4* Cp, int nk, int nk2, int k, int32_t* sub_idx, float* sub_score, const float* cc1,
                const float* cc2) {
   const int half = dq / 2;
@@ -590,8 +590,9 @@ void launch_tm(hipStream_t s, const Plan& pl, const void* q, int64_t ntok, int h
   case NPLV: {                                                                                        \
     if constexpr ((TM / kWaves) * NPLV <= 64) { /* the plan never pairs a tall tile with wide rows */ \
       auto fn = score_topk_kernel<T, TM, NPLV>;                                                       \
-      hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, \
-                          int(pl.lds));                                                               \
+      static LdsLimit lim; /* the largest plan's LDS, set once per device */                          \
+      const hipError_t e = lim.ensure(reinterpret_cast<const void*>(fn), int(kLdsLimit));             \
+      if (e != hipSuccess) return e;                                                                  \
       hipLaunchKernelGGL(fn, grid, dim3(kThreads), pl.lds, s, static_cast<const T*>(q), ntok, F, dq, half, \
                          pl.half_pad, pl.qstride, C, Cp, nk,                                           \
                          nk2, k, pl.cw, pl.sstride, sub_idx, sub_score, cc1, cc2);                   \
@@ -607,18 +608,16 @@ void launch_tm(hipStream_t s, const Plan& pl, const void* q, int64_t ntok, int h
       break;
   }
 #undef PKM_SCORE_CASE
+  return hipSuccess;
 }
 
 template <typename T>
-void launch_t(hipStream_t s, const Plan& pl, const void* q, int64_t ntok, int heads, int dq, const u32x4* C,
+hipError_t launch_t(hipStream_t s, const Plan& pl, const void* q, int64_t ntok, int heads, int dq, const u32x4* C,
               const u32x4* Cp, int nk, int nk2, int k, int32_t* sub_idx, float* sub_score, const float* cc1,
               const float* cc2) {
-  if (pl.TM == 64)
-    launch_tm<T, 64>(s, pl, q, ntok, heads, dq, C, Cp, nk, nk2, k, sub_idx, sub_score, cc1, cc2);
-  else if (pl.TM == 32)
-    launch_tm<T, 32>(s, pl, q, ntok, heads, dq, C, Cp, nk, nk2, k, sub_idx, sub_score, cc1, cc2);
-  else
-    launch_tm<T, 16>(s, pl, q, ntok, heads, dq, C, Cp, nk, nk2, k, sub_idx, sub_score, cc1, cc2);
+  if (pl.TM == 64) return launch_tm<T, 64>(s, pl, q, ntok, heads, dq, C, Cp, nk, nk2, k, sub_idx, sub_score, cc1, cc2);
+  if (pl.TM == 32) return launch_tm<T, 32>(s, pl, q, ntok, heads, dq, C, Cp, nk, nk2, k, sub_idx, sub_score, cc1, cc2);
+  return launch_tm<T, 16>(s, pl, q, ntok, heads, dq, C, Cp, nk, nk2, k, sub_idx, sub_score, cc1, cc2);
 }
 
 }  // namespace
@@ -673,10 +672,10 @@ hipError_t launch_score_topk(hipStream_t s, int dtype, const void* q, int64_t nt
     hipLaunchKernelGGL(pack_keys_kernel<float>, dim3(unsigned(pb + nb)), dim3(256), 0, s,
                        static_cast<const float*>(C), nk, static_cast<const float*>(Cp), nk2, heads, half, nks,
                        int(pb), P1, cc1);
-  if (dtype == kBF16)
-    launch_t<bf16_t>(s, pl, q, ntok, heads, dq, P1, P2, nk, nk2, k, sub_idx, sub_score, cc1, cc2);
-  else
-    launch_t<float>(s, pl, q, ntok, heads, dq, P1, P2, nk, nk2, k, sub_idx, sub_score, cc1, cc2);
+  const hipError_t e = dtype == kBF16
+                           ? launch_t<bf16_t>(s, pl, q, ntok, heads, dq, P1, P2, nk, nk2, k, sub_idx, sub_score, cc1, cc2)
+                           : launch_t<float>(s, pl, q, ntok, heads, dq, P1, P2, nk, nk2, k, sub_idx, sub_score, cc1, cc2);
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

@@ -532,6 +532,12 @@ __global__ __launch_bounds__(kJoinThreads) void group_segments_kernel(
   }
 }
 
+// The one-workgroup sort's LDS limit, raised to what kSmallSortMax keys need.
+hipError_t small_sort_lds_limit() {
+  static LdsLimit lim;
+  return lim.ensure(reinterpret_cast<const void*>(small_sort_segments_kernel), int(small_sort_lds_bytes(kSmallSortMax)));
+}
+
 inline unsigned grid1d(int64_t n, int64_t cap = 16384) {
   int64_t b = (n + 255) / 256;
   if (b > cap) b = cap;
@@ -612,13 +618,9 @@ hipError_t launch_sort_segments_grouped(hipStream_t s, const uint32_t* keys_in, 
   if (groups < 1 || groups > kSortGroupsMax || n % groups || n / groups > kSmallSortMax || plan == nullptr)
     return hipErrorInvalidValue;
   const int n_per = int(n / groups);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(small_sort_segments_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       int(small_sort_lds_bytes(kSmallSortMax)));
+  {
+    const hipError_t e = small_sort_lds_limit();
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   int passes = (key_bits + 7) / 8;
   if (passes < 1) passes = 1;
@@ -641,13 +643,9 @@ hipError_t launch_sort_segments_small(hipStream_t s, const uint32_t* keys_in, in
                                       uint32_t* keys_out, int32_t* vals_out, int32_t* seg_start, int32_t* touched,
                                       int64_t* count, const VgPlan* plan) {
   if (n < 0 || n > kSmallSortMax) return hipErrorInvalidValue;
-  static bool attr_set = false;  // the attribute is per function; setting it again is harmless
-  const size_t lds = small_sort_lds_bytes(kSmallSortMax);
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(small_sort_segments_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  {
+    const hipError_t e = small_sort_lds_limit();
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   int passes = (key_bits + 7) / 8;
   if (passes < 1) passes = 1;
