@@ -39,7 +39,8 @@
  *  - stream: a hipStream_t passed as void* (NULL = the default stream).  Work is
  *    enqueued asynchronously and the call returns without synchronising; values
  *    written on the device (outputs, *n_touched) are valid once the stream has
- *    reached them.
+ *    reached them.  Kernels run on the device current at the call, which must
+ *    be the stream's device and hold (or reach) every device pointer passed.
  *  - Storage dtype (pkm_config.dtype) applies to x, W_q, C, C', V, y, dY, dx and
  *    the saved q.  Arithmetic is fp32 (bf16 storage: bf16 MFMA operands, fp32
  *    accumulation; q is rounded to bf16 after BatchNorm).  All gradients

@@ -694,11 +694,18 @@ static pkm_status backward_impl(pkm_handle_t handle, void* stream, int64_t T, co
     std::lock_guard<std::mutex> lock(hm->side_mu);
     PKM_HIP(hipEventRecord(hm->fork, s), "fork event");
     PKM_HIP(hipStreamWaitEvent(hm->side, hm->fork, 0), "side stream wait");
-    PKM_TRY(run_subkey_halves(handle, hm->side, T, saved->q, dC, dCp, ws));
-    PKM_HIP(hipEventRecord(hm->join, hm->side), "join event");
-    PKM_TRY(run_query_grad(handle, s, T, dq, x, Wq, bn_gamma, saved, dWq, bn ? dgamma : nullptr,
-                           bn ? dbeta : nullptr, dx, ws));
-    PKM_HIP(hipStreamWaitEvent(s, hm->join, 0), "join wait");
+    const pkm_status side_st = run_subkey_halves(handle, hm->side, T, saved->q, dC, dCp, ws);
+    const hipError_t joined = hipEventRecord(hm->join, hm->side);
+    const pkm_status main_st = run_query_grad(handle, s, T, dq, x, Wq, bn_gamma, saved, dWq,
+                                              bn ? dgamma : nullptr, bn ? dbeta : nullptr, dx, ws);
+    // the caller's stream waits for the side stream whatever failed above, so
+    // that no work queued there outlives the call unordered
+    const hipError_t waited =
+        joined == hipSuccess ? hipStreamWaitEvent(s, hm->join, 0) : hipStreamSynchronize(hm->side);
+    PKM_TRY(side_st);
+    PKM_TRY(main_st);
+    PKM_HIP(joined, "join event");
+    PKM_HIP(waited, "join wait");
     return PKM_OK;
   }
   PKM_TRY(run_subkey_halves(handle, s, T, saved->q, dC, dCp, ws));
