@@ -32,8 +32,8 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 # holds for the kernel sources whose combined sha256 prefix is given; any change to them voids it (traffic null).
 KERNEL_TRAFFIC = {
     ("gather", "paper"): {"bytes": 13552071360, "sources": ["gather.hip", "common.h"], "sources_sha256_16": "993549f60bba5340"},
-    ("value_grad", "paper"): {"bytes": 29584441392, "sources": ["value_grad.hip", "sparse_common.h", "common.h"], "sources_sha256_16": "fe02fe8ec3212e42"},
-    ("value_adam", "paper"): {"bytes": 46085680384, "sources": ["value_grad.hip", "sparse_common.h", "common.h"], "sources_sha256_16": "fe02fe8ec3212e42"},
+    ("value_grad", "paper"): {"bytes": 29587513344, "sources": ["value_grad.hip", "sparse_common.h", "common.h"], "sources_sha256_16": "f89182f4dea94374"},
+    ("value_adam", "paper"): {"bytes": 46090845184, "sources": ["value_grad.hip", "sparse_common.h", "common.h"], "sources_sha256_16": "f89182f4dea94374"},
 }
 
 
@@ -72,6 +72,8 @@ def parse():
                     help="run this many fast-weight memorization chunks and nothing else (for profilers)")
     ap.add_argument("--profile-fwpkm-batch", action="store_true",
                     help="run the batched fast-weight memorization calls once and nothing else (for profilers)")
+    ap.add_argument("--profile-fwpkm-one-call", action="store_true",
+                    help="memorize the fast-weight stream in one pkm_fwpkm_chunks call and nothing else (for profilers)")
     ap.add_argument("--no-fwpkm", action="store_true", help="skip the fast-weight memorization legs")
     return ap.parse_args()
 
@@ -183,6 +185,7 @@ def main():
 
     import pkm_inputs as pi
     from product_key_memory_pkm_amd import (PKM_WS_FWPKM_CHUNK, ProductKeyMemory, pkm_diagnostics, pkm_fwpkm_chunk,
+                                            pkm_fwpkm_chunks,
                                             pkm_quantize_values, pkm_stage_gather, pkm_stage_merge_softmax,
                                             pkm_stage_query, pkm_stage_query_grad, pkm_stage_subkey_grad,
                                             pkm_stage_row_groups, pkm_stage_score_topk, pkm_stage_value_adam_grouped,
@@ -276,6 +279,16 @@ def main():
         fwpkm_batch_run(st, FWPKM_BATCH_CHUNKS)
         torch.cuda.synchronize()
         print(json.dumps({"profile_fwpkm_batch": FWPKM_BATCH_CHUNKS}), flush=True)
+        return
+    if args.profile_fwpkm_one_call:
+        st = fwpkm_setup()
+        n_all = FWPKM_CHUNK * FWPKM_CHUNKS
+        pkm_fwpkm_chunks(st["m"].handle, n_all, FWPKM_CHUNK, st["q"], st["C"], st["Cp"], st["V"], st["target"],
+                         FWPKM_LR, st["y"], torch.empty((n_all, 1, FWPKM_TOPK), dtype=torch.int32, device="cuda"),
+                         torch.empty((n_all, 1, FWPKM_TOPK), dtype=torch.float32, device="cuda"),
+                         st["m"].workspace(n_all, PKM_WS_FWPKM_CHUNK))
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_fwpkm_one_call": FWPKM_CHUNKS}), flush=True)
         return
     if args.profile_fwpkm:
         st = fwpkm_setup()
@@ -443,6 +456,25 @@ def main():
         ms_fw_graph = start.elapsed_time(end)
         del graph
         touched_c = int(torch.unique(st["idx"]).numel())   # the last chunk's distinct rows
+        # the same 64 chunks in one pkm_fwpkm_chunks call: the selection of every chunk first (it does
+        # not read V), then each chunk's gather and value step in order; timed on a second pass
+        n_all = FWPKM_CHUNK * FWPKM_CHUNKS
+        ws_all = st["m"].workspace(n_all, PKM_WS_FWPKM_CHUNK)
+        idx_all = torch.empty((n_all, 1, FWPKM_TOPK), dtype=torch.int32, device="cuda")
+        w_all = torch.empty((n_all, 1, FWPKM_TOPK), dtype=torch.float32, device="cuda")
+
+        def fwpkm_one_call():
+            pkm_fwpkm_chunks(st["m"].handle, n_all, FWPKM_CHUNK, st["q"], st["C"], st["Cp"], st["V"], st["target"],
+                             FWPKM_LR, st["y"], idx_all, w_all, ws_all)
+
+        fwpkm_one_call()
+        torch.cuda.synchronize()
+        start.record()
+        fwpkm_one_call()
+        end.record()
+        torch.cuda.synchronize()
+        ms_fw_one = start.elapsed_time(end)
+        del ws_all, idx_all, w_all
         e_ = 2 if cfg.dtype == "bf16" else 4
         cb = fwpkm_chunk_bytes(FWPKM_CHUNK, FWPKM_TOPK, cfg.d_value, e_, touched_c)
         ms_chunk = ms_fw / FWPKM_CHUNKS
@@ -453,6 +485,8 @@ def main():
               "host_enqueue_ms_per_chunk": host_s * 1e3 / FWPKM_CHUNKS,
               "tokens_per_s_graph_replay": FWPKM_CHUNK * FWPKM_CHUNKS / (ms_fw_graph * 1e-3),
               "ms_per_chunk_graph_replay": ms_fw_graph / FWPKM_CHUNKS,
+              "tokens_per_s_one_call": n_all / (ms_fw_one * 1e-3),
+              "ms_per_chunk_one_call": ms_fw_one / FWPKM_CHUNKS,
               "touched_rows_last_chunk": touched_c, "alg_bytes_per_chunk": cb,
               "achieved_GBs_whole_chunk": cb / (ms_chunk * 1e-3) / 1e9}
         del st

@@ -359,6 +359,21 @@ pkm_status pkm_fwpkm_chunk(pkm_handle_t handle, void* stream, int64_t T, int64_t
                            const void* C, const void* Cp, void* V, const void* target, float lr, void* y,
                            int32_t* idx, float* w, void* ws, size_t ws_bytes);
 
+/* A run of memorization calls in one: the same as calling pkm_fwpkm_chunk on
+ * the consecutive slices of call_T tokens of q, target, y, idx and w (slice j
+ * is rows [j*call_T, (j+1)*call_T)), in order, with the same streams, V and lr;
+ * the results are those calls' results, bit for bit.  For a stream whose
+ * queries are all known before it is memorized (a prompt, a document): the
+ * selection reads only q, C and C', not V ("Fast-weight Product Key Memory",
+ * section 2.2: memorization writes the value table only), so it runs once over
+ * all T tokens, and each slice then runs only its gather and its value step.
+ * T a multiple of call_T, call_T a multiple of streams; other arguments as in
+ * pkm_fwpkm_chunk, with T tokens.  ws >= pkm_workspace_size(handle, T,
+ * PKM_WS_FWPKM_CHUNK). */
+pkm_status pkm_fwpkm_chunks(pkm_handle_t handle, void* stream, int64_t T, int64_t call_T, int64_t streams,
+                            const void* q, const void* C, const void* Cp, void* V, const void* target, float lr,
+                            void* y, int32_t* idx, float* w, void* ws, size_t ws_bytes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -80,6 +80,8 @@ _SIGS = {
     "pkm_stage_query_grad": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_saved), _VP, _VP, _VP, _VP,
                              _VP, _SZ],
     "pkm_fwpkm_chunk": [_VP, _VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP, _VP, _VP, _VP, _SZ],
+    "pkm_fwpkm_chunks": [_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP, _VP, _VP, _VP,
+                         _SZ],
 }
 EXPORTED = sorted(list(_SIGS) + ["pkm_status_string", "pkm_last_error"])
 
@@ -361,3 +363,15 @@ def pkm_fwpkm_chunk(h, T, q, C, Cp, V, target, lr, y, idx, w, ws, streams=1):
     _dt(w, torch.float32, "w")
     _check(_invoke("pkm_fwpkm_chunk", h, T, int(streams), _ptr(q), _ptr(C), _ptr(Cp), _ptr(V), _ptr(target),
                    float(lr), _ptr(y), _ptr(idx), _ptr(w), _ptr(ws), _nbytes(ws)), "pkm_fwpkm_chunk")
+
+
+def pkm_fwpkm_chunks(h, T, call_T, q, C, Cp, V, target, lr, y, idx, w, ws, streams=1):
+    """pkm_fwpkm_chunk on the consecutive slices of ``call_T`` tokens, in order, in one call (pkm.h): the
+    selection of all T tokens first (it does not read V), then each slice's gather and value step."""
+    st = h.storage
+    for n, t in (("q", q), ("C", C), ("Cp", Cp), ("V", V), ("target", target), ("y", y)):
+        _dt(t, st, n)
+    _dt(idx, torch.int32, "idx")
+    _dt(w, torch.float32, "w")
+    _check(_invoke("pkm_fwpkm_chunks", h, T, int(call_T), int(streams), _ptr(q), _ptr(C), _ptr(Cp), _ptr(V),
+                   _ptr(target), float(lr), _ptr(y), _ptr(idx), _ptr(w), _ptr(ws), _nbytes(ws)), "pkm_fwpkm_chunks")

@@ -148,7 +148,7 @@ BwdLayout bwd_layout(const pkm_handle_s* h, int64_t T) {
 // after the other), then the residual e [T, d_value] (storage dtype), the
 // touched rows and their count.
 struct ChunkLayout {
-  size_t e, touched, n_touched, total;
+  size_t e, touched, n_touched, plans, total;
 };
 
 ChunkLayout chunk_layout(const pkm_handle_s* h, int64_t T) {
@@ -158,6 +158,7 @@ ChunkLayout chunk_layout(const pkm_handle_s* h, int64_t T) {
   L.e = o; o += al(size_t(T) * h->cfg.d_value * h->elem);
   L.touched = o; o += al(N * 4);
   L.n_touched = o; o += al(sizeof(int64_t));
+  L.plans = o; o += al(size_t(kSortGroupsMax) * group_plan_stride());  // pkm_fwpkm_chunks' per-call plans
   L.total = o;
   return L;
 }
@@ -246,10 +247,10 @@ pkm_status run_score(const pkm_handle_s* h, hipStream_t s, int64_t T, const void
 }
 
 pkm_status run_merge(const pkm_handle_s* h, hipStream_t s, int64_t T, const int32_t* sub_idx, const float* sub_score,
-                     int32_t* idx, float* w, float* score, int64_t group_tokens = 0) {
+                     int32_t* idx, float* w, float* score, int64_t group_tokens = 0, int64_t group_count = 1) {
   const pkm_config& c = h->cfg;
   PKM_HIP(launch_merge_softmax(s, sub_idx, sub_score, T * c.heads, c.topk, c.n_keys2, 1.0f / c.temperature, idx, w,
-                               score, group_tokens * c.heads, int64_t(c.n_keys) * c.n_keys2),
+                               score, group_tokens * c.heads, int64_t(c.n_keys) * c.n_keys2, group_count),
           "candidate merge / softmax");
   return PKM_OK;
 }
@@ -971,9 +972,15 @@ pkm_status pkm_stage_query_grad(pkm_handle_t handle, void* stream, int64_t T, co
 
 }  // extern "C"
 
-pkm_status pkm_fwpkm_chunk(pkm_handle_t handle, void* stream, int64_t T, int64_t streams, const void* q,
-                           const void* C, const void* Cp, void* V, const void* target, float lr, void* y, int32_t* idx,
-                           float* w, void* ws, size_t ws_bytes) {
+namespace {
+
+// pkm_fwpkm_chunk over consecutive slices of call_T tokens, in order.  The
+// selection reads only q, C and C', never V, so it runs once over all T tokens
+// (the merge's table offsets cycle over the streams every call_T tokens); then
+// each slice runs its gather with the residual and its value step.
+pkm_status fwpkm_calls(pkm_handle_t handle, void* stream, int64_t T, int64_t call_T, int64_t streams,
+                       const void* q, const void* C, const void* Cp, void* V, const void* target, float lr, void* y,
+                       int32_t* idx, float* w, void* ws, size_t ws_bytes) {
   PKM_TRY(check_handle(handle));
   PKM_TRY(need_storage_values(handle));
   if (handle->cfg.score_fn != PKM_SCORE_IDW)
@@ -989,8 +996,11 @@ pkm_status pkm_fwpkm_chunk(pkm_handle_t handle, void* stream, int64_t T, int64_t
   PKM_TRY(need(w, "w"));
   if (!(std::isfinite(lr) && lr >= 0.f)) return fail(PKM_ERR_INVALID_ARG, "lr must be finite and >= 0");
   if (streams < 1) return fail(PKM_ERR_INVALID_ARG, "streams = %lld < 1", (long long)streams);
-  if (T % streams) return fail(PKM_ERR_INVALID_ARG, "T = %lld is not a multiple of streams = %lld", (long long)T,
-                               (long long)streams);
+  if (call_T < 1 || T % call_T)
+    return fail(PKM_ERR_INVALID_ARG, "T = %lld is not a multiple of call_T = %lld", (long long)T, (long long)call_T);
+  if (call_T % streams)
+    return fail(PKM_ERR_INVALID_ARG, "call_T = %lld is not a multiple of streams = %lld", (long long)call_T,
+                (long long)streams);
   const pkm_config& c = handle->cfg;
   const int64_t rows = streams * int64_t(c.n_keys) * c.n_keys2;
   if (rows >= (int64_t(1) << 31))
@@ -1001,19 +1011,79 @@ pkm_status pkm_fwpkm_chunk(pkm_handle_t handle, void* stream, int64_t T, int64_t
   while ((int64_t(1) << bits) < rows) ++bits;
   hipStream_t s = as_stream(stream);
   const FwdLayout F = fwd_layout(handle, T);
-  const BwdLayout B = bwd_layout(handle, T);
   const ChunkLayout L = chunk_layout(handle, T);
   int32_t* sub_idx = at<int32_t>(ws, F.sub_idx);
   float* sub_score = at<float>(ws, F.sub_score);
   PKM_TRY(run_score(handle, s, T, q, C, Cp, sub_idx, sub_score, ws));
-  PKM_TRY(run_merge(handle, s, T, sub_idx, sub_score, idx, w, nullptr, streams > 1 ? T / streams : 0));
+  PKM_TRY(run_merge(handle, s, T, sub_idx, sub_score, idx, w, nullptr, streams > 1 ? call_T / streams : 0, streams));
+  // the slices' steps reuse the scoring's workspace (its results are in idx and w)
+  const int64_t R = int64_t(c.heads) * c.topk;
+  const size_t row_bytes = size_t(c.d_value) * size_t(handle->elem);
+  const int64_t calls = T / call_T, n_call = call_T * R;
+  if (streams == 1 && calls > 1 && calls <= kSortGroupsMax && n_call <= kSmallSortMax) {
+    // One stream whose calls each fit one workgroup's grouping: every call's
+    // grouping (and long-run plan) in one launch of a workgroup per call, up
+    // front (it reads only idx), then per call the gather with the residual
+    // and the value step on that call's own table of row segments.  Lookup ids,
+    // segment positions and the residual rows are global, so the per-row sums
+    // run over the same lookups in the same order as in separate calls.
+    const BwdLayout B = bwd_layout(handle, T);
+    uint32_t* sk = at<uint32_t>(ws, B.k0);
+    int32_t* sv = at<int32_t>(ws, B.v0);
+    int32_t* seg_g = at<int32_t>(ws, B.grp);                                            // calls x (n_call + 1)
+    int64_t* cnt_g = reinterpret_cast<int64_t*>(seg_g + 2 * T * R + kSortGroupsMax);  // calls
+    void* plans = at<void>(ws, L.plans);
+    PKM_HIP(launch_sort_segments_separate(s, reinterpret_cast<const uint32_t*>(idx), T * R, int(calls), bits, sk, sv,
+                                          seg_g, cnt_g, plans),
+            "row grouping of every call");
+    char* e = at<char>(ws, L.e);  // T rows: residual rows sit at their tokens' positions
+    VgAdam sgd{};
+    sgd.V = V;
+    sgd.step_size = lr;
+    sgd.sgd = 1;
+    for (int64_t g = 0; g < calls; ++g) {
+      const int64_t t0 = g * call_T;
+      PKM_HIP(launch_gather(s, c.dtype, idx + t0 * R, w + t0 * R, V, static_cast<char*>(y) + t0 * row_bytes, call_T,
+                            int(R), c.d_value, false, static_cast<const char*>(target) + t0 * row_bytes,
+                            e + t0 * row_bytes),
+              "value gather-sum and reconstruction residual");
+      const VgPlan plan = group_plan(plans, int(g));
+      PKM_HIP(launch_value_grad(s, c.dtype, seg_g + g * (n_call + 1), cnt_g + g, n_call, sk, sv, w, e, V, nullptr,
+                                at<float>(ws, B.dw), int(R), c.d_value, c.accumulate_dv != 0, at<void>(ws, B.aux),
+                                &sgd, true, &plan),
+              "value step");
+    }
+    return PKM_OK;
+  }
+  const BwdLayout B = bwd_layout(handle, call_T);
   void* e = at<void>(ws, L.e);
-  PKM_HIP(launch_gather(s, c.dtype, idx, w, V, y, T, c.heads * c.topk, c.d_value, false, target, e),
-          "value gather-sum and reconstruction residual");
-  VgAdam sgd{};
-  sgd.V = V;
-  sgd.step_size = lr;
-  sgd.sgd = 1;
-  return run_value_grad(handle, s, T, idx, w, e, V, nullptr, at<int32_t>(ws, L.touched), at<int64_t>(ws, L.n_touched),
-                        at<float>(ws, B.dw), ws, &sgd, bits, int(streams));
+  for (int64_t t0 = 0; t0 < T; t0 += call_T) {
+    const int32_t* ci = idx + t0 * R;
+    const float* cw = w + t0 * R;
+    PKM_HIP(launch_gather(s, c.dtype, ci, cw, V, static_cast<char*>(y) + t0 * row_bytes, call_T, int(R), c.d_value,
+                          false, static_cast<const char*>(target) + t0 * row_bytes, e),
+            "value gather-sum and reconstruction residual");
+    VgAdam sgd{};
+    sgd.V = V;
+    sgd.step_size = lr;
+    sgd.sgd = 1;
+    PKM_TRY(run_value_grad(handle, s, call_T, ci, cw, e, V, nullptr, at<int32_t>(ws, L.touched),
+                           at<int64_t>(ws, L.n_touched), at<float>(ws, B.dw), ws, &sgd, bits, int(streams)));
+  }
+  return PKM_OK;
+}
+
+}  // namespace
+
+pkm_status pkm_fwpkm_chunk(pkm_handle_t handle, void* stream, int64_t T, int64_t streams, const void* q,
+                           const void* C, const void* Cp, void* V, const void* target, float lr, void* y, int32_t* idx,
+                           float* w, void* ws, size_t ws_bytes) {
+  return fwpkm_calls(handle, stream, T, T > 0 ? T : (streams > 0 ? streams : 1), streams, q, C, Cp, V, target, lr, y,
+                     idx, w, ws, ws_bytes);
+}
+
+pkm_status pkm_fwpkm_chunks(pkm_handle_t handle, void* stream, int64_t T, int64_t call_T, int64_t streams,
+                            const void* q, const void* C, const void* Cp, void* V, const void* target, float lr,
+                            void* y, int32_t* idx, float* w, void* ws, size_t ws_bytes) {
+  return fwpkm_calls(handle, stream, T, call_T, streams, q, C, Cp, V, target, lr, y, idx, w, ws, ws_bytes);
 }

@@ -54,11 +54,13 @@ hipError_t launch_score_topk(hipStream_t s, int dtype, const void* q, int64_t nt
                              float* sub_score, void* packed, bool idw = false);
 
 // a5: k x k candidates -> top-k -> softmax, per (token, head).
-// group_items > 0: item i's rows are offset by (i / group_items) * group_rows
-// (consecutive groups of items address consecutive tables of group_rows rows).
+// group_items > 0: item i's rows are offset by ((i / group_items) % group_count) * group_rows
+// (consecutive groups of items address consecutive tables of group_rows rows,
+// starting over at the first table every group_count groups).
 hipError_t launch_merge_softmax(hipStream_t s, const int32_t* sub_idx, const float* sub_score,
                                 int64_t nitems, int k, int nk2, float inv_tau, int32_t* idx, float* w,
-                                float* score, int64_t group_items = 0, int64_t group_rows = 0);
+                                float* score, int64_t group_items = 0, int64_t group_rows = 0,
+                                int64_t group_count = 1);
 
 // C[M, N] = A[M, K] * B[N, K]^T; A, B storage dtype, C fp32 (or bf16 when out_bf16).
 // splits > 1: blockIdx.z handles a slice of K and writes C + z * split_stride.
@@ -137,6 +139,15 @@ hipError_t launch_sort_segments_small(hipStream_t s, const uint32_t* keys_in, in
 // temp: sort_groups_temp_bytes(n).
 constexpr int kSortGroupsMax = 1024;
 size_t sort_groups_temp_bytes(int64_t n);
+// The groups left apart (no key order between them needed): group g of the
+// n / groups pairs [g n/groups, (g+1) n/groups) gets its own segment table at
+// seg_g + g (n/groups + 1) (positions global), count at cnt_g[g] and long-run
+// plan group_plan(plans, g); plans holds groups * group_plan_stride() bytes.
+size_t group_plan_stride();
+VgPlan group_plan(void* plans, int g);
+hipError_t launch_sort_segments_separate(hipStream_t s, const uint32_t* keys_in, int64_t n, int groups, int key_bits,
+                                         uint32_t* keys_out, int32_t* vals_out, int32_t* seg_g, int64_t* cnt_g,
+                                         void* plans);
 hipError_t launch_sort_segments_grouped(hipStream_t s, const uint32_t* keys_in, int64_t n, int groups,
                                         int key_bits, uint32_t* keys_out, int32_t* vals_out, int32_t* seg_start,
                                         int32_t* touched, int64_t* count, const VgPlan* plan, void* temp);
@@ -167,7 +178,7 @@ hipError_t launch_value_grad(hipStream_t s, int dtype, const int32_t* seg_start,
                              int64_t nitems, const uint32_t* sorted_rows, const int32_t* sorted_c,
                              const float* w, const void* dY, const void* V, float* dV, float* dw,
                              int R, int d_value, bool accumulate, void* aux, const VgAdam* adam = nullptr,
-                             bool plan_ready = false);
+                             bool plan_ready = false, const VgPlan* plan = nullptr);
 
 // a7 + a9: per (token, head) softmax backward, dq from the distinct selected
 // sub-keys, and per slot the sub-key sort key (h*|C|+i / h*|C'|+j, or the

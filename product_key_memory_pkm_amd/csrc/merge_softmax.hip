@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void merge_softmax_kernel(const int32_t* __res
                                                             int64_t nitems, int k, int nk2, float inv_tau,
                                                             int32_t* __restrict__ idx, float* __restrict__ w,
                                                             float* __restrict__ score, int64_t group_items,
-                                                            int64_t group_rows) {
+                                                            int64_t group_rows, int64_t group_count) {
   __shared__ uint16_t pairs[128];
   __shared__ int npairs;
   __shared__ uint64_t scratch[kWavesPerBlock][64];
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void merge_softmax_kernel(const int32_t* __res
     const float sum = wave_sum_dpp(e);
     if (lane < k) {
       const int64_t o = it * k + lane;
-      idx[o] = group_items ? int32_t(row + (it / group_items) * group_rows) : row;
+      idx[o] = group_items ? int32_t(row + ((it / group_items) % group_count) * group_rows) : row;
       w[o] = e / sum;
       if (score) score[o] = sc;
     }
@@ -147,12 +147,13 @@ __global__ __launch_bounds__(256) void merge_softmax_kernel(const int32_t* __res
 
 hipError_t launch_merge_softmax(hipStream_t s, const int32_t* sub_idx, const float* sub_score,
                                 int64_t nitems, int k, int nk2, float inv_tau, int32_t* idx, float* w,
-                                float* score, int64_t group_items, int64_t group_rows) {
+                                float* score, int64_t group_items, int64_t group_rows, int64_t group_count) {
+  if (group_items > 0 && group_count < 1) return hipErrorInvalidValue;
   int64_t blocks = (nitems + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(merge_softmax_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, sub_idx, sub_score,
-                     nitems, k, nk2, inv_tau, idx, w, score, group_items, group_rows);
+                     nitems, k, nk2, inv_tau, idx, w, score, group_items, group_rows, group_count);
   return hipGetLastError();
 }
 

@@ -303,20 +303,30 @@ size_t small_sort_lds_bytes(int64_t n) {
 
 //
 // Grouped (gridDim.x > 1): workgroup g sorts pairs [g n, (g + 1) n) on their
-// own, the caller guaranteeing that every key of group g is below every key
-// of group g + 1, so the groups' sorted runs side by side are the sorted
-// whole.  Its segment table (n + 1 entries, positions global) and touched
-// keys go to group g's slice of seg_start / touched, its count to count[g];
-// group_segments_kernel then joins them (and builds the long-run plan).
+// own.  Its segment table (n + 1 entries, positions global) and touched keys
+// go to group g's slice of seg_start / touched, its count to count[g].  Then
+// either (plan_stride == 0) group_segments_kernel joins the tables into one
+// (the caller guaranteeing that every key of group g is below every key of
+// group g + 1, so the groups' sorted runs side by side are the sorted whole)
+// and builds the long-run plan, or (plan_stride > 0) each group stays on its
+// own and lists its own long runs in its own plan, plan_stride bytes after the
+// previous group's (counts, chunk_list and long_list all move by it).
 __global__ __launch_bounds__(kSmallThreads) void small_sort_segments_kernel(
     const uint32_t* __restrict__ keys_in, int n, int passes, uint32_t* __restrict__ keys_out,
     int32_t* __restrict__ vals_out, int32_t* __restrict__ seg_start, int32_t* __restrict__ touched,
     int64_t* __restrict__ count, int chunk, int2* __restrict__ chunk_list, int2* __restrict__ long_list,
-    uint32_t* __restrict__ plan_counts) {
+    uint32_t* __restrict__ plan_counts, int64_t plan_stride) {
   const int64_t base = int64_t(blockIdx.x) * n;  // this group's first pair
-  if (gridDim.x > 1) {  // grouped: the joining launch lists the long runs, into counters zeroed here
-    if (blockIdx.x == 0 && threadIdx.x == 0 && plan_counts) plan_counts[0] = plan_counts[1] = 0u;
-    plan_counts = nullptr;
+  if (gridDim.x > 1) {
+    if (plan_stride == 0) {  // joined: the joining launch lists the long runs, into counters zeroed here
+      if (blockIdx.x == 0 && threadIdx.x == 0 && plan_counts) plan_counts[0] = plan_counts[1] = 0u;
+      plan_counts = nullptr;
+    } else if (plan_counts) {  // separate groups: this group's own plan
+      const int64_t off = int64_t(blockIdx.x) * plan_stride;
+      plan_counts = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(plan_counts) + off);
+      chunk_list = reinterpret_cast<int2*>(reinterpret_cast<char*>(chunk_list) + off);
+      long_list = reinterpret_cast<int2*>(reinterpret_cast<char*>(long_list) + off);
+    }
   }
   keys_in += base;
   keys_out += base;
@@ -630,7 +640,7 @@ hipError_t launch_sort_segments_grouped(hipStream_t s, const uint32_t* keys_in, 
   int64_t* cnt_g = reinterpret_cast<int64_t*>(touched_g + n);  // groups (8-byte aligned: n + n + 1024 ints)
   hipLaunchKernelGGL(small_sort_segments_kernel, dim3(unsigned(groups)), dim3(kSmallThreads),
                      small_sort_lds_bytes(n_per), s, keys_in, n_per, passes, keys_out, vals_out, seg_g, touched_g,
-                     cnt_g, kVgChunk, nullptr, nullptr, plan->counts);
+                     cnt_g, kVgChunk, nullptr, nullptr, plan->counts, int64_t(0));
   int64_t jb = (n + kJoinThreads - 1) / kJoinThreads;
   if (jb > 1024) jb = 1024;
   hipLaunchKernelGGL(group_segments_kernel, dim3(unsigned(jb)), dim3(kJoinThreads), 0, s, seg_g, touched_g, cnt_g,
@@ -653,7 +663,43 @@ hipError_t launch_sort_segments_small(hipStream_t s, const uint32_t* keys_in, in
   hipLaunchKernelGGL(small_sort_segments_kernel, dim3(1), dim3(kSmallThreads), small_sort_lds_bytes(n), s, keys_in,
                      int(n), passes, keys_out, vals_out, seg_start, touched, count, kVgChunk,
                      plan ? plan->chunk_list : nullptr, plan ? plan->long_list : nullptr,
-                     plan ? plan->counts : nullptr);
+                     plan ? plan->counts : nullptr, int64_t(0));
+  return hipGetLastError();
+}
+
+size_t group_plan_stride() {
+  const size_t slots = 2 * (kSmallSortMax / kVgChunk) + 2;
+  return (64 + 2 * slots * sizeof(int2) + 255) / 256 * 256;
+}
+
+VgPlan group_plan(void* plans, int g) {
+  const size_t slots = 2 * (kSmallSortMax / kVgChunk) + 2;
+  char* b = static_cast<char*>(plans) + size_t(g) * group_plan_stride();
+  VgPlan p;
+  p.counts = reinterpret_cast<uint32_t*>(b);
+  p.chunk_list = reinterpret_cast<int2*>(b + 64);
+  p.long_list = p.chunk_list + slots;
+  return p;
+}
+
+hipError_t launch_sort_segments_separate(hipStream_t s, const uint32_t* keys_in, int64_t n, int groups, int key_bits,
+                                         uint32_t* keys_out, int32_t* vals_out, int32_t* seg_g, int64_t* cnt_g,
+                                         void* plans) {
+  if (groups < 1 || groups > kSortGroupsMax || n % groups || n / groups > kSmallSortMax || plans == nullptr)
+    return hipErrorInvalidValue;
+  const int n_per = int(n / groups);
+  {
+    const hipError_t e = small_sort_lds_limit();
+    if (e != hipSuccess) return e;
+  }
+  int passes = (key_bits + 7) / 8;
+  if (passes < 1) passes = 1;
+  if (passes > 4) passes = 4;
+  const VgPlan p0 = group_plan(plans, 0);
+  hipLaunchKernelGGL(small_sort_segments_kernel, dim3(unsigned(groups)), dim3(kSmallThreads),
+                     small_sort_lds_bytes(n_per), s, keys_in, n_per, passes, keys_out, vals_out, seg_g,
+                     static_cast<int32_t*>(nullptr), cnt_g, kVgChunk, p0.chunk_list, p0.long_list, p0.counts,
+                     int64_t(group_plan_stride()));
   return hipGetLastError();
 }
 

@@ -364,7 +364,8 @@ VgPlan value_grad_plan(void* aux, int64_t nitems, int d_value) {
 hipError_t launch_value_grad(hipStream_t s, int dtype, const int32_t* seg_start, const int64_t* nseg,
                              int64_t nitems, const uint32_t* sorted_rows, const int32_t* sorted_c, const float* w,
                              const void* dY, const void* V, float* dV, float* dw, int R, int d_value,
-                             bool accumulate, void* aux, const VgAdam* adam, bool plan_ready) {
+                             bool accumulate, void* aux, const VgAdam* adam, bool plan_ready,
+                             const VgPlan* plan_in) {
   const int elem = dtype == kBF16 ? 2 : 4;
   const int nvec = d_value * elem / 16;
   const int per_lane = (nvec + 63) / 64;
@@ -398,12 +399,13 @@ hipError_t launch_value_grad(hipStream_t s, int dtype, const int32_t* seg_start,
     a.step_size = adam->step_size;
     a.inv_sqrt_bc2 = adam->inv_sqrt_bc2;
   }
-  const VgPlan plan = value_grad_plan(aux, nitems, d_value);
+  // plan_in: a plan made elsewhere (ready); else the plan in aux
+  const VgPlan plan = plan_in ? *plan_in : value_grad_plan(aux, nitems, d_value);
   a.counts = plan.counts;
   a.partial = reinterpret_cast<float*>(ap + 64);
   a.chunk_list = plan.chunk_list;
   a.long_list = plan.long_list;
-  if (!plan_ready) {
+  if (!plan_ready && plan_in == nullptr) {
     hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, s, plan.counts, 2);
     int64_t pb = (nitems + 255) / 256;
     if (pb > 4096) pb = 4096;

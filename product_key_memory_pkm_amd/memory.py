@@ -122,3 +122,18 @@ class ProductKeyMemory:
         ws = self.workspace(T, L.PKM_WS_FWPKM_CHUNK)
         L.pkm_fwpkm_chunk(self.handle, T, q, C, Cp, V, target, lr, out["y"], out["idx"], out["w"], ws, streams)
         return out["y"], out["idx"], out["w"]
+
+    def fwpkm_chunks(self, q, C, Cp, V, target, lr: float, call_T: int, out=None, streams: int = 1):
+        """``fwpkm_chunk`` on the consecutive slices of ``call_T`` tokens of q and target, in order, in one call
+        (``pkm_fwpkm_chunks``): returns (y, idx, w) for all tokens; V is updated in place."""
+        T = q.shape[0]
+        c = self.cfg
+        dev = self.device
+        if out is None:
+            out = {"y": torch.empty((T, c.d_value), dtype=self.storage, device=dev),
+                   "idx": torch.empty((T, c.heads, c.topk), dtype=torch.int32, device=dev),
+                   "w": torch.empty((T, c.heads, c.topk), dtype=torch.float32, device=dev)}
+        ws = self.workspace(T, L.PKM_WS_FWPKM_CHUNK)
+        L.pkm_fwpkm_chunks(self.handle, T, call_T, q, C, Cp, V, target, lr, out["y"], out["idx"], out["w"], ws,
+                           streams)
+        return out["y"], out["idx"], out["w"]

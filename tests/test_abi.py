@@ -297,6 +297,19 @@ def test_idw_scores_and_fwpkm_chunk_argument_errors():
     assert call(handle=big_keys, T=1022, streams=511, ws_bytes=16) == L.PKM_ERR_WORKSPACE  # fits: next check
     fp8 = L.pkm_create(_cfg(L, score="idw", values="fp8", d_value=64))
     assert call(handle=fp8) == L.PKM_ERR_UNSUPPORTED
+    # several calls in one: T a multiple of call_T, call_T a multiple of streams
+    cs = lib.pkm_fwpkm_chunks
+
+    def calls(T=12, call_T=6, streams=1, ws_bytes=big, handle=h):
+        return cs(handle.ptr, None, T, call_T, streams, *ok[1:6], 0.1, *ok[6:9], ok[20], ws_bytes)
+
+    assert calls(call_T=0) == L.PKM_ERR_INVALID_ARG
+    assert calls(call_T=5) == L.PKM_ERR_INVALID_ARG and "multiple" in lib.pkm_last_error().decode()
+    assert calls(call_T=6, streams=4) == L.PKM_ERR_INVALID_ARG and "multiple" in lib.pkm_last_error().decode()
+    assert calls(handle=dot) == L.PKM_ERR_UNSUPPORTED
+    assert calls(T=0) == L.PKM_OK
+    assert calls(call_T=6, streams=3, ws_bytes=16) == L.PKM_ERR_WORKSPACE           # the other checks pass
+    assert calls(ws_bytes=L.pkm_workspace_size(h, 6, L.PKM_WS_FWPKM_CHUNK)) == L.PKM_ERR_WORKSPACE  # sized for T
     # the score gradients are the dot product's: the backward refuses IDW handles
     sv = L.pkm_saved(_fake(9), _fake(10), _fake(11), _fake(12), _fake(13), _fake(14))
     st = lib.pkm_backward(h.ptr, None, 10, ok[1], ok[2], ok[3], ok[4], ok[5], ok[6], ok[7], ctypes.byref(sv), ok[8],

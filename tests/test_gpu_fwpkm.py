@@ -393,3 +393,44 @@ def test_fwpkm_chunk_batch_of_streams(streams, tps, h, dq, nk, k, dv, dtype):
         G = idx[tok]
         assert ((G >= b * cfg.slots) & (G < (b + 1) * cfg.slots)).all(), "a stream addressed another's table"
         _check_chunk(cfg, qs[b], C, Cp, Vs[b], ts[b], lr, y[tok], G - b * cfg.slots, w[tok], V_all[rows], False)
+
+
+CALLS_CASES = [
+    # streams, tokens per stream and call, calls, heads, dq, nk, k, d_value, dtype
+    (1, 64, 4, 1, 16, 32, 8, 24, "f32"),         # one stream: every call's grouping up front
+    (1, 512, 3, 1, 64, 64, 8, 32, "bf16"),       # the benchmark's chunk length
+    (1, 2000, 3, 1, 16, 4, 4, 32, "f32"),        # 16 slots: runs of ~500 lookups (each call's long-run plan)
+    (1, 4608, 2, 1, 16, 64, 2, 16, "f32"),       # 9216 lookups per call: grouped call by call (radix sort)
+    (3, 40, 3, 2, 16, 12, 4, 24, "f32"),         # a batch of streams: the tables' offsets restart every call
+    (2, 4608, 2, 1, 16, 64, 2, 16, "f32"),       # 9216 lookups per stream and call: the radix sort
+]
+
+
+@pytest.mark.parametrize("streams,tps,calls,h,dq,nk,k,dv,dtype", CALLS_CASES)
+def test_fwpkm_chunks_equal_the_calls_in_sequence(streams, tps, calls, h, dq, nk, k, dv, dtype):
+    # pkm_fwpkm_chunks selects all tokens first, then writes slice by slice: every output and the final
+    # table must be those of pkm_fwpkm_chunk called on the slices one after another, bit for bit
+    cfg = _cfg(T=tps, heads=h, dq=dq, n_keys=nk, n_keys2=nk, topk=k, d_value=dv, dtype=dtype, seed=53)
+    lr = 0.5
+    call_T = streams * tps
+    T = calls * call_T
+    note(f"fwpkm chunks: {calls} calls of {streams} x {tps} tokens: {cfg}")
+    half = dq // 2
+    C = to_dev(pi.random_array(cfg.seed, 11, (h, nk, half), dtype=dtype, std=half ** -0.5))
+    Cp = to_dev(pi.random_array(cfg.seed, 12, (h, nk, half), dtype=dtype, std=half ** -0.5))
+    q = to_dev(pi.random_array(cfg.seed, 20, (T, h * dq), dtype=dtype, std=half ** -0.5))
+    target = to_dev(pi.random_array(cfg.seed, 40, (T, dv), dtype=dtype))
+    V0 = to_dev(pi.random_array(cfg.seed, 60, (streams * cfg.slots, dv), dtype=dtype, std=dv ** -0.5))
+    layer = layer_for(cfg, score="idw")
+    V_seq = V0.clone()
+    seq = [layer.fwpkm_chunk(q[j * call_T:(j + 1) * call_T], C, Cp, V_seq, target[j * call_T:(j + 1) * call_T],
+                             lr, streams=streams) for j in range(calls)]
+    seq = [tuple(t.clone() for t in r) for r in seq]
+    V_one = V0.clone()
+    y, idx, w = layer.fwpkm_chunks(q, C, Cp, V_one, target, lr, call_T, streams=streams)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, torch.cat([r[1] for r in seq])), "selections differ"
+    assert torch.equal(w, torch.cat([r[2] for r in seq])), "weights differ"
+    assert torch.equal(y, torch.cat([r[0] for r in seq])), "outputs differ"
+    assert torch.equal(V_one, V_seq), "tables differ"
+    assert not torch.equal(V_one, V0)
