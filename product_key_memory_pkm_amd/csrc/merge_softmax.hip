@@ -10,7 +10,9 @@
 // Only pairs with (a+1)(b+1) <= k can be among the k best: every (a', b') with
 // a' <= a, b' <= b scores at least as much and, on an equal score, has the
 // lower row (the per-half lists are ordered by score, then index).  For k = 32
-// that leaves 119 of the 1024 pairs.  One wave per (token, head): each lane
+// that leaves 119 of the 1024 pairs.  (Exact for the sums as real numbers; an
+// equality that only fp32 rounding creates between sums of different halves
+// can keep another of the equal-scoring rows than an exhaustive fp32 merge.)  One wave per (token, head): each lane
 // builds up to two candidates, the k-th largest 64-bit key (score key, ~row)
 // is found by bisection with ballots, the k winners are compacted and sorted
 // with a 32-lane bitonic network, and the softmax runs on the sorted lanes.
