@@ -366,7 +366,9 @@ pkm_status pkm_fwpkm_chunk(pkm_handle_t handle, void* stream, int64_t T, int64_t
  * queries are all known before it is memorized (a prompt, a document): the
  * selection reads only q, C and C', not V ("Fast-weight Product Key Memory",
  * section 2.2: memorization writes the value table only), so it runs once over
- * all T tokens, and each slice then runs only its gather and its value step.
+ * all T tokens, as does (when every slice's streams fit one workgroup each)
+ * the grouping of the slices' lookups by row; each slice then runs only its
+ * gather and its value step.
  * T a multiple of call_T, call_T a multiple of streams; other arguments as in
  * pkm_fwpkm_chunk, with T tokens.  ws >= pkm_workspace_size(handle, T,
  * PKM_WS_FWPKM_CHUNK). */

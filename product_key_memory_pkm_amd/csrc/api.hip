@@ -1055,6 +1055,45 @@ pkm_status fwpkm_calls(pkm_handle_t handle, void* stream, int64_t T, int64_t cal
     }
     return PKM_OK;
   }
+  const int64_t n_grp = streams > 0 ? n_call / streams : 0;
+  if (streams > 1 && calls > 1 && calls * streams <= kSortGroupsMax && n_grp <= kSmallSortMax) {
+    // A batch of streams: every (call, stream) chunk grouped up front by its
+    // own workgroup; per call the gather with the residual, one join of that
+    // call's streams' tables (their rows lie in separate tables, so the
+    // tables side by side are the call's sorted whole) with its long-run plan,
+    // and the value step.  Same lookups in the same order per row as separate
+    // calls.
+    const BwdLayout B = bwd_layout(handle, T);
+    uint32_t* sk = at<uint32_t>(ws, B.k0);
+    int32_t* sv = at<int32_t>(ws, B.v0);
+    int32_t* seg_g = at<int32_t>(ws, B.grp);
+    int64_t* cnt_g = reinterpret_cast<int64_t*>(seg_g + 2 * T * R + kSortGroupsMax);
+    PKM_HIP(launch_sort_segments_separate(s, reinterpret_cast<const uint32_t*>(idx), T * R, int(calls * streams),
+                                          bits, sk, sv, seg_g, cnt_g, at<void>(ws, L.plans)),
+            "row grouping of every call and stream");
+    char* e = at<char>(ws, L.e);
+    int32_t* seg = at<int32_t>(ws, B.seg);
+    int64_t* nseg = at<int64_t>(ws, L.n_touched);
+    const VgPlan plan = value_grad_plan(at<void>(ws, B.aux), n_call, c.d_value);
+    VgAdam sgd{};
+    sgd.V = V;
+    sgd.step_size = lr;
+    sgd.sgd = 1;
+    for (int64_t g = 0; g < calls; ++g) {
+      const int64_t t0 = g * call_T;
+      PKM_HIP(launch_gather(s, c.dtype, idx + t0 * R, w + t0 * R, V, static_cast<char*>(y) + t0 * row_bytes, call_T,
+                            int(R), c.d_value, false, static_cast<const char*>(target) + t0 * row_bytes,
+                            e + t0 * row_bytes),
+              "value gather-sum and reconstruction residual");
+      PKM_HIP(launch_join_groups(s, seg_g + g * streams * (n_grp + 1), cnt_g + g * streams, int(streams), int(n_grp),
+                                 (g + 1) * n_call, seg, nseg, &plan),
+              "row segments of the call");
+      PKM_HIP(launch_value_grad(s, c.dtype, seg, nseg, n_call, sk, sv, w, e, V, nullptr, at<float>(ws, B.dw), int(R),
+                                c.d_value, c.accumulate_dv != 0, at<void>(ws, B.aux), &sgd, true),
+              "value step");
+    }
+    return PKM_OK;
+  }
   const BwdLayout B = bwd_layout(handle, call_T);
   void* e = at<void>(ws, L.e);
   for (int64_t t0 = 0; t0 < T; t0 += call_T) {

@@ -148,6 +148,12 @@ VgPlan group_plan(void* plans, int g);
 hipError_t launch_sort_segments_separate(hipStream_t s, const uint32_t* keys_in, int64_t n, int groups, int key_bits,
                                          uint32_t* keys_out, int32_t* vals_out, int32_t* seg_g, int64_t* cnt_g,
                                          void* plans);
+// Joins `groups` consecutive separate tables (seg_g, cnt_g pointing at the
+// first; every key of a group below every key of the next) into seg_start /
+// count, with end_pos the position after the last group's last pair, and
+// lists their long runs in plan (its counts zeroed here first).
+hipError_t launch_join_groups(hipStream_t s, const int32_t* seg_g, const int64_t* cnt_g, int groups, int n_per,
+                              int64_t end_pos, int32_t* seg_start, int64_t* count, const VgPlan* plan);
 hipError_t launch_sort_segments_grouped(hipStream_t s, const uint32_t* keys_in, int64_t n, int groups,
                                         int key_bits, uint32_t* keys_out, int32_t* vals_out, int32_t* seg_start,
                                         int32_t* touched, int64_t* count, const VgPlan* plan, void* temp);

@@ -485,7 +485,7 @@ __global__ __launch_bounds__(kJoinThreads) void group_segments_kernel(
     const int32_t* __restrict__ seg_g, const int32_t* __restrict__ touched_g, const int64_t* __restrict__ cnt_g,
     int groups, int n_per, int32_t* __restrict__ seg_start, int32_t* __restrict__ touched,
     int64_t* __restrict__ count, int chunk, int2* __restrict__ chunk_list, int2* __restrict__ long_list,
-    uint32_t* __restrict__ plan_counts) {
+    uint32_t* __restrict__ plan_counts, int64_t end_pos) {
   constexpr int kPer = kSortGroupsMax / kJoinThreads;  // group counts per thread
   __shared__ uint32_t offs[kSortGroupsMax + 1];
   __shared__ uint32_t wsum[kJoinThreads / 64];
@@ -537,9 +537,13 @@ __global__ __launch_bounds__(kJoinThreads) void group_segments_kernel(
     }
   }
   if (blockIdx.x == 0 && tid == 0) {
-    seg_start[total] = int32_t(int64_t(groups) * n_per);
+    seg_start[total] = int32_t(end_pos);  // the position after the groups' last pair
     *count = int64_t(total);
   }
+}
+
+__global__ void zero_plan_counts_kernel(uint32_t* counts) {
+  if (threadIdx.x < 2) counts[threadIdx.x] = 0u;
 }
 
 // The one-workgroup sort's LDS limit, raised to what kSmallSortMax keys need.
@@ -645,7 +649,7 @@ hipError_t launch_sort_segments_grouped(hipStream_t s, const uint32_t* keys_in, 
   if (jb > 1024) jb = 1024;
   hipLaunchKernelGGL(group_segments_kernel, dim3(unsigned(jb)), dim3(kJoinThreads), 0, s, seg_g, touched_g, cnt_g,
                      groups, n_per, seg_start, touched, count, kVgChunk, plan->chunk_list, plan->long_list,
-                     plan->counts);
+                     plan->counts, int64_t(groups) * n_per);
   return hipGetLastError();
 }
 
@@ -680,6 +684,20 @@ VgPlan group_plan(void* plans, int g) {
   p.chunk_list = reinterpret_cast<int2*>(b + 64);
   p.long_list = p.chunk_list + slots;
   return p;
+}
+
+hipError_t launch_join_groups(hipStream_t s, const int32_t* seg_g, const int64_t* cnt_g, int groups, int n_per,
+                              int64_t end_pos, int32_t* seg_start, int64_t* count, const VgPlan* plan) {
+  if (groups < 1 || groups > kSortGroupsMax || n_per < 0 || plan == nullptr) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(zero_plan_counts_kernel, dim3(1), dim3(64), 0, s, plan->counts);
+  int64_t jb = (int64_t(groups) * n_per + kJoinThreads - 1) / kJoinThreads;
+  if (jb > 1024) jb = 1024;
+  if (jb < 1) jb = 1;
+  hipLaunchKernelGGL(group_segments_kernel, dim3(unsigned(jb)), dim3(kJoinThreads), 0, s, seg_g,
+                     static_cast<const int32_t*>(nullptr), cnt_g, groups, n_per, seg_start,
+                     static_cast<int32_t*>(nullptr), count, kVgChunk, plan->chunk_list, plan->long_list, plan->counts,
+                     end_pos);
+  return hipGetLastError();
 }
 
 hipError_t launch_sort_segments_separate(hipStream_t s, const uint32_t* keys_in, int64_t n, int groups, int key_bits,

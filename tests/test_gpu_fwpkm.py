@@ -402,6 +402,7 @@ CALLS_CASES = [
     (1, 2000, 3, 1, 16, 4, 4, 32, "f32"),        # 16 slots: runs of ~500 lookups (each call's long-run plan)
     (1, 4608, 2, 1, 16, 64, 2, 16, "f32"),       # 9216 lookups per call: grouped call by call (radix sort)
     (3, 40, 3, 2, 16, 12, 4, 24, "f32"),         # a batch of streams: the tables' offsets restart every call
+    (2, 1000, 3, 1, 16, 4, 4, 32, "f32"),        # a batch whose calls have runs of ~250 lookups per row
     (2, 4608, 2, 1, 16, 64, 2, 16, "f32"),       # 9216 lookups per stream and call: the radix sort
 ]
 
