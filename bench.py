@@ -74,6 +74,8 @@ def parse():
                     help="run the batched fast-weight memorization calls once and nothing else (for profilers)")
     ap.add_argument("--profile-fwpkm-one-call", action="store_true",
                     help="memorize the fast-weight stream in one pkm_fwpkm_chunks call and nothing else (for profilers)")
+    ap.add_argument("--profile-fwpkm-batch-one-call", action="store_true",
+                    help="the batched fast-weight calls as one pkm_fwpkm_chunks call and nothing else (for profilers)")
     ap.add_argument("--no-fwpkm", action="store_true", help="skip the fast-weight memorization legs")
     return ap.parse_args()
 
@@ -274,6 +276,17 @@ def main():
                             st["target"][c], FWPKM_LR, st["y"][c], st["idx"], st["w"], st["ws"],
                             streams=FWPKM_STREAMS)
 
+    if args.profile_fwpkm_batch_one_call:
+        st = fwpkm_batch_setup()
+        nt_b = FWPKM_BATCH_CHUNKS * FWPKM_STREAMS * FWPKM_CHUNK
+        pkm_fwpkm_chunks(st["m"].handle, nt_b, FWPKM_STREAMS * FWPKM_CHUNK, st["q"].view(nt_b, -1), st["C"], st["Cp"],
+                         st["V"], st["target"].view(nt_b, -1), FWPKM_LR, st["y"].view(nt_b, -1),
+                         torch.empty((nt_b, 1, FWPKM_TOPK), dtype=torch.int32, device="cuda"),
+                         torch.empty((nt_b, 1, FWPKM_TOPK), dtype=torch.float32, device="cuda"),
+                         st["m"].workspace(nt_b, PKM_WS_FWPKM_CHUNK), streams=FWPKM_STREAMS)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_fwpkm_batch_one_call": FWPKM_BATCH_CHUNKS}), flush=True)
+        return
     if args.profile_fwpkm_batch:
         st = fwpkm_batch_setup()
         fwpkm_batch_run(st, FWPKM_BATCH_CHUNKS)
