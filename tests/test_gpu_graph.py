@@ -132,3 +132,56 @@ def test_fwpkm_chunks_graph_replays(streams):
         for c in range(nchunks):
             for k_ in ("y", "idx", "w"):
                 assert torch.equal(got_outs[c][k_], ref_outs[c][k_]), f"replay {rep}: chunk {c} {k_} differs"
+
+
+@pytest.mark.parametrize("streams", [1, 8])
+def test_fwpkm_one_call_graph_replays(streams):
+    # three memorization slices in one pkm_fwpkm_chunks call (selection and grouping up front, then the
+    # slices' gathers and value steps) captured in one graph and replayed against the eager call
+    tps, ncalls, lr = 256, 3, 0.5
+    cfg = pi.custom(T=tps * streams, d=16, heads=1, dq=32, n_keys=64, n_keys2=64, topk=8, d_value=64, dtype="bf16",
+                    bn=False, seed=54)
+    note(f"graph capture of one fwpkm call over {ncalls} slices, {streams} streams")
+    half = cfg.dq // 2
+    T = cfg.T * ncalls
+    C = to_dev(pi.random_array(cfg.seed, 1, (1, cfg.n_keys, half), dtype="bf16", std=half ** -0.5))
+    Cp = to_dev(pi.random_array(cfg.seed, 2, (1, cfg.n_keys2, half), dtype="bf16", std=half ** -0.5))
+    q = to_dev(pi.random_array(cfg.seed, 10, (T, cfg.dq), dtype="bf16", std=half ** -0.5))
+    t = to_dev(pi.random_array(cfg.seed, 20, (T, cfg.d_value), dtype="bf16"))
+    V0 = to_dev(pi.random_array(cfg.seed, 3, (streams * cfg.slots, cfg.d_value), dtype="bf16", std=0.125))
+    layer = layer_for(cfg, score="idw")
+    out = {"y": torch.empty((T, cfg.d_value), dtype=torch.bfloat16, device="cuda"),
+           "idx": torch.empty((T, 1, cfg.topk), dtype=torch.int32, device="cuda"),
+           "w": torch.empty((T, 1, cfg.topk), dtype=torch.float32, device="cuda")}
+    V = V0.clone()
+
+    def run():
+        layer.fwpkm_chunks(q, C, Cp, V, t, lr, cfg.T, out=out, streams=streams)
+
+    run()  # eager reference (also allocates the workspace)
+    torch.cuda.synchronize()
+    ref = {k_: v_.clone() for k_, v_ in out.items()}
+    ref_V = V.clone()
+    assert not torch.equal(ref_V, V0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        V.copy_(V0)
+        run()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    junk = torch.zeros(1 << 20, device="cuda")
+    for rep in range(3):
+        V.copy_(V0)
+        for v_ in out.values():
+            v_.zero_()
+        junk += torch.randn_like(junk)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(V, ref_V), f"replay {rep}: the table differs from the eager run"
+        for k_ in ("y", "idx", "w"):
+            assert torch.equal(out[k_], ref[k_]), f"replay {rep}: {k_} differs"
