@@ -137,6 +137,39 @@ def _dt(t, want, name):
         raise TypeError(f"{name} must be {want}, got {t.dtype}")
 
 
+def _need(**req):
+    """Each keyword is (tensor or None, elements the call reads or writes): a shorter tensor raises ValueError
+    before anything reaches the library, whose kernels trust the sizes pkm.h states."""
+    for name, (t, n) in req.items():
+        if t is not None and t.numel() < n:
+            raise ValueError(f"{name} holds {t.numel()} elements; this call needs {n}")
+
+
+def _dims(h, T: int, streams: int = 1) -> dict:
+    """Element counts of the buffers pkm.h describes, for handle ``h`` and T tokens."""
+    c = h.cfg
+    F = c.heads * c.d_query
+    half = c.d_query // 2
+    slots = c.n_keys * c.n_keys2 * streams
+    vrow = c.d_value + 16 if c.value_format == PKM_VALUES_FP8 else c.d_value
+    return {"x": T * c.d_in, "Wq": F * c.d_in, "F": F, "C": c.heads * c.n_keys * half,
+            "Cp": c.heads * c.n_keys2 * half, "V": slots * vrow, "dV": slots * c.d_value, "y": T * c.d_value,
+            "lookups": T * c.heads * c.topk, "sub": T * c.heads * 2 * c.topk, "q": T * F,
+            "hits_c": c.heads * c.n_keys, "hits_cp": c.heads * c.n_keys2, "used": 1 + c.heads,
+            "th": T * c.heads}
+
+
+def _need_saved(h, T: int, saved: dict):
+    """The saved state: idx, w [T, h, k]; q, q_pre [T, h*dq]; bn_mean, bn_rstd [h*dq] (BatchNorm only)."""
+    n = _dims(h, T)
+    req = {"saved['idx']": (saved.get("idx"), n["lookups"]), "saved['w']": (saved.get("w"), n["lookups"]),
+           "saved['q']": (saved.get("q"), n["q"]), "saved['q_pre']": (saved.get("q_pre"), n["q"])}
+    if h.cfg.bn == PKM_BN_BATCH:
+        req.update({"saved['bn_mean']": (saved.get("bn_mean"), n["F"]),
+                    "saved['bn_rstd']": (saved.get("bn_rstd"), n["F"])})
+    _need(**req)
+
+
 class Handle:
     """An immutable PKM layer handle (host memory only)."""
 
@@ -208,6 +241,10 @@ def pkm_forward(h, T, x, Wq, bn_gamma, bn_beta, C, Cp, V, y, saved: dict, ws):
     for n, t in (("x", x), ("Wq", Wq), ("C", C), ("Cp", Cp), ("y", y)):
         _dt(t, st, n)
     _dt(V, h.value_dtype, "V")
+    n = _dims(h, T)
+    _need(x=(x, n["x"]), Wq=(Wq, n["Wq"]), bn_gamma=(bn_gamma, n["F"]), bn_beta=(bn_beta, n["F"]), C=(C, n["C"]),
+          Cp=(Cp, n["Cp"]), V=(V, n["V"]), y=(y, n["y"]))
+    _need_saved(h, T, saved)
     sv = _saved_struct(saved)
     _check(_invoke("pkm_forward", h, T, _ptr(x), _ptr(Wq), _ptr(bn_gamma), _ptr(bn_beta), _ptr(C),
                              _ptr(Cp), _ptr(V), _ptr(y), ctypes.byref(sv), _ptr(ws), _nbytes(ws)), "pkm_forward")
@@ -220,11 +257,22 @@ def pkm_backward(h, T, dY, x, Wq, bn_gamma, C, Cp, V, saved: dict, dV, touched, 
         _dt(t, st, n)
     _dt(dV, torch.float32, "dV")
     _dt(n_touched, torch.int64, "n_touched")
+    _need_bwd(h, T, dY, x, Wq, bn_gamma, C, Cp, V, saved, touched, n_touched, dC, dCp, dWq, dgamma, dbeta, dx)
+    _need(dV=(dV, _dims(h, T)["dV"]))
     sv = _saved_struct(saved)
     _check(_invoke("pkm_backward", h, T, _ptr(dY), _ptr(x), _ptr(Wq), _ptr(bn_gamma), _ptr(C), _ptr(Cp),
                               _ptr(V), ctypes.byref(sv), _ptr(dV), _ptr(touched), _ptr(n_touched), _ptr(dC),
                               _ptr(dCp), _ptr(dWq), _ptr(dgamma), _ptr(dbeta), _ptr(dx), _ptr(ws), _nbytes(ws)),
            "pkm_backward")
+
+
+def _need_bwd(h, T, dY, x, Wq, bn_gamma, C, Cp, V, saved, touched, n_touched, dC, dCp, dWq, dgamma, dbeta, dx):
+    n = _dims(h, T)
+    _need(dY=(dY, n["y"]), x=(x, n["x"]), Wq=(Wq, n["Wq"]), bn_gamma=(bn_gamma, n["F"]), C=(C, n["C"]),
+          Cp=(Cp, n["Cp"]), V=(V, n["V"]), touched=(touched, n["lookups"]), n_touched=(n_touched, 1),
+          dC=(dC, n["C"]), dCp=(dCp, n["Cp"]), dWq=(dWq, n["Wq"]), dgamma=(dgamma, n["F"]),
+          dbeta=(dbeta, n["F"]), dx=(dx, n["x"]))
+    _need_saved(h, T, saved)
 
 
 def _adam_struct(adam: dict) -> pkm_adam:
@@ -243,6 +291,8 @@ def pkm_backward_adam(h, T, dY, x, Wq, bn_gamma, C, Cp, V, saved: dict, adam_m, 
     _dt(adam_m, torch.float32, "adam_m")
     _dt(adam_v, torch.float32, "adam_v")
     _dt(n_touched, torch.int64, "n_touched")
+    _need_bwd(h, T, dY, x, Wq, bn_gamma, C, Cp, V, saved, touched, n_touched, dC, dCp, dWq, dgamma, dbeta, dx)
+    _need(adam_m=(adam_m, _dims(h, T)["dV"]), adam_v=(adam_v, _dims(h, T)["dV"]))
     sv = _saved_struct(saved)
     hp = _adam_struct(adam)
     _check(_invoke("pkm_backward_adam", h, T, _ptr(dY), _ptr(x), _ptr(Wq), _ptr(bn_gamma), _ptr(C), _ptr(Cp),
@@ -257,6 +307,10 @@ def pkm_stage_value_adam(h, T, idx, w, dY, V, adam_m, adam_v, adam: dict, touche
     _dt(adam_m, torch.float32, "adam_m")
     _dt(adam_v, torch.float32, "adam_v")
     _dt(dw, torch.float32, "dw")
+    n = _dims(h, T)
+    _need(idx=(idx, n["lookups"]), w=(w, n["lookups"]), dY=(dY, n["y"]), V=(V, n["dV"]), adam_m=(adam_m, n["dV"]),
+          adam_v=(adam_v, n["dV"]), touched=(touched, n["lookups"]), n_touched=(n_touched, 1),
+          dw=(dw, n["lookups"]))
     hp = _adam_struct(adam)
     _check(_invoke("pkm_stage_value_adam", h, T, _ptr(idx), _ptr(w), _ptr(dY), _ptr(V), _ptr(adam_m), _ptr(adam_v),
                    ctypes.byref(hp), _ptr(touched), _ptr(n_touched), _ptr(dw), _ptr(ws), _nbytes(ws)),
@@ -264,6 +318,11 @@ def pkm_stage_value_adam(h, T, idx, w, dY, V, adam_m, adam_v, adam: dict, touche
 
 
 def pkm_stage_query(h, T, x, Wq, bn_gamma, bn_beta, saved: dict, ws):
+    n = _dims(h, T)
+    _need(x=(x, n["x"]), Wq=(Wq, n["Wq"]), bn_gamma=(bn_gamma, n["F"]), bn_beta=(bn_beta, n["F"]),
+          **{"saved['q']": (saved.get("q"), n["q"]), "saved['q_pre']": (saved.get("q_pre"), n["q"])},
+          **({"saved['bn_mean']": (saved.get("bn_mean"), n["F"]), "saved['bn_rstd']": (saved.get("bn_rstd"), n["F"])}
+             if h.cfg.bn == PKM_BN_BATCH else {}))
     sv = _saved_struct(saved)
     _check(_invoke("pkm_stage_query", h, T, _ptr(x), _ptr(Wq), _ptr(bn_gamma), _ptr(bn_beta),
                                  ctypes.byref(sv), _ptr(ws), _nbytes(ws)), "pkm_stage_query")
@@ -272,11 +331,16 @@ def pkm_stage_query(h, T, x, Wq, bn_gamma, bn_beta, saved: dict, ws):
 def pkm_stage_score_topk(h, T, q, C, Cp, sub_idx, sub_score, ws):
     _dt(sub_idx, torch.int32, "sub_idx")
     _dt(sub_score, torch.float32, "sub_score")
+    n = _dims(h, T)
+    _need(q=(q, n["q"]), C=(C, n["C"]), Cp=(Cp, n["Cp"]), sub_idx=(sub_idx, n["sub"]), sub_score=(sub_score, n["sub"]))
     _check(_invoke("pkm_stage_score_topk", h, T, _ptr(q), _ptr(C), _ptr(Cp), _ptr(sub_idx),
                    _ptr(sub_score), _ptr(ws), _nbytes(ws)), "pkm_stage_score_topk")
 
 
 def pkm_stage_merge_softmax(h, T, sub_idx, sub_score, idx, w, score=None):
+    n = _dims(h, T)
+    _need(sub_idx=(sub_idx, n["sub"]), sub_score=(sub_score, n["sub"]), idx=(idx, n["lookups"]), w=(w, n["lookups"]),
+          score=(score, n["lookups"]))
     _check(_invoke("pkm_stage_merge_softmax", h, T, _ptr(sub_idx), _ptr(sub_score), _ptr(idx), _ptr(w),
                                          _ptr(score)), "pkm_stage_merge_softmax")
 
@@ -295,10 +359,15 @@ def pkm_stage_gather(h, T, idx, w, V, y):
     _dt(idx, torch.int32, "idx")
     _dt(w, torch.float32, "w")
     _dt(V, h.value_dtype, "V")
+    n = _dims(h, T)
+    _need(idx=(idx, n["lookups"]), w=(w, n["lookups"]), V=(V, n["V"]), y=(y, n["y"]))
     _check(_invoke("pkm_stage_gather", h, T, _ptr(idx), _ptr(w), _ptr(V), _ptr(y)), "pkm_stage_gather")
 
 
 def pkm_stage_value_grad(h, T, idx, w, dY, V, dV, touched, n_touched, dw, ws):
+    n = _dims(h, T)
+    _need(idx=(idx, n["lookups"]), w=(w, n["lookups"]), dY=(dY, n["y"]), V=(V, n["dV"]), dV=(dV, n["dV"]),
+          touched=(touched, n["lookups"]), n_touched=(n_touched, 1), dw=(dw, n["lookups"]))
     _check(_invoke("pkm_stage_value_grad", h, T, _ptr(idx), _ptr(w), _ptr(dY), _ptr(V), _ptr(dV),
                                       _ptr(touched), _ptr(n_touched), _ptr(dw), _ptr(ws), _nbytes(ws)),
            "pkm_stage_value_grad")
@@ -307,11 +376,16 @@ def pkm_stage_value_grad(h, T, idx, w, dY, V, dV, touched, n_touched, dw, ws):
 def pkm_stage_row_groups(h, T, idx, touched, n_touched, ws):
     _dt(idx, torch.int32, "idx")
     _dt(n_touched, torch.int64, "n_touched")
+    n = _dims(h, T)
+    _need(idx=(idx, n["lookups"]), touched=(touched, n["lookups"]), n_touched=(n_touched, 1))
     _check(_invoke("pkm_stage_row_groups", h, T, _ptr(idx), _ptr(touched), _ptr(n_touched), _ptr(ws), _nbytes(ws)),
            "pkm_stage_row_groups")
 
 
 def pkm_stage_value_grad_grouped(h, T, w, dY, V, dV, dw, n_touched, ws):
+    n = _dims(h, T)
+    _need(w=(w, n["lookups"]), dY=(dY, n["y"]), V=(V, n["dV"]), dV=(dV, n["dV"]), dw=(dw, n["lookups"]),
+          n_touched=(n_touched, 1))
     _check(_invoke("pkm_stage_value_grad_grouped", h, T, _ptr(w), _ptr(dY), _ptr(V), _ptr(dV), _ptr(dw),
                    _ptr(n_touched), _ptr(ws), _nbytes(ws)), "pkm_stage_value_grad_grouped")
 
@@ -319,6 +393,9 @@ def pkm_stage_value_grad_grouped(h, T, w, dY, V, dV, dw, n_touched, ws):
 def pkm_stage_value_adam_grouped(h, T, w, dY, V, adam_m, adam_v, adam: dict, dw, n_touched, ws):
     _dt(adam_m, torch.float32, "adam_m")
     _dt(adam_v, torch.float32, "adam_v")
+    n = _dims(h, T)
+    _need(w=(w, n["lookups"]), dY=(dY, n["y"]), V=(V, n["dV"]), adam_m=(adam_m, n["dV"]), adam_v=(adam_v, n["dV"]),
+          dw=(dw, n["lookups"]), n_touched=(n_touched, 1))
     hp = _adam_struct(adam)
     _check(_invoke("pkm_stage_value_adam_grouped", h, T, _ptr(w), _ptr(dY), _ptr(V), _ptr(adam_m), _ptr(adam_v),
                    ctypes.byref(hp), _ptr(dw), _ptr(n_touched), _ptr(ws), _nbytes(ws)),
@@ -334,21 +411,42 @@ def pkm_diagnostics(h, T, idx, w, hits_c, hits_cp, used, entropy, entropy_sum, w
     _dt(used, torch.int64, "used")
     _dt(entropy, torch.float32, "entropy")
     _dt(entropy_sum, torch.float64, "entropy_sum")
+    n = _dims(h, T)
+    _need(idx=(idx, n["lookups"]), w=(w, n["lookups"]), hits_c=(hits_c, n["hits_c"]), hits_cp=(hits_cp, n["hits_cp"]),
+          used=(used, n["used"]), entropy=(entropy, n["th"]), entropy_sum=(entropy_sum, 1))
     _check(_invoke("pkm_diagnostics", h, T, _ptr(idx), _ptr(w), _ptr(hits_c), _ptr(hits_cp), _ptr(used),
                    _ptr(entropy), _ptr(entropy_sum), _ptr(ws), _nbytes(ws)), "pkm_diagnostics")
 
 
 def pkm_stage_subkey_grad(h, T, idx, w, dw, q, C, Cp, dq, dC, dCp, ws):
+    n = _dims(h, T)
+    _need(idx=(idx, n["lookups"]), w=(w, n["lookups"]), dw=(dw, n["lookups"]), q=(q, n["q"]), C=(C, n["C"]),
+          Cp=(Cp, n["Cp"]), dq=(dq, n["q"]), dC=(dC, n["C"]), dCp=(dCp, n["Cp"]))
     _check(_invoke("pkm_stage_subkey_grad", h, T, _ptr(idx), _ptr(w), _ptr(dw), _ptr(q), _ptr(C),
                                        _ptr(Cp), _ptr(dq), _ptr(dC), _ptr(dCp), _ptr(ws), _nbytes(ws)),
            "pkm_stage_subkey_grad")
 
 
 def pkm_stage_query_grad(h, T, dq, x, Wq, bn_gamma, saved: dict, dWq, dgamma, dbeta, dx, ws):
+    n = _dims(h, T)
+    _need(dq=(dq, n["q"]), x=(x, n["x"]), Wq=(Wq, n["Wq"]), bn_gamma=(bn_gamma, n["F"]), dWq=(dWq, n["Wq"]),
+          dgamma=(dgamma, n["F"]), dbeta=(dbeta, n["F"]), dx=(dx, n["x"]),
+          **{"saved['q_pre']": (saved.get("q_pre"), n["q"])},
+          **({"saved['bn_mean']": (saved.get("bn_mean"), n["F"]), "saved['bn_rstd']": (saved.get("bn_rstd"), n["F"])}
+             if h.cfg.bn == PKM_BN_BATCH else {}))
     sv = _saved_struct(saved)
     _check(_invoke("pkm_stage_query_grad", h, T, _ptr(dq), _ptr(x), _ptr(Wq), _ptr(bn_gamma),
                                       ctypes.byref(sv), _ptr(dWq), _ptr(dgamma), _ptr(dbeta), _ptr(dx), _ptr(ws),
                                       _nbytes(ws)), "pkm_stage_query_grad")
+
+
+def _need_fwpkm(h, T, streams, q, C, Cp, V, target, y, idx, w):
+    """q [T, h*dq], C, Cp, V [streams*|C|*|C'|, d_value], target and y [T, d_value], idx and w [T, h, k]."""
+    if int(streams) < 1:
+        raise ValueError(f"streams = {streams} < 1")
+    n = _dims(h, T, int(streams))
+    _need(q=(q, n["q"]), C=(C, n["C"]), Cp=(Cp, n["Cp"]), V=(V, n["V"]), target=(target, n["y"]), y=(y, n["y"]),
+          idx=(idx, n["lookups"]), w=(w, n["lookups"]))
 
 
 def pkm_fwpkm_chunk(h, T, q, C, Cp, V, target, lr, y, idx, w, ws, streams=1):
@@ -361,6 +459,7 @@ def pkm_fwpkm_chunk(h, T, q, C, Cp, V, target, lr, y, idx, w, ws, streams=1):
         _dt(t, st, n)
     _dt(idx, torch.int32, "idx")
     _dt(w, torch.float32, "w")
+    _need_fwpkm(h, T, streams, q, C, Cp, V, target, y, idx, w)
     _check(_invoke("pkm_fwpkm_chunk", h, T, int(streams), _ptr(q), _ptr(C), _ptr(Cp), _ptr(V), _ptr(target),
                    float(lr), _ptr(y), _ptr(idx), _ptr(w), _ptr(ws), _nbytes(ws)), "pkm_fwpkm_chunk")
 
@@ -373,5 +472,6 @@ def pkm_fwpkm_chunks(h, T, call_T, q, C, Cp, V, target, lr, y, idx, w, ws, strea
         _dt(t, st, n)
     _dt(idx, torch.int32, "idx")
     _dt(w, torch.float32, "w")
+    _need_fwpkm(h, T, streams, q, C, Cp, V, target, y, idx, w)
     _check(_invoke("pkm_fwpkm_chunks", h, T, int(call_T), int(streams), _ptr(q), _ptr(C), _ptr(Cp), _ptr(V),
                    _ptr(target), float(lr), _ptr(y), _ptr(idx), _ptr(w), _ptr(ws), _nbytes(ws)), "pkm_fwpkm_chunks")

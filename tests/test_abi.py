@@ -326,3 +326,72 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError):
         L.pkm_stage_gather(h, 1, torch.zeros(8, dtype=torch.int32), torch.zeros(8), torch.zeros(64),
                            torch.zeros(64))
+
+
+def _t(n, dtype=None):
+    import torch
+    return torch.zeros(max(0, n), dtype=dtype if dtype is not None else torch.float32)
+
+
+def test_binding_rejects_short_tensors_before_the_library():
+    # every size check runs before the device check: a short host tensor names itself, a full-size set of
+    # host tensors gets as far as "must be on the GPU"
+    L = _lib()
+    import torch
+    c = _cfg(L)
+    h = L.pkm_create(c)
+    T = 10
+    F, half, slots = c.heads * c.d_query, c.d_query // 2, c.n_keys * c.n_keys2
+    lk = T * c.heads * c.topk
+    i32 = torch.int32
+
+    def fwd(**over):
+        a = dict(x=_t(T * c.d_in), Wq=_t(F * c.d_in), g=_t(F), b=_t(F), C=_t(c.heads * c.n_keys * half),
+                 Cp=_t(c.heads * c.n_keys2 * half), V=_t(slots * c.d_value), y=_t(T * c.d_value))
+        a.update(over)
+        saved = {"idx": _t(lk, i32), "w": _t(lk), "q": _t(T * F), "q_pre": _t(T * F), "bn_mean": _t(F),
+                 "bn_rstd": _t(F)}
+        saved.update(a.pop("saved", {}))
+        L.pkm_forward(h, T, a["x"], a["Wq"], a["g"], a["b"], a["C"], a["Cp"], a["V"], a["y"], saved, None)
+
+    with pytest.raises(ValueError, match="on the GPU"):
+        fwd()
+    for name, short in (("x", _t(T * c.d_in - 1)), ("V", _t(slots * c.d_value - 4)), ("y", _t(c.d_value)),
+                        ("Cp", _t(3)), ("g", _t(F - 1))):
+        with pytest.raises(ValueError, match="holds"):
+            fwd(**{name: short})
+    with pytest.raises(ValueError, match="holds"):
+        fwd(saved={"idx": _t(lk - 1, i32)})
+
+    # the value gradient stage: V and dV cover every slot, idx/w/dw every lookup
+    def vg(**over):
+        a = dict(idx=_t(lk, i32), w=_t(lk), dY=_t(T * c.d_value), V=_t(slots * c.d_value),
+                 dV=_t(slots * c.d_value), touched=_t(lk, i32), nt=_t(1, torch.int64), dw=_t(lk))
+        a.update(over)
+        L.pkm_stage_value_grad(h, T, a["idx"], a["w"], a["dY"], a["V"], a["dV"], a["touched"], a["nt"], a["dw"], None)
+
+    with pytest.raises(ValueError, match="on the GPU"):
+        vg()
+    for name in ("idx", "w", "dY", "V", "dV", "touched", "dw"):
+        with pytest.raises(ValueError, match="holds"):
+            vg(**{name: _t(5, i32 if name in ("idx", "touched") else None)})
+
+    # the memorization chunk: V holds streams * |C| * |C'| rows
+    hi = L.pkm_create(_cfg(L, score="idw", bn=False))
+
+    def chunk(streams, **over):
+        a = dict(q=_t(T * F), C=_t(c.heads * c.n_keys * half), Cp=_t(c.heads * c.n_keys2 * half),
+                 V=_t(streams * slots * c.d_value), target=_t(T * c.d_value), y=_t(T * c.d_value), idx=_t(lk, i32),
+                 w=_t(lk))
+        a.update(over)
+        L.pkm_fwpkm_chunk(hi, T, a["q"], a["C"], a["Cp"], a["V"], a["target"], 0.1, a["y"], a["idx"], a["w"], None,
+                          streams=streams)
+
+    with pytest.raises(ValueError, match="on the GPU"):
+        chunk(2)
+    with pytest.raises(ValueError, match="holds"):
+        chunk(2, V=_t(slots * c.d_value))
+    with pytest.raises(ValueError, match="holds"):
+        chunk(1, target=_t(T * c.d_value - 1))
+    with pytest.raises(ValueError):
+        chunk(0)

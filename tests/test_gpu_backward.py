@@ -12,7 +12,7 @@ import pkm_inputs as pi
 from oracle import pkm_oracle as O
 from tests import parity as P
 from tests.gpu_util import layer_for, note, require_lib, to_dev, upload
-from tests.test_gpu_forward import FWD_CASES, run_gpu_forward
+from tests.test_gpu_forward import FWD_CASES, forward_check, run_gpu_forward
 
 pytestmark = pytest.mark.gpu
 
@@ -230,10 +230,18 @@ def test_query_grad_stage(T, d, h, dq, dtype, bn):
 # ---------------------------------------------------------------------------
 # whole backward
 # ---------------------------------------------------------------------------
-def backward_check(cfg, inp, gpu, g, dV_np, dY):
-    """Compare a GPU backward with the oracle's for the same upstream gradient dY."""
-    ref = O.forward(cfg, inp)
-    gb = O.backward(cfg, inp, ref, dY)
+def reference_forward(cfg, inp, gpu):
+    """The oracle's forward on the GPU's selection, after judging it (tests/parity.py: forced_forward).
+
+    Near-tie tokens may validly select other rows than the oracle; with their selection forced on the
+    oracle, every gradient has one correct answer and the whole upstream gradient is compared."""
+    stats = forward_check(cfg, inp, gpu)
+    return P.forced_forward(cfg, stats["ref"], stats["sel"], stats["q"], gpu["idx"]), stats
+
+
+def backward_check(cfg, inp, gpu, g, dV_np, dY, fwd):
+    """Compare a GPU backward with the oracle's for the same upstream gradient dY on the forward ``fwd``."""
+    gb = O.backward(cfg, inp, fwd, dY)
     tol = P.TOL[cfg.dtype]
     uniq = np.unique(gpu["idx"])
     nt = int(g["n_touched"].item())
@@ -241,13 +249,13 @@ def backward_check(cfg, inp, gpu, g, dV_np, dY):
     np.testing.assert_array_equal(g["touched"].cpu().numpy()[:nt], uniq)
     untouched = np.setdiff1d(np.arange(cfg.slots), uniq)
     assert (dV_np[untouched] == SENTINEL).all()
-    rows = np.union1d(uniq, np.unique(ref["rows"]))
-    ref_dv = O.value_grad_rows(ref["rows"], ref["w"], dY, cfg.dtype, rows)
+    rows = uniq
+    ref_dv = O.value_grad_rows(fwd["rows"], fwd["w"], dY, cfg.dtype, rows)
     # a row sums w*dY over its lookups; the weights carry the forward's relative error, so the
     # bound is relative to the sum of |w*dY| (rows whose terms cancel would otherwise be held
     # to far less than the inputs' own accuracy)
     dY_abs = (dY & np.uint16(0x7FFF)) if cfg.dtype == "bf16" else np.abs(dY)
-    mag = O.value_grad_rows(ref["rows"], ref["w"], dY_abs, cfg.dtype, rows)
+    mag = O.value_grad_rows(fwd["rows"], fwd["w"], dY_abs, cfg.dtype, rows)
     got = dV_np[rows].astype(np.float64) - SENTINEL
     err = np.abs(got - ref_dv).max(1)
     assert (err <= tol * mag.max(1) + 2.0 ** -23 * (SENTINEL + np.abs(got).max(1))).all()
@@ -264,33 +272,18 @@ def backward_check(cfg, inp, gpu, g, dV_np, dY):
 BWD_CASES = ["tiny", "small", "bf16_mid", "ragged", "one_token", "k1", "tau", "int_ties", "hot", "hot_bf16"]
 
 
-def masked_dy(inp, gpu_idx, ref_rows):
-    """dY with the rows of near-tie tokens zeroed.
-
-    Where a token's selection validly differs from the oracle's (a near tie),
-    its gradients differ too; with a zero upstream gradient such a token adds
-    nothing to any gradient on either side, so every remaining value has one
-    correct answer.  The selections themselves are checked by the forward tests.
-    """
-    exact = (np.sort(gpu_idx, -1) == np.sort(ref_rows, -1)).all(-1).all(-1)
-    dY = inp["dY"].copy()
-    dY[~exact] = 0
-    return dY, exact
-
-
 @pytest.mark.parametrize("name", BWD_CASES)
 def test_backward_end_to_end(name):
     cfg = FWD_CASES[name]
     note(f"backward {name}: {cfg}")
     inp = pi.make_inputs(cfg, with_dy=True)
     gpu, (layer, dev, saved, y) = run_gpu_forward(cfg, inp)
-    ref = O.forward(cfg, inp)
-    dY, exact = masked_dy(inp, gpu["idx"], ref["rows"])
-    assert exact.mean() > (0.999 if cfg.dtype == "f32" else 0.95)
+    fwd, _ = reference_forward(cfg, inp, gpu)
+    dY = inp["dY"]
     dV = torch.full((cfg.slots, cfg.d_value), SENTINEL, dtype=torch.float32, device="cuda")
     g = layer.backward(to_dev(dY), dev["x"], dev["Wq"], dev["gamma"], dev["C"], dev["Cp"], dev["V"], saved, dV)
     torch.cuda.synchronize()
-    backward_check(cfg, inp, gpu, g, dV.cpu().numpy(), dY)
+    backward_check(cfg, inp, gpu, g, dV.cpu().numpy(), dY, fwd)
 
 
 def test_backward_is_deterministic():
@@ -466,9 +459,8 @@ def test_backward_adam_end_to_end(name):
     note(f"backward_adam {name}: {cfg}")
     inp = pi.make_inputs(cfg, with_dy=True)
     gpu, (layer, dev, saved, y) = run_gpu_forward(cfg, inp)
-    ref = O.forward(cfg, inp)
-    dY, exact = masked_dy(inp, gpu["idx"], ref["rows"])
-    assert exact.mean() > 0.999
+    fwd, _ = reference_forward(cfg, inp, gpu)
+    dY = inp["dY"]
     dYd = to_dev(dY)
     dV = torch.zeros((cfg.slots, cfg.d_value), dtype=torch.float32, device="cuda")
     g_plain = layer.backward(dYd, dev["x"], dev["Wq"], dev["gamma"], dev["C"], dev["Cp"], dev["V"], saved, dV)
@@ -488,11 +480,9 @@ def test_backward_adam_end_to_end(name):
             assert torch.equal(got[:n], v[:n])
         else:
             assert torch.equal(got, v), k
-    # Tokens whose selection differs from the oracle's (near-ties) have dY masked to zero; the rows they pick
-    # on either side are left out of the comparison (lazy Adam moves a touched row even at zero gradient).
-    bad = np.union1d(ref["rows"][~exact].reshape(-1), gpu["idx"][~exact].reshape(-1))
-    uniq = np.setdiff1d(np.unique(ref["rows"]), bad)
-    untouched = np.setdiff1d(np.arange(cfg.slots), np.union1d(np.unique(ref["rows"]), np.unique(gpu["idx"])))
-    g_ref = O.value_grad_rows(ref["rows"], ref["w"], dY, cfg.dtype, uniq)
+    # the oracle's Adam step on the rows of the (judged) GPU selection, every other row bit-identical
+    uniq = np.unique(fwd["rows"])
+    untouched = np.setdiff1d(np.arange(cfg.slots), uniq)
+    g_ref = O.value_grad_rows(fwd["rows"], fwd["w"], dY, cfg.dtype, uniq)
     Vh = Vd.cpu().view(torch.int16).numpy().view(np.uint16) if cfg.dtype == "bf16" else Vd.cpu().numpy()
     adam_check(cfg.dtype, V0, m0, v0, uniq, g_ref, Vh, md.cpu().numpy(), vd.cpu().numpy(), untouched)

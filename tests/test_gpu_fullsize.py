@@ -66,6 +66,100 @@ def test_forward_full_size_sampled(name):
                                rtol=1e-4)
 
 
+# The paper workload is checked over every token.  The skewed one (4x the oracle's work) is checked on
+# 4096 sampled tokens: every other token gets a zero upstream gradient, so it adds exactly nothing to any
+# gradient on either side, and the value rows only it selects must keep their sentinel bits.
+E2E_SAMPLE = {"paper": None, "skewed": 4096}
+
+
+def e2e_upstream(cfg, inp, n_sample):
+    """(gradient-carrying tokens, upstream gradient): every token, or ``n_sample`` of them with the other
+    tokens' rows of dY set to zero."""
+    if n_sample is None:
+        return np.arange(cfg.T), inp["dY"]
+    tok = _sample(cfg.T, n_sample, 23)
+    dY = np.zeros_like(inp["dY"])
+    dY[tok] = inp["dY"][tok]
+    return tok, dY
+
+
+def e2e_check(cfg, inp, tok, dY, saved, y, dV, g):
+    """A whole forward + backward (saved state, y, dV with SENTINEL in untouched rows, gradients g; torch
+    tensors on any device) against the oracle on the gradient-carrying tokens ``tok``."""
+    dev = dV.device
+    G = saved["idx"].cpu().numpy()
+    w_g = saved["w"].cpu().numpy()
+    q_g = P.to_f64(saved["q"])
+    # the query: the oracle's own projection and BatchNorm over every token, equal or one bf16 ulp apart
+    ref = O.query(cfg, inp)
+    ref["tokens"] = np.arange(cfg.T)
+    dq_abs = np.abs(q_g - ref["q"])
+    assert (dq_abs <= P.q_allowed(q_g, ref["q"])).all()
+    assert (dq_abs > 0).mean() < 0.01
+    # the selection: judged against the oracle's exact search on the GPU's query (no slack)
+    C, Cp = O.decode(inp["C"], cfg.dtype), O.decode(inp["Cp"], cfg.dtype)
+    sel = P.lookup_chunks(cfg, q_g[tok], C, Cp)
+    score_of, exact_set, _ = P.judge_selection(cfg, sel, G[tok])
+    assert exact_set.mean() > 0.97
+    s_G = score_of(G[tok])
+    del sel
+    w_ref = O.softmax(s_G, cfg.temperature)
+    tol = P.TOL[cfg.dtype]
+    assert np.abs(w_g[tok] - w_ref).max() <= tol * float(np.abs(w_ref).max())
+    fwd = dict(ref, q=q_g[tok], rows=G[tok].astype(np.int64), scores=s_G, w=w_ref)
+    # y on sampled tokens
+    ty = _sample(len(tok), 384, 29)
+    y_g = P.to_f64(y[torch.from_numpy(tok[ty]).to(y.device)])
+    y_ref = O.gather_sum(fwd["rows"][ty], w_ref[ty], inp["V"], cfg.dtype)
+    assert P.row_rel_err(y_g, y_ref).max() <= tol
+
+    # dV: the touched rows bit for bit, rows without gradient keep the sentinel, sampled rows with all their
+    # lookups
+    uniq = np.unique(G)
+    n = int(g["n_touched"].item())
+    assert n == len(uniq)
+    np.testing.assert_array_equal(g["touched"][:n].cpu().numpy(), uniq)
+    live = np.unique(G[tok])                  # rows with a lookup of a gradient-carrying token
+    mask = torch.ones(cfg.slots, dtype=torch.bool, device=dev)
+    mask[torch.from_numpy(live).to(dev).long()] = False
+    for lo, hi in _row_chunks(cfg.slots):
+        blk, m = dV[lo:hi], mask[lo:hi]
+        assert bool((blk[m] == SENTINEL).all().item()), f"a row without gradient changed in [{lo}, {hi})"
+    which = live[_sample(len(live), 400, 31)]
+    dYt = dY[tok]
+    ref_dv = O.value_grad_rows(fwd["rows"], w_ref, dYt, cfg.dtype, which)
+    dYt_abs = (dYt & np.uint16(0x7FFF)) if cfg.dtype == "bf16" else np.abs(dYt)
+    mag = O.value_grad_rows(fwd["rows"], w_ref, dYt_abs, cfg.dtype, which)
+    got = dV[torch.from_numpy(which).to(dev).long()].cpu().double().numpy() - SENTINEL
+    err = np.abs(got - ref_dv).max(1)
+    assert (err <= tol * mag.max(1) + 2.0 ** -23 * (SENTINEL + np.abs(got).max(1))).all()
+
+    # every reduction gradient by norm, against the oracle's backward on the same selection
+    gb = P.backward_chunks(cfg, inp, fwd, dY, tokens=None if len(tok) == cfg.T else tok)
+    keys = ["dC", "dCp", "dWq", "dx"] + (["dgamma", "dbeta"] if cfg.bn else [])
+    for key in keys:
+        e = P.fro_rel_err(P.to_f64(g[key]), gb[key])
+        assert e <= tol, (key, e)
+    return float(exact_set.mean())
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["paper", "skewed"])
+def test_forward_backward_end_to_end_full_size(name):
+    cfg = pi.CONFIGS[name]
+    note(f"full-size forward + backward end to end: {name}")
+    inp = _inputs(name)
+    tok, dY = e2e_upstream(cfg, inp, E2E_SAMPLE[name])
+    layer = layer_for(cfg)
+    dev = upload({kk: inp[kk] for kk in ("x", "Wq", "gamma", "beta", "C", "Cp", "V")})
+    y, saved = layer.forward(dev["x"], dev["Wq"], dev["gamma"], dev["beta"], dev["C"], dev["Cp"], dev["V"])
+    dV = torch.full((cfg.slots, cfg.d_value), SENTINEL, dtype=torch.float32, device="cuda")
+    g = layer.backward(to_dev(dY), dev["x"], dev["Wq"], dev["gamma"], dev["C"], dev["Cp"], dev["V"], saved, dV)
+    torch.cuda.synchronize()
+    del dev
+    e2e_check(cfg, inp, tok, dY, saved, y, dV, g)
+
+
 def _row_chunks(n, step=1 << 18):
     for lo in range(0, n, step):
         yield lo, min(n, lo + step)

@@ -221,6 +221,41 @@ def test_product_key_selection_is_exact_topk(seed):
         assert fwd["sub_idx1"].shape[-1] == nk              # every sub-key is a candidate
 
 
+def _topk1_case(seed):
+    """A random tiny shape (as in test_product_key_selection_is_exact_topk) and its forward."""
+    rng = np.random.Generator(np.random.PCG64(2000 + seed))
+    nk = int(rng.integers(1, 17))
+    nk2 = int(rng.integers(1, 17))
+    k = int(rng.integers(1, min(nk, nk2) + 1))
+    if seed % 5 == 0:
+        k = min(nk, nk2)            # k + 1 exceeds one half's codebook
+    integer = seed % 2 == 1
+    cfg = _cfg(T=int(rng.integers(1, 9)), d=int(rng.integers(1, 9)), heads=int(rng.integers(1, 4)),
+               dq=int(rng.choice([2, 6, 32])), n_keys=nk, n_keys2=nk2, topk=k, seed=seed,
+               bn=(seed % 3 == 0) and not integer,
+               **({"x_kind": "int", "wq_kind": "int", "key_kind": "int", "int_range": 1} if integer else {}))
+    return cfg, integer
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_top_k_plus_one_list_is_exact(seed):
+    # the (k+1)-best full keys that decide the near-tie rule are the exact top-(k+1) of the full key set
+    cfg, integer = _topk1_case(seed)
+    inp = pi.make_inputs(cfg)
+    fwd = O.forward(cfg, inp)
+    C, Cp = O.decode(inp["C"], "f32"), O.decode(inp["Cp"], "f32")
+    kk = min(cfg.topk + 1, cfg.slots)
+    rows, scores = O.brute_force_select(pi.custom(**{**cfg.__dict__, "topk": kk}), fwd["q"], C, Cp)
+    assert fwd["rows_k1"].shape[-1] == kk
+    assert np.array_equal(fwd["rows_k1"], rows)
+    if integer:
+        assert np.array_equal(fwd["scores_k1"], scores)
+    else:
+        np.testing.assert_allclose(fwd["scores_k1"], scores, rtol=1e-12, atol=1e-12)
+    # its first k entries are the selection itself
+    assert np.array_equal(fwd["rows_k1"][..., :cfg.topk], fwd["rows"])
+
+
 def test_selection_integer_ties_small_brute():
     cfg = _cfg(T=8, heads=3, dq=6, n_keys=5, n_keys2=7, topk=6, x_kind="int", wq_kind="int",
                key_kind="int", int_range=1, seed=5)
@@ -317,10 +352,11 @@ def _loss_and_rows(cfg, inp, dY):
     return float((dY * f["y"]).sum()), f["rows"]
 
 
-@pytest.mark.parametrize("bn", [False, True])
-def test_gradients_by_finite_differences(bn):
+@pytest.mark.parametrize("bn,tau", [(False, 1.0), (True, 1.0), (False, 0.37), (True, 0.37)])
+def test_gradients_by_finite_differences(bn, tau):
+    # tau != 1 pins the softmax backward's 1/tau (the loss is differentiated through softmax(s/tau))
     cfg = _cfg(T=12, d=7, heads=2, dq=6, n_keys=5, n_keys2=4, topk=3, d_value=5, dtype="f64",
-               bn=bn, seed=21)
+               bn=bn, seed=21, temperature=tau)
     raw = pi.make_inputs(cfg)
     inp = {k: (v.astype(np.float64) if isinstance(v, np.ndarray) and v.dtype == np.float32 else v)
            for k, v in raw.items()}
