@@ -174,6 +174,22 @@ pkm_status pkm_forward(pkm_handle_t handle, void* stream, int64_t T, const void*
                        const float* bn_gamma, const float* bn_beta, const void* C, const void* Cp,
                        const void* V, void* y, const pkm_saved* saved, void* ws, size_t ws_bytes);
 
+/* pkm_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and results as pkm_forward, with no ws argument.  The
+ * workspace is a static device array of 128 MiB in the library, one copy
+ * per device (at most 64 devices), held until the process ends; its device
+ * address is looked up on the first call on each device (with that device
+ * current).  Nothing is allocated and nothing needs clearing.  T whose
+ * pkm_workspace_size(handle, T, 0) exceeds 128 MiB returns PKM_ERR_WORKSPACE
+ * (59,728 tokens at h = 4, dq = 512, 1024 sub-keys per half, k = 32).  All calls on one device share the
+ * array: calls that overlap in time on one device (different streams, or
+ * host threads without ordering between them) race; calls in order on one
+ * stream do not.  Other arguments as in pkm_forward. */
+pkm_status pkm_forward_noalloc(pkm_handle_t handle, void* stream, int64_t T, const void* x, const void* Wq,
+                               const float* bn_gamma, const float* bn_beta, const void* C, const void* Cp,
+                               const void* V, void* y, const pkm_saved* saved);
+
 /* Backward of sum(dY * y) given the forward's saved state (same T, same inputs).
  * Outputs (device):
  *   dV [|C|*|C'|, d_value] fp32: only touched rows are read/written (accumulate_dv);

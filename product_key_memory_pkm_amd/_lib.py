@@ -59,6 +59,7 @@ _SIGS = {
     "pkm_get_config": [_VP, ctypes.POINTER(pkm_config)],
     "pkm_workspace_size": [_VP, _I64, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)],
     "pkm_forward": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_saved), _VP, _SZ],
+    "pkm_forward_noalloc": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_saved)],
     "pkm_backward": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_saved), _VP, _VP, _VP,
                      _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
     "pkm_backward_adam": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_saved), _VP, _VP,
@@ -248,6 +249,22 @@ def pkm_forward(h, T, x, Wq, bn_gamma, bn_beta, C, Cp, V, y, saved: dict, ws):
     sv = _saved_struct(saved)
     _check(_invoke("pkm_forward", h, T, _ptr(x), _ptr(Wq), _ptr(bn_gamma), _ptr(bn_beta), _ptr(C),
                              _ptr(Cp), _ptr(V), _ptr(y), ctypes.byref(sv), _ptr(ws), _nbytes(ws)), "pkm_forward")
+
+
+def pkm_forward_noalloc(h, T, x, Wq, bn_gamma, bn_beta, C, Cp, V, y, saved: dict):
+    """pkm_forward with the library's static per-device scratch as its workspace (pkm.h): for callers that
+    cannot allocate.  Calls that overlap in time on one GPU race on that scratch."""
+    st = h.storage
+    for n, t in (("x", x), ("Wq", Wq), ("C", C), ("Cp", Cp), ("y", y)):
+        _dt(t, st, n)
+    _dt(V, h.value_dtype, "V")
+    n = _dims(h, T)
+    _need(x=(x, n["x"]), Wq=(Wq, n["Wq"]), bn_gamma=(bn_gamma, n["F"]), bn_beta=(bn_beta, n["F"]), C=(C, n["C"]),
+          Cp=(Cp, n["Cp"]), V=(V, n["V"]), y=(y, n["y"]))
+    _need_saved(h, T, saved)
+    sv = _saved_struct(saved)
+    _check(_invoke("pkm_forward_noalloc", h, T, _ptr(x), _ptr(Wq), _ptr(bn_gamma), _ptr(bn_beta), _ptr(C), _ptr(Cp),
+                   _ptr(V), _ptr(y), ctypes.byref(sv)), "pkm_forward_noalloc")
 
 
 def pkm_backward(h, T, dY, x, Wq, bn_gamma, C, Cp, V, saved: dict, dV, touched, n_touched, dC, dCp, dWq, dgamma,

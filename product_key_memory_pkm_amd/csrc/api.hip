@@ -492,6 +492,66 @@ pkm_status zero_grads(const pkm_handle_s* h, hipStream_t s, int64_t* n_touched, 
   return PKM_OK;
 }
 
+// pkm_forward's argument checks (everything but the workspace), before any HIP call.
+pkm_status check_forward_args(pkm_handle_t handle, int64_t T, const void* x, const void* Wq, const float* bn_gamma,
+                              const float* bn_beta, const void* C, const void* Cp, const void* V, const void* y,
+                              const pkm_saved* saved) {
+  PKM_TRY(check_handle(handle));
+  PKM_TRY(check_T(handle, T));
+  PKM_TRY(need(x, "x"));
+  PKM_TRY(need(Wq, "Wq"));
+  PKM_TRY(need(C, "C"));
+  PKM_TRY(need(Cp, "Cp"));
+  PKM_TRY(need(V, "V"));
+  PKM_TRY(need(y, "y"));
+  if (handle->cfg.bn == PKM_BN_BATCH) {
+    PKM_TRY(need(bn_gamma, "bn_gamma"));
+    PKM_TRY(need(bn_beta, "bn_beta"));
+  }
+  return check_saved(handle, saved, true);
+}
+
+}  // namespace
+
+// ---- pkm_forward_noalloc: the forward with its workspace in a static device array ----
+//
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops): the forward's workspace regions (per-half lists, BatchNorm partial
+// sums, packed sub-keys) live in `scratch`, one copy per device, held until
+// the process ends.  Every region is written before it is read within a call,
+// so nothing needs clearing.  Calls on one device share the array: calls that
+// overlap in time on one device (different streams, or host threads without
+// ordering) race.
+constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
+constexpr int kNoAllocMaxDevices = 64;
+
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kNoAllocMaxDevices];  // device address of `scratch` per device, null until first use
+
+// The device address of the current device's copy of `scratch` (looked up
+// once per device, with that device current; the name itself is only a host
+// stand-in and must never reach a kernel).
+pkm_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  PKM_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kNoAllocMaxDevices)
+    return fail(PKM_ERR_UNSUPPORTED, "device %d is beyond the %d devices pkm_forward_noalloc serves", dev,
+                kNoAllocMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    PKM_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (p == nullptr || !aligned16(p)) return fail(PKM_ERR_HIP, "scratch has no usable device address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -622,19 +682,7 @@ pkm_status pkm_workspace_size(pkm_handle_t handle, int64_t T, int with_backward,
 pkm_status pkm_forward(pkm_handle_t handle, void* stream, int64_t T, const void* x, const void* Wq,
                        const float* bn_gamma, const float* bn_beta, const void* C, const void* Cp, const void* V,
                        void* y, const pkm_saved* saved, void* ws, size_t ws_bytes) {
-  PKM_TRY(check_handle(handle));
-  PKM_TRY(check_T(handle, T));
-  PKM_TRY(need(x, "x"));
-  PKM_TRY(need(Wq, "Wq"));
-  PKM_TRY(need(C, "C"));
-  PKM_TRY(need(Cp, "Cp"));
-  PKM_TRY(need(V, "V"));
-  PKM_TRY(need(y, "y"));
-  if (handle->cfg.bn == PKM_BN_BATCH) {
-    PKM_TRY(need(bn_gamma, "bn_gamma"));
-    PKM_TRY(need(bn_beta, "bn_beta"));
-  }
-  PKM_TRY(check_saved(handle, saved, true));
+  PKM_TRY(check_forward_args(handle, T, x, Wq, bn_gamma, bn_beta, C, Cp, V, y, saved));
   PKM_TRY(check_ws(handle, T, 0, ws, ws_bytes));
   if (T == 0) return PKM_OK;
   hipStream_t s = as_stream(stream);
@@ -646,6 +694,23 @@ pkm_status pkm_forward(pkm_handle_t handle, void* stream, int64_t T, const void*
   PKM_TRY(run_merge(handle, s, T, sub_idx, sub_score, saved->idx, saved->w, nullptr));
   PKM_TRY(run_gather(handle, s, T, saved->idx, saved->w, V, y));
   return PKM_OK;
+}
+
+pkm_status pkm_forward_noalloc(pkm_handle_t handle, void* stream, int64_t T, const void* x, const void* Wq,
+                               const float* bn_gamma, const float* bn_beta, const void* C, const void* Cp,
+                               const void* V, void* y, const pkm_saved* saved) {
+  PKM_TRY(check_handle(handle));
+  PKM_TRY(check_T(handle, T));
+  const size_t want = ws_size(handle, T, PKM_WS_FORWARD);
+  if (want > kNoAllocScratchBytes)
+    return fail(PKM_ERR_WORKSPACE,
+                "pkm_forward_noalloc: T = %lld needs %zu bytes of workspace, above its static %zu-byte scratch; "
+                "use pkm_forward with a caller workspace",
+                (long long)T, want, kNoAllocScratchBytes);
+  PKM_TRY(check_forward_args(handle, T, x, Wq, bn_gamma, bn_beta, C, Cp, V, y, saved));
+  void* ws = nullptr;
+  PKM_TRY(scratch_for_current_device(&ws));
+  return pkm_forward(handle, stream, T, x, Wq, bn_gamma, bn_beta, C, Cp, V, y, saved, ws, kNoAllocScratchBytes);
 }
 
 // pkm_backward (adam == null: dV written) and pkm_backward_adam (Adam step on

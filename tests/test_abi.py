@@ -395,3 +395,18 @@ def test_binding_rejects_short_tensors_before_the_library():
         chunk(1, target=_t(T * c.d_value - 1))
     with pytest.raises(ValueError):
         chunk(0)
+
+
+def test_forward_noalloc_rejects_oversize_T_before_any_device_call():
+    # the workspace check precedes the pointer checks and the scratch lookup
+    L = _lib()
+    lib = L.lib()
+    h = L.pkm_create(_cfg(L, d_in=64, heads=4, d_query=512, n_keys=1024, n_keys2=1024, topk=32, d_value=64,
+                          dtype="bf16"))
+    T = 60000
+    assert L.pkm_workspace_size(h, T, 0) > 128 << 20
+    st = lib.pkm_forward_noalloc(h.ptr, None, T, None, None, None, None, None, None, None, None, None)
+    assert st == L.PKM_ERR_WORKSPACE and "scratch" in lib.pkm_last_error().decode()
+    # within the limit, the NULL pointers are what it rejects
+    assert lib.pkm_forward_noalloc(h.ptr, None, 1000, None, None, None, None, None, None, None, None,
+                                   None) == L.PKM_ERR_INVALID_ARG
