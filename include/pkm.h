@@ -182,7 +182,7 @@ pkm_status pkm_forward(pkm_handle_t handle, void* stream, int64_t T, const void*
  * address is looked up on the first call on each device (with that device
  * current).  Nothing is allocated and nothing needs clearing.  T whose
  * pkm_workspace_size(handle, T, 0) exceeds 128 MiB returns PKM_ERR_WORKSPACE
- * (59,728 tokens at h = 4, dq = 512, 1024 sub-keys per half, k = 32).  All calls on one device share the
+ * (58,872 tokens at h = 4, dq = 512, 1024 sub-keys per half, k = 32).  All calls on one device share the
  * array: calls that overlap in time on one device (different streams, or
  * host threads without ordering between them) race; calls in order on one
  * stream do not.  Other arguments as in pkm_forward. */

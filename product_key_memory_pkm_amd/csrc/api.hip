@@ -73,7 +73,7 @@ int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 // backward layout never needs the forward's regions, so one buffer of the
 // larger size serves both.
 struct FwdLayout {
-  size_t sub_idx, sub_score, bn_part, keys, total;
+  size_t sub_idx, sub_score, bn_part, keys, sel_list, total;
 };
 struct BwdLayout {
   size_t k0, v0, k1, v1, sort_tmp, grp, key1, key2, seg, scan_tmp, nseg, dw, ds, coef2, dq, bn_part,
@@ -97,6 +97,7 @@ FwdLayout fwd_layout(const pkm_handle_s* h, int64_t T) {
   const size_t nblk = size_t((T + kBnRows - 1) / kBnRows);
   L.bn_part = o;  o += al(nblk * 2 * h->F * sizeof(double));
   L.keys = o;     o += al(score_topk_packed_bytes(c.dtype, c.heads, h->half, c.n_keys, c.n_keys2));
+  L.sel_list = o; o += al(score_select_list_bytes(T, c.heads));
   L.total = o;
   return L;
 }
@@ -241,7 +242,7 @@ pkm_status run_score(const pkm_handle_s* h, hipStream_t s, int64_t T, const void
   const pkm_config& c = h->cfg;
   const FwdLayout L = fwd_layout(h, T);
   PKM_HIP(launch_score_topk(s, c.dtype, q, T, c.heads, c.d_query, C, Cp, c.n_keys, c.n_keys2, c.topk, sub_idx,
-                            sub_score, at<void>(ws, L.keys), c.score_fn == PKM_SCORE_IDW),
+                            sub_score, at<void>(ws, L.keys), c.score_fn == PKM_SCORE_IDW, at<void>(ws, L.sel_list)),
           "sub-key scoring / top-k");
   return PKM_OK;
 }

@@ -49,9 +49,19 @@ hipError_t launch_quantize_fp8(hipStream_t s, int dtype, const void* src, int64_
 bool score_topk_supported(int dtype, int half, int nkeys);
 size_t score_topk_packed_bytes(int dtype, int heads, int half, int nk, int nk2);
 // idw: scores -log |q_half - c| (squared distance floored at 1e-12) instead of q_half . c.
+// list: score_select_list_bytes(ntok, heads) of scratch (the rows the
+// register-resident kernel hands to its exact second launch).
 hipError_t launch_score_topk(hipStream_t s, int dtype, const void* q, int64_t ntok, int heads, int dq,
                              const void* C, const void* Cp, int nk, int nk2, int k, int32_t* sub_idx,
-                             float* sub_score, void* packed, bool idw = false);
+                             float* sub_score, void* packed, bool idw, void* list);
+// The same step for bf16 codebooks of 257-2048 sub-keys with the scores of a
+// token tile kept in registers (launch_score_topk takes it where supported).
+bool score_select_supported(int dtype, int half, int nk, int nk2, int k, bool idw);
+size_t score_select_packed_bytes(int heads, int half, int nk, int nk2);
+size_t score_select_list_bytes(int64_t ntok, int heads);
+hipError_t launch_score_select(hipStream_t s, const void* q, int64_t ntok, int heads, int dq, const void* C,
+                               const void* Cp, int nk, int nk2, int k, int32_t* sub_idx, float* sub_score,
+                               void* packed, void* list);
 
 // a5: k x k candidates -> top-k -> softmax, per (token, head).
 // group_items > 0: item i's rows are offset by ((i / group_items) % group_count) * group_rows
@@ -107,10 +117,8 @@ size_t radix_sort_temp_bytes(int64_t n);
 hipError_t launch_radix_sort_from(hipStream_t s, const uint32_t* keys_in, uint32_t* k0, int32_t* v0,
                                   uint32_t* k1, int32_t* v1, int64_t n, int key_bits, void* temp,
                                   bool* result_in_1);
-// Exclusive scan of n uint32 values (n <= 2^31); temp of scan_temp_bytes(n).
+// Scratch of launch_segments over n sorted keys (the per-block segment counts).
 size_t scan_temp_bytes(int64_t n);
-hipError_t launch_exclusive_scan(hipStream_t s, const uint32_t* in, uint32_t* out, int64_t n, void* temp,
-                                 uint32_t* total /*device, may be null*/);
 
 // The value gradient's long-run plan: every run of more than kVgChunk lookups
 // of one row is cut into chunks, listed as (run, chunk) in chunk_list and

@@ -62,13 +62,17 @@ __global__ __launch_bounds__(256) void merge_softmax_kernel(const int32_t* __res
   __shared__ uint16_t pairs[128];
   __shared__ int npairs;
   __shared__ uint64_t scratch[kWavesPerBlock][64];
-  if (threadIdx.x == 0) {
-    int c = 0;
-    for (int a = 0; a < k; ++a) {
-      const int nb = k / (a + 1);
-      for (int b = 0; b < nb; ++b) pairs[c++] = uint16_t(a | (b << 8));
+  if (threadIdx.x < 64) {  // lane a lists the pairs (a, b < k / (a + 1)) after those of a' < a
+    const int a = threadIdx.x;
+    const int cnt = a < k ? k / (a + 1) : 0;
+    int x = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d, 64);
+      if (a >= d) x += y;
     }
-    npairs = c;
+    for (int b = 0; b < cnt; ++b) pairs[x - cnt + b] = uint16_t(a | (b << 8));
+    if (a == 63) npairs = x;
   }
   __syncthreads();
   const int P = npairs;
@@ -152,7 +156,13 @@ hipError_t launch_merge_softmax(hipStream_t s, const int32_t* sub_idx, const flo
                                 float* score, int64_t group_items, int64_t group_rows, int64_t group_count) {
   if (group_items > 0 && group_count < 1) return hipErrorInvalidValue;
   int64_t blocks = (nitems + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (blocks > 65536) blocks = 65536;
+  // at most 8 blocks per CU: large launches loop (the pair table is built once per block)
+  int cus = 256;
+  {
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  }
+  if (blocks > int64_t(cus) * 8) blocks = int64_t(cus) * 8;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(merge_softmax_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, sub_idx, sub_score,
                      nitems, k, nk2, inv_tau, idx, w, score, group_items, group_rows, group_count);

@@ -632,14 +632,19 @@ size_t score_topk_packed_bytes(int dtype, int heads, int half, int nk, int nk2) 
   const int KC = dtype == kBF16 ? 32 : 16;
   const size_t nks = size_t(round_up(half, KC) / KC);
   // packed operands, then the sub-key squared norms of the IDW scores
-  return size_t(heads) * (size_t((nk + 15) / 16) + size_t((nk2 + 15) / 16)) * nks * 64 * 16 +
-         size_t(heads) * size_t(nk + nk2) * 4;
+  const size_t own = size_t(heads) * (size_t((nk + 15) / 16) + size_t((nk2 + 15) / 16)) * nks * 64 * 16 +
+                     size_t(heads) * size_t(nk + nk2) * 4;
+  // the register-resident kernel's layout, where it may run instead
+  const size_t sel = dtype == kBF16 ? score_select_packed_bytes(heads, half, nk, nk2) : 0;
+  return own > sel ? own : sel;
 }
 
 hipError_t launch_score_topk(hipStream_t s, int dtype, const void* q, int64_t ntok, int heads, int dq,
                              const void* C, const void* Cp, int nk, int nk2, int k, int32_t* sub_idx,
-                             float* sub_score, void* packed, bool idw) {
+                             float* sub_score, void* packed, bool idw, void* list) {
   const int half = dq / 2;
+  if (score_select_supported(dtype, half, nk, nk2, k, idw))
+    return launch_score_select(s, q, ntok, heads, dq, C, Cp, nk, nk2, k, sub_idx, sub_score, packed, list);
   int cus = 256;
   {
     int dev = 0;

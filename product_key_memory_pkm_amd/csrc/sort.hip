@@ -7,17 +7,22 @@
 // lookup order, so the backward is bit-identical from run to run without
 // floating-point atomics.
 //
-// Radix pass (8-bit digit): per 4096-key tile a digit histogram, one exclusive
-// scan over the digit-major (digit, tile) table, then a scatter.  In the
-// scatter each wave owns 1024 consecutive keys of the tile and walks them 64 at
-// a time, ranking every key among equal digits by matching the 8 digit bits
-// with ballots and keeping per-digit counts in its own LDS row (no barrier per
-// round); one barrier then turns the four waves' counts into per-wave bases,
-// and the keys, still in registers, are written out in index order per digit.
+// Radix pass (8-bit digit), two launches.  At most kSortBlocks blocks, block b
+// owning the keys [b chunk, (b + 1) chunk) in sub-tiles of 1024 keys per wave.
+// The first launch counts the digits of each block's chunk into a block-major
+// (block, digit) table.  In the second each block first turns the table into
+// its own write bases (the keys of smaller digits anywhere, plus the keys of
+// its digit in earlier blocks: a few KB of table per block, read from L2), so
+// no scan launch sits between the two.  Then, per sub-tile, each wave walks
+// its 1024 keys 64 at a time, ranking every key among equal digits by matching
+// the 8 digit bits with ballots and keeping per-digit counts in its own LDS
+// row; one barrier turns the waves' counts into per-wave bases, and the keys,
+// still in registers, are written out in index order per digit.
 //
 // Segments of a sorted key array are found in one scan over "key differs from
-// its predecessor" computed on the fly: the apply pass writes each segment's
-// start (and key) at its rank directly.
+// its predecessor" computed on the fly: the apply pass (which sums the earlier
+// blocks' counts itself) writes each segment's start (and key) at its rank
+// directly.
 #include "common.h"
 #include "kernels.h"
 
@@ -25,8 +30,8 @@ namespace pkm {
 
 namespace {
 
-constexpr int kTile = 4096;     // keys per tile (256 threads x 16)
 constexpr int kScanBlock = 4096;
+constexpr int kSortBlocks = 256;  // blocks of a radix pass at most (one per CU)
 
 __device__ __forceinline__ int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
@@ -54,155 +59,223 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh /*[
   return pre + x - v;
 }
 
-__global__ __launch_bounds__(256) void scan_reduce_kernel(const uint32_t* __restrict__ in, int64_t n,
-                                                          uint32_t* __restrict__ part) {
-  __shared__ uint32_t sh[4];
-  const int64_t base = int64_t(blockIdx.x) * kScanBlock + threadIdx.x * 16;
-  uint32_t s = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-    if (base + i < n) s += in[base + i];
-  uint32_t tot;
-  block_excl_scan(s, sh, &tot);
-  if (threadIdx.x == 0) part[blockIdx.x] = tot;
+// Blocks of a radix pass: W waves (1024 W keys per sub-tile), nb blocks of
+// chunk keys each (a multiple of the sub-tile).
+struct RadixPlan {
+  int waves, nb;
+  int64_t chunk;
+};
+
+RadixPlan radix_plan(int64_t n) {
+  RadixPlan p{};
+  p.waves = n >= int64_t(kSortBlocks) * 8192 ? 16 : 4;  // 2 M keys and more: one 16-wave block per CU
+  const int64_t sub = int64_t(1024) * p.waves;
+  const int64_t subs = (n + sub - 1) / sub;
+  const int64_t per = (subs + kSortBlocks - 1) / kSortBlocks;
+  p.chunk = (per > 0 ? per : 1) * sub;
+  p.nb = int((n + p.chunk - 1) / p.chunk);
+  return p;
 }
 
-// Single block: exclusive scan of nb block totals (nb <= 256 * 64).
-__global__ __launch_bounds__(256) void scan_top_kernel(uint32_t* __restrict__ part, int nb,
-                                                       uint32_t* __restrict__ total) {
-  __shared__ uint32_t sh[4];
-  const int per = (nb + 255) / 256;
-  const int b0 = threadIdx.x * per;
-  uint32_t s = 0;
-  for (int i = 0; i < per; ++i)
-    if (b0 + i < nb) s += part[b0 + i];
-  uint32_t tot;
-  uint32_t run = block_excl_scan(s, sh, &tot);
-  for (int i = 0; i < per; ++i)
-    if (b0 + i < nb) {
-      uint32_t v = part[b0 + i];
-      part[b0 + i] = run;
-      run += v;
-    }
-  if (threadIdx.x == 0 && total) *total = tot;
-}
-
-__global__ __launch_bounds__(256) void scan_apply_kernel(const uint32_t* __restrict__ in, int64_t n,
-                                                         const uint32_t* __restrict__ part,
-                                                         uint32_t* __restrict__ out) {
-  __shared__ uint32_t sh[4];
-  const int64_t base = int64_t(blockIdx.x) * kScanBlock + threadIdx.x * 16;
-  uint32_t v[16];
-  uint32_t s = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    v[i] = base + i < n ? in[base + i] : 0u;
-    s += v[i];
-  }
-  uint32_t tot;
-  uint32_t run = block_excl_scan(s, sh, &tot) + part[blockIdx.x];
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-    if (base + i < n) {
-      out[base + i] = run;
-      run += v[i];
-    }
-}
-
-// Digit histogram of one tile.  Lanes holding the same digit are matched with
-// ballots first, so each distinct digit of a wave takes one LDS atomic: skewed
-// keys (a few hot sub-keys) would otherwise serialise on one counter.
-__global__ __launch_bounds__(256) void radix_hist_kernel(const uint32_t* __restrict__ keys, int64_t n, int shift,
-                                                         int nb, uint32_t* __restrict__ hist) {
-  __shared__ uint32_t cnt[256];
-  cnt[threadIdx.x] = 0;
+// Digit counts of one block's chunk.  Lanes holding the same digit are matched
+// with ballots first, so each distinct digit of a wave takes one LDS atomic:
+// skewed keys (a few hot rows or sub-keys) would otherwise serialise on one counter.
+template <int W>
+__global__ __launch_bounds__(64 * W) void radix_hist_kernel(const uint32_t* __restrict__ keys, int64_t n, int shift,
+                                                            int64_t chunk, int nb, uint32_t* __restrict__ hist) {
+  constexpr int NT = 64 * W;
+  constexpr int G = W / 4;  // groups of four waves, each with its own counters
+  __shared__ uint32_t cnts[G][256];
+  for (int d = threadIdx.x; d < G * 256; d += NT) cnts[d >> 8][d & 255] = 0;
   __syncthreads();
-  const int64_t base = int64_t(blockIdx.x) * kTile;
-  uint32_t key[kTile / 256];
+  uint32_t* cnt = cnts[(threadIdx.x >> 6) / 4];
+  const int64_t lo = int64_t(blockIdx.x) * chunk;
+  const int64_t hi = lo + chunk < n ? lo + chunk : n;
+  for (int64_t base = lo; base < hi; base += 16 * NT) {
+    uint32_t key[16];
 #pragma unroll
-  for (int i = 0; i < kTile / 256; ++i) {
-    const int64_t e = base + i * 256 + threadIdx.x;
-    key[i] = e < n ? keys[e] : 0u;
-  }
-#pragma unroll
-  for (int i = 0; i < kTile / 256; ++i) {
-    const bool ok = base + i * 256 + threadIdx.x < n;
-    const uint32_t d = (key[i] >> shift) & 0xFF;
-    uint64_t peers = ballot(ok);
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const bool bit = (d >> b) & 1u;
-      const uint64_t m = ballot(bit);
-      peers &= bit ? m : ~m;
+    for (int i = 0; i < 16; ++i) {
+      const int64_t e = base + i * NT + threadIdx.x;
+      key[i] = e < hi ? keys[e] : 0u;
     }
-    if (ok && lanes_below(peers) == 0) atomicAdd(&cnt[d], uint32_t(popc64(peers)));
-  }
-  __syncthreads();
-  hist[int64_t(threadIdx.x) * nb + blockIdx.x] = cnt[threadIdx.x];
-}
-
-// Stable scatter of one tile.  vals_in == nullptr: the value is the key's index.
-constexpr int kWaveKeys = kTile / 4;     // keys per wave and tile
-constexpr int kRounds = kWaveKeys / 64;  // 64 keys per round
-
-__global__ __launch_bounds__(256) void radix_scatter_kernel(const uint32_t* __restrict__ keys_in,
-                                                            const int32_t* __restrict__ vals_in, int64_t n,
-                                                            int shift, int nb, const uint32_t* __restrict__ offs,
-                                                            uint32_t* __restrict__ keys_out,
-                                                            int32_t* __restrict__ vals_out) {
-  __shared__ uint32_t cnt[4][256];  // per-wave digit counts, then per-wave write bases
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) cnt[w][tid] = 0;
-  __syncthreads();
-  const int64_t base = int64_t(blockIdx.x) * kTile + int64_t(wave) * kWaveKeys;
-  uint32_t key[kRounds];
-  int32_t val[kRounds];
-  uint32_t lpos[kRounds];
-#pragma unroll
-  for (int i = 0; i < kRounds; ++i) {
-    const int64_t e = base + i * 64 + lane;
-    const bool ok = e < n;
-    key[i] = ok ? keys_in[e] : 0u;
-    val[i] = ok ? (vals_in ? vals_in[e] : int32_t(e)) : 0;
-  }
-#pragma unroll
-  for (int i = 0; i < kRounds; ++i) {
-    const int64_t e = base + i * 64 + lane;
-    const bool ok = e < n;
-    const uint32_t d = (key[i] >> shift) & 0xFF;
-    uint64_t peers = ballot(ok);
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const bool bit = (d >> b) & 1u;
-      const uint64_t m = ballot(bit);
-      peers &= bit ? m : ~m;
-    }
-    const int rk = lanes_below(peers);
-    const uint32_t before = ok ? cnt[wave][d] : 0u;  // every lane reads before the leader writes
-    lpos[i] = before + uint32_t(rk);
-    if (ok && rk == 0) cnt[wave][d] = before + uint32_t(popc64(peers));
-  }
-  __syncthreads();
-  {  // bases: tile offset of digit tid, then the earlier waves' counts
-    uint32_t run = offs[int64_t(tid) * nb + blockIdx.x];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t c = cnt[w][tid];
-      cnt[w][tid] = run;
-      run += c;
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kRounds; ++i) {
-    const int64_t e = base + i * 64 + lane;
-    if (e < n) {
+    for (int i = 0; i < 16; ++i) {
+      const bool ok = base + i * NT + threadIdx.x < hi;
       const uint32_t d = (key[i] >> shift) & 0xFF;
-      const uint32_t pos = cnt[wave][d] + lpos[i];
-      keys_out[pos] = key[i];
-      vals_out[pos] = val[i];
+      uint64_t peers = ballot(ok);
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const bool bit = (d >> b) & 1u;
+        const uint64_t m = ballot(bit);
+        peers &= bit ? m : ~m;
+      }
+      if (ok && lanes_below(peers) == 0) atomicAdd(&cnt[d], uint32_t(popc64(peers)));
     }
+  }
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) c += cnts[g][threadIdx.x];
+    hist[int64_t(blockIdx.x) * 256 + threadIdx.x] = c;
+  }
+}
+
+// Stable scatter of one block's chunk.  vals_in == nullptr: the value is the key's index.
+// Per sub-tile the ranked keys are first placed in LDS in digit order (each
+// digit's keys in index order), then written out by consecutive threads: a
+// digit's keys land in consecutive output positions, so the writes coalesce.
+template <int W>
+constexpr size_t radix_scatter_lds() {
+  return size_t(1024) * W * 8 + size_t(W) * 256 * 4 + 2 * 256 * 4 + 16;
+}
+
+template <int W>
+__global__ __launch_bounds__(64 * W) void radix_scatter_kernel(const uint32_t* __restrict__ keys_in,
+                                                               const int32_t* __restrict__ vals_in, int64_t n,
+                                                               int shift, int64_t chunk, int nb,
+                                                               const uint32_t* __restrict__ hist,
+                                                               uint32_t* __restrict__ keys_out,
+                                                               int32_t* __restrict__ vals_out) {
+  constexpr int NT = 64 * W;
+  constexpr int SUB = 1024 * W;    // keys per sub-tile
+  constexpr int PARTS = NT / 256;  // threads per digit summing the table
+  constexpr int kRounds = 16;      // 64-key rounds per wave and sub-tile
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  uint32_t* lkey = reinterpret_cast<uint32_t*>(smem);                  // [SUB] sub-tile in digit order
+  int32_t* lval = reinterpret_cast<int32_t*>(lkey + SUB);               // [SUB]
+  uint32_t (*part)[PARTS][256] = reinterpret_cast<uint32_t (*)[PARTS][256]>(smem);  // prologue only (aliases lkey)
+  uint32_t (*cnt)[256] = reinterpret_cast<uint32_t (*)[256]>(lval + SUB);  // [W][256] counts, then LDS bases
+  uint32_t* run = &cnt[W][0];      // [256] output position of the digit's next key
+  uint32_t* gbase = run + 256;     // [256] output position minus LDS position, this sub-tile
+  uint32_t* wsum = gbase + 256;    // [4]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  {  // the digit's keys in earlier blocks (pre) and in all blocks (tot): thread (pp, d)
+     // sums rows pp, pp + PARTS, ... of the block-major table, 16 rows in flight
+    const int d = tid & 255, pp = tid >> 8;
+    uint32_t pre = 0, tot = 0;
+    for (int t0 = pp; t0 < nb; t0 += 16 * PARTS) {
+      uint32_t v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int t = t0 + i * PARTS;
+        v[i] = t < nb ? hist[int64_t(t) * 256 + d] : 0u;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        tot += v[i];
+        pre += t0 + i * PARTS < int(blockIdx.x) ? v[i] : 0u;
+      }
+    }
+    part[0][pp][d] = pre;
+    part[1][pp][d] = tot;
+  }
+  __syncthreads();
+  {
+    uint32_t pre = 0, tot = 0, x = 0;
+    if (tid < 256) {
+#pragma unroll
+      for (int pp = 0; pp < PARTS; ++pp) {
+        pre += part[0][pp][tid];
+        tot += part[1][pp][tid];
+      }
+      x = tot;  // inclusive scan of the digit totals over the wave
+#pragma unroll
+      for (int dd = 1; dd < 64; dd <<= 1) {
+        const uint32_t y = __shfl_up(x, dd, 64);
+        if (lane >= dd) x += y;
+      }
+      if (lane == 63) wsum[wave] = x;
+    }
+    __syncthreads();
+    if (tid < 256) {
+      uint32_t below = 0;
+      for (int w = 0; w < wave; ++w) below += wsum[w];
+      run[tid] = below + x - tot + pre;
+    }
+  }
+  const int64_t lo = int64_t(blockIdx.x) * chunk;
+  const int64_t hi = lo + chunk < n ? lo + chunk : n;
+  for (int64_t sb = lo; sb < hi; sb += SUB) {
+    for (int d = lane; d < 256; d += 64) cnt[wave][d] = 0;
+    const int64_t base = sb + int64_t(wave) * 1024;
+    uint32_t key[kRounds];
+    int32_t val[kRounds];
+    uint32_t lpos[kRounds];
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i) {
+      const int64_t e = base + i * 64 + lane;
+      const bool ok = e < hi;
+      key[i] = ok ? keys_in[e] : 0u;
+      val[i] = ok ? (vals_in ? vals_in[e] : int32_t(e)) : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i) {
+      const int64_t e = base + i * 64 + lane;
+      const bool ok = e < hi;
+      const uint32_t d = (key[i] >> shift) & 0xFF;
+      uint64_t peers = ballot(ok);
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const bool bit = (d >> b) & 1u;
+        const uint64_t m = ballot(bit);
+        peers &= bit ? m : ~m;
+      }
+      const int rk = lanes_below(peers);
+      const uint32_t before = ok ? cnt[wave][d] : 0u;  // every lane reads before the leader writes
+      lpos[i] = before + uint32_t(rk);
+      if (ok && rk == 0) cnt[wave][d] = before + uint32_t(popc64(peers));
+    }
+    __syncthreads();  // counts done (and, on the first sub-tile, the prologue's reads of part)
+    uint32_t tot = 0, x = 0;
+    if (tid < 256) {  // the sub-tile's keys of digit tid, and their scan over the digits
+#pragma unroll
+      for (int w = 0; w < W; ++w) tot += cnt[w][tid];
+      x = tot;
+#pragma unroll
+      for (int dd = 1; dd < 64; dd <<= 1) {
+        const uint32_t y = __shfl_up(x, dd, 64);
+        if (lane >= dd) x += y;
+      }
+      if (lane == 63) wsum[wave] = x;
+    }
+    __syncthreads();
+    if (tid < 256) {  // LDS position of the digit's first key per wave; output offset
+      uint32_t below = 0;
+      for (int w = 0; w < wave; ++w) below += wsum[w];
+      const uint32_t lst = below + x - tot;
+      uint32_t r = lst;
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const uint32_t c = cnt[w][tid];
+        cnt[w][tid] = r;
+        r += c;
+      }
+      gbase[tid] = run[tid] - lst;
+      run[tid] += tot;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i) {
+      if (base + i * 64 + lane < hi) {
+        const uint32_t p = cnt[wave][(key[i] >> shift) & 0xFF] + lpos[i];
+        lkey[p] = key[i];
+        lval[p] = val[i];
+      }
+    }
+    __syncthreads();
+    const int ns = int(hi - sb < SUB ? hi - sb : SUB);
+#pragma unroll 8
+    for (int j = 0; j < SUB / NT; ++j) {
+      const int i = j * NT + tid;
+      if (i < ns) {
+        const uint32_t kk = lkey[i];
+        const uint32_t pos = gbase[(kk >> shift) & 0xFF] + uint32_t(i);
+        keys_out[pos] = kk;
+        vals_out[pos] = lval[i];
+      }
+    }
+    __syncthreads();  // the next sub-tile reuses the LDS buffers and bases
   }
 }
 
@@ -246,17 +319,27 @@ __global__ __launch_bounds__(256) void seg_reduce_kernel(const uint32_t* __restr
 }
 
 // Writes seg_start[rank] = i (and touched[rank] = k[i]) for every segment start
-// i; the last block also closes the table: seg_start[total] = n, *count = total.
+// i, the block's first rank being the sum of the earlier blocks' counts in part
+// (nb entries, summed here); the last block also closes the table:
+// seg_start[total] = n, *count = total.
 __global__ __launch_bounds__(256) void seg_apply_kernel(const uint32_t* __restrict__ k, int64_t n,
-                                                        const uint32_t* __restrict__ part,
-                                                        const uint32_t* __restrict__ total,
+                                                        const uint32_t* __restrict__ part, int nb,
                                                         int32_t* __restrict__ seg_start,
                                                         int32_t* __restrict__ touched, int64_t* __restrict__ count) {
   __shared__ uint32_t sh[4];
+  uint32_t pre = 0, all = 0;
+  for (int t = threadIdx.x; t < nb; t += 256) {
+    const uint32_t v = part[t];
+    all += v;
+    pre += t < int(blockIdx.x) ? v : 0u;
+  }
+  uint32_t base, total;
+  block_excl_scan(pre, sh, &base);
+  block_excl_scan(all, sh, &total);
   const int64_t b0 = int64_t(blockIdx.x) * kScanBlock + threadIdx.x * 16;
   const uint32_t f = seg_flags16(k, n, b0);
   uint32_t tot;
-  uint32_t rank = block_excl_scan(uint32_t(__popc(f)), sh, &tot) + part[blockIdx.x];
+  uint32_t rank = block_excl_scan(uint32_t(__popc(f)), sh, &tot) + base;
 #pragma unroll
   for (int i = 0; i < 16; ++i)
     if (f & (1u << i)) {
@@ -265,8 +348,8 @@ __global__ __launch_bounds__(256) void seg_apply_kernel(const uint32_t* __restri
       ++rank;
     }
   if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) {
-    seg_start[*total] = int32_t(n);
-    *count = int64_t(*total);
+    seg_start[total] = int32_t(n);
+    *count = int64_t(total);
   }
 }
 
@@ -559,6 +642,20 @@ inline unsigned grid1d(int64_t n, int64_t cap = 16384) {
   return unsigned(b);
 }
 
+template <int W>
+hipError_t radix_pass(hipStream_t s, const uint32_t* kin, const int32_t* vin, int64_t n, int shift,
+                      const RadixPlan& pl, uint32_t* hist, uint32_t* kout, int32_t* vout) {
+  static LdsLimit lim;  // dynamic LDS above 64 KB, raised once per device
+  constexpr size_t lds = radix_scatter_lds<W>();
+  const hipError_t e = lim.ensure(reinterpret_cast<const void*>(radix_scatter_kernel<W>), int(lds));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(radix_hist_kernel<W>, dim3(unsigned(pl.nb)), dim3(64 * W), 0, s, kin, n, shift, pl.chunk, pl.nb,
+                     hist);
+  hipLaunchKernelGGL(radix_scatter_kernel<W>, dim3(unsigned(pl.nb)), dim3(64 * W), lds, s, kin, vin, n, shift,
+                     pl.chunk, pl.nb, hist, kout, vout);
+  return hipSuccess;
+}
+
 }  // namespace
 
 size_t scan_temp_bytes(int64_t n) {
@@ -566,33 +663,12 @@ size_t scan_temp_bytes(int64_t n) {
   return size_t((nb + 64) * 4);
 }
 
-hipError_t launch_exclusive_scan(hipStream_t s, const uint32_t* in, uint32_t* out, int64_t n, void* temp,
-                                 uint32_t* total) {
-  const int64_t nb = (n + kScanBlock - 1) / kScanBlock;
-  if (nb > 256 * 64) return hipErrorInvalidValue;
-  uint32_t* part = static_cast<uint32_t*>(temp);
-  if (nb > 0) {
-    hipLaunchKernelGGL(scan_reduce_kernel, dim3(unsigned(nb)), dim3(256), 0, s, in, n, part);
-  }
-  hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(256), 0, s, part, int(nb), total);
-  if (nb > 0) {
-    hipLaunchKernelGGL(scan_apply_kernel, dim3(unsigned(nb)), dim3(256), 0, s, in, n, part, out);
-  }
-  return hipGetLastError();
-}
-
-size_t radix_sort_temp_bytes(int64_t n) {
-  const int64_t nb = (n + kTile - 1) / kTile;
-  const int64_t h = 256 * nb;
-  return size_t(h * 4 * 2) + scan_temp_bytes(h) + 256;
-}
+size_t radix_sort_temp_bytes(int64_t n) { return size_t(256) * radix_plan(n).nb * 4 + 256; }
 
 hipError_t launch_radix_sort_from(hipStream_t s, const uint32_t* keys_in, uint32_t* k0, int32_t* v0, uint32_t* k1,
                                   int32_t* v1, int64_t n, int key_bits, void* temp, bool* result_in_1) {
-  const int64_t nb = (n + kTile - 1) / kTile;
+  const RadixPlan pl = radix_plan(n);
   uint32_t* hist = static_cast<uint32_t*>(temp);
-  uint32_t* offs = hist + 256 * nb;
-  void* stemp = offs + 256 * nb;
   int passes = (key_bits + 7) / 8;
   if (passes < 1) passes = 1;
   const uint32_t* kin = keys_in;
@@ -601,12 +677,15 @@ hipError_t launch_radix_sort_from(hipStream_t s, const uint32_t* keys_in, uint32
   int32_t* vout = v0;
   for (int p = 0; p < passes; ++p) {
     const int shift = 8 * p;
-    if (nb > 0) {
-      hipLaunchKernelGGL(radix_hist_kernel, dim3(unsigned(nb)), dim3(256), 0, s, kin, n, shift, int(nb), hist);
-      hipError_t e = launch_exclusive_scan(s, hist, offs, 256 * nb, stemp, nullptr);
+    if (pl.nb > 0) {
+      hipError_t e = hipSuccess;
+      if (pl.waves == 16)
+        e = radix_pass<16>(s, kin, vin, n, shift, pl, hist, kout, vout);
+      else if (pl.waves == 8)
+        e = radix_pass<8>(s, kin, vin, n, shift, pl, hist, kout, vout);
+      else
+        e = radix_pass<4>(s, kin, vin, n, shift, pl, hist, kout, vout);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(radix_scatter_kernel, dim3(unsigned(nb)), dim3(256), 0, s, kin, vin, n, shift, int(nb),
-                         offs, kout, vout);
     }
     kin = kout;
     vin = vout;
@@ -723,14 +802,12 @@ hipError_t launch_sort_segments_separate(hipStream_t s, const uint32_t* keys_in,
 
 hipError_t launch_segments(hipStream_t s, const uint32_t* sorted_keys, int64_t n, int32_t* seg_start,
                            int32_t* touched, int64_t* count, void* scan_temp) {
-  uint32_t* total = static_cast<uint32_t*>(scan_temp);
-  uint32_t* part = total + 64;
+  uint32_t* part = static_cast<uint32_t*>(scan_temp);
   const int64_t nb = (n + kScanBlock - 1) / kScanBlock;
-  if (nb > 256 * 64) return hipErrorInvalidValue;
-  if (nb > 0) hipLaunchKernelGGL(seg_reduce_kernel, dim3(unsigned(nb)), dim3(256), 0, s, sorted_keys, n, part);
-  hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(256), 0, s, part, int(nb), total);
+  if (nb > (int64_t(1) << 20)) return hipErrorInvalidValue;
   if (nb > 0) {
-    hipLaunchKernelGGL(seg_apply_kernel, dim3(unsigned(nb)), dim3(256), 0, s, sorted_keys, n, part, total,
+    hipLaunchKernelGGL(seg_reduce_kernel, dim3(unsigned(nb)), dim3(256), 0, s, sorted_keys, n, part);
+    hipLaunchKernelGGL(seg_apply_kernel, dim3(unsigned(nb)), dim3(256), 0, s, sorted_keys, n, part, int(nb),
                        seg_start, touched, count);
   } else {
     hipLaunchKernelGGL(seg_empty_kernel, dim3(1), dim3(64), 0, s, seg_start, count);

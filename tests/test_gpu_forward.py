@@ -90,6 +90,13 @@ SCORE_CASES = [
     (33, 3, 32, 300, 280, 8, "f32", True),        # 4 splits, ties across splits: lowest index wins
     (20, 2, 64, 512, 512, 16, "bf16", False),     # 2 splits
     (25, 1, 16, 130, 129, 4, "bf16", True),       # splits of unequal width
+    # bf16 codebooks with many tiles, ragged codebooks, wide halves and heavy ties
+    (4096, 4, 512, 1024, 1024, 32, "bf16", False),  # the paper's key shape, many tiles
+    (1500, 2, 256, 700, 600, 16, "bf16", False),    # ragged codebooks, unequal halves
+    (300, 1, 64, 400, 300, 8, "bf16", False),       # k = 8, one head
+    (257, 2, 1024, 2048, 1500, 32, "bf16", False),  # half of 512 dims, 2048 sub-keys, ragged token tail
+    (2000, 2, 512, 1024, 1024, 32, "bf16", True),   # heavy ties across the whole codebook
+    (100, 2, 512, 2048, 2048, 32, "bf16", True),    # the same with 2048 sub-keys and few tokens
 ]
 
 
