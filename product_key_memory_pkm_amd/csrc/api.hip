@@ -221,12 +221,15 @@ pkm_status run_query(const pkm_handle_s* h, hipStream_t s, int64_t T, const void
                      const float* gamma, const float* beta, const pkm_saved* sv, void* ws) {
   const pkm_config& c = h->cfg;
   const FwdLayout L = fwd_layout(h, T);
-  PKM_HIP(launch_gemm_nt(s, c.dtype, T, h->F, c.d_in, x, c.d_in, Wq, c.d_in, sv->q_pre, h->F, false, 1, 0),
+  const bool bn = c.bn == PKM_BN_BATCH;
+  double* part = at<double>(ws, L.bn_part);
+  bool partials_done = false;  // the projection's epilogue may give the BatchNorm partial sums
+  PKM_HIP(launch_gemm_nt(s, c.dtype, T, h->F, c.d_in, x, c.d_in, Wq, c.d_in, sv->q_pre, h->F, false, 1, 0,
+                         bn ? part : nullptr, &partials_done),
           "projection GEMM");
-  if (c.bn == PKM_BN_BATCH) {
-    double* part = at<double>(ws, L.bn_part);
+  if (bn) {
     const int nblk = int((T + kBnRows - 1) / kBnRows);
-    PKM_HIP(launch_bn_partials(s, sv->q_pre, T, h->F, part), "BatchNorm partial sums");
+    if (!partials_done) PKM_HIP(launch_bn_partials(s, sv->q_pre, T, h->F, part), "BatchNorm partial sums");
     PKM_HIP(launch_bn_finalize(s, part, nblk, T, h->F, c.bn_eps, sv->bn_mean, sv->bn_rstd), "BatchNorm finalize");
     PKM_HIP(launch_bn_apply(s, c.dtype, sv->q_pre, T, h->F, sv->bn_mean, sv->bn_rstd, gamma, beta, sv->q),
             "BatchNorm apply");

@@ -195,7 +195,8 @@ constexpr int kDmaWM = 4, kDmaWN = 2;
 __global__ __launch_bounds__(512) void gemm_nt_dma_kernel(int64_t M, int64_t N, const bf16_t* __restrict__ A,
                                                           int64_t lda, const bf16_t* __restrict__ B, int64_t ldb,
                                                           void* __restrict__ Cout, int64_t ldc, int out_bf16,
-                                                          int64_t K, int64_t kchunk, int64_t split_stride) {
+                                                          int64_t K, int64_t kchunk, int64_t split_stride,
+                                                          double* __restrict__ bn_part) {
   constexpr int BM = 256, BN = 256, NW = kDmaWM * kDmaWN, TI = BM / kDmaWM / 32, TJ = BN / kDmaWN / 32;
   constexpr int BPW = 16 / NW;        // 1 KB blocks per operand, stage and wave
   constexpr int PER = 2 * BPW;        // DMA instructions per stage and wave
@@ -274,6 +275,46 @@ __global__ __launch_bounds__(512) void gemm_nt_dma_kernel(int64_t M, int64_t N, 
     lds_barrier();  // stage kt's buffer is refilled by the next iteration's issue
   }
   // 32x32 accumulator layout: element e of lane l is row 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32
+  if (bn_part != nullptr) {
+    // BatchNorm partial sums of the tile's columns over its 256 rows (rows past M
+    // hold zero), in fp64: per lane over its 32 rows of each column, then the
+    // other half-wave's rows, then the four row waves in a fixed order
+    double sm[TJ], sq[TJ];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      sm[j] = 0.0;
+      sq[j] = 0.0;
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const double v = double(acc[i][j][e]);
+          sm[j] += v;
+          sq[j] += v * v;
+        }
+      sm[j] += __shfl_xor(sm[j], 32, 64);
+      sq[j] += __shfl_xor(sq[j], 32, 64);
+    }
+    double* red = reinterpret_cast<double*>(smem);  // [kDmaWM][2][BN]; the stages are no longer read
+    if (lane < 32) {
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int cl = (wn * TJ + j) * 32 + lane;
+        red[(wm * 2 + 0) * BN + cl] = sm[j];
+        red[(wm * 2 + 1) * BN + cl] = sq[j];
+      }
+    }
+    __syncthreads();
+    if (tid < BN && n0 + tid < N) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        double v = red[a * BN + tid];
+#pragma unroll
+        for (int w = 1; w < kDmaWM; ++w) v += red[(w * 2 + a) * BN + tid];
+        bn_part[((m0 / BM) * 2 + a) * N + n0 + tid] = v;
+      }
+    }
+  }
   char* Cb = reinterpret_cast<char*>(Cout) + int64_t(blockIdx.y) * split_stride * (out_bf16 ? 2 : 4);
 #pragma unroll
   for (int i = 0; i < TI; ++i)
@@ -438,8 +479,9 @@ int gemm_nt_splits(int dtype, int64_t M, int64_t N, int64_t K, int cus, int max_
 
 hipError_t launch_gemm_nt(hipStream_t s, int dtype, int64_t M, int64_t N, int64_t K, const void* A,
                           int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, bool out_bf16,
-                          int splits, int64_t split_stride) {
+                          int splits, int64_t split_stride, double* bn_part, bool* bn_done) {
   if (splits < 1) splits = 1;
+  if (bn_done) *bn_done = false;
   if (dtype == kBF16 && K % 32 == 0 && M * lda * 2 < (int64_t(1) << 32) - 64 &&
       N * ldb * 2 < (int64_t(1) << 32) - 64) {
     int64_t kchunk = (K + splits - 1) / splits;
@@ -449,9 +491,11 @@ hipError_t launch_gemm_nt(hipStream_t s, int dtype, int64_t M, int64_t N, int64_
     static LdsLimit lim;
     const hipError_t e = lim.ensure(reinterpret_cast<const void*>(gemm_nt_dma_kernel), int(lds));
     if (e != hipSuccess) return e;
+    const bool fuse_bn = bn_part != nullptr && splits == 1 && !out_bf16 && kBnRows == 256;
     hipLaunchKernelGGL(gemm_nt_dma_kernel, dim3(unsigned(tiles), unsigned(splits)), dim3(512), lds, s, M, N,
                        static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(B), ldb, C, ldc,
-                       int(out_bf16), K, kchunk, split_stride);
+                       int(out_bf16), K, kchunk, split_stride, fuse_bn ? bn_part : nullptr);
+    if (fuse_bn && bn_done) *bn_done = true;
     return hipGetLastError();
   }
   const int64_t bk = dtype == kBF16 ? 64 : 32;

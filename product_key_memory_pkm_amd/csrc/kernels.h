@@ -74,9 +74,13 @@ hipError_t launch_merge_softmax(hipStream_t s, const int32_t* sub_idx, const flo
 
 // C[M, N] = A[M, K] * B[N, K]^T; A, B storage dtype, C fp32 (or bf16 when out_bf16).
 // splits > 1: blockIdx.z handles a slice of K and writes C + z * split_stride.
+// bn_part (may be null; fp32 output, one split only): also the BatchNorm
+// partial sums of C's columns over row blocks of kBnRows, in the layout of
+// launch_bn_partials, when the kernel taking this shape can give them; then
+// *bn_done is set (else left false and the caller runs launch_bn_partials).
 hipError_t launch_gemm_nt(hipStream_t s, int dtype, int64_t M, int64_t N, int64_t K, const void* A,
                           int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, bool out_bf16,
-                          int splits, int64_t split_stride);
+                          int splits, int64_t split_stride, double* bn_part = nullptr, bool* bn_done = nullptr);
 // Split-K count for launch_gemm_nt on a device with cus compute units: whole
 // rounds of resident blocks, the partial-sum traffic counted against it.
 int gemm_nt_splits(int dtype, int64_t M, int64_t N, int64_t K, int cus, int max_splits);

@@ -309,14 +309,14 @@ __global__ __launch_bounds__(kSelThreads) void score_select_kernel(
 // The listed rows (token, head, half as ((t heads + h) 2 + p)), one workgroup
 // each.  The row's scores are recomputed as fp32 dot products: a group of 16
 // lanes takes one sub-key, each lane 8-dim pieces of it (coalesced 16-byte
-// loads), four sub-keys per group in flight, and the group's partial sums are
-// added with lane exchanges.  Then the k largest (key, ~index) words come from
+// loads; eight sub-keys per group and two pieces of each in flight), and the
+// group's partial sums are added with lane exchanges.  Then the k largest (key, ~index) words come from
 // a bisection over the 64-bit words, every thread holding up to four of them
 // (the words are distinct, so exactly k are at or above the result), and are
 // sorted by one wave.
 constexpr int kExactThreads = 512;
 constexpr int kExactSlots = kExactThreads / 16;  // sub-keys per round and column of 16-lane groups
-constexpr int kExactU = 4;                       // sub-keys per group in flight
+constexpr int kExactU = 8;                       // sub-keys per group in flight
 constexpr int kExactWords = 2048 / kExactThreads;
 
 __global__ __launch_bounds__(kExactThreads) void score_rows_exact_kernel(
@@ -348,23 +348,30 @@ __global__ __launch_bounds__(kExactThreads) void score_rows_exact_kernel(
       float acc[kExactU];
 #pragma unroll
       for (int u = 0; u < kExactU; ++u) acc[u] = 0.f;
-      for (int c = g; c < nch; c += 16) {
-        u32x4 v[kExactU];
+      for (int c0 = g; c0 < nch; c0 += 32) {  // two 8-dim pieces per lane and sub-key in flight
+        u32x4 v[2][kExactU];
 #pragma unroll
-        for (int u = 0; u < kExactU; ++u) {
-          const int j = j0 + u * kExactSlots + slot;
-          v[u] = j < ncols ? ld16(K + size_t(j) * half + c * 8) : u32x4{0u, 0u, 0u, 0u};
-        }
-        float qv[8];
+        for (int hp = 0; hp < 2; ++hp)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qv[e] = qs[c * 8 + e];
+          for (int u = 0; u < kExactU; ++u) {
+            const int j = j0 + u * kExactSlots + slot, c = c0 + 16 * hp;
+            v[hp][u] = j < ncols && c < nch ? ld16(K + size_t(j) * half + c * 8) : u32x4{0u, 0u, 0u, 0u};
+          }
 #pragma unroll
-        for (int u = 0; u < kExactU; ++u) {
-          const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        for (int hp = 0; hp < 2; ++hp) {
+          const int c = c0 + 16 * hp;
+          if (c >= nch) continue;
+          float qv[8];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[u] = fmaf(qv[2 * e], __uint_as_float(wd[e] << 16), acc[u]);
-            acc[u] = fmaf(qv[2 * e + 1], __uint_as_float(wd[e] & 0xFFFF0000u), acc[u]);
+          for (int e = 0; e < 8; ++e) qv[e] = qs[c * 8 + e];
+#pragma unroll
+          for (int u = 0; u < kExactU; ++u) {
+            const uint32_t wd[4] = {v[hp][u].x, v[hp][u].y, v[hp][u].z, v[hp][u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc[u] = fmaf(qv[2 * e], __uint_as_float(wd[e] << 16), acc[u]);
+              acc[u] = fmaf(qv[2 * e + 1], __uint_as_float(wd[e] & 0xFFFF0000u), acc[u]);
+            }
           }
         }
       }
