@@ -695,6 +695,14 @@ pkm_status pkm_forward(pkm_handle_t handle, void* stream, int64_t T, const void*
   float* sub_score = at<float>(ws, L.sub_score);
   PKM_TRY(run_query(handle, s, T, x, Wq, bn_gamma, bn_beta, saved, ws));
   PKM_TRY(run_score(handle, s, T, saved->q, C, Cp, sub_idx, sub_score, ws));
+  const pkm_config& c = handle->cfg;
+  const bool fp8 = c.value_format == PKM_VALUES_FP8;
+  if (merge_gather_supported(c.dtype, c.topk, c.d_value, fp8)) {
+    PKM_HIP(launch_merge_gather(s, c.dtype, sub_idx, sub_score, T, c.heads, c.topk, c.n_keys2, 1.0f / c.temperature,
+                                saved->idx, saved->w, V, y, c.d_value, fp8),
+            "candidate merge / softmax + value gather-sum");
+    return PKM_OK;
+  }
   PKM_TRY(run_merge(handle, s, T, sub_idx, sub_score, saved->idx, saved->w, nullptr));
   PKM_TRY(run_gather(handle, s, T, saved->idx, saved->w, V, y));
   return PKM_OK;

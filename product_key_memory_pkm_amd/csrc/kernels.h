@@ -40,6 +40,14 @@ constexpr int kBF16 = 1;
 hipError_t launch_gather(hipStream_t s, int dtype, const int32_t* idx, const float* w, const void* V,
                          void* y, int64_t ntok, int R, int d_value, bool fp8_values,
                          const void* target = nullptr, void* resid = nullptr);
+// a5 + a6 in one launch (the forward): merge_softmax's idx and w for every
+// (token, head) and launch_gather's y from them, bit-identical to the two
+// launches.  Supported when merge_gather_supported (k divides 64, rows of at
+// most 256 16-byte vectors, storage-dtype values); else hipErrorInvalidValue.
+bool merge_gather_supported(int dtype, int k, int d_value, bool fp8_values);
+hipError_t launch_merge_gather(hipStream_t s, int dtype, const int32_t* sub_idx, const float* sub_score, int64_t ntok,
+                               int heads, int k, int nk2, float inv_tau, int32_t* idx, float* w, const void* V,
+                               void* y, int d_value, bool fp8_values);
 // fp8 value rows from rows in the storage dtype (d_value % 16 == 0).
 hipError_t launch_quantize_fp8(hipStream_t s, int dtype, const void* src, int64_t rows, int d_value, void* dst);
 

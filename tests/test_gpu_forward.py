@@ -337,6 +337,32 @@ def test_forward_end_to_end(name):
         assert stats["exact_set"] > 0.999
 
 
+@pytest.mark.parametrize("name", ["bf16_mid", "ragged", "small", "tau", "k1", "int_ties"])
+def test_forward_fused_merge_gather_matches_the_stages(name):
+    """pkm_forward merges and gathers in one launch where k divides 64 (else in two): its idx, w and y
+    must equal, bit for bit, the merge and gather stage launches run on the same scoring output."""
+    from product_key_memory_pkm_amd import pkm_stage_gather, pkm_stage_merge_softmax, pkm_stage_score_topk
+    cfg = FWD_CASES[name]
+    note(f"fused merge + gather vs stages {name}")
+    inp = pi.make_inputs(cfg)
+    _, (layer, dev, saved, y) = run_gpu_forward(cfg, inp)
+    T, h, k = cfg.T, cfg.heads, cfg.topk
+    ws = layer.workspace(T, False)
+    si = torch.empty((T, h, 2, k), dtype=torch.int32, device="cuda")
+    ss = torch.empty((T, h, 2, k), dtype=torch.float32, device="cuda")
+    pkm_stage_score_topk(layer.handle, T, saved["q"], dev["C"], dev["Cp"], si, ss, ws)
+    idx = torch.empty((T, h, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, h, k), dtype=torch.float32, device="cuda")
+    pkm_stage_merge_softmax(layer.handle, T, si, ss, idx, w)
+    y2 = torch.empty_like(y)
+    pkm_stage_gather(layer.handle, T, idx, w, dev["V"], y2)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, saved["idx"])
+    assert torch.equal(w.view(torch.int32), saved["w"].view(torch.int32))
+    assert torch.equal(y2.view(torch.int16) if y2.dtype == torch.bfloat16 else y2.view(torch.int32),
+                       y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32))
+
+
 def test_forward_is_deterministic():
     cfg = FWD_CASES["bf16_mid"]
     note("forward determinism")
