@@ -15,8 +15,8 @@ OUT = os.path.join(PKG, "libpkm.so")
 PROBE_OUT = os.path.join(PKG, "libpkm_probe.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.hip", "gather.hip", "score_topk.hip", "score_select.hip", "merge_softmax.hip", "gemm.hip", "bn.hip",
-           "sort.hip", "value_grad.hip", "subkey_grad.hip", "diagnostics.hip"]
+SOURCES = ["api.hip", "gather.hip", "score_topk.hip", "score_select.hip", "merge_softmax.hip", "merge_gather.hip",
+           "gemm.hip", "bn.hip", "sort.hip", "value_grad.hip", "subkey_grad.hip", "diagnostics.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
