@@ -64,6 +64,8 @@ def parse():
                     help="only run a plain device copy of known size (for HBM counter calibration)")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="run this many steps and nothing else (for profilers)")
+    ap.add_argument("--profile-stages", type=int, default=0,
+                    help="run every stage entry point this many times alone, the GPU drained in between (for profilers)")
     ap.add_argument("--profile-diag", action="store_true",
                     help="after one step, five launches of the diagnostics on its selection and nothing else")
     ap.add_argument("--profile-adam", action="store_true",
@@ -340,6 +342,43 @@ def main():
         pkm_stage_value_adam_grouped(m.handle, T, saved["w"], dY, V, adam_m, adam_v, hp, dw, nt, ws)
         torch.cuda.synchronize()
         print(json.dumps({"profile_adam": 1, "touched_rows": int(nt.item())}), flush=True)
+        return
+    if args.profile_stages:
+        # every step of the path alone through its stage entry point, K launches each with the GPU
+        # drained in between, so a kernel trace shows each kernel without the backward's second stream
+        ws = m.workspace(T, True)
+        N = T * cfg.heads * cfg.topk
+        touched = torch.empty(N, dtype=torch.int32, device="cuda")
+        nt = torch.zeros(1, dtype=torch.int64, device="cuda")
+        dw = torch.empty(N, dtype=torch.float32, device="cuda")
+        F = cfg.heads * cfg.dq
+        dq = torch.empty((T, F), dtype=torch.float32, device="cuda")
+        sdC = torch.empty((cfg.heads, cfg.n_keys, cfg.dq // 2), dtype=torch.float32, device="cuda")
+        sdCp = torch.empty((cfg.heads, cfg.n_keys2, cfg.dq // 2), dtype=torch.float32, device="cuda")
+        sdWq = torch.empty((F, cfg.d), dtype=torch.float32, device="cuda")
+        sdg = torch.empty(F, dtype=torch.float32, device="cuda") if cfg.bn else None
+        sdb = torch.empty(F, dtype=torch.float32, device="cuda") if cfg.bn else None
+        sdx = torch.empty((T, cfg.d), dtype=m.storage, device="cuda")
+        sub_idx = torch.empty((T, cfg.heads, 2, cfg.topk), dtype=torch.int32, device="cuda")
+        sub_score = torch.empty((T, cfg.heads, 2, cfg.topk), dtype=torch.float32, device="cuda")
+        dV = torch.zeros((cfg.slots, cfg.d_value), dtype=torch.float32, device="cuda")
+        y_s = torch.empty((T, cfg.d_value), dtype=m.storage, device="cuda")
+        stages = [
+            lambda: pkm_stage_query(m.handle, T, x, Wq, gamma, beta, saved, ws),
+            lambda: pkm_stage_score_topk(m.handle, T, saved["q"], C, Cp, sub_idx, sub_score, ws),
+            lambda: pkm_stage_merge_softmax(m.handle, T, sub_idx, sub_score, saved["idx"], saved["w"]),
+            lambda: pkm_stage_gather(m.handle, T, saved["idx"], saved["w"], V, y_s),
+            lambda: pkm_stage_row_groups(m.handle, T, saved["idx"], touched, nt, ws),
+            lambda: pkm_stage_value_grad_grouped(m.handle, T, saved["w"], dY, V, dV, dw, nt, ws),
+            lambda: pkm_stage_subkey_grad(m.handle, T, saved["idx"], saved["w"], dw, saved["q"], C, Cp, dq, sdC,
+                                          sdCp, ws),
+            lambda: pkm_stage_query_grad(m.handle, T, dq, x, Wq, gamma, saved, sdWq, sdg, sdb, sdx, ws),
+        ]
+        for fn in stages:
+            for _ in range(args.profile_stages):
+                fn()
+                torch.cuda.synchronize()
+        print(json.dumps({"profile_stages": args.profile_stages}), flush=True)
         return
     if args.profile_steps:
         for _ in range(args.profile_steps):
