@@ -47,6 +47,11 @@ VG_CASES = [
     (256, 2, 16, 32, 64, "f32", 1.2, True),        # 8192 lookups, skewed: long runs
     (257, 2, 16, 32, 64, "f32", 1.2, True),        # 8224 lookups
     (1000, 2, 4, 4, 32, "bf16", 0.0, False),       # 8000 lookups over 16 rows: every row split in chunks
+    # the radix passes' block shapes: 4-wave blocks with two sub-tiles each (1.5 M lookups), the ragged
+    # tail of a skewed 1.2 M, and 16-wave blocks with two sub-tiles each (5.2 M lookups)
+    (12000, 4, 32, 1024, 16, "f32", 0.0, True),
+    (12345, 3, 32, 1024, 8, "f32", 0.9, False),
+    (40960, 4, 32, 1024, 8, "f32", 0.0, True),
 ]
 
 
