@@ -135,6 +135,90 @@ def adam_no_bias_correction(V_rows, m_rows, v_rows, g, lr, beta1, beta2, eps, st
     return O.round_to_storage(V1, v_dtype), m1, v1
 
 
+def e4m3_decode_subnormal_step(codes):
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -7, (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode_ties_away(x):
+    finite = np.array([c for c in range(256) if not np.isnan(O.e4m3_decode(np.array([c]))[0])], dtype=np.int64)
+    vals = O.e4m3_decode(finite)
+    pos = finite[(vals >= 0) & ~((vals == 0) & (finite == 0x80))]
+    pv = O.e4m3_decode(pos)
+    order = np.argsort(pv)
+    pos, pv = pos[order], pv[order]
+    a = np.minimum(np.abs(np.asarray(x, dtype=np.float64)), O.E4M3_MAX)
+    i = np.clip(np.searchsorted(pv, a), 1, len(pv) - 1)
+    take_hi = (pv[i] - a) <= (a - pv[i - 1])                         # a tie goes up, not to the even code
+    code = np.where(a == 0, 0, np.where(take_hi, pos[i], pos[i - 1]))
+    neg = np.signbit(np.asarray(x, dtype=np.float64)) & (code != 0)
+    return (code | np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+def quantize_rows_fp8_fnuz_max(V, v_dtype):
+    # the row maximum mapped to 240 (the largest value of the other e4m3 variant) instead of 448
+    Vf = O.decode(V, v_dtype).astype(np.float32)
+    mx = np.abs(Vf).max(axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        scale = np.where(mx > 0, mx / np.float32(240), np.float32(0)).astype(np.float32)
+        inv = np.where(mx > 0, np.float32(240) / mx, np.float32(0)).astype(np.float32)
+    return scale, O.e4m3_encode((Vf * inv[:, None]).astype(np.float32))
+
+
+def idw_scores_squared_distance(q1, q2, C, Cp):
+    def idw(qh, K):
+        d2 = ((qh[:, :, None, :] - K[None, :, :, :]) ** 2).sum(-1)
+        return -np.log(np.maximum(d2, O.IDW_FLOOR))
+    return idw(q1, C), idw(q2, Cp)
+
+
+def idw_scores_plus_log(q1, q2, C, Cp):
+    s1, s2 = _real_idw(q1, q2, C, Cp)
+    return -s1, -s2
+
+
+_real_idw = O.subkey_scores_idw
+_real_fwpkm = O.fwpkm_chunk
+
+
+def fwpkm_chunk_ascent(cfg, q, C, Cp, V, target, lr, dense=True):
+    return _real_fwpkm(cfg, q, C, Cp, V, target, -lr, dense)
+
+
+def fwpkm_chunk_read_after_write(cfg, q, C, Cp, V, target, lr, dense=True):
+    y, Vn, sel = _real_fwpkm(cfg, q, C, Cp, V, target, lr, True)
+    y = O.round_to_storage(O.gather_sum(sel["rows"], sel["w"], Vn, O.F64), cfg.dtype)
+    return y, Vn, sel
+
+
+_real_diagnostics = O.diagnostics
+
+
+def diagnostics_entropy_log2(rows, w, n_keys, n_keys2):
+    hc, hcp, used, ent = _real_diagnostics(rows, w, n_keys, n_keys2)
+    return hc, hcp, used, ent / np.log(2.0)
+
+
+def diagnostics_first_index_by_n_keys(rows, w, n_keys, n_keys2):
+    hc, hcp, used, ent = _real_diagnostics(rows, w, n_keys, n_keys2)
+    for hh in range(rows.shape[1]):
+        r = rows[:, hh, :].reshape(-1).astype(np.int64)
+        hc[hh] = np.bincount(np.minimum(r // n_keys, n_keys - 1), minlength=n_keys)[:n_keys]
+    return hc, hcp, used, ent
+
+
+_real_weight_grad = O.weight_grad
+
+
+def weight_grad_tokens_reversed(rows, dY, V, dtype, chunk=256):
+    return _real_weight_grad(rows, dY[::-1], V, dtype, chunk)
+
+
 # ---------------------------------------------------------------------------
 # the pins each mistake must trip (functions of tests/test_oracle_pins.py)
 # ---------------------------------------------------------------------------
@@ -153,6 +237,12 @@ def _selection_pins():
 def _k1_pins():
     for seed in range(40):
         pins.test_top_k_plus_one_list_is_exact(seed)
+
+
+def _idw_pins():
+    pins.test_idw_scores_closed_forms()
+    for seed in range(3):
+        pins.test_idw_product_key_selection_is_exact_topk(seed)
 
 
 def _bf16_pins():
@@ -183,6 +273,24 @@ MUTATIONS = {
     "dC from the second half's query": ("subkey_backward", subkey_backward_dC_from_q2, [_fd_all]),
     "Adam: no bias correction": ("sparse_adam_rows", adam_no_bias_correction,
                                  [pins.test_sparse_adam_all_rows_touched_matches_dense_adam]),
+    "e4m3 decode: subnormal step": ("e4m3_decode", e4m3_decode_subnormal_step,
+                                    [pins.test_e4m3_decode_matches_torch_float8_on_every_code]),
+    "e4m3 encode: ties away from zero": ("e4m3_encode", e4m3_encode_ties_away,
+                                         [pins.test_e4m3_encode_matches_torch_cast_including_ties]),
+    "fp8 rows: maximum 240": ("quantize_rows_fp8", quantize_rows_fp8_fnuz_max,
+                              [pins.test_quantize_rows_fp8_closed_forms_and_error_bound]),
+    "IDW: log of the squared distance": ("subkey_scores_idw", idw_scores_squared_distance,
+                                         [pins.test_idw_scores_closed_forms]),
+    "IDW: sign": ("subkey_scores_idw", idw_scores_plus_log, [_idw_pins]),
+    "FwPKM write: ascent": ("fwpkm_chunk", fwpkm_chunk_ascent,
+                            [pins.test_fwpkm_chunk_write_is_the_gradient_step_of_the_reconstruction_loss]),
+    "FwPKM: read after the write": ("fwpkm_chunk", fwpkm_chunk_read_after_write,
+                                    [pins.test_fwpkm_chunk_write_is_the_gradient_step_of_the_reconstruction_loss]),
+    "entropy in bits": ("diagnostics", diagnostics_entropy_log2,
+                        [pins.test_diagnostics_against_python_loops, pins.test_diagnostics_entropy_closed_forms]),
+    "hits of C: row // |C|": ("diagnostics", diagnostics_first_index_by_n_keys,
+                              [pins.test_diagnostics_against_python_loops]),
+    "dw: tokens reversed": ("weight_grad", weight_grad_tokens_reversed, [_fd_all]),
 }
 
 
