@@ -33,7 +33,9 @@ rounded to the nearest bf16 (the value the scores are computed from) and the
 rounding is passed straight through in the backward.
 
 Beyond the lookup, ``sparse_adam_rows`` is the optimizer step on the touched
-value rows that [Blog] §6.3 describes (moments only for rows with gradient),
+value rows that [Blog] §6.3 describes (moments only for rows with gradient;
+``adam_rows_state_step`` keeps them in a pool of slots handed out on a row's
+first gradient),
 ``diagnostics`` the monitoring signals of [Blog] §9.3 and §11.2, and
 ``quantize_rows_fp8`` / ``e4m3_*`` the fp8 value storage of [Blog] §16.3,
 ``subkey_scores_idw`` and ``fwpkm_chunk`` the fast-weight memorization of the
@@ -340,6 +342,47 @@ def sparse_adam_rows(V_rows: np.ndarray, m_rows: np.ndarray, v_rows: np.ndarray,
     v_hat = v1 / (1.0 - beta2 ** step)
     V1 = decode(V_rows, v_dtype) - lr * m_hat / (np.sqrt(v_hat) + eps)
     return round_to_storage(V1, v_dtype), m1, v1
+
+
+def adam_rows_state_step(touched: np.ndarray, slot: np.ndarray, M: np.ndarray, Vm: np.ndarray, n_used: int,
+                         capacity: int, V_rows: np.ndarray, g: np.ndarray, lr: float, beta1: float, beta2: float,
+                         eps: float, step: int, v_dtype: str):
+    """``sparse_adam_rows`` with the moments held only for rows that have received gradient.
+
+    ([Blog] §6.3: optimizer state is allocated only for the parameters that got
+    gradient.)  Readings: the state is a slot map ``slot`` [n_rows] (-1: the row
+    has no moments yet) and a pool of ``capacity`` moment rows ``M``, ``Vm``
+    [capacity, d]; ``n_used`` slots are handed out.  The rows of ``touched``
+    (ascending, this step's rows with gradient) that have no slot take the
+    next slots in ascending row order: the i-th of them (from 0) gets slot
+    n_used + i.  One whose slot would be capacity or more keeps -1 and is not
+    stepped (its value and state unchanged); ``n_used`` still counts it, so a
+    result above ``capacity`` reports the shortfall.  A row's first step starts
+    from zero moments, so every stepped row follows ``sparse_adam_rows``.
+    ``V_rows``, ``g``: [U, d] the touched rows' stored values and gradients.
+    Returns (value rows [U, d] after the step, float64 storage values; slot map;
+    M; Vm; n_used; stepped [U] bool).
+    """
+    touched = np.asarray(touched, dtype=np.int64)
+    slot = np.array(slot, dtype=np.int64)
+    M = np.array(M, dtype=np.float64)
+    Vm = np.array(Vm, dtype=np.float64)
+    new = slot[touched] == -1
+    s_new = n_used + np.cumsum(new) - 1              # slot of each new row, in row order
+    granted = new & (s_new < capacity)
+    slot[touched[granted]] = s_new[granted]
+    stepped = ~new | granted
+    out = decode(V_rows, v_dtype).copy()
+    s = slot[touched[stepped]]
+    fresh = new[stepped][:, None]
+    m0 = np.where(fresh, 0.0, M[s])
+    v0 = np.where(fresh, 0.0, Vm[s])
+    V1, m1, v1 = sparse_adam_rows(np.asarray(V_rows)[stepped], m0, v0, np.asarray(g)[stepped], lr, beta1, beta2,
+                                  eps, step, v_dtype)
+    out[stepped] = V1
+    M[s] = m1
+    Vm[s] = v1
+    return out, slot, M, Vm, int(n_used + new.sum()), stepped
 
 
 # ---------------------------------------------------------------------------

@@ -219,6 +219,48 @@ def weight_grad_tokens_reversed(rows, dY, V, dtype, chunk=256):
     return _real_weight_grad(rows, dY[::-1], V, dtype, chunk)
 
 
+
+_real_adam_rows = O.adam_rows_state_step
+
+
+def _adam_rows_variant(touched, slot, M, Vm, n_used, capacity, V_rows, g, lr, beta1, beta2, eps, step, v_dtype,
+                       descending=False, fresh_from_pool=False, count_granted_only=False):
+    touched = np.asarray(touched, dtype=np.int64)
+    slot = np.array(slot, dtype=np.int64)
+    M = np.array(M, dtype=np.float64)
+    Vm = np.array(Vm, dtype=np.float64)
+    new = slot[touched] == -1
+    rank = np.cumsum(new) - 1
+    if descending:
+        rank = new.sum() - 1 - rank
+    s_new = n_used + rank
+    granted = new & (s_new < capacity)
+    slot[touched[granted]] = s_new[granted]
+    stepped = ~new | granted
+    out = O.decode(V_rows, v_dtype).copy()
+    s = slot[touched[stepped]]
+    fresh = np.zeros_like(new[stepped]) if fresh_from_pool else new[stepped]
+    m0 = np.where(fresh[:, None], 0.0, M[s])
+    v0 = np.where(fresh[:, None], 0.0, Vm[s])
+    V1, m1, v1 = O.sparse_adam_rows(np.asarray(V_rows)[stepped], m0, v0, np.asarray(g)[stepped], lr, beta1, beta2,
+                                    eps, step, v_dtype)
+    out[stepped] = V1
+    M[s] = m1
+    Vm[s] = v1
+    return out, slot, M, Vm, int(n_used + (granted.sum() if count_granted_only else new.sum())), stepped
+
+
+def adam_rows_descending(*a):
+    return _adam_rows_variant(*a, descending=True)
+
+
+def adam_rows_fresh_from_pool(*a):
+    return _adam_rows_variant(*a, fresh_from_pool=True)
+
+
+def adam_rows_count_granted_only(*a):
+    return _adam_rows_variant(*a, count_granted_only=True)
+
 # ---------------------------------------------------------------------------
 # the pins each mistake must trip (functions of tests/test_oracle_pins.py)
 # ---------------------------------------------------------------------------
@@ -291,6 +333,12 @@ MUTATIONS = {
     "hits of C: row // |C|": ("diagnostics", diagnostics_first_index_by_n_keys,
                               [pins.test_diagnostics_against_python_loops]),
     "dw: tokens reversed": ("weight_grad", weight_grad_tokens_reversed, [_fd_all]),
+    "row state: slots in descending row order": ("adam_rows_state_step", adam_rows_descending,
+                                                 [pins.test_adam_rows_state_slot_rule_worked_example]),
+    "row state: a fresh row reads the pool": ("adam_rows_state_step", adam_rows_fresh_from_pool,
+                                              [pins.test_adam_rows_state_matches_torch_sparse_adam]),
+    "row state: refused rows not counted": ("adam_rows_state_step", adam_rows_count_granted_only,
+                                            [pins.test_adam_rows_state_slot_rule_worked_example]),
 }
 
 

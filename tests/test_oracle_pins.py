@@ -505,6 +505,65 @@ def test_sparse_adam_first_step_closed_form_and_bf16_rounding():
     np.testing.assert_array_equal(Vb1, want)
 
 
+
+def _adam_rows_iterate(V0, steps, lr, b1, b2, eps, capacity, pool_fill=7.0):
+    # the pool starts with stale values: a row's first step must not read them
+    n_rows, d = V0.shape
+    V = V0.copy()
+    slot = -np.ones(n_rows, dtype=np.int64)
+    M = np.full((capacity, d), pool_fill)
+    Vm = np.full((capacity, d), pool_fill)
+    n_used, stepped_all = 0, []
+    for t, (rows, g) in enumerate(steps, 1):
+        out, slot, M, Vm, n_used, stepped = O.adam_rows_state_step(rows, slot, M, Vm, n_used, capacity, V[rows], g,
+                                                                   lr, b1, b2, eps, t, O.F64)
+        V[rows] = out
+        stepped_all.append(stepped)
+    return V, slot, M, Vm, n_used, stepped_all
+
+
+def test_adam_rows_state_matches_torch_sparse_adam():
+    # moments held in slots handed out on a row's first gradient: the same
+    # trajectory as torch's SparseAdam (dense state), whatever the pool held
+    rng = np.random.default_rng(16)
+    n_rows, d = 40, 3
+    V0 = rng.standard_normal((n_rows, d))
+    steps = []
+    for n in range(6):
+        rows = np.sort(rng.choice(n_rows, size=rng.integers(1, 25), replace=False))
+        steps.append((rows, rng.standard_normal((rows.size, d))))
+    lr, b1, b2 = 3e-2, 0.8, 0.95
+    V, slot, M, Vm, n_used, _ = _adam_rows_iterate(V0, steps, lr, b1, b2, 1e-30, capacity=n_rows)
+    p = torch.nn.Parameter(torch.tensor(V0))
+    opt = torch.optim.SparseAdam([p], lr=lr, betas=(b1, b2), eps=1e-30)
+    for rows, g in steps:
+        p.grad = torch.sparse_coo_tensor(torch.tensor(rows)[None], torch.tensor(g), (n_rows, d))
+        opt.step()
+    st = opt.state[p]
+    np.testing.assert_allclose(V, p.detach().numpy(), rtol=1e-12, atol=1e-14)
+    seen = np.unique(np.concatenate([r for r, _ in steps]))
+    assert n_used == seen.size and sorted(slot[seen]) == list(range(seen.size))
+    assert (slot[np.setdiff1d(np.arange(n_rows), seen)] == -1).all()
+    np.testing.assert_allclose(M[slot[seen]], st["exp_avg"].to_dense().numpy()[seen], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(Vm[slot[seen]], st["exp_avg_sq"].to_dense().numpy()[seen], rtol=1e-12, atol=1e-14)
+
+
+def test_adam_rows_state_slot_rule_worked_example():
+    # 10 rows, a pool of 4 slots; slots go to new rows in ascending row order,
+    # a row that finds the pool full keeps no state and is not stepped
+    V0 = np.arange(20, dtype=np.float64).reshape(10, 2)
+    steps = [(np.array([2, 5, 7]), np.ones((3, 2))),
+             (np.array([1, 5, 9]), np.ones((3, 2))),
+             (np.array([0, 9]), np.ones((2, 2)))]
+    V, slot, _, _, n_used, stepped = _adam_rows_iterate(V0, steps, 0.1, 0.9, 0.999, 1e-8, capacity=4)
+    assert list(slot) == [-1, 3, 0, -1, -1, 1, -1, 2, -1, -1]
+    assert n_used == 7                     # 3 + 2 + 2 rows asked for a slot, 2 of them in vain
+    assert [list(x) for x in stepped] == [[True, True, True], [True, True, False], [False, False]]
+    np.testing.assert_array_equal(V[[0, 3, 4, 6, 8, 9]], V0[[0, 3, 4, 6, 8, 9]])
+    # a first step from zero moments moves each element by lr * g / (|g| + eps)
+    np.testing.assert_allclose(V[[2, 7]], V0[[2, 7]] - 0.1 / (1 + 1e-8), rtol=1e-15)
+
+
 # ---------------------------------------------------------------------------
 # Monitoring signals ([Blog] §9.3, §11.2; [PKM-summary] key results)
 # ---------------------------------------------------------------------------
