@@ -32,8 +32,8 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 # holds for the kernel sources whose combined sha256 prefix is given; any change to them voids it (traffic null).
 KERNEL_TRAFFIC = {
     ("gather", "paper"): {"bytes": 13552071360, "sources": ["gather.hip", "common.h"], "sources_sha256_16": "993549f60bba5340"},
-    ("value_grad", "paper"): {"bytes": 29814557696, "sources": ["value_grad.hip", "sparse_common.h", "common.h"], "sources_sha256_16": "45318c5f87a811fc"},
-    ("value_adam", "paper"): {"bytes": 46952124416, "sources": ["value_grad.hip", "sparse_common.h", "common.h"], "sources_sha256_16": "45318c5f87a811fc"},
+    ("value_grad", "paper"): {"bytes": 29789221888, "sources": ["value_grad.hip", "sparse_common.h", "common.h"], "sources_sha256_16": "c71e5fb32d3e118e"},
+    ("value_adam", "paper"): {"bytes": 47242236928, "sources": ["value_grad.hip", "sparse_common.h", "common.h"], "sources_sha256_16": "c71e5fb32d3e118e"},
 }
 
 
@@ -194,7 +194,8 @@ def main():
                                             pkm_fwpkm_chunks,
                                             pkm_quantize_values, pkm_stage_gather, pkm_stage_merge_softmax,
                                             pkm_stage_query, pkm_stage_query_grad, pkm_stage_subkey_grad,
-                                            pkm_stage_row_groups, pkm_stage_score_topk, pkm_stage_value_adam_grouped,
+                                            pkm_stage_row_groups, pkm_stage_score_topk, pkm_stage_value_adam,
+                                            pkm_stage_value_adam_grouped, pkm_stage_value_adam_rows,
                                             pkm_stage_value_grad_grouped)
 
     if args.copy_calibration:
@@ -443,7 +444,21 @@ def main():
     hp = {"lr": 1e-3, "beta1": 0.9, "beta2": 0.999, "eps": 1e-8, "step": 1}
     va_ms = timed(lambda: pkm_stage_value_adam_grouped(m.handle, T, saved["w"], dY, V_opt, adam_m, adam_v, hp, dw, nt,
                                                        ws), nf)
-    del V_opt, adam_m, adam_v
+    # the whole stage (grouping + kernel) with dense moments, and with the moments in a pool of slots handed
+    # out on a row's first gradient (grouping, slot hand-out, kernel); the pool holds the touched rows, and
+    # after the untimed first call every row has its slot
+    touched_a = torch.empty(T * cfg.heads * cfg.topk, dtype=torch.int32, device="cuda")
+    va_stage_ms = timed(lambda: pkm_stage_value_adam(m.handle, T, saved["idx"], saved["w"], dY, V_opt, adam_m, adam_v,
+                                                     hp, touched_a, nt, dw, ws), nf)
+    del adam_m, adam_v
+    torch.cuda.empty_cache()
+    pool = m.adam_row_state(n_touched)
+    var_stage_ms = timed(lambda: pkm_stage_value_adam_rows(m.handle, T, saved["idx"], saved["w"], dY, V_opt, pool, hp,
+                                                           touched_a, nt, dw, ws), nf)
+    adam_rows = {"stage_ms_dense_moments": va_stage_ms, "stage_ms_row_slots": var_stage_ms,
+                 "pool_rows": int(pool["n_used"].item()), "pool_bytes": 2 * n_touched * cfg.d_value * 4,
+                 "dense_moment_bytes": 2 * cfg.slots * cfg.d_value * 4}
+    del V_opt, pool, touched_a
     torch.cuda.empty_cache()
     # monitoring signals of the step's selection
     hits_c = torch.empty((cfg.heads, cfg.n_keys), dtype=torch.int32, device="cuda")
@@ -629,7 +644,7 @@ def main():
     dom = max(kern, key=lambda n: kern[n]["ms"])
     # not a step of the lookup itself: the optimizer step fused into a8 (reported beside it)
     kern["value_adam"] = {"kernel": "value_grad with the Adam step of the touched value rows (a7 dw + a8 + optimizer)",
-                          "ms": va_ms, "alg": ab["value_adam"]}
+                          "ms": va_ms, "alg": ab["value_adam"], "row_slot_state": adam_rows}
     kern["diagnostics"] = {"kernel": "diagnostics (hit counts, slots in use, softmax entropy)", "ms": dg_ms,
                            "alg": ab["diagnostics"]}
     kern["gather_fp8"] = {"kernel": "gather_sum over fp8 value rows (a6, value_format fp8)", "ms": g8_ms,
@@ -642,6 +657,8 @@ def main():
         r = {"kernel": k_["kernel"], "bound": "hbm", "achieved": k_["achieved"], "peak": HBM_PEAK_GBS,
              "unit": "GB/s", "frac": k_["achieved"] / HBM_PEAK_GBS, "traffic": measured_traffic(name, args.workload),
              "alg_bytes_per_launch": k_["alg"], "avg_launch_ms": k_["ms"]}
+        if "row_slot_state" in k_:
+            r["row_slot_state"] = k_["row_slot_state"]
         if peaks:
             r["frac_of_measured_peak"] = k_["achieved"] / peaks["hbm_read_GBs"]
         return r

@@ -149,6 +149,33 @@ typedef struct {
   int64_t step; /* 1-based global count of optimizer steps, this one included (bias correction) */
 } pkm_adam;
 
+/* Adam moments kept only for the rows that have received gradient
+ * ("Meta AI 可扩展内存层", section 6.3: optimizer state allocated only for the
+ * parameters that got gradient), for pkm_backward_adam_rows and
+ * pkm_stage_value_adam_rows.  All pointers are caller-allocated device memory.
+ *   slot [|C|*|C'|] int32: -1 for a row without moments, else the row of m and
+ *     v holding its moments.  Set to -1 everywhere before the first step; the
+ *     library writes it (between calls every entry is -1 or a slot below
+ *     capacity; a call writes other values transiently).
+ *   m, v [capacity, d_value] fp32: the pool; need not be initialised (a row's
+ *     first step starts from zero moments and does not read its slot).
+ *   n_used [1] int64 (8-byte aligned): slots handed out so far; 0 before the
+ *     first step.  A call gives the touched rows without a slot, in ascending
+ *     row order, the slots n_used, n_used + 1, ...; a row whose slot would be
+ *     capacity or more keeps -1 and is not stepped (its V row and the pool are
+ *     unchanged), yet n_used counts it: n_used > capacity after a call means
+ *     that many rows asked in vain, and the caller should grow the pool.
+ *   capacity: rows of m and v, 0 <= capacity <= |C|*|C'| (checked).
+ * Entries of slot outside [-1, capacity) are never used as pool rows (such a
+ * row is not stepped). */
+typedef struct {
+  int32_t* slot;
+  float* m;
+  float* v;
+  int64_t* n_used;
+  int64_t capacity;
+} pkm_adam_rows;
+
 /* Validate cfg and build a handle.  Besides host state, the handle owns one
  * HIP stream (default priority, non-blocking) and two events created on the
  * device current at this call; pkm_backward uses them to run the sub-key
@@ -226,6 +253,17 @@ pkm_status pkm_backward_adam(pkm_handle_t handle, void* stream, int64_t T, const
                              const pkm_saved* saved, float* adam_m, float* adam_v, const pkm_adam* adam,
                              int32_t* touched, int64_t* n_touched, float* dC, float* dCp, float* dWq,
                              float* dgamma, float* dbeta, void* dx, void* ws, size_t ws_bytes);
+
+/* pkm_backward_adam with the moments in the pool of `state` (pkm_adam_rows)
+ * instead of dense tables: the same step for every touched row that has or
+ * gets a slot; a touched row refused a slot (pool full) is not stepped.  Other
+ * arguments, outputs and the workspace as in pkm_backward_adam.  Calls that
+ * share a state must be ordered (one stream, or synchronised). */
+pkm_status pkm_backward_adam_rows(pkm_handle_t handle, void* stream, int64_t T, const void* dY, const void* x,
+                                  const void* Wq, const float* bn_gamma, const void* C, const void* Cp, void* V,
+                                  const pkm_saved* saved, const pkm_adam_rows* state, const pkm_adam* adam,
+                                  int32_t* touched, int64_t* n_touched, float* dC, float* dCp, float* dWq,
+                                  float* dgamma, float* dbeta, void* dx, void* ws, size_t ws_bytes);
 
 const char* pkm_status_string(pkm_status s);
 /* Message of the last failed call on this thread ("" if none). */
@@ -329,6 +367,15 @@ pkm_status pkm_stage_value_adam_grouped(pkm_handle_t handle, void* stream, int64
                                         const void* dY, void* V, float* adam_m, float* adam_v,
                                         const pkm_adam* adam, float* dw, const int64_t* n_touched, void* ws,
                                         size_t ws_bytes);
+
+/* pkm_stage_value_adam with the moments in the pool of `state` (as in
+ * pkm_backward_adam_rows): the grouping, the slot hand-out for the touched
+ * rows without one, then the value-gradient kernel with the Adam step.
+ * ws >= pkm_workspace_size(handle, T, 1). */
+pkm_status pkm_stage_value_adam_rows(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx,
+                                     const float* w, const void* dY, void* V, const pkm_adam_rows* state,
+                                     const pkm_adam* adam, int32_t* touched, int64_t* n_touched, float* dw,
+                                     void* ws, size_t ws_bytes);
 
 /* Steps a7 (softmax backward) and a9: ds = w (dw - sum_s w dw) / tau; then
  * dq[t, h*dq] fp32 (both halves of each head) and dC, dCp (overwritten) through

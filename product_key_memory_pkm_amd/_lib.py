@@ -49,6 +49,11 @@ class pkm_adam(ctypes.Structure):
                 ("eps", ctypes.c_float), ("step", ctypes.c_int64)]
 
 
+class pkm_adam_rows(ctypes.Structure):
+    _fields_ = [("slot", ctypes.c_void_p), ("m", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("n_used", ctypes.c_void_p), ("capacity", ctypes.c_int64)]
+
+
 _lib = None
 
 # name -> argument types (all return pkm_status as int)
@@ -64,6 +69,9 @@ _SIGS = {
                      _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
     "pkm_backward_adam": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_saved), _VP, _VP,
                           ctypes.POINTER(pkm_adam), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
+    "pkm_backward_adam_rows": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_saved),
+                               ctypes.POINTER(pkm_adam_rows), ctypes.POINTER(pkm_adam), _VP, _VP, _VP, _VP, _VP, _VP,
+                               _VP, _VP, _VP, _SZ],
     "pkm_stage_query": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_saved), _VP, _SZ],
     "pkm_stage_score_topk": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
     "pkm_stage_merge_softmax": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP],
@@ -73,6 +81,8 @@ _SIGS = {
                              _VP, _SZ],
     "pkm_stage_value_adam_grouped": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_adam), _VP, _VP,
                                      _VP, _SZ],
+    "pkm_stage_value_adam_rows": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, ctypes.POINTER(pkm_adam_rows),
+                                  ctypes.POINTER(pkm_adam), _VP, _VP, _VP, _VP, _SZ],
     "pkm_diagnostics": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ],
     "pkm_quantize_values": [_VP, _VP, _VP, _I64, _VP],
     "pkm_stage_row_groups": [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _SZ],
@@ -332,6 +342,51 @@ def pkm_stage_value_adam(h, T, idx, w, dY, V, adam_m, adam_v, adam: dict, touche
     _check(_invoke("pkm_stage_value_adam", h, T, _ptr(idx), _ptr(w), _ptr(dY), _ptr(V), _ptr(adam_m), _ptr(adam_v),
                    ctypes.byref(hp), _ptr(touched), _ptr(n_touched), _ptr(dw), _ptr(ws), _nbytes(ws)),
            "pkm_stage_value_adam")
+
+
+def _adam_rows_struct(h, state: dict) -> pkm_adam_rows:
+    """state: {"slot": int32 [n_keys * n_keys2], "m", "v": fp32 [capacity, d_value], "n_used": int64 [1]};
+    the capacity is the row count of m."""
+    c = h.cfg
+    _dt(state["slot"], torch.int32, "state['slot']")
+    _dt(state["m"], torch.float32, "state['m']")
+    _dt(state["v"], torch.float32, "state['v']")
+    _dt(state["n_used"], torch.int64, "state['n_used']")
+    cap = state["m"].numel() // c.d_value
+    _need(**{"state['slot']": (state["slot"], c.n_keys * c.n_keys2), "state['v']": (state["v"], cap * c.d_value),
+             "state['n_used']": (state["n_used"], 1)})
+    return pkm_adam_rows(_ptr(state["slot"]), _ptr(state["m"]), _ptr(state["v"]), _ptr(state["n_used"]), cap)
+
+
+def pkm_backward_adam_rows(h, T, dY, x, Wq, bn_gamma, C, Cp, V, saved: dict, state: dict, adam: dict, touched,
+                           n_touched, dC, dCp, dWq, dgamma, dbeta, dx, ws):
+    """pkm_backward_adam with the moments in a pool of slots (``state``, see _adam_rows_struct)."""
+    st = h.storage
+    for n, t in (("dY", dY), ("x", x), ("Wq", Wq), ("C", C), ("Cp", Cp), ("V", V), ("dx", dx)):
+        _dt(t, st, n)
+    _dt(n_touched, torch.int64, "n_touched")
+    _need_bwd(h, T, dY, x, Wq, bn_gamma, C, Cp, V, saved, touched, n_touched, dC, dCp, dWq, dgamma, dbeta, dx)
+    sv = _saved_struct(saved)
+    rs = _adam_rows_struct(h, state)
+    hp = _adam_struct(adam)
+    _check(_invoke("pkm_backward_adam_rows", h, T, _ptr(dY), _ptr(x), _ptr(Wq), _ptr(bn_gamma), _ptr(C), _ptr(Cp),
+                   _ptr(V), ctypes.byref(sv), ctypes.byref(rs), ctypes.byref(hp), _ptr(touched), _ptr(n_touched),
+                   _ptr(dC), _ptr(dCp), _ptr(dWq), _ptr(dgamma), _ptr(dbeta), _ptr(dx), _ptr(ws), _nbytes(ws)),
+           "pkm_backward_adam_rows")
+
+
+def pkm_stage_value_adam_rows(h, T, idx, w, dY, V, state: dict, adam: dict, touched, n_touched, dw, ws):
+    _dt(idx, torch.int32, "idx")
+    _dt(w, torch.float32, "w")
+    _dt(dw, torch.float32, "dw")
+    n = _dims(h, T)
+    _need(idx=(idx, n["lookups"]), w=(w, n["lookups"]), dY=(dY, n["y"]), V=(V, n["dV"]),
+          touched=(touched, n["lookups"]), n_touched=(n_touched, 1), dw=(dw, n["lookups"]))
+    rs = _adam_rows_struct(h, state)
+    hp = _adam_struct(adam)
+    _check(_invoke("pkm_stage_value_adam_rows", h, T, _ptr(idx), _ptr(w), _ptr(dY), _ptr(V), ctypes.byref(rs),
+                   ctypes.byref(hp), _ptr(touched), _ptr(n_touched), _ptr(dw), _ptr(ws), _nbytes(ws)),
+           "pkm_stage_value_adam_rows")
 
 
 def pkm_stage_query(h, T, x, Wq, bn_gamma, bn_beta, saved: dict, ws):

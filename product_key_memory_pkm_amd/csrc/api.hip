@@ -77,7 +77,7 @@ struct FwdLayout {
 };
 struct BwdLayout {
   size_t k0, v0, k1, v1, sort_tmp, grp, key1, key2, seg, scan_tmp, nseg, dw, ds, coef2, dq, bn_part,
-      dqpre, dqpre_t, x_t, wq_t, split, aux, total;
+      dqpre, dqpre_t, x_t, wq_t, split, aux, rstate, total;
   int splits;
   int64_t tpad;
   // leading dimensions of the GEMM operands written here: 64 elements past a
@@ -141,6 +141,7 @@ BwdLayout bwd_layout(const pkm_handle_s* h, int64_t T) {
   L.split = o; o += al(size_t(L.splits) * h->F * c.d_in * 4);
   // long-run lists and partial sums of the value and sub-key gradients (used one after the other)
   L.aux = o; o += al(std::max(value_grad_aux_bytes(int64_t(N), c.d_value), subkey_grad_aux_bytes(int64_t(N), c.d_query)));
+  L.rstate = o; o += al(row_state_temp_bytes());  // slot hand-out of the Adam moment pool
   L.total = o;
   return L;
 }
@@ -340,6 +341,11 @@ pkm_status run_value_grad(const pkm_handle_s* h, hipStream_t s, int64_t T, const
                           const void* dY, const void* V, float* dV, int32_t* touched, int64_t* n_touched, float* dw,
                           void* ws, const VgAdam* adam = nullptr, int bits = -1, int groups = 1) {
   PKM_TRY(run_row_groups(h, s, T, idx, touched, n_touched, ws, bits, groups));
+  if (adam && adam->slot) {
+    PKM_HIP(launch_row_state_assign(s, touched, n_touched, adam->slot, adam->capacity, adam->n_used,
+                                    at<void>(ws, bwd_layout(h, T).rstate)),
+            "slot hand-out of the moment pool");
+  }
   return run_value_grad_grouped(h, s, T, w, dY, V, dV, dw, n_touched, ws, adam, bits, groups);
 }
 
@@ -362,6 +368,28 @@ pkm_status adam_args(const pkm_adam* hp, void* V, float* m, float* v, VgAdam* ou
   out->step_size = float(double(hp->lr) / bc1);
   out->inv_sqrt_bc2 = float(1.0 / std::sqrt(bc2));
   out->sgd = 0;
+  out->slot = nullptr;
+  out->capacity = 0;
+  out->n_used = nullptr;
+  return PKM_OK;
+}
+
+// adam_args with the moments in the slot pool of `st`.
+pkm_status adam_rows_args(const pkm_handle_s* h, const pkm_adam* hp, void* V, const pkm_adam_rows* st, VgAdam* out) {
+  if (st == nullptr) return fail(PKM_ERR_INVALID_ARG, "state is NULL");
+  PKM_TRY(need(st->slot, "state.slot"));
+  PKM_TRY(need(st->m, "state.m"));
+  PKM_TRY(need(st->v, "state.v"));
+  if (st->n_used == nullptr) return fail(PKM_ERR_INVALID_ARG, "state.n_used is NULL");
+  if (reinterpret_cast<uintptr_t>(st->n_used) % 8 != 0)
+    return fail(PKM_ERR_INVALID_ARG, "state.n_used must be 8-byte aligned");
+  const int64_t rows = int64_t(h->cfg.n_keys) * h->cfg.n_keys2;
+  if (st->capacity < 0 || st->capacity > rows)
+    return fail(PKM_ERR_INVALID_ARG, "state.capacity must lie in [0, n_keys * n_keys2]");
+  PKM_TRY(adam_args(hp, V, st->m, st->v, out));
+  out->slot = st->slot;
+  out->capacity = st->capacity;
+  out->n_used = st->n_used;
   return PKM_OK;
 }
 
@@ -815,6 +843,19 @@ pkm_status pkm_backward_adam(pkm_handle_t handle, void* stream, int64_t T, const
                        dCp, dWq, dgamma, dbeta, dx, ws, ws_bytes);
 }
 
+pkm_status pkm_backward_adam_rows(pkm_handle_t handle, void* stream, int64_t T, const void* dY, const void* x,
+                                  const void* Wq, const float* bn_gamma, const void* C, const void* Cp, void* V,
+                                  const pkm_saved* saved, const pkm_adam_rows* state, const pkm_adam* adam,
+                                  int32_t* touched, int64_t* n_touched, float* dC, float* dCp, float* dWq,
+                                  float* dgamma, float* dbeta, void* dx, void* ws, size_t ws_bytes) {
+  PKM_TRY(check_handle(handle));
+  PKM_TRY(need(V, "V"));
+  VgAdam ad;
+  PKM_TRY(adam_rows_args(handle, adam, V, state, &ad));
+  return backward_impl(handle, stream, T, dY, x, Wq, bn_gamma, C, Cp, V, saved, nullptr, &ad, touched, n_touched, dC,
+                       dCp, dWq, dgamma, dbeta, dx, ws, ws_bytes);
+}
+
 pkm_status pkm_stage_query(pkm_handle_t handle, void* stream, int64_t T, const void* x, const void* Wq,
                            const float* bn_gamma, const float* bn_beta, const pkm_saved* saved, void* ws,
                            size_t ws_bytes) {
@@ -905,6 +946,28 @@ pkm_status pkm_stage_value_adam(pkm_handle_t handle, void* stream, int64_t T, co
   PKM_TRY(need(adam_v, "adam_v"));
   VgAdam ad;
   PKM_TRY(adam_args(adam, V, adam_m, adam_v, &ad));
+  PKM_TRY(need(touched, "touched"));
+  if (n_touched == nullptr) return fail(PKM_ERR_INVALID_ARG, "n_touched is NULL");
+  PKM_TRY(need(dw, "dw"));
+  PKM_TRY(check_ws(handle, T, 1, ws, ws_bytes));
+  hipStream_t s = as_stream(stream);
+  if (T == 0) return zero_grads(handle, s, n_touched, nullptr, nullptr, nullptr, nullptr, nullptr);
+  return run_value_grad(handle, s, T, idx, w, dY, V, nullptr, touched, n_touched, dw, ws, &ad);
+}
+
+pkm_status pkm_stage_value_adam_rows(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx,
+                                     const float* w, const void* dY, void* V, const pkm_adam_rows* state,
+                                     const pkm_adam* adam, int32_t* touched, int64_t* n_touched, float* dw,
+                                     void* ws, size_t ws_bytes) {
+  PKM_TRY(check_handle(handle));
+  PKM_TRY(need_storage_values(handle));
+  PKM_TRY(check_T(handle, T));
+  PKM_TRY(need(idx, "idx"));
+  PKM_TRY(need(w, "w"));
+  PKM_TRY(need(dY, "dY"));
+  PKM_TRY(need(V, "V"));
+  VgAdam ad;
+  PKM_TRY(adam_rows_args(handle, adam, V, state, &ad));
   PKM_TRY(need(touched, "touched"));
   if (n_touched == nullptr) return fail(PKM_ERR_INVALID_ARG, "n_touched is NULL");
   PKM_TRY(need(dw, "dw"));

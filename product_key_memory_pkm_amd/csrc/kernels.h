@@ -198,7 +198,19 @@ struct VgAdam {
   float step_size;     // lr / (1 - beta1^step); with sgd the learning rate
   float inv_sqrt_bc2;  // 1 / sqrt(1 - beta2^step)
   int sgd;             // 1: plain step V -= step_size * g (m, v unused)
+  // moments in a pool of slots (null: m, v are dense [rows, d_value] tables):
+  // slot[r] = -1 (no moments: the row is not stepped), s (moments in pool row
+  // s), or -2 - s (slot s handed out in this call: zero moments, then s stored)
+  int32_t* slot;
+  int64_t capacity;
+  int64_t* n_used;  // slots handed out so far (device)
 };
+// Hands out pool slots to the touched rows that have none (slot[r] == -1), in
+// ascending row order from *n_used; a slot at or past capacity is refused (the
+// entry stays -1) but counted in *n_used.  tmp: row_state_temp_bytes().
+size_t row_state_temp_bytes();
+hipError_t launch_row_state_assign(hipStream_t s, const int32_t* touched, const int64_t* n_touched, int32_t* slot,
+                                   int64_t capacity, int64_t* n_used, void* tmp);
 size_t value_grad_aux_bytes(int64_t nitems, int d_value);
 hipError_t launch_value_grad(hipStream_t s, int dtype, const int32_t* seg_start, const int64_t* nseg,
                              int64_t nitems, const uint32_t* sorted_rows, const int32_t* sorted_c,

@@ -87,6 +87,8 @@ struct VgArgs {
   float step_size;     // lr / (1 - b1^t); the plain learning rate when sgd
   float inv_sqrt_bc2;  // 1 / sqrt(1 - b2^t)
   int sgd;             // plain gradient step V -= step_size * g (no moments)
+  int32_t* slot;       // moments in pool slots (VgAdam::slot); null: dense moment tables
+  int64_t capacity;
 };
 
 // The wave's lanes own 16-byte vectors l, l+64, ... of a row; the first NVL-1
@@ -247,11 +249,28 @@ __device__ __forceinline__ void vg_adam_row(const VgArgs& a, const LaneVecs<NVL>
     }
     return;
   }
-  float* mrow = a.am + size_t(r) * dv;
-  float* vrow = a.av + size_t(r) * dv;
+  size_t prow = r;
+  bool fresh = false;
+  if (a.slot) {  // wave-uniform: the row's entry of the slot map
+    const int32_t e = a.slot[r];
+    if (e == -1) return;  // refused a slot: not stepped
+    const int64_t sl = e >= 0 ? int64_t(e) : -2 - int64_t(e);
+    if (sl >= a.capacity) return;
+    prow = size_t(sl);
+    fresh = e < -1;
+  }
+  float* mrow = a.am + prow * dv;
+  float* vrow = a.av + prow * dv;
   float m0[NVL][E], v0[NVL][E];
-  vg_load_f32<T, NVL>(lv, mrow, m0);
-  vg_load_f32<T, NVL>(lv, vrow, v0);
+  if (fresh) {  // a row's first step: zero moments, the pool row is not read
+#pragma unroll
+    for (int m = 0; m < NVL; ++m)
+#pragma unroll
+      for (int e = 0; e < E; ++e) m0[m][e] = v0[m][e] = 0.f;
+  } else {
+    vg_load_f32<T, NVL>(lv, mrow, m0);
+    vg_load_f32<T, NVL>(lv, vrow, v0);
+  }
 #pragma unroll
   for (int m = 0; m < NVL; ++m) {
     if (m == NVL - 1 && !lv.last_ok) continue;
@@ -270,6 +289,7 @@ __device__ __forceinline__ void vg_adam_row(const VgArgs& a, const LaneVecs<NVL>
   }
   vg_store<T, NVL>(lv, mrow, m0, false);
   vg_store<T, NVL>(lv, vrow, v0, false);
+  if (fresh && lane_id() == 0) a.slot[r] = int32_t(prow);
 }
 
 // MODE 0: one wave per work item, a resident grid striding over the items:
@@ -356,7 +376,103 @@ __global__ __launch_bounds__(256) void value_grad_kernel(VgArgs a) {
   }
 }
 
+// Slot hand-out of the moment pool (VgAdam::slot): the touched rows (sorted,
+// distinct) are cut into kRsBlocks equal ranges; a first launch counts each
+// range's rows without a slot, a second gives them slots in row order, each
+// block starting after the new rows of the ranges before it.
+constexpr int kRsBlocks = 512;
+constexpr int kRsThreads = 256;
+constexpr int kRsWaves = kRsThreads / 64;
+
+__device__ __forceinline__ void rs_range(const int64_t* n_touched, int64_t* lo, int64_t* hi) {
+  const int64_t U = *n_touched;
+  const int64_t per = (U + kRsBlocks - 1) / kRsBlocks;
+  *lo = int64_t(blockIdx.x) * per;
+  *hi = *lo + per < U ? *lo + per : U;
+}
+
+// sum of one int per thread over the block (every thread gets it)
+__device__ __forceinline__ int rs_block_sum(int v, int* red) {
+  v = wave_sum_i(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int w = 0; w < kRsWaves; ++w) t += red[w];
+  return t;
+}
+
+__global__ __launch_bounds__(kRsThreads) void row_state_count_kernel(const int32_t* __restrict__ touched,
+                                                                     const int64_t* __restrict__ n_touched,
+                                                                     const int32_t* __restrict__ slot,
+                                                                     const int64_t* __restrict__ n_used,
+                                                                     int* __restrict__ block_new,
+                                                                     int64_t* __restrict__ base) {
+  __shared__ int red[kRsWaves];
+  int64_t lo, hi;
+  rs_range(n_touched, &lo, &hi);
+  int c = 0;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += kRsThreads) c += slot[touched[i]] == -1 ? 1 : 0;
+  c = rs_block_sum(c, red);
+  if (threadIdx.x == 0) {
+    block_new[blockIdx.x] = c;
+    if (blockIdx.x == 0) *base = *n_used;
+  }
+}
+
+__global__ __launch_bounds__(kRsThreads) void row_state_assign_kernel(const int32_t* __restrict__ touched,
+                                                                      const int64_t* __restrict__ n_touched,
+                                                                      int32_t* __restrict__ slot,
+                                                                      const int* __restrict__ block_new,
+                                                                      const int64_t* __restrict__ base,
+                                                                      int64_t capacity, int64_t* __restrict__ n_used) {
+  __shared__ int red[kRsWaves];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int before = 0;
+  for (int b = threadIdx.x; b < int(blockIdx.x); b += kRsThreads) before += block_new[b];
+  before = rs_block_sum(before, red);
+  int64_t lo, hi;
+  rs_range(n_touched, &lo, &hi);
+  int64_t next = *base + before;
+  for (int64_t i0 = lo; i0 < hi; i0 += kRsThreads) {  // block-uniform trip count
+    const int64_t i = i0 + threadIdx.x;
+    const int32_t r = i < hi ? touched[i] : 0;
+    const bool isnew = i < hi && slot[r] == -1;
+    int wt = 0;
+    const int wr = wave_excl_scan(isnew ? 1 : 0, &wt);
+    __syncthreads();
+    if (lane == 0) red[wave] = wt;
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kRsWaves; ++w) {
+      off += w < wave ? red[w] : 0;
+      tot += red[w];
+    }
+    if (isnew) {
+      const int64_t sl = next + off + wr;
+      if (sl < capacity) slot[r] = int32_t(-2 - sl);
+    }
+    next += tot;
+  }
+  if (blockIdx.x == kRsBlocks - 1 && threadIdx.x == 0) *n_used = *base + before + block_new[blockIdx.x];
+}
+
 }  // namespace
+
+size_t row_state_temp_bytes() { return size_t(kRsBlocks) * sizeof(int) + 64; }
+
+hipError_t launch_row_state_assign(hipStream_t s, const int32_t* touched, const int64_t* n_touched, int32_t* slot,
+                                   int64_t capacity, int64_t* n_used, void* tmp) {
+  int64_t* base = static_cast<int64_t*>(tmp);
+  int* block_new = reinterpret_cast<int*>(static_cast<char*>(tmp) + 64);
+  hipLaunchKernelGGL(row_state_count_kernel, dim3(kRsBlocks), dim3(kRsThreads), 0, s, touched, n_touched, slot,
+                     n_used, block_new, base);
+  hipLaunchKernelGGL(row_state_assign_kernel, dim3(kRsBlocks), dim3(kRsThreads), 0, s, touched, n_touched, slot,
+                     block_new, base, capacity, n_used);
+  return hipGetLastError();
+}
 
 size_t value_grad_aux_bytes(int64_t nitems, int d_value) {
   const int64_t slots = 2 * (nitems / kVgChunk) + 2;  // chunks of runs longer than a chunk: < 2 N / kVgChunk
@@ -400,8 +516,12 @@ hipError_t launch_value_grad(hipStream_t s, int dtype, const int32_t* seg_start,
   a.am = a.av = nullptr;
   a.b1 = a.b2 = a.eps = a.step_size = a.inv_sqrt_bc2 = 0.f;
   a.sgd = 0;
+  a.slot = nullptr;
+  a.capacity = 0;
   if (adam) {
     a.sgd = adam->sgd;
+    a.slot = adam->slot;
+    a.capacity = adam->capacity;
     a.Vout = adam->V;
     a.am = adam->m;
     a.av = adam->v;

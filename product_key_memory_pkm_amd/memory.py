@@ -109,6 +109,38 @@ class ProductKeyMemory:
                             g["n_touched"], g["dC"], g["dCp"], g["dWq"], g["dgamma"], g["dbeta"], g["dx"], ws)
         return g
 
+    def adam_row_state(self, capacity: int) -> dict:
+        """Moment pool for ``backward_adam_rows``: ``capacity`` rows of first and second moments, handed
+        out to value rows on their first gradient (slot -1: none yet; n_used: slots handed out)."""
+        c = self.cfg
+        dev = self.device
+        return {"slot": torch.full((c.n_keys * c.n_keys2,), -1, dtype=torch.int32, device=dev),
+                "m": torch.empty((capacity, c.d_value), dtype=torch.float32, device=dev),
+                "v": torch.empty((capacity, c.d_value), dtype=torch.float32, device=dev),
+                "n_used": torch.zeros(1, dtype=torch.int64, device=dev)}
+
+    def backward_adam_rows(self, dY, x, Wq, gamma, C, Cp, V, saved, state: dict, adam: dict, want_dx=True):
+        """``backward_adam`` with the moments in a pool of slots (``adam_row_state``).  A touched row that
+        finds the pool full is not stepped; ``state["n_used"]`` above the capacity reports that."""
+        c = self.cfg
+        T = x.shape[0]
+        F = c.heads * c.d_query
+        dev = self.device
+        g = {
+            "touched": torch.empty(max(1, T * c.heads * c.topk), dtype=torch.int32, device=dev),
+            "n_touched": torch.zeros(1, dtype=torch.int64, device=dev),
+            "dC": torch.empty((c.heads, c.n_keys, c.d_query // 2), dtype=torch.float32, device=dev),
+            "dCp": torch.empty((c.heads, c.n_keys2, c.d_query // 2), dtype=torch.float32, device=dev),
+            "dWq": torch.empty((F, c.d_in), dtype=torch.float32, device=dev),
+            "dgamma": torch.empty(F, dtype=torch.float32, device=dev) if c.bn else None,
+            "dbeta": torch.empty(F, dtype=torch.float32, device=dev) if c.bn else None,
+            "dx": torch.empty((T, c.d_in), dtype=self.storage, device=dev) if want_dx else None,
+        }
+        ws = self.workspace(T, True)
+        L.pkm_backward_adam_rows(self.handle, T, dY, x, Wq, gamma, C, Cp, V, saved, state, adam, g["touched"],
+                                 g["n_touched"], g["dC"], g["dCp"], g["dWq"], g["dgamma"], g["dbeta"], g["dx"], ws)
+        return g
+
     def fwpkm_chunk(self, q, C, Cp, V, target, lr: float, out=None, streams: int = 1):
         """One memorization chunk of the fast-weight memory (``pkm_fwpkm_chunk``) for each of ``streams``
         streams: returns (y, idx, w), y read from V before the write; V is updated in place."""

@@ -1,0 +1,247 @@
+"""GPU parity of the Adam step with moments kept only for rows that have received gradient.
+
+([Blog] §6.3: optimizer state allocated only for the parameters that got
+gradient.)  The library keeps the moments in a pool of slots handed out on a
+row's first gradient (``pkm_adam_rows`` in include/pkm.h); the oracle's
+``adam_rows_state_step`` states the rule.  Each step is compared on the same
+inputs: the oracle gets the GPU's value table and pool from before the step.
+The pool starts as NaN, so a row's first step that read its slot would show.
+"""
+import numpy as np
+import pytest
+import torch
+
+import pkm_inputs as pi
+from oracle import pkm_oracle as O
+from tests import parity as P
+from tests.gpu_util import layer_for, note, require_lib, to_dev
+from tests.test_gpu_backward import ADAM, _cfg, reference_forward
+from tests.test_gpu_forward import FWD_CASES, run_gpu_forward
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    require_lib()
+
+
+def _hp(step):
+    # the boundary carries the hyper-parameters as fp32 (pkm_adam): the oracle gets those values
+    hp = {k: (float(np.float32(v)) if k != "step" else v) for k, v in ADAM.items()}
+    hp["step"] = step
+    return hp
+
+
+def _host_V(Vd, dtype):
+    return Vd.cpu().view(torch.int16).numpy().view(np.uint16) if dtype == "bf16" else Vd.cpu().numpy()
+
+
+def _new_state(nrows, cap, dv):
+    return {"slot": torch.full((nrows,), -1, dtype=torch.int32, device="cuda"),
+            "m": torch.full((max(cap, 1), dv), float("nan"), dtype=torch.float32, device="cuda")[:cap],
+            "v": torch.full((max(cap, 1), dv), float("nan"), dtype=torch.float32, device="cuda")[:cap],
+            "n_used": torch.zeros(1, dtype=torch.int64, device="cuda")}
+
+
+def _check_step(dtype, V_before, st_before, rows, w, dY, step, cap, V_after, st_after):
+    """One call against the oracle fed the same value table and pool.
+
+    The GPU sums a row's gradient in fp32, in its own order: element j of row r
+    is within D = (n_r + 2) 2^-24 sum_c |w_c dY_c[j]| of the exact sum (n_r
+    lookups; every product and addition rounds once).  A first step from zero
+    moments moves an element by about lr sign(g), so where a row's lookups
+    nearly cancel the sign itself is open: the value must lie between the
+    oracle's steps with g - D and g + D, up to the fp32 rounding of the step
+    (on the scale of the old value and the update, which can cancel) and the
+    rounding to storage; the moments within the matching spread."""
+    slot0, M0, Vm0, n0 = st_before
+    slot1, M1, Vm1, n1 = st_after
+    uniq = np.unique(rows)
+    w64 = w.astype(np.float64)
+    g = O.value_grad_rows(rows, w64, dY, dtype, uniq)
+    dY_abs = (dY & np.uint16(0x7FFF)) if dtype == "bf16" else np.abs(dY)
+    n_r = np.bincount(rows.reshape(-1), minlength=V_before.shape[0])[uniq]
+    D = (n_r[:, None] + 2) * 2.0 ** -24 * O.value_grad_rows(rows, np.abs(w64), dY_abs, dtype, uniq)
+    hp = _hp(step)
+
+    def oracle(gg):
+        return O.adam_rows_state_step(uniq, slot0, M0.astype(np.float64), Vm0.astype(np.float64), n0, cap,
+                                      V_before[uniq], gg, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], step, dtype)
+
+    out, slot_r, M_r, Vm_r, n_r_used, stepped = oracle(g)
+    out_lo, out_hi = oracle(g - D)[0], oracle(g + D)[0]
+    np.testing.assert_array_equal(slot1, slot_r.astype(np.int32))
+    assert n1 == n_r_used
+    # rows without a step (untouched, or refused a slot): bit-identical
+    moved = uniq[stepped]
+    still = np.setdiff1d(np.arange(V_before.shape[0]), moved)
+    np.testing.assert_array_equal(V_after[still], V_before[still])
+    lo = np.minimum(np.minimum(out_lo, out_hi), out)[stepped]
+    hi = np.maximum(np.maximum(out_lo, out_hi), out)[stepped]
+    gV = O.decode(V_after[moved], dtype)
+    # the fp32 step (a few roundings on the scale of the old value and of the
+    # update, which may nearly cancel), then the rounding to storage: both
+    # sides round to bf16 and may land one bf16 step apart
+    old = O.decode(V_before[moved], dtype)
+    slack = 2.0 ** -21 * (np.abs(old) + np.maximum(np.abs(old - lo), np.abs(old - hi)))
+    if dtype == "bf16":
+        slack += np.maximum(P.bf16_ulp(lo), P.bf16_ulp(hi))
+    else:
+        slack += 2.0 ** -22 * np.maximum(np.abs(lo), np.abs(hi)) + 1e-4 * hp["lr"]
+    bad = (gV < lo - slack) | (gV > hi + slack)
+    if bad.any():
+        i, j = np.argwhere(bad)[0]
+        r = moved[i]
+        raise AssertionError(f"adam V: step {step}, {int(bad.sum())} elements, first row {r} (slot before "
+                             f"{slot0[r]}) col {j}: gpu {gV[i, j]!r} not in [{lo[i, j]!r}, {hi[i, j]!r}] +- "
+                             f"{slack[i, j]!r}; old {O.decode(V_before[r:r + 1], dtype)[0, j]!r}, "
+                             f"g {g[stepped][i, j]!r}, D {D[stepped][i, j]!r}")
+    s = slot_r[moved]
+    Ds, gs = D[stepped], np.abs(g[stepped])
+    # the fp32 step rounds a few times on the scale of its terms (m: b1 m0 and (1 - b1) g may cancel)
+    old_m = np.where((slot0[moved] == -1)[:, None], 0.0, np.abs(M0[np.maximum(s, 0)].astype(np.float64)))
+    mag_m = hp["beta1"] * old_m + (1 - hp["beta1"]) * gs
+    for got, ref, spread, mag, name in ((M1[s], M_r[s], (1 - hp["beta1"]) * Ds, mag_m, "m"),
+                                        (Vm1[s], Vm_r[s], (1 - hp["beta2"]) * (2 * gs * Ds + Ds * Ds), Vm_r[s],
+                                         "v")):
+        err = np.abs(got.astype(np.float64) - ref)
+        assert (err <= spread + 2.0 ** -22 * np.abs(mag) + 1e-30).all(), f"adam {name}"
+    # pool rows no row owns: not written (still NaN)
+    owned = np.zeros(cap, dtype=bool)
+    owned[slot_r[slot_r >= 0]] = True
+    assert np.isnan(M1[~owned]).all() and np.isnan(Vm1[~owned]).all()
+    return int(stepped.sum())
+
+
+def _run_steps(T, h, k, nk, dv, dtype, zipf, cap, nsteps=3, seed=0):
+    nrows = nk * nk
+    cfg = _cfg(T=T, heads=h, topk=k, n_keys=nk, n_keys2=nk, d_value=dv, dtype=dtype)
+    layer = layer_for(cfg)
+    from product_key_memory_pkm_amd import pkm_stage_value_adam_rows
+    V = pi.random_array(20 + seed, 1, (nrows, dv), dtype=dtype, std=0.05)
+    Vd = to_dev(V)
+    st = _new_state(nrows, cap, dv)
+    stepped = []
+    for t in range(1, nsteps + 1):
+        rows, w = pi.random_selection(100 * seed + t, T, h, k, nrows, zipf=zipf)
+        dY = pi.random_array(30 + seed, t, (T, dv), dtype=dtype)
+        before = (st["slot"].cpu().numpy(), st["m"].cpu().numpy(), st["v"].cpu().numpy(), int(st["n_used"].item()))
+        V_before = _host_V(Vd, dtype)
+        touched = torch.full((T * h * k,), -1, dtype=torch.int32, device="cuda")
+        nt = torch.zeros(1, dtype=torch.int64, device="cuda")
+        dw = torch.empty((T, h, k), dtype=torch.float32, device="cuda")
+        pkm_stage_value_adam_rows(layer.handle, T, to_dev(rows), to_dev(w), to_dev(dY), Vd, st, dict(ADAM, step=t),
+                                  touched, nt, dw, layer.workspace(T, True))
+        torch.cuda.synchronize()
+        uniq = np.unique(rows)
+        assert int(nt.item()) == uniq.size
+        after = (st["slot"].cpu().numpy(), st["m"].cpu().numpy(), st["v"].cpu().numpy(), int(st["n_used"].item()))
+        # dw comes from the rows before the step
+        ref_dw = O.weight_grad(rows, dY, V_before, dtype)
+        assert P.row_rel_err(dw.cpu().numpy().reshape(T, -1), ref_dw.reshape(T, -1)).max() <= 1e-5
+        stepped.append(_check_step(dtype, V_before, before, rows, w, dY, t, cap, _host_V(Vd, dtype), after))
+    return stepped, int(st["n_used"].item())
+
+
+ROWS_CASES = [
+    # T, heads, k, nk (slots = nk^2), d_value, dtype, zipf
+    (40, 2, 8, 16, 64, "f32", 0.0),          # fewer touched rows than hand-out blocks
+    (300, 4, 32, 64, 512, "f32", 1.2),       # long runs: chunks, step in the combine launch
+    (128, 4, 32, 128, 1600, "bf16", 0.0),
+    (2000, 2, 16, 16, 16, "f32", 0.0),       # every row touched every step
+    (1, 1, 1, 4, 8, "bf16", 0.0),
+    (4096, 4, 32, 256, 64, "bf16", 0.0),     # 524 K lookups, ~65 K touched rows over 512 hand-out ranges
+]
+
+
+@pytest.mark.parametrize("T,h,k,nk,dv,dtype,zipf", ROWS_CASES)
+def test_value_adam_rows_stage_over_steps(T, h, k, nk, dv, dtype, zipf):
+    note(f"value_adam_rows T={T} h={h} k={k} slots={nk * nk} dv={dv} {dtype} zipf={zipf}")
+    stepped, n_used = _run_steps(T, h, k, nk, dv, dtype, zipf, cap=nk * nk)
+    assert n_used <= nk * nk
+
+
+def test_value_adam_rows_pool_too_small():
+    # rows that find the pool full keep no state and are not stepped; n_used counts them
+    note("value_adam_rows pool too small")
+    T, h, k, nk, dv = 200, 2, 8, 32, 32
+    first = np.unique(pi.random_selection(1, T, h, k, nk * nk)[0]).size   # the first step's rows (seed 1)
+    cap = first * 3 // 5
+    stepped, n_used = _run_steps(T, h, k, nk, dv, "f32", 0.0, cap=cap, nsteps=3)
+    assert stepped[0] == cap and n_used > cap
+
+
+def test_value_adam_rows_equals_dense_moments():
+    # moments in slots and dense zero-initialised tables: bit-identical steps
+    note("value_adam_rows vs dense moments")
+    T, h, k, nk, dv = 300, 4, 32, 64, 256
+    nrows = nk * nk
+    cfg = _cfg(T=T, heads=h, topk=k, n_keys=nk, n_keys2=nk, d_value=dv, dtype="bf16")
+    layer = layer_for(cfg)
+    from product_key_memory_pkm_amd import pkm_stage_value_adam, pkm_stage_value_adam_rows
+    V = pi.random_array(40, 1, (nrows, dv), dtype="bf16", std=0.05)
+    Va, Vb = to_dev(V), to_dev(V)
+    md = torch.zeros((nrows, dv), dtype=torch.float32, device="cuda")
+    vd = torch.zeros((nrows, dv), dtype=torch.float32, device="cuda")
+    st = _new_state(nrows, nrows, dv)
+    for t in range(1, 4):
+        rows, w = pi.random_selection(200 + t, T, h, k, nrows, zipf=1.0)
+        dY = to_dev(pi.random_array(41, t, (T, dv), dtype="bf16"))
+        rd, wd = to_dev(rows), to_dev(w)
+        hp = dict(ADAM, step=t)
+        for V_, fn in ((Va, "dense"), (Vb, "rows")):
+            touched = torch.empty(T * h * k, dtype=torch.int32, device="cuda")
+            nt = torch.zeros(1, dtype=torch.int64, device="cuda")
+            dw = torch.empty((T, h, k), dtype=torch.float32, device="cuda")
+            if fn == "dense":
+                pkm_stage_value_adam(layer.handle, T, rd, wd, dY, V_, md, vd, hp, touched, nt, dw,
+                                     layer.workspace(T, True))
+            else:
+                pkm_stage_value_adam_rows(layer.handle, T, rd, wd, dY, V_, st, hp, touched, nt, dw,
+                                          layer.workspace(T, True))
+        torch.cuda.synchronize()
+        assert torch.equal(Va.cpu(), Vb.cpu())
+        slot = st["slot"].cpu()
+        has = slot >= 0
+        assert torch.equal(st["m"].cpu()[slot[has].long()], md.cpu()[has])
+        assert torch.equal(st["v"].cpu()[slot[has].long()], vd.cpu()[has])
+        assert (md.cpu()[~has] == 0).all()
+
+
+def test_backward_adam_rows_end_to_end():
+    """pkm_backward_adam_rows against pkm_backward_adam with zero dense moments: the same step and every other
+    output bit-identical; the slot map against the oracle's rule."""
+    cfg = FWD_CASES["small"]
+    note(f"backward_adam_rows small: {cfg}")
+    inp = pi.make_inputs(cfg, with_dy=True)
+    gpu, (layer, dev, saved, y) = run_gpu_forward(cfg, inp)
+    fwd, _ = reference_forward(cfg, inp, gpu)
+    dYd = to_dev(inp["dY"])
+    V0 = inp["V"]
+    Va, Vb = to_dev(V0), to_dev(V0)
+    md = torch.zeros((cfg.slots, cfg.d_value), dtype=torch.float32, device="cuda")
+    vd = torch.zeros_like(md)
+    hp = dict(ADAM, step=1)
+    g_dense = layer.backward_adam(dYd, dev["x"], dev["Wq"], dev["gamma"], dev["C"], dev["Cp"], Va, saved, md, vd, hp)
+    torch.cuda.synchronize()
+    dense = {k: v.cpu().clone() for k, v in g_dense.items() if v is not None}
+    st = layer.adam_row_state(cfg.slots)
+    g_rows = layer.backward_adam_rows(dYd, dev["x"], dev["Wq"], dev["gamma"], dev["C"], dev["Cp"], Vb, saved, st, hp)
+    torch.cuda.synchronize()
+    n = int(dense["n_touched"].item())
+    for k, v in dense.items():
+        got = g_rows[k].cpu()
+        if k == "touched":
+            assert torch.equal(got[:n], v[:n])
+        else:
+            assert torch.equal(got, v), k
+    assert torch.equal(Va.cpu(), Vb.cpu())
+    uniq = np.unique(fwd["rows"])
+    slot = st["slot"].cpu().numpy()
+    want = -np.ones(cfg.slots, dtype=np.int32)
+    want[uniq] = np.arange(uniq.size)            # first step: slots in ascending row order
+    np.testing.assert_array_equal(slot, want)
+    assert int(st["n_used"].item()) == uniq.size
+    assert torch.equal(st["m"].cpu()[: uniq.size], md.cpu()[uniq])
+    assert torch.equal(st["v"].cpu()[: uniq.size], vd.cpu()[uniq])
