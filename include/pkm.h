@@ -158,7 +158,8 @@ typedef struct {
  *     library writes it (between calls every entry is -1 or a slot below
  *     capacity; a call writes other values transiently).
  *   m, v [capacity, d_value] fp32: the pool; need not be initialised (a row's
- *     first step starts from zero moments and does not read its slot).
+ *     first step starts from zero moments and does not read its slot); may be
+ *     NULL when capacity is 0.
  *   n_used [1] int64 (8-byte aligned): slots handed out so far; 0 before the
  *     first step.  A call gives the touched rows without a slot, in ascending
  *     row order, the slots n_used, n_used + 1, ...; a row whose slot would be

@@ -378,8 +378,8 @@ pkm_status adam_args(const pkm_adam* hp, void* V, float* m, float* v, VgAdam* ou
 pkm_status adam_rows_args(const pkm_handle_s* h, const pkm_adam* hp, void* V, const pkm_adam_rows* st, VgAdam* out) {
   if (st == nullptr) return fail(PKM_ERR_INVALID_ARG, "state is NULL");
   PKM_TRY(need(st->slot, "state.slot"));
-  PKM_TRY(need(st->m, "state.m"));
-  PKM_TRY(need(st->v, "state.v"));
+  if (st->capacity != 0 || st->m != nullptr) PKM_TRY(need(st->m, "state.m"));  // a pool of no rows is never read
+  if (st->capacity != 0 || st->v != nullptr) PKM_TRY(need(st->v, "state.v"));
   if (st->n_used == nullptr) return fail(PKM_ERR_INVALID_ARG, "state.n_used is NULL");
   if (reinterpret_cast<uintptr_t>(st->n_used) % 8 != 0)
     return fail(PKM_ERR_INVALID_ARG, "state.n_used must be 8-byte aligned");

@@ -210,6 +210,49 @@ def test_adam_argument_errors():
     assert st == L.PKM_ERR_INVALID_ARG and "adam_m" in lib.pkm_last_error().decode()
 
 
+
+def test_adam_rows_argument_errors():
+    L = _lib()
+    lib = L.lib()
+    h = L.pkm_create(_cfg(L))
+    sv = L.pkm_saved(_fake(9), _fake(10), _fake(11), _fake(12), _fake(13), _fake(14))
+    ok = [_fake(i) for i in range(30)]
+    hp = L.pkm_adam(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, step=1)
+    slots = h.cfg.n_keys * h.cfg.n_keys2
+
+    def state(**over):
+        f = dict(slot=_fake(20), m=_fake(21), v=_fake(22), n_used=_fake(23), capacity=slots)
+        f.update(over)
+        return L.pkm_adam_rows(f["slot"], f["m"], f["v"], f["n_used"], f["capacity"])
+
+    def stage(st, adam=hp, ws_bytes=16):
+        ref = ctypes.byref(st) if st is not None else None
+        return lib.pkm_stage_value_adam_rows(h.ptr, None, 4, ok[1], ok[2], ok[3], ok[4], ref, ctypes.byref(adam),
+                                             ok[7], ok[8], ok[9], ok[10], ws_bytes)
+
+    assert stage(state()) == L.PKM_ERR_WORKSPACE                  # every other check passes
+    assert stage(state(capacity=0)) == L.PKM_ERR_WORKSPACE        # an empty pool is allowed
+    assert stage(state(capacity=0, m=None, v=None)) == L.PKM_ERR_WORKSPACE
+    assert stage(None) == L.PKM_ERR_INVALID_ARG
+    for field in ("slot", "m", "v", "n_used"):   # m and v are needed for a pool of rows
+        assert stage(state(**{field: None})) == L.PKM_ERR_INVALID_ARG, field
+        assert f"state.{field}" in lib.pkm_last_error().decode()
+    assert stage(state(n_used=ctypes.c_void_p(FAKE + 4))) == L.PKM_ERR_INVALID_ARG
+    assert "aligned" in lib.pkm_last_error().decode()
+    for cap in (-1, slots + 1):
+        assert stage(state(capacity=cap)) == L.PKM_ERR_INVALID_ARG, cap
+        assert "capacity" in lib.pkm_last_error().decode()
+    assert stage(state(), adam=L.pkm_adam(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, step=0)) == \
+        L.PKM_ERR_INVALID_ARG
+    bwd = lib.pkm_backward_adam_rows
+    st = bwd(h.ptr, None, 10, ok[1], ok[2], ok[3], ok[4], ok[5], ok[6], ok[7], ctypes.byref(sv),
+             ctypes.byref(state()), ctypes.byref(hp), ok[10], ok[11], ok[12], ok[13], ok[14], ok[15], ok[16], None,
+             ok[17], 16)
+    assert st == L.PKM_ERR_WORKSPACE
+    st = bwd(h.ptr, None, 10, ok[1], ok[2], ok[3], ok[4], ok[5], ok[6], ok[7], ctypes.byref(sv), None,
+             ctypes.byref(hp), ok[10], ok[11], ok[12], ok[13], ok[14], ok[15], ok[16], None, ok[17], 1 << 40)
+    assert st == L.PKM_ERR_INVALID_ARG and "state" in lib.pkm_last_error().decode()
+
 def test_diagnostics_argument_errors():
     L = _lib()
     lib = L.lib()

@@ -172,6 +172,29 @@ def test_value_adam_rows_pool_too_small():
     assert stepped[0] == cap and n_used > cap
 
 
+
+def test_value_adam_rows_empty_pool_and_no_tokens():
+    # a pool of no rows refuses every row (nothing stepped, the demand counted); T = 0 changes nothing
+    note("value_adam_rows empty pool, T = 0")
+    stepped, n_used = _run_steps(50, 2, 8, 16, 32, "bf16", 0.0, cap=0, nsteps=2)
+    assert stepped == [0, 0] and n_used > 0
+    cfg = _cfg(T=8, heads=2, topk=8, n_keys=16, n_keys2=16, d_value=32, dtype="bf16")
+    layer = layer_for(cfg)
+    from product_key_memory_pkm_amd import pkm_stage_value_adam_rows
+    st = _new_state(256, 4, 32)
+    st["slot"][3] = 1
+    st["n_used"].fill_(2)
+    V = to_dev(pi.random_array(5, 1, (256, 32), dtype="bf16"))
+    V0 = V.clone()
+    nt = torch.full((1,), 7, dtype=torch.int64, device="cuda")
+    pkm_stage_value_adam_rows(layer.handle, 0, torch.empty(1, dtype=torch.int32, device="cuda"),
+                              torch.empty(1, dtype=torch.float32, device="cuda"), V[:1], V, st, dict(ADAM, step=1),
+                              torch.empty(1, dtype=torch.int32, device="cuda"), nt,
+                              torch.empty(1, dtype=torch.float32, device="cuda"), layer.workspace(8, True))
+    torch.cuda.synchronize()
+    assert int(nt.item()) == 0 and int(st["n_used"].item()) == 2
+    assert torch.equal(V, V0) and int(st["slot"][3].item()) == 1 and int((st["slot"] == -1).sum().item()) == 255
+
 def test_value_adam_rows_equals_dense_moments():
     # moments in slots and dense zero-initialised tables: bit-identical steps
     note("value_adam_rows vs dense moments")
