@@ -307,7 +307,8 @@ pkm_status pkm_stage_gather(pkm_handle_t handle, void* stream, int64_t T, const 
 /* Steps a7 (dw) and a8: rows of idx sorted (stable), then per touched row r:
  * dw[c] = <dY[t(c)], V[r]> for every lookup c with idx[c] == r, and
  * dV[r] (+)= sum_c w[c] dY[t(c)].  dw [T, h, k] fp32; dV, touched, n_touched as
- * in pkm_backward.  ws >= pkm_workspace_size(handle, T, 1). */
+ * in pkm_backward; every idx must lie in [0, |C|*|C'|) (not checked on the
+ * device).  ws >= pkm_workspace_size(handle, T, 1). */
 pkm_status pkm_stage_value_grad(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx,
                                 const float* w, const void* dY, const void* V, float* dV,
                                 int32_t* touched, int64_t* n_touched, float* dw, void* ws,
@@ -315,7 +316,8 @@ pkm_status pkm_stage_value_grad(pkm_handle_t handle, void* stream, int64_t T, co
 
 /* Steps a7 (dw) and a8 with the Adam step of pkm_backward_adam in place of
  * dV: dw [T, h, k] fp32 from the rows of V before the step; V, adam_m, adam_v
- * updated at the touched rows; touched, n_touched as in pkm_backward.
+ * updated at the touched rows; touched, n_touched as in pkm_backward; every
+ * idx must lie in [0, |C|*|C'|) (not checked on the device).
  * ws >= pkm_workspace_size(handle, T, 1). */
 pkm_status pkm_stage_value_adam(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx,
                                 const float* w, const void* dY, void* V, float* adam_m, float* adam_v,
@@ -350,7 +352,8 @@ pkm_status pkm_quantize_values(pkm_handle_t handle, void* stream, const void* V_
 
 /* Step a8's grouping alone: the lookups of idx [T, h, k] stably sorted by row,
  * written into the workspace (for pkm_stage_value_grad_grouped), plus touched
- * and *n_touched as in pkm_backward.  ws >= pkm_workspace_size(handle, T, 1). */
+ * and *n_touched as in pkm_backward; every idx must lie in [0, |C|*|C'|) (not
+ * checked on the device).  ws >= pkm_workspace_size(handle, T, 1). */
 pkm_status pkm_stage_row_groups(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx,
                                 int32_t* touched, int64_t* n_touched, void* ws, size_t ws_bytes);
 
@@ -371,7 +374,8 @@ pkm_status pkm_stage_value_adam_grouped(pkm_handle_t handle, void* stream, int64
 
 /* pkm_stage_value_adam with the moments in the pool of `state` (as in
  * pkm_backward_adam_rows): the grouping, the slot hand-out for the touched
- * rows without one, then the value-gradient kernel with the Adam step.
+ * rows without one, then the value-gradient kernel with the Adam step.  Every
+ * idx must lie in [0, |C|*|C'|) (not checked on the device).
  * ws >= pkm_workspace_size(handle, T, 1). */
 pkm_status pkm_stage_value_adam_rows(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx,
                                      const float* w, const void* dY, void* V, const pkm_adam_rows* state,
@@ -380,7 +384,8 @@ pkm_status pkm_stage_value_adam_rows(pkm_handle_t handle, void* stream, int64_t 
 
 /* Steps a7 (softmax backward) and a9: ds = w (dw - sum_s w dw) / tau; then
  * dq[t, h*dq] fp32 (both halves of each head) and dC, dCp (overwritten) through
- * the selected sub-keys only.  q is the saved query (storage dtype).
+ * the selected sub-keys only.  q is the saved query (storage dtype); every idx
+ * must lie in [0, |C|*|C'|) (not checked on the device).
  * ws >= pkm_workspace_size(handle, T, 1). */
 pkm_status pkm_stage_subkey_grad(pkm_handle_t handle, void* stream, int64_t T, const int32_t* idx,
                                  const float* w, const float* dw, const void* q, const void* C,
