@@ -81,6 +81,9 @@ def parse():
     ap.add_argument("--no-fwpkm", action="store_true", help="skip the fast-weight memorization legs")
     ap.add_argument("--no-skewed", action="store_true",
                     help="skip the skewed 4,194,304-slot workload reported beside the paper-scale line")
+    ap.add_argument("--sweep-keys", action="store_true",
+                    help="only time the forward and forward + backward at |C| = |C'| = 256, 512, 1024 and 2048 "
+                         "sub-keys, the other sizes those of the paper scale, and print one JSON line")
     return ap.parse_args()
 
 
@@ -206,6 +209,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "launches": 5}), flush=True)
+        return
+
+    if args.sweep_keys:
+        print(json.dumps(sweep_keys(args)), flush=True)
         return
 
     cfg = pi.CONFIGS[args.workload]
@@ -708,6 +715,69 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_tokens)
     print(json.dumps(out), flush=True)
+
+
+def sweep_keys(args) -> dict:
+    """Forward and forward + backward tokens/s of the paper-scale layer (T = 32,768, d = 1600, h = 4, k = 32,
+    bf16, BatchNorm) at several codebook sizes: the speed side of the product-key summary's 512^2 -> 1024^2
+    slot comparison ("关键结果"), for this layer alone.  Inputs from the same seeded generator per size."""
+    import dataclasses
+    import numpy as np
+    import torch
+
+    import pkm_inputs as pi
+    from product_key_memory_pkm_amd import ProductKeyMemory
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    rows = []
+    for nk in (256, 512, 1024, 2048):
+        c = dataclasses.replace(pi.CONFIGS["paper"], name=f"paper_keys{nk}", n_keys=nk, n_keys2=nk)
+        inp = pi.make_inputs(c, with_dy=True)
+        x, Wq, C, Cp, V, dY = (dev(inp[k]) for k in ("x", "Wq", "C", "Cp", "V", "dY"))
+        gamma, beta = dev(inp["gamma"]), dev(inp["beta"])
+        del inp
+        m = ProductKeyMemory(c.d, c.heads, c.dq, c.n_keys, c.n_keys2, c.topk, c.d_value, dtype=c.dtype, bn=c.bn,
+                             bn_eps=c.bn_eps, temperature=c.temperature, accumulate_dv=True)
+        saved = m.alloc_saved(c.T)
+        y = torch.empty((c.T, c.d_value), dtype=m.storage, device="cuda")
+        dV = torch.zeros((c.slots, c.d_value), dtype=torch.float32, device="cuda")
+        grads = None
+
+        def fwd():
+            m.forward(x, Wq, gamma, beta, C, Cp, V, saved=saved, y=y)
+
+        def step():
+            nonlocal grads
+            fwd()
+            grads = m.backward(dY, x, Wq, gamma, C, Cp, V, saved, dV, want_dx=True, out=grads)
+
+        res = {"n_keys": nk, "slots": c.slots}
+        for name, fn in (("fwd", fwd), ("fwd_bwd", step)):
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(args.steps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / args.steps
+            res[f"{name}_ms"] = ms
+            res[f"{name}_tokens_per_s"] = c.T / (ms * 1e-3)
+        res["touched_rows"] = int(grads["n_touched"].item())
+        res["memory_usage"] = res["touched_rows"] / c.slots
+        rows.append(res)
+        print(json.dumps(res), file=sys.stderr, flush=True)
+        del x, Wq, C, Cp, V, dY, gamma, beta, m, saved, y, dV, grads
+        torch.cuda.empty_cache()
+    return {"sweep": "codebook size |C| = |C'|", "workload": "paper scale otherwise: T=32768, d=1600, heads=4, "
+            "dq=512, k=32, d_value=1600, bf16 storage, BatchNorm, dV accumulated in fp32", "data": "synthetic",
+            "steps": args.steps, "warmup": args.warmup, "rows": rows}
 
 
 def rank_frequency(idx, slots: int) -> dict:
