@@ -386,6 +386,52 @@ def test_value_adam_full_size_sampled():
     assert (np.abs(P.to_f64(V1[wt]) - Vr) <= P.bf16_ulp(Vr)).all(), "adam V (bf16)"
 
 
+
+def test_value_adam_rows_full_size_against_dense_moments():
+    # two Adam steps of paper-shaped selections (about a million touched rows each) with the moments in pool
+    # slots and in dense tables: value tables bit-identical; the first step's slots in ascending row order;
+    # pool rows equal to the dense rows they stand for
+    cfg = pi.CONFIGS["paper"]
+    note("full-size Adam step with moments in pool slots against dense moments (paper)")
+    T, h, k = cfg.T, cfg.heads, cfg.topk
+    inp = _inputs("paper")
+    layer = layer_for(cfg)
+    from product_key_memory_pkm_amd import pkm_stage_value_adam, pkm_stage_value_adam_rows
+    Vd = to_dev(inp["V"])
+    Vr = Vd.clone()
+    dY = to_dev(inp["dY"])
+    md = torch.zeros((cfg.slots, cfg.d_value), dtype=torch.float32, device="cuda")
+    vd = torch.zeros_like(md)
+    st = layer.adam_row_state(cfg.slots)
+    touched = torch.empty(T * h * k, dtype=torch.int32, device="cuda")
+    nt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    dw = torch.empty((T, h, k), dtype=torch.float32, device="cuda")
+    ws = layer.workspace(T, True)
+    seen = np.zeros(0, dtype=np.int64)
+    for step, seed in ((1, 41), (2, 42)):
+        rows, w = pi.random_selection(seed, T, h, k, cfg.slots)
+        rd, wd = to_dev(rows), to_dev(w)
+        hp = dict(lr=1e-2, beta1=0.9, beta2=0.999, eps=1e-8, step=step)
+        pkm_stage_value_adam(layer.handle, T, rd, wd, dY, Vd, md, vd, hp, touched, nt, dw, ws)
+        pkm_stage_value_adam_rows(layer.handle, T, rd, wd, dY, Vr, st, hp, touched, nt, dw, ws)
+        torch.cuda.synchronize()
+        uniq = np.unique(rows)
+        fresh = np.setdiff1d(uniq, seen)
+        seen = np.union1d(seen, uniq)
+        for lo, hi in _row_chunks(cfg.slots):
+            assert torch.equal(Vd[lo:hi].view(torch.int16), Vr[lo:hi].view(torch.int16)), f"step {step} [{lo}, {hi})"
+        slot = st["slot"].cpu().numpy()
+        assert int(st["n_used"].item()) == seen.size
+        np.testing.assert_array_equal(slot[fresh], np.arange(seen.size - fresh.size, seen.size))
+        assert (slot[np.setdiff1d(np.arange(cfg.slots), seen)] == -1).all()
+        if step == 1:
+            np.testing.assert_array_equal(slot[uniq], np.arange(uniq.size))
+        for lo in range(0, seen.size, 1 << 17):
+            r = torch.from_numpy(seen[lo:lo + (1 << 17)]).cuda().long()
+            sl = st["slot"][r].long()
+            assert torch.equal(st["m"][sl], md[r]) and torch.equal(st["v"][sl], vd[r]), f"step {step} moments"
+
+
 @pytest.mark.parametrize("name,zipf", [("paper", 0.0), ("skewed", 0.8)])
 def test_diagnostics_full_size(name, zipf):
     # exact integer counts over the whole selection; entropies within fp32 rounding
