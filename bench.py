@@ -34,6 +34,7 @@ KERNEL_TRAFFIC = {
     ("gather", "paper"): {"bytes": 13552071360, "sources": ["gather.hip", "common.h"], "sources_sha256_16": "993549f60bba5340"},
     ("value_grad", "paper"): {"bytes": 29789221888, "sources": ["value_grad.hip", "sparse_common.h", "common.h"], "sources_sha256_16": "c71e5fb32d3e118e"},
     ("value_adam", "paper"): {"bytes": 47242236928, "sources": ["value_grad.hip", "sparse_common.h", "common.h"], "sources_sha256_16": "c71e5fb32d3e118e"},
+    ("gather_fp8", "paper"): {"bytes": 7855391744, "sources": ["gather.hip", "common.h"], "sources_sha256_16": "993549f60bba5340"},
     ("value_grad", "skewed"): {"bytes": 58854975488, "sources": ["value_grad.hip", "sparse_common.h", "common.h"], "sources_sha256_16": "c71e5fb32d3e118e"},
 }
 
