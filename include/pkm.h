@@ -79,14 +79,17 @@ typedef enum { PKM_F32 = 0, PKM_BF16 = 1 } pkm_dtype;
 typedef enum { PKM_BN_NONE = 0, PKM_BN_BATCH = 1 } pkm_bn_mode;
 /* How the value table V is stored.  PKM_VALUES_FP8 ("Meta AI 可扩展内存层",
  * section 16.3: the value matrix compressed to a low-bit format): row r takes
- * d_value + 16 bytes, a 16-byte header whose first 4 bytes are the fp32 scale
- * s_r (the other 12 bytes zero), then d_value E4M3 codes (1 sign bit, 4 exponent
- * bits with bias 7, 3 mantissa bits, no infinities); the value is s_r * code.
+ * PKM_FP8_ROW_BYTES(d_value) bytes, d_value + 16 rounded up to a multiple of
+ * 128 (a row then spans whole 128-byte lines): a 16-byte header whose first 4
+ * bytes are the fp32 scale s_r (the other 12 bytes zero), then d_value E4M3
+ * codes (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities), then zero bytes up to the row's end; the value is s_r * code.
  * pkm_quantize_values writes such a table.  It is a forward (inference)
  * format: pkm_forward and pkm_stage_gather read it; the entry points that need
  * V in the backward return PKM_ERR_UNSUPPORTED (train a table in the storage
  * dtype and quantize it). */
 typedef enum { PKM_VALUES_STORAGE = 0, PKM_VALUES_FP8 = 1 } pkm_value_format;
+#define PKM_FP8_ROW_BYTES(d_value) ((((int64_t)(d_value) + 16 + 127) / 128) * 128)
 /* Sub-key score.  PKM_SCORE_DOT: s1[i] = q1 . C[h,i] (as above).  PKM_SCORE_IDW
  * ("Fast-weight Product Key Memory", section 2.2: inverse-distance scores):
  * s1[i] = -log ||q1 - C[h,i]||, computed as -1/2 log(max(||q1||^2 - (2 q1 . C[h,i]
@@ -345,8 +348,8 @@ pkm_status pkm_diagnostics(pkm_handle_t handle, void* stream, int64_t T, const i
  * each of the `rows` rows of V_src [rows, d_value], s_r = max_j |V_src[r, j]| / 448
  * and code j = the E4M3 value nearest to V_src[r, j] * (448 / max_j |V_src[r, j]|)
  * (ties to the even code; scale, factor and product rounded to fp32); a zero
- * row gets s_r = 0 and zero codes.  V_fp8: rows * (d_value + 16) bytes, layout
- * as described at pkm_value_format.  The handle must have value_format =
+ * row gets s_r = 0 and zero codes.  V_fp8: rows * PKM_FP8_ROW_BYTES(d_value)
+ * bytes, layout as described at pkm_value_format (every byte is written).  The handle must have value_format =
  * PKM_VALUES_FP8.  rows >= 0. */
 pkm_status pkm_quantize_values(pkm_handle_t handle, void* stream, const void* V_src, int64_t rows, void* V_fp8);
 

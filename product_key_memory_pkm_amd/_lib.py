@@ -156,13 +156,18 @@ def _need(**req):
             raise ValueError(f"{name} holds {t.numel()} elements; this call needs {n}")
 
 
+def fp8_row_bytes(d_value: int) -> int:
+    """Bytes of one fp8 value row (pkm.h PKM_FP8_ROW_BYTES): d_value + 16 rounded up to a multiple of 128."""
+    return (d_value + 16 + 127) // 128 * 128
+
+
 def _dims(h, T: int, streams: int = 1) -> dict:
     """Element counts of the buffers pkm.h describes, for handle ``h`` and T tokens."""
     c = h.cfg
     F = c.heads * c.d_query
     half = c.d_query // 2
     slots = c.n_keys * c.n_keys2 * streams
-    vrow = c.d_value + 16 if c.value_format == PKM_VALUES_FP8 else c.d_value
+    vrow = fp8_row_bytes(c.d_value) if c.value_format == PKM_VALUES_FP8 else c.d_value
     return {"x": T * c.d_in, "Wq": F * c.d_in, "F": F, "C": c.heads * c.n_keys * half,
             "Cp": c.heads * c.n_keys2 * half, "V": slots * vrow, "dV": slots * c.d_value, "y": T * c.d_value,
             "lookups": T * c.heads * c.topk, "sub": T * c.heads * 2 * c.topk, "q": T * F,
@@ -422,8 +427,8 @@ def pkm_quantize_values(h, V_src, V_fp8, rows=None):
     _dt(V_src, h.storage, "V_src")
     _dt(V_fp8, torch.uint8, "V_fp8")
     n = V_src.shape[0] if rows is None else rows
-    if V_fp8.numel() < n * (h.cfg.d_value + 16):
-        raise ValueError("V_fp8 holds fewer than rows * (d_value + 16) bytes")
+    if V_fp8.numel() < n * fp8_row_bytes(h.cfg.d_value):
+        raise ValueError("V_fp8 holds fewer than rows * PKM_FP8_ROW_BYTES(d_value) bytes")
     _check(lib().pkm_quantize_values(h.ptr, _stream(), _ptr(V_src), n, _ptr(V_fp8)), "pkm_quantize_values")
 
 

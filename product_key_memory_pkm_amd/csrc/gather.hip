@@ -116,9 +116,10 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const int32_t* __restri
 
 // ---------------------------------------------------------------------------
 // fp8 value rows ("Meta AI 可扩展内存层", section 16.3: the value table stored
-// in a low-bit format).  Row r takes d_value + 16 bytes: a 16-byte header
-// whose first 4 bytes are the fp32 scale s_r, then d_value E4M3 codes (1 sign,
-// 4 exponent bits with bias 7, 3 mantissa bits); the value is s_r * code.
+// in a low-bit format).  Row r takes d_value + 16 bytes rounded up to a
+// multiple of 128 (whole 128-byte lines): a 16-byte header whose first 4 bytes
+// are the fp32 scale s_r, then d_value E4M3 codes (1 sign, 4 exponent bits with
+// bias 7, 3 mantissa bits), then zeros; the value is s_r * code.
 // ---------------------------------------------------------------------------
 constexpr float kE4M3Max = 448.f;
 
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(256) void gather_fp8_kernel(const int32_t* __restri
   const int lane = lane_id();
   const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= ntok) return;
-  const size_t row_bytes = size_t(nvec) * 16 + 16;
+  const size_t row_bytes = fp8_row_bytes(nvec);
   const char* Vb = reinterpret_cast<const char*>(V);
   bool valid[NVL];
   int voff[NVL];
@@ -236,7 +237,8 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const T* __restrict__
   const int64_t gw = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
   const int64_t nw = (int64_t(gridDim.x) * blockDim.x) >> 6;
   const size_t in_row = size_t(nvec) * 16 * sizeof(T);  // bytes of a source row
-  const size_t out_row = size_t(nvec) * 16 + 16;
+  const size_t out_row = fp8_row_bytes(nvec);
+  const int npad = int((out_row - 16) / 16) - nvec;  // zero vectors after the codes
   for (int64_t r = gw; r < rows; r += nw) {
     const char* rs = reinterpret_cast<const char*>(src) + size_t(r) * in_row;
     float f[NVL][16];
@@ -259,6 +261,7 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const T* __restrict__
     const float inv = mx > 0.f ? kE4M3Max / mx : 0.f;
     char* rd = reinterpret_cast<char*>(dst) + size_t(r) * out_row;
     if (lane == 0) st16(rd, u32x4{__float_as_uint(scale), 0u, 0u, 0u});
+    if (lane < npad) st16(rd + 16 + size_t(nvec + lane) * 16, u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
     for (int m = 0; m < NVL; ++m) {
       const int v = m * 64 + lane;

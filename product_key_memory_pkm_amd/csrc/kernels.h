@@ -205,6 +205,11 @@ struct VgAdam {
   int64_t capacity;
   int64_t* n_used;  // slots handed out so far (device)
 };
+// Bytes of one fp8 value row of nvec 16-code vectors: the 16-byte header and
+// the codes, rounded up to whole 128-byte lines.
+__host__ __device__ constexpr size_t fp8_row_bytes(int nvec) {
+  return (size_t(nvec) * 16 + 16 + 127) / 128 * 128;
+}
 // Hands out pool slots to the touched rows that have none (slot[r] == -1), in
 // ascending row order from *n_used; a slot at or past capacity is refused (the
 // entry stays -1) but counted in *n_used.  tmp: row_state_temp_bytes().

@@ -54,7 +54,7 @@ class ProductKeyMemory:
 
     def quantize_values(self, V):
         """fp8 value table (uint8 bytes, rows of a fp32 scale header and E4M3 codes) of V [rows, d_value]."""
-        out = torch.empty(V.shape[0] * (self.cfg.d_value + 16), dtype=torch.uint8, device=self.device)
+        out = torch.empty(V.shape[0] * L.fp8_row_bytes(self.cfg.d_value), dtype=torch.uint8, device=self.device)
         L.pkm_quantize_values(self.handle, V, out)
         return out
 

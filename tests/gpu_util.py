@@ -38,11 +38,11 @@ def layer_for(cfg, accumulate_dv=True, values="storage", score="dot"):
 
 def fp8_table(scale: np.ndarray, codes: np.ndarray) -> np.ndarray:
     """Bytes of an fp8 value table (pkm.h, PKM_VALUES_FP8): per row a 16-byte header holding the fp32 scale
-    (other bytes zero), then the row's E4M3 codes."""
+    (other bytes zero), then the row's E4M3 codes, then zeros up to d + 16 rounded up to 128 bytes."""
     n, d = codes.shape
-    out = np.zeros((n, d + 16), dtype=np.uint8)
+    out = np.zeros((n, (d + 16 + 127) // 128 * 128), dtype=np.uint8)
     out[:, :4] = np.asarray(scale, dtype=np.float32).reshape(n, 1).view(np.uint8)
-    out[:, 16:] = codes
+    out[:, 16:16 + d] = codes
     return out.reshape(-1)
 
 

@@ -456,14 +456,16 @@ def test_quantize_values_bit_exact(rows, dv, dtype):
     cfg = _cfg(d_value=dv, dtype=dtype, n_keys=32, n_keys2=32, d=16, dq=32)
     layer = layer_for(cfg, values="fp8")
     from product_key_memory_pkm_amd import pkm_quantize_values
-    out = torch.full((rows * (dv + 16),), 0xAB, dtype=torch.uint8, device="cuda")
+    rb = (dv + 16 + 127) // 128 * 128       # row stride: header and codes in whole 128-byte lines
+    out = torch.full((rows * rb,), 0xAB, dtype=torch.uint8, device="cuda")
     pkm_quantize_values(layer.handle, to_dev(V), out)
     torch.cuda.synchronize()
-    got = out.cpu().numpy().reshape(rows, dv + 16)
+    got = out.cpu().numpy().reshape(rows, rb)
     scale, codes = O.quantize_rows_fp8(V, dtype)
     np.testing.assert_array_equal(got[:, :4].copy().view(np.float32).reshape(-1), scale)
     assert (got[:, 4:16] == 0).all()
-    np.testing.assert_array_equal(got[:, 16:], codes)
+    np.testing.assert_array_equal(got[:, 16:16 + dv], codes)
+    assert (got[:, 16 + dv:] == 0).all()     # every byte of the row is written
 
 
 FP8_GATHER_CASES = [
@@ -472,6 +474,10 @@ FP8_GATHER_CASES = [
     (37, 3, 5, 100, 32, "f32"),
     (33, 1, 3, 50, 2048, "bf16"),      # 4 vectors per lane
     (70, 4, 32, 4096, 768, "f32"),     # 3 vectors per lane
+    # the header and the codes over the lanes: exactly 64 vectors, one past, exactly 128
+    (20, 2, 8, 300, 1008, "bf16"),
+    (20, 2, 8, 300, 1024, "bf16"),
+    (20, 2, 8, 300, 2032, "bf16"),
 ]
 
 

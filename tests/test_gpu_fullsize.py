@@ -319,7 +319,7 @@ def test_fp8_values_full_size_sampled():
     V = inp["V"]
     layer = layer_for(cfg, values="fp8")
     from product_key_memory_pkm_amd import pkm_quantize_values, pkm_stage_gather
-    rb = cfg.d_value + 16
+    rb = (cfg.d_value + 16 + 127) // 128 * 128   # fp8 row stride
     table = torch.empty(cfg.slots * rb, dtype=torch.uint8, device="cuda")
     pkm_quantize_values(layer.handle, to_dev(V), table)
     torch.cuda.synchronize()
@@ -328,7 +328,8 @@ def test_fp8_values_full_size_sampled():
     scale, codes = O.quantize_rows_fp8(V[which], cfg.dtype)
     np.testing.assert_array_equal(got[:, :4].copy().view(np.float32).reshape(-1), scale)
     assert (got[:, 4:16] == 0).all()
-    np.testing.assert_array_equal(got[:, 16:], codes)
+    np.testing.assert_array_equal(got[:, 16:16 + cfg.d_value], codes)
+    assert (got[:, 16 + cfg.d_value:] == 0).all()
     T, h, k = cfg.T, cfg.heads, cfg.topk
     rows, w = pi.random_selection(37, T, h, k, cfg.slots)
     y = torch.empty((T, cfg.d_value), dtype=torch.bfloat16, device="cuda")
