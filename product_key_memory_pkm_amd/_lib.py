@@ -423,7 +423,8 @@ def pkm_stage_merge_softmax(h, T, sub_idx, sub_score, idx, w, score=None):
 
 
 def pkm_quantize_values(h, V_src, V_fp8, rows=None):
-    """fp8 rows (fp32 scale + E4M3 codes, pkm.h) of the value table V_src [rows, d_value] into V_fp8 (uint8)."""
+    """fp8 rows (fp32 scale + E4M3 codes, padded to fp8_row_bytes(d_value), pkm.h) of the value table
+    V_src [rows, d_value] into V_fp8 (uint8)."""
     _dt(V_src, h.storage, "V_src")
     _dt(V_fp8, torch.uint8, "V_fp8")
     n = V_src.shape[0] if rows is None else rows

@@ -53,7 +53,8 @@ class ProductKeyMemory:
         return sv
 
     def quantize_values(self, V):
-        """fp8 value table (uint8 bytes, rows of a fp32 scale header and E4M3 codes) of V [rows, d_value]."""
+        """fp8 value table of V [rows, d_value]: uint8 bytes, rows of a fp32 scale header and E4M3 codes padded
+        to whole 128-byte lines (fp8_row_bytes(d_value) bytes each)."""
         out = torch.empty(V.shape[0] * L.fp8_row_bytes(self.cfg.d_value), dtype=torch.uint8, device=self.device)
         L.pkm_quantize_values(self.handle, V, out)
         return out
