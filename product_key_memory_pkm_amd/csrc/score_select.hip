@@ -9,8 +9,12 @@
 // codebook as a matrix product and only its top-k survive; product-key paper
 // summary, method details: q split into q1, q2, top-k search in each half.)
 //
-// One workgroup = 8 waves = (TM tokens, one head, one half).  Rows are
+// One workgroup = 16 waves = (TM tokens, one head, one half).  Rows are
 // (token, head, half); a row's key k-th is its k-th largest (score, ~index).
+// With 16 waves a lane holds at most 64 scores and the kernel fits in 128
+// VGPRs, so each SIMD runs four waves of the workgroup: the selection's
+// dependent chains hide each other's latency better than with eight waves of
+// twice the scores (two per SIMD).
 //  1. The TM x dq/2 query tile goes to LDS.
 //  2. MFMA 32x32x16 bf16 (fp32 accumulation): wave w owns key tiles
 //     [w KT, (w+1) KT) of 32 keys and all TM tokens; the sub-keys are the first
@@ -18,8 +22,8 @@
 //     Sub-key fragments come straight from L2 in a layout where one (tile,
 //     16-deep step) operand is one contiguous 1 KB block.  The scores stay in
 //     registers (KT * TM/32 * 16 per lane).
-//  3. Bound: each lane takes 4 maxima over consecutive runs of its scores of a
-//     token, so a row has 64 group maxima.  The k-th largest group maximum is
+//  3. Bound: each lane takes 2 maxima over consecutive runs of its scores of a
+//     token, so a row has 64 group maxima (16 waves x 2 lanes x 2).  The k-th largest group maximum is
 //     a lower bound of the row's k-th largest score (k groups hold a score at
 //     least that large), found by a bitonic sort of the 64 maxima, 16 lanes
 //     per row.
@@ -40,7 +44,7 @@ namespace pkm {
 
 namespace {
 
-constexpr int kSelWaves = 8;
+constexpr int kSelWaves = 16;
 constexpr int kSelThreads = kSelWaves * 64;
 constexpr int kSelCand = 64;  // candidate slots per row
 constexpr int kSelLdsLimit = 96 * 1024;
@@ -133,6 +137,7 @@ __global__ __launch_bounds__(kSelThreads) void score_select_kernel(
     float* __restrict__ sub_score, uint32_t* __restrict__ ovf_count, uint32_t* __restrict__ ovf_rows) {
   constexpr int TM = 32 * NT;
   constexpr int NV = KT * 16;  // scores per lane and token tile
+  constexpr int kG = 32 / kSelWaves;  // group maxima per lane and token: 64 per row
   extern __shared__ __attribute__((aligned(16))) char smem[];
   bf16_t* qt = reinterpret_cast<bf16_t*>(smem);
   char* uni = smem + size_t(TM) * qstride * 2;                // group maxima, then candidate words
@@ -215,20 +220,21 @@ __global__ __launch_bounds__(kSelThreads) void score_select_kernel(
       }
   }
 
-  // 3. four group maxima per lane and token: runs of NV / 4 consecutive scores
+  // 3. kG group maxima per lane and token: runs of NV / kG consecutive scores
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
-    float g[4];
+    float g[kG];
 #pragma unroll
-    for (int gi = 0; gi < 4; ++gi) {
+    for (int gi = 0; gi < kG; ++gi) {
       float m = -INFINITY;
 #pragma unroll
-      for (int j = gi * (NV / 4); j < (gi + 1) * (NV / 4); ++j) m = fmaxf(m, acc[j / 16][n][j % 16]);
+      for (int j = gi * (NV / kG); j < (gi + 1) * (NV / kG); ++j) m = fmaxf(m, acc[j / 16][n][j % 16]);
       g[gi] = m;
     }
     const int row = n * 32 + (lane & 31);
-    u32x4 w = {float_key(g[0]), float_key(g[1]), float_key(g[2]), float_key(g[3])};
-    st16(gmax + size_t(row) * 64 + wave * 8 + (lane >> 5) * 4, w);
+    uint32_t* gd = gmax + size_t(row) * 64 + wave * (2 * kG) + (lane >> 5) * kG;
+#pragma unroll
+    for (int gi = 0; gi < kG; ++gi) gd[gi] = float_key(g[gi]);
   }
   __syncthreads();
 
@@ -250,26 +256,45 @@ __global__ __launch_bounds__(kSelThreads) void score_select_kernel(
   // (score bits, column); the others are written to the lane's spare slot, so the
   // loop has no branch per score.  A lane whose survivors would pass the list's
   // end (its row goes to the exact launch) sends all of them to the spare slot.
+  float bf[NT];
+  uint32_t slot[NT];
+  bool fits[NT];
+  u32x2* rowbuf[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     const int row = n * 32 + (lane & 31);
     const bool live = t0 + row < ntok;
-    const float bf = key_float(bound[row]);
+    bf[n] = key_float(bound[row]);
     int c = 0;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) c += acc[j / 16][n][j % 16] >= bf ? 1 : 0;
-    uint32_t slot = 0;
-    if (live && c > 0) slot = atomicAdd(&cnt[row], uint32_t(c));
-    const bool fits = live && slot + uint32_t(c) <= uint32_t(kSelCand);
-    u32x2* rowbuf = reinterpret_cast<u32x2*>(cand + size_t(row) * kSelCand);
-    u32x2* mine = spare + tid;
+    for (int j = 0; j < NV; ++j) c += acc[j / 16][n][j % 16] >= bf[n] ? 1 : 0;
+    slot[n] = 0;
+    if (live && c > 0) slot[n] = atomicAdd(&cnt[row], uint32_t(c));
+    fits[n] = live && slot[n] + uint32_t(c) <= uint32_t(kSelCand);
+    rowbuf[n] = reinterpret_cast<u32x2*>(cand + size_t(row) * kSelCand);
+  }
+  u32x2* mine = spare + tid;
+  // the column base and the bounds again, opaque to the compiler: otherwise it
+  // computes every column of the loop below right after the MFMAs, and keeps
+  // the count's compare masks for the stores, all live at once.  A lane whose
+  // survivors do not fit compares against NaN, which no score reaches.
+  int cbf = colbase;
+  asm volatile("" : "+v"(cbf));
+  float bs[NT];
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
+  for (int n = 0; n < NT; ++n) {
+    bs[n] = fits[n] ? bf[n] : __builtin_nanf("");
+    asm volatile("" : "+v"(bs[n]));
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const uint32_t col = uint32_t(cbf + (j / 16) * 32 + 8 * ((j % 16) >> 2) + (j & 3));
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
       const float s = acc[j / 16][n][j % 16];
-      const bool keep = fits && s >= bf;
-      const uint32_t col = uint32_t(colbase + (j / 16) * 32 + 8 * ((j % 16) >> 2) + (j & 3));
-      *(keep ? rowbuf + slot : mine) = u32x2{__float_as_uint(s), col};
-      slot += keep ? 1u : 0u;
+      const bool keep = s >= bs[n];
+      *(keep ? rowbuf[n] + slot[n] : mine) = u32x2{__float_as_uint(s), col};
+      slot[n] += keep ? 1u : 0u;
     }
   }
   __syncthreads();
@@ -428,9 +453,9 @@ struct SelPlan {
 SelPlan sel_plan(int half, int nk, int nk2) {
   SelPlan s{};
   const int nmax = nk > nk2 ? nk : nk2;
-  s.KT = nmax <= 512 ? 2 : nmax <= 1024 ? 4 : 8;
-  s.NT = s.KT == 8 ? 1 : 2;
-  s.ntile = 8 * s.KT;
+  s.KT = (nmax <= 512 ? 16 : nmax <= 1024 ? 32 : 64) / kSelWaves;
+  s.NT = nmax > 1024 ? 1 : 2;
+  s.ntile = kSelWaves * s.KT;
   s.nks = half / 16;
   s.qstride = half + 8;
   const int TM = 32 * s.NT;
@@ -487,9 +512,9 @@ hipError_t launch_score_select(hipStream_t s, const void* q, int64_t ntok, int h
                        static_cast<const bf16_t*>(q), ntok, F, dq, half, pl.qstride, P, pl.ntile, pl.nks, nk, nk2, \
                        heads, k, sub_idx, sub_score, ovf_count, ovf_rows);                                      \
   }
+  PKM_SEL_CASE(1, 2)
   PKM_SEL_CASE(2, 2)
-  PKM_SEL_CASE(4, 2)
-  PKM_SEL_CASE(8, 1)
+  PKM_SEL_CASE(4, 1)
 #undef PKM_SEL_CASE
   // rows with heavy ties (usually none): exact selection, one workgroup per listed row
   hipLaunchKernelGGL(score_rows_exact_kernel, dim3(256), dim3(kExactThreads), 0, s, static_cast<const bf16_t*>(q), F, dq, half,
