@@ -365,23 +365,36 @@ __global__ void seg_empty_kernel(int32_t* seg_start, int64_t* count) {
 // 1024 threads, so a few thousand lookups cost one launch instead of a
 // histogram, a scan and a scatter per digit plus the segment passes.  The
 // (key, lookup id) pairs, packed as key << 32 | id, ping-pong between two LDS
-// buffers.  Per 8-bit digit each of the 16 waves owns a contiguous run of
-// pairs, ranks them among equal digits with ballots and counts them in its own
-// LDS row (as radix_scatter_kernel does per tile); one scan over (digit, wave)
+// buffers.  Per digit (DB = 8 or 10 bits) each of the 16 waves owns a
+// contiguous run of pairs, ranks them among equal digits with DB ballots and
+// counts them in its own LDS row of 2^DB counters (as radix_scatter_kernel does
+// per tile); one scan over (digit, wave)
 // turns the counts into bases, and the pairs, still in registers, are written
 // to the other buffer.  The order is stable, so equal keys keep their lookup
 // order.  Then the segment table is built from the sorted keys in the same
 // workgroup, and (plan_counts != null) the value gradient's long-run plan of
 // those segments, from a copy of the segment starts in the free LDS buffer
 // (LDS atomics hand out the chunk slots; the sums over a run's chunks are
-// taken in chunk order, so the slot order does not matter).
+// taken in chunk order, so the slot order does not matter).  10-bit digits
+// sort 17- to 20-bit row ids in two passes instead of three; their 64 KB of
+// counters fit beside the pairs up to kSmallWideMax pairs.
 // ---------------------------------------------------------------------------
 constexpr int kSmallThreads = 1024;
 constexpr int kSmallWaves = kSmallThreads / 64;
 constexpr int kSmallRounds = kSmallSortMax / kSmallWaves / 64;  // 64-pair rounds per wave at most
+constexpr int kSmallPer = kSmallSortMax / kSmallThreads;        // keys per thread at most
+constexpr int kSmallWideMax = 4096;  // pairs up to which 10-bit digits fit the LDS
 
-size_t small_sort_lds_bytes(int64_t n) {
-  return size_t(n) * 16 + size_t(kSmallWaves) * 256 * 4 + 64 * 4;
+// two pair buffers, a row of 2^DB digit counters per wave, 64 words of sums
+size_t small_sort_lds_bytes(int64_t n, int db) {
+  return size_t(n) * 16 + size_t(kSmallWaves) * (size_t(1) << db) * 4 + 64 * 4;
+}
+
+// Digit width of the one-workgroup sort: 10 bits where that saves a pass and
+// the counters fit beside the pairs, else 8.
+int small_digit_bits(int64_t n, int key_bits) {
+  const int p8 = key_bits > 8 ? (key_bits + 7) / 8 : 1, p10 = key_bits > 10 ? (key_bits + 9) / 10 : 1;
+  return n <= kSmallWideMax && p10 < p8 ? 10 : 8;
 }
 
 //
@@ -394,6 +407,7 @@ size_t small_sort_lds_bytes(int64_t n) {
 // and builds the long-run plan, or (plan_stride > 0) each group stays on its
 // own and lists its own long runs in its own plan, plan_stride bytes after the
 // previous group's (counts, chunk_list and long_list all move by it).
+template <int DB>
 __global__ __launch_bounds__(kSmallThreads) void small_sort_segments_kernel(
     const uint32_t* __restrict__ keys_in, int n, int passes, uint32_t* __restrict__ keys_out,
     int32_t* __restrict__ vals_out, int32_t* __restrict__ seg_start, int32_t* __restrict__ touched,
@@ -420,19 +434,32 @@ __global__ __launch_bounds__(kSmallThreads) void small_sort_segments_kernel(
   extern __shared__ __attribute__((aligned(16))) char smem[];
   uint64_t* bufA = reinterpret_cast<uint64_t*>(smem);
   uint64_t* bufB = bufA + n;
-  uint32_t* cnt = reinterpret_cast<uint32_t*>(bufB + n);  // [kSmallWaves][256]
-  uint32_t* wsum = cnt + kSmallWaves * 256;                 // [64]
+  constexpr int NB = 1 << DB;  // digits per pass
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(bufB + n);  // [kSmallWaves][NB]
+  uint32_t* wsum = cnt + kSmallWaves * NB;                  // [64]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) wsum[32] = wsum[33] = 0u;  // long-run plan counters
-  for (int i = tid; i < n; i += kSmallThreads) bufA[i] = (uint64_t(keys_in[i]) << 32) | uint32_t(base + i);
+  {
+    uint32_t kk[kSmallPer];  // every load in flight before the first store
+#pragma unroll
+    for (int r = 0; r < kSmallPer; ++r) {
+      const int i = tid + r * kSmallThreads;
+      kk[r] = i < n ? keys_in[i] : 0u;
+    }
+#pragma unroll
+    for (int r = 0; r < kSmallPer; ++r) {
+      const int i = tid + r * kSmallThreads;
+      if (i < n) bufA[i] = (uint64_t(kk[r]) << 32) | uint32_t(base + i);
+    }
+  }
   // wave w owns pairs [w * per, (w + 1) * per), per a multiple of 64
   const int per = ((n + kSmallWaves - 1) / kSmallWaves + 63) / 64 * 64;
   const int rounds = per / 64;
   uint64_t* src = bufA;
   uint64_t* dst = bufB;
   for (int p = 0; p < passes; ++p) {
-    const int shift = 32 + 8 * p;
-    for (int d = lane; d < 256; d += 64) cnt[wave * 256 + d] = 0;
+    const int shift = 32 + DB * p;
+    for (int d = lane; d < NB; d += 64) cnt[wave * NB + d] = 0;
     __syncthreads();  // bufA filled / previous scatter done; counters cleared
     uint64_t kv[kSmallRounds];
     uint32_t lpos[kSmallRounds];
@@ -442,25 +469,25 @@ __global__ __launch_bounds__(kSmallThreads) void small_sort_segments_kernel(
         const int e = wave * per + r * 64 + lane;
         const bool ok = e < n;
         kv[r] = ok ? src[e] : 0ull;
-        const uint32_t d = uint32_t(kv[r] >> shift) & 0xFFu;
+        const uint32_t d = uint32_t(kv[r] >> shift) & uint32_t(NB - 1);
         uint64_t peers = ballot(ok);
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
+        for (int b = 0; b < DB; ++b) {
           const bool bit = (d >> b) & 1u;
           const uint64_t m = ballot(bit);
           peers &= bit ? m : ~m;
         }
         const int rk = lanes_below(peers);
-        const uint32_t before = ok ? cnt[wave * 256 + d] : 0u;  // every lane reads before the leader writes
+        const uint32_t before = ok ? cnt[wave * NB + d] : 0u;  // every lane reads before the leader writes
         lpos[r] = before + uint32_t(rk);
-        if (ok && rk == 0) cnt[wave * 256 + d] = before + uint32_t(popc64(peers));
+        if (ok && rk == 0) cnt[wave * NB + d] = before + uint32_t(popc64(peers));
       }
     }
     __syncthreads();
-    // bases in (digit, wave) order: digit tid's total, scanned over the 256 digits
+    // bases in (digit, wave) order: digit tid's total, scanned over the NB digits
     uint32_t tot = 0, incl = 0;
-    if (tid < 256) {
-      for (int w = 0; w < kSmallWaves; ++w) tot += cnt[w * 256 + tid];
+    if (tid < NB) {
+      for (int w = 0; w < kSmallWaves; ++w) tot += cnt[w * NB + tid];
       incl = tot;
 #pragma unroll
       for (int dd = 1; dd < 64; dd <<= 1) {
@@ -470,12 +497,12 @@ __global__ __launch_bounds__(kSmallThreads) void small_sort_segments_kernel(
       if (lane == 63) wsum[wave] = incl;
     }
     __syncthreads();
-    if (tid < 256) {
+    if (tid < NB) {
       uint32_t run = incl - tot;
       for (int w = 0; w < wave; ++w) run += wsum[w];
       for (int w = 0; w < kSmallWaves; ++w) {
-        const uint32_t c = cnt[w * 256 + tid];
-        cnt[w * 256 + tid] = run;
+        const uint32_t c = cnt[w * NB + tid];
+        cnt[w * NB + tid] = run;
         run += c;
       }
     }
@@ -485,8 +512,8 @@ __global__ __launch_bounds__(kSmallThreads) void small_sort_segments_kernel(
       if (r < rounds) {
         const int e = wave * per + r * 64 + lane;
         if (e < n) {
-          const uint32_t d = uint32_t(kv[r] >> shift) & 0xFFu;
-          dst[cnt[wave * 256 + d] + lpos[r]] = kv[r];
+          const uint32_t d = uint32_t(kv[r] >> shift) & uint32_t(NB - 1);
+          dst[cnt[wave * NB + d] + lpos[r]] = kv[r];
         }
       }
     }
@@ -629,10 +656,33 @@ __global__ void zero_plan_counts_kernel(uint32_t* counts) {
   if (threadIdx.x < 2) counts[threadIdx.x] = 0u;
 }
 
-// The one-workgroup sort's LDS limit, raised to what kSmallSortMax keys need.
+// The one-workgroup sort's LDS limits, raised to what each digit width's
+// largest batch needs.
 hipError_t small_sort_lds_limit() {
-  static LdsLimit lim;
-  return lim.ensure(reinterpret_cast<const void*>(small_sort_segments_kernel), int(small_sort_lds_bytes(kSmallSortMax)));
+  static LdsLimit lim8, lim10;
+  const hipError_t e = lim8.ensure(reinterpret_cast<const void*>(small_sort_segments_kernel<8>),
+                                   int(small_sort_lds_bytes(kSmallSortMax, 8)));
+  if (e != hipSuccess) return e;
+  return lim10.ensure(reinterpret_cast<const void*>(small_sort_segments_kernel<10>),
+                      int(small_sort_lds_bytes(kSmallWideMax, 10)));
+}
+
+// The one-workgroup sort with digits of db (8 or 10) bits.
+void launch_small_sort(int db, dim3 grid, size_t lds, hipStream_t s, const uint32_t* keys_in, int n, int passes,
+                       uint32_t* keys_out, int32_t* vals_out, int32_t* seg_start, int32_t* touched, int64_t* count,
+                       int chunk, int2* chunk_list, int2* long_list, uint32_t* plan_counts, int64_t plan_stride) {
+  if (db == 10)
+    hipLaunchKernelGGL(small_sort_segments_kernel<10>, grid, dim3(kSmallThreads), lds, s, keys_in, n, passes, keys_out,
+                       vals_out, seg_start, touched, count, chunk, chunk_list, long_list, plan_counts, plan_stride);
+  else
+    hipLaunchKernelGGL(small_sort_segments_kernel<8>, grid, dim3(kSmallThreads), lds, s, keys_in, n, passes, keys_out,
+                       vals_out, seg_start, touched, count, chunk, chunk_list, long_list, plan_counts, plan_stride);
+}
+
+// Digits of db bits for keys of key_bits bits: the passes (at least one).
+int small_passes(int key_bits, int db) {
+  const int p = (key_bits + db - 1) / db;
+  return p < 1 ? 1 : p > 4 ? 4 : p;
 }
 
 inline unsigned grid1d(int64_t n, int64_t cap = 16384) {
@@ -715,15 +765,14 @@ hipError_t launch_sort_segments_grouped(hipStream_t s, const uint32_t* keys_in, 
     const hipError_t e = small_sort_lds_limit();
     if (e != hipSuccess) return e;
   }
-  int passes = (key_bits + 7) / 8;
-  if (passes < 1) passes = 1;
-  if (passes > 4) passes = 4;
+  const int db = small_digit_bits(n_per, key_bits);
+  const int passes = small_passes(key_bits, db);
   int32_t* seg_g = static_cast<int32_t*>(temp);             // groups x (n_per + 1)
   int32_t* touched_g = seg_g + n + kSortGroupsMax;          // groups x n_per
   int64_t* cnt_g = reinterpret_cast<int64_t*>(touched_g + n);  // groups (8-byte aligned: n + n + 1024 ints)
-  hipLaunchKernelGGL(small_sort_segments_kernel, dim3(unsigned(groups)), dim3(kSmallThreads),
-                     small_sort_lds_bytes(n_per), s, keys_in, n_per, passes, keys_out, vals_out, seg_g, touched_g,
-                     cnt_g, kVgChunk, nullptr, nullptr, plan->counts, int64_t(0));
+  launch_small_sort(db, dim3(unsigned(groups)), small_sort_lds_bytes(n_per, db), s, keys_in, n_per, passes, keys_out,
+                    vals_out, seg_g, touched_g, cnt_g, kVgChunk, static_cast<int2*>(nullptr),
+                    static_cast<int2*>(nullptr), plan->counts, int64_t(0));
   int64_t jb = (n + kJoinThreads - 1) / kJoinThreads;
   if (jb > 1024) jb = 1024;
   hipLaunchKernelGGL(group_segments_kernel, dim3(unsigned(jb)), dim3(kJoinThreads), 0, s, seg_g, touched_g, cnt_g,
@@ -740,13 +789,12 @@ hipError_t launch_sort_segments_small(hipStream_t s, const uint32_t* keys_in, in
     const hipError_t e = small_sort_lds_limit();
     if (e != hipSuccess) return e;
   }
-  int passes = (key_bits + 7) / 8;
-  if (passes < 1) passes = 1;
-  if (passes > 4) passes = 4;
-  hipLaunchKernelGGL(small_sort_segments_kernel, dim3(1), dim3(kSmallThreads), small_sort_lds_bytes(n), s, keys_in,
-                     int(n), passes, keys_out, vals_out, seg_start, touched, count, kVgChunk,
-                     plan ? plan->chunk_list : nullptr, plan ? plan->long_list : nullptr,
-                     plan ? plan->counts : nullptr, int64_t(0));
+  const int db = small_digit_bits(n, key_bits);
+  const int passes = small_passes(key_bits, db);
+  launch_small_sort(db, dim3(1), small_sort_lds_bytes(n, db), s, keys_in, int(n), passes, keys_out, vals_out,
+                    seg_start, touched, count, kVgChunk, plan ? plan->chunk_list : static_cast<int2*>(nullptr),
+                    plan ? plan->long_list : static_cast<int2*>(nullptr),
+                    plan ? plan->counts : static_cast<uint32_t*>(nullptr), int64_t(0));
   return hipGetLastError();
 }
 
@@ -789,14 +837,12 @@ hipError_t launch_sort_segments_separate(hipStream_t s, const uint32_t* keys_in,
     const hipError_t e = small_sort_lds_limit();
     if (e != hipSuccess) return e;
   }
-  int passes = (key_bits + 7) / 8;
-  if (passes < 1) passes = 1;
-  if (passes > 4) passes = 4;
+  const int db = small_digit_bits(n_per, key_bits);
+  const int passes = small_passes(key_bits, db);
   const VgPlan p0 = group_plan(plans, 0);
-  hipLaunchKernelGGL(small_sort_segments_kernel, dim3(unsigned(groups)), dim3(kSmallThreads),
-                     small_sort_lds_bytes(n_per), s, keys_in, n_per, passes, keys_out, vals_out, seg_g,
-                     static_cast<int32_t*>(nullptr), cnt_g, kVgChunk, p0.chunk_list, p0.long_list, p0.counts,
-                     int64_t(group_plan_stride()));
+  launch_small_sort(db, dim3(unsigned(groups)), small_sort_lds_bytes(n_per, db), s, keys_in, n_per, passes, keys_out,
+                    vals_out, seg_g, static_cast<int32_t*>(nullptr), cnt_g, kVgChunk, p0.chunk_list, p0.long_list,
+                    p0.counts, int64_t(group_plan_stride()));
   return hipGetLastError();
 }
 
