@@ -1155,11 +1155,14 @@ pkm_status fwpkm_calls(pkm_handle_t handle, void* stream, int64_t T, int64_t cal
   int32_t* sub_idx = at<int32_t>(ws, F.sub_idx);
   float* sub_score = at<float>(ws, F.sub_score);
   PKM_TRY(run_score(handle, s, T, q, C, Cp, sub_idx, sub_score, ws));
-  PKM_TRY(run_merge(handle, s, T, sub_idx, sub_score, idx, w, nullptr, streams > 1 ? call_T / streams : 0, streams));
-  // the slices' steps reuse the scoring's workspace (its results are in idx and w)
   const int64_t R = int64_t(c.heads) * c.topk;
   const size_t row_bytes = size_t(c.d_value) * size_t(handle->elem);
   const int64_t calls = T / call_T, n_call = call_T * R;
+  // one call of one stream: the merge, the gather and the residual in one launch
+  const bool fused = streams == 1 && calls == 1 && merge_gather_supported(c.dtype, c.topk, c.d_value, false);
+  if (!fused)
+    PKM_TRY(run_merge(handle, s, T, sub_idx, sub_score, idx, w, nullptr, streams > 1 ? call_T / streams : 0, streams));
+  // the slices' steps reuse the scoring's workspace (its results are in idx and w)
   if (streams == 1 && calls > 1 && calls <= kSortGroupsMax && n_call <= kSmallSortMax) {
     // One stream whose calls each fit one workgroup's grouping: every call's
     // grouping (and long-run plan) in one launch of a workgroup per call, up
@@ -1239,9 +1242,14 @@ pkm_status fwpkm_calls(pkm_handle_t handle, void* stream, int64_t T, int64_t cal
   for (int64_t t0 = 0; t0 < T; t0 += call_T) {
     const int32_t* ci = idx + t0 * R;
     const float* cw = w + t0 * R;
-    PKM_HIP(launch_gather(s, c.dtype, ci, cw, V, static_cast<char*>(y) + t0 * row_bytes, call_T, int(R), c.d_value,
-                          false, static_cast<const char*>(target) + t0 * row_bytes, e),
-            "value gather-sum and reconstruction residual");
+    if (fused)
+      PKM_HIP(launch_merge_gather(s, c.dtype, sub_idx, sub_score, T, c.heads, c.topk, c.n_keys2,
+                                  1.0f / c.temperature, idx, w, V, y, c.d_value, false, target, e),
+              "candidate merge, value gather-sum and reconstruction residual");
+    else
+      PKM_HIP(launch_gather(s, c.dtype, ci, cw, V, static_cast<char*>(y) + t0 * row_bytes, call_T, int(R), c.d_value,
+                            false, static_cast<const char*>(target) + t0 * row_bytes, e),
+              "value gather-sum and reconstruction residual");
     VgAdam sgd{};
     sgd.V = V;
     sgd.step_size = lr;

@@ -45,9 +45,12 @@ hipError_t launch_gather(hipStream_t s, int dtype, const int32_t* idx, const flo
 // launches.  Supported when merge_gather_supported (k divides 64, rows of at
 // most 256 16-byte vectors, storage-dtype values); else hipErrorInvalidValue.
 bool merge_gather_supported(int dtype, int k, int d_value, bool fp8_values);
+// target, resid (both or neither): also the residual resid = y - target [ntok,
+// d_value], as launch_gather writes it.
 hipError_t launch_merge_gather(hipStream_t s, int dtype, const int32_t* sub_idx, const float* sub_score, int64_t ntok,
                                int heads, int k, int nk2, float inv_tau, int32_t* idx, float* w, const void* V,
-                               void* y, int d_value, bool fp8_values);
+                               void* y, int d_value, bool fp8_values, const void* target = nullptr,
+                               void* resid = nullptr);
 // fp8 value rows from rows in the storage dtype (d_value % 16 == 0).
 hipError_t launch_quantize_fp8(hipStream_t s, int dtype, const void* src, int64_t rows, int d_value, void* dst);
 

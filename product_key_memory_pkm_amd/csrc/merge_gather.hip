@@ -15,13 +15,16 @@ namespace {
 // rows and weights the backward keeps, and gathers the value rows of each
 // 64-row chunk (64 / k heads) with the loop of gather_sum_kernel, rows in the
 // same order, so y is bit-identical to the two launches.  The merge's VALU
-// work runs while the other waves' row loads are in flight.
+// work runs while the other waves' row loads are in flight.  resid != null
+// (the fast-weight memorization): also the residual y - target, as
+// gather_sum_kernel writes it.
 template <typename T, int NVL, int U>
 __global__ __launch_bounds__(256) void merge_gather_kernel(const int32_t* __restrict__ sub_idx,
                                                            const float* __restrict__ sub_score, int64_t ntok,
                                                            int heads, int k, int nk2, float inv_tau,
                                                            int32_t* __restrict__ idx_out, float* __restrict__ w_out,
-                                                           const T* __restrict__ V, T* __restrict__ y, int nvec) {
+                                                           const T* __restrict__ V, T* __restrict__ y, int nvec,
+                                                           const T* __restrict__ target, T* __restrict__ resid) {
   constexpr int E = Vec16<T>::N;
   __shared__ uint16_t pairs[128];
   __shared__ int npairs;
@@ -114,6 +117,20 @@ __global__ __launch_bounds__(256) void merge_gather_kernel(const int32_t* __rest
 #pragma unroll
   for (int m = 0; m < NVL; ++m)
     if (valid[m]) st16(yb + voff[m], Vec16<T>::narrow(acc[m]));
+  if (resid) {  // wave-uniform
+    const char* tb = reinterpret_cast<const char*>(target) + size_t(t) * row_bytes;
+    char* eb = reinterpret_cast<char*>(resid) + size_t(t) * row_bytes;
+#pragma unroll
+    for (int m = 0; m < NVL; ++m)
+      if (valid[m]) {
+        float yf[E], tf[E];
+        Vec16<T>::widen(Vec16<T>::narrow(acc[m]), yf);
+        Vec16<T>::widen(ld16(tb + voff[m]), tf);
+#pragma unroll
+        for (int e = 0; e < E; ++e) yf[e] -= tf[e];
+        st16(eb + voff[m], Vec16<T>::narrow(yf));
+      }
+  }
 }
 
 }  // namespace
@@ -121,26 +138,30 @@ __global__ __launch_bounds__(256) void merge_gather_kernel(const int32_t* __rest
 template <typename T, int NVL>
 static void launch_merge_gather_nvl(hipStream_t s, const int32_t* sub_idx, const float* sub_score, int64_t ntok,
                                     int heads, int k, int nk2, float inv_tau, int32_t* idx, float* w, const void* V,
-                                    void* y, int nvec) {
+                                    void* y, int nvec, const void* target, void* resid) {
   constexpr int U = NVL <= 2 ? 8 : 4;
   hipLaunchKernelGGL((merge_gather_kernel<T, NVL, U>), dim3(unsigned((ntok + 3) / 4)), dim3(256), 0, s, sub_idx,
                      sub_score, ntok, heads, k, nk2, inv_tau, idx, w, static_cast<const T*>(V), static_cast<T*>(y),
-                     nvec);
+                     nvec, static_cast<const T*>(target), static_cast<T*>(resid));
 }
 
 template <typename T>
 static void launch_merge_gather_t(hipStream_t s, const int32_t* sub_idx, const float* sub_score, int64_t ntok,
                                   int heads, int k, int nk2, float inv_tau, int32_t* idx, float* w, const void* V,
-                                  void* y, int nvec) {
+                                  void* y, int nvec, const void* target, void* resid) {
   const int per_lane = (nvec + 63) / 64;
   if (per_lane <= 1)
-    launch_merge_gather_nvl<T, 1>(s, sub_idx, sub_score, ntok, heads, k, nk2, inv_tau, idx, w, V, y, nvec);
+    launch_merge_gather_nvl<T, 1>(s, sub_idx, sub_score, ntok, heads, k, nk2, inv_tau, idx, w, V, y, nvec, target,
+                                  resid);
   else if (per_lane == 2)
-    launch_merge_gather_nvl<T, 2>(s, sub_idx, sub_score, ntok, heads, k, nk2, inv_tau, idx, w, V, y, nvec);
+    launch_merge_gather_nvl<T, 2>(s, sub_idx, sub_score, ntok, heads, k, nk2, inv_tau, idx, w, V, y, nvec, target,
+                                  resid);
   else if (per_lane == 3)
-    launch_merge_gather_nvl<T, 3>(s, sub_idx, sub_score, ntok, heads, k, nk2, inv_tau, idx, w, V, y, nvec);
+    launch_merge_gather_nvl<T, 3>(s, sub_idx, sub_score, ntok, heads, k, nk2, inv_tau, idx, w, V, y, nvec, target,
+                                  resid);
   else
-    launch_merge_gather_nvl<T, 4>(s, sub_idx, sub_score, ntok, heads, k, nk2, inv_tau, idx, w, V, y, nvec);
+    launch_merge_gather_nvl<T, 4>(s, sub_idx, sub_score, ntok, heads, k, nk2, inv_tau, idx, w, V, y, nvec, target,
+                                  resid);
 }
 
 bool merge_gather_supported(int dtype, int k, int d_value, bool fp8_values) {
@@ -151,15 +172,18 @@ bool merge_gather_supported(int dtype, int k, int d_value, bool fp8_values) {
 
 hipError_t launch_merge_gather(hipStream_t s, int dtype, const int32_t* sub_idx, const float* sub_score, int64_t ntok,
                                int heads, int k, int nk2, float inv_tau, int32_t* idx, float* w, const void* V,
-                               void* y, int d_value, bool fp8_values) {
+                               void* y, int d_value, bool fp8_values, const void* target, void* resid) {
   if (!merge_gather_supported(dtype, k, d_value, fp8_values)) return hipErrorInvalidValue;
+  if ((resid == nullptr) != (target == nullptr)) return hipErrorInvalidValue;
   if (ntok == 0) return hipGetLastError();
   const int elem = dtype == kBF16 ? 2 : 4;
   const int nvec = d_value * elem / 16;
   if (dtype == kBF16)
-    launch_merge_gather_t<bf16_t>(s, sub_idx, sub_score, ntok, heads, k, nk2, inv_tau, idx, w, V, y, nvec);
+    launch_merge_gather_t<bf16_t>(s, sub_idx, sub_score, ntok, heads, k, nk2, inv_tau, idx, w, V, y, nvec, target,
+                                  resid);
   else
-    launch_merge_gather_t<float>(s, sub_idx, sub_score, ntok, heads, k, nk2, inv_tau, idx, w, V, y, nvec);
+    launch_merge_gather_t<float>(s, sub_idx, sub_score, ntok, heads, k, nk2, inv_tau, idx, w, V, y, nvec, target,
+                                 resid);
   return hipGetLastError();
 }
 
