@@ -13,7 +13,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpkm.so")
+# PKM_LIB_PATH names another build of the same library (the CPU tests load a
+# copy whose host code carries address and undefined-behaviour checks)
+LIB_PATH = os.environ.get("PKM_LIB_PATH") or os.path.join(_HERE, "libpkm.so")
 
 PKM_OK, PKM_ERR_INVALID_ARG, PKM_ERR_UNSUPPORTED, PKM_ERR_WORKSPACE, PKM_ERR_HIP = range(5)
 PKM_F32, PKM_BF16 = 0, 1
