@@ -26,23 +26,28 @@ def _asan_runtime():
 
 
 def _build_sanitized():
+    """Every source compiled afresh into its own folder (never the in-tree library's objects, which
+    may predate the sources): api.hip with the host sanitizers, the others as the regular build does."""
+    from concurrent.futures import ThreadPoolExecutor
+
     from product_key_memory_pkm_amd import build as B
     os.makedirs(OUT_DIR, exist_ok=True)
-    objs = []
-    for src in B.SOURCES:
-        if src == "api.hip":
-            continue
-        obj = os.path.join(B.BUILD, src.replace(".hip", ".o"))
-        if not os.path.exists(obj):
-            B.build()
-        objs.append(obj)
     san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
-    api_obj = os.path.join(OUT_DIR, "api.o")
-    flags = [f for f in B.FLAGS if f != "-O3"] + ["-O1", "-g"]
-    B._run([HIPCC, *flags, *san, "-c", os.path.join(B.CSRC, "api.hip"), "-o", api_obj])
+
+    def compile_one(src):
+        obj = os.path.join(OUT_DIR, src.replace(".hip", ".o"))
+        if src == "api.hip":
+            flags = [f for f in B.FLAGS if f != "-O3"] + ["-O1", "-g"] + san
+        else:
+            flags = list(B.FLAGS)
+        B._run([HIPCC, *flags, "-c", os.path.join(B.CSRC, src), "-o", obj])
+        return obj
+
+    with ThreadPoolExecutor(min(8, os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(compile_one, B.SOURCES))
     lib = os.path.join(OUT_DIR, "libpkm.so")
-    B._run([HIPCC, "-shared", "-fPIC", f"--offload-arch={B.ARCH}", *san, api_obj, *objs, "-o", lib])
+    B._run([HIPCC, "-shared", "-fPIC", f"--offload-arch={B.ARCH}", *san, *objs, "-o", lib])
     return lib
 
 
